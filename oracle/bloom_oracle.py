@@ -1,0 +1,346 @@
+"""Plain float64 CPU oracle of BLOOM greedy KV-cached generation.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py``; never by the product.  Shares no code
+with the HIP path.
+
+What it computes, and where the pages say so:
+
+* greedy generation of new tokens with a KV cache ("Incredibly Fast BLOOM Inference
+  with DeepSpeed and Accelerate", Benchmark Environment: do_sample=False, KV cache on);
+* a pre-LayerNorm decoder layer: input LayerNorm feeding the fused QKV projection,
+  attention, the output projection with bias and residual, the post-attention
+  LayerNorm feeding the MLP ("DeepSpeed Inference ...", Section III.D, Putting It
+  Together: the four fused groups name exactly these steps);
+* ALiBi positional bias ("Hugging Face BLOOM Inference Optimization", Efficient
+  PyTorch Implementation), with the slopes of the ALiBi paper (Press, Smith and
+  Lewis, "Train Short, Test Long", ICLR 2022, Section 3), since the pages give none;
+* masked fill of the attention scores followed by a softmax ("Hugging Face BLOOM
+  Inference Optimization", Custom CUDA Kernels and Hardware Acceleration); masked
+  keys get probability exactly 0;
+* the tanh form of GeLU (same page, Kernel Fusion with torch.jit.script, which names
+  ``bloom_gelu_forward``), with the Hendrycks-Gimpel constants sqrt(2/pi), 0.044715;
+* tied embeddings: the LM head is the embedding matrix.
+
+Readings where the pages are silent (all in float64 unless a caller asks otherwise):
+LayerNorm uses the biased variance with eps from the model shape (1e-5); the
+ALiBi bias is slope * (key position - left padding), i.e. positions counted over
+real tokens only; the bias is added after the 1/sqrt(head_dim) score scale; the
+fused QKV rows are ordered [head][q, k, v][head_dim]; every linear has a bias;
+int8 weights mean W[r, k] = scale[r] * q[r, k]; a query with no valid key gives a
+zero attention output; greedy ties go to the lowest token id, taken on logits
+rounded to float32 (the precision the GPU path decides in).
+
+No blocking, fusion or reordering beyond the definitions above, except that the
+LM-head product is evaluated over slices of the vocabulary (each logit is still
+one dot product) so that a 250880 x 14336 embedding is never widened at once.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import List, Optional
+
+import numpy as np
+
+F64 = np.float64
+
+
+# ---------------------------------------------------------------------------
+# elementary operations
+# ---------------------------------------------------------------------------
+
+def alibi_slopes(n_head_total: int, dtype=F64) -> np.ndarray:
+    """Per-head ALiBi slopes for a model with ``n_head_total`` heads.
+
+    ALiBi paper, Section 3: for n heads (n a power of two) the slopes are the
+    geometric sequence starting at 2^(-8/n) with that same ratio.  For other n, the
+    first c = 2^floor(log2 n) heads take the c-head sequence and the remaining
+    n - c heads take every other term (the 1st, 3rd, 5th, ...) of the 2c-head
+    sequence.
+    """
+    n = int(n_head_total)
+    if n < 1:
+        raise ValueError("n_head_total must be >= 1")
+    c = 1 << (n.bit_length() - 1)
+    seq_c = [2.0 ** (-8.0 * k / c) for k in range(1, c + 1)]
+    seq_2c = [2.0 ** (-8.0 * k / (2 * c)) for k in range(1, 2 * c + 1)]
+    rest = seq_2c[0::2][: n - c]
+    return np.array(seq_c + rest, dtype=dtype)
+
+
+def layer_norm(x: np.ndarray, gamma, beta, eps: float) -> np.ndarray:
+    """LayerNorm over the last axis: gamma * (x - mean) / sqrt(biased var + eps) + beta."""
+    mu = x.mean(axis=-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+    return (x - mu) / np.sqrt(var + eps) * gamma + beta
+
+
+def gelu_tanh(x: np.ndarray) -> np.ndarray:
+    """0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))."""
+    return 0.5 * x * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (x + 0.044715 * x ** 3)))
+
+
+def masked_softmax(s: np.ndarray, valid: np.ndarray) -> np.ndarray:
+    """Softmax over the last axis restricted to ``valid`` entries.
+
+    Masked entries get probability exactly 0 (masked_fill with -inf before the
+    softmax).  A row with no valid entry is all zeros.
+    """
+    valid = np.broadcast_to(valid, s.shape)
+    filled = np.where(valid, s, -np.inf)
+    m = filled.max(axis=-1, keepdims=True)
+    m = np.where(np.isfinite(m), m, 0.0)
+    e = np.where(valid, np.exp(np.where(valid, filled - m, 0.0)), 0.0)
+    z = e.sum(axis=-1, keepdims=True)
+    return np.where(z > 0, e / np.where(z > 0, z, 1.0), 0.0)
+
+
+def alibi_masked_softmax(scores: np.ndarray, valid_len, n_head_total: int,
+                         head_offset: int = 0, dtype=F64) -> np.ndarray:
+    """The standalone fused op: ALiBi bias, left-pad + causal mask, softmax.
+
+    ``scores`` [B, H, Q, K] are already scaled by 1/sqrt(head_dim).  Row b has
+    ``valid_len[b]`` real keys at the right end (keys j >= K - valid_len[b]); query i
+    sits at key position K - Q + i and sees keys up to that position.  Heads are
+    global heads head_offset .. head_offset + H - 1 of an n_head_total-head model.
+    """
+    s = np.asarray(scores, dtype)
+    B, H, Q, K = s.shape
+    slopes = alibi_slopes(n_head_total, dtype)[head_offset: head_offset + H]
+    pad = K - np.asarray(valid_len, dtype=np.int64).reshape(B)
+    j = np.arange(K)
+    qpos = K - Q + np.arange(Q)
+    rel = (j[None, :] - pad[:, None]).astype(dtype)                       # [B, K]
+    bias = slopes[None, :, None, None] * rel[:, None, None, :]            # [B, H, 1, K]
+    valid = (j[None, None, None, :] >= pad[:, None, None, None]) & \
+            (j[None, None, None, :] <= qpos[None, None, :, None])         # [B, 1, Q, K]
+    return masked_softmax(s + bias, valid)
+
+
+class Int8RowScale:
+    """Weight-only int8 matrix: W[r, k] = scale[r] * q[r, k]."""
+
+    def __init__(self, q: np.ndarray, scale: np.ndarray):
+        self.q = np.asarray(q, dtype=np.int8)
+        self.scale = np.asarray(scale)
+        if self.scale.shape != (self.q.shape[0],):
+            raise ValueError("one scale per output row")
+
+    @property
+    def shape(self):
+        return self.q.shape
+
+    def dense(self, dtype=F64) -> np.ndarray:
+        return self.scale.astype(dtype)[:, None] * self.q.astype(dtype)
+
+
+def _dense(w, dtype):
+    return w.dense(dtype) if isinstance(w, Int8RowScale) else np.asarray(w, dtype=dtype)
+
+
+def linear(x: np.ndarray, w, b=None, dtype=F64) -> np.ndarray:
+    """y = x W^T + b with W stored [out, in]."""
+    y = x @ _dense(w, dtype).T
+    return y if b is None else y + np.asarray(b, dtype=dtype)
+
+
+def attention(q: np.ndarray, k_all: np.ndarray, v_all: np.ndarray, slopes: np.ndarray,
+              pad: np.ndarray, start: int) -> np.ndarray:
+    """ALiBi attention of S new queries over the cached keys.
+
+    q [B, S, H, d] (query s at absolute position start + s); k_all, v_all [B, H, T, d]
+    hold positions 0 .. T-1.  Key j is visible to the query at position p iff
+    pad[b] <= j <= p.  score = q.k / sqrt(d) + slope_h * (j - pad[b]).
+    Returns o [B, S, H, d].
+    """
+    B, S, H, d = q.shape
+    T = k_all.shape[2]
+    scores = np.einsum("bshd,bhtd->bhst", q, k_all) / math.sqrt(d)
+    j = np.arange(T)
+    p = start + np.arange(S)
+    rel = (j[None, :] - pad[:, None]).astype(q.dtype)                      # [B, T]
+    bias = slopes[None, :, None, None] * rel[:, None, None, :]
+    valid = (j[None, None, None, :] >= pad[:, None, None, None]) & \
+            (j[None, None, None, :] <= p[None, None, :, None])
+    probs = masked_softmax(scores + bias, valid)
+    return np.einsum("bhst,bhtd->bshd", probs, v_all)
+
+
+# ---------------------------------------------------------------------------
+# model
+# ---------------------------------------------------------------------------
+
+def _widen(a: np.ndarray, storage: str) -> np.ndarray:
+    """Exact value of a stored tensor: bf16 / fp16 bit patterns (uint16) or floats."""
+    a = np.asarray(a)
+    if storage == "bf16" and a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32)
+    if storage == "f16" and a.dtype == np.uint16:
+        return a.view(np.float16).astype(np.float32)
+    return a
+
+
+@dataclasses.dataclass
+class OracleModel:
+    """Shape plus weight values of one BLOOM stack (whole model or one TP share)."""
+    n_layer: int
+    hidden: int
+    n_head_total: int
+    head_offset: int
+    n_head_local: int
+    head_dim: int
+    ffn: int
+    vocab: int
+    embed_ln: bool
+    ln_eps: float
+    embed: np.ndarray
+    emb_ln: Optional[tuple]
+    lnf: tuple
+    layers: List[dict]
+    dtype: type = F64
+
+    @classmethod
+    def from_storage(cls, shape, tensors: dict, dtype=F64, widen_weights: bool = True):
+        """Build from a shape (attributes as in the workload description) and tensors in
+        storage form: bf16 as uint16 bits, fp16 scales as uint16 bits, int8, float32."""
+        wd = shape.weight_dtype
+        pd = "f32" if wd == "f32" else "bf16"
+
+        def par(a):
+            return _widen(a, pd).astype(dtype)
+
+        def mat(lw, field):
+            if wd == "int8":
+                return Int8RowScale(lw["w_" + field], _widen(lw["s_" + field], "f16"))
+            w = _widen(lw["w_" + field], wd)
+            return w.astype(dtype) if widen_weights else w
+
+        layers = []
+        for lw in tensors["layers"]:
+            layers.append({
+                "ln1": (par(lw["ln1_g"]), par(lw["ln1_b"])),
+                "qkv": mat(lw, "qkv"), "b_qkv": par(lw["b_qkv"]),
+                "dense": mat(lw, "dense"), "b_dense": par(lw["b_dense"]),
+                "ln2": (par(lw["ln2_g"]), par(lw["ln2_b"])),
+                "up": mat(lw, "up"), "b_up": par(lw["b_up"]),
+                "down": mat(lw, "down"), "b_down": par(lw["b_down"]),
+            })
+        emb_ln = None
+        if shape.embed_ln:
+            emb_ln = (par(tensors["emb_ln_g"]), par(tensors["emb_ln_b"]))
+        return cls(n_layer=len(layers), hidden=shape.hidden, n_head_total=shape.n_head_total,
+                   head_offset=shape.head_offset, n_head_local=shape.n_head_local,
+                   head_dim=shape.head_dim, ffn=shape.ffn, vocab=shape.vocab,
+                   embed_ln=bool(shape.embed_ln), ln_eps=float(shape.ln_eps),
+                   embed=_widen(tensors["embed"], pd), emb_ln=emb_ln,
+                   lnf=(par(tensors["lnf_g"]), par(tensors["lnf_b"])), layers=layers,
+                   dtype=dtype)
+
+    @property
+    def slopes(self) -> np.ndarray:
+        all_slopes = alibi_slopes(self.n_head_total, self.dtype)
+        return all_slopes[self.head_offset: self.head_offset + self.n_head_local]
+
+
+def new_cache(model: OracleModel, batch: int) -> list:
+    H, d = model.n_head_local, model.head_dim
+    empty = np.zeros((batch, H, 0, d), dtype=model.dtype)
+    return [{"k": empty, "v": empty} for _ in range(model.n_layer)]
+
+
+def forward(model: OracleModel, tokens: np.ndarray, start: int, pad: np.ndarray,
+            cache: list, trace: Optional[list] = None) -> np.ndarray:
+    """Run S new tokens per row through the stack, appending their K/V to ``cache``.
+
+    tokens [B, S] sit at absolute positions start .. start+S-1; ``cache`` already holds
+    positions 0 .. start-1.  pad[b] = number of left-pad slots of row b.  Returns the
+    final-LayerNorm hidden state [B, S, hidden].  If ``trace`` is a list, the residual
+    stream after every layer is appended to it.
+    """
+    dt = model.dtype
+    tokens = np.asarray(tokens)
+    pad = np.asarray(pad, dtype=np.int64)
+    B, S = tokens.shape
+    H, d = model.n_head_local, model.head_dim
+    if cache[0]["k"].shape[2] != start:
+        raise ValueError("cache length does not match start position")
+    x = np.asarray(model.embed[tokens], dtype=dt)
+    if model.embed_ln:
+        x = layer_norm(x, model.emb_ln[0], model.emb_ln[1], model.ln_eps)
+    slopes = model.slopes
+    for li, lw in enumerate(model.layers):
+        a = layer_norm(x, lw["ln1"][0], lw["ln1"][1], model.ln_eps)
+        qkv = linear(a, lw["qkv"], lw["b_qkv"], dt).reshape(B, S, H, 3, d)
+        q, k, v = qkv[:, :, :, 0, :], qkv[:, :, :, 1, :], qkv[:, :, :, 2, :]
+        c = cache[li]
+        c["k"] = np.concatenate([c["k"], k.transpose(0, 2, 1, 3)], axis=2)
+        c["v"] = np.concatenate([c["v"], v.transpose(0, 2, 1, 3)], axis=2)
+        o = attention(q, c["k"], c["v"], slopes, pad, start)
+        x = x + linear(o.reshape(B, S, H * d), lw["dense"], lw["b_dense"], dt)
+        a2 = layer_norm(x, lw["ln2"][0], lw["ln2"][1], model.ln_eps)
+        u = gelu_tanh(linear(a2, lw["up"], lw["b_up"], dt))
+        x = x + linear(u, lw["down"], lw["b_down"], dt)
+        if trace is not None:
+            trace.append(x.copy())
+    return layer_norm(x, model.lnf[0], model.lnf[1], model.ln_eps)
+
+
+def lm_logits(model: OracleModel, hidden: np.ndarray, chunk: int = 16384) -> np.ndarray:
+    """Tied LM head: logits = hidden E^T, one dot product per logit (vocab taken in slices)."""
+    hidden = np.asarray(hidden, dtype=model.dtype)
+    out = np.empty(hidden.shape[:-1] + (model.vocab,), dtype=model.dtype)
+    for v0 in range(0, model.vocab, chunk):
+        e = np.asarray(model.embed[v0: v0 + chunk], dtype=model.dtype)
+        out[..., v0: v0 + chunk] = hidden @ e.T
+    return out
+
+
+@dataclasses.dataclass
+class GenerateResult:
+    tokens: np.ndarray        # [B, n_new] oracle greedy choice at each step
+    hidden: np.ndarray        # [n_new, B, hidden] final-LN state that produced each token
+    top1: np.ndarray          # [n_new, B] largest logit
+    top2: np.ndarray          # [n_new, B] second largest logit
+    rms: np.ndarray           # [n_new, B] root-mean-square of the logits row
+    chosen: Optional[np.ndarray]  # [n_new, B] oracle logit of the forced token (teacher forcing)
+    cache: list
+
+
+def greedy_argmax(logits: np.ndarray) -> np.ndarray:
+    """Lowest token id among the maxima, decided on float32-rounded logits."""
+    return np.argmax(logits.astype(np.float32), axis=-1).astype(np.int32)
+
+
+def greedy_generate(model: OracleModel, prompt: np.ndarray, valid_len, n_new: int,
+                    forced: Optional[np.ndarray] = None) -> GenerateResult:
+    """Greedy generation of ``n_new`` tokens: one forward over the left-padded prompt
+    (which yields token 1), then one single-token forward per further token.
+
+    With ``forced`` [B, n_new] (teacher forcing) the token fed back at step t is
+    forced[:, t] instead of the oracle's own choice; the oracle's choice and the
+    logit of the forced token are still recorded.
+    """
+    prompt = np.asarray(prompt)
+    B, P = prompt.shape
+    pad = P - np.asarray(valid_len, dtype=np.int64).reshape(B)
+    cache = new_cache(model, B)
+    toks = np.zeros((B, n_new), dtype=np.int32)
+    hid = np.zeros((n_new, B, model.hidden), dtype=model.dtype)
+    top1 = np.zeros((n_new, B)); top2 = np.zeros((n_new, B)); rms = np.zeros((n_new, B))
+    chosen = None if forced is None else np.zeros((n_new, B))
+    h = forward(model, prompt, 0, pad, cache)[:, -1]
+    for t in range(n_new):
+        logits = lm_logits(model, h)
+        toks[:, t] = greedy_argmax(logits)
+        hid[t] = h
+        part = np.partition(logits, -2, axis=-1)
+        top1[t], top2[t] = part[:, -1], part[:, -2]
+        rms[t] = np.sqrt(np.mean(logits ** 2, axis=-1))
+        nxt = toks[:, t]
+        if forced is not None:
+            nxt = np.asarray(forced[:, t], dtype=np.int32)
+            chosen[t] = logits[np.arange(B), nxt]
+        if t + 1 < n_new:
+            h = forward(model, nxt[:, None], P + t, pad, cache)[:, 0]
+    return GenerateResult(toks, hid, top1, top2, rms, chosen, cache)

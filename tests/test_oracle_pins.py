@@ -1,0 +1,422 @@
+"""Pins of the CPU oracle against things other than itself.
+
+* the Hugging Face ``transformers`` BLOOM model (an independent implementation of
+  the model the pages serve), run in float64 on the CPU;
+* values printed in the ALiBi paper (tests/golden/alibi_paper_slopes.txt);
+* library routines for the textbook special cases (torch LayerNorm and tanh-GeLU,
+  scipy softmax and erf);
+* closed forms and invariants (row sums, exact zeros, shift invariance, one-hot,
+  left-pad and batch-permutation invariance, incremental decode == full re-run).
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import bloom_inputs as bi
+import oracle
+from oracle import bloom_oracle as bo
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------------------
+# ALiBi slopes
+# ---------------------------------------------------------------------------
+
+def test_alibi_slopes_match_paper_values():
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "alibi_paper_slopes.txt"))
+            if l.strip() and not l.startswith("#")]
+    by_n = {}
+    for n, h, e in rows:
+        by_n.setdefault(int(n), {})[int(h)] = float(e)
+    for n, table in by_n.items():
+        s = oracle.alibi_slopes(n)
+        assert len(s) == n
+        for h, e in table.items():
+            expect = 2.0 ** -e
+            if float(e).is_integer():
+                assert s[h] == expect            # exact powers of two
+            else:
+                assert s[h] == pytest.approx(expect, rel=1e-15)
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 5, 6, 8, 12, 14, 16, 20, 24, 32, 40, 48, 64, 96, 112, 128])
+def test_alibi_slopes_match_hf_bloom(n, hf_available):
+    from transformers.models.bloom.modeling_bloom import build_alibi_tensor
+
+    mask = torch.ones(1, 2, dtype=torch.int64)
+    alibi = build_alibi_tensor(mask, n, torch.float64)  # [n, 1, 2]: slope * position
+    hf = alibi[:, 0, 1].numpy()
+    # HF raises a float32 base to integer powers, so agreement is to a few float32 ulps;
+    # any structural slip (wrong base, even instead of odd extra terms) is >= 4%
+    np.testing.assert_allclose(oracle.alibi_slopes(n), hf, rtol=1e-6, atol=0)
+
+
+def test_alibi_112_heads_rank0_share_values():
+    # heads 0..13 of the 112-head model are the 64-head sequence 2^-(h+1)/8
+    s = oracle.alibi_slopes(112)[:14]
+    assert s[7] == 0.5 and s[15 - 8] == 0.5
+    np.testing.assert_allclose(s, [0.917004, 0.840896, 0.771105, 0.707107, 0.648420, 0.594604,
+                                   0.545254, 0.5, 0.458502, 0.420448, 0.385553, 0.353553,
+                                   0.324210, 0.297302], atol=5e-7)
+
+
+# ---------------------------------------------------------------------------
+# LayerNorm, GeLU
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("scale", [1e-4, 1e-2, 1.0, 30.0])
+def test_layer_norm_matches_torch(scale):
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((5, 7, 96)) * scale + rng.standard_normal((5, 7, 1))
+    g = 1 + 0.1 * rng.standard_normal(96)
+    b = 0.1 * rng.standard_normal(96)
+    ref = torch.nn.functional.layer_norm(torch.from_numpy(x), (96,), torch.from_numpy(g),
+                                         torch.from_numpy(b), eps=1e-5).numpy()
+    np.testing.assert_allclose(oracle.layer_norm(x, g, b, 1e-5), ref, rtol=1e-11, atol=1e-12)
+
+
+def test_layer_norm_closed_form_moments():
+    rng = np.random.default_rng(2)
+    for sigma in (1e-3, 3e-3, 1.0):
+        x = rng.standard_normal((4, 4096)) * sigma + 5.0
+        y = oracle.layer_norm(x, 1.0, 0.0, 1e-5)
+        var = x.var(axis=-1)
+        np.testing.assert_allclose(y.mean(axis=-1), 0.0, atol=1e-12)
+        np.testing.assert_allclose(y.var(axis=-1), var / (var + 1e-5), rtol=1e-10)
+
+
+def test_gelu_matches_torch_tanh_form():
+    x = np.linspace(-12, 12, 20001)
+    ref = torch.nn.functional.gelu(torch.from_numpy(x), approximate="tanh").numpy()
+    np.testing.assert_allclose(oracle.gelu_tanh(x), ref, rtol=1e-14, atol=1e-15)
+
+
+def test_gelu_identities_and_erf_gap():
+    x = np.linspace(-8, 8, 16001)
+    g = oracle.gelu_tanh(x)
+    # odd part of x*Phi-like GeLU: gelu(x) - gelu(-x) == x exactly in real arithmetic
+    np.testing.assert_allclose(g - oracle.gelu_tanh(-x), x, atol=1e-14)
+    assert oracle.gelu_tanh(np.array([0.0]))[0] == 0.0
+    exact = 0.5 * x * (1 + scipy.special.erf(x / math.sqrt(2)))
+    gap = np.abs(g - exact)
+    # the tanh form differs from the erf form by at most ~4.74e-4 (near |x| ~ 2.7) -- it
+    # must differ, or the oracle uses the wrong GeLU
+    assert 4.6e-4 < gap.max() < 4.8e-4
+
+
+# ---------------------------------------------------------------------------
+# softmax
+# ---------------------------------------------------------------------------
+
+def _brute_alibi_softmax(scores, valid_len, n_total, off):
+    """Row-by-row loop with absolute key positions (slope * j), via scipy softmax."""
+    B, H, Q, K = scores.shape
+    slopes = oracle.alibi_slopes(n_total)[off: off + H]
+    out = np.zeros_like(scores, dtype=np.float64)
+    for b in range(B):
+        first = K - valid_len[b]
+        for h in range(H):
+            for i in range(Q):
+                last = K - Q + i
+                if last < first:
+                    continue
+                keys = np.arange(first, last + 1)
+                row = scores[b, h, i, keys].astype(np.float64) + slopes[h] * keys
+                out[b, h, i, keys] = scipy.special.softmax(row)
+    return out
+
+
+@pytest.mark.parametrize("Q", [1, 3])
+def test_alibi_masked_softmax_matches_brute_force(Q):
+    rng = np.random.default_rng(3)
+    B, H, K = 4, 14, 97
+    scores = rng.standard_normal((B, H, Q, K)) * 4
+    valid = np.array([97, 50, 1, 2])
+    p = oracle.alibi_masked_softmax(scores, valid, 112, 0)
+    np.testing.assert_allclose(p, _brute_alibi_softmax(scores, valid, 112, 0), rtol=1e-12,
+                               atol=1e-15)
+
+
+def test_alibi_masked_softmax_invariants():
+    rng = np.random.default_rng(4)
+    B, H, Q, K = 6, 5, 2, 64
+    scores = rng.standard_normal((B, H, Q, K)) * 4
+    valid = np.array([64, 63, 10, 2, 1, 33])
+    p = oracle.alibi_masked_softmax(scores, valid, 40, 7)
+    pad = K - valid
+    for b in range(B):
+        assert np.all(p[b, :, :, : pad[b]] == 0.0)          # masked: exactly 0
+    assert np.all(p[:, :, 0, K - 1] == 0.0)                   # causal: q0 cannot see key K-1
+    np.testing.assert_allclose(p.sum(-1)[valid >= 2], 1.0, rtol=0, atol=1e-14)
+    # valid length 1 (only key K-Q+... visible to the last query) gives a one-hot row
+    assert np.all(p[4, :, 1, K - 1] == 1.0)
+    assert np.all(p[4, :, 0] == 0.0)                           # no visible key: all zero
+    # shift invariance: adding a per-row constant changes nothing
+    shifted = scores + rng.standard_normal((B, H, Q, 1)) * 50
+    np.testing.assert_allclose(oracle.alibi_masked_softmax(shifted, valid, 40, 7), p,
+                               atol=1e-13)
+    # masked scores may hold anything, even +huge, without effect
+    evil = scores.copy()
+    for b in range(B):
+        evil[b, :, :, : pad[b]] = 3e38
+    np.testing.assert_array_equal(oracle.alibi_masked_softmax(evil, valid, 40, 7), p)
+
+
+def test_masked_softmax_reduces_to_textbook():
+    rng = np.random.default_rng(5)
+    s = rng.standard_normal((8, 33)) * 6
+    valid = np.ones_like(s, dtype=bool)
+    np.testing.assert_allclose(oracle.masked_softmax(s, valid), scipy.special.softmax(s, axis=-1),
+                               rtol=1e-13)
+    t = torch.softmax(torch.from_numpy(s), dim=-1).numpy()
+    np.testing.assert_allclose(oracle.masked_softmax(s, valid), t, rtol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# attention special cases
+# ---------------------------------------------------------------------------
+
+def test_attention_single_key_returns_value():
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((2, 1, 3, 8))
+    k = rng.standard_normal((2, 3, 1, 8))
+    v = rng.standard_normal((2, 3, 1, 8))
+    o = oracle.attention(q, k, v, oracle.alibi_slopes(3), np.array([0, 0]), 0)
+    np.testing.assert_array_equal(o[:, 0], v[:, :, 0])
+
+
+def test_attention_identical_keys_zero_slope_is_mean():
+    rng = np.random.default_rng(7)
+    T = 9
+    q = rng.standard_normal((1, 1, 2, 16))
+    k = np.repeat(rng.standard_normal((1, 2, 1, 16)), T, axis=2)
+    v = rng.standard_normal((1, 2, T, 16))
+    o = oracle.attention(q, k, v, np.zeros(2), np.array([2]), T - 1)
+    np.testing.assert_allclose(o[0, 0], v[0, :, 2:].mean(axis=1), rtol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# whole model against Hugging Face BLOOM (float64)
+# ---------------------------------------------------------------------------
+
+def _tiny(weight_dtype="f32", **kw):
+    import dataclasses
+    return dataclasses.replace(bi.TINY, weight_dtype=weight_dtype, **kw)
+
+
+@pytest.mark.parametrize("weight_dtype", ["f32", "bf16", "int8"])
+def test_model_hidden_matches_hf_bloom(weight_dtype, hf_available):
+    import hf_pin
+
+    m = _tiny(weight_dtype)
+    T = bi.model_tensors(m)
+    om = oracle.OracleModel.from_storage(m, T)
+    hf = hf_pin.hf_bloom(m, T)
+    ids, valid = bi.prompts(m, 3, 8, (8, 5, 1))
+    pad = 8 - valid
+    h = oracle.forward(om, ids, 0, pad, oracle.new_cache(om, 3))
+    logits = bo.lm_logits(om, h)
+    for b in range(3):
+        # a left-padded row means exactly its real tokens run alone
+        alone = ids[b: b + 1, pad[b]:]
+        ref = hf_pin.hf_hidden(hf, alone, [valid[b]])[0]
+        got = h[b, pad[b]:]
+        assert np.linalg.norm(got - ref) <= 1e-7 * np.linalg.norm(ref)
+        with torch.no_grad():
+            ref_logits = hf.lm_head(torch.from_numpy(ref)).numpy()
+        np.testing.assert_allclose(logits[b, pad[b]:], ref_logits, rtol=0,
+                                   atol=1e-7 * np.abs(ref_logits).max())
+
+
+def test_greedy_generation_matches_hf_bloom(hf_available):
+    import hf_pin
+
+    m = bi.TINY
+    T = bi.model_tensors(m)
+    om = oracle.OracleModel.from_storage(m, T)
+    hf = hf_pin.hf_bloom(m, T)
+    ids, valid = bi.prompts(m, 2, 8, (8, 5))
+    g = oracle.greedy_generate(om, ids, valid, 20)
+    for b in range(2):
+        ref = hf_pin.hf_generate(hf, ids[b: b + 1, 8 - valid[b]:], [valid[b]], 20)[0]
+        np.testing.assert_array_equal(g.tokens[b], ref)
+
+
+def test_greedy_generation_matches_hf_bloom_varied_prompts(hf_available):
+    """Prompts whose greedy continuations do not collapse to one repeated token."""
+    import hf_pin
+
+    m = _tiny(ln_eps=1e-5)
+    T = bi.model_tensors(m, seed=11)
+    om = oracle.OracleModel.from_storage(m, T)
+    hf = hf_pin.hf_bloom(m, T)
+    ids, valid = bi.prompts(m, 3, 8, (8, 6, 3), seed=12)
+    g = oracle.greedy_generate(om, ids, valid, 12)
+    for b in range(3):
+        ref = hf_pin.hf_generate(hf, ids[b: b + 1, 8 - valid[b]:], [valid[b]], 12)[0]
+        np.testing.assert_array_equal(g.tokens[b], ref)
+
+
+# ---------------------------------------------------------------------------
+# invariants of the generation loop
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def tiny_model():
+    m = bi.TINY
+    return m, oracle.OracleModel.from_storage(m, bi.model_tensors(m))
+
+
+def test_incremental_decode_equals_full_rerun(tiny_model):
+    m, om = tiny_model
+    ids, valid = bi.prompts(m, 2, 8, (8, 5))
+    g = oracle.greedy_generate(om, ids, valid, 6)
+    for t in range(6):
+        seq = np.concatenate([ids, g.tokens[:, :t]], axis=1)
+        full = oracle.forward(om, seq, 0, 8 - valid, oracle.new_cache(om, 2))[:, -1]
+        np.testing.assert_allclose(g.hidden[t], full, rtol=1e-12, atol=1e-12)
+
+
+def test_pad_token_ids_do_not_matter(tiny_model):
+    m, om = tiny_model
+    ids, valid = bi.prompts(m, 2, 8, (8, 5))
+    other = ids.copy()
+    other[1, :3] = [7, 999, 123]
+    a = oracle.greedy_generate(om, ids, valid, 5)
+    b = oracle.greedy_generate(om, other, valid, 5)
+    np.testing.assert_array_equal(a.tokens, b.tokens)
+    np.testing.assert_array_equal(a.hidden, b.hidden)
+
+
+def test_left_padding_invariance(tiny_model):
+    m, om = tiny_model
+    ids, valid = bi.prompts(m, 2, 8, (8, 5))
+    padded = oracle.greedy_generate(om, ids, valid, 5)
+    alone = oracle.greedy_generate(om, ids[1:, 3:], [5], 5)
+    np.testing.assert_array_equal(padded.tokens[1], alone.tokens[0])
+    np.testing.assert_allclose(padded.hidden[:, 1], alone.hidden[:, 0], rtol=1e-12, atol=1e-12)
+
+
+def test_batch_permutation_equivariance(tiny_model):
+    m, om = tiny_model
+    ids, valid = bi.prompts(m, 4, 8, (8, 5, 2, 7), seed=21)
+    perm = np.array([2, 0, 3, 1])
+    a = oracle.greedy_generate(om, ids, valid, 4)
+    b = oracle.greedy_generate(om, ids[perm], valid[perm], 4)
+    np.testing.assert_array_equal(a.tokens[perm], b.tokens)
+    np.testing.assert_allclose(a.hidden[:, perm], b.hidden, rtol=1e-12, atol=1e-12)
+
+
+def test_float32_oracle_agrees_with_float64(tiny_model):
+    m, om = tiny_model
+    om32 = oracle.OracleModel.from_storage(m, bi.model_tensors(m), dtype=np.float32)
+    ids, valid = bi.prompts(m, 2, 8, (8, 5))
+    a = oracle.greedy_generate(om, ids, valid, 5)
+    b = oracle.greedy_generate(om32, ids, valid, 5)
+    rel = np.linalg.norm(a.hidden - b.hidden) / np.linalg.norm(a.hidden)
+    assert rel < 1e-5
+
+
+def test_teacher_forcing_records_forced_logits(tiny_model):
+    m, om = tiny_model
+    ids, valid = bi.prompts(m, 2, 8, (8, 5))
+    free = oracle.greedy_generate(om, ids, valid, 5)
+    forced = oracle.greedy_generate(om, ids, valid, 5, forced=free.tokens)
+    np.testing.assert_array_equal(free.tokens, forced.tokens)
+    np.testing.assert_array_equal(forced.chosen, forced.top1)
+
+
+# ---------------------------------------------------------------------------
+# int8 row-scale weights and tensor-parallel shares
+# ---------------------------------------------------------------------------
+
+def test_int8_rowscale_one_hot_columns():
+    rng = np.random.default_rng(8)
+    q = rng.integers(-127, 128, size=(24, 40)).astype(np.int8)
+    s = rng.uniform(1e-4, 4e-4, size=24)
+    b = rng.standard_normal(24)
+    w = oracle.Int8RowScale(q, s)
+    for k in (0, 17, 39):
+        e = np.zeros(40)
+        e[k] = 1.0
+        np.testing.assert_array_equal(oracle.linear(e, w, b), s * q[:, k] + b)
+
+
+def test_tensor_parallel_shares_sum_to_full_attention_block():
+    """Splitting heads across two shares (heads [0, 8) and [8, 16)) and summing the
+    two output-projection partials reproduces the full layer: pins head_offset slope
+    selection and the per-head row order of the fused QKV matrix."""
+    import dataclasses
+
+    full = dataclasses.replace(bi.TINY, n_layer=1, n_head_total=16, n_head_local=16, head_dim=4)
+    T = bi.model_tensors(full, seed=5)
+    lw = T["layers"][0]
+    for f in ("w_up", "b_up", "w_down", "b_down"):
+        lw[f] = np.zeros_like(lw[f])
+    ids, valid = bi.prompts(full, 2, 8, (8, 6))
+
+    def residual(shape, tensors):
+        om = oracle.OracleModel.from_storage(shape, tensors)
+        tr = []
+        oracle.forward(om, ids, 0, 8 - valid, oracle.new_cache(om, 2), trace=tr)
+        x0 = om.embed[ids].astype(np.float64)
+        x0 = oracle.layer_norm(x0, om.emb_ln[0], om.emb_ln[1], om.ln_eps)
+        return tr[0] - x0
+
+    whole = residual(full, T)
+    parts = []
+    for rank, (h0, h1) in enumerate(((0, 8), (8, 16))):
+        sh = dataclasses.replace(full, head_offset=h0, n_head_local=h1 - h0)
+        t2 = {k: v for k, v in T.items() if k != "layers"}
+        l2 = dict(lw)
+        d = full.head_dim
+        l2["w_qkv"] = lw["w_qkv"][h0 * 3 * d: h1 * 3 * d]
+        l2["b_qkv"] = lw["b_qkv"][h0 * 3 * d: h1 * 3 * d]
+        l2["w_dense"] = np.ascontiguousarray(lw["w_dense"][:, h0 * d: h1 * d])
+        if rank:
+            l2["b_dense"] = np.zeros_like(lw["b_dense"])  # row-parallel bias added once
+        t2["layers"] = [l2]
+        parts.append(residual(sh, t2))
+    np.testing.assert_allclose(parts[0] + parts[1], whole, rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# input generator (module of its own) sanity
+# ---------------------------------------------------------------------------
+
+def test_generator_is_a_pure_function_of_seed_tensor_index():
+    a = bi.normal(0, 77, (1 << 21,), 0.02, kind="bf16", threads=8)
+    b = bi.normal(0, 77, (1 << 21,), 0.02, kind="bf16", threads=1)
+    np.testing.assert_array_equal(a, b)
+    part = bi.normal(0, 77, (1000,), 0.02, kind="bf16")
+    np.testing.assert_array_equal(part, a[:1000])
+    assert not np.array_equal(bi.normal(1, 77, (1000,), 0.02), part)
+
+
+def test_generator_matches_its_published_definition():
+    """SplitMix64 finaliser constants (Steele, Lea, Flood 2014) and the Irwin-Hall step."""
+    M = (1 << 64) - 1
+
+    def smix(z):
+        z = (z + 0x9E3779B97F4A7C15) & M
+        z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & M
+        z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & M
+        return z ^ (z >> 31)
+
+    seed, tid = 3, 1029
+    key = smix((seed << 32) ^ tid)
+    for i in (0, 1, 12345):
+        assert bi.hash64(seed, tid, i) == smix((key + i) & M)
+    x = bi.normal(seed, tid, (4,), 0.02, kind="f32")
+    scale = np.float32(0.02 / math.sqrt((65536.0 ** 2 - 1) / 3))
+    for i in range(4):
+        r = smix((key + i) & M)
+        z = sum((r >> s) & 0xFFFF for s in (0, 16, 32, 48)) - 131070
+        assert x[i] == np.float32(z) * scale
+    w = bi.normal(seed, tid, (1 << 16,), 0.02, kind="f32")
+    assert abs(w.std() / 0.02 - 1) < 0.02 and abs(w.mean()) < 5e-4
