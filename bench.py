@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""ms/token of BLOOM greedy KV-cached generation on one MI355X.
+
+The metric is the pages' (ms/token = wall time / (batch x tokens); "Incredibly Fast
+BLOOM Inference with DeepSpeed and Accelerate", Benchmark Environment): greedy
+generation of 100 new tokens from a 16-token prompt with the KV cache on.  One
+"step" is one whole generation for the batch: bloom_prefill, then 99
+bloom_decode_step calls.  Default workload: one tensor-parallel rank's share of the
+BLOOM-176B layer stack (70 layers, hidden 14336, 14 of 112 heads, MLP share 7168,
+bf16) with the full 250880-token tied LM head, batch 1.  Weights are random
+(seeded), inputs synthetic; everything is resident in HBM before timing starts.
+
+Printed: one JSON line with the metric, the roofline of the dominant kernel (the
+weight-streaming GEMV, timed per launch with HIP events on the library's stream
+inside the timed steps) and the CPU oracle timed on a bounded sample.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor peak
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3, help="timed generations")
+    ap.add_argument("--warmup", type=int, default=1, help="untimed generations")
+    ap.add_argument("--workload", default="bloom-176b-tp8-rank0")
+    ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--new-tokens", type=int, default=None)
+    ap.add_argument("--layers", type=int, default=None, help="truncate the stack (development)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--no-kernel-timer", action="store_true",
+                    help="do not bracket GEMV launches with events")
+    return ap.parse_args()
+
+
+def upload_weights(m, seed=0):
+    """Generate each tensor on the host and copy it to HBM right away."""
+    import bloom_inputs as bi
+    import transformer_bloom_decode_amd as tb
+
+    g = {name: tb.to_device(bi.tensor(m, name, seed=seed)) for name in bi.global_field_names(m)}
+    layers = []
+    for l in range(m.n_layer):
+        layers.append({f: tb.to_device(bi.tensor(m, f, l, seed=seed))
+                       for f in bi.layer_field_names(m)})
+    return tb.DeviceWeights(g, layers)
+
+
+def step_bytes(m, B, P, n_new):
+    """Algorithmic HBM bytes of one decode step averaged over the generation: every
+    weight byte once (layers + tied LM head + LayerNorm/bias/scales) plus the KV cache
+    read (T keys and values per head) and the new key/value written."""
+    act = 4 if m.weight_dtype == "f32" else 2
+    weights = m.n_layer * m.layer_weight_bytes() + m.head_bytes()
+    if m.embed_ln:
+        weights += 2 * m.hidden * (4 if m.param_dtype == "f32" else 2)
+    T_avg = sum(P + t for t in range(1, n_new)) / max(1, n_new - 1)  # keys seen per step
+    kv_read = 2 * m.n_layer * B * m.n_head_local * T_avg * m.head_dim * act
+    kv_write = 2 * m.n_layer * B * m.n_head_local * m.head_dim * act
+    return weights + kv_read + kv_write, weights
+
+
+def cpu_baseline(m, B, P, n_new, budget_s):
+    """The CPU oracle, as it stands, on a bounded sample: a 2-layer full-width slice of
+    the same model, its prompt pass and as many single-token steps as fit the budget;
+    per-layer and LM-head times are scaled to the full stack and the full generation."""
+    import numpy as np
+
+    import bloom_inputs as bi
+    import oracle
+    from oracle import bloom_oracle as bo
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    Ls = min(2, m.n_layer)
+    ms = m.truncated(Ls)
+    tensors = bi.model_tensors(ms)
+    om = oracle.OracleModel.from_storage(ms, tensors)
+    prompt, valid = bi.prompts(ms, B, P)
+    pad = P - valid
+    cache = oracle.new_cache(om, B)
+    t0 = time.perf_counter()
+    h = oracle.forward(om, prompt, 0, pad, cache)[:, -1]
+    t_prompt_layers = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    logits = bo.lm_logits(om, h)
+    t_head = time.perf_counter() - t0
+    nxt = bo.greedy_argmax(logits)
+    steps, t_step_layers = 0, 0.0
+    start = time.perf_counter()
+    while steps < n_new - 1 and (time.perf_counter() - start) < budget_s * 0.5:
+        t0 = time.perf_counter()
+        h = oracle.forward(om, nxt[:, None], P + steps, pad, cache)[:, 0]
+        t_step_layers += time.perf_counter() - t0
+        t0 = time.perf_counter()
+        nxt = bo.greedy_argmax(bo.lm_logits(om, h))
+        t_head += time.perf_counter() - t0
+        steps += 1
+    per_layer_prompt = t_prompt_layers / Ls
+    per_layer_step = t_step_layers / max(1, steps) / Ls
+    per_head = t_head / (steps + 1)
+    total_s = m.n_layer * (per_layer_prompt + (n_new - 1) * per_layer_step) + n_new * per_head
+    return {
+        "value": round(total_s * 1e3 / (B * n_new), 3),
+        "unit": "ms/token",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": (f"float64 numpy oracle on {Ls} of {m.n_layer} layers at full width, batch {B}: "
+                   f"{P}-token prompt pass + {steps} single-token steps, each with the full "
+                   f"{m.vocab}-row LM head; per-layer time x {m.n_layer} and LM-head time x "
+                   f"{n_new} scaled to the {n_new}-token generation"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported (this build "
+              "has no multi-GPU path; tensor-parallel sharding is described, not built).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import bloom_inputs as bi
+    import transformer_bloom_decode_amd as tb
+
+    wl = bi.WORKLOADS[args.workload]
+    m = wl.model if args.layers is None else wl.model.truncated(args.layers)
+    B = args.batch
+    P = wl.prompt_len
+    n_new = args.new_tokens or wl.new_tokens
+    torch.cuda.set_device(0)
+
+    t0 = time.perf_counter()
+    dw = upload_weights(m)
+    cfg = tb.make_config(m)
+    prompt, valid = bi.prompts(m, B, P)
+    tok = torch.from_numpy(prompt).cuda()
+    vl = torch.from_numpy(valid).cuda()
+    kv = tb.KVCache(cfg, B, P + n_new)
+    ws = tb.workspace(cfg, B, P)
+    ids = torch.empty((n_new, B), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    log(f"setup {time.perf_counter() - t0:.1f}s: {m.name} L={m.n_layer} B={B} P={P} new={n_new}")
+
+    def generation(ev_mid=None):
+        kv.struct.len = 0
+        kv.struct.prompt_len = 0
+        if not args.no_kernel_timer:
+            tb.bloom_timer_pause(True)
+        tb.bloom_prefill(cfg, dw, kv, B, P, tok, vl, ids[0], None, ws, stream)
+        if ev_mid is not None:
+            ev_mid.record(stream)
+        if not args.no_kernel_timer:
+            tb.bloom_timer_pause(False)
+        for t in range(1, n_new):
+            tb.bloom_decode_step(cfg, dw, kv, B, ids[t - 1], vl, ids[t], None, ws, stream)
+
+    for _ in range(args.warmup):
+        generation()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    launches_per_gen = (n_new - 1) * (4 * m.n_layer + 1 + (B - 1) // 128)
+    if not args.no_kernel_timer:
+        tb.bloom_timer_enable(K * launches_per_gen)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for k in range(K):
+        ev[k][0].record(stream)
+        generation(ev[k][1])
+        ev[k][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    gen_ms = [a.elapsed_time(c) for a, _, c in ev]
+    prefill_ms = [a.elapsed_time(b) for a, b, _ in ev]
+    decode_ms = [b.elapsed_time(c) / (n_new - 1) for _, b, c in ev]
+
+    ms_per_step = wall * 1e3 / K
+    ms_per_token = ms_per_step / (B * n_new)
+    sb, wbytes = step_bytes(m, B, P, n_new)
+    dec_step_ms = float(np.median(decode_ms))
+    roofline = None
+    if not args.no_kernel_timer:
+        k_ms, k_n, k_bytes = tb.bloom_timer_read()
+        tb.bloom_timer_disable()
+        if k_n:
+            achieved = k_bytes / (k_ms * 1e-3) / 1e9
+            roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                        "traffic": None, "kernel": "k_gemv_mfma (decode linears + LM head)",
+                        "launches": k_n, "avg_launch_us": round(k_ms * 1e3 / k_n, 2),
+                        "bytes_per_launch": round(k_bytes / k_n)}
+    ids_host = ids.cpu().numpy()
+
+    out = {
+        "metric": "ms/token (wall/(batch*tokens)), BLOOM-176B-shape greedy decode",
+        "value": round(ms_per_token, 4),
+        "unit": "ms/token",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if m.weight_dtype == "bf16" else ("int8-w/bf16" if m.weight_dtype == "int8" else "f32"),
+        "data": "synthetic (seeded random weights and prompt ids)",
+        "config": {"workload": m.name, "batch": B, "prompt_len": P, "new_tokens": n_new,
+                   "layers": m.n_layer, "hidden": m.hidden, "heads_local": m.n_head_local,
+                   "heads_total": m.n_head_total, "ffn_local": m.ffn, "vocab": m.vocab,
+                   "weights": m.weight_dtype, "kv_cache": True, "greedy": True,
+                   "parallelism": "none (1 GPU)"},
+        "tokens_per_s": round(B * n_new / (ms_per_step * 1e-3), 2),
+        "prefill_ms": round(float(np.median(prefill_ms)), 3),
+        "decode_step_ms": round(dec_step_ms, 4),
+        "decode_step_gb": round(sb / 1e9, 3),
+        "decode_step_hbm_frac": round(sb / (dec_step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "event_ms_per_step": round(float(np.median(gen_ms)), 3),
+        "roofline": roofline,
+        "checksum_ids": int(ids_host.astype(np.int64).sum()),
+    }
+    if not args.no_cpu_baseline:
+        del dw, kv, ws
+        torch.cuda.empty_cache()
+        t0 = time.perf_counter()
+        out["cpu_baseline"] = cpu_baseline(m, B, P, n_new, args.cpu_budget_s)
+        log(f"cpu baseline {time.perf_counter() - t0:.1f}s")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,203 @@
+/*
+ * bloom.h -- C ABI of the MI355X (gfx950) BLOOM greedy-decode library.
+ *
+ * The library runs the hot path of BLOOM text generation with a KV cache: the
+ * pre-LayerNorm decoder layer (input LayerNorm, fused QKV projection, ALiBi
+ * attention over the cached keys with masked fill and an fp32 softmax, output
+ * projection with bias and residual, post-attention LayerNorm, tanh-GeLU MLP),
+ * the final LayerNorm and the tied LM head with a greedy argmax.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [P1] "Incredibly Fast BLOOM Inference with DeepSpeed and Accelerate",
+ *        Benchmark Environment: greedy generation (do_sample=False) of 100 tokens with
+ *        the KV cache on; ms/token = wall time / (batch x tokens).
+ *   [P3] "DeepSpeed Inference: Enabling Efficient Inference of Transformer Models at
+ *        Unprecedented Scale", Section III.D (Putting It Together): the fused groups
+ *        input-LayerNorm + QKV GeMM, attention, post-attention LayerNorm + intermediate
+ *        GeMM, bias + residual; Section III.A: small batches are bound by weight reads.
+ *   [P4] "Hugging Face BLOOM Inference Optimization": Kernel Fusion with
+ *        torch.jit.script (fused tanh GeLU), Efficient PyTorch Implementation (ALiBi
+ *        computed once; KV "past" laid out to avoid reshapes), Custom CUDA Kernels and
+ *        Hardware Acceleration (masked_fill then a float32 softmax).
+ *
+ * Conventions
+ *   - Every pointer named d_* (and every pointer inside the structs below) is device
+ *     memory allocated and owned by the caller.  The library allocates nothing on
+ *     the call path; scratch space comes from the caller's workspace.
+ *   - Calls are asynchronous on the given HIP stream (a hipStream_t passed as void*;
+ *     NULL = the null stream).  The return value reports only synchronous checks and
+ *     launch errors; device faults surface at the caller's next synchronisation.
+ *   - Errors: BLOOM_EINVAL (bad shape, null pointer, bad index), BLOOM_EDTYPE (dtype
+ *     or dtype combination not built), BLOOM_ECAPACITY (KV cache too short or too
+ *     narrow), BLOOM_EWORKSPACE (workspace too small), BLOOM_EHIP (a HIP call
+ *     failed).  On any error nothing is launched and no host-side state changes.
+ *   - A batch of 0 rows is a valid no-op.
+ *   - Concurrent calls must use distinct KV caches and workspaces.
+ *
+ * Data types
+ *   - weight_dtype BLOOM_F32: all tensors float32 (a generic, unoptimised path).
+ *   - weight_dtype BLOOM_BF16: linear weights, embedding, biases, LayerNorm
+ *     parameters, activations and the KV cache are bf16; the residual stream,
+ *     LayerNorm statistics, GEMM accumulation, softmax and logits are float32.
+ *   - weight_dtype BLOOM_INT8_ROWSCALE: as BF16, except the four per-layer linear
+ *     weights are int8 [out][in] with one fp16 scale per output row in s_*:
+ *     W[r][k] = s[r] * q[r][k] (weight-only; activations stay bf16).
+ *
+ * Layouts (all row-major, C order)
+ *   embed            [vocab][hidden]             also the LM head (tied embeddings)
+ *   w_qkv            [3*n_head_local*head_dim][hidden], rows ordered [head][q,k,v][dim]
+ *   w_dense          [hidden][n_head_local*head_dim]
+ *   w_up             [ffn][hidden]
+ *   w_down           [hidden][ffn]
+ *   biases, scales   [out]
+ *   LayerNorm g, b   [hidden]
+ *   KV cache k, v    [n_layer][max_batch][n_head_local][max_len][head_dim]
+ */
+#ifndef BLOOM_MI355X_H
+#define BLOOM_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum bloom_status {
+  BLOOM_OK = 0,
+  BLOOM_EINVAL = -1,
+  BLOOM_EDTYPE = -2,
+  BLOOM_ECAPACITY = -3,
+  BLOOM_EWORKSPACE = -4,
+  BLOOM_EHIP = -5
+};
+
+enum bloom_dtype { BLOOM_F32 = 0, BLOOM_BF16 = 1, BLOOM_INT8_ROWSCALE = 2, BLOOM_F16 = 3 };
+
+/* Shape of one BLOOM stack held on this GPU: a whole model, or one tensor-parallel
+ * share of it (n_head_local heads starting at global head head_offset, ffn columns of
+ * the MLP).  n_head_total fixes the ALiBi slopes.  Requirements (else BLOOM_EINVAL):
+ * all sizes > 0; head_offset + n_head_local <= n_head_total; head_dim a power of two
+ * in [8, 256]; ln_eps >= 0; for BF16 / INT8_ROWSCALE, hidden, ffn and
+ * n_head_local*head_dim multiples of 64.  Device pointers must be 16-byte aligned. */
+typedef struct bloom_config {
+  int32_t n_layer;
+  int32_t hidden;
+  int32_t n_head_total;
+  int32_t head_offset;
+  int32_t n_head_local;
+  int32_t head_dim;
+  int32_t ffn;
+  int32_t vocab;
+  int32_t weight_dtype; /* enum bloom_dtype */
+  int32_t embed_ln;     /* 1: LayerNorm right after the embedding gather */
+  float ln_eps;         /* LayerNorm epsilon (biased variance) */
+} bloom_config;
+
+/* Device pointers of one decoder layer.  s_* are the int8 row scales (fp16) and must be
+ * NULL for F32 / BF16 weights. */
+typedef struct bloom_layer_weights {
+  const void *ln1_g, *ln1_b;
+  const void *w_qkv, *b_qkv, *s_qkv;
+  const void *w_dense, *b_dense, *s_dense;
+  const void *ln2_g, *ln2_b;
+  const void *w_up, *b_up, *s_up;
+  const void *w_down, *b_down, *s_down;
+} bloom_layer_weights;
+
+/* emb_ln_* may be NULL when embed_ln == 0.  `layers` is a HOST array of n_layer
+ * entries (each holding device pointers); it is read during the call only. */
+typedef struct bloom_weights {
+  const void *embed;
+  const void *emb_ln_g, *emb_ln_b;
+  const void *lnf_g, *lnf_b;
+  const bloom_layer_weights *layers;
+} bloom_weights;
+
+/* KV cache.  k and v are caller-owned device buffers of
+ * n_layer * max_batch * n_head_local * max_len * head_dim elements of the activation
+ * type (float32 for F32 models, bf16 otherwise).  len and prompt_len are host-side:
+ * bloom_prefill sets prompt_len and len = prompt_len; bloom_decode_step writes slot
+ * len and then increments it.  Slot j holds absolute position j of every row (left
+ * padding slots are written but never attended).  A caller may reset len to 0.
+ * max_len is at most 8192 (one attention row of scores is held in LDS). */
+typedef struct bloom_kv_cache {
+  void *k, *v;
+  int32_t max_batch, max_len;
+  int32_t len;
+  int32_t prompt_len;
+} bloom_kv_cache;
+
+/* Human-readable text for a status code. */
+const char *bloom_status_string(int status);
+
+/* Bytes of device workspace bloom_prefill / bloom_decode_step need for batches of up
+ * to max_batch rows and prompts of up to max_prompt tokens.  Writes *bytes. */
+int bloom_workspace_bytes(const bloom_config *cfg, int32_t max_batch, int32_t max_prompt,
+                          size_t *bytes);
+
+/* Prompt pass ([P1] Benchmark Environment: generation starts from a short prompt).
+ * d_tokens [batch][prompt_len] int32, LEFT-padded: row b has d_valid_len[b] real
+ * tokens (1 <= valid_len <= prompt_len) at its right end; pad ids are ignored.
+ * Runs every prompt position through the stack, writes KV slots [0, prompt_len),
+ * sets kv->prompt_len = kv->len = prompt_len, and writes the greedy next token of
+ * each row to d_next_tokens [batch] (lowest id among equal float32 logits).
+ * d_hidden_out (nullable) [batch][hidden] float32 receives the final-LayerNorm state
+ * of each row's last position.  ECAPACITY if batch > kv->max_batch or
+ * prompt_len > kv->max_len. */
+int bloom_prefill(const bloom_config *cfg, const bloom_weights *w, bloom_kv_cache *kv,
+                  int32_t batch, int32_t prompt_len, const int32_t *d_tokens,
+                  const int32_t *d_valid_len, int32_t *d_next_tokens, float *d_hidden_out,
+                  void *d_ws, size_t ws_bytes, void *stream);
+
+/* One generation step ([P1] Benchmark Environment; [P3] III.D fused groups).
+ * d_tokens [batch] int32 are the tokens at position kv->len; d_valid_len [batch] are
+ * the same valid prompt lengths given to bloom_prefill (left-pad masking).  Writes
+ * KV slot kv->len of every layer, attends over slots [prompt_len - valid_len[b],
+ * kv->len], writes the greedy next token to d_next_tokens and optionally the
+ * final-LayerNorm state to d_hidden_out [batch][hidden], then increments kv->len.
+ * ECAPACITY if kv->len >= kv->max_len or batch > kv->max_batch; EINVAL if
+ * bloom_prefill has not run (kv->prompt_len <= 0). */
+int bloom_decode_step(const bloom_config *cfg, const bloom_weights *w, bloom_kv_cache *kv,
+                      int32_t batch, const int32_t *d_tokens, const int32_t *d_valid_len,
+                      int32_t *d_next_tokens, float *d_hidden_out, void *d_ws,
+                      size_t ws_bytes, void *stream);
+
+/* Standalone fused ALiBi bias + masked fill + float32 softmax ([P4] Custom CUDA Kernels
+ * and Hardware Acceleration; Efficient PyTorch Implementation for ALiBi).
+ * d_scores [B][H][Q][K] (in_dtype BLOOM_BF16 or BLOOM_F32) are attention scores
+ * already scaled by 1/sqrt(head_dim).  Row b keeps keys j >= K - d_valid_len[b] (left
+ * padding; 0 <= valid_len <= K); query i sits at key position K - Q + i and keeps keys
+ * j <= K - Q + i.  Head h uses the ALiBi slope of global head head_offset + h of an
+ * n_head_total-head model.  p = softmax over kept keys of score + slope * (j - (K-Q+i));
+ * dropped keys get exactly 0, and a row with no kept key is all 0.  All arithmetic is
+ * float32; d_probs [B][H][Q][K] is written in out_dtype (BLOOM_F32 or BLOOM_BF16). */
+int alibi_masked_softmax(const void *d_scores, int32_t in_dtype, const int32_t *d_valid_len,
+                         int32_t B, int32_t H, int32_t Q, int32_t K, int32_t n_head_total,
+                         int32_t head_offset, void *d_probs, int32_t out_dtype, void *stream);
+
+/* Copy n_new new key/value vectors into the cache ([P4] Efficient PyTorch
+ * Implementation: the KV "past" kept in a layout that needs no reshape or transpose).
+ * d_k, d_v [batch][n_head_local][n_new][head_dim] (activation type) go to slots
+ * [pos, pos + n_new) of layer `layer`, rows 0..batch-1.  Does not change kv->len.
+ * ECAPACITY if pos + n_new > kv->max_len or batch > kv->max_batch. */
+int kv_cache_append(const bloom_config *cfg, bloom_kv_cache *kv, int32_t layer, int32_t batch,
+                    int32_t pos, const void *d_k, const void *d_v, int32_t n_new, void *stream);
+
+/* Launch timer for measurement: while enabled, the library brackets every launch of
+ * its layer-linear (weight-streaming GEMV / GEMM) kernels with a pair of hipEvents on
+ * the call's stream, for up to max_launches launches.  bloom_timer_read synchronises
+ * on the last event and returns the summed launch time (ms), the number of timed
+ * launches and the summed weight bytes those launches streamed; it then resets the
+ * timer.  Events are created by bloom_timer_enable (not on the call path). */
+int bloom_timer_enable(int32_t max_launches);
+int bloom_timer_disable(void);
+int bloom_timer_read(double *total_ms, int32_t *n_launches, double *weight_bytes);
+/* While an enabled timer is paused (paused != 0) launches are not recorded. */
+int bloom_timer_pause(int32_t paused);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BLOOM_MI355X_H */

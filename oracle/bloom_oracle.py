@@ -203,7 +203,11 @@ class OracleModel:
     @classmethod
     def from_storage(cls, shape, tensors: dict, dtype=F64, widen_weights: bool = True):
         """Build from a shape (attributes as in the workload description) and tensors in
-        storage form: bf16 as uint16 bits, fp16 scales as uint16 bits, int8, float32."""
+        storage form: bf16 as uint16 bits, fp16 scales as uint16 bits, int8, float32.
+
+        widen_weights=True converts every layer matrix to ``dtype`` once (int8 ones are
+        dequantised, W = s q); False keeps the stored form and widens at each use.
+        Either way the arithmetic is the same."""
         wd = shape.weight_dtype
         pd = "f32" if wd == "f32" else "bf16"
 
@@ -212,7 +216,8 @@ class OracleModel:
 
         def mat(lw, field):
             if wd == "int8":
-                return Int8RowScale(lw["w_" + field], _widen(lw["s_" + field], "f16"))
+                w8 = Int8RowScale(lw["w_" + field], _widen(lw["s_" + field], "f16"))
+                return w8.dense(dtype) if widen_weights else w8
             w = _widen(lw["w_" + field], wd)
             return w.astype(dtype) if widen_weights else w
 

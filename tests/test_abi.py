@@ -1,0 +1,175 @@
+"""The C-ABI library loads, exports every function include/bloom.h declares, and its
+synchronous validation returns the documented status codes.  Nothing here launches
+a kernel: every call fails (or is a no-op) before touching the device, so these run
+without a GPU."""
+import ctypes
+import dataclasses
+import re
+
+import pytest
+
+import bloom_inputs as bi
+import transformer_bloom_decode_amd as tb
+
+
+def _declared_functions():
+    text = open(tb.HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names) - {"if", "return"})
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for required in ("bloom_prefill", "bloom_decode_step", "alibi_masked_softmax",
+                     "kv_cache_append", "bloom_workspace_bytes", "bloom_status_string"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    so = ctypes.CDLL(tb.LIB_PATH)
+    missing = [n for n in _declared_functions() if not hasattr(so, n)]
+    assert not missing, missing
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, -5):
+        assert tb.bloom_status_string(code)
+    assert tb.bloom_status_string(-99) == "unknown status"
+
+
+def test_struct_layout_matches_header():
+    # 10 int32 + 1 float; 16 pointers; 5 pointers + 1 pointer; 2 pointers + 4 int32
+    assert ctypes.sizeof(tb.bloom_config) == 44
+    assert ctypes.sizeof(tb.bloom_layer_weights) == 16 * 8
+    assert ctypes.sizeof(tb.bloom_weights) == 6 * 8
+    assert ctypes.sizeof(tb.bloom_kv_cache) == 2 * 8 + 4 * 4
+
+
+def _cfg(**kw):
+    return tb.make_config(dataclasses.replace(bi.BLOOM_560M, **kw))
+
+
+def _err(fn, *a):
+    with pytest.raises(tb.BloomError) as ei:
+        fn(*a)
+    return ei.value.code
+
+
+@pytest.mark.parametrize("change, code", [
+    (dict(head_dim=96), tb.BLOOM_EINVAL),           # not a power of two
+    (dict(head_dim=512), tb.BLOOM_EINVAL),
+    (dict(hidden=1000), tb.BLOOM_EINVAL),           # bf16 needs multiples of 64
+    (dict(n_layer=0), tb.BLOOM_EINVAL),
+    (dict(head_offset=10), tb.BLOOM_EINVAL),        # 10 + 16 heads > 16
+    (dict(ln_eps=float("nan")), tb.BLOOM_EINVAL),
+])
+def test_workspace_rejects_bad_config(change, code):
+    assert _err(tb.bloom_workspace_bytes, _cfg(**change), 1, 16) == code
+
+
+def test_workspace_rejects_bad_dtype():
+    c = _cfg()
+    c.weight_dtype = 7
+    assert _err(tb.bloom_workspace_bytes, c, 1, 16) == tb.BLOOM_EDTYPE
+
+
+def test_workspace_grows_with_batch_and_prompt():
+    c = _cfg()
+    a = tb.bloom_workspace_bytes(c, 1, 1)
+    b = tb.bloom_workspace_bytes(c, 8, 16)
+    assert 0 < a < b
+    assert tb.bloom_workspace_bytes(_cfg(weight_dtype="f32"), 0, 0) >= 0
+
+
+class _Fake:
+    """Non-null dummy device pointers: validation must fail before any use."""
+
+    def __init__(self, shape):
+        self.cfg = tb.make_config(shape)
+        self.layers = (tb.bloom_layer_weights * shape.n_layer)()
+        for lw in self.layers:
+            for f in tb.LAYER_FIELDS:
+                if not f.startswith("s_") or shape.weight_dtype == "int8":
+                    setattr(lw, f, 0x1000)
+        self.w = tb.bloom_weights(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, self.layers)
+        self.kv = tb.bloom_kv_cache(0x1000, 0x1000, 4, 32, 0, 0)
+
+
+def _prefill(f, batch=2, prompt=8, ws_bytes=1 << 40, tokens=0x1000):
+    return tb.lib.bloom_prefill(ctypes.byref(f.cfg), ctypes.byref(f.w), ctypes.byref(f.kv), batch,
+                                prompt, tokens, 0x1000, 0x1000, None, 0x1000, ws_bytes, None)
+
+
+def _decode(f, batch=2, ws_bytes=1 << 40):
+    return tb.lib.bloom_decode_step(ctypes.byref(f.cfg), ctypes.byref(f.w), ctypes.byref(f.kv),
+                                    batch, 0x1000, 0x1000, 0x1000, None, 0x1000, ws_bytes, None)
+
+
+def test_prefill_validation_paths():
+    f = _Fake(bi.BLOOM_560M)
+    assert _prefill(f, batch=5) == tb.BLOOM_ECAPACITY           # > max_batch
+    assert _prefill(f, prompt=33) == tb.BLOOM_ECAPACITY         # > max_len
+    assert _prefill(f, prompt=0) == tb.BLOOM_EINVAL
+    assert _prefill(f, batch=-1) == tb.BLOOM_EINVAL
+    assert _prefill(f, ws_bytes=1024) == tb.BLOOM_EWORKSPACE
+    assert _prefill(f, tokens=None) == tb.BLOOM_EINVAL
+    assert _prefill(f, batch=0) == tb.BLOOM_OK                   # empty batch: no-op
+    assert f.kv.len == 0 and f.kv.prompt_len == 0                # state untouched
+    f.layers[3].w_up = None
+    assert _prefill(f) == tb.BLOOM_EINVAL
+    f.layers[3].w_up = 0x1000
+    f.layers[0].s_up = 0x1000                                    # scales on bf16 weights
+    assert _prefill(f) == tb.BLOOM_EINVAL
+
+
+def test_int8_requires_row_scales():
+    f = _Fake(bi.BLOOM_176B_INT8.truncated(2))
+    f.kv.max_len = 32
+    f.layers[1].s_down = None
+    assert _prefill(f) == tb.BLOOM_EINVAL
+
+
+def test_decode_validation_paths():
+    f = _Fake(bi.BLOOM_560M)
+    assert _decode(f) == tb.BLOOM_EINVAL                         # no prompt pass yet
+    f.kv.prompt_len = 8
+    f.kv.len = 32
+    assert _decode(f) == tb.BLOOM_ECAPACITY                      # cache full
+    f.kv.len = 20
+    assert _decode(f, batch=9) == tb.BLOOM_ECAPACITY
+    assert _decode(f, ws_bytes=10) == tb.BLOOM_EWORKSPACE
+    assert _decode(f, batch=0) == tb.BLOOM_OK
+    assert f.kv.len == 20
+    f.kv.len = 4                                                  # len < prompt_len
+    assert _decode(f) == tb.BLOOM_EINVAL
+    f.kv.max_len = 9000                                           # beyond the supported 8192
+    f.kv.len = 20
+    assert _decode(f) == tb.BLOOM_EINVAL
+
+
+def test_kv_append_validation_paths():
+    f = _Fake(bi.BLOOM_560M)
+    app = lambda layer, batch, pos, n: tb.lib.kv_cache_append(
+        ctypes.byref(f.cfg), ctypes.byref(f.kv), layer, batch, pos, 0x1000, 0x1000, n, None)
+    assert app(24, 1, 0, 1) == tb.BLOOM_EINVAL        # layer out of range
+    assert app(0, 5, 0, 1) == tb.BLOOM_ECAPACITY      # batch > max_batch
+    assert app(0, 1, 30, 3) == tb.BLOOM_ECAPACITY     # 30 + 3 > 32
+    assert app(0, 1, 0, 0) == tb.BLOOM_OK             # nothing to copy
+    assert app(0, 1, -1, 1) == tb.BLOOM_EINVAL
+
+
+def test_softmax_validation_paths():
+    sm = lambda *a: tb.lib.alibi_masked_softmax(*a)
+    assert sm(0x10, 1, 0x10, 1, 1, 3, 2, 8, 0, 0x10, 0, None) == tb.BLOOM_EINVAL   # Q > K
+    assert sm(0x10, 9, 0x10, 1, 1, 1, 2, 8, 0, 0x10, 0, None) == tb.BLOOM_EDTYPE
+    assert sm(0x10, 1, 0x10, 1, 1, 1, 2, 8, 0, 0x10, 5, None) == tb.BLOOM_EDTYPE
+    assert sm(0x10, 1, 0x10, 1, 4, 1, 2, 8, 6, 0x10, 0, None) == tb.BLOOM_EINVAL   # heads > total
+    assert sm(None, 1, None, 1, 1, 1, 2, 8, 0, None, 0, None) == tb.BLOOM_EINVAL
+    assert sm(None, 1, None, 0, 1, 1, 2, 8, 0, None, 0, None) == tb.BLOOM_OK       # empty
+
+
+def test_timer_read_without_launches():
+    tb.bloom_timer_disable()
+    ms, n, b = tb.bloom_timer_read()
+    assert (ms, n, b) == (0.0, 0, 0.0)

@@ -1,0 +1,288 @@
+"""Python binding of the MI355X (gfx950) BLOOM greedy-decode library.
+
+Argument marshalling only: torch tensors supply device memory and the HIP stream,
+and every step of the hot path runs in the HIP kernels of ``libbloom_mi355x.so``
+(declared in ``include/bloom.h``).  The functions below carry the C names
+(``bloom_prefill``, ``bloom_decode_step``, ``alibi_masked_softmax``,
+``kv_cache_append``, ...) and raise ``BloomError`` on a non-zero status.
+
+Importing this package loads the shared library and fails loudly if it has not been
+built (``python transformer_bloom_decode_amd/build.py``); there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libbloom_mi355x.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "bloom.h")
+
+BLOOM_OK, BLOOM_EINVAL, BLOOM_EDTYPE, BLOOM_ECAPACITY, BLOOM_EWORKSPACE, BLOOM_EHIP = (
+    0, -1, -2, -3, -4, -5)
+BLOOM_F32, BLOOM_BF16, BLOOM_INT8_ROWSCALE, BLOOM_F16 = 0, 1, 2, 3
+DTYPE_CODES = {"f32": BLOOM_F32, "bf16": BLOOM_BF16, "int8": BLOOM_INT8_ROWSCALE}
+
+_c_void_p = ctypes.c_void_p
+_i32 = ctypes.c_int32
+
+
+class bloom_config(ctypes.Structure):
+    _fields_ = [("n_layer", _i32), ("hidden", _i32), ("n_head_total", _i32),
+                ("head_offset", _i32), ("n_head_local", _i32), ("head_dim", _i32),
+                ("ffn", _i32), ("vocab", _i32), ("weight_dtype", _i32), ("embed_ln", _i32),
+                ("ln_eps", ctypes.c_float)]
+
+
+LAYER_FIELDS = ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "s_qkv", "w_dense", "b_dense", "s_dense",
+                "ln2_g", "ln2_b", "w_up", "b_up", "s_up", "w_down", "b_down", "s_down")
+
+
+class bloom_layer_weights(ctypes.Structure):
+    _fields_ = [(f, _c_void_p) for f in LAYER_FIELDS]
+
+
+class bloom_weights(ctypes.Structure):
+    _fields_ = [("embed", _c_void_p), ("emb_ln_g", _c_void_p), ("emb_ln_b", _c_void_p),
+                ("lnf_g", _c_void_p), ("lnf_b", _c_void_p),
+                ("layers", ctypes.POINTER(bloom_layer_weights))]
+
+
+class bloom_kv_cache(ctypes.Structure):
+    _fields_ = [("k", _c_void_p), ("v", _c_void_p), ("max_batch", _i32), ("max_len", _i32),
+                ("len", _i32), ("prompt_len", _i32)]
+
+
+class BloomError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {bloom_status_string(code)} ({code})")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run transformer_bloom_decode_amd/build.py "
+                          "(the HIP library is required: there is no CPU fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    vp = _c_void_p
+    lib.bloom_status_string.argtypes = [ctypes.c_int]
+    lib.bloom_status_string.restype = ctypes.c_char_p
+    lib.bloom_workspace_bytes.argtypes = [P(bloom_config), _i32, _i32, P(ctypes.c_size_t)]
+    lib.bloom_prefill.argtypes = [P(bloom_config), P(bloom_weights), P(bloom_kv_cache), _i32, _i32,
+                                  vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.bloom_decode_step.argtypes = [P(bloom_config), P(bloom_weights), P(bloom_kv_cache), _i32,
+                                      vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.alibi_masked_softmax.argtypes = [vp, _i32, vp, _i32, _i32, _i32, _i32, _i32, _i32, vp,
+                                         _i32, vp]
+    lib.kv_cache_append.argtypes = [P(bloom_config), P(bloom_kv_cache), _i32, _i32, _i32, vp, vp,
+                                    _i32, vp]
+    lib.bloom_timer_enable.argtypes = [_i32]
+    lib.bloom_timer_disable.argtypes = []
+    lib.bloom_timer_read.argtypes = [P(ctypes.c_double), P(_i32), P(ctypes.c_double)]
+    lib.bloom_timer_pause.argtypes = [_i32]
+    for name in ("bloom_workspace_bytes", "bloom_prefill", "bloom_decode_step",
+                 "alibi_masked_softmax", "kv_cache_append", "bloom_timer_enable",
+                 "bloom_timer_disable", "bloom_timer_read", "bloom_timer_pause"):
+        getattr(lib, name).restype = ctypes.c_int
+    return lib
+
+
+lib = _load()
+
+
+def _check(code: int, where: str):
+    if code != BLOOM_OK:
+        raise BloomError(code, where)
+
+
+def _ptr(t) -> Optional[int]:
+    """Device pointer of a torch tensor (or an int address, or None)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ---------------------------------------------------------------------------
+# C functions, same names
+# ---------------------------------------------------------------------------
+
+def bloom_status_string(code: int) -> str:
+    return lib.bloom_status_string(code).decode()
+
+
+def bloom_workspace_bytes(cfg: bloom_config, max_batch: int, max_prompt: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib.bloom_workspace_bytes(ctypes.byref(cfg), max_batch, max_prompt, ctypes.byref(out)),
+           "bloom_workspace_bytes")
+    return out.value
+
+
+def bloom_prefill(cfg, weights, kv, batch: int, prompt_len: int, tokens, valid_len, next_tokens,
+                  hidden_out, ws, stream=None):
+    w = weights.struct if hasattr(weights, "struct") else weights
+    k = kv.struct if hasattr(kv, "struct") else kv
+    _check(lib.bloom_prefill(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(k), batch,
+                             prompt_len, _ptr(tokens), _ptr(valid_len), _ptr(next_tokens),
+                             _ptr(hidden_out), _ptr(ws), _nbytes(ws), _stream(stream)),
+           "bloom_prefill")
+
+
+def bloom_decode_step(cfg, weights, kv, batch: int, tokens, valid_len, next_tokens, hidden_out,
+                      ws, stream=None):
+    w = weights.struct if hasattr(weights, "struct") else weights
+    k = kv.struct if hasattr(kv, "struct") else kv
+    _check(lib.bloom_decode_step(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(k), batch,
+                                 _ptr(tokens), _ptr(valid_len), _ptr(next_tokens),
+                                 _ptr(hidden_out), _ptr(ws), _nbytes(ws), _stream(stream)),
+           "bloom_decode_step")
+
+
+def alibi_masked_softmax(scores, in_dtype: int, valid_len, B: int, H: int, Q: int, K: int,
+                         n_head_total: int, head_offset: int, probs, out_dtype: int, stream=None):
+    _check(lib.alibi_masked_softmax(_ptr(scores), in_dtype, _ptr(valid_len), B, H, Q, K,
+                                    n_head_total, head_offset, _ptr(probs), out_dtype,
+                                    _stream(stream)), "alibi_masked_softmax")
+
+
+def kv_cache_append(cfg, kv, layer: int, batch: int, pos: int, k, v, n_new: int, stream=None):
+    s = kv.struct if hasattr(kv, "struct") else kv
+    _check(lib.kv_cache_append(ctypes.byref(cfg), ctypes.byref(s), layer, batch, pos, _ptr(k),
+                               _ptr(v), n_new, _stream(stream)), "kv_cache_append")
+
+
+def bloom_timer_enable(max_launches: int):
+    _check(lib.bloom_timer_enable(max_launches), "bloom_timer_enable")
+
+
+def bloom_timer_disable():
+    _check(lib.bloom_timer_disable(), "bloom_timer_disable")
+
+
+def bloom_timer_pause(paused: bool):
+    _check(lib.bloom_timer_pause(int(bool(paused))), "bloom_timer_pause")
+
+
+def bloom_timer_read():
+    ms, n, b = ctypes.c_double(0), _i32(0), ctypes.c_double(0)
+    _check(lib.bloom_timer_read(ctypes.byref(ms), ctypes.byref(n), ctypes.byref(b)),
+           "bloom_timer_read")
+    return ms.value, n.value, b.value
+
+
+def _nbytes(t) -> int:
+    if t is None:
+        return 0
+    return t.numel() * t.element_size()
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers: build the C structs from torch device tensors
+# ---------------------------------------------------------------------------
+
+def make_config(shape) -> bloom_config:
+    """bloom_config from any object with the shape attributes (n_layer, hidden, ...)."""
+    return bloom_config(shape.n_layer, shape.hidden, shape.n_head_total, shape.head_offset,
+                        shape.n_head_local, shape.head_dim, shape.ffn, shape.vocab,
+                        DTYPE_CODES[shape.weight_dtype], int(bool(shape.embed_ln)),
+                        float(shape.ln_eps))
+
+
+def to_device(a, device="cuda"):
+    """numpy array (float32, int8, or uint16 bit patterns) -> torch device tensor, same bytes."""
+    import numpy as np
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(device)
+
+
+class DeviceWeights:
+    """Device tensors of one model plus the bloom_weights struct pointing at them."""
+
+    def __init__(self, globals_: dict, layers: Sequence[dict]):
+        self.tensors = {"globals": globals_, "layers": list(layers)}
+        self._layer_arr = (bloom_layer_weights * len(layers))()
+        for i, lw in enumerate(layers):
+            for f in LAYER_FIELDS:
+                setattr(self._layer_arr[i], f, _ptr(lw.get(f)))
+        g = globals_
+        self.struct = bloom_weights(_ptr(g["embed"]), _ptr(g.get("emb_ln_g")),
+                                    _ptr(g.get("emb_ln_b")), _ptr(g["lnf_g"]), _ptr(g["lnf_b"]),
+                                    self._layer_arr)
+
+    @classmethod
+    def from_arrays(cls, tensors: dict, device="cuda"):
+        """From {'embed': ..., 'lnf_g': ..., 'layers': [{field: array}]} host arrays."""
+        g = {k: to_device(v, device) for k, v in tensors.items() if k != "layers"}
+        layers = [{k: to_device(v, device) for k, v in lw.items()} for lw in tensors["layers"]]
+        return cls(g, layers)
+
+
+class KVCache:
+    """Caller-owned KV cache buffers ([n_layer][max_batch][H][max_len][d]) and the struct."""
+
+    def __init__(self, cfg: bloom_config, max_batch: int, max_len: int, device="cuda",
+                 fill: Optional[float] = None):
+        import torch
+        dt = torch.float32 if cfg.weight_dtype == BLOOM_F32 else torch.bfloat16
+        shape = (cfg.n_layer, max_batch, cfg.n_head_local, max_len, cfg.head_dim)
+        if fill is None:
+            self.k = torch.empty(shape, dtype=dt, device=device)
+            self.v = torch.empty(shape, dtype=dt, device=device)
+        else:
+            self.k = torch.full(shape, fill, dtype=dt, device=device)
+            self.v = torch.full(shape, fill, dtype=dt, device=device)
+        self.struct = bloom_kv_cache(_ptr(self.k), _ptr(self.v), max_batch, max_len, 0, 0)
+
+    @property
+    def len(self) -> int:
+        return self.struct.len
+
+    @property
+    def prompt_len(self) -> int:
+        return self.struct.prompt_len
+
+
+def workspace(cfg: bloom_config, max_batch: int, max_prompt: int, device="cuda"):
+    import torch
+    return torch.empty(bloom_workspace_bytes(cfg, max_batch, max_prompt), dtype=torch.uint8,
+                       device=device)
+
+
+def greedy_generate(cfg: bloom_config, weights: DeviceWeights, kv: KVCache, tokens, valid_len,
+                    n_new: int, ws, want_hidden: bool = True, stream=None):
+    """Greedy generation loop ("Incredibly Fast BLOOM Inference with DeepSpeed and
+    Accelerate", Benchmark Environment): one bloom_prefill over the left-padded prompt
+    (which yields the first new token), then n_new - 1 bloom_decode_step calls.  Token
+    ids stay on the device between steps.
+
+    tokens [batch, prompt_len] int32 and valid_len [batch] int32 are device tensors.
+    Returns (ids [n_new, batch] int32, hidden [n_new, batch, hidden] float32 or None),
+    both on the device; nothing is synchronised.
+    """
+    import torch
+    batch, prompt_len = tokens.shape
+    dev = tokens.device
+    ids = torch.empty((n_new, batch), dtype=torch.int32, device=dev)
+    hid = (torch.empty((n_new, batch, cfg.hidden), dtype=torch.float32, device=dev)
+           if want_hidden else None)
+    bloom_prefill(cfg, weights, kv, batch, prompt_len, tokens, valid_len, ids[0],
+                  None if hid is None else hid[0], ws, stream)
+    for t in range(1, n_new):
+        bloom_decode_step(cfg, weights, kv, batch, ids[t - 1], valid_len, ids[t],
+                          None if hid is None else hid[t], ws, stream)
+    return ids, hid

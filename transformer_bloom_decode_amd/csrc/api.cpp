@@ -1,0 +1,416 @@
+// C ABI of the BLOOM decode library: argument validation, workspace carve-up and the
+// launch sequence of one forward pass (prompt pass or one generation step).
+//
+// Launch sequence for M = batch * tokens_per_row rows ("DeepSpeed Inference ...",
+// Section III.D fused groups; "Incredibly Fast BLOOM Inference ...", Benchmark
+// Environment for the greedy, KV-cached loop):
+//   embed (+ embedding LayerNorm)                                    -> x (fp32)
+//   per layer: LayerNorm1 -> QKV linear (+bias; q scaled to fp32, k/v into the cache)
+//              -> attention -> dense linear (+bias, += x) -> LayerNorm2
+//              -> up linear (+bias, tanh GeLU) -> down linear (+bias, += x)
+//   final LayerNorm of each row's last position -> LM head (tied embedding) with a
+//   per-tile argmax -> argmax merge -> next token ids.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <vector>
+
+#include "../../include/bloom.h"
+#include "common.hpp"
+#include "kernels.hpp"
+
+using namespace bl;
+
+namespace {
+
+constexpr int kMaxLen = 8192;  // KV slots the attention kernel's LDS score row can hold
+
+struct WsPlan {
+  size_t x, xa, q, o, u, af, amv, ami, part, total;
+  int lm_blocks;
+};
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+int act_bytes(const bloom_config *c) { return c->weight_dtype == BLOOM_F32 ? 4 : 2; }
+int wtype(const bloom_config *c) {
+  return c->weight_dtype == BLOOM_F32 ? WT_F32 : (c->weight_dtype == BLOOM_BF16 ? WT_BF16 : WT_INT8);
+}
+int lm_blocks(const bloom_config *c) {
+  return c->weight_dtype == BLOOM_F32 ? (c->vocab + 255) / 256 : (c->vocab + 15) / 16;
+}
+
+WsPlan plan_ws(const bloom_config *c, int batch, int tokens_per_row) {
+  WsPlan p{};
+  const size_t M = (size_t)batch * (size_t)std::max(tokens_per_row, 1);
+  const size_t act = act_bytes(c);
+  const size_t hd = (size_t)c->n_head_local * c->head_dim;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off += align256(bytes); return o; };
+  p.x = take(M * c->hidden * 4);
+  p.xa = take(M * c->hidden * act);
+  p.q = take(M * hd * 4);
+  p.o = take(M * hd * act);
+  p.u = take(M * (size_t)c->ffn * act);
+  p.af = take((size_t)batch * c->hidden * act);
+  p.lm_blocks = lm_blocks(c);
+  p.amv = take((size_t)batch * p.lm_blocks * 4);
+  p.ami = take((size_t)batch * p.lm_blocks * 4);
+  p.part = take(c->weight_dtype == BLOOM_F32 ? 0 : (size_t)kPartialCapFloats * 4);
+  p.total = off;
+  return p;
+}
+
+bool pow2_dim(int d) { return d >= 8 && d <= 256 && (d & (d - 1)) == 0; }
+
+int check_config(const bloom_config *c) {
+  if (!c) return BLOOM_EINVAL;
+  if (c->n_layer <= 0 || c->hidden <= 0 || c->n_head_total <= 0 || c->n_head_local <= 0 ||
+      c->head_dim <= 0 || c->ffn <= 0 || c->vocab <= 0 || c->head_offset < 0)
+    return BLOOM_EINVAL;
+  if (c->head_offset + c->n_head_local > c->n_head_total) return BLOOM_EINVAL;
+  if (!pow2_dim(c->head_dim)) return BLOOM_EINVAL;
+  if (!(c->ln_eps >= 0.f)) return BLOOM_EINVAL;
+  if (c->weight_dtype != BLOOM_F32 && c->weight_dtype != BLOOM_BF16 &&
+      c->weight_dtype != BLOOM_INT8_ROWSCALE)
+    return BLOOM_EDTYPE;
+  if (c->weight_dtype != BLOOM_F32) {
+    const int hd = c->n_head_local * c->head_dim;
+    if (c->hidden % 64 || c->ffn % 64 || hd % 64) return BLOOM_EINVAL;
+  }
+  return BLOOM_OK;
+}
+
+int check_weights(const bloom_config *c, const bloom_weights *w) {
+  if (!w || !w->embed || !w->lnf_g || !w->lnf_b || !w->layers) return BLOOM_EINVAL;
+  if (c->embed_ln && (!w->emb_ln_g || !w->emb_ln_b)) return BLOOM_EINVAL;
+  const bool i8 = c->weight_dtype == BLOOM_INT8_ROWSCALE;
+  for (int l = 0; l < c->n_layer; ++l) {
+    const bloom_layer_weights &L = w->layers[l];
+    const void *need[] = {L.ln1_g, L.ln1_b, L.w_qkv, L.b_qkv, L.w_dense, L.b_dense,
+                          L.ln2_g, L.ln2_b, L.w_up,  L.b_up,  L.w_down, L.b_down};
+    for (const void *p : need)
+      if (!p) return BLOOM_EINVAL;
+    const void *sc[] = {L.s_qkv, L.s_dense, L.s_up, L.s_down};
+    for (const void *p : sc)
+      if ((p != nullptr) != i8) return BLOOM_EINVAL;
+  }
+  return BLOOM_OK;
+}
+
+int check_kv(const bloom_config *c, const bloom_kv_cache *kv) {
+  (void)c;
+  if (!kv || !kv->k || !kv->v || kv->max_batch <= 0 || kv->max_len <= 0) return BLOOM_EINVAL;
+  if (kv->max_len > kMaxLen) return BLOOM_EINVAL;
+  if (kv->len < 0 || kv->len > kv->max_len || kv->prompt_len < 0) return BLOOM_EINVAL;
+  return BLOOM_OK;
+}
+
+// ---------------------------------------------------------------------------
+// launch timer
+// ---------------------------------------------------------------------------
+struct Timer {
+  bool on = false;
+  bool paused = false;
+  std::vector<hipEvent_t> start, stop;
+  int used = 0;
+  double bytes = 0.0;
+} g_timer;
+
+void destroy_timer_events() {
+  for (hipEvent_t e : g_timer.start) (void)hipEventDestroy(e);
+  for (hipEvent_t e : g_timer.stop) (void)hipEventDestroy(e);
+  g_timer.start.clear();
+  g_timer.stop.clear();
+}
+
+hipError_t timed_linear(int wdt, const LinearPlan &p, const void *X, const void *W, float *part,
+                        const EpiParams &ep, hipStream_t st, double wbytes) {
+  const bool timed = g_timer.on && !g_timer.paused && g_timer.used < (int)g_timer.start.size();
+  if (timed) {
+    hipError_t e = hipEventRecord(g_timer.start[g_timer.used], st);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t err = launch_linear(wdt, p, X, W, part, ep, st);
+  if (err != hipSuccess) return err;
+  if (timed) {
+    err = hipEventRecord(g_timer.stop[g_timer.used], st);
+    if (err != hipSuccess) return err;
+    g_timer.used++;
+    g_timer.bytes += wbytes;
+  }
+  return hipSuccess;
+}
+
+// ---------------------------------------------------------------------------
+// one forward pass over `tpr` tokens per row
+// ---------------------------------------------------------------------------
+int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *kv, int batch,
+                int tpr, int pos_base, int prompt_len, const int32_t *d_tokens,
+                const int32_t *d_valid, int32_t *d_next, float *d_hidden, char *ws,
+                hipStream_t st) {
+  const WsPlan wp = plan_ws(c, batch, tpr);
+  const bool f32 = c->weight_dtype == BLOOM_F32;
+  const int wdt = wtype(c);
+  const int M = batch * tpr;
+  const int h = c->hidden, H = c->n_head_local, d = c->head_dim, F = c->ffn;
+  const int hd = H * d;
+  const size_t wb = c->weight_dtype == BLOOM_F32 ? 4 : (c->weight_dtype == BLOOM_BF16 ? 2 : 1);
+  const size_t pb = f32 ? 4 : 2;
+  const size_t sb = c->weight_dtype == BLOOM_INT8_ROWSCALE ? 2 : 0;
+  const size_t act = act_bytes(c);
+  auto wbytes = [&](int N, int K) { return (double)((size_t)N * K * wb + (size_t)N * (pb + sb)); };
+
+  float *x = (float *)(ws + wp.x);
+  void *xa = ws + wp.xa;
+  float *q = (float *)(ws + wp.q);
+  void *o = ws + wp.o;
+  void *u = ws + wp.u;
+  void *af = ws + wp.af;
+  float *amv = (float *)(ws + wp.amv);
+  int *ami = (int *)(ws + wp.ami);
+  float *part = (float *)(ws + wp.part);
+
+  hipError_t err = launch_embed(f32, d_tokens, w->embed, w->emb_ln_g, w->emb_ln_b, x, M, h,
+                                c->vocab, c->embed_ln, c->ln_eps, st);
+  if (err != hipSuccess) return BLOOM_EHIP;
+
+  const size_t layer_stride = (size_t)kv->max_batch * H * kv->max_len * d * act;
+  const LinearPlan p_qkv = plan_linear(wdt, M, 3 * hd, h, false);
+  const LinearPlan p_dense = plan_linear(wdt, M, h, hd, false);
+  const LinearPlan p_up = plan_linear(wdt, M, F, h, false);
+  const LinearPlan p_down = plan_linear(wdt, M, h, F, false);
+
+  for (int l = 0; l < c->n_layer; ++l) {
+    const bloom_layer_weights &L = w->layers[l];
+    void *kc = (char *)kv->k + l * layer_stride;
+    void *vc = (char *)kv->v + l * layer_stride;
+
+    err = launch_layernorm(f32, x, 1, 0, L.ln1_g, L.ln1_b, xa, nullptr, M, h, c->ln_eps, st);
+    if (err != hipSuccess) return BLOOM_EHIP;
+
+    EpiParams e{};
+    e.mode = EPI_QKV;
+    e.bias = L.b_qkv;
+    e.scale = (const uint16_t *)L.s_qkv;
+    e.q = q; e.kc = kc; e.vc = vc;
+    e.H = H; e.d = d; e.max_len = kv->max_len;
+    e.pos_base = pos_base; e.rows_per_seq = tpr;
+    e.q_scale = 1.0f / sqrtf((float)d);
+    err = timed_linear(wdt, p_qkv, xa, L.w_qkv, part, e, st, wbytes(3 * hd, h));
+    if (err != hipSuccess) return BLOOM_EHIP;
+
+    err = launch_attention(f32, q, kc, vc, d_valid, o, M, H, d, kv->max_len, c->n_head_total,
+                           c->head_offset, tpr, pos_base, prompt_len, st);
+    if (err != hipSuccess) return BLOOM_EHIP;
+
+    EpiParams r{};
+    r.mode = EPI_RESID;
+    r.bias = L.b_dense;
+    r.scale = (const uint16_t *)L.s_dense;
+    r.out = x; r.ld = h;
+    err = timed_linear(wdt, p_dense, o, L.w_dense, part, r, st, wbytes(h, hd));
+    if (err != hipSuccess) return BLOOM_EHIP;
+
+    err = launch_layernorm(f32, x, 1, 0, L.ln2_g, L.ln2_b, xa, nullptr, M, h, c->ln_eps, st);
+    if (err != hipSuccess) return BLOOM_EHIP;
+
+    EpiParams g{};
+    g.mode = EPI_GELU;
+    g.bias = L.b_up;
+    g.scale = (const uint16_t *)L.s_up;
+    g.out = u; g.ld = F;
+    err = timed_linear(wdt, p_up, xa, L.w_up, part, g, st, wbytes(F, h));
+    if (err != hipSuccess) return BLOOM_EHIP;
+
+    EpiParams dn{};
+    dn.mode = EPI_RESID;
+    dn.bias = L.b_down;
+    dn.scale = (const uint16_t *)L.s_down;
+    dn.out = x; dn.ld = h;
+    err = timed_linear(wdt, p_down, u, L.w_down, part, dn, st, wbytes(h, F));
+    if (err != hipSuccess) return BLOOM_EHIP;
+  }
+
+  // final LayerNorm of each row's last position, then the tied LM head + argmax
+  err = launch_layernorm(f32, x, tpr, tpr - 1, w->lnf_g, w->lnf_b, af, d_hidden, batch, h,
+                         c->ln_eps, st);
+  if (err != hipSuccess) return BLOOM_EHIP;
+  const int nblk = wp.lm_blocks;
+  const int wdt_lm = f32 ? WT_F32 : WT_BF16;  // the embedding is never int8
+  for (int r0 = 0; r0 < batch; r0 += 128) {
+    const int rows = std::min(128, batch - r0);
+    EpiParams a{};
+    a.mode = EPI_ARGMAX;
+    a.am_val = amv + (size_t)r0 * nblk;
+    a.am_idx = ami + (size_t)r0 * nblk;
+    a.am_stride = nblk;
+    const LinearPlan p_lm = plan_linear(wdt_lm, rows, c->vocab, h, true);
+    err = timed_linear(wdt_lm, p_lm, (const char *)af + (size_t)r0 * h * act, w->embed, part, a,
+                       st, (double)c->vocab * h * pb);
+    if (err != hipSuccess) return BLOOM_EHIP;
+  }
+  err = launch_argmax_merge(amv, ami, nblk, nblk, batch, d_next, st);
+  if (err != hipSuccess) return BLOOM_EHIP;
+  return BLOOM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *bloom_status_string(int s) {
+  switch (s) {
+    case BLOOM_OK: return "ok";
+    case BLOOM_EINVAL: return "invalid argument (shape, pointer or index)";
+    case BLOOM_EDTYPE: return "unsupported data type";
+    case BLOOM_ECAPACITY: return "KV cache capacity exceeded";
+    case BLOOM_EWORKSPACE: return "workspace too small";
+    case BLOOM_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int bloom_workspace_bytes(const bloom_config *cfg, int32_t max_batch, int32_t max_prompt,
+                          size_t *bytes) {
+  int s = check_config(cfg);
+  if (s != BLOOM_OK) return s;
+  if (!bytes || max_batch < 0 || max_prompt < 0) return BLOOM_EINVAL;
+  *bytes = plan_ws(cfg, max_batch, std::max(max_prompt, 1)).total;
+  return BLOOM_OK;
+}
+
+int bloom_prefill(const bloom_config *cfg, const bloom_weights *w, bloom_kv_cache *kv,
+                  int32_t batch, int32_t prompt_len, const int32_t *d_tokens,
+                  const int32_t *d_valid_len, int32_t *d_next_tokens, float *d_hidden_out,
+                  void *d_ws, size_t ws_bytes, void *stream) {
+  int s = check_config(cfg);
+  if (s != BLOOM_OK) return s;
+  if ((s = check_weights(cfg, w)) != BLOOM_OK) return s;
+  if ((s = check_kv(cfg, kv)) != BLOOM_OK) return s;
+  if (batch < 0 || prompt_len < 1) return BLOOM_EINVAL;
+  if (batch > kv->max_batch || prompt_len > kv->max_len) return BLOOM_ECAPACITY;
+  if (batch == 0) return BLOOM_OK;
+  if (!d_tokens || !d_valid_len || !d_next_tokens || !d_ws) return BLOOM_EINVAL;
+  if (ws_bytes < plan_ws(cfg, batch, prompt_len).total) return BLOOM_EWORKSPACE;
+  s = run_forward(cfg, w, kv, batch, prompt_len, 0, prompt_len, d_tokens, d_valid_len,
+                  d_next_tokens, d_hidden_out, (char *)d_ws, (hipStream_t)stream);
+  if (s == BLOOM_OK) {
+    kv->prompt_len = prompt_len;
+    kv->len = prompt_len;
+  }
+  return s;
+}
+
+int bloom_decode_step(const bloom_config *cfg, const bloom_weights *w, bloom_kv_cache *kv,
+                      int32_t batch, const int32_t *d_tokens, const int32_t *d_valid_len,
+                      int32_t *d_next_tokens, float *d_hidden_out, void *d_ws, size_t ws_bytes,
+                      void *stream) {
+  int s = check_config(cfg);
+  if (s != BLOOM_OK) return s;
+  if ((s = check_weights(cfg, w)) != BLOOM_OK) return s;
+  if ((s = check_kv(cfg, kv)) != BLOOM_OK) return s;
+  if (batch < 0) return BLOOM_EINVAL;
+  if (kv->prompt_len <= 0 || kv->len < kv->prompt_len) return BLOOM_EINVAL;
+  if (batch > kv->max_batch || kv->len >= kv->max_len) return BLOOM_ECAPACITY;
+  if (batch == 0) return BLOOM_OK;
+  if (!d_tokens || !d_valid_len || !d_next_tokens || !d_ws) return BLOOM_EINVAL;
+  if (ws_bytes < plan_ws(cfg, batch, 1).total) return BLOOM_EWORKSPACE;
+  s = run_forward(cfg, w, kv, batch, 1, kv->len, kv->prompt_len, d_tokens, d_valid_len,
+                  d_next_tokens, d_hidden_out, (char *)d_ws, (hipStream_t)stream);
+  if (s == BLOOM_OK) kv->len += 1;
+  return s;
+}
+
+int alibi_masked_softmax(const void *d_scores, int32_t in_dtype, const int32_t *d_valid_len,
+                         int32_t B, int32_t H, int32_t Q, int32_t K, int32_t n_head_total,
+                         int32_t head_offset, void *d_probs, int32_t out_dtype, void *stream) {
+  if (B < 0 || H < 0 || Q < 0 || K < 0 || Q > K) return BLOOM_EINVAL;
+  if (n_head_total < 1 || head_offset < 0 || head_offset + H > n_head_total) return BLOOM_EINVAL;
+  if ((in_dtype != BLOOM_F32 && in_dtype != BLOOM_BF16) ||
+      (out_dtype != BLOOM_F32 && out_dtype != BLOOM_BF16))
+    return BLOOM_EDTYPE;
+  if ((long)B * H * Q == 0 || K == 0) return BLOOM_OK;
+  if (!d_scores || !d_valid_len || !d_probs) return BLOOM_EINVAL;
+  hipError_t err = launch_alibi_softmax(d_scores, in_dtype == BLOOM_BF16, d_valid_len, d_probs,
+                                        out_dtype == BLOOM_BF16, B, H, Q, K, n_head_total,
+                                        head_offset, (hipStream_t)stream);
+  return err == hipSuccess ? BLOOM_OK : BLOOM_EHIP;
+}
+
+int kv_cache_append(const bloom_config *cfg, bloom_kv_cache *kv, int32_t layer, int32_t batch,
+                    int32_t pos, const void *d_k, const void *d_v, int32_t n_new, void *stream) {
+  int s = check_config(cfg);
+  if (s != BLOOM_OK) return s;
+  if ((s = check_kv(cfg, kv)) != BLOOM_OK) return s;
+  if (layer < 0 || layer >= cfg->n_layer || batch < 0 || pos < 0 || n_new < 0)
+    return BLOOM_EINVAL;
+  if (batch > kv->max_batch || (long)pos + n_new > kv->max_len) return BLOOM_ECAPACITY;
+  if (batch == 0 || n_new == 0) return BLOOM_OK;
+  if (!d_k || !d_v) return BLOOM_EINVAL;
+  const size_t act = act_bytes(cfg);
+  const size_t layer_stride =
+      (size_t)kv->max_batch * cfg->n_head_local * kv->max_len * cfg->head_dim * act;
+  hipError_t err = launch_kv_append(cfg->weight_dtype == BLOOM_F32, d_k, d_v,
+                                    (char *)kv->k + layer * layer_stride,
+                                    (char *)kv->v + layer * layer_stride, batch,
+                                    cfg->n_head_local, n_new, cfg->head_dim, kv->max_len, pos,
+                                    (hipStream_t)stream);
+  return err == hipSuccess ? BLOOM_OK : BLOOM_EHIP;
+}
+
+int bloom_timer_enable(int32_t max_launches) {
+  if (max_launches <= 0) return BLOOM_EINVAL;
+  destroy_timer_events();
+  g_timer.start.resize(max_launches);
+  g_timer.stop.resize(max_launches);
+  for (int i = 0; i < max_launches; ++i) {
+    if (hipEventCreate(&g_timer.start[i]) != hipSuccess ||
+        hipEventCreate(&g_timer.stop[i]) != hipSuccess) {
+      g_timer.start.resize(i);
+      g_timer.stop.resize(i);
+      destroy_timer_events();
+      return BLOOM_EHIP;
+    }
+  }
+  g_timer.used = 0;
+  g_timer.bytes = 0.0;
+  g_timer.on = true;
+  g_timer.paused = false;
+  return BLOOM_OK;
+}
+
+int bloom_timer_pause(int32_t paused) {
+  g_timer.paused = paused != 0;
+  return BLOOM_OK;
+}
+
+int bloom_timer_disable(void) {
+  g_timer.on = false;
+  destroy_timer_events();
+  g_timer.used = 0;
+  g_timer.bytes = 0.0;
+  return BLOOM_OK;
+}
+
+int bloom_timer_read(double *total_ms, int32_t *n_launches, double *weight_bytes) {
+  if (!total_ms || !n_launches || !weight_bytes) return BLOOM_EINVAL;
+  double total = 0.0;
+  if (g_timer.used > 0 && hipEventSynchronize(g_timer.stop[g_timer.used - 1]) != hipSuccess)
+    return BLOOM_EHIP;
+  for (int i = 0; i < g_timer.used; ++i) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, g_timer.start[i], g_timer.stop[i]) != hipSuccess)
+      return BLOOM_EHIP;
+    total += ms;
+  }
+  *total_ms = total;
+  *n_launches = g_timer.used;
+  *weight_bytes = g_timer.bytes;
+  g_timer.used = 0;
+  g_timer.bytes = 0.0;
+  return BLOOM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,174 @@
+// ALiBi attention of one query row over the KV cache, and the standalone KV append.
+//
+// One 256-thread block per (query row m, head h).  Query row m belongs to sequence
+// b = m / rows_per_seq at absolute position qpos = pos_base + m % rows_per_seq (the
+// decode step: rows_per_seq = 1, pos_base = current length; the prompt pass:
+// rows_per_seq = prompt length, pos_base = 0).  Keys j in [pad_b, qpos] are visible,
+// pad_b = prompt_len - valid_len[b] (left padding).  Steps, all in float32:
+//   1. s_j = q . k_j + slope_h * (j - qpos)   (q already carries 1/sqrt(d); keys read
+//      as 16-byte pieces, d/8 lanes per key, partial dots summed across those lanes)
+//   2. masked softmax over the visible keys only (block max, exp, block sum) --
+//      masked keys are never touched, i.e. they get probability exactly 0
+//   3. o = sum_j p_j v_j, split over key phases then summed in LDS in a fixed order.
+// A query with no visible key (a left-pad position of the prompt) gets o = 0.
+// ("Hugging Face BLOOM Inference Optimization", Custom CUDA Kernels and Hardware
+// Acceleration, for the fused mask + float32 softmax; "DeepSpeed Inference ...",
+// Section III.D, attention fused as one kernel.)
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace bl {
+
+template <typename TA> struct KVLoad8;
+template <> struct KVLoad8<bf16_t> {
+  static __device__ __forceinline__ void load(const bf16_t *p, float v[8]) {
+    const u32x4 t = *(const u32x4 *)p;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[2 * i] = lo_bf(t[i]); v[2 * i + 1] = hi_bf(t[i]); }
+  }
+};
+template <> struct KVLoad8<float> {
+  static __device__ __forceinline__ void load(const float *p, float v[8]) {
+    const float4 a = *(const float4 *)p, b = *(const float4 *)(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+};
+
+template <typename TA>
+__global__ __launch_bounds__(256) void k_attention(const float *__restrict__ q,
+                                                   const TA *__restrict__ kc,
+                                                   const TA *__restrict__ vc,
+                                                   const int *__restrict__ valid_len,
+                                                   TA *__restrict__ o, int H, int d, int max_len,
+                                                   int n_total, int head_off, int rows_per_seq,
+                                                   int pos_base, int prompt_len) {
+  extern __shared__ float smem[];   // [max_len] scores, then [256] PV partials
+  __shared__ float red[4];
+  const int m = blockIdx.x, h = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int b = m / rows_per_seq;
+  const int qpos = pos_base + (m - b * rows_per_seq);
+  int vl = valid_len[b];
+  vl = vl < 1 ? 1 : (vl > prompt_len ? prompt_len : vl);
+  const int first = prompt_len - vl;
+  TA *out = o + ((size_t)m * H + h) * d;
+  if (qpos < first) {
+    for (int e = tid; e < d; e += 256) out[e] = from_f<TA>(0.f);
+    return;
+  }
+  const int T = qpos - first + 1;
+  const float slope = alibi_slope(n_total, head_off + h);
+  const size_t head_base = ((size_t)b * H + h) * (size_t)max_len * d;
+  const TA *kb = kc + head_base;
+  const TA *vb = vc + head_base;
+  const float *qr = q + ((size_t)m * H + h) * d;
+  float *sc = smem;
+  float *pv = smem + max_len;
+
+  // 1. scores
+  const int L = d >> 3;           // lanes per key (1..32)
+  const int G = 256 / L;          // keys per pass over the block
+  const int g = tid / L, sub = tid - g * L;
+  float qv[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) qv[t] = qr[8 * sub + t];
+  for (int j0 = 0; j0 < T; j0 += G) {
+    const int jj = j0 + g;
+    float dot = 0.f;
+    if (jj < T) {
+      float kv[8];
+      KVLoad8<TA>::load(kb + (size_t)(first + jj) * d + 8 * sub, kv);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) dot = fmaf(qv[t], kv[t], dot);
+    }
+    for (int off = L >> 1; off > 0; off >>= 1) dot += __shfl_xor(dot, off, 64);
+    if (jj < T && sub == 0) sc[jj] = dot + slope * (float)(first + jj - qpos);
+  }
+  __syncthreads();
+
+  // 2. softmax over the T visible keys
+  float mx = -INFINITY;
+  for (int j = tid; j < T; j += 256) mx = fmaxf(mx, sc[j]);
+  mx = block_max<4>(mx, red);
+  float sum = 0.f;
+  for (int j = tid; j < T; j += 256) {
+    const float e = __expf(sc[j] - mx);
+    sc[j] = e;
+    sum += e;
+  }
+  sum = block_sum<4>(sum, red);
+  const float inv = 1.0f / sum;
+
+  // 3. o = sum_j p_j v_j; thread (phase, e) covers dim e for keys j = phase mod P
+  const int P = 256 / d;          // key phases (1 when d = 256)
+  const int phase = tid / d, e = tid - phase * d;
+  float acc = 0.f;
+  if (phase < P) {
+    for (int j = phase; j < T; j += P)
+      acc = fmaf(sc[j], to_f<TA>(vb[(size_t)(first + j) * d + e]), acc);
+  }
+  pv[tid] = acc;
+  __syncthreads();
+  if (tid < d) {
+    float s = 0.f;
+    for (int p = 0; p < P; ++p) s += pv[p * d + tid];
+    out[tid] = from_f<TA>(s * inv);
+  }
+}
+
+hipError_t launch_attention(bool f32, const float *q, const void *kc, const void *vc,
+                            const int *valid_len, void *o, int rows, int H, int d, int max_len,
+                            int n_total, int head_off, int rows_per_seq, int pos_base,
+                            int prompt_len, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  const dim3 grid(rows, H), block(256);
+  const size_t shmem = ((size_t)max_len + 256) * sizeof(float);
+  if (f32)
+    hipLaunchKernelGGL(k_attention<float>, grid, block, shmem, st, q, (const float *)kc,
+                       (const float *)vc, valid_len, (float *)o, H, d, max_len, n_total,
+                       head_off, rows_per_seq, pos_base, prompt_len);
+  else
+    hipLaunchKernelGGL(k_attention<bf16_t>, grid, block, shmem, st, q, (const bf16_t *)kc,
+                       (const bf16_t *)vc, valid_len, (bf16_t *)o, H, d, max_len, n_total,
+                       head_off, rows_per_seq, pos_base, prompt_len);
+  return hipGetLastError();
+}
+
+// src [batch][H][n_new][d] -> cache [layer][max_batch][H][max_len][d] slots pos..pos+n_new-1
+template <typename TA>
+__global__ __launch_bounds__(256) void k_kv_append(const TA *__restrict__ sk,
+                                                   const TA *__restrict__ sv,
+                                                   TA *__restrict__ ck, TA *__restrict__ cv,
+                                                   int batch, int H, int n_new, int d,
+                                                   int max_len, int pos) {
+  const size_t total = (size_t)batch * H * n_new * d;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < total;
+       i += (size_t)gridDim.x * 256) {
+    const int e = (int)(i % d);
+    size_t r = i / d;
+    const int t = (int)(r % n_new);
+    r /= n_new;  // r = b * H + h
+    const size_t dst = (r * max_len + pos + t) * d + e;
+    ck[dst] = sk[i];
+    cv[dst] = sv[i];
+  }
+}
+
+hipError_t launch_kv_append(bool f32, const void *k, const void *v, void *ck, void *cv,
+                            int batch, int H, int n_new, int d, int max_len, int pos,
+                            hipStream_t st) {
+  const size_t total = (size_t)batch * H * n_new * d;
+  if (total == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)std::min<size_t>((total + 255) / 256, 65536);
+  if (f32)
+    hipLaunchKernelGGL(k_kv_append<float>, dim3(blocks), dim3(256), 0, st, (const float *)k,
+                       (const float *)v, (float *)ck, (float *)cv, batch, H, n_new, d, max_len,
+                       pos);
+  else
+    hipLaunchKernelGGL(k_kv_append<bf16_t>, dim3(blocks), dim3(256), 0, st, (const bf16_t *)k,
+                       (const bf16_t *)v, (bf16_t *)ck, (bf16_t *)cv, batch, H, n_new, d,
+                       max_len, pos);
+  return hipGetLastError();
+}
+
+}  // namespace bl

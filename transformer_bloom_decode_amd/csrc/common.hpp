@@ -1,0 +1,183 @@
+// Device helpers shared by the gfx950 kernels: storage-type conversions, wave and
+// block reductions, the ALiBi slope, the tanh GeLU, and the epilogue description
+// used by every linear-layer kernel.
+#pragma once
+
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bl {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+typedef uint16_t bf16_t;  // bf16 bit pattern
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// conversions
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// fp32 -> bf16, round to nearest even (NaN kept quiet)
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
+
+template <typename T> __device__ __forceinline__ float to_f(T v);
+template <> __device__ __forceinline__ float to_f<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f<bf16_t>(bf16_t v) { return bf2f(v); }
+
+template <typename T> __device__ __forceinline__ T from_f(float v);
+template <> __device__ __forceinline__ float from_f<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float v) { return f2bf(v); }
+
+// two bf16 packed in a dword -> floats
+__device__ __forceinline__ float lo_bf(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// ---------------------------------------------------------------------------
+// reductions (fixed order: results are bitwise reproducible)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// Sum over a block of NW waves; `sh` holds NW floats.  All threads get the result.
+template <int NW>
+__device__ __forceinline__ float block_sum(float v, float *sh) {
+  v = wave_sum(v);
+  const int w = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) sh[w] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) t += sh[i];
+  __syncthreads();
+  return t;
+}
+
+template <int NW>
+__device__ __forceinline__ float block_max(float v, float *sh) {
+  v = wave_max(v);
+  const int w = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) sh[w] = v;
+  __syncthreads();
+  float t = sh[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) t = fmaxf(t, sh[i]);
+  __syncthreads();
+  return t;
+}
+
+// ---------------------------------------------------------------------------
+// model pieces
+// ---------------------------------------------------------------------------
+
+// ALiBi slope of global head g in an n_total-head model (ALiBi paper, Section 3):
+// c = largest power of two <= n_total; heads g < c use 2^(-8(g+1)/c), the others the
+// odd terms 2^(-4(2(g-c)+1)/c) of the 2c-head sequence.  The exponent is exact in
+// fp32 (c is a power of two), so only exp2 rounds.
+__device__ __forceinline__ float alibi_slope(int n_total, int g) {
+  const int c = 1 << (31 - __clz(n_total));
+  const float e = (g < c) ? (-8.0f * (float)(g + 1)) / (float)c
+                          : (-4.0f * (float)(2 * (g - c) + 1)) / (float)c;
+  return exp2f(e);
+}
+
+// tanh form of GeLU: 0.5 y (1 + tanh(sqrt(2/pi) (y + 0.044715 y^3)))
+__device__ __forceinline__ float gelu_tanh(float y) {
+  const float k0 = 0.7978845608028654f;
+  const float k1 = 0.044715f;
+  return 0.5f * y * (1.0f + tanhf(k0 * (y + k1 * y * y * y)));
+}
+
+// ---------------------------------------------------------------------------
+// linear-layer epilogues
+// ---------------------------------------------------------------------------
+enum EpiMode : int {
+  EPI_QKV = 0,     // split fused q|k|v rows: q (fp32, scaled) to a buffer, k/v to the cache
+  EPI_RESID = 1,   // residual stream x[m][n] += y
+  EPI_GELU = 2,    // u[m][n] = act(gelu(y))
+  EPI_ARGMAX = 3,  // per-tile (max, lowest index) over n, for the LM head
+  EPI_STORE = 4,   // out[m][n] = y as fp32 (used by tests of the raw product)
+};
+
+struct EpiParams {
+  int mode;
+  const void *bias;        // [N] parameter type, nullable
+  const uint16_t *scale;   // [N] fp16 per-row scales (int8 weights), nullable
+  // EPI_QKV
+  float *q;                // [M][H][d]
+  void *kc, *vc;           // cache of this layer: [max_batch][H][max_len][d]
+  int H, d, max_len;
+  int pos_base;            // absolute position of row m is pos_base + m % rows_per_seq
+  int rows_per_seq;        // 1 (decode) or the prompt length (prefill)
+  float q_scale;           // 1/sqrt(d)
+  // EPI_RESID / EPI_GELU / EPI_STORE
+  void *out;               // [M][ld]
+  int ld;
+  // EPI_ARGMAX
+  float *am_val;           // [M][am_stride]
+  int *am_idx;
+  int am_stride;
+};
+
+// y = acc * scale[n] + bias[n], then the mode's action.  TP = parameter type, TA =
+// activation type.
+template <typename TP, typename TA>
+__device__ __forceinline__ void epilogue(const EpiParams &e, int m, int n, float acc) {
+  float y = acc;
+  if (e.scale) y *= h2f(e.scale[n]);
+  if (e.bias) y += to_f<TP>(((const TP *)e.bias)[n]);
+  switch (e.mode) {
+    case EPI_QKV: {
+      const int d = e.d, H = e.H;
+      const int hd = n / (3 * d);
+      const int r = n - hd * 3 * d;
+      const int t = r / d;
+      const int c = r - t * d;
+      if (t == 0) {
+        e.q[((size_t)m * H + hd) * d + c] = y * e.q_scale;
+      } else {
+        const int b = m / e.rows_per_seq;
+        const int pos = e.pos_base + (m - b * e.rows_per_seq);
+        TA *cache = (TA *)(t == 1 ? e.kc : e.vc);
+        cache[(((size_t)b * H + hd) * e.max_len + pos) * d + c] = from_f<TA>(y);
+      }
+      break;
+    }
+    case EPI_RESID: {
+      float *x = (float *)e.out + (size_t)m * e.ld + n;
+      *x = *x + y;
+      break;
+    }
+    case EPI_GELU:
+      ((TA *)e.out)[(size_t)m * e.ld + n] = from_f<TA>(gelu_tanh(y));
+      break;
+    case EPI_STORE:
+      ((float *)e.out)[(size_t)m * e.ld + n] = y;
+      break;
+    default:
+      break;
+  }
+}
+
+}  // namespace bl

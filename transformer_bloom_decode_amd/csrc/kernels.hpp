@@ -1,0 +1,51 @@
+// Host-side launch entry points of the gfx950 kernels (used by the C ABI layer).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bl {
+
+struct EpiParams;
+
+enum WeightType : int { WT_F32 = 0, WT_BF16 = 1, WT_INT8 = 2 };
+enum LinearKind : int { LIN_F32 = 0, LIN_GEMV = 1, LIN_TILED = 2 };
+
+// Cap on the split-K partial buffer (float32 elements) any one linear may use.
+constexpr long kPartialCapFloats = 8l << 20;
+
+struct LinearPlan {
+  int kind;
+  int M, N, K;
+  int mt;        // GEMV: 16-row activation tiles (1, 2, 4, 8)
+  int grid_x, grid_y;
+  int splits;    // K splits (> 1: partial sums + reduction kernel)
+};
+
+LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax);
+hipError_t launch_linear(int wdtype, const LinearPlan &p, const void *X, const void *W,
+                         float *partial, const EpiParams &ep, hipStream_t st);
+hipError_t launch_argmax_merge(const float *val, const int *idx, int stride, int nblk, int rows,
+                               int *out, hipStream_t st);
+
+hipError_t launch_alibi_softmax(const void *scores, bool in_bf16, const int *valid_len,
+                                void *probs, bool out_bf16, int B, int H, int Q, int K,
+                                int n_total, int head_off, hipStream_t stream);
+
+hipError_t launch_embed(bool f32, const int *tokens, const void *embed, const void *g,
+                        const void *b, float *x, int rows, int h, int vocab, int do_ln, float eps,
+                        hipStream_t stream);
+hipError_t launch_layernorm(bool f32, const float *x, int in_step, int in_off, const void *g,
+                            const void *b, void *out, float *out_f32, int rows, int h, float eps,
+                            hipStream_t stream);
+
+hipError_t launch_attention(bool f32, const float *q, const void *kc, const void *vc,
+                            const int *valid_len, void *o, int rows, int H, int d, int max_len,
+                            int n_total, int head_off, int rows_per_seq, int pos_base,
+                            int prompt_len, hipStream_t st);
+hipError_t launch_kv_append(bool f32, const void *k, const void *v, void *ck, void *cv,
+                            int batch, int H, int n_new, int d, int max_len, int pos,
+                            hipStream_t st);
+
+}  // namespace bl
