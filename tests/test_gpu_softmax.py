@@ -127,8 +127,9 @@ def test_softmax_bf16_output_within_rounding():
     scores, valid = bi.softmax_inputs()
     got = _run(scores, valid, out="bf16")
     ref = _ref(scores, valid)
-    # round-to-nearest bf16 is within half an ulp: 2^-9 relative (plus fp32 noise)
-    assert np.all(np.abs(got - ref) <= 2 ** -9 * np.abs(ref) + 1e-6)
+    # bf16 keeps 8 significant bits: round-to-nearest is within 2^-8 relative (half an
+    # ulp, i.e. 2^-9 absolute on [0.5, 1)), plus the fp32 noise of the softmax itself
+    assert np.all(np.abs(got - ref) <= 2 ** -8 * np.abs(ref) + 1e-6)
     for b, vl in enumerate(valid):
         assert np.all(got[b, :, :, : 2048 - vl] == 0.0)
 

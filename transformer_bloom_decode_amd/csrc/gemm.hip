@@ -96,7 +96,12 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(const bf16_t *__restrict__ X,
   __shared__ float red[4][MT][16][17];
   __shared__ float fin[MT][16][17];
 
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  // The wave index goes through readfirstlane so that the chunk range, and with it
+  // every branch around an MFMA, is scalar: an MFMA placed under an exec mask that
+  // happens to be all-zero still executes and accumulates whatever its stale operand
+  // registers hold.
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, c = lane >> 4;
   const int n0 = blockIdx.x * 16;
   const int nrow = min(n0 + r, N - 1);
