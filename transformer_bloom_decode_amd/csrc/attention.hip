@@ -9,7 +9,8 @@
 //      as 16-byte pieces, d/8 lanes per key, partial dots summed across those lanes)
 //   2. masked softmax over the visible keys only (block max, exp, block sum) --
 //      masked keys are never touched, i.e. they get probability exactly 0
-//   3. o = sum_j p_j v_j, split over key phases then summed in LDS in a fixed order.
+//   3. o = sum_j p_j v_j, per lane group over its keys, then summed over the groups
+//      in LDS in a fixed order.
 // A query with no visible key (a left-pad position of the prompt) gets o = 0.
 // ("Hugging Face BLOOM Inference Optimization", Custom CUDA Kernels and Hardware
 // Acceleration, for the fused mask + float32 softmax; "DeepSpeed Inference ...",
@@ -34,6 +35,8 @@ template <> struct KVLoad8<float> {
   }
 };
 
+constexpr int kKeysPerBatch = 4;  // keys each lane group loads before using any of them
+
 template <typename TA>
 __global__ __launch_bounds__(256) void k_attention(const float *__restrict__ q,
                                                    const TA *__restrict__ kc,
@@ -42,7 +45,7 @@ __global__ __launch_bounds__(256) void k_attention(const float *__restrict__ q,
                                                    TA *__restrict__ o, int H, int d, int max_len,
                                                    int n_total, int head_off, int rows_per_seq,
                                                    int pos_base, int prompt_len) {
-  extern __shared__ float smem[];   // [max_len] scores, then [256] PV partials
+  extern __shared__ float smem[];   // [max_len] scores, then [256 / (d/8)][d] P.V partials
   __shared__ float red[4];
   const int m = blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x;
@@ -59,34 +62,44 @@ __global__ __launch_bounds__(256) void k_attention(const float *__restrict__ q,
   const int T = qpos - first + 1;
   const float slope = alibi_slope(n_total, head_off + h);
   const size_t head_base = ((size_t)b * H + h) * (size_t)max_len * d;
-  const TA *kb = kc + head_base;
-  const TA *vb = vc + head_base;
+  const TA *kb = kc + head_base + (size_t)first * d;
+  const TA *vb = vc + head_base + (size_t)first * d;
   const float *qr = q + ((size_t)m * H + h) * d;
   float *sc = smem;
   float *pv = smem + max_len;
 
-  // 1. scores
-  const int L = d >> 3;           // lanes per key (1..32)
-  const int G = 256 / L;          // keys per pass over the block
+  // lane group g (L = d/8 lanes) handles keys j = g (mod G); lane `sub` owns dims
+  // [8 sub, 8 sub + 8) of each of them
+  const int L = d >> 3;
+  const int G = 256 / L;
   const int g = tid / L, sub = tid - g * L;
   float qv[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) qv[t] = qr[8 * sub + t];
-  for (int j0 = 0; j0 < T; j0 += G) {
-    const int jj = j0 + g;
-    float dot = 0.f;
-    if (jj < T) {
-      float kv[8];
-      KVLoad8<TA>::load(kb + (size_t)(first + jj) * d + 8 * sub, kv);
+
+  // 1. scores s_j = q.k_j + slope * (j - qpos)
+  for (int j0 = 0; j0 < T; j0 += G * kKeysPerBatch) {
+    float kv[kKeysPerBatch][8];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) dot = fmaf(qv[t], kv[t], dot);
+    for (int u = 0; u < kKeysPerBatch; ++u) {
+      const int jj = j0 + u * G + g;
+      if (jj < T) KVLoad8<TA>::load(kb + (size_t)jj * d + 8 * sub, kv[u]);
     }
-    for (int off = L >> 1; off > 0; off >>= 1) dot += __shfl_xor(dot, off, 64);
-    if (jj < T && sub == 0) sc[jj] = dot + slope * (float)(first + jj - qpos);
+#pragma unroll
+    for (int u = 0; u < kKeysPerBatch; ++u) {
+      const int jj = j0 + u * G + g;
+      float dot = 0.f;
+      if (jj < T) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) dot = fmaf(qv[t], kv[u][t], dot);
+      }
+      for (int off = L >> 1; off > 0; off >>= 1) dot += __shfl_xor(dot, off, 64);
+      if (jj < T && sub == 0) sc[jj] = dot + slope * (float)(first + jj - qpos);
+    }
   }
   __syncthreads();
 
-  // 2. softmax over the T visible keys
+  // 2. softmax over the T visible keys (masked keys are simply never visited)
   float mx = -INFINITY;
   for (int j = tid; j < T; j += 256) mx = fmaxf(mx, sc[j]);
   mx = block_max<4>(mx, red);
@@ -96,23 +109,37 @@ __global__ __launch_bounds__(256) void k_attention(const float *__restrict__ q,
     sc[j] = e;
     sum += e;
   }
-  sum = block_sum<4>(sum, red);
+  sum = block_sum<4>(sum, red);   // its barriers also publish sc[] to every thread
   const float inv = 1.0f / sum;
 
-  // 3. o = sum_j p_j v_j; thread (phase, e) covers dim e for keys j = phase mod P
-  const int P = 256 / d;          // key phases (1 when d = 256)
-  const int phase = tid / d, e = tid - phase * d;
-  float acc = 0.f;
-  if (phase < P) {
-    for (int j = phase; j < T; j += P)
-      acc = fmaf(sc[j], to_f<TA>(vb[(size_t)(first + j) * d + e]), acc);
+  // 3. o = sum_j p_j v_j: per-group partial sums, then a fixed-order sum over groups
+  float acc[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) acc[t] = 0.f;
+  for (int j0 = 0; j0 < T; j0 += G * kKeysPerBatch) {
+    float vv[kKeysPerBatch][8];
+#pragma unroll
+    for (int u = 0; u < kKeysPerBatch; ++u) {
+      const int jj = j0 + u * G + g;
+      if (jj < T) KVLoad8<TA>::load(vb + (size_t)jj * d + 8 * sub, vv[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kKeysPerBatch; ++u) {
+      const int jj = j0 + u * G + g;
+      if (jj < T) {
+        const float p = sc[jj];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) acc[t] = fmaf(p, vv[u][t], acc[t]);
+      }
+    }
   }
-  pv[tid] = acc;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) pv[g * d + 8 * sub + t] = acc[t];
   __syncthreads();
-  if (tid < d) {
+  for (int e = tid; e < d; e += 256) {
     float s = 0.f;
-    for (int p = 0; p < P; ++p) s += pv[p * d + tid];
-    out[tid] = from_f<TA>(s * inv);
+    for (int gg = 0; gg < G; ++gg) s += pv[gg * d + e];
+    out[e] = from_f<TA>(s * inv);
   }
 }
 
@@ -122,7 +149,7 @@ hipError_t launch_attention(bool f32, const float *q, const void *kc, const void
                             int prompt_len, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
   const dim3 grid(rows, H), block(256);
-  const size_t shmem = ((size_t)max_len + 256) * sizeof(float);
+  const size_t shmem = ((size_t)max_len + 256 * 8) * sizeof(float);
   if (f32)
     hipLaunchKernelGGL(k_attention<float>, grid, block, shmem, st, q, (const float *)kc,
                        (const float *)vc, valid_len, (float *)o, H, d, max_len, n_total,

@@ -393,17 +393,31 @@ __global__ __launch_bounds__(256) void k_splitk_epilogue(const float *__restrict
   epilogue<TP, TA>(ep, (int)(idx / N), (int)(idx % N), s);
 }
 
-// Final greedy choice per row: lowest index among the per-tile maxima.
-__global__ __launch_bounds__(256) void k_argmax_merge(const float *__restrict__ val,
-                                                      const int *__restrict__ idx, int stride,
-                                                      int nblk, int *__restrict__ out) {
-  __shared__ float sv[4];
-  __shared__ int si[4];
+// Final greedy choice per row: lowest index among the per-tile maxima.  1024 threads,
+// each folding a strided slice of the partials with independent loads.
+constexpr int kMergeThreads = 1024;
+
+__global__ __launch_bounds__(kMergeThreads) void k_argmax_merge(const float *__restrict__ val,
+                                                                const int *__restrict__ idx,
+                                                                int stride, int nblk,
+                                                                int *__restrict__ out) {
+  __shared__ float sv[kMergeThreads / 64];
+  __shared__ int si[kMergeThreads / 64];
   const int m = blockIdx.x;
+  const float *vr = val + (size_t)m * stride;
+  const int *ir = idx + (size_t)m * stride;
   float bv = -INFINITY;
   int bi = 0x7fffffff;
-  for (int b = threadIdx.x; b < nblk; b += 256)
-    argmax_take(bv, bi, val[(size_t)m * stride + b], idx[(size_t)m * stride + b]);
+  int b = threadIdx.x;
+  for (; b + 3 * kMergeThreads < nblk; b += 4 * kMergeThreads) {
+    float v[4];
+    int i[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) { v[u] = vr[b + u * kMergeThreads]; i[u] = ir[b + u * kMergeThreads]; }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) argmax_take(bv, bi, v[u], i[u]);
+  }
+  for (; b < nblk; b += kMergeThreads) argmax_take(bv, bi, vr[b], ir[b]);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const float ov = __shfl_xor(bv, o, 64);
@@ -413,7 +427,7 @@ __global__ __launch_bounds__(256) void k_argmax_merge(const float *__restrict__ 
   if ((threadIdx.x & 63) == 0) { sv[threadIdx.x >> 6] = bv; si[threadIdx.x >> 6] = bi; }
   __syncthreads();
   if (threadIdx.x == 0) {
-    for (int w = 1; w < 4; ++w) argmax_take(bv, bi, sv[w], si[w]);
+    for (int w = 1; w < kMergeThreads / 64; ++w) argmax_take(bv, bi, sv[w], si[w]);
     out[m] = bi == 0x7fffffff ? 0 : bi;
   }
 }
@@ -504,7 +518,8 @@ hipError_t launch_linear(int wdtype, const LinearPlan &p, const void *X, const v
 hipError_t launch_argmax_merge(const float *val, const int *idx, int stride, int nblk, int rows,
                                int *out, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_argmax_merge, dim3(rows), dim3(256), 0, st, val, idx, stride, nblk, out);
+  hipLaunchKernelGGL(k_argmax_merge, dim3(rows), dim3(kMergeThreads), 0, st, val, idx, stride,
+                     nblk, out);
   return hipGetLastError();
 }
 

@@ -1,51 +1,138 @@
 // Embedding gather and row LayerNorm.
 //
-// One 256-thread block per row.  LayerNorm statistics are float32 and two-pass
-// (mean, then the biased variance of the centred values), matching the definition
-// gamma * (x - mean) / sqrt(var + eps) + beta.  The residual stream is float32.
+// One block per row.  A row of up to kLnThreads * 4 * kLnVec floats is held in
+// registers (float4 pieces), so the row is read from memory once: the mean is a
+// block sum of the registers, the biased variance a second block sum of the centred
+// registers (two-pass, float32), then gamma * (x - mean) / sqrt(var + eps) + beta is
+// written.  Longer rows fall back to re-reading the row.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace bl {
 
-// x[row] = E[token[row]] as float32, then optionally LayerNorm'd in place.
+constexpr int kLnThreads = 1024;
+constexpr int kLnWaves = kLnThreads / 64;
+constexpr int kLnVec = 4;   // float4 pieces per thread: rows up to 16384
+
+template <typename T> struct Vec4;
+template <> struct Vec4<float> {
+  static __device__ __forceinline__ float4 load(const float *p) { return *(const float4 *)p; }
+  static __device__ __forceinline__ void store(float *p, float4 v) { *(float4 *)p = v; }
+};
+template <> struct Vec4<bf16_t> {
+  static __device__ __forceinline__ float4 load(const bf16_t *p) {
+    const uint2 t = *(const uint2 *)p;
+    return make_float4(lo_bf(t.x), hi_bf(t.x), lo_bf(t.y), hi_bf(t.y));
+  }
+  static __device__ __forceinline__ void store(bf16_t *p, float4 v) {
+    uint2 t;
+    t.x = (uint32_t)f2bf(v.x) | ((uint32_t)f2bf(v.y) << 16);
+    t.y = (uint32_t)f2bf(v.z) | ((uint32_t)f2bf(v.w) << 16);
+    *(uint2 *)p = t;
+  }
+};
+
+__device__ __forceinline__ float sum4(float4 v) { return (v.x + v.y) + (v.z + v.w); }
+
+// Normalise the register-held row piece v[] (columns 4*(threadIdx.x + i*kLnThreads)).
+// Returns mean and rstd; `h` is the row length (a multiple of 4).
+__device__ __forceinline__ void ln_stats(const float4 (&v)[kLnVec], int h, float eps, float *sh,
+                                         float &mean, float &rstd) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < kLnVec; ++i)
+    if (4 * (threadIdx.x + i * kLnThreads) < h) s += sum4(v[i]);
+  mean = block_sum<kLnWaves>(s, sh) / (float)h;
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < kLnVec; ++i)
+    if (4 * (threadIdx.x + i * kLnThreads) < h) {
+      const float a = v[i].x - mean, b = v[i].y - mean, c = v[i].z - mean, d = v[i].w - mean;
+      ss += (a * a + b * b) + (c * c + d * d);
+    }
+  const float var = block_sum<kLnWaves>(ss, sh) / (float)h;
+  rstd = 1.0f / sqrtf(var + eps);
+}
+
 template <typename TP>
-__global__ __launch_bounds__(256) void k_embed(const int *__restrict__ tokens,
-                                               const TP *__restrict__ embed,
-                                               const TP *__restrict__ g, const TP *__restrict__ b,
-                                               float *__restrict__ x, int h, int vocab, int do_ln,
-                                               float eps) {
-  __shared__ float sh[4];
+__device__ __forceinline__ float4 ln_apply(float4 x, float mean, float rstd, const TP *g,
+                                           const TP *b, int col) {
+  const float4 gg = Vec4<TP>::load(g + col), bb = Vec4<TP>::load(b + col);
+  return make_float4((x.x - mean) * rstd * gg.x + bb.x, (x.y - mean) * rstd * gg.y + bb.y,
+                     (x.z - mean) * rstd * gg.z + bb.z, (x.w - mean) * rstd * gg.w + bb.w);
+}
+
+// x[row] = E[token[row]] as float32, then optionally LayerNorm'd.
+template <typename TP>
+__global__ __launch_bounds__(kLnThreads) void k_embed(const int *__restrict__ tokens,
+                                                      const TP *__restrict__ embed,
+                                                      const TP *__restrict__ g,
+                                                      const TP *__restrict__ b,
+                                                      float *__restrict__ x, int h, int vocab,
+                                                      int do_ln, float eps) {
+  __shared__ float sh[kLnWaves];
   const int row = blockIdx.x;
   int tok = tokens[row];
   tok = tok < 0 ? 0 : (tok >= vocab ? vocab - 1 : tok);  // ids outside the vocabulary clamp
   const TP *e = embed + (size_t)tok * h;
   float *xr = x + (size_t)row * h;
-  if (!do_ln) {
-    for (int i = threadIdx.x; i < h; i += 256) xr[i] = to_f<TP>(e[i]);
-    return;
+  float4 v[kLnVec];
+#pragma unroll
+  for (int i = 0; i < kLnVec; ++i) {
+    const int col = 4 * (threadIdx.x + i * kLnThreads);
+    v[i] = col < h ? Vec4<TP>::load(e + col) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  float s = 0.f;
-  for (int i = threadIdx.x; i < h; i += 256) s += to_f<TP>(e[i]);
-  const float mean = block_sum<4>(s, sh) / (float)h;
-  float ss = 0.f;
-  for (int i = threadIdx.x; i < h; i += 256) {
-    const float dlt = to_f<TP>(e[i]) - mean;
-    ss += dlt * dlt;
+  float mean = 0.f, rstd = 1.f;
+  if (do_ln) ln_stats(v, h, eps, sh, mean, rstd);
+#pragma unroll
+  for (int i = 0; i < kLnVec; ++i) {
+    const int col = 4 * (threadIdx.x + i * kLnThreads);
+    if (col < h) Vec4<float>::store(xr + col, do_ln ? ln_apply<TP>(v[i], mean, rstd, g, b, col) : v[i]);
   }
-  const float var = block_sum<4>(ss, sh) / (float)h;
-  const float rstd = 1.0f / sqrtf(var + eps);
-  for (int i = threadIdx.x; i < h; i += 256)
-    xr[i] = (to_f<TP>(e[i]) - mean) * rstd * to_f<TP>(g[i]) + to_f<TP>(b[i]);
 }
 
 // out[row] = LN(x[row * in_step + in_off]) in the activation type; out_f32 (nullable)
 // receives the same values before rounding.
 template <typename TP, typename TA>
-__global__ __launch_bounds__(256) void k_layernorm(const float *__restrict__ x, int in_step,
-                                                   int in_off, const TP *__restrict__ g,
-                                                   const TP *__restrict__ b, TA *__restrict__ out,
-                                                   float *__restrict__ out_f32, int h, float eps) {
+__global__ __launch_bounds__(kLnThreads) void k_layernorm(const float *__restrict__ x,
+                                                          int in_step, int in_off,
+                                                          const TP *__restrict__ g,
+                                                          const TP *__restrict__ b,
+                                                          TA *__restrict__ out,
+                                                          float *__restrict__ out_f32, int h,
+                                                          float eps) {
+  __shared__ float sh[kLnWaves];
+  const int row = blockIdx.x;
+  const float *xr = x + ((size_t)row * in_step + in_off) * h;
+  float4 v[kLnVec];
+#pragma unroll
+  for (int i = 0; i < kLnVec; ++i) {
+    const int col = 4 * (threadIdx.x + i * kLnThreads);
+    v[i] = col < h ? Vec4<float>::load(xr + col) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  float mean, rstd;
+  ln_stats(v, h, eps, sh, mean, rstd);
+  TA *o = out + (size_t)row * h;
+  float *of = out_f32 ? out_f32 + (size_t)row * h : nullptr;
+#pragma unroll
+  for (int i = 0; i < kLnVec; ++i) {
+    const int col = 4 * (threadIdx.x + i * kLnThreads);
+    if (col < h) {
+      const float4 y = ln_apply<TP>(v[i], mean, rstd, g, b, col);
+      Vec4<TA>::store(o + col, y);
+      if (of) Vec4<float>::store(of + col, y);
+    }
+  }
+}
+
+// Rows longer than the register tile, or not a multiple of 4: re-read the row.
+template <typename TP, typename TA>
+__global__ __launch_bounds__(256) void k_layernorm_any(const float *__restrict__ x, int in_step,
+                                                       int in_off, const TP *__restrict__ g,
+                                                       const TP *__restrict__ b,
+                                                       TA *__restrict__ out,
+                                                       float *__restrict__ out_f32, int h,
+                                                       float eps) {
   __shared__ float sh[4];
   const int row = blockIdx.x;
   const float *xr = x + ((size_t)row * in_step + in_off) * h;
@@ -68,18 +155,63 @@ __global__ __launch_bounds__(256) void k_layernorm(const float *__restrict__ x, 
   }
 }
 
+template <typename TP>
+__global__ __launch_bounds__(256) void k_embed_any(const int *__restrict__ tokens,
+                                                   const TP *__restrict__ embed,
+                                                   const TP *__restrict__ g,
+                                                   const TP *__restrict__ b,
+                                                   float *__restrict__ x, int h, int vocab,
+                                                   int do_ln, float eps) {
+  __shared__ float sh[4];
+  const int row = blockIdx.x;
+  int tok = tokens[row];
+  tok = tok < 0 ? 0 : (tok >= vocab ? vocab - 1 : tok);
+  const TP *e = embed + (size_t)tok * h;
+  float *xr = x + (size_t)row * h;
+  float mean = 0.f, rstd = 1.f;
+  if (do_ln) {
+    float s = 0.f;
+    for (int i = threadIdx.x; i < h; i += 256) s += to_f<TP>(e[i]);
+    mean = block_sum<4>(s, sh) / (float)h;
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < h; i += 256) {
+      const float dlt = to_f<TP>(e[i]) - mean;
+      ss += dlt * dlt;
+    }
+    rstd = 1.0f / sqrtf(block_sum<4>(ss, sh) / (float)h + eps);
+  }
+  for (int i = threadIdx.x; i < h; i += 256) {
+    const float v = to_f<TP>(e[i]);
+    xr[i] = do_ln ? (v - mean) * rstd * to_f<TP>(g[i]) + to_f<TP>(b[i]) : v;
+  }
+}
+
+static bool fits_regs(int h) { return h % 4 == 0 && h <= kLnThreads * 4 * kLnVec; }
+
 hipError_t launch_embed(bool f32, const int *tokens, const void *embed, const void *g,
                         const void *b, float *x, int rows, int h, int vocab, int do_ln, float eps,
                         hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
-  if (f32)
-    hipLaunchKernelGGL(k_embed<float>, dim3(rows), dim3(256), 0, stream, tokens,
-                       (const float *)embed, (const float *)g, (const float *)b, x, h, vocab,
-                       do_ln, eps);
-  else
-    hipLaunchKernelGGL(k_embed<bf16_t>, dim3(rows), dim3(256), 0, stream, tokens,
-                       (const bf16_t *)embed, (const bf16_t *)g, (const bf16_t *)b, x, h, vocab,
-                       do_ln, eps);
+  const bool reg = fits_regs(h);
+  if (f32) {
+    if (reg)
+      hipLaunchKernelGGL(k_embed<float>, dim3(rows), dim3(kLnThreads), 0, stream, tokens,
+                         (const float *)embed, (const float *)g, (const float *)b, x, h, vocab,
+                         do_ln, eps);
+    else
+      hipLaunchKernelGGL(k_embed_any<float>, dim3(rows), dim3(256), 0, stream, tokens,
+                         (const float *)embed, (const float *)g, (const float *)b, x, h, vocab,
+                         do_ln, eps);
+  } else {
+    if (reg)
+      hipLaunchKernelGGL(k_embed<bf16_t>, dim3(rows), dim3(kLnThreads), 0, stream, tokens,
+                         (const bf16_t *)embed, (const bf16_t *)g, (const bf16_t *)b, x, h,
+                         vocab, do_ln, eps);
+    else
+      hipLaunchKernelGGL(k_embed_any<bf16_t>, dim3(rows), dim3(256), 0, stream, tokens,
+                         (const bf16_t *)embed, (const bf16_t *)g, (const bf16_t *)b, x, h,
+                         vocab, do_ln, eps);
+  }
   return hipGetLastError();
 }
 
@@ -87,13 +219,26 @@ hipError_t launch_layernorm(bool f32, const float *x, int in_step, int in_off, c
                             const void *b, void *out, float *out_f32, int rows, int h, float eps,
                             hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
-  if (f32)
-    hipLaunchKernelGGL((k_layernorm<float, float>), dim3(rows), dim3(256), 0, stream, x, in_step,
-                       in_off, (const float *)g, (const float *)b, (float *)out, out_f32, h, eps);
-  else
-    hipLaunchKernelGGL((k_layernorm<bf16_t, bf16_t>), dim3(rows), dim3(256), 0, stream, x,
-                       in_step, in_off, (const bf16_t *)g, (const bf16_t *)b, (bf16_t *)out,
-                       out_f32, h, eps);
+  const bool reg = fits_regs(h);
+  if (f32) {
+    if (reg)
+      hipLaunchKernelGGL((k_layernorm<float, float>), dim3(rows), dim3(kLnThreads), 0, stream, x,
+                         in_step, in_off, (const float *)g, (const float *)b, (float *)out,
+                         out_f32, h, eps);
+    else
+      hipLaunchKernelGGL((k_layernorm_any<float, float>), dim3(rows), dim3(256), 0, stream, x,
+                         in_step, in_off, (const float *)g, (const float *)b, (float *)out,
+                         out_f32, h, eps);
+  } else {
+    if (reg)
+      hipLaunchKernelGGL((k_layernorm<bf16_t, bf16_t>), dim3(rows), dim3(kLnThreads), 0, stream,
+                         x, in_step, in_off, (const bf16_t *)g, (const bf16_t *)b,
+                         (bf16_t *)out, out_f32, h, eps);
+    else
+      hipLaunchKernelGGL((k_layernorm_any<bf16_t, bf16_t>), dim3(rows), dim3(256), 0, stream, x,
+                         in_step, in_off, (const bf16_t *)g, (const bf16_t *)b, (bf16_t *)out,
+                         out_f32, h, eps);
+  }
   return hipGetLastError();
 }
 
