@@ -184,15 +184,25 @@ int alibi_masked_softmax(const void *d_scores, int32_t in_dtype, const int32_t *
 int kv_cache_append(const bloom_config *cfg, bloom_kv_cache *kv, int32_t layer, int32_t batch,
                     int32_t pos, const void *d_k, const void *d_v, int32_t n_new, void *stream);
 
-/* Launch timer for measurement: while enabled, the library brackets every launch of
- * its layer-linear (weight-streaming GEMV / GEMM) kernels with a pair of hipEvents on
- * the call's stream, for up to max_launches launches.  bloom_timer_read synchronises
- * on the last event and returns the summed launch time (ms), the number of timed
- * launches and the summed weight bytes those launches streamed; it then resets the
- * timer.  Events are created by bloom_timer_enable (not on the call path). */
+/* Launch timer for measurement.  While enabled (and not paused), the library brackets
+ * every launch of its linear-layer kernels (the weight-streaming GEMV / GEMM of the
+ * four layer linears and the LM head) with a pair of hipEvents on the call's stream,
+ * for up to max_launches launches, and tags each with its kernel class below.
+ * bloom_timer_enable creates the events (not on the call path) and clears old
+ * records; bloom_timer_read synchronises on the last event and returns, for one
+ * kernel class (or all, kernel_class = -1), the summed launch time in ms, the number
+ * of launches and the summed weight bytes (weights, biases, scales) they streamed;
+ * reading does not clear.  The events add a little time to every timed launch. */
+enum bloom_kernel_class {
+  BLOOM_KERNEL_GEMV = 2,        /* vector-ALU GEMV (batch <= 4) */
+  BLOOM_KERNEL_GEMV_MFMA = 3,   /* MFMA GEMV (batch <= 64, and LM heads up to 128 rows) */
+  BLOOM_KERNEL_GEMM_TILED = 4,  /* LDS-tiled MFMA GEMM (larger batches, prompt pass) */
+  BLOOM_KERNEL_GEMM_F32 = 5     /* float32 model */
+};
 int bloom_timer_enable(int32_t max_launches);
 int bloom_timer_disable(void);
-int bloom_timer_read(double *total_ms, int32_t *n_launches, double *weight_bytes);
+int bloom_timer_read(int32_t kernel_class, double *total_ms, int32_t *n_launches,
+                     double *weight_bytes);
 /* While an enabled timer is paused (paused != 0) launches are not recorded. */
 int bloom_timer_pause(int32_t paused);
 

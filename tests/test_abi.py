@@ -171,5 +171,6 @@ def test_softmax_validation_paths():
 
 def test_timer_read_without_launches():
     tb.bloom_timer_disable()
-    ms, n, b = tb.bloom_timer_read()
-    assert (ms, n, b) == (0.0, 0, 0.0)
+    for cls in (-1, 1, 2, 3):
+        ms, n, b = tb.bloom_timer_read(cls)
+        assert (ms, n, b) == (0.0, 0, 0.0)

@@ -61,15 +61,17 @@ def test_tiny_shape_low_precision(wdt, tol):
     _kv_check(run, v.oracle, 3, 8 + 11, 2 * tol)
 
 
-def test_bloom560m_truncated_ragged_batch():
+@pytest.mark.parametrize("valid", [(16, 11, 3), (16, 7), (5,)])
+def test_bloom560m_truncated_ragged_batch(valid):
     m = bi.BLOOM_560M.truncated(4)
     T, dw, cfg = upload(m)
-    prompt, valid = bi.prompts(m, 3, 16, (16, 11, 3))
+    B = len(valid)
+    prompt, valid = bi.prompts(m, B, 16, valid)
     run = run_gpu(cfg, dw, prompt, valid, 12)
     v = compare(m, T, prompt, valid, run, 1e-2, widen_embed=True)
-    print(f"560m L4 B3: hidden rel {v.hidden_rel:.2e}, exact ids {v.exact_frac:.3f}")
+    print(f"560m L4 B{B}: hidden rel {v.hidden_rel:.2e}, exact ids {v.exact_frac:.3f}")
     assert v.hidden_rel <= 1e-2 and v.tokens_ok
-    _kv_check(run, v.oracle, 3, 16 + 11, 2e-2)
+    _kv_check(run, v.oracle, B, 16 + 11, 2e-2)
 
 
 @pytest.mark.parametrize("batch, n_new", [(1, 100), (8, 30)])

@@ -80,7 +80,7 @@ def _load():
                                     _i32, vp]
     lib.bloom_timer_enable.argtypes = [_i32]
     lib.bloom_timer_disable.argtypes = []
-    lib.bloom_timer_read.argtypes = [P(ctypes.c_double), P(_i32), P(ctypes.c_double)]
+    lib.bloom_timer_read.argtypes = [_i32, P(ctypes.c_double), P(_i32), P(ctypes.c_double)]
     lib.bloom_timer_pause.argtypes = [_i32]
     for name in ("bloom_workspace_bytes", "bloom_prefill", "bloom_decode_step",
                  "alibi_masked_softmax", "kv_cache_append", "bloom_timer_enable",
@@ -175,10 +175,14 @@ def bloom_timer_pause(paused: bool):
     _check(lib.bloom_timer_pause(int(bool(paused))), "bloom_timer_pause")
 
 
-def bloom_timer_read():
+KERNEL_CLASSES = {2: "k_gemv_valu", 3: "k_gemv_mfma", 4: "k_gemm_tiled", 5: "k_gemm_f32"}
+
+
+def bloom_timer_read(kernel_class: int = -1):
+    """(total ms, launches, weight bytes) of the timed launches of one kernel class."""
     ms, n, b = ctypes.c_double(0), _i32(0), ctypes.c_double(0)
-    _check(lib.bloom_timer_read(ctypes.byref(ms), ctypes.byref(n), ctypes.byref(b)),
-           "bloom_timer_read")
+    _check(lib.bloom_timer_read(kernel_class, ctypes.byref(ms), ctypes.byref(n),
+                                ctypes.byref(b)), "bloom_timer_read")
     return ms.value, n.value, b.value
 
 

@@ -38,7 +38,7 @@ int wtype(const bloom_config *c) {
   return c->weight_dtype == BLOOM_F32 ? WT_F32 : (c->weight_dtype == BLOOM_BF16 ? WT_BF16 : WT_INT8);
 }
 int lm_blocks(const bloom_config *c) {
-  return c->weight_dtype == BLOOM_F32 ? (c->vocab + 255) / 256 : (c->vocab + 15) / 16;
+  return c->weight_dtype == BLOOM_F32 ? (c->vocab + 255) / 256 : lm_partial_stride(c->vocab);
 }
 
 WsPlan plan_ws(const bloom_config *c, int batch, int tokens_per_row) {
@@ -114,8 +114,9 @@ struct Timer {
   bool on = false;
   bool paused = false;
   std::vector<hipEvent_t> start, stop;
+  std::vector<int> cls;
+  std::vector<double> bytes;
   int used = 0;
-  double bytes = 0.0;
 } g_timer;
 
 void destroy_timer_events() {
@@ -123,24 +124,45 @@ void destroy_timer_events() {
   for (hipEvent_t e : g_timer.stop) (void)hipEventDestroy(e);
   g_timer.start.clear();
   g_timer.stop.clear();
+  g_timer.cls.clear();
+  g_timer.bytes.clear();
+  g_timer.used = 0;
+}
+
+int kernel_class(const LinearPlan &p) {
+  switch (p.kind) {
+    case LIN_VALU: return BLOOM_KERNEL_GEMV;
+    case LIN_GEMV: return BLOOM_KERNEL_GEMV_MFMA;
+    case LIN_TILED: return BLOOM_KERNEL_GEMM_TILED;
+    default: return BLOOM_KERNEL_GEMM_F32;
+  }
+}
+
+// Brackets one linear-layer launch (`launch` is a callable returning hipError_t) with
+// timer events when the timer is on.
+template <typename F>
+hipError_t timed(int cls, double wbytes, hipStream_t st, F &&launch) {
+  const bool on = g_timer.on && !g_timer.paused && g_timer.used < (int)g_timer.start.size();
+  if (on) {
+    hipError_t e = hipEventRecord(g_timer.start[g_timer.used], st);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t err = launch();
+  if (err != hipSuccess) return err;
+  if (on) {
+    err = hipEventRecord(g_timer.stop[g_timer.used], st);
+    if (err != hipSuccess) return err;
+    g_timer.cls[g_timer.used] = cls;
+    g_timer.bytes[g_timer.used] = wbytes;
+    g_timer.used++;
+  }
+  return hipSuccess;
 }
 
 hipError_t timed_linear(int wdt, const LinearPlan &p, const void *X, const void *W, float *part,
                         const EpiParams &ep, hipStream_t st, double wbytes) {
-  const bool timed = g_timer.on && !g_timer.paused && g_timer.used < (int)g_timer.start.size();
-  if (timed) {
-    hipError_t e = hipEventRecord(g_timer.start[g_timer.used], st);
-    if (e != hipSuccess) return e;
-  }
-  hipError_t err = launch_linear(wdt, p, X, W, part, ep, st);
-  if (err != hipSuccess) return err;
-  if (timed) {
-    err = hipEventRecord(g_timer.stop[g_timer.used], st);
-    if (err != hipSuccess) return err;
-    g_timer.used++;
-    g_timer.bytes += wbytes;
-  }
-  return hipSuccess;
+  return timed(kernel_class(p), wbytes, st,
+               [&] { return launch_linear(wdt, p, X, W, part, ep, st); });
 }
 
 // ---------------------------------------------------------------------------
@@ -234,11 +256,12 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
   }
 
   // final LayerNorm of each row's last position, then the tied LM head + argmax
+  const int nblk = wp.lm_blocks;
+  const int wdt_lm = f32 ? WT_F32 : WT_BF16;  // the embedding is never int8
+  const double lm_bytes = (double)c->vocab * h * pb;
   err = launch_layernorm(f32, x, tpr, tpr - 1, w->lnf_g, w->lnf_b, af, d_hidden, batch, h,
                          c->ln_eps, st);
   if (err != hipSuccess) return BLOOM_EHIP;
-  const int nblk = wp.lm_blocks;
-  const int wdt_lm = f32 ? WT_F32 : WT_BF16;  // the embedding is never int8
   for (int r0 = 0; r0 < batch; r0 += 128) {
     const int rows = std::min(128, batch - r0);
     EpiParams a{};
@@ -248,11 +271,12 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
     a.am_stride = nblk;
     const LinearPlan p_lm = plan_linear(wdt_lm, rows, c->vocab, h, true);
     err = timed_linear(wdt_lm, p_lm, (const char *)af + (size_t)r0 * h * act, w->embed, part, a,
-                       st, (double)c->vocab * h * pb);
+                       st, lm_bytes);
+    if (err != hipSuccess) return BLOOM_EHIP;
+    // this chunk's kernel wrote grid_x partials per row
+    err = launch_argmax_merge(a.am_val, a.am_idx, nblk, p_lm.grid_x, rows, d_next + r0, st);
     if (err != hipSuccess) return BLOOM_EHIP;
   }
-  err = launch_argmax_merge(amv, ami, nblk, nblk, batch, d_next, st);
-  if (err != hipSuccess) return BLOOM_EHIP;
   return BLOOM_OK;
 }
 
@@ -365,6 +389,8 @@ int bloom_timer_enable(int32_t max_launches) {
   destroy_timer_events();
   g_timer.start.resize(max_launches);
   g_timer.stop.resize(max_launches);
+  g_timer.cls.assign(max_launches, 0);
+  g_timer.bytes.assign(max_launches, 0.0);
   for (int i = 0; i < max_launches; ++i) {
     if (hipEventCreate(&g_timer.start[i]) != hipSuccess ||
         hipEventCreate(&g_timer.stop[i]) != hipSuccess) {
@@ -374,10 +400,14 @@ int bloom_timer_enable(int32_t max_launches) {
       return BLOOM_EHIP;
     }
   }
-  g_timer.used = 0;
-  g_timer.bytes = 0.0;
   g_timer.on = true;
   g_timer.paused = false;
+  return BLOOM_OK;
+}
+
+int bloom_timer_disable(void) {
+  g_timer.on = false;
+  destroy_timer_events();
   return BLOOM_OK;
 }
 
@@ -386,30 +416,25 @@ int bloom_timer_pause(int32_t paused) {
   return BLOOM_OK;
 }
 
-int bloom_timer_disable(void) {
-  g_timer.on = false;
-  destroy_timer_events();
-  g_timer.used = 0;
-  g_timer.bytes = 0.0;
-  return BLOOM_OK;
-}
-
-int bloom_timer_read(double *total_ms, int32_t *n_launches, double *weight_bytes) {
+int bloom_timer_read(int32_t kernel_class, double *total_ms, int32_t *n_launches,
+                     double *weight_bytes) {
   if (!total_ms || !n_launches || !weight_bytes) return BLOOM_EINVAL;
-  double total = 0.0;
+  double total = 0.0, bytes = 0.0;
+  int n = 0;
   if (g_timer.used > 0 && hipEventSynchronize(g_timer.stop[g_timer.used - 1]) != hipSuccess)
     return BLOOM_EHIP;
   for (int i = 0; i < g_timer.used; ++i) {
+    if (kernel_class >= 0 && g_timer.cls[i] != kernel_class) continue;
     float ms = 0.f;
     if (hipEventElapsedTime(&ms, g_timer.start[i], g_timer.stop[i]) != hipSuccess)
       return BLOOM_EHIP;
     total += ms;
+    bytes += g_timer.bytes[i];
+    ++n;
   }
   *total_ms = total;
-  *n_launches = g_timer.used;
-  *weight_bytes = g_timer.bytes;
-  g_timer.used = 0;
-  g_timer.bytes = 0.0;
+  *n_launches = n;
+  *weight_bytes = bytes;
   return BLOOM_OK;
 }
 

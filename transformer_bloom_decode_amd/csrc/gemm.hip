@@ -223,6 +223,160 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(const bf16_t *__restrict__ X,
 }
 
 // ---------------------------------------------------------------------------
+// decode GEMV on the vector ALU (M <= 4 activation rows)
+// ---------------------------------------------------------------------------
+// Each wave owns R consecutive weight rows over the full K.  Per step every lane
+// loads one 16-byte piece of each of its rows, so a wave load instruction covers
+// 1 KB of one row contiguously; the loads are non-temporal (streamed weights are
+// not kept in the caches that hold activations and the KV cache).  Weights are
+// widened to float32 in registers and multiplied by the matching activation values
+// with fmaf; each lane keeps R*M running sums, reduced across the wave at the end.
+// U steps are loaded ahead of the one being multiplied.
+template <typename TW> struct VOps;
+
+template <> struct VOps<bf16_t> {
+  static constexpr int kPerLane = 8;                      // elements per 16-byte piece
+  static __device__ __forceinline__ void widen(u32x4 w, float f[8]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) { f[2 * t] = lo_bf(w[t]); f[2 * t + 1] = hi_bf(w[t]); }
+  }
+};
+
+template <> struct VOps<int8_t> {
+  static constexpr int kPerLane = 16;
+  static __device__ __forceinline__ void widen(u32x4 w, float f[16]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) f[4 * t + b] = (float)(int)(int8_t)(w[t] >> (8 * b));
+  }
+};
+
+template <typename TW, typename TP, int MR, int R, int U>
+__global__ __launch_bounds__(256) void k_gemv_valu(const bf16_t *__restrict__ X,
+                                                   const TW *__restrict__ W, int M, int N, int K,
+                                                   EpiParams ep) {
+  using VO = VOps<TW>;
+  constexpr int E = VO::kPerLane;
+  constexpr int XP = E / 8;                               // 16-byte activation pieces per step
+  __shared__ float am_v[4][MR];
+  __shared__ int am_i[4][MR];
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int row0 = (blockIdx.x * 4 + wid) * R;
+  const TW *wr[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) wr[i] = W + (size_t)min(row0 + i, N - 1) * K;
+  const bf16_t *xr[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) xr[m] = X + (size_t)min(m, M - 1) * K;
+
+  float acc[R][MR];
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int m = 0; m < MR; ++m) acc[i][m] = 0.f;
+
+  const int step = 64 * E;                                // elements per wave step
+  const int nsteps = (K + step - 1) / step;
+  u32x4 cw[U][R], nw[U][R], cx[U][MR][XP], nx[U][MR][XP];
+
+  auto load = [&](int s0, u32x4(&w)[U][R], u32x4(&x)[U][MR][XP]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = (s0 + u) * step + lane * E;
+      const bool ok = (s0 + u) < nsteps && k < K;
+#pragma unroll
+      for (int i = 0; i < R; ++i)
+        w[u][i] = ok ? __builtin_nontemporal_load((const u32x4 *)(wr[i] + k)) : zero4();
+#pragma unroll
+      for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int p = 0; p < XP; ++p)
+          x[u][m][p] = ok ? *(const u32x4 *)(xr[m] + k + 8 * p) : zero4();
+    }
+  };
+
+  load(0, cw, cx);
+  for (int s0 = 0; s0 < nsteps; s0 += U) {
+    if (s0 + U < nsteps) load(s0 + U, nw, nx);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float xf[MR][E];
+#pragma unroll
+      for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int p = 0; p < XP; ++p)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            xf[m][8 * p + 2 * t] = lo_bf(cx[u][m][p][t]);
+            xf[m][8 * p + 2 * t + 1] = hi_bf(cx[u][m][p][t]);
+          }
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        float wf[E];
+        VO::widen(cw[u][i], wf);
+#pragma unroll
+        for (int m = 0; m < MR; ++m)
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[i][m] = fmaf(wf[e], xf[m][e], acc[i][m]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int i = 0; i < R; ++i) cw[u][i] = nw[u][i];
+#pragma unroll
+      for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int p = 0; p < XP; ++p) cx[u][m][p] = nx[u][m][p];
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int m = 0; m < MR; ++m) acc[i][m] = wave_sum(acc[i][m]);
+
+  if (ep.mode == EPI_ARGMAX) {
+    // best of this wave's R rows per activation row, then of the block's 4 waves
+    if (lane == 0) {
+#pragma unroll
+      for (int m = 0; m < MR; ++m) {
+        float bv = -INFINITY;
+        int bi = min(row0, N - 1);
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+          if (row0 + i < N) argmax_take(bv, bi, acc[i][m], row0 + i);
+        am_v[wid][m] = bv;
+        am_i[wid][m] = bi;
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x < MR && threadIdx.x < M) {
+      const int m = threadIdx.x;
+      float bv = am_v[0][m];
+      int bi = am_i[0][m];
+      for (int w = 1; w < 4; ++w) argmax_take(bv, bi, am_v[w][m], am_i[w][m]);
+      ep.am_val[(size_t)m * ep.am_stride + blockIdx.x] = bv;
+      ep.am_idx[(size_t)m * ep.am_stride + blockIdx.x] = bi;
+    }
+    return;
+  }
+  // lane l < R*MR finishes output (row0 + l / MR, activation row l % MR)
+  if (lane < R * MR) {
+    float v = 0.f;
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+      for (int m = 0; m < MR; ++m)
+        if (lane == i * MR + m) v = acc[i][m];
+    const int n = row0 + lane / MR, m = lane % MR;
+    if (n < N && m < M) epilogue<TP, bf16_t>(ep, m, n, v);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // LDS-tiled GEMM on MFMA (prompt pass)
 // ---------------------------------------------------------------------------
 constexpr int TBM = 128, TBN = 128, TBK = 64, TLD = TBK + 8;  // +8: stagger LDS rows
@@ -445,6 +599,13 @@ LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax) {
     return p;
   }
   const long cap = kPartialCapFloats;
+  if (M <= kValuMaxRows) {
+    p.kind = LIN_VALU;
+    p.mt = M <= 1 ? 1 : (M <= 2 ? 2 : 4);
+    p.grid_x = (N + 4 * kValuRows - 1) / (4 * kValuRows);
+    p.splits = 1;
+    return p;
+  }
   if (M <= 64 || argmax) {
     p.kind = LIN_GEMV;
     p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : (M <= 64 ? 4 : 8));
@@ -487,12 +648,31 @@ static void launch_gemv_t(const LinearPlan &p, const void *X, const void *W, flo
   }
 }
 
+template <typename TW, typename TP>
+static void launch_valu_t(const LinearPlan &p, const void *X, const void *W, const EpiParams &ep,
+                          hipStream_t st) {
+  const dim3 grid(p.grid_x), block(256);
+  const bf16_t *x = (const bf16_t *)X;
+  const TW *w = (const TW *)W;
+  constexpr int R = kValuRows;
+  switch (p.mt) {
+    case 1: hipLaunchKernelGGL((k_gemv_valu<TW, TP, 1, R, 4>), grid, block, 0, st, x, w, p.M, p.N, p.K, ep); break;
+    case 2: hipLaunchKernelGGL((k_gemv_valu<TW, TP, 2, R, 4>), grid, block, 0, st, x, w, p.M, p.N, p.K, ep); break;
+    default: hipLaunchKernelGGL((k_gemv_valu<TW, TP, 4, R, 2>), grid, block, 0, st, x, w, p.M, p.N, p.K, ep); break;
+  }
+}
+
 hipError_t launch_linear(int wdtype, const LinearPlan &p, const void *X, const void *W,
                          float *partial, const EpiParams &ep, hipStream_t st) {
   if (p.M <= 0) return hipSuccess;
   if (p.kind == LIN_F32) {
     hipLaunchKernelGGL(k_gemm_f32, dim3(p.grid_x, p.M), dim3(256), 0, st, (const float *)X,
                        (const float *)W, p.M, p.N, p.K, ep);
+    return hipGetLastError();
+  }
+  if (p.kind == LIN_VALU) {
+    if (wdtype == WT_BF16) launch_valu_t<bf16_t, bf16_t>(p, X, W, ep, st);
+    else launch_valu_t<int8_t, bf16_t>(p, X, W, ep, st);
     return hipGetLastError();
   }
   if (p.kind == LIN_GEMV) {
