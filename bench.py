@@ -25,7 +25,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor peak
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, vendor peak
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (no sparsity)
 
 
 def log(*a):
@@ -44,8 +45,23 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--no-kernel-timer", action="store_true",
-                    help="do not bracket GEMV launches with events")
+                    help="do not time the linear-layer launches")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run 5 device-to-device copies of 1 GiB (a known-size stream "
+                         "to scale hardware traffic counters against), then exit")
     return ap.parse_args()
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_copy": n, "copies": 5}), flush=True)
 
 
 def upload_weights(m, seed=0):
@@ -64,6 +80,30 @@ def upload_weights(m, seed=0):
     return tb.DeviceWeights(g, layers)
 
 
+def counted_traffic(kernel, workload, batch):
+    """HBM bytes per launch of `kernel` measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
+    (scaled by a plain-copy calibration), from the committed summary in profiles/; None
+    when there is no summary for this kernel and workload or the kernel source changed
+    since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel}__{workload}_b{batch}_decode.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("#", "|", "`")):
+            k, _, v = line.partition(":")
+            fields[k.strip()] = v.strip()
+    src = os.path.join(ROOT, "transformer_bloom_decode_amd", "csrc", "gemm.hip")
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if fields.get("kernel") != kernel or fields.get("gemm_hip_sha256_16") != digest:
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def step_bytes(m, B, P, n_new):
     """Algorithmic HBM bytes of one decode step averaged over the generation: every
     weight byte once (layers + tied LM head + LayerNorm/bias/scales) plus the KV cache
@@ -76,6 +116,16 @@ def step_bytes(m, B, P, n_new):
     kv_read = 2 * m.n_layer * B * m.n_head_local * T_avg * m.head_dim * act
     kv_write = 2 * m.n_layer * B * m.n_head_local * m.head_dim * act
     return weights + kv_read + kv_write, weights
+
+
+def prefill_flops(m, B, P):
+    """Flops of the prompt pass: the four linears on B*P rows, causal attention over P
+    keys, and the LM head on the last position of each row."""
+    params = m.qkv_rows * m.hidden + m.hidden * m.attn_width + 2 * m.ffn * m.hidden
+    lin = 2.0 * B * P * m.n_layer * params
+    attn = 4.0 * m.n_layer * B * m.n_head_local * m.head_dim * P * (P + 1) / 2
+    head = 2.0 * B * m.vocab * m.hidden
+    return lin + attn + head
 
 
 def cpu_baseline(m, B, P, n_new, budget_s):
@@ -140,6 +190,10 @@ def main():
               "has no multi-GPU path; tensor-parallel sharding is described, not built).",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import numpy as np
     import torch
@@ -229,7 +283,8 @@ def main():
             achieved = kd["gb_per_s"]
             roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                        "traffic": None, "kernel": name, "launches": kd["launches"],
+                        "traffic": counted_traffic(name, m.name, B), "kernel": name,
+                        "launches": kd["launches"],
                         "avg_launch_us": kd["avg_launch_us"],
                         "bytes_per_launch": kd["bytes_per_launch"]}
     ids_host = ids.cpu().numpy()
@@ -254,6 +309,10 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "tokens_per_s": round(B * n_new / (ms_per_step * 1e-3), 2),
         "prefill_ms": round(float(np.median(prefill_ms)), 3),
+        "prefill_tflops": round(prefill_flops(m, B, P) / (float(np.median(prefill_ms)) * 1e-3)
+                                / 1e12, 1),
+        "prefill_mfma_frac": round(prefill_flops(m, B, P) / (float(np.median(prefill_ms)) * 1e-3)
+                                   / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "decode_step_ms": round(dec_step_ms, 4),
         "decode_step_gb": round(sb / 1e9, 3),
         "decode_step_hbm_frac": round(sb / (dec_step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

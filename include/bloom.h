@@ -131,6 +131,9 @@ typedef struct bloom_kv_cache {
 /* Human-readable text for a status code. */
 const char *bloom_status_string(int status);
 
+/* Text of the HIP error behind the last BLOOM_EHIP returned on the calling thread. */
+const char *bloom_last_hip_error(void);
+
 /* Bytes of device workspace bloom_prefill / bloom_decode_step need for batches of up
  * to max_batch rows and prompts of up to max_prompt tokens.  Writes *bytes. */
 int bloom_workspace_bytes(const bloom_config *cfg, int32_t max_batch, int32_t max_prompt,
@@ -184,15 +187,16 @@ int alibi_masked_softmax(const void *d_scores, int32_t in_dtype, const int32_t *
 int kv_cache_append(const bloom_config *cfg, bloom_kv_cache *kv, int32_t layer, int32_t batch,
                     int32_t pos, const void *d_k, const void *d_v, int32_t n_new, void *stream);
 
-/* Launch timer for measurement.  While enabled (and not paused), the library brackets
- * every launch of its linear-layer kernels (the weight-streaming GEMV / GEMM of the
- * four layer linears and the LM head) with a pair of hipEvents on the call's stream,
- * for up to max_launches launches, and tags each with its kernel class below.
+/* Launch timer for measurement.  While enabled (and not paused), every launch of the
+ * library's linear-layer kernels (the weight-streaming GEMV / GEMM of the four layer
+ * linears and the LM head) is made with hipExtLaunchKernelGGL and a pair of hipEvents,
+ * which the kernel's dispatch packet itself timestamps, for up to max_launches
+ * launches; each is tagged with its kernel class below.
  * bloom_timer_enable creates the events (not on the call path) and clears old
  * records; bloom_timer_read synchronises on the last event and returns, for one
  * kernel class (or all, kernel_class = -1), the summed launch time in ms, the number
  * of launches and the summed weight bytes (weights, biases, scales) they streamed;
- * reading does not clear.  The events add a little time to every timed launch. */
+ * reading does not clear.  (A split-K reduction kernel is not included.) */
 enum bloom_kernel_class {
   BLOOM_KERNEL_GEMV = 2,        /* vector-ALU GEMV (batch <= 4) */
   BLOOM_KERNEL_GEMV_MFMA = 3,   /* MFMA GEMV (batch <= 64, and LM heads up to 128 rows) */

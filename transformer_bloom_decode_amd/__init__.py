@@ -57,10 +57,20 @@ class bloom_kv_cache(ctypes.Structure):
 class BloomError(RuntimeError):
     def __init__(self, code: int, where: str):
         self.code = code
-        super().__init__(f"{where}: {bloom_status_string(code)} ({code})")
+        msg = f"{where}: {bloom_status_string(code)} ({code})"
+        if code == BLOOM_EHIP:
+            msg += f": {lib.bloom_last_hip_error().decode()}"
+        super().__init__(msg)
 
 
 def _load():
+    # torch ships its own HIP runtime (libamdhip64.so.7 + libhsa-runtime64.so).  Loading
+    # torch first makes the dynamic loader bind this library's libamdhip64.so.7
+    # dependency to that same, already-loaded runtime; loading this library first
+    # would bring in a second HSA runtime next to torch's, which can fail to open the
+    # device.
+    import torch  # noqa: F401
+
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run transformer_bloom_decode_amd/build.py "
                           "(the HIP library is required: there is no CPU fallback)")
@@ -69,6 +79,8 @@ def _load():
     vp = _c_void_p
     lib.bloom_status_string.argtypes = [ctypes.c_int]
     lib.bloom_status_string.restype = ctypes.c_char_p
+    lib.bloom_last_hip_error.argtypes = []
+    lib.bloom_last_hip_error.restype = ctypes.c_char_p
     lib.bloom_workspace_bytes.argtypes = [P(bloom_config), _i32, _i32, P(ctypes.c_size_t)]
     lib.bloom_prefill.argtypes = [P(bloom_config), P(bloom_weights), P(bloom_kv_cache), _i32, _i32,
                                   vp, vp, vp, vp, vp, ctypes.c_size_t, vp]

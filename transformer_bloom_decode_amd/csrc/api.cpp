@@ -26,6 +26,19 @@ namespace {
 
 constexpr int kMaxLen = 8192;  // KV slots the attention kernel's LDS score row can hold
 
+// HIP error behind the last BLOOM_EHIP returned on this thread.
+thread_local hipError_t g_last_hip_error = hipSuccess;
+
+// hipGetLastError() reports the last error of *any* runtime call on the thread (e.g. a
+// hipErrorNotReady from an event query made by the caller's allocator), so each entry
+// point clears it before launching and checks only its own launches.
+void clear_stale_hip_error() { (void)hipGetLastError(); }
+
+int hip_fail(hipError_t e) {
+  g_last_hip_error = e;
+  return BLOOM_EHIP;
+}
+
 struct WsPlan {
   size_t x, xa, q, o, u, af, amv, ami, part, total;
   int lm_blocks;
@@ -138,20 +151,17 @@ int kernel_class(const LinearPlan &p) {
   }
 }
 
-// Brackets one linear-layer launch (`launch` is a callable returning hipError_t) with
-// timer events when the timer is on.
+// Times one linear-layer launch (`launch` is a callable returning hipError_t) when the
+// timer is on: its first kernel is launched with the timer's event pair attached.
 template <typename F>
 hipError_t timed(int cls, double wbytes, hipStream_t st, F &&launch) {
+  (void)st;
   const bool on = g_timer.on && !g_timer.paused && g_timer.used < (int)g_timer.start.size();
-  if (on) {
-    hipError_t e = hipEventRecord(g_timer.start[g_timer.used], st);
-    if (e != hipSuccess) return e;
-  }
+  if (on) g_launch_events = LaunchEvents{g_timer.start[g_timer.used], g_timer.stop[g_timer.used]};
   hipError_t err = launch();
+  g_launch_events = LaunchEvents{};
   if (err != hipSuccess) return err;
   if (on) {
-    err = hipEventRecord(g_timer.stop[g_timer.used], st);
-    if (err != hipSuccess) return err;
     g_timer.cls[g_timer.used] = cls;
     g_timer.bytes[g_timer.used] = wbytes;
     g_timer.used++;
@@ -196,7 +206,7 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
 
   hipError_t err = launch_embed(f32, d_tokens, w->embed, w->emb_ln_g, w->emb_ln_b, x, M, h,
                                 c->vocab, c->embed_ln, c->ln_eps, st);
-  if (err != hipSuccess) return BLOOM_EHIP;
+  if (err != hipSuccess) return hip_fail(err);
 
   const size_t layer_stride = (size_t)kv->max_batch * H * kv->max_len * d * act;
   const LinearPlan p_qkv = plan_linear(wdt, M, 3 * hd, h, false);
@@ -210,7 +220,7 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
     void *vc = (char *)kv->v + l * layer_stride;
 
     err = launch_layernorm(f32, x, 1, 0, L.ln1_g, L.ln1_b, xa, nullptr, M, h, c->ln_eps, st);
-    if (err != hipSuccess) return BLOOM_EHIP;
+    if (err != hipSuccess) return hip_fail(err);
 
     EpiParams e{};
     e.mode = EPI_QKV;
@@ -221,11 +231,11 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
     e.pos_base = pos_base; e.rows_per_seq = tpr;
     e.q_scale = 1.0f / sqrtf((float)d);
     err = timed_linear(wdt, p_qkv, xa, L.w_qkv, part, e, st, wbytes(3 * hd, h));
-    if (err != hipSuccess) return BLOOM_EHIP;
+    if (err != hipSuccess) return hip_fail(err);
 
     err = launch_attention(f32, q, kc, vc, d_valid, o, M, H, d, kv->max_len, c->n_head_total,
                            c->head_offset, tpr, pos_base, prompt_len, st);
-    if (err != hipSuccess) return BLOOM_EHIP;
+    if (err != hipSuccess) return hip_fail(err);
 
     EpiParams r{};
     r.mode = EPI_RESID;
@@ -233,10 +243,10 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
     r.scale = (const uint16_t *)L.s_dense;
     r.out = x; r.ld = h;
     err = timed_linear(wdt, p_dense, o, L.w_dense, part, r, st, wbytes(h, hd));
-    if (err != hipSuccess) return BLOOM_EHIP;
+    if (err != hipSuccess) return hip_fail(err);
 
     err = launch_layernorm(f32, x, 1, 0, L.ln2_g, L.ln2_b, xa, nullptr, M, h, c->ln_eps, st);
-    if (err != hipSuccess) return BLOOM_EHIP;
+    if (err != hipSuccess) return hip_fail(err);
 
     EpiParams g{};
     g.mode = EPI_GELU;
@@ -244,7 +254,7 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
     g.scale = (const uint16_t *)L.s_up;
     g.out = u; g.ld = F;
     err = timed_linear(wdt, p_up, xa, L.w_up, part, g, st, wbytes(F, h));
-    if (err != hipSuccess) return BLOOM_EHIP;
+    if (err != hipSuccess) return hip_fail(err);
 
     EpiParams dn{};
     dn.mode = EPI_RESID;
@@ -252,7 +262,7 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
     dn.scale = (const uint16_t *)L.s_down;
     dn.out = x; dn.ld = h;
     err = timed_linear(wdt, p_down, u, L.w_down, part, dn, st, wbytes(h, F));
-    if (err != hipSuccess) return BLOOM_EHIP;
+    if (err != hipSuccess) return hip_fail(err);
   }
 
   // final LayerNorm of each row's last position, then the tied LM head + argmax
@@ -261,7 +271,7 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
   const double lm_bytes = (double)c->vocab * h * pb;
   err = launch_layernorm(f32, x, tpr, tpr - 1, w->lnf_g, w->lnf_b, af, d_hidden, batch, h,
                          c->ln_eps, st);
-  if (err != hipSuccess) return BLOOM_EHIP;
+  if (err != hipSuccess) return hip_fail(err);
   for (int r0 = 0; r0 < batch; r0 += 128) {
     const int rows = std::min(128, batch - r0);
     EpiParams a{};
@@ -272,10 +282,10 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
     const LinearPlan p_lm = plan_linear(wdt_lm, rows, c->vocab, h, true);
     err = timed_linear(wdt_lm, p_lm, (const char *)af + (size_t)r0 * h * act, w->embed, part, a,
                        st, lm_bytes);
-    if (err != hipSuccess) return BLOOM_EHIP;
+    if (err != hipSuccess) return hip_fail(err);
     // this chunk's kernel wrote grid_x partials per row
     err = launch_argmax_merge(a.am_val, a.am_idx, nblk, p_lm.grid_x, rows, d_next + r0, st);
-    if (err != hipSuccess) return BLOOM_EHIP;
+    if (err != hipSuccess) return hip_fail(err);
   }
   return BLOOM_OK;
 }
@@ -295,6 +305,8 @@ const char *bloom_status_string(int s) {
     default: return "unknown status";
   }
 }
+
+const char *bloom_last_hip_error(void) { return hipGetErrorString(g_last_hip_error); }
 
 int bloom_workspace_bytes(const bloom_config *cfg, int32_t max_batch, int32_t max_prompt,
                           size_t *bytes) {
@@ -318,6 +330,7 @@ int bloom_prefill(const bloom_config *cfg, const bloom_weights *w, bloom_kv_cach
   if (batch == 0) return BLOOM_OK;
   if (!d_tokens || !d_valid_len || !d_next_tokens || !d_ws) return BLOOM_EINVAL;
   if (ws_bytes < plan_ws(cfg, batch, prompt_len).total) return BLOOM_EWORKSPACE;
+  clear_stale_hip_error();
   s = run_forward(cfg, w, kv, batch, prompt_len, 0, prompt_len, d_tokens, d_valid_len,
                   d_next_tokens, d_hidden_out, (char *)d_ws, (hipStream_t)stream);
   if (s == BLOOM_OK) {
@@ -341,6 +354,7 @@ int bloom_decode_step(const bloom_config *cfg, const bloom_weights *w, bloom_kv_
   if (batch == 0) return BLOOM_OK;
   if (!d_tokens || !d_valid_len || !d_next_tokens || !d_ws) return BLOOM_EINVAL;
   if (ws_bytes < plan_ws(cfg, batch, 1).total) return BLOOM_EWORKSPACE;
+  clear_stale_hip_error();
   s = run_forward(cfg, w, kv, batch, 1, kv->len, kv->prompt_len, d_tokens, d_valid_len,
                   d_next_tokens, d_hidden_out, (char *)d_ws, (hipStream_t)stream);
   if (s == BLOOM_OK) kv->len += 1;
@@ -357,10 +371,11 @@ int alibi_masked_softmax(const void *d_scores, int32_t in_dtype, const int32_t *
     return BLOOM_EDTYPE;
   if ((long)B * H * Q == 0 || K == 0) return BLOOM_OK;
   if (!d_scores || !d_valid_len || !d_probs) return BLOOM_EINVAL;
+  clear_stale_hip_error();
   hipError_t err = launch_alibi_softmax(d_scores, in_dtype == BLOOM_BF16, d_valid_len, d_probs,
                                         out_dtype == BLOOM_BF16, B, H, Q, K, n_head_total,
                                         head_offset, (hipStream_t)stream);
-  return err == hipSuccess ? BLOOM_OK : BLOOM_EHIP;
+  return err == hipSuccess ? BLOOM_OK : hip_fail(err);
 }
 
 int kv_cache_append(const bloom_config *cfg, bloom_kv_cache *kv, int32_t layer, int32_t batch,
@@ -373,6 +388,7 @@ int kv_cache_append(const bloom_config *cfg, bloom_kv_cache *kv, int32_t layer, 
   if (batch > kv->max_batch || (long)pos + n_new > kv->max_len) return BLOOM_ECAPACITY;
   if (batch == 0 || n_new == 0) return BLOOM_OK;
   if (!d_k || !d_v) return BLOOM_EINVAL;
+  clear_stale_hip_error();
   const size_t act = act_bytes(cfg);
   const size_t layer_stride =
       (size_t)kv->max_batch * cfg->n_head_local * kv->max_len * cfg->head_dim * act;
@@ -381,7 +397,7 @@ int kv_cache_append(const bloom_config *cfg, bloom_kv_cache *kv, int32_t layer, 
                                     (char *)kv->v + layer * layer_stride, batch,
                                     cfg->n_head_local, n_new, cfg->head_dim, kv->max_len, pos,
                                     (hipStream_t)stream);
-  return err == hipSuccess ? BLOOM_OK : BLOOM_EHIP;
+  return err == hipSuccess ? BLOOM_OK : hip_fail(err);
 }
 
 int bloom_timer_enable(int32_t max_launches) {

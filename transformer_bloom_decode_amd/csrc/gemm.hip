@@ -28,6 +28,8 @@
 
 namespace bl {
 
+thread_local LaunchEvents g_launch_events;
+
 __device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
 
 // two signed bytes of w (selected by the byte offset) -> two bf16 in one dword (exact)
@@ -641,10 +643,10 @@ static void launch_gemv_t(const LinearPlan &p, const void *X, const void *W, flo
   const bf16_t *x = (const bf16_t *)X;
   const TW *w = (const TW *)W;
   switch (p.mt) {
-    case 1: hipLaunchKernelGGL((k_gemv_mfma<TW, TP, 1, 4>), grid, block, 0, st, x, w, p.M, p.N, p.K, partial, ep); break;
-    case 2: hipLaunchKernelGGL((k_gemv_mfma<TW, TP, 2, 2>), grid, block, 0, st, x, w, p.M, p.N, p.K, partial, ep); break;
-    case 4: hipLaunchKernelGGL((k_gemv_mfma<TW, TP, 4, 2>), grid, block, 0, st, x, w, p.M, p.N, p.K, partial, ep); break;
-    default: hipLaunchKernelGGL((k_gemv_mfma<TW, TP, 8, 1>), grid, block, 0, st, x, w, p.M, p.N, p.K, partial, ep); break;
+    case 1: BL_LAUNCH((k_gemv_mfma<TW, TP, 1, 4>), grid, block, 0, st, x, w, p.M, p.N, p.K, partial, ep); break;
+    case 2: BL_LAUNCH((k_gemv_mfma<TW, TP, 2, 2>), grid, block, 0, st, x, w, p.M, p.N, p.K, partial, ep); break;
+    case 4: BL_LAUNCH((k_gemv_mfma<TW, TP, 4, 2>), grid, block, 0, st, x, w, p.M, p.N, p.K, partial, ep); break;
+    default: BL_LAUNCH((k_gemv_mfma<TW, TP, 8, 1>), grid, block, 0, st, x, w, p.M, p.N, p.K, partial, ep); break;
   }
 }
 
@@ -656,9 +658,9 @@ static void launch_valu_t(const LinearPlan &p, const void *X, const void *W, con
   const TW *w = (const TW *)W;
   constexpr int R = kValuRows;
   switch (p.mt) {
-    case 1: hipLaunchKernelGGL((k_gemv_valu<TW, TP, 1, R, 4>), grid, block, 0, st, x, w, p.M, p.N, p.K, ep); break;
-    case 2: hipLaunchKernelGGL((k_gemv_valu<TW, TP, 2, R, 4>), grid, block, 0, st, x, w, p.M, p.N, p.K, ep); break;
-    default: hipLaunchKernelGGL((k_gemv_valu<TW, TP, 4, R, 2>), grid, block, 0, st, x, w, p.M, p.N, p.K, ep); break;
+    case 1: BL_LAUNCH((k_gemv_valu<TW, TP, 1, R, 4>), grid, block, 0, st, x, w, p.M, p.N, p.K, ep); break;
+    case 2: BL_LAUNCH((k_gemv_valu<TW, TP, 2, R, 4>), grid, block, 0, st, x, w, p.M, p.N, p.K, ep); break;
+    default: BL_LAUNCH((k_gemv_valu<TW, TP, 4, R, 2>), grid, block, 0, st, x, w, p.M, p.N, p.K, ep); break;
   }
 }
 
@@ -666,7 +668,7 @@ hipError_t launch_linear(int wdtype, const LinearPlan &p, const void *X, const v
                          float *partial, const EpiParams &ep, hipStream_t st) {
   if (p.M <= 0) return hipSuccess;
   if (p.kind == LIN_F32) {
-    hipLaunchKernelGGL(k_gemm_f32, dim3(p.grid_x, p.M), dim3(256), 0, st, (const float *)X,
+    BL_LAUNCH(k_gemm_f32, dim3(p.grid_x, p.M), dim3(256), 0, st, (const float *)X,
                        (const float *)W, p.M, p.N, p.K, ep);
     return hipGetLastError();
   }
@@ -681,16 +683,16 @@ hipError_t launch_linear(int wdtype, const LinearPlan &p, const void *X, const v
   } else {
     const dim3 grid(p.grid_x, p.grid_y, p.splits);
     if (wdtype == WT_BF16)
-      hipLaunchKernelGGL((k_gemm_tiled<bf16_t, bf16_t>), grid, dim3(256), 0, st,
+      BL_LAUNCH((k_gemm_tiled<bf16_t, bf16_t>), grid, dim3(256), 0, st,
                          (const bf16_t *)X, (const bf16_t *)W, p.M, p.N, p.K, partial, ep);
     else
-      hipLaunchKernelGGL((k_gemm_tiled<int8_t, bf16_t>), grid, dim3(256), 0, st,
+      BL_LAUNCH((k_gemm_tiled<int8_t, bf16_t>), grid, dim3(256), 0, st,
                          (const bf16_t *)X, (const int8_t *)W, p.M, p.N, p.K, partial, ep);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || p.splits <= 1) return err;
   const size_t MN = (size_t)p.M * p.N;
-  hipLaunchKernelGGL((k_splitk_epilogue<bf16_t, bf16_t>), dim3((unsigned)((MN + 255) / 256)),
+  BL_LAUNCH((k_splitk_epilogue<bf16_t, bf16_t>), dim3((unsigned)((MN + 255) / 256)),
                      dim3(256), 0, st, partial, p.splits, p.M, p.N, ep);
   return hipGetLastError();
 }

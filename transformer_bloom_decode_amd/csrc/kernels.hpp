@@ -1,11 +1,32 @@
 // Host-side launch entry points of the gfx950 kernels (used by the C ABI layer).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace bl {
+
+// Events for the launch timer.  When set, the next BL_LAUNCH goes through
+// hipExtLaunchKernelGGL, whose start/stop events are timestamped by the kernel's own
+// dispatch packet (the same timestamps a kernel-trace profiler reads, with no extra
+// marker packets in the stream), and the events are then cleared.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+extern thread_local LaunchEvents g_launch_events;
+
+#define BL_LAUNCH(kernel, grid, block, shmem, stream, ...)                                    \
+  do {                                                                                       \
+    if (::bl::g_launch_events.start) {                                                       \
+      hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, ::bl::g_launch_events.start, \
+                            ::bl::g_launch_events.stop, 0, __VA_ARGS__);                     \
+      ::bl::g_launch_events = ::bl::LaunchEvents{};                                         \
+    } else {                                                                                 \
+      hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);                   \
+    }                                                                                        \
+  } while (0)
 
 struct EpiParams;
 
