@@ -120,7 +120,7 @@ typedef struct bloom_weights {
  * bloom_prefill sets prompt_len and len = prompt_len; bloom_decode_step writes slot
  * len and then increments it.  Slot j holds absolute position j of every row (left
  * padding slots are written but never attended).  A caller may reset len to 0.
- * max_len is at most 8192 (one attention row of scores is held in LDS). */
+ * max_len is at most 2^20. */
 typedef struct bloom_kv_cache {
   void *k, *v;
   int32_t max_batch, max_len;

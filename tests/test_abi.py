@@ -143,7 +143,7 @@ def test_decode_validation_paths():
     assert f.kv.len == 20
     f.kv.len = 4                                                  # len < prompt_len
     assert _decode(f) == tb.BLOOM_EINVAL
-    f.kv.max_len = 9000                                           # beyond the supported 8192
+    f.kv.max_len = (1 << 20) + 1                                  # beyond the supported 2^20
     f.kv.len = 20
     assert _decode(f) == tb.BLOOM_EINVAL
 

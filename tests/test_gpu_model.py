@@ -122,3 +122,17 @@ def test_bloom560m_wide_batch_uses_tiled_and_wide_gemv():
     v = compare(m, T, prompt, valid, run, 1e-2, widen_embed=True)
     print(f"560m L2 B72: hidden rel {v.hidden_rel:.2e}, exact ids {v.exact_frac:.3f}")
     assert v.hidden_rel <= 1e-2 and v.tokens_ok
+
+
+def test_long_rows_cross_attention_batches():
+    """head_dim 128 and up to 160 visible keys: more keys than one batch of the attention
+    kernel (16 lane groups x 8 keys), so the running-max rescale across batches runs."""
+    m = dataclasses.replace(bi.BLOOM_560M, name="d128", n_layer=1, hidden=256, n_head_total=2,
+                            n_head_local=2, head_dim=128, ffn=1024, vocab=512)
+    T, dw, cfg = upload(m, seed=21)
+    prompt, valid = bi.prompts(m, 2, 100, (100, 37), seed=22)
+    run = run_gpu(cfg, dw, prompt, valid, 60)
+    v = compare(m, T, prompt, valid, run, 1e-2)
+    print(f"d128 L1 T<=160: hidden rel {v.hidden_rel:.2e}, exact ids {v.exact_frac:.3f}")
+    assert v.hidden_rel <= 1e-2 and v.tokens_ok
+    _kv_check(run, v.oracle, 2, 100 + 59, 2e-2)

@@ -24,7 +24,7 @@ using namespace bl;
 
 namespace {
 
-constexpr int kMaxLen = 8192;  // KV slots the attention kernel's LDS score row can hold
+constexpr int kMaxLen = 1 << 20;  // KV slots per row (positions are int32 throughout)
 
 // HIP error behind the last BLOOM_EHIP returned on this thread.
 thread_local hipError_t g_last_hip_error = hipSuccess;

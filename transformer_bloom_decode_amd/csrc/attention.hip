@@ -5,12 +5,16 @@
 // decode step: rows_per_seq = 1, pos_base = current length; the prompt pass:
 // rows_per_seq = prompt length, pos_base = 0).  Keys j in [pad_b, qpos] are visible,
 // pad_b = prompt_len - valid_len[b] (left padding).  Steps, all in float32:
-//   1. s_j = q . k_j + slope_h * (j - qpos)   (q already carries 1/sqrt(d); keys read
-//      as 16-byte pieces, d/8 lanes per key, partial dots summed across those lanes)
-//   2. masked softmax over the visible keys only (block max, exp, block sum) --
-//      masked keys are never touched, i.e. they get probability exactly 0
-//   3. o = sum_j p_j v_j, per lane group over its keys, then summed over the groups
-//      in LDS in a fixed order.
+//   1. s_j = q . k_j + slope_h * (j - qpos)   (q already carries 1/sqrt(d); keys and
+//      values read as 16-byte pieces, d/8 lanes per key, partial dots summed across
+//      those lanes; all K and V loads of a batch of keys are issued together)
+//   2. softmax over the visible keys only -- masked keys are never touched, i.e. they
+//      get probability exactly 0.  Within a batch: block max, exp, running sum; across
+//      batches (rows longer than one batch) the running sum and the P.V accumulators
+//      are rescaled by exp(old max - new max), the usual online form of the same
+//      softmax.
+//   3. o = (sum_j p_j v_j) / sum_j p_j, per lane group over its keys, then summed over
+//      the groups in LDS in a fixed order.
 // A query with no visible key (a left-pad position of the prompt) gets o = 0.
 // ("Hugging Face BLOOM Inference Optimization", Custom CUDA Kernels and Hardware
 // Acceleration, for the fused mask + float32 softmax; "DeepSpeed Inference ...",
@@ -35,7 +39,30 @@ template <> struct KVLoad8<float> {
   }
 };
 
-constexpr int kKeysPerBatch = 4;  // keys each lane group loads before using any of them
+// Raw 8-element pieces of a key / value row as loaded (bf16: one 16-byte load).
+template <typename TA> struct KVRaw;
+template <> struct KVRaw<bf16_t> {
+  u32x4 a;
+  __device__ __forceinline__ void load(const bf16_t *p) { a = *(const u32x4 *)p; }
+  __device__ __forceinline__ float get(int t) const {
+    return (t & 1) ? hi_bf(a[t >> 1]) : lo_bf(a[t >> 1]);
+  }
+};
+template <> struct KVRaw<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float *p) {
+    a = *(const float4 *)p;
+    b = *(const float4 *)(p + 4);
+  }
+  __device__ __forceinline__ float get(int t) const {
+    const float4 &v = t < 4 ? a : b;
+    switch (t & 3) { case 0: return v.x; case 1: return v.y; case 2: return v.z; default: return v.w; }
+  }
+};
+
+// Keys per lane group per batch: all K and V loads of a batch are issued together.
+template <typename TA> struct KeysPerBatch { static constexpr int value = 8; };
+template <> struct KeysPerBatch<float> { static constexpr int value = 4; };
 
 template <typename TA>
 __global__ __launch_bounds__(256) void k_attention(const float *__restrict__ q,
@@ -45,7 +72,8 @@ __global__ __launch_bounds__(256) void k_attention(const float *__restrict__ q,
                                                    TA *__restrict__ o, int H, int d, int max_len,
                                                    int n_total, int head_off, int rows_per_seq,
                                                    int pos_base, int prompt_len) {
-  extern __shared__ float smem[];   // [max_len] scores, then [256 / (d/8)][d] P.V partials
+  constexpr int KB = KeysPerBatch<TA>::value;
+  __shared__ float pv[256 * 8];     // [G][d] per-group P.V partials
   __shared__ float red[4];
   const int m = blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x;
@@ -65,8 +93,6 @@ __global__ __launch_bounds__(256) void k_attention(const float *__restrict__ q,
   const TA *kb = kc + head_base + (size_t)first * d;
   const TA *vb = vc + head_base + (size_t)first * d;
   const float *qr = q + ((size_t)m * H + h) * d;
-  float *sc = smem;
-  float *pv = smem + max_len;
 
   // lane group g (L = d/8 lanes) handles keys j = g (mod G); lane `sub` owns dims
   // [8 sub, 8 sub + 8) of each of them
@@ -77,62 +103,57 @@ __global__ __launch_bounds__(256) void k_attention(const float *__restrict__ q,
 #pragma unroll
   for (int t = 0; t < 8; ++t) qv[t] = qr[8 * sub + t];
 
-  // 1. scores s_j = q.k_j + slope * (j - qpos)
-  for (int j0 = 0; j0 < T; j0 += G * kKeysPerBatch) {
-    float kv[kKeysPerBatch][8];
+  // Online softmax over batches of G*KB keys (one batch when T <= G*KB): running
+  // maximum mrun (block-uniform), per-thread running sum and P.V accumulators, all
+  // rescaled by exp(mrun_old - mrun_new) when the maximum grows.
+  float mrun = -INFINITY, lsum = 0.f;
+  float acc[8];
 #pragma unroll
-    for (int u = 0; u < kKeysPerBatch; ++u) {
+  for (int t = 0; t < 8; ++t) acc[t] = 0.f;
+  for (int j0 = 0; j0 < T; j0 += G * KB) {
+    KVRaw<TA> kr[KB], vr[KB];
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
       const int jj = j0 + u * G + g;
-      if (jj < T) KVLoad8<TA>::load(kb + (size_t)jj * d + 8 * sub, kv[u]);
+      if (jj < T) {
+        kr[u].load(kb + (size_t)jj * d + 8 * sub);
+        vr[u].load(vb + (size_t)jj * d + 8 * sub);
+      }
     }
+    // scores s_j = q.k_j + slope * (j - qpos), summed across the group's L lanes
+    float sc[KB];
+    float bmax = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < kKeysPerBatch; ++u) {
+    for (int u = 0; u < KB; ++u) {
       const int jj = j0 + u * G + g;
       float dot = 0.f;
       if (jj < T) {
 #pragma unroll
-        for (int t = 0; t < 8; ++t) dot = fmaf(qv[t], kv[u][t], dot);
+        for (int t = 0; t < 8; ++t) dot = fmaf(qv[t], kr[u].get(t), dot);
       }
       for (int off = L >> 1; off > 0; off >>= 1) dot += __shfl_xor(dot, off, 64);
-      if (jj < T && sub == 0) sc[jj] = dot + slope * (float)(first + jj - qpos);
+      sc[u] = jj < T ? dot + slope * (float)(first + jj - qpos) : -INFINITY;
+      bmax = fmaxf(bmax, sc[u]);
     }
-  }
-  __syncthreads();
-
-  // 2. softmax over the T visible keys (masked keys are simply never visited)
-  float mx = -INFINITY;
-  for (int j = tid; j < T; j += 256) mx = fmaxf(mx, sc[j]);
-  mx = block_max<4>(mx, red);
-  float sum = 0.f;
-  for (int j = tid; j < T; j += 256) {
-    const float e = __expf(sc[j] - mx);
-    sc[j] = e;
-    sum += e;
-  }
-  sum = block_sum<4>(sum, red);   // its barriers also publish sc[] to every thread
-  const float inv = 1.0f / sum;
-
-  // 3. o = sum_j p_j v_j: per-group partial sums, then a fixed-order sum over groups
-  float acc[8];
+    const float mnew = fmaxf(mrun, block_max<4>(bmax, red));
+    const float alpha = __expf(mrun - mnew);      // 0 on the first batch
+    lsum *= alpha;
 #pragma unroll
-  for (int t = 0; t < 8; ++t) acc[t] = 0.f;
-  for (int j0 = 0; j0 < T; j0 += G * kKeysPerBatch) {
-    float vv[kKeysPerBatch][8];
+    for (int t = 0; t < 8; ++t) acc[t] *= alpha;
 #pragma unroll
-    for (int u = 0; u < kKeysPerBatch; ++u) {
-      const int jj = j0 + u * G + g;
-      if (jj < T) KVLoad8<TA>::load(vb + (size_t)jj * d + 8 * sub, vv[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < kKeysPerBatch; ++u) {
+    for (int u = 0; u < KB; ++u) {
       const int jj = j0 + u * G + g;
       if (jj < T) {
-        const float p = sc[jj];
+        const float p = __expf(sc[u] - mnew);
+        if (sub == 0) lsum += p;                  // each key counted once per group
 #pragma unroll
-        for (int t = 0; t < 8; ++t) acc[t] = fmaf(p, vv[u][t], acc[t]);
+        for (int t = 0; t < 8; ++t) acc[t] = fmaf(p, vr[u].get(t), acc[t]);
       }
     }
+    mrun = mnew;
   }
+  const float inv = 1.0f / block_sum<4>(lsum, red);
+
 #pragma unroll
   for (int t = 0; t < 8; ++t) pv[g * d + 8 * sub + t] = acc[t];
   __syncthreads();
@@ -149,13 +170,12 @@ hipError_t launch_attention(bool f32, const float *q, const void *kc, const void
                             int prompt_len, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
   const dim3 grid(rows, H), block(256);
-  const size_t shmem = ((size_t)max_len + 256 * 8) * sizeof(float);
   if (f32)
-    hipLaunchKernelGGL(k_attention<float>, grid, block, shmem, st, q, (const float *)kc,
+    hipLaunchKernelGGL(k_attention<float>, grid, block, 0, st, q, (const float *)kc,
                        (const float *)vc, valid_len, (float *)o, H, d, max_len, n_total,
                        head_off, rows_per_seq, pos_base, prompt_len);
   else
-    hipLaunchKernelGGL(k_attention<bf16_t>, grid, block, shmem, st, q, (const bf16_t *)kc,
+    hipLaunchKernelGGL(k_attention<bf16_t>, grid, block, 0, st, q, (const bf16_t *)kc,
                        (const bf16_t *)vc, valid_len, (bf16_t *)o, H, d, max_len, n_total,
                        head_off, rows_per_seq, pos_base, prompt_len);
   return hipGetLastError();
