@@ -23,6 +23,8 @@
 // The k index carried by each MFMA operand element may be any bijection of the chunk,
 // as long as the weight and the activation operand use the same one; the one used
 // here keeps each lane's weight loads 16 bytes wide and contiguous.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -254,7 +256,11 @@ template <> struct VOps<int8_t> {
   }
 };
 
-template <typename TW, typename TP, int MR, int R, int U>
+// DB: double-buffered (the next U pieces per row are issued before the current ones
+// are used) or single-buffered (U pieces per row issued at once, then used; with U >=
+// the row's pieces, a wave issues its whole row in one go, which keeps the most bytes
+// in flight when the grid is too small to fill every wave slot).
+template <typename TW, typename TP, int MR, int R, int U, bool DB>
 __global__ __launch_bounds__(256) void k_gemv_valu(const bf16_t *__restrict__ X,
                                                    const TW *__restrict__ W, int M, int N, int K,
                                                    EpiParams ep) {
@@ -281,7 +287,7 @@ __global__ __launch_bounds__(256) void k_gemv_valu(const bf16_t *__restrict__ X,
 
   const int step = 64 * E;                                // elements per wave step
   const int nsteps = (K + step - 1) / step;
-  u32x4 cw[U][R], nw[U][R], cx[U][MR][XP], nx[U][MR][XP];
+  u32x4 cw[U][R], cx[U][MR][XP];
 
   auto load = [&](int s0, u32x4(&w)[U][R], u32x4(&x)[U][MR][XP]) {
 #pragma unroll
@@ -299,9 +305,7 @@ __global__ __launch_bounds__(256) void k_gemv_valu(const bf16_t *__restrict__ X,
     }
   };
 
-  load(0, cw, cx);
-  for (int s0 = 0; s0 < nsteps; s0 += U) {
-    if (s0 + U < nsteps) load(s0 + U, nw, nx);
+  auto compute = [&]() {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float xf[MR][E];
@@ -324,14 +328,28 @@ __global__ __launch_bounds__(256) void k_gemv_valu(const bf16_t *__restrict__ X,
           for (int e = 0; e < E; ++e) acc[i][m] = fmaf(wf[e], xf[m][e], acc[i][m]);
       }
     }
+  };
+
+  if constexpr (DB) {
+    u32x4 nw[U][R], nx[U][MR][XP];
+    load(0, cw, cx);
+    for (int s0 = 0; s0 < nsteps; s0 += U) {
+      if (s0 + U < nsteps) load(s0 + U, nw, nx);
+      compute();
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+      for (int u = 0; u < U; ++u) {
 #pragma unroll
-      for (int i = 0; i < R; ++i) cw[u][i] = nw[u][i];
+        for (int i = 0; i < R; ++i) cw[u][i] = nw[u][i];
 #pragma unroll
-      for (int m = 0; m < MR; ++m)
+        for (int m = 0; m < MR; ++m)
 #pragma unroll
-        for (int p = 0; p < XP; ++p) cx[u][m][p] = nx[u][m][p];
+          for (int p = 0; p < XP; ++p) cx[u][m][p] = nx[u][m][p];
+      }
+    }
+  } else {
+    for (int s0 = 0; s0 < nsteps; s0 += U) {
+      load(s0, cw, cx);
+      compute();
     }
   }
 
@@ -604,7 +622,22 @@ LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax) {
   if (M <= kValuMaxRows) {
     p.kind = LIN_VALU;
     p.mt = M <= 1 ? 1 : (M <= 2 ? 2 : 4);
-    p.grid_x = (N + 4 * kValuRows - 1) / (4 * kValuRows);
+    // Default: 2 rows per wave, 4 pieces per row double-buffered (8 KB in flight per
+    // wave); enough when the grid fills every wave slot (LM head) or rows are short.
+    // Batch-1 bf16 linears with long rows and grids that leave wave slots empty issue
+    // a wave's whole row at once instead (14-28 KB in flight per wave): measured on
+    // MI355X, QKV 5376 x 14336 5.15 -> 5.88 TB/s, up 7168 x 14336 5.75 -> 6.47,
+    // down 14336 x 7168 6.39 -> 6.60.
+    p.vr = 2;
+    p.vu = p.mt == 4 ? 2 : 4;
+    p.vdb = true;
+    const int pieces = (K + 511) / 512;  // 1 KB wave loads of bf16
+    if (p.mt == 1 && wdtype == WT_BF16 && N < 65536 && pieces > 4 && pieces <= 28) {
+      p.vr = 1;
+      p.vu = pieces <= 16 ? 16 : 28;
+      p.vdb = false;
+    }
+    p.grid_x = (N + 4 * p.vr - 1) / (4 * p.vr);
     p.splits = 1;
     return p;
   }
@@ -656,11 +689,19 @@ static void launch_valu_t(const LinearPlan &p, const void *X, const void *W, con
   const dim3 grid(p.grid_x), block(256);
   const bf16_t *x = (const bf16_t *)X;
   const TW *w = (const TW *)W;
-  constexpr int R = kValuRows;
+  if constexpr (std::is_same<TW, bf16_t>::value) {
+    if (p.vr == 1 && p.mt == 1 && !p.vdb) {
+      if (p.vu == 16)
+        BL_LAUNCH((k_gemv_valu<TW, TP, 1, 1, 16, false>), grid, block, 0, st, x, w, p.M, p.N, p.K, ep);
+      else
+        BL_LAUNCH((k_gemv_valu<TW, TP, 1, 1, 28, false>), grid, block, 0, st, x, w, p.M, p.N, p.K, ep);
+      return;
+    }
+  }
   switch (p.mt) {
-    case 1: BL_LAUNCH((k_gemv_valu<TW, TP, 1, R, 4>), grid, block, 0, st, x, w, p.M, p.N, p.K, ep); break;
-    case 2: BL_LAUNCH((k_gemv_valu<TW, TP, 2, R, 4>), grid, block, 0, st, x, w, p.M, p.N, p.K, ep); break;
-    default: BL_LAUNCH((k_gemv_valu<TW, TP, 4, R, 2>), grid, block, 0, st, x, w, p.M, p.N, p.K, ep); break;
+    case 1: BL_LAUNCH((k_gemv_valu<TW, TP, 1, 2, 4, true>), grid, block, 0, st, x, w, p.M, p.N, p.K, ep); break;
+    case 2: BL_LAUNCH((k_gemv_valu<TW, TP, 2, 2, 4, true>), grid, block, 0, st, x, w, p.M, p.N, p.K, ep); break;
+    default: BL_LAUNCH((k_gemv_valu<TW, TP, 4, 2, 2, true>), grid, block, 0, st, x, w, p.M, p.N, p.K, ep); break;
   }
 }
 

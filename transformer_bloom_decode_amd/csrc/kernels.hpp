@@ -33,10 +33,9 @@ struct EpiParams;
 enum WeightType : int { WT_F32 = 0, WT_BF16 = 1, WT_INT8 = 2 };
 enum LinearKind : int { LIN_F32 = 0, LIN_GEMV = 1, LIN_TILED = 2, LIN_VALU = 3 };
 
-// Vector-ALU GEMV: used for up to kValuMaxRows activation rows, kValuRows weight rows
-// per wave, 4 waves per block.
+// Vector-ALU GEMV: used for up to kValuMaxRows activation rows, 4 waves per block,
+// 1 or 2 weight rows per wave.
 constexpr int kValuMaxRows = 4;
-constexpr int kValuRows = 2;
 // Columns of the LM-head partial-argmax buffer per activation row: one partial per
 // kLmRowsPerPartial weight rows, the finest split any LM-head kernel uses.
 constexpr int kLmRowsPerPartial = 4;
@@ -52,6 +51,8 @@ struct LinearPlan {
   int kind;
   int M, N, K;
   int mt;        // GEMV: 16-row activation tiles (1, 2, 4, 8); VALU: activation rows (1, 2, 4)
+  int vr, vu;    // VALU: weight rows per wave, 16-byte pieces per row issued per batch
+  bool vdb;      // VALU: double-buffered batches
   int grid_x, grid_y;
   int splits;    // K splits (> 1: partial sums + reduction kernel)
 };
