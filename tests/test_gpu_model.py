@@ -136,3 +136,19 @@ def test_long_rows_cross_attention_batches():
     print(f"d128 L1 T<=160: hidden rel {v.hidden_rel:.2e}, exact ids {v.exact_frac:.3f}")
     assert v.hidden_rel <= 1e-2 and v.tokens_ok
     _kv_check(run, v.oracle, 2, 100 + 59, 2e-2)
+
+
+@pytest.mark.parametrize("hidden, ffn, n_new", [(2112, 4224, 24), (3072, 8192, 12)])
+def test_batch1_fused_layernorm_and_whole_row_gemv(hidden, ffn, n_new):
+    """Batch 1 with rows of 5-16 KB: QKV and MLP-up run the GEMV with the LayerNorm fused
+    in, dense / down / the LM head the one-row-per-wave GEMV (LM head with the argmax
+    epilogue).  Hidden 2112 leaves a partial last 1 KB piece in every row."""
+    m = dataclasses.replace(bi.BLOOM_560M, name=f"h{hidden}", n_layer=2, hidden=hidden,
+                            n_head_total=32, n_head_local=16, head_dim=64, ffn=ffn, vocab=8192)
+    T, dw, cfg = upload(m, seed=31)
+    prompt, valid = bi.prompts(m, 1, 16, seed=32)
+    run = run_gpu(cfg, dw, prompt, valid, n_new)
+    v = compare(m, T, prompt, valid, run, 1e-2)
+    print(f"h{hidden} L2 B1: hidden rel {v.hidden_rel:.2e}, exact ids {v.exact_frac:.3f}")
+    assert v.hidden_rel <= 1e-2 and v.tokens_ok
+    _kv_check(run, v.oracle, 1, 16 + n_new - 1, 2e-2)

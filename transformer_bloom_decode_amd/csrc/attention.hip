@@ -7,7 +7,8 @@
 // pad_b = prompt_len - valid_len[b] (left padding).  Steps, all in float32:
 //   1. s_j = q . k_j + slope_h * (j - qpos)   (q already carries 1/sqrt(d); keys and
 //      values read as 16-byte pieces, d/8 lanes per key, partial dots summed across
-//      those lanes; all K and V loads of a batch of keys are issued together)
+//      those lanes; all K and V loads of a batch of slots are issued together, before
+//      the row's valid length is known; slots before pad_b are masked)
 //   2. softmax over the visible keys only -- masked keys are never touched, i.e. they
 //      get probability exactly 0.  Within a batch: block max, exp, running sum; across
 //      batches (rows longer than one batch) the running sum and the P.V accumulators
@@ -79,22 +80,19 @@ __global__ __launch_bounds__(256) void k_attention(const float *__restrict__ q,
   const int tid = threadIdx.x;
   const int b = m / rows_per_seq;
   const int qpos = pos_base + (m - b * rows_per_seq);
-  int vl = valid_len[b];
-  vl = vl < 1 ? 1 : (vl > prompt_len ? prompt_len : vl);
-  const int first = prompt_len - vl;
+  // The K/V loads below address slots 0..qpos directly and do not wait for valid_len:
+  // the left-pad slots [0, first) are loaded too (the prompt pass wrote them) and
+  // masked in the scores.
+  const int vl_in = valid_len[b];
   TA *out = o + ((size_t)m * H + h) * d;
-  if (qpos < first) {
-    for (int e = tid; e < d; e += 256) out[e] = from_f<TA>(0.f);
-    return;
-  }
-  const int T = qpos - first + 1;
+  const int S = qpos + 1;
   const float slope = alibi_slope(n_total, head_off + h);
   const size_t head_base = ((size_t)b * H + h) * (size_t)max_len * d;
-  const TA *kb = kc + head_base + (size_t)first * d;
-  const TA *vb = vc + head_base + (size_t)first * d;
+  const TA *kb = kc + head_base;
+  const TA *vb = vc + head_base;
   const float *qr = q + ((size_t)m * H + h) * d;
 
-  // lane group g (L = d/8 lanes) handles keys j = g (mod G); lane `sub` owns dims
+  // lane group g (L = d/8 lanes) handles slots j = g (mod G); lane `sub` owns dims
   // [8 sub, 8 sub + 8) of each of them
   const int L = d >> 3;
   const int G = 256 / L;
@@ -102,48 +100,52 @@ __global__ __launch_bounds__(256) void k_attention(const float *__restrict__ q,
   float qv[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) qv[t] = qr[8 * sub + t];
+  const int vl = vl_in < 1 ? 1 : (vl_in > prompt_len ? prompt_len : vl_in);
+  const int first = prompt_len - vl;
 
-  // Online softmax over batches of G*KB keys (one batch when T <= G*KB): running
+  // Online softmax over batches of G*KB slots (one batch when qpos < G*KB): running
   // maximum mrun (block-uniform), per-thread running sum and P.V accumulators, all
   // rescaled by exp(mrun_old - mrun_new) when the maximum grows.
   float mrun = -INFINITY, lsum = 0.f;
   float acc[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) acc[t] = 0.f;
-  for (int j0 = 0; j0 < T; j0 += G * KB) {
+  for (int j0 = 0; j0 < S; j0 += G * KB) {
     KVRaw<TA> kr[KB], vr[KB];
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
       const int jj = j0 + u * G + g;
-      if (jj < T) {
+      if (jj < S) {
         kr[u].load(kb + (size_t)jj * d + 8 * sub);
         vr[u].load(vb + (size_t)jj * d + 8 * sub);
       }
     }
-    // scores s_j = q.k_j + slope * (j - qpos), summed across the group's L lanes
+    // scores s_j = q.k_j + slope * (j - qpos), summed across the group's L lanes;
+    // slots before `first` are masked
     float sc[KB];
     float bmax = -INFINITY;
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
       const int jj = j0 + u * G + g;
       float dot = 0.f;
-      if (jj < T) {
+      if (jj < S) {
 #pragma unroll
         for (int t = 0; t < 8; ++t) dot = fmaf(qv[t], kr[u].get(t), dot);
       }
       for (int off = L >> 1; off > 0; off >>= 1) dot += __shfl_xor(dot, off, 64);
-      sc[u] = jj < T ? dot + slope * (float)(first + jj - qpos) : -INFINITY;
+      sc[u] = (jj < S && jj >= first) ? dot + slope * (float)(jj - qpos) : -INFINITY;
       bmax = fmaxf(bmax, sc[u]);
     }
     const float mnew = fmaxf(mrun, block_max<4>(bmax, red));
-    const float alpha = __expf(mrun - mnew);      // 0 on the first batch
+    // 0 while no slot has been visible (mrun = -inf): lsum and acc are still 0
+    const float alpha = mrun == -INFINITY ? 0.f : __expf(mrun - mnew);
     lsum *= alpha;
 #pragma unroll
     for (int t = 0; t < 8; ++t) acc[t] *= alpha;
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
       const int jj = j0 + u * G + g;
-      if (jj < T) {
+      if (jj < S && jj >= first) {
         const float p = __expf(sc[u] - mnew);
         if (sub == 0) lsum += p;                  // each key counted once per group
 #pragma unroll
@@ -152,7 +154,9 @@ __global__ __launch_bounds__(256) void k_attention(const float *__restrict__ q,
     }
     mrun = mnew;
   }
-  const float inv = 1.0f / block_sum<4>(lsum, red);
+  const float total = block_sum<4>(lsum, red);
+  // a query with no visible key (a left-pad position of the prompt) gets o = 0
+  const float inv = qpos < first ? 0.f : 1.0f / total;
 
 #pragma unroll
   for (int t = 0; t < 8; ++t) pv[g * d + 8 * sub + t] = acc[t];

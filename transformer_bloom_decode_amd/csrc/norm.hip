@@ -54,10 +54,26 @@ __device__ __forceinline__ void ln_stats(const float4 (&v)[kLnVec], int h, float
   rstd = 1.0f / sqrtf(var + eps);
 }
 
+// Four parameters (gamma or beta) as loaded, unpacked only when used, so that their
+// loads can be issued together with the row's and retire while the statistics run.
+template <typename TP> struct Param4;
+template <> struct Param4<float> {
+  float4 v;
+  __device__ __forceinline__ void load(const float *p) { v = *(const float4 *)p; }
+  __device__ __forceinline__ float4 get() const { return v; }
+};
+template <> struct Param4<bf16_t> {
+  uint2 v;
+  __device__ __forceinline__ void load(const bf16_t *p) { v = *(const uint2 *)p; }
+  __device__ __forceinline__ float4 get() const {
+    return make_float4(lo_bf(v.x), hi_bf(v.x), lo_bf(v.y), hi_bf(v.y));
+  }
+};
+
 template <typename TP>
-__device__ __forceinline__ float4 ln_apply(float4 x, float mean, float rstd, const TP *g,
-                                           const TP *b, int col) {
-  const float4 gg = Vec4<TP>::load(g + col), bb = Vec4<TP>::load(b + col);
+__device__ __forceinline__ float4 ln_apply(float4 x, float mean, float rstd, const Param4<TP> &g,
+                                           const Param4<TP> &b) {
+  const float4 gg = g.get(), bb = b.get();
   return make_float4((x.x - mean) * rstd * gg.x + bb.x, (x.y - mean) * rstd * gg.y + bb.y,
                      (x.z - mean) * rstd * gg.z + bb.z, (x.w - mean) * rstd * gg.w + bb.w);
 }
@@ -77,17 +93,26 @@ __global__ __launch_bounds__(kLnThreads) void k_embed(const int *__restrict__ to
   const TP *e = embed + (size_t)tok * h;
   float *xr = x + (size_t)row * h;
   float4 v[kLnVec];
+  Param4<TP> gv[kLnVec], bv[kLnVec];
 #pragma unroll
   for (int i = 0; i < kLnVec; ++i) {
     const int col = 4 * (threadIdx.x + i * kLnThreads);
     v[i] = col < h ? Vec4<TP>::load(e + col) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  if (do_ln) {
+#pragma unroll
+    for (int i = 0; i < kLnVec; ++i) {
+      const int col = min(4 * (threadIdx.x + i * kLnThreads), h - 4);
+      gv[i].load(g + col);
+      bv[i].load(b + col);
+    }
   }
   float mean = 0.f, rstd = 1.f;
   if (do_ln) ln_stats(v, h, eps, sh, mean, rstd);
 #pragma unroll
   for (int i = 0; i < kLnVec; ++i) {
     const int col = 4 * (threadIdx.x + i * kLnThreads);
-    if (col < h) Vec4<float>::store(xr + col, do_ln ? ln_apply<TP>(v[i], mean, rstd, g, b, col) : v[i]);
+    if (col < h) Vec4<float>::store(xr + col, do_ln ? ln_apply<TP>(v[i], mean, rstd, gv[i], bv[i]) : v[i]);
   }
 }
 
@@ -105,10 +130,17 @@ __global__ __launch_bounds__(kLnThreads) void k_layernorm(const float *__restric
   const int row = blockIdx.x;
   const float *xr = x + ((size_t)row * in_step + in_off) * h;
   float4 v[kLnVec];
+  Param4<TP> gv[kLnVec], bv[kLnVec];
 #pragma unroll
   for (int i = 0; i < kLnVec; ++i) {
     const int col = 4 * (threadIdx.x + i * kLnThreads);
     v[i] = col < h ? Vec4<float>::load(xr + col) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int i = 0; i < kLnVec; ++i) {
+    const int col = min(4 * (threadIdx.x + i * kLnThreads), h - 4);  // in bounds; unused past h
+    gv[i].load(g + col);
+    bv[i].load(b + col);
   }
   float mean, rstd;
   ln_stats(v, h, eps, sh, mean, rstd);
@@ -118,7 +150,7 @@ __global__ __launch_bounds__(kLnThreads) void k_layernorm(const float *__restric
   for (int i = 0; i < kLnVec; ++i) {
     const int col = 4 * (threadIdx.x + i * kLnThreads);
     if (col < h) {
-      const float4 y = ln_apply<TP>(v[i], mean, rstd, g, b, col);
+      const float4 y = ln_apply<TP>(v[i], mean, rstd, gv[i], bv[i]);
       Vec4<TA>::store(o + col, y);
       if (of) Vec4<float>::store(of + col, y);
     }
