@@ -201,7 +201,8 @@ enum bloom_kernel_class {
   BLOOM_KERNEL_GEMV = 2,        /* vector-ALU GEMV (batch <= 4) */
   BLOOM_KERNEL_GEMV_MFMA = 3,   /* MFMA GEMV (batch <= 64, and LM heads up to 128 rows) */
   BLOOM_KERNEL_GEMM_TILED = 4,  /* LDS-tiled MFMA GEMM (larger batches, prompt pass) */
-  BLOOM_KERNEL_GEMM_F32 = 5     /* float32 model */
+  BLOOM_KERNEL_GEMM_F32 = 5,    /* float32 model */
+  BLOOM_KERNEL_GEMM_LDS = 6     /* direct-to-LDS MFMA GEMM (prompt pass, 256+ rows, bf16) */
 };
 int bloom_timer_enable(int32_t max_launches);
 int bloom_timer_disable(void);

@@ -152,3 +152,31 @@ def test_batch1_fused_layernorm_and_whole_row_gemv(hidden, ffn, n_new):
     print(f"h{hidden} L2 B1: hidden rel {v.hidden_rel:.2e}, exact ids {v.exact_frac:.3f}")
     assert v.hidden_rel <= 1e-2 and v.tokens_ok
     _kv_check(run, v.oracle, 1, 16 + n_new - 1, 2e-2)
+
+
+@pytest.mark.parametrize("batch, hidden, ffn", [(20, 1088, 4160), (70, 1088, 4160)])
+def test_prompt_pass_direct_to_lds_gemm_ragged(batch, hidden, ffn):
+    """Prompt passes of 320 and 1120 rows run the direct-to-LDS MFMA GEMM (128 x 128 and
+    256 x 256 tiles, split-K) with M and N that are not multiples of the tile, and
+    ragged left padding."""
+    m = dataclasses.replace(bi.BLOOM_560M, name=f"lg{batch}", n_layer=2, hidden=hidden,
+                            n_head_total=16, n_head_local=16, head_dim=64, ffn=ffn, vocab=4096)
+    T, dw, cfg = upload(m, seed=41)
+    prompt, valid = bi.prompts(m, batch, 16, np.arange(batch) % 16 + 1, seed=42)
+    run = run_gpu(cfg, dw, prompt, valid, 3)
+    v = compare(m, T, prompt, valid, run, 1e-2)
+    print(f"lg B{batch} h{hidden}: hidden rel {v.hidden_rel:.2e}, exact ids {v.exact_frac:.3f}")
+    assert v.hidden_rel <= 1e-2 and v.tokens_ok
+    _kv_check(run, v.oracle, batch, 16 + 2, 2e-2)
+
+
+def test_tp_share_176b_prompt_pass_batch32():
+    """The 176B rank-0 share at full width, batch 32: the 512-row prompt pass runs the
+    direct-to-LDS GEMM with split-K on the real layer shapes."""
+    m = bi.BLOOM_176B_TP8_RANK0.truncated(2)
+    T, dw, cfg = upload(m)
+    prompt, vl = bi.prompts(m, 32, 16)
+    run = run_gpu(cfg, dw, prompt, vl, 2)
+    v = compare(m, T, prompt, vl, run, 1e-2, widen_embed=True)
+    print(f"176b rank-0 share L2 B32: hidden rel {v.hidden_rel:.2e}, exact ids {v.exact_frac:.3f}")
+    assert v.hidden_rel <= 1e-2 and v.tokens_ok

@@ -70,7 +70,18 @@ WsPlan plan_ws(const bloom_config *c, int batch, int tokens_per_row) {
   p.lm_blocks = lm_blocks(c);
   p.amv = take((size_t)batch * p.lm_blocks * 4);
   p.ami = take((size_t)batch * p.lm_blocks * 4);
-  p.part = take(c->weight_dtype == BLOOM_F32 ? 0 : (size_t)kPartialCapFloats * 4);
+  size_t part = c->weight_dtype == BLOOM_F32 ? 0 : (size_t)kPartialCapFloats * 4;
+  if (c->weight_dtype != BLOOM_F32) {
+    // the prompt-pass GEMM may split K over more partials than the other kernels
+    const int wdt = wtype(c);
+    const int hd_ = c->n_head_local * c->head_dim;
+    const int dims[4][2] = {{3 * hd_, c->hidden}, {c->hidden, hd_}, {c->ffn, c->hidden},
+                            {c->hidden, c->ffn}};
+    for (const int mrows : {(int)M, batch})
+      for (const auto &nk : dims)
+        part = std::max(part, linear_partial_bytes(plan_linear(wdt, mrows, nk[0], nk[1], false)));
+  }
+  p.part = take(part);
   p.total = off;
   return p;
 }
@@ -147,6 +158,7 @@ int kernel_class(const LinearPlan &p) {
     case LIN_VALU: return BLOOM_KERNEL_GEMV;
     case LIN_GEMV: return BLOOM_KERNEL_GEMV_MFMA;
     case LIN_TILED: return BLOOM_KERNEL_GEMM_TILED;
+    case LIN_LG: return BLOOM_KERNEL_GEMM_LDS;
     default: return BLOOM_KERNEL_GEMM_F32;
   }
 }

@@ -517,6 +517,185 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(const bf16_t *__restrict__ X
 }
 
 // ---------------------------------------------------------------------------
+// Prompt-pass GEMM on MFMA 32x32x16 with LDS staged by direct-to-LDS loads
+// ---------------------------------------------------------------------------
+// Y = X . W^T for M >= 256 rows, bf16 weights.  A block owns a BM x BN output tile and
+// WGM x WGN waves, each a (BM/WGM) x (BN/WGN) tile of 32x32 MFMA blocks with float32
+// accumulators.  K advances in 64-wide tiles through two LDS stages: each wave copies
+// 1 KB pieces (8 rows x 128 bytes) of the X and W tiles straight from global memory
+// into LDS (global_load_lds_dwordx4, no register staging), one tile ahead of the MFMAs.
+// Inside a row the eight 16-byte k-pieces sit at slot piece ^ ((row >> 1) & 7), which
+// makes the MFMA operand reads (32 rows x 16 bytes per half-wave) free of LDS bank
+// conflicts (measured with the LDS bank-conflict counter on MI355X).  Blocks are
+// numbered so that the blocks one XCD runs take consecutive tiles (M fastest): the W
+// tile they share stays in that XCD's L2.  With split-K the block writes float32
+// partials and k_splitk_epilogue sums them in a fixed order.
+constexpr int kLg = 64;          // K tile
+constexpr int kLgStages = 2;
+
+// s_waitcnt vmcnt(V), expcnt and lgkmcnt left unconstrained
+template <int V> __device__ __forceinline__ void wait_vmcnt() {
+  static_assert(V >= 0 && V < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((V & 15) | ((V >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+template <int BM, int BN, int WGM, int WGN>
+struct LgCfg {
+  static constexpr int kWaves = WGM * WGN;
+  static constexpr int kThreads = kWaves * 64;
+  static constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  static constexpr int TM = WTM / 32, TN = WTN / 32;
+  static constexpr int CX = BM / 8, CW = BN / 8;           // 1 KB pieces per K tile
+  static constexpr int CPW = (CX + CW) / kWaves;           // pieces per wave per K tile
+  static constexpr int kStage = (BM + BN) * 128;            // bytes per stage
+  static constexpr int kLds = kLgStages * kStage;
+  static_assert((CX + CW) % kWaves == 0 && CPW < 64, "piece split");
+  static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
+};
+
+// The 16 outputs one lane holds of a 32x32 block: column n, rows m0 + 8 (v / 4) +
+// v % 4 (m0 includes the lane's 4 (lane / 32)).  Kept out of line: inlined for every
+// block of a wave, the epilogue made the compiler leave the accumulator loops rolled,
+// which turned the accumulators into a scratch-memory array stored on every K step.
+// The residual mode issues all 16 loads of x before any store.
+template <typename TP>
+__device__ __attribute__((noinline)) void lg_out16(const EpiParams &ep, float *partial, int z,
+                                                   int M, int N, int m0, int n, f32x16 acc) {
+  if (n >= N) return;
+  if (partial) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int m = m0 + 8 * (v >> 2) + (v & 3);
+      if (m < M) partial[((size_t)z * M + m) * N + n] = acc[v];
+    }
+    return;
+  }
+  if (ep.mode == EPI_RESID) {
+    const float sc = ep.scale ? h2f(ep.scale[n]) : 1.f;
+    const float bi = ep.bias ? to_f<TP>(((const TP *)ep.bias)[n]) : 0.f;
+    float *x = (float *)ep.out + n;
+    float xv[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int m = min(m0 + 8 * (v >> 2) + (v & 3), M - 1);
+      xv[v] = x[(size_t)m * ep.ld];
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int m = m0 + 8 * (v >> 2) + (v & 3);
+      float y = acc[v];
+      if (ep.scale) y *= sc;
+      if (ep.bias) y += bi;
+      if (m < M) x[(size_t)m * ep.ld] = xv[v] + y;
+    }
+    return;
+  }
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int m = m0 + 8 * (v >> 2) + (v & 3);
+    if (m < M) epilogue<TP, bf16_t>(ep, m, n, acc[v]);
+  }
+}
+
+template <typename TP, int BM, int BN, int WGM, int WGN>
+__global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_lg(
+    const bf16_t *__restrict__ X, const bf16_t *__restrict__ W, int M, int N, int K,
+    int tiles_m, int tiles_n, int splits, float *__restrict__ partial, EpiParams ep) {
+  using C = LgCfg<BM, BN, WGM, WGN>;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char lg_lds[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wid % WGM, wn = wid / WGM;
+  const int nb = gridDim.x, b = blockIdx.x, xcd = b & 7, slot = b >> 3;
+  const int L = xcd * (nb >> 3) + min(xcd, nb & 7) + slot;     // bijective renumbering
+  const int mt = L % tiles_m, nt = (L / tiles_m) % tiles_n, z = L / (tiles_m * tiles_n);
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int KT = K / kLg;
+  const int kt0 = (int)(((long)KT * z) / splits), kt1 = (int)(((long)KT * (z + 1)) / splits);
+
+  // source of each of this wave's pieces: lane -> row (lane >> 3), swizzled k-piece
+  const bf16_t *src[C::CPW];
+#pragma unroll
+  for (int c = 0; c < C::CPW; ++c) {
+    const int pc = wid * C::CPW + c;
+    const bool is_x = pc < C::CX;
+    const int rr = (is_x ? pc : pc - C::CX) * 8 + (lane >> 3);
+    const int piece = (lane & 7) ^ ((rr >> 1) & 7);
+    src[c] = is_x ? X + (size_t)min(m0 + rr, M - 1) * K + piece * 8
+                  : W + (size_t)min(n0 + rr, N - 1) * K + piece * 8;
+  }
+  auto issue = [&](int kt) {
+    unsigned char *st = lg_lds + (kt % kLgStages) * C::kStage;
+#pragma unroll
+    for (int c = 0; c < C::CPW; ++c)
+      __builtin_amdgcn_global_load_lds((const void *)(src[c] + (size_t)kt * kLg),
+                                       (__attribute__((address_space(3))) void *)(
+                                           st + (wid * C::CPW + c) * 1024),
+                                       16, 0, 0);
+  };
+
+  f32x16 acc[C::TM][C::TN];
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) acc[i][j] = f32x16{};
+
+  if (kt0 < kt1) issue(kt0);
+  for (int kt = kt0; kt < kt1; ++kt) {
+    // This wave's copies of tile kt have landed; the barrier (deliberately without a
+    // memory fence, which would make the compiler wait for every outstanding load)
+    // then makes every wave's copies visible, and also orders every wave's reads of
+    // the stage refilled below, which the previous step read.
+    wait_vmcnt<0>();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (kt + 1 < kt1) issue(kt + 1);
+    const unsigned char *xb = lg_lds + (kt % kLgStages) * C::kStage;
+    const unsigned char *wb = xb + C::CX * 1024;
+    // operands of 16-wide substep s + 1 are read while the MFMAs of substep s run
+    u32x4 a[2][C::TM], bv[2][C::TN];
+    auto rd = [&](int s, int q) {
+      const int piece = 2 * s + (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i) {
+        const int r = wm * C::WTM + 32 * i + (lane & 31);
+        a[q][i] = *(const u32x4 *)(xb + r * 128 + 16 * (piece ^ ((r >> 1) & 7)));
+      }
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) {
+        const int r = wn * C::WTN + 32 * j + (lane & 31);
+        bv[q][j] = *(const u32x4 *)(wb + r * 128 + 16 * (piece ^ ((r >> 1) & 7)));
+      }
+    };
+    rd(0, 0);
+#pragma unroll
+    for (int s = 0; s < kLg / 16; ++s) {
+      if (s + 1 < kLg / 16) rd(s + 1, (s + 1) & 1);
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) acc[i][j] = mfma32(a[s & 1][i], bv[s & 1][j], acc[i][j]);
+    }
+  }
+
+  // D layout of a 32x32 block: lane holds column lane % 32, value v row
+  // 8 (v / 4) + 4 (lane / 32) + v % 4
+  float *part = splits > 1 ? partial : nullptr;
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j)
+      lg_out16<TP>(ep, part, z, M, N, m0 + wm * C::WTM + 32 * i + 4 * (lane >> 5),
+                   n0 + wn * C::WTN + 32 * j + (lane & 31), acc[i][j]);
+}
+
+// ---------------------------------------------------------------------------
 // generic float32 path: one thread per output, blocks of 256 consecutive n
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_gemm_f32(const float *__restrict__ X,
@@ -641,6 +820,29 @@ LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax) {
     p.splits = 1;
     return p;
   }
+  if (!argmax && wdtype == WT_BF16 && M >= 256 && K % kLg == 0) {
+    // Direct-to-LDS MFMA GEMM.  Tiles of 256 x 256 (one block per CU: 128 KB of LDS)
+    // from 1024 rows, else 128 x 128 (two blocks per CU).  Split-K is chosen to
+    // minimise (rounds of resident blocks) / splits, with a 10% charge for the
+    // reduction pass.
+    p.kind = LIN_LG;
+    p.lg = M >= 1024 ? 1 : 0;
+    const int bt = p.lg ? 256 : 128;
+    const int slots = p.lg ? 256 : 512;
+    p.grid_x = (M + bt - 1) / bt;
+    p.grid_y = (N + bt - 1) / bt;
+    const long tiles = (long)p.grid_x * p.grid_y;
+    const int KT = K / kLg;
+    int best = 1;
+    double best_cost = 1e30;
+    for (int sp = 1; sp <= 8 && sp <= KT; ++sp) {
+      if (sp > 1 && (long)sp * M * N > kLgPartialCapFloats) break;
+      const double cost = (double)((tiles * sp + slots - 1) / slots) / sp + (sp > 1 ? 0.1 : 0.0);
+      if (cost < best_cost - 1e-9) { best_cost = cost; best = sp; }
+    }
+    p.splits = best;
+    return p;
+  }
   if (M <= 64 || argmax) {
     p.kind = LIN_GEMV;
     p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : (M <= 64 ? 4 : 8));
@@ -705,6 +907,29 @@ static void launch_valu_t(const LinearPlan &p, const void *X, const void *W, con
   }
 }
 
+size_t linear_partial_bytes(const LinearPlan &p) {
+  return p.splits > 1 ? (size_t)p.splits * p.M * p.N * sizeof(float) : 0;
+}
+
+template <int BM, int BN, int WGM, int WGN>
+static hipError_t launch_lg_t(const LinearPlan &p, const void *X, const void *W, float *partial,
+                              const EpiParams &ep, hipStream_t st) {
+  using C = LgCfg<BM, BN, WGM, WGN>;
+  static bool lds_attr = false;  // more than 64 KB of dynamic LDS must be allowed once
+  if (!lds_attr) {
+    const hipError_t e = hipFuncSetAttribute(
+        (const void *)k_gemm_lg<bf16_t, BM, BN, WGM, WGN>,
+        hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
+    if (e != hipSuccess) return e;
+    lds_attr = true;
+  }
+  BL_LAUNCH((k_gemm_lg<bf16_t, BM, BN, WGM, WGN>),
+            dim3((unsigned)(p.grid_x * p.grid_y * p.splits)), dim3(C::kThreads), C::kLds, st,
+            (const bf16_t *)X, (const bf16_t *)W, p.M, p.N, p.K, p.grid_x, p.grid_y, p.splits,
+            partial, ep);
+  return hipGetLastError();
+}
+
 hipError_t launch_linear(int wdtype, const LinearPlan &p, const void *X, const void *W,
                          float *partial, const EpiParams &ep, hipStream_t st) {
   if (p.M <= 0) return hipSuccess;
@@ -718,7 +943,11 @@ hipError_t launch_linear(int wdtype, const LinearPlan &p, const void *X, const v
     else launch_valu_t<int8_t, bf16_t>(p, X, W, ep, st);
     return hipGetLastError();
   }
-  if (p.kind == LIN_GEMV) {
+  if (p.kind == LIN_LG) {
+    const hipError_t e = p.lg ? launch_lg_t<256, 256, 2, 4>(p, X, W, partial, ep, st)
+                              : launch_lg_t<128, 128, 2, 2>(p, X, W, partial, ep, st);
+    if (e != hipSuccess) return e;
+  } else if (p.kind == LIN_GEMV) {
     if (wdtype == WT_BF16) launch_gemv_t<bf16_t, bf16_t>(p, X, W, partial, ep, st);
     else launch_gemv_t<int8_t, bf16_t>(p, X, W, partial, ep, st);
   } else {

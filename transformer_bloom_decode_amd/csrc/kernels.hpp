@@ -31,7 +31,7 @@ extern thread_local LaunchEvents g_launch_events;
 struct EpiParams;
 
 enum WeightType : int { WT_F32 = 0, WT_BF16 = 1, WT_INT8 = 2 };
-enum LinearKind : int { LIN_F32 = 0, LIN_GEMV = 1, LIN_TILED = 2, LIN_VALU = 3 };
+enum LinearKind : int { LIN_F32 = 0, LIN_GEMV = 1, LIN_TILED = 2, LIN_VALU = 3, LIN_LG = 4 };
 
 // Vector-ALU GEMV: used for up to kValuMaxRows activation rows, 4 waves per block,
 // 1 or 2 weight rows per wave.
@@ -44,8 +44,10 @@ inline int lm_partial_stride(int vocab) {
 }
 
 
-// Cap on the split-K partial buffer (float32 elements) any one linear may use.
+// Cap on the split-K partial buffer (float32 elements) any one linear may use; the
+// direct-to-LDS prompt-pass GEMM may use up to kLgPartialCapFloats.
 constexpr long kPartialCapFloats = 8l << 20;
+constexpr long kLgPartialCapFloats = 48l << 20;
 
 struct LinearPlan {
   int kind;
@@ -53,11 +55,14 @@ struct LinearPlan {
   int mt;        // GEMV: 16-row activation tiles (1, 2, 4, 8); VALU: activation rows (1, 2, 4)
   int vr, vu;    // VALU: weight rows per wave, 16-byte pieces per row issued per batch
   bool vdb;      // VALU: double-buffered batches
+  int lg;        // LG: 1 = 256 x 256 tiles (8 waves), 0 = 128 x 128 tiles (4 waves)
   int grid_x, grid_y;
   int splits;    // K splits (> 1: partial sums + reduction kernel)
 };
 
 LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax);
+// Bytes of split-K partials the plan needs (0 without split-K).
+size_t linear_partial_bytes(const LinearPlan &p);
 hipError_t launch_linear(int wdtype, const LinearPlan &p, const void *X, const void *W,
                          float *partial, const EpiParams &ep, hipStream_t st);
 hipError_t launch_argmax_merge(const float *val, const int *idx, int stride, int nblk, int rows,
