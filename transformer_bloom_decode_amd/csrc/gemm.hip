@@ -531,7 +531,6 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(const bf16_t *__restrict__ X
 // tile they share stays in that XCD's L2.  With split-K the block writes float32
 // partials and k_splitk_epilogue sums them in a fixed order.
 constexpr int kLg = 64;          // K tile
-constexpr int kLgStages = 2;
 
 // s_waitcnt vmcnt(V), expcnt and lgkmcnt left unconstrained
 template <int V> __device__ __forceinline__ void wait_vmcnt() {
@@ -544,7 +543,7 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-template <int BM, int BN, int WGM, int WGN>
+template <int BM, int BN, int WGM, int WGN, int S>
 struct LgCfg {
   static constexpr int kWaves = WGM * WGN;
   static constexpr int kThreads = kWaves * 64;
@@ -553,8 +552,9 @@ struct LgCfg {
   static constexpr int CX = BM / 8, CW = BN / 8;           // 1 KB pieces per K tile
   static constexpr int CPW = (CX + CW) / kWaves;           // pieces per wave per K tile
   static constexpr int kStage = (BM + BN) * 128;            // bytes per stage
-  static constexpr int kLds = kLgStages * kStage;
-  static_assert((CX + CW) % kWaves == 0 && CPW < 64, "piece split");
+  static constexpr int kLds = S * kStage;
+  static_assert((CX + CW) % kWaves == 0 && CPW * (S - 1) < 64, "piece split");
+  static_assert(S >= 2 && S <= 4, "stages");
   static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
 };
 
@@ -602,11 +602,11 @@ __device__ __attribute__((noinline)) void lg_out16(const EpiParams &ep, float *p
   }
 }
 
-template <typename TP, int BM, int BN, int WGM, int WGN>
+template <typename TP, int BM, int BN, int WGM, int WGN, int S>
 __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_lg(
     const bf16_t *__restrict__ X, const bf16_t *__restrict__ W, int M, int N, int K,
     int tiles_m, int tiles_n, int splits, float *__restrict__ partial, EpiParams ep) {
-  using C = LgCfg<BM, BN, WGM, WGN>;
+  using C = LgCfg<BM, BN, WGM, WGN, S>;
   extern __shared__ __attribute__((aligned(1024))) unsigned char lg_lds[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -630,7 +630,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_lg(
                   : W + (size_t)min(n0 + rr, N - 1) * K + piece * 8;
   }
   auto issue = [&](int kt) {
-    unsigned char *st = lg_lds + (kt % kLgStages) * C::kStage;
+    unsigned char *st = lg_lds + (kt % S) * C::kStage;
 #pragma unroll
     for (int c = 0; c < C::CPW; ++c)
       __builtin_amdgcn_global_load_lds((const void *)(src[c] + (size_t)kt * kLg),
@@ -645,18 +645,24 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_lg(
 #pragma unroll
     for (int j = 0; j < C::TN; ++j) acc[i][j] = f32x16{};
 
-  if (kt0 < kt1) issue(kt0);
+#pragma unroll
+  for (int p = 0; p < S - 1; ++p)
+    if (kt0 + p < kt1) issue(kt0 + p);
   for (int kt = kt0; kt < kt1; ++kt) {
-    // This wave's copies of tile kt have landed; the barrier (deliberately without a
-    // memory fence, which would make the compiler wait for every outstanding load)
-    // then makes every wave's copies visible, and also orders every wave's reads of
-    // the stage refilled below, which the previous step read.
-    wait_vmcnt<0>();
+    // This wave's copies of tile kt have landed once at most (tiles issued after it) x
+    // CPW of its loads are outstanding; the barrier (deliberately without a memory
+    // fence, which would make the compiler wait for every outstanding load) then makes
+    // every wave's copies visible, and also orders every wave's reads of the stage
+    // refilled below, which the previous step read.
+    const int after = min(S - 2, kt1 - 1 - kt);
+    if (S >= 4 && after >= 2) wait_vmcnt<(S >= 4 ? 2 * C::CPW : 0)>();
+    else if (S >= 3 && after >= 1) wait_vmcnt<(S >= 3 ? C::CPW : 0)>();
+    else wait_vmcnt<0>();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_barrier();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    if (kt + 1 < kt1) issue(kt + 1);
-    const unsigned char *xb = lg_lds + (kt % kLgStages) * C::kStage;
+    if (kt + S - 1 < kt1) issue(kt + S - 1);
+    const unsigned char *xb = lg_lds + (kt % S) * C::kStage;
     const unsigned char *wb = xb + C::CX * 1024;
     // operands of 16-wide substep s + 1 are read while the MFMAs of substep s run
     u32x4 a[2][C::TM], bv[2][C::TN];
@@ -788,6 +794,15 @@ __global__ __launch_bounds__(kMergeThreads) void k_argmax_merge(const float *__r
 // ---------------------------------------------------------------------------
 // host-side planning and launch
 // ---------------------------------------------------------------------------
+// Tile configurations of the direct-to-LDS GEMM (LinearPlan::lg).
+enum LgTile : int {
+  LG_256 = 1,      // 256 x 256, 8 waves, 2 stages (prompt pass, 1024+ rows)
+  LG_128 = 0,      // 128 x 128, 4 waves, 2 stages (prompt pass, 256+ rows)
+  LG_D32 = 2,      // 32 x 128, 4 waves, 4 stages (decode / short passes, <= 32 rows)
+  LG_D64 = 3,      // 64 x 128, 4 waves, 3 stages (<= 64 rows)
+  LG_D128 = 4,     // 128 x 128, 4 waves, 3 stages (<= 128 rows)
+};
+
 LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax) {
   LinearPlan p{};
   p.M = M; p.N = N; p.K = K;
@@ -826,9 +841,9 @@ LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax) {
     // minimise (rounds of resident blocks) / splits, with a 10% charge for the
     // reduction pass.
     p.kind = LIN_LG;
-    p.lg = M >= 1024 ? 1 : 0;
-    const int bt = p.lg ? 256 : 128;
-    const int slots = p.lg ? 256 : 512;
+    p.lg = M >= 1024 ? LG_256 : LG_128;
+    const int bt = p.lg == LG_256 ? 256 : 128;
+    const int slots = p.lg == LG_256 ? 256 : 512;
     p.grid_x = (M + bt - 1) / bt;
     p.grid_y = (N + bt - 1) / bt;
     const long tiles = (long)p.grid_x * p.grid_y;
@@ -841,6 +856,24 @@ LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax) {
       if (cost < best_cost - 1e-9) { best_cost = cost; best = sp; }
     }
     p.splits = best;
+    return p;
+  }
+  if (!argmax && wdtype == WT_BF16 && M < 256 && K % kLg == 0) {
+    // Decode batches and short passes: the direct-to-LDS GEMM with a 32/64/128-row
+    // activation tile against 128 weight rows, 3-4 LDS stages in flight, and K split
+    // so that each block streams about 48+ K tiles (at least 2 splits when there are
+    // few N tiles).  Measured on MI355X against the MFMA GEMV (64 bytes per row per
+    // load): 176B-share QKV at 32 rows 82 -> 37 us, at 64 rows 137 -> 42 us.
+    p.kind = LIN_LG;
+    p.lg = M <= 32 ? LG_D32 : (M <= 64 ? LG_D64 : LG_D128);
+    const int bm = M <= 32 ? 32 : (M <= 64 ? 64 : 128);
+    p.grid_x = (M + bm - 1) / bm;
+    p.grid_y = (N + 127) / 128;
+    const int KT = K / kLg;
+    int sp = max(1, min(8, KT / 48));
+    if (sp < 2 && KT >= 2 && p.grid_x * p.grid_y < 160) sp = 2;
+    while (sp > 1 && (long)sp * M * N > kLgPartialCapFloats) --sp;
+    p.splits = sp;
     return p;
   }
   if (M <= 64 || argmax) {
@@ -911,23 +944,34 @@ size_t linear_partial_bytes(const LinearPlan &p) {
   return p.splits > 1 ? (size_t)p.splits * p.M * p.N * sizeof(float) : 0;
 }
 
-template <int BM, int BN, int WGM, int WGN>
+template <int BM, int BN, int WGM, int WGN, int S>
 static hipError_t launch_lg_t(const LinearPlan &p, const void *X, const void *W, float *partial,
                               const EpiParams &ep, hipStream_t st) {
-  using C = LgCfg<BM, BN, WGM, WGN>;
+  using C = LgCfg<BM, BN, WGM, WGN, S>;
   static bool lds_attr = false;  // more than 64 KB of dynamic LDS must be allowed once
   if (!lds_attr) {
     const hipError_t e = hipFuncSetAttribute(
-        (const void *)k_gemm_lg<bf16_t, BM, BN, WGM, WGN>,
+        (const void *)k_gemm_lg<bf16_t, BM, BN, WGM, WGN, S>,
         hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
     if (e != hipSuccess) return e;
     lds_attr = true;
   }
-  BL_LAUNCH((k_gemm_lg<bf16_t, BM, BN, WGM, WGN>),
+  BL_LAUNCH((k_gemm_lg<bf16_t, BM, BN, WGM, WGN, S>),
             dim3((unsigned)(p.grid_x * p.grid_y * p.splits)), dim3(C::kThreads), C::kLds, st,
             (const bf16_t *)X, (const bf16_t *)W, p.M, p.N, p.K, p.grid_x, p.grid_y, p.splits,
             partial, ep);
   return hipGetLastError();
+}
+
+static hipError_t launch_lg(const LinearPlan &p, const void *X, const void *W, float *partial,
+                            const EpiParams &ep, hipStream_t st) {
+  switch (p.lg) {
+    case LG_256: return launch_lg_t<256, 256, 2, 4, 2>(p, X, W, partial, ep, st);
+    case LG_128: return launch_lg_t<128, 128, 2, 2, 2>(p, X, W, partial, ep, st);
+    case LG_D32: return launch_lg_t<32, 128, 1, 4, 4>(p, X, W, partial, ep, st);
+    case LG_D64: return launch_lg_t<64, 128, 1, 4, 3>(p, X, W, partial, ep, st);
+    default: return launch_lg_t<128, 128, 2, 2, 3>(p, X, W, partial, ep, st);
+  }
 }
 
 hipError_t launch_linear(int wdtype, const LinearPlan &p, const void *X, const void *W,
@@ -944,8 +988,7 @@ hipError_t launch_linear(int wdtype, const LinearPlan &p, const void *X, const v
     return hipGetLastError();
   }
   if (p.kind == LIN_LG) {
-    const hipError_t e = p.lg ? launch_lg_t<256, 256, 2, 4>(p, X, W, partial, ep, st)
-                              : launch_lg_t<128, 128, 2, 2>(p, X, W, partial, ep, st);
+    const hipError_t e = launch_lg(p, X, W, partial, ep, st);
     if (e != hipSuccess) return e;
   } else if (p.kind == LIN_GEMV) {
     if (wdtype == WT_BF16) launch_gemv_t<bf16_t, bf16_t>(p, X, W, partial, ep, st);
