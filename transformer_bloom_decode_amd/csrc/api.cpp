@@ -295,8 +295,9 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
     err = timed_linear(wdt_lm, p_lm, (const char *)af + (size_t)r0 * h * act, w->embed, part, a,
                        st, lm_bytes);
     if (err != hipSuccess) return hip_fail(err);
-    // this chunk's kernel wrote grid_x partials per row
-    err = launch_argmax_merge(a.am_val, a.am_idx, nblk, p_lm.grid_x, rows, d_next + r0, st);
+    // this chunk's kernel wrote one partial per row per weight tile
+    err = launch_argmax_merge(a.am_val, a.am_idx, nblk, argmax_partials_per_row(p_lm), rows,
+                              d_next + r0, st);
     if (err != hipSuccess) return hip_fail(err);
   }
   return BLOOM_OK;

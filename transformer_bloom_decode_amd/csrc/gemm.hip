@@ -602,6 +602,33 @@ __device__ __attribute__((noinline)) void lg_out16(const EpiParams &ep, float *p
   }
 }
 
+// Argmax epilogue of one 32x32 block (LM head): for each of the lane's 16 rows, the
+// best (value, lowest index) over the 32 columns its half-wave holds, written by the
+// half's first lane to red_v / red_i [local row][col_slot].
+template <typename TP>
+__device__ __attribute__((noinline)) void lg_argmax16(const EpiParams &ep, int N, int lrow0,
+                                                      int n, int col_slot, int nslots,
+                                                      float *red_v, int *red_i, f32x16 acc) {
+  const float sc = (ep.scale && n < N) ? h2f(ep.scale[n]) : 1.f;
+  const float bi0 = (ep.bias && n < N) ? to_f<TP>(((const TP *)ep.bias)[n]) : 0.f;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    float bv = n < N ? acc[v] * sc + bi0 : -INFINITY;
+    int bi = n < N ? n : 0x7fffffff;
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) {
+      const float ov = __shfl_xor(bv, o, 64);
+      const int oi = __shfl_xor(bi, o, 64);
+      argmax_take(bv, bi, ov, oi);
+    }
+    if ((threadIdx.x & 31) == 0) {
+      const int lr = lrow0 + 8 * (v >> 2) + (v & 3);
+      red_v[lr * nslots + col_slot] = bv;
+      red_i[lr * nslots + col_slot] = bi;
+    }
+  }
+}
+
 template <typename TP, int BM, int BN, int WGM, int WGN, int S>
 __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_lg(
     const bf16_t *__restrict__ X, const bf16_t *__restrict__ W, int M, int N, int K,
@@ -692,6 +719,31 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_lg(
 
   // D layout of a 32x32 block: lane holds column lane % 32, value v row
   // 8 (v / 4) + 4 (lane / 32) + v % 4
+  if (ep.mode == EPI_ARGMAX) {
+    // one (max, index) partial per row per N tile (the plan never splits K here)
+    constexpr int NS = WGN * C::TN;
+    float *red_v = (float *)lg_lds;
+    int *red_i = (int *)(lg_lds + BM * NS * sizeof(float));
+    __syncthreads();  // every wave is done reading the LDS stages
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j)
+        lg_argmax16<TP>(ep, N, wm * C::WTM + 32 * i + 4 * (lane >> 5),
+                        n0 + wn * C::WTN + 32 * j + (lane & 31), wn * C::TN + j, NS, red_v,
+                        red_i, acc[i][j]);
+    __syncthreads();
+    for (int lr = tid; lr < BM; lr += C::kThreads) {
+      const int m = m0 + lr;
+      if (m >= M) continue;
+      float bv = red_v[lr * NS];
+      int bi = red_i[lr * NS];
+      for (int c = 1; c < NS; ++c) argmax_take(bv, bi, red_v[lr * NS + c], red_i[lr * NS + c]);
+      ep.am_val[(size_t)m * ep.am_stride + nt] = bv;
+      ep.am_idx[(size_t)m * ep.am_stride + nt] = bi;
+    }
+    return;
+  }
   float *part = splits > 1 ? partial : nullptr;
 #pragma unroll
   for (int i = 0; i < C::TM; ++i)
@@ -858,7 +910,7 @@ LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax) {
     p.splits = best;
     return p;
   }
-  if (!argmax && wdtype == WT_BF16 && M < 256 && K % kLg == 0) {
+  if (wdtype == WT_BF16 && M < 256 && (!argmax || M <= 128) && K % kLg == 0) {
     // Decode batches and short passes: the direct-to-LDS GEMM with a 32/64/128-row
     // activation tile against 128 weight rows, 3-4 LDS stages in flight, and K split
     // so that each block streams about 48+ K tiles (at least 2 splits when there are
@@ -873,7 +925,7 @@ LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax) {
     int sp = max(1, min(8, KT / 48));
     if (sp < 2 && KT >= 2 && p.grid_x * p.grid_y < 160) sp = 2;
     while (sp > 1 && (long)sp * M * N > kLgPartialCapFloats) --sp;
-    p.splits = sp;
+    p.splits = argmax ? 1 : sp;   // the argmax epilogue needs whole dot products
     return p;
   }
   if (M <= 64 || argmax) {
@@ -938,6 +990,10 @@ static void launch_valu_t(const LinearPlan &p, const void *X, const void *W, con
     case 2: BL_LAUNCH((k_gemv_valu<TW, TP, 2, 2, 4, true>), grid, block, 0, st, x, w, p.M, p.N, p.K, ep); break;
     default: BL_LAUNCH((k_gemv_valu<TW, TP, 4, 2, 2, true>), grid, block, 0, st, x, w, p.M, p.N, p.K, ep); break;
   }
+}
+
+int argmax_partials_per_row(const LinearPlan &p) {
+  return p.kind == LIN_LG ? p.grid_y : p.grid_x;
 }
 
 size_t linear_partial_bytes(const LinearPlan &p) {

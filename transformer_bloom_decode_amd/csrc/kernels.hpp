@@ -61,6 +61,8 @@ struct LinearPlan {
 };
 
 LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax);
+// (max, index) partials per activation row an argmax-mode launch of the plan writes.
+int argmax_partials_per_row(const LinearPlan &p);
 // Bytes of split-K partials the plan needs (0 without split-K).
 size_t linear_partial_bytes(const LinearPlan &p);
 hipError_t launch_linear(int wdtype, const LinearPlan &p, const void *X, const void *W,
