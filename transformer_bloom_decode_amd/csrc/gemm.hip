@@ -519,11 +519,13 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(const bf16_t *__restrict__ X
 // ---------------------------------------------------------------------------
 // Prompt-pass GEMM on MFMA 32x32x16 with LDS staged by direct-to-LDS loads
 // ---------------------------------------------------------------------------
-// Y = X . W^T for M >= 256 rows, bf16 weights.  A block owns a BM x BN output tile and
+// Y = X . W^T for 5+ rows, bf16 or int8 weights.  A block owns a BM x BN output tile and
 // WGM x WGN waves, each a (BM/WGM) x (BN/WGN) tile of 32x32 MFMA blocks with float32
 // accumulators.  K advances in 64-wide tiles through two LDS stages: each wave copies
-// 1 KB pieces (8 rows x 128 bytes) of the X and W tiles straight from global memory
-// into LDS (global_load_lds_dwordx4, no register staging), one tile ahead of the MFMAs.
+// 1 KB pieces (8 rows x 128 bytes; int8 W: 16 rows x 64 bytes) of the X and W tiles
+// straight from global memory into LDS (global_load_lds_dwordx4, no register staging),
+// S - 1 tiles ahead of the MFMAs.  int8 weights are widened to bf16 (exactly) as they
+// are read from LDS and scaled per row in the epilogue.
 // Inside a row the eight 16-byte k-pieces sit at slot piece ^ ((row >> 1) & 7), which
 // makes the MFMA operand reads (32 rows x 16 bytes per half-wave) free of LDS bank
 // conflicts (measured with the LDS bank-conflict counter on MI355X).  Blocks are
@@ -543,15 +545,16 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-template <int BM, int BN, int WGM, int WGN, int S>
+template <typename TW, int BM, int BN, int WGM, int WGN, int S>
 struct LgCfg {
   static constexpr int kWaves = WGM * WGN;
   static constexpr int kThreads = kWaves * 64;
   static constexpr int WTM = BM / WGM, WTN = BN / WGN;
   static constexpr int TM = WTM / 32, TN = WTN / 32;
-  static constexpr int CX = BM / 8, CW = BN / 8;           // 1 KB pieces per K tile
+  static constexpr int WRB = kLg * (int)sizeof(TW);         // W bytes per row per K tile
+  static constexpr int CX = BM / 8, CW = BN * WRB / 1024;   // 1 KB pieces per K tile
   static constexpr int CPW = (CX + CW) / kWaves;           // pieces per wave per K tile
-  static constexpr int kStage = (BM + BN) * 128;            // bytes per stage
+  static constexpr int kStage = BM * 128 + BN * WRB;        // bytes per stage
   static constexpr int kLds = S * kStage;
   static_assert((CX + CW) % kWaves == 0 && CPW * (S - 1) < 64, "piece split");
   static_assert(S >= 2 && S <= 4, "stages");
@@ -629,11 +632,12 @@ __device__ __attribute__((noinline)) void lg_argmax16(const EpiParams &ep, int N
   }
 }
 
-template <typename TP, int BM, int BN, int WGM, int WGN, int S>
+template <typename TW, typename TP, int BM, int BN, int WGM, int WGN, int S>
 __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_lg(
-    const bf16_t *__restrict__ X, const bf16_t *__restrict__ W, int M, int N, int K,
+    const bf16_t *__restrict__ X, const TW *__restrict__ W, int M, int N, int K,
     int tiles_m, int tiles_n, int splits, float *__restrict__ partial, EpiParams ep) {
-  using C = LgCfg<BM, BN, WGM, WGN, S>;
+  using C = LgCfg<TW, BM, BN, WGM, WGN, S>;
+  constexpr bool kI8 = sizeof(TW) == 1;
   extern __shared__ __attribute__((aligned(1024))) unsigned char lg_lds[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -645,25 +649,38 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_lg(
   const int KT = K / kLg;
   const int kt0 = (int)(((long)KT * z) / splits), kt1 = (int)(((long)KT * (z + 1)) / splits);
 
-  // source of each of this wave's pieces: lane -> row (lane >> 3), swizzled k-piece
-  const bf16_t *src[C::CPW];
+  // Source of each of this wave's pieces.  X (and bf16 W): lane -> row (lane >> 3) of
+  // 8 rows x 128 bytes, k-piece (lane & 7) ^ ((row >> 1) & 7).  int8 W: lane -> row
+  // (lane >> 2) of 16 rows x 64 bytes, 16-byte slot (lane & 3) ^ ((row >> 2) & 3).
+  const unsigned char *src[C::CPW];
 #pragma unroll
   for (int c = 0; c < C::CPW; ++c) {
     const int pc = wid * C::CPW + c;
-    const bool is_x = pc < C::CX;
-    const int rr = (is_x ? pc : pc - C::CX) * 8 + (lane >> 3);
-    const int piece = (lane & 7) ^ ((rr >> 1) & 7);
-    src[c] = is_x ? X + (size_t)min(m0 + rr, M - 1) * K + piece * 8
-                  : W + (size_t)min(n0 + rr, N - 1) * K + piece * 8;
+    if (pc < C::CX) {
+      const int rr = pc * 8 + (lane >> 3);
+      const int piece = (lane & 7) ^ ((rr >> 1) & 7);
+      src[c] = (const unsigned char *)(X + (size_t)min(m0 + rr, M - 1) * K + piece * 8);
+    } else if (!kI8) {
+      const int rr = (pc - C::CX) * 8 + (lane >> 3);
+      const int piece = (lane & 7) ^ ((rr >> 1) & 7);
+      src[c] = (const unsigned char *)(W + (size_t)min(n0 + rr, N - 1) * K + piece * 8);
+    } else {
+      const int rr = (pc - C::CX) * 16 + (lane >> 2);
+      const int slot = (lane & 3) ^ ((rr >> 2) & 3);
+      src[c] = (const unsigned char *)(W + (size_t)min(n0 + rr, N - 1) * K + slot * 16);
+    }
   }
   auto issue = [&](int kt) {
     unsigned char *st = lg_lds + (kt % S) * C::kStage;
 #pragma unroll
-    for (int c = 0; c < C::CPW; ++c)
-      __builtin_amdgcn_global_load_lds((const void *)(src[c] + (size_t)kt * kLg),
+    for (int c = 0; c < C::CPW; ++c) {
+      const int pc = wid * C::CPW + c;
+      const size_t adv = (size_t)kt * (pc < C::CX ? kLg * 2 : C::WRB);   // bytes per K tile
+      __builtin_amdgcn_global_load_lds((const void *)(src[c] + adv),
                                        (__attribute__((address_space(3))) void *)(
-                                           st + (wid * C::CPW + c) * 1024),
+                                           st + pc * 1024),
                                        16, 0, 0);
+    }
   };
 
   f32x16 acc[C::TM][C::TN];
@@ -703,7 +720,14 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_lg(
 #pragma unroll
       for (int j = 0; j < C::TN; ++j) {
         const int r = wn * C::WTN + 32 * j + (lane & 31);
-        bv[q][j] = *(const u32x4 *)(wb + r * 128 + 16 * (piece ^ ((r >> 1) & 7)));
+        if constexpr (kI8) {
+          // 8 int8 of k-piece `piece`, widened to bf16 (exact)
+          const uint2 t = *(const uint2 *)(wb + r * 64 + 16 * ((piece >> 1) ^ ((r >> 2) & 3)) +
+                                           8 * (piece & 1));
+          bv[q][j] = i8x8_to_bf16x8(t.x, t.y);
+        } else {
+          bv[q][j] = *(const u32x4 *)(wb + r * 128 + 16 * (piece ^ ((r >> 1) & 7)));
+        }
       }
     };
     rd(0, 0);
@@ -887,7 +911,7 @@ LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax) {
     p.splits = 1;
     return p;
   }
-  if (!argmax && wdtype == WT_BF16 && M >= 256 && K % kLg == 0) {
+  if (!argmax && M >= 256 && K % kLg == 0) {
     // Direct-to-LDS MFMA GEMM.  Tiles of 256 x 256 (one block per CU: 128 KB of LDS)
     // from 1024 rows, else 128 x 128 (two blocks per CU).  Split-K is chosen to
     // minimise (rounds of resident blocks) / splits, with a 10% charge for the
@@ -910,7 +934,7 @@ LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax) {
     p.splits = best;
     return p;
   }
-  if (wdtype == WT_BF16 && M < 256 && (!argmax || M <= 128) && K % kLg == 0) {
+  if (M < 256 && (!argmax || M <= 128) && K % kLg == 0) {
     // Decode batches and short passes: the direct-to-LDS GEMM with a 32/64/128-row
     // activation tile against 128 weight rows, 3-4 LDS stages in flight, and K split
     // so that each block streams about 48+ K tiles (at least 2 splits when there are
@@ -1000,33 +1024,34 @@ size_t linear_partial_bytes(const LinearPlan &p) {
   return p.splits > 1 ? (size_t)p.splits * p.M * p.N * sizeof(float) : 0;
 }
 
-template <int BM, int BN, int WGM, int WGN, int S>
+template <typename TW, int BM, int BN, int WGM, int WGN, int S>
 static hipError_t launch_lg_t(const LinearPlan &p, const void *X, const void *W, float *partial,
                               const EpiParams &ep, hipStream_t st) {
-  using C = LgCfg<BM, BN, WGM, WGN, S>;
+  using C = LgCfg<TW, BM, BN, WGM, WGN, S>;
   static bool lds_attr = false;  // more than 64 KB of dynamic LDS must be allowed once
   if (!lds_attr) {
     const hipError_t e = hipFuncSetAttribute(
-        (const void *)k_gemm_lg<bf16_t, BM, BN, WGM, WGN, S>,
+        (const void *)k_gemm_lg<TW, bf16_t, BM, BN, WGM, WGN, S>,
         hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
     if (e != hipSuccess) return e;
     lds_attr = true;
   }
-  BL_LAUNCH((k_gemm_lg<bf16_t, BM, BN, WGM, WGN, S>),
+  BL_LAUNCH((k_gemm_lg<TW, bf16_t, BM, BN, WGM, WGN, S>),
             dim3((unsigned)(p.grid_x * p.grid_y * p.splits)), dim3(C::kThreads), C::kLds, st,
-            (const bf16_t *)X, (const bf16_t *)W, p.M, p.N, p.K, p.grid_x, p.grid_y, p.splits,
+            (const bf16_t *)X, (const TW *)W, p.M, p.N, p.K, p.grid_x, p.grid_y, p.splits,
             partial, ep);
   return hipGetLastError();
 }
 
+template <typename TW>
 static hipError_t launch_lg(const LinearPlan &p, const void *X, const void *W, float *partial,
                             const EpiParams &ep, hipStream_t st) {
   switch (p.lg) {
-    case LG_256: return launch_lg_t<256, 256, 2, 4, 2>(p, X, W, partial, ep, st);
-    case LG_128: return launch_lg_t<128, 128, 2, 2, 2>(p, X, W, partial, ep, st);
-    case LG_D32: return launch_lg_t<32, 128, 1, 4, 4>(p, X, W, partial, ep, st);
-    case LG_D64: return launch_lg_t<64, 128, 1, 4, 3>(p, X, W, partial, ep, st);
-    default: return launch_lg_t<128, 128, 2, 2, 3>(p, X, W, partial, ep, st);
+    case LG_256: return launch_lg_t<TW, 256, 256, 2, 4, 2>(p, X, W, partial, ep, st);
+    case LG_128: return launch_lg_t<TW, 128, 128, 2, 2, 2>(p, X, W, partial, ep, st);
+    case LG_D32: return launch_lg_t<TW, 32, 128, 1, 4, 4>(p, X, W, partial, ep, st);
+    case LG_D64: return launch_lg_t<TW, 64, 128, 1, 4, 3>(p, X, W, partial, ep, st);
+    default: return launch_lg_t<TW, 128, 128, 2, 2, 3>(p, X, W, partial, ep, st);
   }
 }
 
@@ -1044,7 +1069,8 @@ hipError_t launch_linear(int wdtype, const LinearPlan &p, const void *X, const v
     return hipGetLastError();
   }
   if (p.kind == LIN_LG) {
-    const hipError_t e = launch_lg(p, X, W, partial, ep, st);
+    const hipError_t e = wdtype == WT_BF16 ? launch_lg<bf16_t>(p, X, W, partial, ep, st)
+                                           : launch_lg<int8_t>(p, X, W, partial, ep, st);
     if (e != hipSuccess) return e;
   } else if (p.kind == LIN_GEMV) {
     if (wdtype == WT_BF16) launch_gemv_t<bf16_t, bf16_t>(p, X, W, partial, ep, st);
