@@ -198,11 +198,9 @@ int kv_cache_append(const bloom_config *cfg, bloom_kv_cache *kv, int32_t layer, 
  * of launches and the summed weight bytes (weights, biases, scales) they streamed;
  * reading does not clear.  (A split-K reduction kernel is not included.) */
 enum bloom_kernel_class {
-  BLOOM_KERNEL_GEMV = 2,        /* vector-ALU GEMV (batch <= 4) */
-  BLOOM_KERNEL_GEMV_MFMA = 3,   /* MFMA GEMV (batch <= 64, and LM heads up to 128 rows) */
-  BLOOM_KERNEL_GEMM_TILED = 4,  /* LDS-tiled MFMA GEMM (larger batches, prompt pass) */
+  BLOOM_KERNEL_GEMV = 2,        /* vector-ALU GEMV (up to 4 rows) */
   BLOOM_KERNEL_GEMM_F32 = 5,    /* float32 model */
-  BLOOM_KERNEL_GEMM_LDS = 6     /* direct-to-LDS MFMA GEMM (prompt pass, 256+ rows, bf16) */
+  BLOOM_KERNEL_GEMM_LDS = 6     /* direct-to-LDS MFMA GEMM (5+ rows, bf16 or int8 weights) */
 };
 int bloom_timer_enable(int32_t max_launches);
 int bloom_timer_disable(void);

@@ -187,8 +187,7 @@ def bloom_timer_pause(paused: bool):
     _check(lib.bloom_timer_pause(int(bool(paused))), "bloom_timer_pause")
 
 
-KERNEL_CLASSES = {2: "k_gemv_valu", 3: "k_gemv_mfma", 4: "k_gemm_tiled", 5: "k_gemm_f32",
-                  6: "k_gemm_lg"}
+KERNEL_CLASSES = {2: "k_gemv_valu", 5: "k_gemm_f32", 6: "k_gemm_lg"}
 
 
 def bloom_timer_read(kernel_class: int = -1):

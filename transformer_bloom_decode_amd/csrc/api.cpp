@@ -156,8 +156,6 @@ void destroy_timer_events() {
 int kernel_class(const LinearPlan &p) {
   switch (p.kind) {
     case LIN_VALU: return BLOOM_KERNEL_GEMV;
-    case LIN_GEMV: return BLOOM_KERNEL_GEMV_MFMA;
-    case LIN_TILED: return BLOOM_KERNEL_GEMM_TILED;
     case LIN_LG: return BLOOM_KERNEL_GEMM_LDS;
     default: return BLOOM_KERNEL_GEMM_F32;
   }

@@ -8,21 +8,15 @@
 // output tiles; Section III.D fuses bias, GeLU, residual and the QKV split into the
 // GEMM.  Here, on gfx950:
 //
-//  * k_gemv_mfma  (M <= 16*MT rows of activations, the decode step): a block of four
-//    waves owns 16 weight rows; the waves split K (and, for narrow layers, blocks
-//    split K too).  Each lane streams 16-byte pieces of its weight row directly into
-//    MFMA A-operand registers (v_mfma_f32_16x16x32_bf16, batch padded to 16 in the B
-//    operand), with the next chunk's loads issued before the current chunk's MFMAs.
-//    int8 weights are widened to bf16 in registers (exact: |q| <= 127).  The four
-//    waves' partial tiles are summed in LDS in a fixed order, then the fused epilogue
-//    runs.
-//  * k_gemm_tiled (larger M, the prompt pass): 128x128 output tiles, 64-wide K
-//    steps staged through LDS, four waves of 64x64 (16 MFMA tiles each).
+//  * k_gemv_valu (up to 4 activation rows, the batch-1..4 decode step): vector-ALU
+//    dot products; each wave streams one or two weight rows in 1 KB non-temporal
+//    loads (whole rows at once when the grid leaves wave slots empty), the block's
+//    output rows are finished by the fused epilogue (or an argmax for the LM head).
+//  * k_gemm_lg (5+ rows: decode batches, LM heads, prompt passes): MFMA 32x32x16 with
+//    both operands copied straight from global memory into LDS (global_load_lds), tile
+//    sizes and K splits chosen per shape (plan_linear); int8 weights widened from LDS.
 //  * k_gemm_f32: a plain float32 path for the fp32 model.
 //
-// The k index carried by each MFMA operand element may be any bijection of the chunk,
-// as long as the weight and the activation operand use the same one; the one used
-// here keeps each lane's weight loads 16 bytes wide and contiguous.
 #include <type_traits>
 
 #include "common.hpp"
@@ -46,184 +40,8 @@ __device__ __forceinline__ u32x4 i8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
                i8x2_to_bf16x2(hi, 2)};
 }
 
-// Weight-operand access per 64-wide K chunk.  Lane (r, c) = (lane & 15, lane >> 4)
-// feeds two MFMAs (s = 0, 1) for weight row r; koff(s, c) is the first of the 8
-// consecutive k it supplies to MFMA s.
-template <typename TW> struct WOps;
-
-template <> struct WOps<bf16_t> {
-  struct Raw { u32x4 a, b; };
-  static __device__ __forceinline__ Raw load(const bf16_t *row, int k0, int c) {
-    Raw r;
-    r.a = *(const u32x4 *)(row + k0 + 8 * c);
-    r.b = *(const u32x4 *)(row + k0 + 32 + 8 * c);
-    return r;
-  }
-  static __device__ __forceinline__ u32x4 op(const Raw &r, int s) { return s ? r.b : r.a; }
-  static __device__ __forceinline__ int koff(int s, int c) { return 32 * s + 8 * c; }
-  static constexpr size_t bytes = 2;
-};
-
-template <> struct WOps<int8_t> {
-  struct Raw { u32x4 a; };
-  static __device__ __forceinline__ Raw load(const int8_t *row, int k0, int c) {
-    Raw r;
-    r.a = *(const u32x4 *)(row + k0 + 16 * c);
-    return r;
-  }
-  static __device__ __forceinline__ u32x4 op(const Raw &r, int s) {
-    return s ? i8x8_to_bf16x8(r.a[2], r.a[3]) : i8x8_to_bf16x8(r.a[0], r.a[1]);
-  }
-  static __device__ __forceinline__ int koff(int s, int c) { return 16 * c + 8 * s; }
-  static constexpr size_t bytes = 1;
-};
-
-__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
-// Best (value, index) with the lowest index among equal values; NaN never wins.
 __device__ __forceinline__ void argmax_take(float &bv, int &bi, float v, int i) {
   if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
-}
-
-// ---------------------------------------------------------------------------
-// decode GEMV on MFMA
-// ---------------------------------------------------------------------------
-template <typename TW, typename TP, int MT, int U>
-__global__ __launch_bounds__(256) void k_gemv_mfma(const bf16_t *__restrict__ X,
-                                                   const TW *__restrict__ W, int M, int N, int K,
-                                                   float *__restrict__ partial, EpiParams ep) {
-  using WO = WOps<TW>;
-  constexpr bool kPrefetchX = (MT <= 2);
-  __shared__ float red[4][MT][16][17];
-  __shared__ float fin[MT][16][17];
-
-  // The wave index goes through readfirstlane so that the chunk range, and with it
-  // every branch around an MFMA, is scalar: an MFMA placed under an exec mask that
-  // happens to be all-zero still executes and accumulates whatever its stale operand
-  // registers hold.
-  const int lane = threadIdx.x & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r = lane & 15, c = lane >> 4;
-  const int n0 = blockIdx.x * 16;
-  const int nrow = min(n0 + r, N - 1);
-  const TW *__restrict__ wrow = W + (size_t)nrow * K;
-
-  const int KC = K >> 6;
-  const int nslots = gridDim.y * 4;
-  const int slot = blockIdx.y * 4 + wid;
-  const int cb = (int)(((long)KC * slot) / nslots);
-  const int ce = (int)(((long)KC * (slot + 1)) / nslots);
-
-  const bf16_t *xrow[MT];
-  bool xok[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int m = 16 * mt + r;
-    xok[mt] = m < M;
-    xrow[mt] = X + (size_t)(xok[mt] ? m : 0) * K;
-  }
-
-  f32x4 acc[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  typename WO::Raw wcur[U], wnxt[U];
-  u32x4 xcur[kPrefetchX ? U : 1][2][MT], xnxt[kPrefetchX ? U : 1][2][MT];
-
-  auto load_stage = [&](int chb, typename WO::Raw(&w)[U], u32x4(&x)[kPrefetchX ? U : 1][2][MT]) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int ch = chb + u;
-      if (ch < ce) {
-        w[u] = WO::load(wrow, ch * 64, c);
-        if constexpr (kPrefetchX) {
-#pragma unroll
-          for (int s = 0; s < 2; ++s)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-              x[u][s][mt] = xok[mt] ? *(const u32x4 *)(xrow[mt] + ch * 64 + WO::koff(s, c))
-                                    : zero4();
-        }
-      }
-    }
-  };
-
-  int ch = cb;
-  if (ch < ce) load_stage(ch, wcur, xcur);
-  while (ch < ce) {
-    const int nx = ch + U;
-    if (nx < ce) load_stage(nx, wnxt, xnxt);
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (ch + u < ce) {
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const u32x4 a = WO::op(wcur[u], s);
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            u32x4 xb;
-            if constexpr (kPrefetchX) {
-              xb = xcur[u][s][mt];
-            } else {
-              xb = xok[mt] ? *(const u32x4 *)(xrow[mt] + (ch + u) * 64 + WO::koff(s, c))
-                           : zero4();
-            }
-            acc[mt] = mfma16(a, xb, acc[mt]);
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      wcur[u] = wnxt[u];
-      if constexpr (kPrefetchX) {
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) xcur[u][s][mt] = xnxt[u][s][mt];
-      }
-    }
-    ch = nx;
-  }
-
-  // D layout of the 16x16 MFMA: lane holds rows i = 4c + t (t = 0..3), column j = r.
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int t = 0; t < 4; ++t) red[wid][mt][4 * c + t][r] = acc[mt][t];
-  __syncthreads();
-
-  const bool split = gridDim.y > 1;
-  for (int e = threadIdx.x; e < MT * 256; e += 256) {
-    const int mt = e >> 8, i = (e >> 4) & 15, j = e & 15;
-    const float sum = ((red[0][mt][i][j] + red[1][mt][i][j]) + red[2][mt][i][j]) + red[3][mt][i][j];
-    const int m = 16 * mt + j, n = n0 + i;
-    if (ep.mode == EPI_ARGMAX) {
-      fin[mt][i][j] = sum;
-    } else if (m < M && n < N) {
-      if (split)
-        partial[((size_t)blockIdx.y * M + m) * N + n] = sum;
-      else
-        epilogue<TP, bf16_t>(ep, m, n, sum);
-    }
-  }
-  if (ep.mode == EPI_ARGMAX) {
-    __syncthreads();
-    if (threadIdx.x < MT * 16) {
-      const int mt = threadIdx.x >> 4, j = threadIdx.x & 15;
-      const int m = 16 * mt + j;
-      if (m < M) {
-        float bv = -INFINITY;
-        int bi = n0;
-        for (int i = 0; i < 16 && n0 + i < N; ++i) argmax_take(bv, bi, fin[mt][i][j], n0 + i);
-        ep.am_val[(size_t)m * ep.am_stride + blockIdx.x] = bv;
-        ep.am_idx[(size_t)m * ep.am_stride + blockIdx.x] = bi;
-      }
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -394,126 +212,6 @@ __global__ __launch_bounds__(256) void k_gemv_valu(const bf16_t *__restrict__ X,
     const int n = row0 + lane / MR, m = lane % MR;
     if (n < N && m < M) epilogue<TP, bf16_t>(ep, m, n, v);
   }
-}
-
-// ---------------------------------------------------------------------------
-// LDS-tiled GEMM on MFMA (prompt pass)
-// ---------------------------------------------------------------------------
-constexpr int TBM = 128, TBN = 128, TBK = 64, TLD = TBK + 8;  // +8: stagger LDS rows
-
-template <typename TW> struct TileLoad;
-
-template <> struct TileLoad<bf16_t> {
-  // 128 rows x 64 bf16 = 1024 16-byte pieces; 4 per thread
-  static constexpr int kPieces = 4;
-  u32x4 v[kPieces];
-  __device__ __forceinline__ void load(const bf16_t *W, int rows_valid, int row0, int K, int k0) {
-#pragma unroll
-    for (int p = 0; p < kPieces; ++p) {
-      const int q = threadIdx.x + 256 * p;
-      const int rr = min(row0 + (q >> 3), rows_valid - 1);
-      v[p] = *(const u32x4 *)(W + (size_t)rr * K + k0 + (q & 7) * 8);
-    }
-  }
-  __device__ __forceinline__ void store(bf16_t *lds) const {
-#pragma unroll
-    for (int p = 0; p < kPieces; ++p) {
-      const int q = threadIdx.x + 256 * p;
-      *(u32x4 *)(lds + (q >> 3) * TLD + (q & 7) * 8) = v[p];
-    }
-  }
-};
-
-template <> struct TileLoad<int8_t> {
-  // 128 rows x 64 int8 = 512 16-byte pieces; 2 per thread, widened to bf16 in LDS
-  static constexpr int kPieces = 2;
-  u32x4 v[kPieces];
-  __device__ __forceinline__ void load(const int8_t *W, int rows_valid, int row0, int K, int k0) {
-#pragma unroll
-    for (int p = 0; p < kPieces; ++p) {
-      const int q = threadIdx.x + 256 * p;
-      const int rr = min(row0 + (q >> 2), rows_valid - 1);
-      v[p] = *(const u32x4 *)(W + (size_t)rr * K + k0 + (q & 3) * 16);
-    }
-  }
-  __device__ __forceinline__ void store(bf16_t *lds) const {
-#pragma unroll
-    for (int p = 0; p < kPieces; ++p) {
-      const int q = threadIdx.x + 256 * p;
-      bf16_t *dst = lds + (q >> 2) * TLD + (q & 3) * 16;
-      *(u32x4 *)dst = i8x8_to_bf16x8(v[p][0], v[p][1]);
-      *(u32x4 *)(dst + 8) = i8x8_to_bf16x8(v[p][2], v[p][3]);
-    }
-  }
-};
-
-template <typename TW, typename TP>
-__global__ __launch_bounds__(256) void k_gemm_tiled(const bf16_t *__restrict__ X,
-                                                    const TW *__restrict__ W, int M, int N, int K,
-                                                    float *__restrict__ partial, EpiParams ep) {
-  __shared__ __attribute__((aligned(16))) bf16_t xs[TBM * TLD];
-  __shared__ __attribute__((aligned(16))) bf16_t ws[TBN * TLD];
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int r = lane & 15, c = lane >> 4;
-  const int wm = wid & 1, wn = wid >> 1;
-  const int n_base = blockIdx.x * TBN, m_base = blockIdx.y * TBM;
-  const int KT = K / TBK;
-  const int S = gridDim.z;
-  const int kt0 = (int)(((long)KT * blockIdx.z) / S), kt1 = (int)(((long)KT * (blockIdx.z + 1)) / S);
-
-  f32x4 acc[4][4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  TileLoad<bf16_t> xl;
-  TileLoad<TW> wl;
-  if (kt0 < kt1) {
-    xl.load(X, M, m_base, K, kt0 * TBK);
-    wl.load(W, N, n_base, K, kt0 * TBK);
-  }
-  for (int kt = kt0; kt < kt1; ++kt) {
-    __syncthreads();
-    xl.store(xs);
-    wl.store(ws);
-    __syncthreads();
-    if (kt + 1 < kt1) {
-      xl.load(X, M, m_base, K, (kt + 1) * TBK);
-      wl.load(W, N, n_base, K, (kt + 1) * TBK);
-    }
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      u32x4 xa[4], wa[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        xa[i] = *(const u32x4 *)(xs + (wm * 64 + 16 * i + r) * TLD + 32 * s + 8 * c);
-#pragma unroll
-      for (int jn = 0; jn < 4; ++jn)
-        wa[jn] = *(const u32x4 *)(ws + (wn * 64 + 16 * jn + r) * TLD + 32 * s + 8 * c);
-#pragma unroll
-      for (int jn = 0; jn < 4; ++jn)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[jn][i] = mfma16(wa[jn], xa[i], acc[jn][i]);
-    }
-  }
-
-  const bool split = S > 1;
-#pragma unroll
-  for (int jn = 0; jn < 4; ++jn)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int n = n_base + wn * 64 + 16 * jn + 4 * c + t;
-        const int m = m_base + wm * 64 + 16 * i + r;
-        if (m < M && n < N) {
-          if (split)
-            partial[((size_t)blockIdx.z * M + m) * N + n] = acc[jn][i][t];
-          else
-            epilogue<TP, bf16_t>(ep, m, n, acc[jn][i][t]);
-        }
-      }
 }
 
 // ---------------------------------------------------------------------------
@@ -888,7 +586,6 @@ LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax) {
     p.splits = 1;
     return p;
   }
-  const long cap = kPartialCapFloats;
   if (M <= kValuMaxRows) {
     p.kind = LIN_VALU;
     p.mt = M <= 1 ? 1 : (M <= 2 ? 2 : 4);
@@ -911,19 +608,19 @@ LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax) {
     p.splits = 1;
     return p;
   }
-  if (!argmax && M >= 256 && K % kLg == 0) {
-    // Direct-to-LDS MFMA GEMM.  Tiles of 256 x 256 (one block per CU: 128 KB of LDS)
-    // from 1024 rows, else 128 x 128 (two blocks per CU).  Split-K is chosen to
-    // minimise (rounds of resident blocks) / splits, with a 10% charge for the
-    // reduction pass.
-    p.kind = LIN_LG;
+  // Direct-to-LDS MFMA GEMM for everything else (hidden sizes are multiples of 64).
+  p.kind = LIN_LG;
+  const int KT = K / kLg;
+  if (!argmax && M >= 256) {
+    // Prompt passes: tiles of 256 x 256 (one block per CU: 128 KB of LDS) from 1024
+    // rows, else 128 x 128 (two blocks per CU).  Split-K is chosen to minimise
+    // (rounds of resident blocks) / splits, with a 10% charge for the reduction pass.
     p.lg = M >= 1024 ? LG_256 : LG_128;
     const int bt = p.lg == LG_256 ? 256 : 128;
     const int slots = p.lg == LG_256 ? 256 : 512;
     p.grid_x = (M + bt - 1) / bt;
     p.grid_y = (N + bt - 1) / bt;
     const long tiles = (long)p.grid_x * p.grid_y;
-    const int KT = K / kLg;
     int best = 1;
     double best_cost = 1e30;
     for (int sp = 1; sp <= 8 && sp <= KT; ++sp) {
@@ -934,64 +631,21 @@ LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax) {
     p.splits = best;
     return p;
   }
-  if (M < 256 && (!argmax || M <= 128) && K % kLg == 0) {
-    // Decode batches and short passes: the direct-to-LDS GEMM with a 32/64/128-row
-    // activation tile against 128 weight rows, 3-4 LDS stages in flight, and K split
-    // so that each block streams about 48+ K tiles (at least 2 splits when there are
-    // few N tiles).  Measured on MI355X against the MFMA GEMV (64 bytes per row per
-    // load): 176B-share QKV at 32 rows 82 -> 37 us, at 64 rows 137 -> 42 us.
-    p.kind = LIN_LG;
-    p.lg = M <= 32 ? LG_D32 : (M <= 64 ? LG_D64 : LG_D128);
-    const int bm = M <= 32 ? 32 : (M <= 64 ? 64 : 128);
-    p.grid_x = (M + bm - 1) / bm;
-    p.grid_y = (N + 127) / 128;
-    const int KT = K / kLg;
-    int sp = max(1, min(8, KT / 48));
-    if (sp < 2 && KT >= 2 && p.grid_x * p.grid_y < 160) sp = 2;
-    while (sp > 1 && (long)sp * M * N > kLgPartialCapFloats) --sp;
-    p.splits = argmax ? 1 : sp;   // the argmax epilogue needs whole dot products
-    return p;
-  }
-  if (M <= 64 || argmax) {
-    p.kind = LIN_GEMV;
-    p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : (M <= 64 ? 4 : 8));
-    p.grid_x = (N + 15) / 16;
-    int s = 1;
-    if (!argmax && p.grid_x < 256) {
-      s = (512 + p.grid_x - 1) / p.grid_x;
-      const int kc = K / 64;
-      s = min(s, max(1, kc / 4));  // keep >= 1 chunk per wave
-      while (s > 1 && (long)s * M * N > cap) --s;
-    }
-    p.splits = s;
-  } else {
-    p.kind = LIN_TILED;
-    p.grid_x = (N + TBN - 1) / TBN;
-    p.grid_y = (M + TBM - 1) / TBM;
-    const int blocks = p.grid_x * p.grid_y;
-    int s = 1;
-    if (blocks < 256) {
-      s = (512 + blocks - 1) / blocks;
-      s = min(s, max(1, (K / TBK) / 2));
-      while (s > 1 && (long)s * M * N > cap) --s;
-    }
-    p.splits = s;
-  }
+  // Decode batches, LM heads and short passes: a 32/64/128-row activation tile against
+  // 128 weight rows, 3-4 LDS stages in flight, and K split so that each block streams
+  // about 48+ K tiles (at least 2 splits when there are few N tiles).  Measured on
+  // MI355X against an MFMA GEMV loading 64 bytes per row: 176B-share QKV at 32 rows
+  // 82 -> 37 us, at 64 rows 137 -> 42 us.  The argmax epilogue needs whole dot
+  // products, so the LM head is never split.
+  p.lg = M <= 32 ? LG_D32 : (M <= 64 ? LG_D64 : LG_D128);
+  const int bm = M <= 32 ? 32 : (M <= 64 ? 64 : 128);
+  p.grid_x = (M + bm - 1) / bm;
+  p.grid_y = (N + 127) / 128;
+  int sp = max(1, min(8, KT / 48));
+  if (sp < 2 && KT >= 2 && p.grid_x * p.grid_y < 160) sp = 2;
+  while (sp > 1 && (long)sp * M * N > kLgPartialCapFloats) --sp;
+  p.splits = argmax ? 1 : sp;
   return p;
-}
-
-template <typename TW, typename TP>
-static void launch_gemv_t(const LinearPlan &p, const void *X, const void *W, float *partial,
-                          const EpiParams &ep, hipStream_t st) {
-  const dim3 grid(p.grid_x, p.splits), block(256);
-  const bf16_t *x = (const bf16_t *)X;
-  const TW *w = (const TW *)W;
-  switch (p.mt) {
-    case 1: BL_LAUNCH((k_gemv_mfma<TW, TP, 1, 4>), grid, block, 0, st, x, w, p.M, p.N, p.K, partial, ep); break;
-    case 2: BL_LAUNCH((k_gemv_mfma<TW, TP, 2, 2>), grid, block, 0, st, x, w, p.M, p.N, p.K, partial, ep); break;
-    case 4: BL_LAUNCH((k_gemv_mfma<TW, TP, 4, 2>), grid, block, 0, st, x, w, p.M, p.N, p.K, partial, ep); break;
-    default: BL_LAUNCH((k_gemv_mfma<TW, TP, 8, 1>), grid, block, 0, st, x, w, p.M, p.N, p.K, partial, ep); break;
-  }
 }
 
 template <typename TW, typename TP>
@@ -1068,22 +722,10 @@ hipError_t launch_linear(int wdtype, const LinearPlan &p, const void *X, const v
     else launch_valu_t<int8_t, bf16_t>(p, X, W, ep, st);
     return hipGetLastError();
   }
-  if (p.kind == LIN_LG) {
-    const hipError_t e = wdtype == WT_BF16 ? launch_lg<bf16_t>(p, X, W, partial, ep, st)
-                                           : launch_lg<int8_t>(p, X, W, partial, ep, st);
-    if (e != hipSuccess) return e;
-  } else if (p.kind == LIN_GEMV) {
-    if (wdtype == WT_BF16) launch_gemv_t<bf16_t, bf16_t>(p, X, W, partial, ep, st);
-    else launch_gemv_t<int8_t, bf16_t>(p, X, W, partial, ep, st);
-  } else {
-    const dim3 grid(p.grid_x, p.grid_y, p.splits);
-    if (wdtype == WT_BF16)
-      BL_LAUNCH((k_gemm_tiled<bf16_t, bf16_t>), grid, dim3(256), 0, st,
-                         (const bf16_t *)X, (const bf16_t *)W, p.M, p.N, p.K, partial, ep);
-    else
-      BL_LAUNCH((k_gemm_tiled<int8_t, bf16_t>), grid, dim3(256), 0, st,
-                         (const bf16_t *)X, (const int8_t *)W, p.M, p.N, p.K, partial, ep);
-  }
+  if (p.kind != LIN_LG) return hipErrorInvalidValue;
+  const hipError_t e = wdtype == WT_BF16 ? launch_lg<bf16_t>(p, X, W, partial, ep, st)
+                                         : launch_lg<int8_t>(p, X, W, partial, ep, st);
+  if (e != hipSuccess) return e;
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || p.splits <= 1) return err;
   const size_t MN = (size_t)p.M * p.N;

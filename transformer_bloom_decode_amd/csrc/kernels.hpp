@@ -31,7 +31,7 @@ extern thread_local LaunchEvents g_launch_events;
 struct EpiParams;
 
 enum WeightType : int { WT_F32 = 0, WT_BF16 = 1, WT_INT8 = 2 };
-enum LinearKind : int { LIN_F32 = 0, LIN_GEMV = 1, LIN_TILED = 2, LIN_VALU = 3, LIN_LG = 4 };
+enum LinearKind : int { LIN_F32 = 0, LIN_VALU = 3, LIN_LG = 4 };
 
 // Vector-ALU GEMV: used for up to kValuMaxRows activation rows, 4 waves per block,
 // 1 or 2 weight rows per wave.
@@ -44,18 +44,18 @@ inline int lm_partial_stride(int vocab) {
 }
 
 
-// Cap on the split-K partial buffer (float32 elements) any one linear may use; the
-// direct-to-LDS prompt-pass GEMM may use up to kLgPartialCapFloats.
+// Minimum size of the split-K partial buffer (float32 elements) and the cap any one
+// linear of the direct-to-LDS GEMM may use.
 constexpr long kPartialCapFloats = 8l << 20;
 constexpr long kLgPartialCapFloats = 48l << 20;
 
 struct LinearPlan {
   int kind;
   int M, N, K;
-  int mt;        // GEMV: 16-row activation tiles (1, 2, 4, 8); VALU: activation rows (1, 2, 4)
+  int mt;        // VALU: activation rows (1, 2, 4)
   int vr, vu;    // VALU: weight rows per wave, 16-byte pieces per row issued per batch
   bool vdb;      // VALU: double-buffered batches
-  int lg;        // LG: 1 = 256 x 256 tiles (8 waves), 0 = 128 x 128 tiles (4 waves)
+  int lg;        // LG: tile configuration (LgTile in gemm.hip)
   int grid_x, grid_y;
   int splits;    // K splits (> 1: partial sums + reduction kernel)
 };
