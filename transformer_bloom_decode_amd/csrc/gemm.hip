@@ -243,21 +243,30 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-template <typename TW, int BM, int BN, int WGM, int WGN, int S>
+template <typename TW, int BM, int BN, int WGM, int WGN, int S, int BK>
 struct LgCfg {
   static constexpr int kWaves = WGM * WGN;
   static constexpr int kThreads = kWaves * 64;
   static constexpr int WTM = BM / WGM, WTN = BN / WGN;
   static constexpr int TM = WTM / 32, TN = WTN / 32;
-  static constexpr int WRB = kLg * (int)sizeof(TW);         // W bytes per row per K tile
-  static constexpr int CX = BM / 8, CW = BN * WRB / 1024;   // 1 KB pieces per K tile
+  static constexpr int XRB = BK * 2;                        // X bytes per row per K tile
+  static constexpr int WRB = BK * (int)sizeof(TW);          // W bytes per row per K tile
+  static constexpr int CX = BM * XRB / 1024, CW = BN * WRB / 1024;  // 1 KB pieces per K tile
   static constexpr int CPW = (CX + CW) / kWaves;           // pieces per wave per K tile
-  static constexpr int kStage = BM * 128 + BN * WRB;        // bytes per stage
+  static constexpr int kStage = BM * XRB + BN * WRB;        // bytes per stage
   static constexpr int kLds = S * kStage;
   static_assert((CX + CW) % kWaves == 0 && CPW * (S - 1) < 64, "piece split");
   static_assert(S >= 2 && S <= 4, "stages");
   static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
+  static_assert(BK == 64 || (BK == 32 && sizeof(TW) == 2), "K tile");
 };
+
+// LDS slot of 16-byte piece q of row r for rows of RB bytes (128 or 64): pieces are
+// XOR-swizzled by the row's position in the 256-byte bank period, which keeps 16
+// consecutive rows' reads of one piece on distinct banks.
+template <int RB> __device__ __forceinline__ int lg_slot(int r, int q) {
+  return RB == 128 ? (q ^ ((r >> 1) & 7)) : (q ^ ((r >> 2) & 3));
+}
 
 // The 16 outputs one lane holds of a 32x32 block: column n, rows m0 + 8 (v / 4) +
 // v % 4 (m0 includes the lane's 4 (lane / 32)).  Kept out of line: inlined for every
@@ -330,11 +339,12 @@ __device__ __attribute__((noinline)) void lg_argmax16(const EpiParams &ep, int N
   }
 }
 
-template <typename TW, typename TP, int BM, int BN, int WGM, int WGN, int S>
+template <typename TW, typename TP, int BM, int BN, int WGM, int WGN, int S, int BK,
+          bool SCHED = false>
 __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_lg(
     const bf16_t *__restrict__ X, const TW *__restrict__ W, int M, int N, int K,
     int tiles_m, int tiles_n, int splits, float *__restrict__ partial, EpiParams ep) {
-  using C = LgCfg<TW, BM, BN, WGM, WGN, S>;
+  using C = LgCfg<TW, BM, BN, WGM, WGN, S, BK>;
   constexpr bool kI8 = sizeof(TW) == 1;
   extern __shared__ __attribute__((aligned(1024))) unsigned char lg_lds[];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -344,28 +354,26 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_lg(
   const int L = xcd * (nb >> 3) + min(xcd, nb & 7) + slot;     // bijective renumbering
   const int mt = L % tiles_m, nt = (L / tiles_m) % tiles_n, z = L / (tiles_m * tiles_n);
   const int m0 = mt * BM, n0 = nt * BN;
-  const int KT = K / kLg;
+  const int KT = K / BK;
   const int kt0 = (int)(((long)KT * z) / splits), kt1 = (int)(((long)KT * (z + 1)) / splits);
 
-  // Source of each of this wave's pieces.  X (and bf16 W): lane -> row (lane >> 3) of
-  // 8 rows x 128 bytes, k-piece (lane & 7) ^ ((row >> 1) & 7).  int8 W: lane -> row
-  // (lane >> 2) of 16 rows x 64 bytes, 16-byte slot (lane & 3) ^ ((row >> 2) & 3).
+  // Source of each of this wave's pieces: a 1 KB piece holds 1024 / RB rows of RB
+  // bytes; lane -> row lane / (RB / 16), LDS slot lane % (RB / 16), which holds the
+  // row's 16-byte piece lg_slot(row, slot) (the swizzle is an involution).
   const unsigned char *src[C::CPW];
 #pragma unroll
   for (int c = 0; c < C::CPW; ++c) {
     const int pc = wid * C::CPW + c;
     if (pc < C::CX) {
-      const int rr = pc * 8 + (lane >> 3);
-      const int piece = (lane & 7) ^ ((rr >> 1) & 7);
-      src[c] = (const unsigned char *)(X + (size_t)min(m0 + rr, M - 1) * K + piece * 8);
-    } else if (!kI8) {
-      const int rr = (pc - C::CX) * 8 + (lane >> 3);
-      const int piece = (lane & 7) ^ ((rr >> 1) & 7);
-      src[c] = (const unsigned char *)(W + (size_t)min(n0 + rr, N - 1) * K + piece * 8);
+      constexpr int LPR = C::XRB / 16;
+      const int rr = pc * (1024 / C::XRB) + lane / LPR;
+      const int q = lg_slot<C::XRB>(rr, lane % LPR);
+      src[c] = (const unsigned char *)(X + (size_t)min(m0 + rr, M - 1) * K) + q * 16;
     } else {
-      const int rr = (pc - C::CX) * 16 + (lane >> 2);
-      const int slot = (lane & 3) ^ ((rr >> 2) & 3);
-      src[c] = (const unsigned char *)(W + (size_t)min(n0 + rr, N - 1) * K + slot * 16);
+      constexpr int LPR = C::WRB / 16;
+      const int rr = (pc - C::CX) * (1024 / C::WRB) + lane / LPR;
+      const int q = lg_slot<C::WRB>(rr, lane % LPR);
+      src[c] = (const unsigned char *)(W + (size_t)min(n0 + rr, N - 1) * K) + q * 16;
     }
   }
   auto issue = [&](int kt) {
@@ -373,7 +381,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_lg(
 #pragma unroll
     for (int c = 0; c < C::CPW; ++c) {
       const int pc = wid * C::CPW + c;
-      const size_t adv = (size_t)kt * (pc < C::CX ? kLg * 2 : C::WRB);   // bytes per K tile
+      const size_t adv = (size_t)kt * (pc < C::CX ? C::XRB : C::WRB);   // bytes per K tile
       __builtin_amdgcn_global_load_lds((const void *)(src[c] + adv),
                                        (__attribute__((address_space(3))) void *)(
                                            st + pc * 1024),
@@ -409,33 +417,45 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_lg(
     // operands of 16-wide substep s + 1 are read while the MFMAs of substep s run
     u32x4 a[2][C::TM], bv[2][C::TN];
     auto rd = [&](int s, int q) {
-      const int piece = 2 * s + (lane >> 5);
+      const int piece = 2 * s + (lane >> 5);   // 8-element k-piece within the K tile
 #pragma unroll
       for (int i = 0; i < C::TM; ++i) {
         const int r = wm * C::WTM + 32 * i + (lane & 31);
-        a[q][i] = *(const u32x4 *)(xb + r * 128 + 16 * (piece ^ ((r >> 1) & 7)));
+        a[q][i] = *(const u32x4 *)(xb + r * C::XRB + 16 * lg_slot<C::XRB>(r, piece));
       }
 #pragma unroll
       for (int j = 0; j < C::TN; ++j) {
         const int r = wn * C::WTN + 32 * j + (lane & 31);
         if constexpr (kI8) {
-          // 8 int8 of k-piece `piece`, widened to bf16 (exact)
-          const uint2 t = *(const uint2 *)(wb + r * 64 + 16 * ((piece >> 1) ^ ((r >> 2) & 3)) +
+          // 8 int8 of k-piece `piece` (half of a 16-byte slot), widened to bf16 (exact)
+          const uint2 t = *(const uint2 *)(wb + r * C::WRB +
+                                           16 * lg_slot<C::WRB>(r, piece >> 1) +
                                            8 * (piece & 1));
           bv[q][j] = i8x8_to_bf16x8(t.x, t.y);
         } else {
-          bv[q][j] = *(const u32x4 *)(wb + r * 128 + 16 * (piece ^ ((r >> 1) & 7)));
+          bv[q][j] = *(const u32x4 *)(wb + r * C::WRB + 16 * lg_slot<C::WRB>(r, piece));
         }
       }
     };
     rd(0, 0);
 #pragma unroll
-    for (int s = 0; s < kLg / 16; ++s) {
-      if (s + 1 < kLg / 16) rd(s + 1, (s + 1) & 1);
+    for (int s = 0; s < BK / 16; ++s) {
+      if (s + 1 < BK / 16) rd(s + 1, (s + 1) & 1);
 #pragma unroll
       for (int i = 0; i < C::TM; ++i)
 #pragma unroll
         for (int j = 0; j < C::TN; ++j) acc[i][j] = mfma32(a[s & 1][i], bv[s & 1][j], acc[i][j]);
+      if constexpr (SCHED) {
+        // interleave: one MFMA, then one of the next substep's LDS reads, ...
+        if (s + 1 < BK / 16) {
+#pragma unroll
+          for (int q = 0; q < C::TM + C::TN; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, C::TM * C::TN - (C::TM + C::TN), 0);
+        }
+      }
     }
   }
 
@@ -570,7 +590,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_argmax_merge(const float *__r
 // ---------------------------------------------------------------------------
 // Tile configurations of the direct-to-LDS GEMM (LinearPlan::lg).
 enum LgTile : int {
-  LG_256 = 1,      // 256 x 256, 8 waves, 2 stages (prompt pass, 1024+ rows)
+  LG_256 = 1,      // 256 x 256, 8 waves (4 x 2), 2 stages (prompt pass, 512+ rows)
   LG_128 = 0,      // 128 x 128, 4 waves, 2 stages (prompt pass, 256+ rows)
   LG_D32 = 2,      // 32 x 128, 4 waves, 4 stages (decode / short passes, <= 32 rows)
   LG_D64 = 3,      // 64 x 128, 4 waves, 3 stages (<= 64 rows)
@@ -612,10 +632,13 @@ LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax) {
   p.kind = LIN_LG;
   const int KT = K / kLg;
   if (!argmax && M >= 256) {
-    // Prompt passes: tiles of 256 x 256 (one block per CU: 128 KB of LDS) from 1024
-    // rows, else 128 x 128 (two blocks per CU).  Split-K is chosen to minimise
-    // (rounds of resident blocks) / splits, with a 10% charge for the reduction pass.
-    p.lg = M >= 1024 ? LG_256 : LG_128;
+    // Prompt passes: tiles of 256 x 256 (8 waves of 64 x 128, one block per CU: 128 KB
+    // of LDS) from 512 rows when K is long, else 128 x 128 (two blocks per CU).
+    // Split-K is chosen to minimise (rounds of resident blocks) / splits, with a 10%
+    // charge for the reduction pass.  Measured at 512 rows (176B share): QKV 29% of
+    // the bf16 MFMA peak with 256 x 256 tiles against 28% with 128 x 128, dense
+    // (K = 1792) 17% against 22%.
+    p.lg = (M >= 512 && K >= 4096) ? LG_256 : LG_128;
     const int bt = p.lg == LG_256 ? 256 : 128;
     const int slots = p.lg == LG_256 ? 256 : 512;
     p.grid_x = (M + bt - 1) / bt;
@@ -678,19 +701,20 @@ size_t linear_partial_bytes(const LinearPlan &p) {
   return p.splits > 1 ? (size_t)p.splits * p.M * p.N * sizeof(float) : 0;
 }
 
-template <typename TW, int BM, int BN, int WGM, int WGN, int S>
+template <typename TW, int BM, int BN, int WGM, int WGN, int S, int BK = kLg,
+          bool SCHED = false>
 static hipError_t launch_lg_t(const LinearPlan &p, const void *X, const void *W, float *partial,
                               const EpiParams &ep, hipStream_t st) {
-  using C = LgCfg<TW, BM, BN, WGM, WGN, S>;
+  using C = LgCfg<TW, BM, BN, WGM, WGN, S, BK>;
   static bool lds_attr = false;  // more than 64 KB of dynamic LDS must be allowed once
   if (!lds_attr) {
     const hipError_t e = hipFuncSetAttribute(
-        (const void *)k_gemm_lg<TW, bf16_t, BM, BN, WGM, WGN, S>,
+        (const void *)k_gemm_lg<TW, bf16_t, BM, BN, WGM, WGN, S, BK, SCHED>,
         hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
     if (e != hipSuccess) return e;
     lds_attr = true;
   }
-  BL_LAUNCH((k_gemm_lg<TW, bf16_t, BM, BN, WGM, WGN, S>),
+  BL_LAUNCH((k_gemm_lg<TW, bf16_t, BM, BN, WGM, WGN, S, BK, SCHED>),
             dim3((unsigned)(p.grid_x * p.grid_y * p.splits)), dim3(C::kThreads), C::kLds, st,
             (const bf16_t *)X, (const TW *)W, p.M, p.N, p.K, p.grid_x, p.grid_y, p.splits,
             partial, ep);
@@ -701,7 +725,7 @@ template <typename TW>
 static hipError_t launch_lg(const LinearPlan &p, const void *X, const void *W, float *partial,
                             const EpiParams &ep, hipStream_t st) {
   switch (p.lg) {
-    case LG_256: return launch_lg_t<TW, 256, 256, 2, 4, 2>(p, X, W, partial, ep, st);
+    case LG_256: return launch_lg_t<TW, 256, 256, 4, 2, 2>(p, X, W, partial, ep, st);
     case LG_128: return launch_lg_t<TW, 128, 128, 2, 2, 2>(p, X, W, partial, ep, st);
     case LG_D32: return launch_lg_t<TW, 32, 128, 1, 4, 4>(p, X, W, partial, ep, st);
     case LG_D64: return launch_lg_t<TW, 64, 128, 1, 4, 3>(p, X, W, partial, ep, st);
