@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--new-tokens", type=int, default=None)
     ap.add_argument("--layers", type=int, default=None, help="truncate the stack (development)")
+    ap.add_argument("--loop", choices=("eager", "graph"), default="eager",
+                    help="decode loop: one bloom_decode_step call per token, or bloom_generate "
+                         "(replays of a captured decode step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--no-kernel-timer", action="store_true",
@@ -221,9 +224,14 @@ def main():
     torch.cuda.synchronize()
     log(f"setup {time.perf_counter() - t0:.1f}s: {m.name} L={m.n_layer} B={B} P={P} new={n_new}")
 
+    graph = args.loop == "graph"
+
     def generation(ev_mid=None, timed=False):
         kv.struct.len = 0
         kv.struct.prompt_len = 0
+        if graph and not timed:
+            tb.bloom_generate(cfg, dw, kv, B, P, tok, vl, n_new, ids, None, ws, stream)
+            return
         if timed:
             tb.bloom_timer_pause(True)
         tb.bloom_prefill(cfg, dw, kv, B, P, tok, vl, ids[0], None, ws, stream)
@@ -246,13 +254,25 @@ def main():
     w0 = time.perf_counter()
     for k in range(K):
         ev[k][0].record(stream)
-        generation(ev[k][1])
+        generation(None if graph else ev[k][1])
         ev[k][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     gen_ms = [a.elapsed_time(c) for a, _, c in ev]
-    prefill_ms = [a.elapsed_time(b) for a, b, _ in ev]
-    decode_ms = [b.elapsed_time(c) / (n_new - 1) for _, b, c in ev]
+    if graph:
+        # bloom_generate is one call: time its prompt pass on its own, outside the
+        # timed region, and take the decode steps as the rest of each generation
+        for k in range(K):
+            kv.struct.len = kv.struct.prompt_len = 0
+            ev[k][0].record(stream)
+            tb.bloom_prefill(cfg, dw, kv, B, P, tok, vl, ids[0], None, ws, stream)
+            ev[k][1].record(stream)
+        torch.cuda.synchronize()
+        prefill_ms = [a.elapsed_time(b) for a, b, _ in ev]
+        decode_ms = [(g - p) / (n_new - 1) for g, p in zip(gen_ms, prefill_ms)]
+    else:
+        prefill_ms = [a.elapsed_time(b) for a, b, _ in ev]
+        decode_ms = [b.elapsed_time(c) / (n_new - 1) for _, b, c in ev]
 
     ms_per_step = wall * 1e3 / K
     ms_per_token = ms_per_step / (B * n_new)
@@ -306,7 +326,7 @@ def main():
                    "layers": m.n_layer, "hidden": m.hidden, "heads_local": m.n_head_local,
                    "heads_total": m.n_head_total, "ffn_local": m.ffn, "vocab": m.vocab,
                    "weights": m.weight_dtype, "kv_cache": True, "greedy": True,
-                   "parallelism": "none (1 GPU)"},
+                   "parallelism": "none (1 GPU)", "loop": args.loop},
         "tokens_per_s": round(B * n_new / (ms_per_step * 1e-3), 2),
         "prefill_ms": round(float(np.median(prefill_ms)), 3),
         "prefill_tflops": round(prefill_flops(m, B, P) / (float(np.median(prefill_ms)) * 1e-3)

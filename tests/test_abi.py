@@ -21,7 +21,7 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    for required in ("bloom_prefill", "bloom_decode_step", "alibi_masked_softmax",
+    for required in ("bloom_prefill", "bloom_decode_step", "bloom_generate", "alibi_masked_softmax",
                      "kv_cache_append", "bloom_workspace_bytes", "bloom_status_string"):
         assert required in names
 
@@ -146,6 +146,24 @@ def test_decode_validation_paths():
     f.kv.max_len = (1 << 20) + 1                                  # beyond the supported 2^20
     f.kv.len = 20
     assert _decode(f) == tb.BLOOM_EINVAL
+
+
+def _generate(f, batch=2, prompt=8, n_new=4, ws_bytes=1 << 40, ids=0x1000):
+    return tb.lib.bloom_generate(ctypes.byref(f.cfg), ctypes.byref(f.w), ctypes.byref(f.kv),
+                                 batch, prompt, 0x1000, 0x1000, n_new, ids, None, 0x1000,
+                                 ws_bytes, None)
+
+
+def test_generate_validation_paths():
+    f = _Fake(bi.BLOOM_560M)
+    assert _generate(f, prompt=8, n_new=26) == tb.BLOOM_ECAPACITY   # 8 + 25 > 32
+    assert _generate(f, batch=5) == tb.BLOOM_ECAPACITY
+    assert _generate(f, n_new=0) == tb.BLOOM_EINVAL
+    assert _generate(f, prompt=0) == tb.BLOOM_EINVAL
+    assert _generate(f, ids=None) == tb.BLOOM_EINVAL
+    assert _generate(f, ws_bytes=1024) == tb.BLOOM_EWORKSPACE
+    assert _generate(f, batch=0) == tb.BLOOM_OK
+    assert f.kv.len == 0 and f.kv.prompt_len == 0
 
 
 def test_kv_append_validation_paths():

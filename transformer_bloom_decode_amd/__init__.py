@@ -86,6 +86,8 @@ def _load():
                                   vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.bloom_decode_step.argtypes = [P(bloom_config), P(bloom_weights), P(bloom_kv_cache), _i32,
                                       vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.bloom_generate.argtypes = [P(bloom_config), P(bloom_weights), P(bloom_kv_cache), _i32,
+                                   _i32, vp, vp, _i32, vp, vp, vp, ctypes.c_size_t, vp]
     lib.alibi_masked_softmax.argtypes = [vp, _i32, vp, _i32, _i32, _i32, _i32, _i32, _i32, vp,
                                          _i32, vp]
     lib.kv_cache_append.argtypes = [P(bloom_config), P(bloom_kv_cache), _i32, _i32, _i32, vp, vp,
@@ -94,7 +96,7 @@ def _load():
     lib.bloom_timer_disable.argtypes = []
     lib.bloom_timer_read.argtypes = [_i32, P(ctypes.c_double), P(_i32), P(ctypes.c_double)]
     lib.bloom_timer_pause.argtypes = [_i32]
-    for name in ("bloom_workspace_bytes", "bloom_prefill", "bloom_decode_step",
+    for name in ("bloom_workspace_bytes", "bloom_prefill", "bloom_decode_step", "bloom_generate",
                  "alibi_masked_softmax", "kv_cache_append", "bloom_timer_enable",
                  "bloom_timer_disable", "bloom_timer_read", "bloom_timer_pause"):
         getattr(lib, name).restype = ctypes.c_int
@@ -160,6 +162,16 @@ def bloom_decode_step(cfg, weights, kv, batch: int, tokens, valid_len, next_toke
                                  _ptr(tokens), _ptr(valid_len), _ptr(next_tokens),
                                  _ptr(hidden_out), _ptr(ws), _nbytes(ws), _stream(stream)),
            "bloom_decode_step")
+
+
+def bloom_generate(cfg, weights, kv, batch: int, prompt_len: int, tokens, valid_len, n_new: int,
+                   ids, hidden_out, ws, stream=None):
+    w = weights.struct if hasattr(weights, "struct") else weights
+    k = kv.struct if hasattr(kv, "struct") else kv
+    _check(lib.bloom_generate(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(k), batch,
+                              prompt_len, _ptr(tokens), _ptr(valid_len), n_new, _ptr(ids),
+                              _ptr(hidden_out), _ptr(ws), _nbytes(ws), _stream(stream)),
+           "bloom_generate")
 
 
 def alibi_masked_softmax(scores, in_dtype: int, valid_len, B: int, H: int, Q: int, K: int,
@@ -280,15 +292,17 @@ def workspace(cfg: bloom_config, max_batch: int, max_prompt: int, device="cuda")
 
 
 def greedy_generate(cfg: bloom_config, weights: DeviceWeights, kv: KVCache, tokens, valid_len,
-                    n_new: int, ws, want_hidden: bool = True, stream=None):
+                    n_new: int, ws, want_hidden: bool = True, stream=None, graph: bool = False):
     """Greedy generation loop ("Incredibly Fast BLOOM Inference with DeepSpeed and
     Accelerate", Benchmark Environment): one bloom_prefill over the left-padded prompt
     (which yields the first new token), then n_new - 1 bloom_decode_step calls.  Token
-    ids stay on the device between steps.
+    ids stay on the device between steps.  With graph=True the whole loop is one
+    bloom_generate call, which replays a captured decode step.
 
     tokens [batch, prompt_len] int32 and valid_len [batch] int32 are device tensors.
     Returns (ids [n_new, batch] int32, hidden [n_new, batch, hidden] float32 or None),
-    both on the device; nothing is synchronised.
+    both on the device; nothing is synchronised in the eager loop (bloom_generate
+    returns after its replays have finished).
     """
     import torch
     batch, prompt_len = tokens.shape
@@ -296,6 +310,10 @@ def greedy_generate(cfg: bloom_config, weights: DeviceWeights, kv: KVCache, toke
     ids = torch.empty((n_new, batch), dtype=torch.int32, device=dev)
     hid = (torch.empty((n_new, batch, cfg.hidden), dtype=torch.float32, device=dev)
            if want_hidden else None)
+    if graph:
+        bloom_generate(cfg, weights, kv, batch, prompt_len, tokens, valid_len, n_new, ids, hid,
+                       ws, stream)
+        return ids, hid
     bloom_prefill(cfg, weights, kv, batch, prompt_len, tokens, valid_len, ids[0],
                   None if hid is None else hid[0], ws, stream)
     for t in range(1, n_new):

@@ -40,6 +40,7 @@ int hip_fail(hipError_t e) {
 }
 
 struct WsPlan {
+  size_t gen, cur, nxt, hfix;   // generation loop state (same offsets for every pass)
   size_t x, xa, q, o, u, af, amv, ami, part, total;
   int lm_blocks;
 };
@@ -61,6 +62,10 @@ WsPlan plan_ws(const bloom_config *c, int batch, int tokens_per_row) {
   const size_t hd = (size_t)c->n_head_local * c->head_dim;
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off += align256(bytes); return o; };
+  p.gen = take(2 * sizeof(int));
+  p.cur = take((size_t)batch * sizeof(int));
+  p.nxt = take((size_t)batch * sizeof(int));
+  p.hfix = take((size_t)batch * c->hidden * sizeof(float));
   p.x = take(M * c->hidden * 4);
   p.xa = take(M * c->hidden * act);
   p.q = take(M * hd * 4);
@@ -137,6 +142,7 @@ int check_kv(const bloom_config *c, const bloom_kv_cache *kv) {
 struct Timer {
   bool on = false;
   bool paused = false;
+  bool capturing = false;   // launches being captured into a graph are never timed
   std::vector<hipEvent_t> start, stop;
   std::vector<int> cls;
   std::vector<double> bytes;
@@ -166,7 +172,8 @@ int kernel_class(const LinearPlan &p) {
 template <typename F>
 hipError_t timed(int cls, double wbytes, hipStream_t st, F &&launch) {
   (void)st;
-  const bool on = g_timer.on && !g_timer.paused && g_timer.used < (int)g_timer.start.size();
+  const bool on = g_timer.on && !g_timer.paused && !g_timer.capturing &&
+                  g_timer.used < (int)g_timer.start.size();
   if (on) g_launch_events = LaunchEvents{g_timer.start[g_timer.used], g_timer.stop[g_timer.used]};
   hipError_t err = launch();
   g_launch_events = LaunchEvents{};
@@ -185,13 +192,24 @@ hipError_t timed_linear(int wdt, const LinearPlan &p, const void *X, const void 
                [&] { return launch_linear(wdt, p, X, W, part, ep, st); });
 }
 
+// Non-blocking stream (default priority) per device on which bloom_generate captures its
+// decode step; created on first use, kept for the life of the process.
+hipStream_t capture_stream() {
+  static hipStream_t side[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  if (!side[dev] && hipStreamCreateWithFlags(&side[dev], hipStreamNonBlocking) != hipSuccess)
+    side[dev] = nullptr;
+  return side[dev];
+}
+
 // ---------------------------------------------------------------------------
 // one forward pass over `tpr` tokens per row
 // ---------------------------------------------------------------------------
 int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *kv, int batch,
                 int tpr, int pos_base, int prompt_len, const int32_t *d_tokens,
                 const int32_t *d_valid, int32_t *d_next, float *d_hidden, char *ws,
-                hipStream_t st) {
+                hipStream_t st, const int *d_pos = nullptr) {
   const WsPlan wp = plan_ws(c, batch, tpr);
   const bool f32 = c->weight_dtype == BLOOM_F32;
   const int wdt = wtype(c);
@@ -238,13 +256,13 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
     e.scale = (const uint16_t *)L.s_qkv;
     e.q = q; e.kc = kc; e.vc = vc;
     e.H = H; e.d = d; e.max_len = kv->max_len;
-    e.pos_base = pos_base; e.rows_per_seq = tpr;
+    e.pos_base = pos_base; e.pos_dev = d_pos; e.rows_per_seq = tpr;
     e.q_scale = 1.0f / sqrtf((float)d);
     err = timed_linear(wdt, p_qkv, xa, L.w_qkv, part, e, st, wbytes(3 * hd, h));
     if (err != hipSuccess) return hip_fail(err);
 
     err = launch_attention(f32, q, kc, vc, d_valid, o, M, H, d, kv->max_len, c->n_head_total,
-                           c->head_offset, tpr, pos_base, prompt_len, st);
+                           c->head_offset, tpr, pos_base, d_pos, prompt_len, st);
     if (err != hipSuccess) return hip_fail(err);
 
     EpiParams r{};
@@ -370,6 +388,78 @@ int bloom_decode_step(const bloom_config *cfg, const bloom_weights *w, bloom_kv_
                   d_next_tokens, d_hidden_out, (char *)d_ws, (hipStream_t)stream);
   if (s == BLOOM_OK) kv->len += 1;
   return s;
+}
+
+int bloom_generate(const bloom_config *cfg, const bloom_weights *w, bloom_kv_cache *kv,
+                   int32_t batch, int32_t prompt_len, const int32_t *d_tokens,
+                   const int32_t *d_valid_len, int32_t n_new, int32_t *d_ids, float *d_hidden,
+                   void *d_ws, size_t ws_bytes, void *stream) {
+  int s = check_config(cfg);
+  if (s != BLOOM_OK) return s;
+  if ((s = check_weights(cfg, w)) != BLOOM_OK) return s;
+  if ((s = check_kv(cfg, kv)) != BLOOM_OK) return s;
+  if (batch < 0 || prompt_len < 1 || n_new < 1) return BLOOM_EINVAL;
+  if (batch > kv->max_batch || (long)prompt_len + n_new - 1 > kv->max_len) return BLOOM_ECAPACITY;
+  if (batch == 0) return BLOOM_OK;
+  if (!d_tokens || !d_valid_len || !d_ids || !d_ws) return BLOOM_EINVAL;
+  if (ws_bytes < plan_ws(cfg, batch, prompt_len).total) return BLOOM_EWORKSPACE;
+  clear_stale_hip_error();
+  hipStream_t st = (hipStream_t)stream;
+  char *ws = (char *)d_ws;
+  const size_t hsz = (size_t)batch * cfg->hidden;
+  // the prompt pass, then the first step eagerly (it also runs any one-time set-up)
+  s = run_forward(cfg, w, kv, batch, prompt_len, 0, prompt_len, d_tokens, d_valid_len, d_ids,
+                  d_hidden, ws, st);
+  if (s != BLOOM_OK) return s;
+  kv->prompt_len = prompt_len;
+  kv->len = prompt_len;
+  if (n_new == 1) return BLOOM_OK;
+  s = run_forward(cfg, w, kv, batch, 1, kv->len, kv->prompt_len, d_ids, d_valid_len,
+                  d_ids + batch, d_hidden ? d_hidden + hsz : nullptr, ws, st);
+  if (s != BLOOM_OK) return s;
+  kv->len += 1;
+  if (n_new == 2) return BLOOM_OK;
+
+  // One decode step captured on a side stream: position and input tokens come from
+  // device memory, so the same graph is replayed for every remaining step.
+  const WsPlan wp = plan_ws(cfg, batch, 1);
+  int *state = (int *)(ws + wp.gen);
+  int *cur = (int *)(ws + wp.cur);
+  int *nxt = (int *)(ws + wp.nxt);
+  float *hfix = d_hidden ? (float *)(ws + wp.hfix) : nullptr;
+  hipError_t err = launch_gen_init(state, kv->len, 2, d_ids + batch, cur, batch, st);
+  if (err != hipSuccess) return hip_fail(err);
+  hipStream_t side = capture_stream();
+  if (!side) return hip_fail(hipErrorInvalidResourceHandle);
+  if ((err = hipStreamBeginCapture(side, hipStreamCaptureModeThreadLocal)) != hipSuccess)
+    return hip_fail(err);
+  g_timer.capturing = true;
+  s = run_forward(cfg, w, kv, batch, 1, 0, kv->prompt_len, cur, d_valid_len, nxt, hfix, ws, side,
+                  state);
+  g_timer.capturing = false;
+  if (s == BLOOM_OK) {
+    err = launch_gen_record(nxt, cur, d_ids, hfix, d_hidden, state, batch, cfg->hidden, side);
+    if (err != hipSuccess) s = hip_fail(err);
+  }
+  hipGraph_t graph = nullptr;
+  const hipError_t cerr = hipStreamEndCapture(side, &graph);
+  if (s != BLOOM_OK) {
+    if (graph) (void)hipGraphDestroy(graph);
+    return s;
+  }
+  if (cerr != hipSuccess) return hip_fail(cerr);
+  hipGraphExec_t exec = nullptr;
+  err = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(graph);
+  if (err != hipSuccess) return hip_fail(err);
+  for (int t = 2; t < n_new && err == hipSuccess; ++t) err = hipGraphLaunch(exec, st);
+  // the executable graph is released once its launches have finished
+  const hipError_t serr = hipStreamSynchronize(st);
+  (void)hipGraphExecDestroy(exec);
+  if (err != hipSuccess) return hip_fail(err);
+  if (serr != hipSuccess) return hip_fail(serr);
+  kv->len = prompt_len + n_new - 1;
+  return BLOOM_OK;
 }
 
 int alibi_masked_softmax(const void *d_scores, int32_t in_dtype, const int32_t *d_valid_len,

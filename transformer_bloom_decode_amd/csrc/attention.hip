@@ -72,14 +72,15 @@ __global__ __launch_bounds__(256) void k_attention(const float *__restrict__ q,
                                                    const int *__restrict__ valid_len,
                                                    TA *__restrict__ o, int H, int d, int max_len,
                                                    int n_total, int head_off, int rows_per_seq,
-                                                   int pos_base, int prompt_len) {
+                                                   int pos_base, const int *__restrict__ pos_dev,
+                                                   int prompt_len) {
   constexpr int KB = KeysPerBatch<TA>::value;
   __shared__ float pv[256 * 8];     // [G][d] per-group P.V partials
   __shared__ float red[4];
   const int m = blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x;
   const int b = m / rows_per_seq;
-  const int qpos = pos_base + (m - b * rows_per_seq);
+  const int qpos = (pos_dev ? *pos_dev : pos_base) + (m - b * rows_per_seq);
   // The K/V loads below address slots 0..qpos directly and do not wait for valid_len:
   // the left-pad slots [0, first) are loaded too (the prompt pass wrote them) and
   // masked in the scores.
@@ -171,17 +172,17 @@ __global__ __launch_bounds__(256) void k_attention(const float *__restrict__ q,
 hipError_t launch_attention(bool f32, const float *q, const void *kc, const void *vc,
                             const int *valid_len, void *o, int rows, int H, int d, int max_len,
                             int n_total, int head_off, int rows_per_seq, int pos_base,
-                            int prompt_len, hipStream_t st) {
+                            const int *pos_dev, int prompt_len, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
   const dim3 grid(rows, H), block(256);
   if (f32)
     hipLaunchKernelGGL(k_attention<float>, grid, block, 0, st, q, (const float *)kc,
                        (const float *)vc, valid_len, (float *)o, H, d, max_len, n_total,
-                       head_off, rows_per_seq, pos_base, prompt_len);
+                       head_off, rows_per_seq, pos_base, pos_dev, prompt_len);
   else
     hipLaunchKernelGGL(k_attention<bf16_t>, grid, block, 0, st, q, (const bf16_t *)kc,
                        (const bf16_t *)vc, valid_len, (bf16_t *)o, H, d, max_len, n_total,
-                       head_off, rows_per_seq, pos_base, prompt_len);
+                       head_off, rows_per_seq, pos_base, pos_dev, prompt_len);
   return hipGetLastError();
 }
 

@@ -129,6 +129,7 @@ struct EpiParams {
   void *kc, *vc;           // cache of this layer: [max_batch][H][max_len][d]
   int H, d, max_len;
   int pos_base;            // absolute position of row m is pos_base + m % rows_per_seq
+  const int *pos_dev;      // if set, *pos_dev replaces pos_base (replayed decode step)
   int rows_per_seq;        // 1 (decode) or the prompt length (prefill)
   float q_scale;           // 1/sqrt(d)
   // EPI_RESID / EPI_GELU / EPI_STORE
@@ -158,7 +159,7 @@ __device__ __forceinline__ void epilogue(const EpiParams &e, int m, int n, float
         e.q[((size_t)m * H + hd) * d + c] = y * e.q_scale;
       } else {
         const int b = m / e.rows_per_seq;
-        const int pos = e.pos_base + (m - b * e.rows_per_seq);
+        const int pos = (e.pos_dev ? *e.pos_dev : e.pos_base) + (m - b * e.rows_per_seq);
         TA *cache = (TA *)(t == 1 ? e.kc : e.vc);
         cache[(((size_t)b * H + hd) * e.max_len + pos) * d + c] = from_f<TA>(y);
       }

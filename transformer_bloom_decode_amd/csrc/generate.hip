@@ -1,0 +1,57 @@
+// Device-side bookkeeping of the greedy generation loop ("Incredibly Fast BLOOM
+// Inference with DeepSpeed and Accelerate", Benchmark Environment: greedy decoding of
+// new tokens with the KV cache).  The decode step that bloom_generate captures in a HIP
+// graph reads its KV position and input tokens from device memory, so one graph serves
+// every step; these kernels record each step's output and advance the position.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace bl {
+
+__global__ void k_gen_init(int *__restrict__ state, int pos, int step,
+                           const int *__restrict__ first, int *__restrict__ cur, int batch) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < batch; i += gridDim.x * blockDim.x)
+    cur[i] = first[i];
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    state[0] = pos;
+    state[1] = step;
+  }
+}
+
+// One block: every thread reads the step index before thread 0 advances it.
+__global__ __launch_bounds__(1024) void k_gen_record(const int *__restrict__ next,
+                                                     int *__restrict__ cur, int *__restrict__ ids,
+                                                     const float *__restrict__ hfix,
+                                                     float *__restrict__ hout, int *state,
+                                                     int batch, int hidden) {
+  const int t = state[1];
+  for (int i = threadIdx.x; i < batch; i += blockDim.x) {
+    ids[(size_t)t * batch + i] = next[i];
+    cur[i] = next[i];
+  }
+  if (hout) {
+    const size_t n = (size_t)batch * hidden;
+    float *dst = hout + (size_t)t * n;
+    for (size_t i = threadIdx.x; i < n; i += blockDim.x) dst[i] = hfix[i];
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    state[0] += 1;
+    state[1] = t + 1;
+  }
+}
+
+hipError_t launch_gen_init(int *state, int pos, int step, const int *first, int *cur, int batch,
+                           hipStream_t st) {
+  hipLaunchKernelGGL(k_gen_init, dim3(1), dim3(256), 0, st, state, pos, step, first, cur, batch);
+  return hipGetLastError();
+}
+
+hipError_t launch_gen_record(const int *next, int *cur, int *ids, const float *hfix, float *hout,
+                             int *state, int batch, int hidden, hipStream_t st) {
+  hipLaunchKernelGGL(k_gen_record, dim3(1), dim3(1024), 0, st, next, cur, ids, hfix, hout, state,
+                     batch, hidden);
+  return hipGetLastError();
+}
+
+}  // namespace bl

@@ -84,7 +84,16 @@ hipError_t launch_layernorm(bool f32, const float *x, int in_step, int in_off, c
 hipError_t launch_attention(bool f32, const float *q, const void *kc, const void *vc,
                             const int *valid_len, void *o, int rows, int H, int d, int max_len,
                             int n_total, int head_off, int rows_per_seq, int pos_base,
-                            int prompt_len, hipStream_t st);
+                            const int *pos_dev, int prompt_len, hipStream_t st);
+
+// Bookkeeping of a replayed generation step (state[0] = KV position, state[1] = index of
+// the step being recorded): ids[step][b] = next[b], cur[b] = next[b], hout[step] = hfix
+// (hout nullable); then state[0] += 1, state[1] += 1.  gen_init seeds the state and the
+// current tokens.
+hipError_t launch_gen_init(int *state, int pos, int step, const int *first, int *cur, int batch,
+                           hipStream_t st);
+hipError_t launch_gen_record(const int *next, int *cur, int *ids, const float *hfix, float *hout,
+                             int *state, int batch, int hidden, hipStream_t st);
 hipError_t launch_kv_append(bool f32, const void *k, const void *v, void *ck, void *cv,
                             int batch, int H, int n_new, int d, int max_len, int pos,
                             hipStream_t st);
