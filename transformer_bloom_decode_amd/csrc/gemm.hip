@@ -238,6 +238,18 @@ template <int V> __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((V & 15) | ((V >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Wait until at most J * CPW loads of this wave are outstanding, for the largest J <=
+// `after` (J <= JMAX): the copies of every K tile issued before the last `after` have
+// landed.
+template <int CPW, int JMAX> __device__ __forceinline__ void lg_wait(int after) {
+  if constexpr (JMAX <= 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (after >= JMAX) wait_vmcnt<JMAX * CPW>();
+    else lg_wait<CPW, JMAX - 1>(after);
+  }
+}
+
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -256,7 +268,7 @@ struct LgCfg {
   static constexpr int kStage = BM * XRB + BN * WRB;        // bytes per stage
   static constexpr int kLds = S * kStage;
   static_assert((CX + CW) % kWaves == 0 && CPW * (S - 1) < 64, "piece split");
-  static_assert(S >= 2 && S <= 4, "stages");
+  static_assert(S >= 2 && S <= 6, "stages");
   static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
   static_assert(BK == 64 || (BK == 32 && sizeof(TW) == 2), "K tile");
 };
@@ -404,10 +416,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_lg(
     // fence, which would make the compiler wait for every outstanding load) then makes
     // every wave's copies visible, and also orders every wave's reads of the stage
     // refilled below, which the previous step read.
-    const int after = min(S - 2, kt1 - 1 - kt);
-    if (S >= 4 && after >= 2) wait_vmcnt<(S >= 4 ? 2 * C::CPW : 0)>();
-    else if (S >= 3 && after >= 1) wait_vmcnt<(S >= 3 ? C::CPW : 0)>();
-    else wait_vmcnt<0>();
+    lg_wait<C::CPW, S - 2>(min(S - 2, kt1 - 1 - kt));
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_barrier();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
