@@ -127,18 +127,25 @@ def test_bloom560m_wide_batch_uses_tiled_and_wide_gemv():
     assert v.hidden_rel <= 1e-2 and v.tokens_ok
 
 
-def test_long_rows_cross_attention_batches():
-    """head_dim 128 and up to 160 visible keys: more keys than one batch of the attention
-    kernel (16 lane groups x 8 keys), so the running-max rescale across batches runs."""
-    m = dataclasses.replace(bi.BLOOM_560M, name="d128", n_layer=1, hidden=256, n_head_total=2,
-                            n_head_local=2, head_dim=128, ffn=1024, vocab=512)
+@pytest.mark.parametrize("d, P, valid", [(128, 100, (100, 37)), (256, 70, (70, 1)),
+                                         (64, 130, (130, 129, 64))])
+def test_long_rows_cross_attention_batches(d, P, valid):
+    """Long prompts and up to P + 59 visible keys: the prompt pass runs several chunks of
+    query rows per sequence and several LDS key tiles (32 keys per tile at d = 256, 64
+    otherwise), with padding that leaves whole chunks without a visible key; the decode
+    steps see more keys than one batch of the decode kernel (16 lane groups x 8 keys at
+    d = 128), so the running-max rescale across batches runs."""
+    H = 512 // d
+    m = dataclasses.replace(bi.BLOOM_560M, name=f"d{d}", n_layer=1, hidden=512, n_head_total=H,
+                            n_head_local=H, head_dim=d, ffn=1024, vocab=512)
     T, dw, cfg = upload(m, seed=21)
-    prompt, valid = bi.prompts(m, 2, 100, (100, 37), seed=22)
+    B = len(valid)
+    prompt, valid = bi.prompts(m, B, P, valid, seed=22)
     run = run_gpu(cfg, dw, prompt, valid, 60)
     v = compare(m, T, prompt, valid, run, 1e-2)
-    print(f"d128 L1 T<=160: hidden rel {v.hidden_rel:.2e}, exact ids {v.exact_frac:.3f}")
+    print(f"d{d} L1 P{P}: hidden rel {v.hidden_rel:.2e}, exact ids {v.exact_frac:.3f}")
     assert v.hidden_rel <= 1e-2 and v.tokens_ok
-    _kv_check(run, v.oracle, 2, 100 + 59, 2e-2)
+    _kv_check(run, v.oracle, B, P + 59, 2e-2)
 
 
 @pytest.mark.parametrize("hidden, ffn, n_new", [(2112, 4224, 24), (3072, 8192, 12)])

@@ -169,11 +169,125 @@ __global__ __launch_bounds__(256) void k_attention(const float *__restrict__ q,
   }
 }
 
+// Prompt pass: the same attention for the rows_per_seq query rows of each sequence,
+// one 256-thread block per (sequence b, head h, chunk of 256 / (d/8) query rows).  Lane
+// group g (d/8 lanes) owns query row r = chunk * rows_per_block + g at position
+// qpos = pos_base + r; the block walks the keys from the sequence's first valid slot to
+// its last row's position in tiles staged in LDS (each tile read once from the cache and
+// shared by all the block's rows), 8 keys at a time per group: scores (masked above
+// qpos: causal), their maximum, the rescale of the running sum and P.V accumulators,
+// then exp and P.V -- the online form of the same float32 softmax.  A row with no
+// visible key gets o = 0, as in k_attention.
+constexpr int kPromptTileBytes = 16384;   // LDS per K (and per V) tile
+
+template <typename TA>
+__global__ __launch_bounds__(256) void k_attention_prompt(
+    const float *__restrict__ q, const TA *__restrict__ kc, const TA *__restrict__ vc,
+    const int *__restrict__ valid_len, TA *__restrict__ o, int H, int d, int max_len,
+    int n_total, int head_off, int rows_per_seq, int pos_base, int prompt_len, int nchunk) {
+  __shared__ __attribute__((aligned(16))) unsigned char ks_raw[kPromptTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char vs_raw[kPromptTileBytes];
+  const TA *ks = (const TA *)ks_raw;
+  const TA *vs = (const TA *)vs_raw;
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x / nchunk, c = blockIdx.x - b * nchunk, h = blockIdx.y;
+  const int L = d >> 3, QR = 256 / L;
+  const int g = tid / L, sub = tid - g * L;
+  const int r = c * QR + g;
+  const bool active = r < rows_per_seq;
+  const int qpos = pos_base + r;
+  const int last = pos_base + min(rows_per_seq, c * QR + QR) - 1;   // block's last position
+  const int vl_in = valid_len[b];
+  const int vl = vl_in < 1 ? 1 : (vl_in > prompt_len ? prompt_len : vl_in);
+  const int first = prompt_len - vl;
+  const float slope = alibi_slope(n_total, head_off + h);
+  const size_t head_base = ((size_t)b * H + h) * (size_t)max_len * d;
+  const TA *kb = kc + head_base;
+  const TA *vb = vc + head_base;
+  const size_t m = (size_t)b * rows_per_seq + (active ? r : 0);
+  float qv[8];
+  const float *qr = q + (m * H + h) * d + 8 * sub;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) qv[t] = active ? qr[t] : 0.f;
+
+  const int tile = min(64, kPromptTileBytes / (d * (int)sizeof(TA)));   // keys per tile
+  const int piece_elems = 16 / (int)sizeof(TA);
+  float mrun = -INFINITY, lsum = 0.f;
+  float acc[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) acc[t] = 0.f;
+  for (int j0 = first; j0 <= last; j0 += tile) {
+    const int cnt = min(tile, last + 1 - j0);
+    __syncthreads();   // the previous tile has been read by every group
+    const int pieces = cnt * d / piece_elems;
+    for (int i = tid; i < pieces; i += 256) {
+      ((u32x4 *)ks_raw)[i] = *(const u32x4 *)(kb + (size_t)j0 * d + (size_t)i * piece_elems);
+      ((u32x4 *)vs_raw)[i] = *(const u32x4 *)(vb + (size_t)j0 * d + (size_t)i * piece_elems);
+    }
+    __syncthreads();
+    // every group runs every key of the tile (the shuffles stay convergent); keys
+    // above the group's own position are masked
+    for (int u0 = 0; u0 < cnt; u0 += 8) {
+      float sc[8];
+      float cmax = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int jj = u0 + u;
+        float dot = 0.f;
+        if (jj < cnt) {
+          const TA *kp = ks + jj * d + 8 * sub;
+#pragma unroll
+          for (int t = 0; t < 8; ++t) dot = fmaf(qv[t], to_f<TA>(kp[t]), dot);
+        }
+        for (int off = L >> 1; off > 0; off >>= 1) dot += __shfl_xor(dot, off, 64);
+        const int j = j0 + jj;
+        sc[u] = (jj < cnt && j <= qpos) ? dot + slope * (float)(j - qpos) : -INFINITY;
+        cmax = fmaxf(cmax, sc[u]);
+      }
+      const float mnew = fmaxf(mrun, cmax);
+      if (mnew == -INFINITY) continue;        // nothing visible to this row yet
+      const float alpha = mrun == -INFINITY ? 0.f : __expf(mrun - mnew);
+      lsum *= alpha;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc[t] *= alpha;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (sc[u] == -INFINITY) continue;
+        const float p = __expf(sc[u] - mnew);
+        lsum += p;
+        const TA *vp = vs + (u0 + u) * d + 8 * sub;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) acc[t] = fmaf(p, to_f<TA>(vp[t]), acc[t]);
+      }
+      mrun = mnew;
+    }
+  }
+  if (!active) return;
+  const float inv = (qpos < first || lsum == 0.f) ? 0.f : 1.0f / lsum;
+  TA *out = o + (m * H + h) * d + 8 * sub;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) out[t] = from_f<TA>(acc[t] * inv);
+}
+
 hipError_t launch_attention(bool f32, const float *q, const void *kc, const void *vc,
                             const int *valid_len, void *o, int rows, int H, int d, int max_len,
                             int n_total, int head_off, int rows_per_seq, int pos_base,
                             const int *pos_dev, int prompt_len, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
+  if (rows_per_seq > 1 && !pos_dev) {
+    const int QR = 256 / (d >> 3);
+    const int nchunk = (rows_per_seq + QR - 1) / QR;
+    const dim3 grid((unsigned)(rows / rows_per_seq * nchunk), H), block(256);
+    if (f32)
+      hipLaunchKernelGGL(k_attention_prompt<float>, grid, block, 0, st, q, (const float *)kc,
+                         (const float *)vc, valid_len, (float *)o, H, d, max_len, n_total,
+                         head_off, rows_per_seq, pos_base, prompt_len, nchunk);
+    else
+      hipLaunchKernelGGL(k_attention_prompt<bf16_t>, grid, block, 0, st, q, (const bf16_t *)kc,
+                         (const bf16_t *)vc, valid_len, (bf16_t *)o, H, d, max_len, n_total,
+                         head_off, rows_per_seq, pos_base, prompt_len, nchunk);
+    return hipGetLastError();
+  }
   const dim3 grid(rows, H), block(256);
   if (f32)
     hipLaunchKernelGGL(k_attention<float>, grid, block, 0, st, q, (const float *)kc,
