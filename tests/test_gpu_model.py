@@ -165,12 +165,14 @@ def test_batch1_fused_layernorm_and_whole_row_gemv(hidden, ffn, n_new):
 
 
 @pytest.mark.parametrize("wdt, tol", [("bf16", 1e-2), ("int8", 2e-2)])
-@pytest.mark.parametrize("batch, hidden, ffn", [(20, 1088, 4160), (70, 1088, 4160)])
+@pytest.mark.parametrize("batch, hidden, ffn", [(20, 1088, 4160), (40, 1088, 4160),
+                                                (70, 1088, 4160)])
 def test_prompt_pass_direct_to_lds_gemm_ragged(batch, hidden, ffn, wdt, tol):
-    """Prompt passes of 320 and 1120 rows run the direct-to-LDS MFMA GEMM (128 x 128 and
-    256 x 256 tiles, split-K) with M and N that are not multiples of the tile, and
-    ragged left padding; the decode steps (20 and 70 rows) its skinny tiles; int8
-    weights are widened from LDS and scaled per row in the epilogue."""
+    """Prompt passes of 320, 640 and 1120 rows run the direct-to-LDS MFMA GEMM (128 x
+    128, 256 x 128 and 256 x 256 tiles, split-K) with M and N that are not multiples of
+    the tile, and ragged left padding; the decode steps (20, 40 and 70 rows) its skinny
+    tiles (32 x 256 for int8 weights at 20 rows); int8 weights are widened from LDS and
+    scaled per row in the epilogue."""
     m = dataclasses.replace(bi.BLOOM_560M, name=f"lg{batch}", n_layer=2, hidden=hidden,
                             n_head_total=16, n_head_local=16, head_dim=64, ffn=ffn, vocab=4096,
                             weight_dtype=wdt)
@@ -182,6 +184,24 @@ def test_prompt_pass_direct_to_lds_gemm_ragged(batch, hidden, ffn, wdt, tol):
           f"exact ids {v.exact_frac:.3f}")
     assert v.hidden_rel <= tol and v.tokens_ok
     _kv_check(run, v.oracle, batch, 16 + 2, 2e-2)
+
+
+@pytest.mark.parametrize("batch", [48, 100])
+def test_int8_wide_ffn_decode_tiles(batch):
+    """int8 weights with a 32832-wide MLP (not a multiple of 256): decode steps of 48
+    rows run the MLP-up with 64 x 256 tiles and the other linears with 64 x 128 tiles,
+    100 rows the 128-row tile with all four waves side by side; splits from the
+    rounds-of-resident-blocks rule."""
+    m = dataclasses.replace(bi.BLOOM_560M, name=f"i8w{batch}", n_layer=2, hidden=1088,
+                            n_head_total=16, n_head_local=16, head_dim=64, ffn=32832,
+                            vocab=4096, weight_dtype="int8")
+    T, dw, cfg = upload(m, seed=51)
+    prompt, valid = bi.prompts(m, batch, 4, np.arange(batch) % 4 + 1, seed=52)
+    run = run_gpu(cfg, dw, prompt, valid, 3)
+    v = compare(m, T, prompt, valid, run, 2e-2)
+    print(f"int8 ffn 32832 B{batch}: hidden rel {v.hidden_rel:.2e}, exact ids {v.exact_frac:.3f}")
+    assert v.hidden_rel <= 2e-2 and v.tokens_ok
+    _kv_check(run, v.oracle, batch, 4 + 2, 4e-2)
 
 
 def test_tp_share_176b_prompt_pass_batch32():

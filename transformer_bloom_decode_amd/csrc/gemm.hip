@@ -604,6 +604,10 @@ enum LgTile : int {
   LG_D32 = 2,      // 32 x 128, 4 waves, 4 stages (decode / short passes, <= 32 rows)
   LG_D64 = 3,      // 64 x 128, 4 waves, 3 stages (<= 64 rows)
   LG_D128 = 4,     // 128 x 128, 4 waves, 3 stages (<= 128 rows)
+  LG_256x128 = 5,  // 256 x 128, 8 waves (4 x 2), 3 stages (prompt pass, 512-1023 rows)
+  LG_D32W = 6,     // 32 x 256, 4 waves, 4 stages (int8 weights, <= 32 rows)
+  LG_D64W = 7,     // 64 x 256, 4 waves (1 x 4), 3 stages (int8 weights, <= 64 rows, long N)
+  LG_D128N = 8,    // 128 x 128, 4 waves (1 x 4), 3 stages (int8 weights, <= 128 rows)
 };
 
 LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax) {
@@ -642,16 +646,18 @@ LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax) {
   const int KT = K / kLg;
   if (!argmax && M >= 256) {
     // Prompt passes: tiles of 256 x 256 (8 waves of 64 x 128, one block per CU: 128 KB
-    // of LDS) from 512 rows when K is long, else 128 x 128 (two blocks per CU).
-    // Split-K is chosen to minimise (rounds of resident blocks) / splits, with a 10%
-    // charge for the reduction pass.  Measured at 512 rows (176B share): QKV 29% of
-    // the bf16 MFMA peak with 256 x 256 tiles against 28% with 128 x 128, dense
-    // (K = 1792) 17% against 22%.
-    p.lg = (M >= 512 && K >= 4096) ? LG_256 : LG_128;
-    const int bt = p.lg == LG_256 ? 256 : 128;
-    const int slots = p.lg == LG_256 ? 256 : 512;
-    p.grid_x = (M + bt - 1) / bt;
-    p.grid_y = (N + bt - 1) / bt;
+    // of LDS) from 1024 rows, 256 x 128 with 3 stages (8 waves of 64 x 64, 144 KB) from
+    // 512 rows, else 128 x 128 (two blocks per CU).  Split-K is chosen to minimise
+    // (rounds of resident blocks) / splits, with a 10% charge for the reduction pass.
+    // Measured on the 176B share (% of the bf16 MFMA peak): 512 rows, 256 x 128 against
+    // 256 x 256: QKV 32.8 / 30.7, dense 23.3 / 18.2, down 34.9 / 33.9, up 33.6 / 34.7;
+    // 2048 rows, dense 29.0 with 256 x 256 against 23.5 with 128 x 128.
+    p.lg = M >= 1024 ? LG_256 : (M >= 512 ? LG_256x128 : LG_128);
+    const int bm = p.lg == LG_128 ? 128 : 256;
+    const int bn = p.lg == LG_256 ? 256 : 128;
+    const int slots = p.lg == LG_128 ? 512 : 256;
+    p.grid_x = (M + bm - 1) / bm;
+    p.grid_y = (N + bn - 1) / bn;
     const long tiles = (long)p.grid_x * p.grid_y;
     int best = 1;
     double best_cost = 1e30;
@@ -664,17 +670,46 @@ LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax) {
     return p;
   }
   // Decode batches, LM heads and short passes: a 32/64/128-row activation tile against
-  // 128 weight rows, 3-4 LDS stages in flight, and K split so that each block streams
-  // about 48+ K tiles (at least 2 splits when there are few N tiles).  Measured on
-  // MI355X against an MFMA GEMV loading 64 bytes per row: 176B-share QKV at 32 rows
-  // 82 -> 37 us, at 64 rows 137 -> 42 us.  The argmax epilogue needs whole dot
-  // products, so the LM head is never split.
-  p.lg = M <= 32 ? LG_D32 : (M <= 64 ? LG_D64 : LG_D128);
-  const int bm = M <= 32 ? 32 : (M <= 64 ? 64 : 128);
+  // 128 weight rows, 3-4 LDS stages in flight, and K split (each split keeping >= 8 K
+  // tiles).  bf16 weights: the split gives about one block per CU.  Measured on MI355X
+  // (176B share, 128 rows; per-shape best split in brackets): QKV 5376 x 14336 53.4 us
+  // with 4 splits -> 45.5 us with 6 [6], up 4 splits [4], down and dense 2 [2].
+  // int8 weights: the 64-byte K-tile rows leave little in flight per stage and the
+  // widening to bf16 costs vector-ALU time, so the tiles take 256 weight rows where N
+  // is long (one wave per 64 columns), the 128-row tile gives each wave all 128 rows
+  // and 32 columns (every weight widened once), two blocks fit per CU, and the split
+  // minimises rounds of 512 resident blocks per split (+10% for the reduction).
+  // Measured (full 176B int8): 16 rows QKV 43008 x 14336 175.6 -> 146.0 us, up
+  // 214.4 -> 193.3, down 247.0 -> 196.9; 64 rows QKV 197.3 -> 172.8, up 263.1 ->
+  // 227.2; 128 rows QKV 295.0 -> 258.0, down 364.7 -> 345.0.  The argmax epilogue
+  // needs whole dot products, so the LM head is never split.
+  const bool i8 = wdtype == WT_INT8;
+  int bm, bn;
+  if (!i8) {
+    p.lg = M <= 32 ? LG_D32 : (M <= 64 ? LG_D64 : LG_D128);
+    bm = M <= 32 ? 32 : (M <= 64 ? 64 : 128);
+    bn = 128;
+  } else if (M <= 32) {
+    p.lg = LG_D32W; bm = 32; bn = 256;
+  } else if (M <= 64) {
+    p.lg = N >= 32768 ? LG_D64W : LG_D64; bm = 64; bn = N >= 32768 ? 256 : 128;
+  } else {
+    p.lg = LG_D128N; bm = 128; bn = 128;
+  }
   p.grid_x = (M + bm - 1) / bm;
-  p.grid_y = (N + 127) / 128;
-  int sp = max(1, min(8, KT / 48));
-  if (sp < 2 && KT >= 2 && p.grid_x * p.grid_y < 160) sp = 2;
+  p.grid_y = (N + bn - 1) / bn;
+  const long tiles = (long)p.grid_x * p.grid_y;
+  int sp = 1;
+  if (!i8) {
+    sp = (int)max(1l, min(8l, 256 / tiles));
+  } else {
+    double best_cost = 1e30;
+    for (int s2 = 1; s2 <= 8; ++s2) {
+      const double cost = (double)((tiles * s2 + 511) / 512) / s2 + (s2 > 1 ? 0.1 : 0.0);
+      if (cost < best_cost - 1e-9) { best_cost = cost; sp = s2; }
+    }
+  }
+  while (sp > 1 && KT / sp < 8) --sp;
   while (sp > 1 && (long)sp * M * N > kLgPartialCapFloats) --sp;
   p.splits = argmax ? 1 : sp;
   return p;
@@ -738,6 +773,16 @@ static hipError_t launch_lg(const LinearPlan &p, const void *X, const void *W, f
     case LG_128: return launch_lg_t<TW, 128, 128, 2, 2, 2>(p, X, W, partial, ep, st);
     case LG_D32: return launch_lg_t<TW, 32, 128, 1, 4, 4>(p, X, W, partial, ep, st);
     case LG_D64: return launch_lg_t<TW, 64, 128, 1, 4, 3>(p, X, W, partial, ep, st);
+    case LG_256x128: return launch_lg_t<TW, 256, 128, 4, 2, 3>(p, X, W, partial, ep, st);
+    case LG_D32W:
+      if constexpr (sizeof(TW) == 1) return launch_lg_t<TW, 32, 256, 1, 4, 4>(p, X, W, partial, ep, st);
+      return hipErrorInvalidValue;
+    case LG_D64W:
+      if constexpr (sizeof(TW) == 1) return launch_lg_t<TW, 64, 256, 1, 4, 3>(p, X, W, partial, ep, st);
+      return hipErrorInvalidValue;
+    case LG_D128N:
+      if constexpr (sizeof(TW) == 1) return launch_lg_t<TW, 128, 128, 1, 4, 3>(p, X, W, partial, ep, st);
+      return hipErrorInvalidValue;
     default: return launch_lg_t<TW, 128, 128, 2, 2, 3>(p, X, W, partial, ep, st);
   }
 }
