@@ -83,6 +83,16 @@ def upload_weights(m, seed=0):
     return tb.DeviceWeights(g, layers)
 
 
+def kernel_source_digest():
+    """Hash of the sources that define the batch-1 GEMV as launched: its kernel, planner
+    and launcher (gemv.hip) and the fused epilogues it calls (common.hpp)."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in ("gemv.hip", "common.hpp"):
+        h.update(open(os.path.join(ROOT, "transformer_bloom_decode_amd", "csrc", name), "rb").read())
+    return h.hexdigest()[:16]
+
+
 def counted_traffic(kernel, workload, batch):
     """HBM bytes per launch of `kernel` measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
     (scaled by a plain-copy calibration), from the committed summary in profiles/; None
@@ -97,9 +107,7 @@ def counted_traffic(kernel, workload, batch):
         if ":" in line and not line.startswith(("#", "|", "`")):
             k, _, v = line.partition(":")
             fields[k.strip()] = v.strip()
-    src = os.path.join(ROOT, "transformer_bloom_decode_amd", "csrc", "gemm.hip")
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    if fields.get("kernel") != kernel or fields.get("gemm_hip_sha256_16") != digest:
+    if fields.get("kernel") != kernel or fields.get("source_sha256_16") != kernel_source_digest():
         return None
     try:
         return int(fields["traffic_bytes_per_launch"])

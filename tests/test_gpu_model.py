@@ -127,14 +127,19 @@ def test_bloom560m_wide_batch_uses_tiled_and_wide_gemv():
     assert v.hidden_rel <= 1e-2 and v.tokens_ok
 
 
-@pytest.mark.parametrize("d, P, valid", [(128, 100, (100, 37)), (256, 70, (70, 1)),
-                                         (64, 130, (130, 129, 64))])
+@pytest.mark.parametrize("d, P, valid", [
+    (128, 100, (100, 37)),                                          # per-row prompt kernel
+    (128, 100, (100, 37, 1, 64, 99, 100, 2, 50, 77, 13)),           # 280 prompt blocks
+    (256, 70, (70, 1, 33, 8, 69, 70, 2, 40, 9, 16, 55, 3, 64, 17, 70)),
+    (64, 130, (130, 129, 64, 1, 33, 100, 7))])
 def test_long_rows_cross_attention_batches(d, P, valid):
-    """Long prompts and up to P + 59 visible keys: the prompt pass runs several chunks of
-    query rows per sequence and several LDS key tiles (32 keys per tile at d = 256, 64
-    otherwise), with padding that leaves whole chunks without a visible key; the decode
-    steps see more keys than one batch of the decode kernel (16 lane groups x 8 keys at
-    d = 128), so the running-max rescale across batches runs."""
+    """Long prompts and up to P + 59 visible keys.  With >= 256 (sequence, head, chunk)
+    blocks the prompt pass runs the chunked prompt kernel: several chunks of query rows
+    per sequence and several LDS key tiles (32 keys per tile at d = 256, 64 otherwise),
+    with padding that leaves whole chunks without a visible key; with fewer it runs one
+    block per (row, head).  The decode steps see more keys than one batch of the decode
+    kernel (16 lane groups x 8 keys at d = 128), so the running-max rescale across
+    batches runs."""
     H = 512 // d
     m = dataclasses.replace(bi.BLOOM_560M, name=f"d{d}", n_layer=1, hidden=512, n_head_total=H,
                             n_head_local=H, head_dim=d, ffn=1024, vocab=512)

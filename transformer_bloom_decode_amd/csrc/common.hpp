@@ -95,6 +95,11 @@ __device__ __forceinline__ float block_max(float v, float *sh) {
 // c = largest power of two <= n_total; heads g < c use 2^(-8(g+1)/c), the others the
 // odd terms 2^(-4(2(g-c)+1)/c) of the 2c-head sequence.  The exponent is exact in
 // fp32 (c is a power of two), so only exp2 rounds.
+// Greedy choice: larger value wins, equal values go to the lower index.
+__device__ __forceinline__ void argmax_take(float &bv, int &bi, float v, int i) {
+  if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
+}
+
 __device__ __forceinline__ float alibi_slope(int n_total, int g) {
   const int c = 1 << (31 - __clz(n_total));
   const float e = (g < c) ? (-8.0f * (float)(g + 1)) / (float)c

@@ -1,0 +1,241 @@
+// Decode GEMV on the vector ALU for up to 4 activation rows (the batch-1..4 decode
+// step and LM head): each wave streams one or two weight rows in 1 KB non-temporal
+// loads (whole rows at once when the grid leaves wave slots empty); the block's output
+// rows are finished by the fused epilogue (or an argmax for the LM head).  The pages'
+// analysis ("DeepSpeed Inference ...", Section III.A) is that small-batch inference is
+// bound by reading the weights once; this kernel is built around streaming W at full
+// bandwidth.  Its planning (rows per wave, pieces in flight) and launch live here too.
+#include <type_traits>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace bl {
+
+__device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
+
+// ---------------------------------------------------------------------------
+// decode GEMV on the vector ALU (M <= 4 activation rows)
+// ---------------------------------------------------------------------------
+// Each wave owns R consecutive weight rows over the full K.  Per step every lane
+// loads one 16-byte piece of each of its rows, so a wave load instruction covers
+// 1 KB of one row contiguously; the loads are non-temporal (streamed weights are
+// not kept in the caches that hold activations and the KV cache).  Weights are
+// widened to float32 in registers and multiplied by the matching activation values
+// with fmaf; each lane keeps R*M running sums, reduced across the wave at the end.
+// U steps are loaded ahead of the one being multiplied.
+template <typename TW> struct VOps;
+
+template <> struct VOps<bf16_t> {
+  static constexpr int kPerLane = 8;                      // elements per 16-byte piece
+  static __device__ __forceinline__ void widen(u32x4 w, float f[8]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) { f[2 * t] = lo_bf(w[t]); f[2 * t + 1] = hi_bf(w[t]); }
+  }
+};
+
+template <> struct VOps<int8_t> {
+  static constexpr int kPerLane = 16;
+  static __device__ __forceinline__ void widen(u32x4 w, float f[16]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) f[4 * t + b] = (float)(int)(int8_t)(w[t] >> (8 * b));
+  }
+};
+
+// DB: double-buffered (the next U pieces per row are issued before the current ones
+// are used) or single-buffered (U pieces per row issued at once, then used; with U >=
+// the row's pieces, a wave issues its whole row in one go, which keeps the most bytes
+// in flight when the grid is too small to fill every wave slot).
+template <typename TW, typename TP, int MR, int R, int U, bool DB>
+__global__ __launch_bounds__(256) void k_gemv_valu(const bf16_t *__restrict__ X,
+                                                   const TW *__restrict__ W, int M, int N, int K,
+                                                   EpiParams ep) {
+  using VO = VOps<TW>;
+  constexpr int E = VO::kPerLane;
+  constexpr int XP = E / 8;                               // 16-byte activation pieces per step
+  __shared__ float am_v[4][MR];
+  __shared__ int am_i[4][MR];
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int row0 = (blockIdx.x * 4 + wid) * R;
+  const TW *wr[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) wr[i] = W + (size_t)min(row0 + i, N - 1) * K;
+  const bf16_t *xr[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) xr[m] = X + (size_t)min(m, M - 1) * K;
+
+  float acc[R][MR];
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int m = 0; m < MR; ++m) acc[i][m] = 0.f;
+
+  const int step = 64 * E;                                // elements per wave step
+  const int nsteps = (K + step - 1) / step;
+  u32x4 cw[U][R], cx[U][MR][XP];
+
+  auto load = [&](int s0, u32x4(&w)[U][R], u32x4(&x)[U][MR][XP]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = (s0 + u) * step + lane * E;
+      const bool ok = (s0 + u) < nsteps && k < K;
+#pragma unroll
+      for (int i = 0; i < R; ++i)
+        w[u][i] = ok ? __builtin_nontemporal_load((const u32x4 *)(wr[i] + k)) : zero4();
+#pragma unroll
+      for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int p = 0; p < XP; ++p)
+          x[u][m][p] = ok ? *(const u32x4 *)(xr[m] + k + 8 * p) : zero4();
+    }
+  };
+
+  auto compute = [&]() {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float xf[MR][E];
+#pragma unroll
+      for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int p = 0; p < XP; ++p)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            xf[m][8 * p + 2 * t] = lo_bf(cx[u][m][p][t]);
+            xf[m][8 * p + 2 * t + 1] = hi_bf(cx[u][m][p][t]);
+          }
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        float wf[E];
+        VO::widen(cw[u][i], wf);
+#pragma unroll
+        for (int m = 0; m < MR; ++m)
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[i][m] = fmaf(wf[e], xf[m][e], acc[i][m]);
+      }
+    }
+  };
+
+  if constexpr (DB) {
+    u32x4 nw[U][R], nx[U][MR][XP];
+    load(0, cw, cx);
+    for (int s0 = 0; s0 < nsteps; s0 += U) {
+      if (s0 + U < nsteps) load(s0 + U, nw, nx);
+      compute();
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int i = 0; i < R; ++i) cw[u][i] = nw[u][i];
+#pragma unroll
+        for (int m = 0; m < MR; ++m)
+#pragma unroll
+          for (int p = 0; p < XP; ++p) cx[u][m][p] = nx[u][m][p];
+      }
+    }
+  } else {
+    for (int s0 = 0; s0 < nsteps; s0 += U) {
+      load(s0, cw, cx);
+      compute();
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int m = 0; m < MR; ++m) acc[i][m] = wave_sum(acc[i][m]);
+
+  if (ep.mode == EPI_ARGMAX) {
+    // best of this wave's R rows per activation row, then of the block's 4 waves
+    if (lane == 0) {
+#pragma unroll
+      for (int m = 0; m < MR; ++m) {
+        float bv = -INFINITY;
+        int bi = min(row0, N - 1);
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+          if (row0 + i < N) argmax_take(bv, bi, acc[i][m], row0 + i);
+        am_v[wid][m] = bv;
+        am_i[wid][m] = bi;
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x < MR && threadIdx.x < M) {
+      const int m = threadIdx.x;
+      float bv = am_v[0][m];
+      int bi = am_i[0][m];
+      for (int w = 1; w < 4; ++w) argmax_take(bv, bi, am_v[w][m], am_i[w][m]);
+      ep.am_val[(size_t)m * ep.am_stride + blockIdx.x] = bv;
+      ep.am_idx[(size_t)m * ep.am_stride + blockIdx.x] = bi;
+    }
+    return;
+  }
+  // lane l < R*MR finishes output (row0 + l / MR, activation row l % MR)
+  if (lane < R * MR) {
+    float v = 0.f;
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+      for (int m = 0; m < MR; ++m)
+        if (lane == i * MR + m) v = acc[i][m];
+    const int n = row0 + lane / MR, m = lane % MR;
+    if (n < N && m < M) epilogue<TP, bf16_t>(ep, m, n, v);
+  }
+}
+
+LinearPlan plan_valu(int wdtype, int M, int N, int K) {
+  LinearPlan p{};
+  p.M = M; p.N = N; p.K = K;
+  p.kind = LIN_VALU;
+  p.mt = M <= 1 ? 1 : (M <= 2 ? 2 : 4);
+  // Default: 2 rows per wave, 4 pieces per row double-buffered (8 KB in flight per
+  // wave); enough when the grid fills every wave slot (LM head) or rows are short.
+  // Batch-1 bf16 linears with long rows and grids that leave wave slots empty issue
+  // a wave's whole row at once instead (14-28 KB in flight per wave): measured on
+  // MI355X, QKV 5376 x 14336 5.15 -> 5.88 TB/s, up 7168 x 14336 5.75 -> 6.47,
+  // down 14336 x 7168 6.39 -> 6.60.
+  p.vr = 2;
+  p.vu = p.mt == 4 ? 2 : 4;
+  p.vdb = true;
+  const int pieces = (K + 511) / 512;  // 1 KB wave loads of bf16
+  if (p.mt == 1 && wdtype == WT_BF16 && N < 65536 && pieces > 4 && pieces <= 28) {
+    p.vr = 1;
+    p.vu = pieces <= 16 ? 16 : 28;
+    p.vdb = false;
+  }
+  p.grid_x = (N + 4 * p.vr - 1) / (4 * p.vr);
+  p.splits = 1;
+  return p;
+}
+
+template <typename TW, typename TP>
+static void launch_valu_t(const LinearPlan &p, const void *X, const void *W, const EpiParams &ep,
+                          hipStream_t st) {
+  const dim3 grid(p.grid_x), block(256);
+  const bf16_t *x = (const bf16_t *)X;
+  const TW *w = (const TW *)W;
+  if constexpr (std::is_same<TW, bf16_t>::value) {
+    if (p.vr == 1 && p.mt == 1 && !p.vdb) {
+      if (p.vu == 16)
+        BL_LAUNCH((k_gemv_valu<TW, TP, 1, 1, 16, false>), grid, block, 0, st, x, w, p.M, p.N, p.K, ep);
+      else
+        BL_LAUNCH((k_gemv_valu<TW, TP, 1, 1, 28, false>), grid, block, 0, st, x, w, p.M, p.N, p.K, ep);
+      return;
+    }
+  }
+  switch (p.mt) {
+    case 1: BL_LAUNCH((k_gemv_valu<TW, TP, 1, 2, 4, true>), grid, block, 0, st, x, w, p.M, p.N, p.K, ep); break;
+    case 2: BL_LAUNCH((k_gemv_valu<TW, TP, 2, 2, 4, true>), grid, block, 0, st, x, w, p.M, p.N, p.K, ep); break;
+    default: BL_LAUNCH((k_gemv_valu<TW, TP, 4, 2, 2, true>), grid, block, 0, st, x, w, p.M, p.N, p.K, ep); break;
+  }
+}
+
+hipError_t launch_valu(int wdtype, const LinearPlan &p, const void *X, const void *W,
+                       const EpiParams &ep, hipStream_t st) {
+  if (wdtype == WT_BF16) launch_valu_t<bf16_t, bf16_t>(p, X, W, ep, st);
+  else launch_valu_t<int8_t, bf16_t>(p, X, W, ep, st);
+  return hipGetLastError();
+}
+
+}  // namespace bl

@@ -60,6 +60,10 @@ struct LinearPlan {
   int splits;    // K splits (> 1: partial sums + reduction kernel)
 };
 
+// Vector-ALU GEMV (gemv.hip): plan for M <= kValuMaxRows rows, and its launch.
+LinearPlan plan_valu(int wdtype, int M, int N, int K);
+hipError_t launch_valu(int wdtype, const LinearPlan &p, const void *X, const void *W,
+                       const EpiParams &ep, hipStream_t st);
 LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax);
 // (max, index) partials per activation row an argmax-mode launch of the plan writes.
 int argmax_partials_per_row(const LinearPlan &p);
