@@ -187,9 +187,10 @@ hipError_t timed(int cls, double wbytes, hipStream_t st, F &&launch) {
 }
 
 hipError_t timed_linear(int wdt, const LinearPlan &p, const void *X, const void *W, float *part,
-                        const EpiParams &ep, hipStream_t st, double wbytes) {
+                        const EpiParams &ep, hipStream_t st, double wbytes,
+                        bool splitk_epilogue = true) {
   return timed(kernel_class(p), wbytes, st,
-               [&] { return launch_linear(wdt, p, X, W, part, ep, st); });
+               [&] { return launch_linear(wdt, p, X, W, part, ep, st, splitk_epilogue); });
 }
 
 // Non-blocking stream (default priority) per device on which bloom_generate captures its
@@ -242,13 +243,23 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
   const LinearPlan p_up = plan_linear(wdt, M, F, h, false);
   const LinearPlan p_down = plan_linear(wdt, M, h, F, false);
 
+  // K-split dense / down projections reduce their partials in the kernel that also adds
+  // bias and residual and runs the next LayerNorm (LN2 after dense, the next layer's LN1
+  // after down); unsplit ones keep the epilogue in the GEMM and a separate LayerNorm.
+  auto fuse_ln = [&](const LinearPlan &p) {
+    return !f32 && p.splits > 1 && splitk_resid_ln_supported(h, p.splits);
+  };
+  bool ln1_done = false;   // xa already holds LN1(x) of this layer
   for (int l = 0; l < c->n_layer; ++l) {
     const bloom_layer_weights &L = w->layers[l];
     void *kc = (char *)kv->k + l * layer_stride;
     void *vc = (char *)kv->v + l * layer_stride;
 
-    err = launch_layernorm(f32, x, 1, 0, L.ln1_g, L.ln1_b, xa, nullptr, M, h, c->ln_eps, st);
-    if (err != hipSuccess) return hip_fail(err);
+    if (!ln1_done) {
+      err = launch_layernorm(f32, x, 1, 0, L.ln1_g, L.ln1_b, xa, nullptr, M, h, c->ln_eps, st);
+      if (err != hipSuccess) return hip_fail(err);
+    }
+    ln1_done = false;
 
     EpiParams e{};
     e.mode = EPI_QKV;
@@ -270,10 +281,15 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
     r.bias = L.b_dense;
     r.scale = (const uint16_t *)L.s_dense;
     r.out = x; r.ld = h;
-    err = timed_linear(wdt, p_dense, o, L.w_dense, part, r, st, wbytes(h, hd));
+    const bool fuse_dense = fuse_ln(p_dense);
+    err = timed_linear(wdt, p_dense, o, L.w_dense, part, r, st, wbytes(h, hd), !fuse_dense);
     if (err != hipSuccess) return hip_fail(err);
 
-    err = launch_layernorm(f32, x, 1, 0, L.ln2_g, L.ln2_b, xa, nullptr, M, h, c->ln_eps, st);
+    if (fuse_dense)
+      err = launch_splitk_resid_ln(part, p_dense.splits, M, L.s_dense, L.b_dense, x, L.ln2_g,
+                                   L.ln2_b, xa, h, c->ln_eps, st);
+    else
+      err = launch_layernorm(f32, x, 1, 0, L.ln2_g, L.ln2_b, xa, nullptr, M, h, c->ln_eps, st);
     if (err != hipSuccess) return hip_fail(err);
 
     EpiParams g{};
@@ -289,8 +305,16 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
     dn.bias = L.b_down;
     dn.scale = (const uint16_t *)L.s_down;
     dn.out = x; dn.ld = h;
-    err = timed_linear(wdt, p_down, u, L.w_down, part, dn, st, wbytes(h, F));
+    const bool fuse_down = l + 1 < c->n_layer && fuse_ln(p_down);
+    err = timed_linear(wdt, p_down, u, L.w_down, part, dn, st, wbytes(h, F), !fuse_down);
     if (err != hipSuccess) return hip_fail(err);
+    if (fuse_down) {
+      const bloom_layer_weights &N1 = w->layers[l + 1];
+      err = launch_splitk_resid_ln(part, p_down.splits, M, L.s_down, L.b_down, x, N1.ln1_g,
+                                   N1.ln1_b, xa, h, c->ln_eps, st);
+      if (err != hipSuccess) return hip_fail(err);
+      ln1_done = true;
+    }
   }
 
   // final LayerNorm of each row's last position, then the tied LM head + argmax

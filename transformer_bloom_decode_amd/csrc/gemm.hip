@@ -576,7 +576,8 @@ static hipError_t launch_lg(const LinearPlan &p, const void *X, const void *W, f
 }
 
 hipError_t launch_linear(int wdtype, const LinearPlan &p, const void *X, const void *W,
-                         float *partial, const EpiParams &ep, hipStream_t st) {
+                         float *partial, const EpiParams &ep, hipStream_t st,
+                         bool splitk_epilogue) {
   if (p.M <= 0) return hipSuccess;
   if (p.kind == LIN_F32) {
     BL_LAUNCH(k_gemm_f32, dim3(p.grid_x, p.M), dim3(256), 0, st, (const float *)X,
@@ -589,7 +590,7 @@ hipError_t launch_linear(int wdtype, const LinearPlan &p, const void *X, const v
                                          : launch_lg<int8_t>(p, X, W, partial, ep, st);
   if (e != hipSuccess) return e;
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || p.splits <= 1) return err;
+  if (err != hipSuccess || p.splits <= 1 || !splitk_epilogue) return err;
   const size_t MN = (size_t)p.M * p.N;
   BL_LAUNCH((k_splitk_epilogue<bf16_t, bf16_t>), dim3((unsigned)((MN + 255) / 256)),
                      dim3(256), 0, st, partial, p.splits, p.M, p.N, ep);

@@ -69,8 +69,10 @@ LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax);
 int argmax_partials_per_row(const LinearPlan &p);
 // Bytes of split-K partials the plan needs (0 without split-K).
 size_t linear_partial_bytes(const LinearPlan &p);
+// splitk_epilogue = false leaves a K-split launch's partials for the caller to reduce.
 hipError_t launch_linear(int wdtype, const LinearPlan &p, const void *X, const void *W,
-                         float *partial, const EpiParams &ep, hipStream_t st);
+                         float *partial, const EpiParams &ep, hipStream_t st,
+                         bool splitk_epilogue = true);
 hipError_t launch_argmax_merge(const float *val, const int *idx, int stride, int nblk, int rows,
                                int *out, hipStream_t st);
 
@@ -81,6 +83,12 @@ hipError_t launch_alibi_softmax(const void *scores, bool in_bf16, const int *val
 hipError_t launch_embed(bool f32, const int *tokens, const void *embed, const void *g,
                         const void *b, float *x, int rows, int h, int vocab, int do_ln, float eps,
                         hipStream_t stream);
+// Split-K partials of a bf16 linear [splits][rows][h] -> x += sum * scale + bias, then
+// out = LN(x) (bf16); only for splitk_resid_ln_supported(h, splits).
+bool splitk_resid_ln_supported(int h, int splits);
+hipError_t launch_splitk_resid_ln(const float *partial, int splits, int rows, const void *scale,
+                                  const void *bias, float *x, const void *g, const void *b,
+                                  void *out, int h, float eps, hipStream_t stream);
 hipError_t launch_layernorm(bool f32, const float *x, int in_step, int in_off, const void *g,
                             const void *b, void *out, float *out_f32, int rows, int h, float eps,
                             hipStream_t stream);

@@ -157,6 +157,67 @@ __global__ __launch_bounds__(kLnThreads) void k_layernorm(const float *__restric
   }
 }
 
+// Residual + LayerNorm epilogue of a K-split linear ("DeepSpeed Inference ...", Section
+// III.D: bias with residual addition, then the next layer-norm): for each column n of
+// the row, y = (sum over the S partials in split order) * scale[n] + bias[n] and x += y
+// -- the same float32 operations, in the same order, as k_splitk_epilogue in residual
+// mode -- then out = LN(x) of the updated row, as k_layernorm.  All S partial pieces of a
+// column group are loaded before the first add.
+template <typename TP, typename TA, int S>
+__global__ __launch_bounds__(kLnThreads) void k_splitk_resid_ln(
+    const float *__restrict__ partial, int M, const uint16_t *__restrict__ scale,
+    const TP *__restrict__ bias, float *__restrict__ x, const TP *__restrict__ g,
+    const TP *__restrict__ b, TA *__restrict__ out, int h, float eps) {
+  __shared__ float sh[kLnWaves];
+  const int row = blockIdx.x;
+  const size_t MN = (size_t)M * h;
+  float *xr = x + (size_t)row * h;
+  const float *pr = partial + (size_t)row * h;
+  float4 v[kLnVec];
+  Param4<TP> gv[kLnVec], bv[kLnVec];
+#pragma unroll
+  for (int i = 0; i < kLnVec; ++i) {
+    const int col = 4 * (threadIdx.x + i * kLnThreads);
+    if (col >= h) {
+      v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      continue;
+    }
+    float4 pz[S];
+#pragma unroll
+    for (int z = 0; z < S; ++z) pz[z] = *(const float4 *)(pr + z * MN + col);
+    const float4 x0 = *(const float4 *)(xr + col);
+    float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int z = 0; z < S; ++z) {
+      y.x += pz[z].x; y.y += pz[z].y; y.z += pz[z].z; y.w += pz[z].w;
+    }
+    if (scale) {
+      y.x *= h2f(scale[col]); y.y *= h2f(scale[col + 1]);
+      y.z *= h2f(scale[col + 2]); y.w *= h2f(scale[col + 3]);
+    }
+    if (bias) {
+      y.x += to_f<TP>(bias[col]); y.y += to_f<TP>(bias[col + 1]);
+      y.z += to_f<TP>(bias[col + 2]); y.w += to_f<TP>(bias[col + 3]);
+    }
+    v[i] = make_float4(x0.x + y.x, x0.y + y.y, x0.z + y.z, x0.w + y.w);
+    Vec4<float>::store(xr + col, v[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < kLnVec; ++i) {
+    const int col = min(4 * (threadIdx.x + i * kLnThreads), h - 4);
+    gv[i].load(g + col);
+    bv[i].load(b + col);
+  }
+  float mean, rstd;
+  ln_stats(v, h, eps, sh, mean, rstd);
+  TA *o = out + (size_t)row * h;
+#pragma unroll
+  for (int i = 0; i < kLnVec; ++i) {
+    const int col = 4 * (threadIdx.x + i * kLnThreads);
+    if (col < h) Vec4<TA>::store(o + col, ln_apply<TP>(v[i], mean, rstd, gv[i], bv[i]));
+  }
+}
+
 // Rows longer than the register tile, or not a multiple of 4: re-read the row.
 template <typename TP, typename TA>
 __global__ __launch_bounds__(256) void k_layernorm_any(const float *__restrict__ x, int in_step,
@@ -244,6 +305,32 @@ hipError_t launch_embed(bool f32, const int *tokens, const void *embed, const vo
                          (const bf16_t *)embed, (const bf16_t *)g, (const bf16_t *)b, x, h,
                          vocab, do_ln, eps);
   }
+  return hipGetLastError();
+}
+
+bool splitk_resid_ln_supported(int h, int splits) {
+  return fits_regs(h) && splits >= 2 && splits <= 8;
+}
+
+hipError_t launch_splitk_resid_ln(const float *partial, int splits, int rows, const void *scale,
+                                  const void *bias, float *x, const void *g, const void *b,
+                                  void *out, int h, float eps, hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  if (!splitk_resid_ln_supported(h, splits)) return hipErrorInvalidValue;
+  const dim3 grid(rows), block(kLnThreads);
+  const uint16_t *sc = (const uint16_t *)scale;
+  const bf16_t *bi = (const bf16_t *)bias, *gg = (const bf16_t *)g, *bb = (const bf16_t *)b;
+  bf16_t *o = (bf16_t *)out;
+#define BL_SRL(S)                                                                          \
+  case S:                                                                                  \
+    hipLaunchKernelGGL((k_splitk_resid_ln<bf16_t, bf16_t, S>), grid, block, 0, stream,    \
+                       partial, rows, sc, bi, x, gg, bb, o, h, eps);                        \
+    break;
+  switch (splits) {
+    BL_SRL(2) BL_SRL(3) BL_SRL(4) BL_SRL(5) BL_SRL(6) BL_SRL(7) BL_SRL(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef BL_SRL
   return hipGetLastError();
 }
 
