@@ -209,6 +209,22 @@ def test_int8_wide_ffn_decode_tiles(batch):
     _kv_check(run, v.oracle, batch, 4 + 2, 4e-2)
 
 
+def test_four_way_split_residual_layernorm():
+    """Hidden 6656 at 8 rows: dense and MLP-down split K four ways, so their partials go
+    through the fused split-K + bias + residual + LayerNorm kernel with four partials
+    (LN2 after dense, the second layer's LN1 after the first layer's down)."""
+    m = dataclasses.replace(bi.BLOOM_560M, name="h6656", n_layer=2, hidden=6656,
+                            n_head_total=52, n_head_local=52, head_dim=128, ffn=6656,
+                            vocab=4096)
+    T, dw, cfg = upload(m, seed=61)
+    prompt, valid = bi.prompts(m, 8, 4, (4, 3, 2, 1, 4, 4, 2, 3), seed=62)
+    run = run_gpu(cfg, dw, prompt, valid, 4)
+    v = compare(m, T, prompt, valid, run, 1e-2)
+    print(f"h6656 B8: hidden rel {v.hidden_rel:.2e}, exact ids {v.exact_frac:.3f}")
+    assert v.hidden_rel <= 1e-2 and v.tokens_ok
+    _kv_check(run, v.oracle, 8, 4 + 3, 2e-2)
+
+
 def test_tp_share_176b_prompt_pass_batch32():
     """The 176B rank-0 share at full width, batch 32: the 512-row prompt pass runs the
     direct-to-LDS GEMM with split-K on the real layer shapes."""
