@@ -197,8 +197,8 @@ def cpu_baseline(m, B, P, n_new, budget_s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported (this build "
-              "has no multi-GPU path; tensor-parallel sharding is described, not built).",
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported (no "
+              "multi-GPU path is implemented: the library runs one GPU's share of the model).",
               file=sys.stderr)
         sys.exit(2)
 
