@@ -38,7 +38,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3, help="timed generations")
     ap.add_argument("--warmup", type=int, default=1, help="untimed generations")
-    ap.add_argument("--workload", default="bloom-176b-tp8-rank0")
+    ap.add_argument("--workload", default="bloom-176b-tp8-rank0",
+                    help="a decode workload, or 'softmax' for the standalone fused ALiBi + "
+                         "masked softmax (its own JSON line)")
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--new-tokens", type=int, default=None)
     ap.add_argument("--layers", type=int, default=None, help="truncate the stack (development)")
@@ -194,6 +196,64 @@ def cpu_baseline(m, B, P, n_new, budget_s):
     }
 
 
+def softmax_bench(args):
+    """Standalone alibi_masked_softmax on its workload shape (bf16 scores [32, 14, 1, 2048],
+    left-pad valid lengths uniform in [64, 2048], fp32 probabilities): the kernel time on
+    one resident buffer set (it fits the 256 MB MALL), and the rate over 80 rotating sets
+    (> 350 MB, so the scores and probabilities come from and go to HBM)."""
+    import numpy as np
+    import torch
+
+    import bloom_inputs as bi
+    import transformer_bloom_decode_amd as tb
+
+    w = bi.SOFTMAX
+    scores, lengths = bi.softmax_inputs(w)
+    B, H, Q, K = w.batch, w.heads, w.q_len, w.kv_len
+    n_sets = 80
+    s_dev = torch.from_numpy(scores.view(np.int16)).cuda()
+    sets = [s_dev.clone() for _ in range(n_sets)]
+    vl = torch.from_numpy(lengths.astype(np.int32)).cuda()
+    outs = [torch.empty((B, H, Q, K), dtype=torch.float32, device="cuda") for _ in range(n_sets)]
+    stream = torch.cuda.current_stream()
+    # algorithmic bytes: the valid scores read, every probability written, the lengths
+    valid_keys = int(np.minimum(lengths, K).sum()) * H * Q
+    nbytes = valid_keys * 2 + B * H * Q * K * 4 + B * 4
+
+    def call(i):
+        tb.alibi_masked_softmax(sets[i], tb.BLOOM_BF16, vl, B, H, Q, K, w.n_head_total,
+                                w.head_offset, outs[i], tb.BLOOM_F32, stream)
+
+    def timed(reps, rotate):
+        for i in range(3):
+            call(i % n_sets if rotate else 0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            call(i % n_sets if rotate else 0)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    us_res = timed(400, False)
+    us_rot = timed(400, True)
+    out = {
+        "metric": "fused ALiBi + masked softmax kernel time",
+        "value": round(us_res, 2), "unit": "us", "higher_is_better": False,
+        "n_gpus": 1, "dtype": "bf16 in, f32 softmax and out", "data": "synthetic",
+        "config": {"workload": "alibi_masked_softmax", "batch": B, "heads": H, "q_len": Q,
+                   "kv_len": K, "valid_len": f"uniform [{w.min_valid}, {K}]",
+                   "score_std": w.score_std},
+        "algorithmic_bytes": nbytes,
+        "resident_gb_per_s": round(nbytes / (us_res * 1e-6) / 1e9, 1),
+        "hbm_resident": {"sets": n_sets, "us": round(us_rot, 2),
+                         "gb_per_s": round(nbytes / (us_rot * 1e-6) / 1e9, 1),
+                         "frac": round(nbytes / (us_rot * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -204,6 +264,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.workload == "softmax":
+        softmax_bench(args)
         return
 
     import numpy as np
