@@ -115,9 +115,9 @@ def test_full_176b_int8_two_layers(batch):
     assert v.hidden_rel <= 2e-2 and v.tokens_ok
 
 
-def test_bloom560m_wide_batch_uses_tiled_and_wide_gemv():
-    """72 rows: the prompt pass and the decode steps take the LDS-tiled MFMA GEMM and
-    the LM head the 8-tile GEMV."""
+def test_bloom560m_wide_batch_direct_to_lds_tiles():
+    """72 rows: the 1152-row prompt pass takes the 256 x 256 tiles, the decode steps and
+    the LM head (argmax epilogue) the 128-row decode tiles."""
     m = bi.BLOOM_560M.truncated(2)
     T, dw, cfg = upload(m, seed=9)
     prompt, valid = bi.prompts(m, 72, 16, np.arange(72) % 16 + 1, seed=10)
@@ -154,10 +154,11 @@ def test_long_rows_cross_attention_batches(d, P, valid):
 
 
 @pytest.mark.parametrize("hidden, ffn, n_new", [(2112, 4224, 24), (3072, 8192, 12)])
-def test_batch1_fused_layernorm_and_whole_row_gemv(hidden, ffn, n_new):
-    """Batch 1 with rows of 5-16 KB: QKV and MLP-up run the GEMV with the LayerNorm fused
-    in, dense / down / the LM head the one-row-per-wave GEMV (LM head with the argmax
-    epilogue).  Hidden 2112 leaves a partial last 1 KB piece in every row."""
+def test_batch1_whole_row_gemv_widths(hidden, ffn, n_new):
+    """Batch 1: QKV, MLP-up, MLP-down and the LM head (rows of 4-16 KB; the LM head with
+    the argmax epilogue) run the GEMV that issues a wave's whole weight row at once, the
+    dense projection (2 KB rows) the two-rows-per-wave GEMV.  Hidden 2112 leaves a partial
+    last 1 KB piece in every row."""
     m = dataclasses.replace(bi.BLOOM_560M, name=f"h{hidden}", n_layer=2, hidden=hidden,
                             n_head_total=32, n_head_local=16, head_dim=64, ffn=ffn, vocab=8192)
     T, dw, cfg = upload(m, seed=31)
