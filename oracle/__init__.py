@@ -14,11 +14,16 @@ from .bloom_oracle import (  # noqa: F401
     alibi_masked_softmax,
     alibi_slopes,
     attention,
+    decoder_layer,
     forward,
     gelu_tanh,
+    greedy_argmax,
     greedy_generate,
+    layer_from_storage,
     layer_norm,
     linear,
+    lm_logits,
     masked_softmax,
     new_cache,
+    round_bf16,
 )

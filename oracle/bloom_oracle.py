@@ -181,6 +181,32 @@ def _widen(a: np.ndarray, storage: str) -> np.ndarray:
     return a
 
 
+def layer_from_storage(shape, lw: dict, dtype=F64, widen_weights: bool = True) -> dict:
+    """One decoder layer's parameters from their storage form (see
+    OracleModel.from_storage), as the dict that ``decoder_layer`` takes."""
+    wd = shape.weight_dtype
+    pd = "f32" if wd == "f32" else "bf16"
+
+    def par(a):
+        return _widen(a, pd).astype(dtype)
+
+    def mat(field):
+        if wd == "int8":
+            w8 = Int8RowScale(lw["w_" + field], _widen(lw["s_" + field], "f16"))
+            return w8.dense(dtype) if widen_weights else w8
+        w = _widen(lw["w_" + field], wd)
+        return w.astype(dtype) if widen_weights else w
+
+    return {
+        "ln1": (par(lw["ln1_g"]), par(lw["ln1_b"])),
+        "qkv": mat("qkv"), "b_qkv": par(lw["b_qkv"]),
+        "dense": mat("dense"), "b_dense": par(lw["b_dense"]),
+        "ln2": (par(lw["ln2_g"]), par(lw["ln2_b"])),
+        "up": mat("up"), "b_up": par(lw["b_up"]),
+        "down": mat("down"), "b_down": par(lw["b_down"]),
+    }
+
+
 @dataclasses.dataclass
 class OracleModel:
     """Shape plus weight values of one BLOOM stack (whole model or one TP share)."""
@@ -214,23 +240,8 @@ class OracleModel:
         def par(a):
             return _widen(a, pd).astype(dtype)
 
-        def mat(lw, field):
-            if wd == "int8":
-                w8 = Int8RowScale(lw["w_" + field], _widen(lw["s_" + field], "f16"))
-                return w8.dense(dtype) if widen_weights else w8
-            w = _widen(lw["w_" + field], wd)
-            return w.astype(dtype) if widen_weights else w
-
-        layers = []
-        for lw in tensors["layers"]:
-            layers.append({
-                "ln1": (par(lw["ln1_g"]), par(lw["ln1_b"])),
-                "qkv": mat(lw, "qkv"), "b_qkv": par(lw["b_qkv"]),
-                "dense": mat(lw, "dense"), "b_dense": par(lw["b_dense"]),
-                "ln2": (par(lw["ln2_g"]), par(lw["ln2_b"])),
-                "up": mat(lw, "up"), "b_up": par(lw["b_up"]),
-                "down": mat(lw, "down"), "b_down": par(lw["b_down"]),
-            })
+        layers = [layer_from_storage(shape, lw, dtype, widen_weights)
+                  for lw in tensors["layers"]]
         emb_ln = None
         if shape.embed_ln:
             emb_ln = (par(tensors["emb_ln_g"]), par(tensors["emb_ln_b"]))
@@ -266,29 +277,53 @@ def forward(model: OracleModel, tokens: np.ndarray, start: int, pad: np.ndarray,
     dt = model.dtype
     tokens = np.asarray(tokens)
     pad = np.asarray(pad, dtype=np.int64)
-    B, S = tokens.shape
-    H, d = model.n_head_local, model.head_dim
     if cache[0]["k"].shape[2] != start:
         raise ValueError("cache length does not match start position")
     x = np.asarray(model.embed[tokens], dtype=dt)
     if model.embed_ln:
         x = layer_norm(x, model.emb_ln[0], model.emb_ln[1], model.ln_eps)
-    slopes = model.slopes
     for li, lw in enumerate(model.layers):
-        a = layer_norm(x, lw["ln1"][0], lw["ln1"][1], model.ln_eps)
-        qkv = linear(a, lw["qkv"], lw["b_qkv"], dt).reshape(B, S, H, 3, d)
-        q, k, v = qkv[:, :, :, 0, :], qkv[:, :, :, 1, :], qkv[:, :, :, 2, :]
-        c = cache[li]
-        c["k"] = np.concatenate([c["k"], k.transpose(0, 2, 1, 3)], axis=2)
-        c["v"] = np.concatenate([c["v"], v.transpose(0, 2, 1, 3)], axis=2)
-        o = attention(q, c["k"], c["v"], slopes, pad, start)
-        x = x + linear(o.reshape(B, S, H * d), lw["dense"], lw["b_dense"], dt)
-        a2 = layer_norm(x, lw["ln2"][0], lw["ln2"][1], model.ln_eps)
-        u = gelu_tanh(linear(a2, lw["up"], lw["b_up"], dt))
-        x = x + linear(u, lw["down"], lw["b_down"], dt)
+        x = decoder_layer(model, lw, x, pad, start, cache[li])
         if trace is not None:
             trace.append(x.copy())
     return layer_norm(x, model.lnf[0], model.lnf[1], model.ln_eps)
+
+
+def round_bf16(a: np.ndarray) -> np.ndarray:
+    """Nearest bfloat16 value (ties to even) of each element, returned as float64: the
+    value is first rounded to float32, then its low 16 bits are rounded away."""
+    f = np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def decoder_layer(model: OracleModel, lw: dict, x: np.ndarray, pad: np.ndarray, start: int,
+                  c: dict, act=None) -> np.ndarray:
+    """One pre-LayerNorm decoder layer ("DeepSpeed Inference ...", Section III.D) on the
+    residual stream x [B, S, hidden] at positions start .. start+S-1, appending the
+    layer's K/V to the cache entry ``c`` ({"k", "v"}: [B, H, start, d]).  Only the shape
+    fields, ln_eps and the ALiBi slopes of ``model`` are used.
+
+    ``act`` (optional, e.g. round_bf16) is applied to the activations a path may store
+    in a narrower type: both LayerNorm outputs, the new keys and values, the attention
+    output and the GeLU output; the residual stream and q are left exact.  Without it
+    every value stays in ``model.dtype``."""
+    dt = model.dtype
+    r = act if act is not None else (lambda t: t)
+    pad = np.asarray(pad, dtype=np.int64)
+    B, S = x.shape[:2]
+    H, d = model.n_head_local, model.head_dim
+    a = r(layer_norm(x, lw["ln1"][0], lw["ln1"][1], model.ln_eps))
+    qkv = linear(a, lw["qkv"], lw["b_qkv"], dt).reshape(B, S, H, 3, d)
+    q, k, v = qkv[:, :, :, 0, :], r(qkv[:, :, :, 1, :]), r(qkv[:, :, :, 2, :])
+    c["k"] = np.concatenate([c["k"], k.transpose(0, 2, 1, 3)], axis=2)
+    c["v"] = np.concatenate([c["v"], v.transpose(0, 2, 1, 3)], axis=2)
+    o = r(attention(q, c["k"], c["v"], model.slopes, pad, start))
+    x = x + linear(o.reshape(B, S, H * d), lw["dense"], lw["b_dense"], dt)
+    a2 = r(layer_norm(x, lw["ln2"][0], lw["ln2"][1], model.ln_eps))
+    u = r(gelu_tanh(linear(a2, lw["up"], lw["b_up"], dt)))
+    return x + linear(u, lw["down"], lw["b_down"], dt)
 
 
 def lm_logits(model: OracleModel, hidden: np.ndarray, chunk: int = 16384) -> np.ndarray:

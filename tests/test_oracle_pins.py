@@ -420,3 +420,46 @@ def test_generator_matches_its_published_definition():
         assert x[i] == np.float32(z) * scale
     w = bi.normal(seed, tid, (1 << 16,), 0.02, kind="f32")
     assert abs(w.std() / 0.02 - 1) < 0.02 and abs(w.mean()) < 5e-4
+
+
+def test_round_bf16_closed_forms_and_torch():
+    """Nearest bfloat16, ties to even: against hand-worked values at 1 (ulp 2^-7) and
+    against torch's float32 -> bfloat16 conversion over ten decades."""
+    r = oracle.round_bf16(np.array([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -7,
+                                    1 + 2 ** -8 + 2 ** -20, -(1 + 2 ** -8), 0.0]))
+    np.testing.assert_array_equal(r, [1.0, 1.0, 1 + 2 ** -6, 1 + 2 ** -7, 1 + 2 ** -7, -1.0, 0.0])
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal(50000) * 10.0 ** rng.uniform(-5, 5, 50000)
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(oracle.round_bf16(x), ref)
+
+
+def test_decoder_layer_rounding_points(tiny_model):
+    """The optional activation rounding of decoder_layer touches exactly the stored
+    activations (LN1 out, new k, new v, attention out, LN2 out, GeLU out) in that
+    order, never the residual stream; without it the layer is the one forward() runs."""
+    m, om = tiny_model
+    ids, valid = bi.prompts(m, 2, 8, (8, 5))
+    pad = 8 - valid
+    x0 = oracle.layer_norm(np.asarray(om.embed[ids], dtype=np.float64), om.emb_ln[0],
+                           om.emb_ln[1], om.ln_eps)
+    empty = np.zeros((2, m.n_head_local, 0, m.head_dim))
+    calls = []
+
+    def record(t):
+        calls.append(t.shape)
+        return t
+
+    y = oracle.decoder_layer(om, om.layers[0], x0, pad, 0, {"k": empty, "v": empty}, act=record)
+    B, S, h, H, d = 2, 8, m.hidden, m.n_head_local, m.head_dim
+    assert calls == [(B, S, h), (B, S, H, d), (B, S, H, d), (B, S, H, d), (B, S, h),
+                     (B, S, m.ffn)]
+    trace = []
+    oracle.forward(om, ids, 0, pad, oracle.new_cache(om, 2), trace=trace)
+    np.testing.assert_array_equal(y, trace[0])
+    c = {"k": empty, "v": empty}
+    yr = oracle.decoder_layer(om, om.layers[0], x0, pad, 0, c, act=oracle.round_bf16)
+    np.testing.assert_array_equal(c["k"], oracle.round_bf16(c["k"]))
+    np.testing.assert_array_equal(c["v"], oracle.round_bf16(c["v"]))
+    rel = np.linalg.norm(yr - y) / np.linalg.norm(y)
+    assert 0 < rel < 1e-2
