@@ -10,12 +10,12 @@
 //      those lanes; all K and V loads of a batch of slots are issued together, before
 //      the row's valid length is known; slots before pad_b are masked)
 //   2. softmax over the visible keys only -- masked keys are never touched, i.e. they
-//      get probability exactly 0.  Each lane group keeps its own running maximum, sum
-//      and P.V accumulators over its keys (rescaled by exp(old max - new max) when the
-//      maximum grows: the online form of the same softmax), with no block-wide step
-//      until the end.
-//   3. the groups are combined once through LDS, in a fixed order:
-//      o = sum_g exp(m_g - M) acc_g / sum_g exp(m_g - M) l_g, M the largest m_g.
+//      get probability exactly 0.  Within a batch: block max, exp, running sum; across
+//      batches (rows longer than one batch) the running sum and the P.V accumulators
+//      are rescaled by exp(old max - new max), the usual online form of the same
+//      softmax.
+//   3. o = (sum_j p_j v_j) / sum_j p_j, per lane group over its keys, then summed over
+//      the groups in LDS in a fixed order.
 // A query with no visible key (a left-pad position of the prompt) gets o = 0.
 // ("Hugging Face BLOOM Inference Optimization", Custom CUDA Kernels and Hardware
 // Acceleration, for the fused mask + float32 softmax; "DeepSpeed Inference ...",
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256) void k_attention(const float *__restrict__ q,
                                                    int prompt_len) {
   constexpr int KB = KeysPerBatch<TA>::value;
   __shared__ float pv[256 * 8];     // [G][d] per-group P.V partials
-  __shared__ float gm[256], gl[256];  // per-group running maximum and sum
+  __shared__ float red[4];
   const int m = blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x;
   const int b = m / rows_per_seq;
@@ -104,11 +104,10 @@ __global__ __launch_bounds__(256) void k_attention(const float *__restrict__ q,
   const int vl = vl_in < 1 ? 1 : (vl_in > prompt_len ? prompt_len : vl_in);
   const int first = prompt_len - vl;
 
-  // Online softmax per lane group over its slots, in batches of G*KB slots (one batch
-  // when qpos < G*KB): running maximum mg, sum lg and P.V accumulators, rescaled by
-  // exp(mg_old - mg_new) when the group's maximum grows.  The groups are combined once,
-  // at the end, through LDS: o = sum_g e^(mg - M) acc_g / sum_g e^(mg - M) lg.
-  float mg = -INFINITY, lg = 0.f;
+  // Online softmax over batches of G*KB slots (one batch when qpos < G*KB): running
+  // maximum mrun (block-uniform), per-thread running sum and P.V accumulators, all
+  // rescaled by exp(mrun_old - mrun_new) when the maximum grows.
+  float mrun = -INFINITY, lsum = 0.f;
   float acc[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) acc[t] = 0.f;
@@ -125,7 +124,7 @@ __global__ __launch_bounds__(256) void k_attention(const float *__restrict__ q,
     // scores s_j = q.k_j + slope * (j - qpos), summed across the group's L lanes;
     // slots before `first` are masked
     float sc[KB];
-    float gmax = -INFINITY;
+    float bmax = -INFINITY;
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
       const int jj = j0 + u * G + g;
@@ -136,45 +135,37 @@ __global__ __launch_bounds__(256) void k_attention(const float *__restrict__ q,
       }
       for (int off = L >> 1; off > 0; off >>= 1) dot += __shfl_xor(dot, off, 64);
       sc[u] = (jj < S && jj >= first) ? dot + slope * (float)(jj - qpos) : -INFINITY;
-      gmax = fmaxf(gmax, sc[u]);
+      bmax = fmaxf(bmax, sc[u]);
     }
-    const float mnew = fmaxf(mg, gmax);
-    if (mnew != -INFINITY) {            // uniform within a group
-      // 0 while the group has seen no visible slot (mg = -inf): lg and acc are still 0
-      const float alpha = mg == -INFINITY ? 0.f : __expf(mg - mnew);
-      lg *= alpha;
+    const float mnew = fmaxf(mrun, block_max<4>(bmax, red));
+    // 0 while no slot has been visible (mrun = -inf): lsum and acc are still 0
+    const float alpha = mrun == -INFINITY ? 0.f : __expf(mrun - mnew);
+    lsum *= alpha;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) acc[t] *= alpha;
+    for (int t = 0; t < 8; ++t) acc[t] *= alpha;
 #pragma unroll
-      for (int u = 0; u < KB; ++u) {
-        if (sc[u] == -INFINITY) continue;
+    for (int u = 0; u < KB; ++u) {
+      const int jj = j0 + u * G + g;
+      if (jj < S && jj >= first) {
         const float p = __expf(sc[u] - mnew);
-        lg += p;
+        if (sub == 0) lsum += p;                  // each key counted once per group
 #pragma unroll
         for (int t = 0; t < 8; ++t) acc[t] = fmaf(p, vr[u].get(t), acc[t]);
       }
-      mg = mnew;
     }
+    mrun = mnew;
   }
-  if (sub == 0) {
-    gm[g] = mg;
-    gl[g] = lg;
-  }
+  const float total = block_sum<4>(lsum, red);
+  // a query with no visible key (a left-pad position of the prompt) gets o = 0
+  const float inv = qpos < first ? 0.f : 1.0f / total;
+
 #pragma unroll
   for (int t = 0; t < 8; ++t) pv[g * d + 8 * sub + t] = acc[t];
   __syncthreads();
   for (int e = tid; e < d; e += 256) {
-    float M = -INFINITY;
-    for (int gg = 0; gg < G; ++gg) M = fmaxf(M, gm[gg]);
-    float num = 0.f, den = 0.f;
-    for (int gg = 0; gg < G; ++gg) {
-      if (gm[gg] == -INFINITY) continue;
-      const float w = __expf(gm[gg] - M);
-      num = fmaf(w, pv[gg * d + e], num);
-      den = fmaf(w, gl[gg], den);
-    }
-    // a query with no visible key (a left-pad position of the prompt) gets o = 0
-    out[e] = from_f<TA>((qpos < first || den == 0.f) ? 0.f : num / den);
+    float s = 0.f;
+    for (int gg = 0; gg < G; ++gg) s += pv[gg * d + e];
+    out[e] = from_f<TA>(s * inv);
   }
 }
 
