@@ -202,6 +202,19 @@ int alibi_masked_softmax(const void *d_scores, int32_t in_dtype, const int32_t *
 int kv_cache_append(const bloom_config *cfg, bloom_kv_cache *kv, int32_t layer, int32_t batch,
                     int32_t pos, const void *d_k, const void *d_v, int32_t n_new, void *stream);
 
+/* Dynamic batch extraction ("Hugging Face BLOOM Inference Optimization", Webserver
+ * Architecture and Request Handling: requests that have finished are taken out of the
+ * running batch instead of waiting for the longest one).  Compacts the KV cache in
+ * place: for i < n_keep, row i of every layer and head takes the slots [0, kv->len) of
+ * row keep[i].  keep is a HOST array of n_keep row indices, strictly increasing, each
+ * in [0, batch); rows n_keep .. batch-1 keep stale contents.  The caller compacts its
+ * own per-row arrays (tokens, valid lengths) the same way and continues with batch =
+ * n_keep.  Asynchronous on `stream` (the indices are passed by value, so keep may be
+ * reused at once).  EINVAL for a bad index list, ECAPACITY if batch > kv->max_batch;
+ * n_keep = 0 is a no-op.  Does not change kv->len or kv->prompt_len. */
+int kv_cache_compact(const bloom_config *cfg, bloom_kv_cache *kv, int32_t batch,
+                     const int32_t *keep, int32_t n_keep, void *stream);
+
 /* Launch timer for measurement.  While enabled (and not paused), every launch of the
  * library's linear-layer kernels (the weight-streaming GEMV / GEMM of the four layer
  * linears and the LM head) is made with hipExtLaunchKernelGGL and a pair of hipEvents,

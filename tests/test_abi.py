@@ -177,6 +177,22 @@ def test_kv_append_validation_paths():
     assert app(0, 1, -1, 1) == tb.BLOOM_EINVAL
 
 
+def test_kv_compact_validation_paths():
+    f = _Fake(bi.BLOOM_560M)
+    f.kv.len = 8
+    comp = lambda batch, keep: tb.lib.kv_cache_compact(
+        ctypes.byref(f.cfg), ctypes.byref(f.kv), batch, (ctypes.c_int32 * max(1, len(keep)))(*keep),
+        len(keep), None)
+    assert comp(4, [2, 2]) == tb.BLOOM_EINVAL               # not strictly increasing
+    assert comp(4, [1, 0]) == tb.BLOOM_EINVAL
+    assert comp(4, [0, 4]) == tb.BLOOM_EINVAL               # index >= batch
+    assert comp(4, [-1]) == tb.BLOOM_EINVAL
+    assert comp(2, [0, 1, 1]) == tb.BLOOM_EINVAL            # n_keep > batch
+    assert comp(5, [0]) == tb.BLOOM_ECAPACITY               # batch > max_batch
+    assert comp(4, []) == tb.BLOOM_OK                       # nothing kept: no-op
+    assert f.kv.len == 8
+
+
 def test_softmax_validation_paths():
     sm = lambda *a: tb.lib.alibi_masked_softmax(*a)
     assert sm(0x10, 1, 0x10, 1, 1, 3, 2, 8, 0, 0x10, 0, None) == tb.BLOOM_EINVAL   # Q > K

@@ -100,3 +100,49 @@ def test_tp_share_176b_graph_two_layers_oracle():
           f"exact ids {v.exact_frac:.3f}")
     assert v.hidden_rel <= 1e-2 and v.tokens_ok
     _same(g, _run(cfg, dw, prompt, vl, 6, graph=False))
+
+
+def test_dynamic_batch_extraction_compacts_kv_cache():
+    """Four rows decode together; two of them are extracted after 5 tokens
+    (kv_cache_compact keeps rows 0 and 2) and the other two go on alone as a batch of 2.
+    The compacted cache holds the kept rows' slots bit for bit, and the kept rows' whole
+    generation matches the oracle."""
+    m = bi.BLOOM_560M.truncated(3)
+    T, dw, cfg = upload(m, seed=71)
+    B, P, n1, n2 = 4, 12, 5, 6
+    prompt, valid = bi.prompts(m, B, P, (12, 7, 12, 3), seed=72)
+    kv = tb.KVCache(cfg, B, P + n1 + n2, fill=float("nan"))
+    ws = tb.workspace(cfg, B, P)
+    tok = torch.from_numpy(prompt.astype(np.int32)).cuda()
+    vl = torch.from_numpy(np.asarray(valid, dtype=np.int32)).cuda()
+    ids1 = torch.empty((n1, B), dtype=torch.int32, device="cuda")
+    hid1 = torch.empty((n1, B, m.hidden), dtype=torch.float32, device="cuda")
+    tb.bloom_prefill(cfg, dw, kv, B, P, tok, vl, ids1[0], hid1[0], ws)
+    for t in range(1, n1):
+        tb.bloom_decode_step(cfg, dw, kv, B, ids1[t - 1], vl, ids1[t], hid1[t], ws)
+    keep = [0, 2]
+    L = kv.len
+    k_before, v_before = kv.k.clone(), kv.v.clone()
+    tb.kv_cache_compact(cfg, kv, B, keep)
+    torch.cuda.synchronize()
+    for new, old in ((kv.k, k_before), (kv.v, v_before)):
+        for i, r in enumerate(keep):
+            assert torch.equal(new[:, i, :, :L].view(torch.int16),
+                               old[:, r, :, :L].view(torch.int16))
+    assert kv.len == L
+    vl2 = vl[keep].contiguous()
+    cur = ids1[n1 - 1, keep].contiguous()
+    ids2 = torch.empty((n2, 2), dtype=torch.int32, device="cuda")
+    hid2 = torch.empty((n2, 2, m.hidden), dtype=torch.float32, device="cuda")
+    for t in range(n2):
+        tb.bloom_decode_step(cfg, dw, kv, 2, cur if t == 0 else ids2[t - 1], vl2, ids2[t],
+                             hid2[t], ws)
+    torch.cuda.synchronize()
+    ids = np.concatenate([ids1.cpu().numpy()[:, keep], ids2.cpu().numpy()], axis=0).T.copy()
+    hid = np.concatenate([hid1.cpu().numpy()[:, keep], hid2.cpu().numpy()], axis=0)
+    from gpu_util import GpuRun
+    v = compare(m, T, prompt[keep], np.asarray(valid)[keep], GpuRun(ids, hid, kv, cfg), 1e-2,
+                widen_embed=True)
+    print(f"extraction 4 -> 2 rows: hidden rel {v.hidden_rel:.2e}, exact ids {v.exact_frac:.3f}")
+    assert v.hidden_rel <= 1e-2 and v.tokens_ok
+    assert kv.len == P + n1 + n2 - 1

@@ -92,12 +92,14 @@ def _load():
                                          _i32, vp]
     lib.kv_cache_append.argtypes = [P(bloom_config), P(bloom_kv_cache), _i32, _i32, _i32, vp, vp,
                                     _i32, vp]
+    lib.kv_cache_compact.argtypes = [P(bloom_config), P(bloom_kv_cache), _i32, P(_i32), _i32, vp]
     lib.bloom_timer_enable.argtypes = [_i32]
     lib.bloom_timer_disable.argtypes = []
     lib.bloom_timer_read.argtypes = [_i32, P(ctypes.c_double), P(_i32), P(ctypes.c_double)]
     lib.bloom_timer_pause.argtypes = [_i32]
     for name in ("bloom_workspace_bytes", "bloom_prefill", "bloom_decode_step", "bloom_generate",
-                 "alibi_masked_softmax", "kv_cache_append", "bloom_timer_enable",
+                 "alibi_masked_softmax", "kv_cache_append", "kv_cache_compact",
+                 "bloom_timer_enable",
                  "bloom_timer_disable", "bloom_timer_read", "bloom_timer_pause"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
@@ -185,6 +187,14 @@ def kv_cache_append(cfg, kv, layer: int, batch: int, pos: int, k, v, n_new: int,
     s = kv.struct if hasattr(kv, "struct") else kv
     _check(lib.kv_cache_append(ctypes.byref(cfg), ctypes.byref(s), layer, batch, pos, _ptr(k),
                                _ptr(v), n_new, _stream(stream)), "kv_cache_append")
+
+
+def kv_cache_compact(cfg, kv, batch: int, keep, stream=None):
+    """Rows keep[i] of the cache -> row i (keep: host sequence of strictly increasing ints)."""
+    s = kv.struct if hasattr(kv, "struct") else kv
+    arr = (_i32 * max(1, len(keep)))(*[int(k) for k in keep])
+    _check(lib.kv_cache_compact(ctypes.byref(cfg), ctypes.byref(s), batch, arr, len(keep),
+                                _stream(stream)), "kv_cache_compact")
 
 
 def bloom_timer_enable(max_launches: int):

@@ -525,6 +525,25 @@ int kv_cache_append(const bloom_config *cfg, bloom_kv_cache *kv, int32_t layer, 
   return err == hipSuccess ? BLOOM_OK : hip_fail(err);
 }
 
+int kv_cache_compact(const bloom_config *cfg, bloom_kv_cache *kv, int32_t batch,
+                     const int32_t *keep, int32_t n_keep, void *stream) {
+  int s = check_config(cfg);
+  if (s != BLOOM_OK) return s;
+  if ((s = check_kv(cfg, kv)) != BLOOM_OK) return s;
+  if (batch < 0 || n_keep < 0 || n_keep > batch) return BLOOM_EINVAL;
+  if (batch > kv->max_batch) return BLOOM_ECAPACITY;
+  if (n_keep == 0) return BLOOM_OK;
+  if (!keep) return BLOOM_EINVAL;
+  for (int i = 0; i < n_keep; ++i)
+    if (keep[i] < 0 || keep[i] >= batch || (i > 0 && keep[i] <= keep[i - 1])) return BLOOM_EINVAL;
+  clear_stale_hip_error();
+  const hipError_t err = launch_kv_compact(kv->k, kv->v, cfg->n_layer, cfg->n_head_local,
+                                           kv->max_batch, kv->max_len, cfg->head_dim,
+                                           act_bytes(cfg), kv->len, keep, n_keep,
+                                           (hipStream_t)stream);
+  return err == hipSuccess ? BLOOM_OK : hip_fail(err);
+}
+
 int bloom_timer_enable(int32_t max_launches) {
   if (max_launches <= 0) return BLOOM_EINVAL;
   destroy_timer_events();

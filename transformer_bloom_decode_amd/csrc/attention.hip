@@ -341,4 +341,57 @@ hipError_t launch_kv_append(bool f32, const void *k, const void *v, void *ck, vo
   return hipGetLastError();
 }
 
+// In-place compaction of the KV cache ("Hugging Face BLOOM Inference Optimization",
+// Webserver Architecture and Request Handling: finished requests are extracted from
+// the running batch): destination row j0 + i takes source row rows[i] (rows strictly
+// increasing, rows[i] >= j0 + i), slots [0, len), keys and values, every layer and head.
+// One block per (layer, head) walks its destination rows in increasing order; every
+// thread copies the same 16-byte offsets of each row, so a row is read (as a source)
+// before the same thread overwrites it (as a later destination) and no barrier is
+// needed; blocks touch disjoint (layer, head) ranges.
+struct KvRows {
+  int src[kKvCompactChunk];
+};
+
+__global__ __launch_bounds__(256) void k_kv_compact(unsigned char *__restrict__ kc,
+                                                    unsigned char *__restrict__ vc,
+                                                    size_t layer_stride, size_t row_stride,
+                                                    size_t head_stride, size_t row_bytes,
+                                                    KvRows rows, int n, int j0) {
+  const size_t base = blockIdx.x * layer_stride + blockIdx.y * head_stride;
+  const size_t pieces = row_bytes / 16;
+  for (int i = 0; i < n; ++i) {
+    const int src = rows.src[i], dst = j0 + i;
+    if (src == dst) continue;
+    const size_t so = base + (size_t)src * row_stride, dof = base + (size_t)dst * row_stride;
+    for (size_t p = threadIdx.x; p < pieces; p += 256) {
+      const u32x4 a = *(const u32x4 *)(kc + so + 16 * p);
+      const u32x4 b = *(const u32x4 *)(vc + so + 16 * p);
+      *(u32x4 *)(kc + dof + 16 * p) = a;
+      *(u32x4 *)(vc + dof + 16 * p) = b;
+    }
+  }
+}
+
+hipError_t launch_kv_compact(void *kc, void *vc, int n_layer, int H, int max_batch, int max_len,
+                             int d, size_t act, int len, const int *rows, int n_keep,
+                             hipStream_t st) {
+  const size_t head_stride = (size_t)max_len * d * act;
+  const size_t row_stride = (size_t)H * head_stride;
+  const size_t layer_stride = (size_t)max_batch * row_stride;
+  const size_t row_bytes = (size_t)len * d * act;
+  if (row_bytes == 0 || n_keep <= 0) return hipSuccess;
+  for (int j0 = 0; j0 < n_keep; j0 += kKvCompactChunk) {
+    KvRows r{};
+    const int n = std::min(kKvCompactChunk, n_keep - j0);
+    for (int i = 0; i < n; ++i) r.src[i] = rows[j0 + i];
+    hipLaunchKernelGGL(k_kv_compact, dim3(n_layer, H), dim3(256), 0, st, (unsigned char *)kc,
+                       (unsigned char *)vc, layer_stride, row_stride, head_stride, row_bytes, r,
+                       n, j0);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 }  // namespace bl

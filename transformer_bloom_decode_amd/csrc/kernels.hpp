@@ -106,6 +106,12 @@ hipError_t launch_gen_init(int *state, int pos, int step, const int *first, int 
                            hipStream_t st);
 hipError_t launch_gen_record(const int *next, int *cur, int *ids, const float *hfix, float *hout,
                              int *state, int batch, int hidden, hipStream_t st);
+// KV-cache compaction: rows[i] -> row i (strictly increasing sources), slots [0, len),
+// all layers and heads, in place.  Sources are passed by value in chunks.
+constexpr int kKvCompactChunk = 256;
+hipError_t launch_kv_compact(void *kc, void *vc, int n_layer, int H, int max_batch, int max_len,
+                             int d, size_t act, int len, const int *rows, int n_keep,
+                             hipStream_t st);
 hipError_t launch_kv_append(bool f32, const void *k, const void *v, void *ck, void *cv,
                             int batch, int H, int n_new, int d, int max_len, int pos,
                             hipStream_t st);
