@@ -166,20 +166,37 @@ int bloom_decode_step(const bloom_config *cfg, const bloom_weights *w, bloom_kv_
                       int32_t *d_next_tokens, float *d_hidden_out, void *d_ws,
                       size_t ws_bytes, void *stream);
 
+/* Per-row generation control of bloom_generate ("Hugging Face BLOOM Inference
+ * Optimization", Webserver Architecture and Request Handling: a custom generation loop
+ * with per-request parameters in one batch).  Row b finishes at the step where it
+ * emits eos_id (that token is kept) or where it has d_max_new[b] tokens; its later
+ * steps record pad_id (the row is still computed, fed pad_id, so its KV slots and
+ * hidden states of those steps are those of pad tokens).  eos_id < 0: no end token;
+ * d_max_new (device [batch] int32) nullable: no per-row limit; d_out_len (device
+ * [batch] int32, nullable) receives each row's token count (n_new if it never
+ * finished).  Finished rows can be taken out between calls with kv_cache_compact. */
+typedef struct {
+  int32_t eos_id;
+  int32_t pad_id;
+  const int32_t *d_max_new;
+  int32_t *d_out_len;
+} bloom_gen_control;
+
 /* Greedy generation loop ([P1] Benchmark Environment: greedy generation of new tokens
  * with the KV cache; [P3] III.D: launch overhead at small batch is removed with graphs).
  * Runs the prompt pass (as bloom_prefill), then n_new - 1 decode steps: the first
  * eagerly, the rest as replays of one HIP graph captured from a decode step whose KV
  * position and input tokens live in device memory.  d_ids [n_new][batch] int32
- * receives the greedy token of every step (row 0 from the prompt pass); d_hidden
- * (nullable) [n_new][batch][hidden] float32 the final-LayerNorm states.  kv->len ends
- * at prompt_len + n_new - 1.  Returns after the generation has finished (the graph is
- * released).  ECAPACITY if prompt_len + n_new - 1 > kv->max_len or batch >
- * kv->max_batch; the workspace is bloom_workspace_bytes(cfg, batch, prompt_len). */
+ * receives the token of every step (row 0 from the prompt pass); d_hidden (nullable)
+ * [n_new][batch][hidden] float32 the final-LayerNorm states; ctl (host struct,
+ * nullable: plain greedy) the per-row stop rule above.  kv->len ends at prompt_len +
+ * n_new - 1.  Returns after the generation has finished (the graph is released).
+ * ECAPACITY if prompt_len + n_new - 1 > kv->max_len or batch > kv->max_batch; EINVAL if
+ * ctl->eos_id >= vocab; the workspace is bloom_workspace_bytes(cfg, batch, prompt_len). */
 int bloom_generate(const bloom_config *cfg, const bloom_weights *w, bloom_kv_cache *kv,
                    int32_t batch, int32_t prompt_len, const int32_t *d_tokens,
                    const int32_t *d_valid_len, int32_t n_new, int32_t *d_ids, float *d_hidden,
-                   void *d_ws, size_t ws_bytes, void *stream);
+                   const bloom_gen_control *ctl, void *d_ws, size_t ws_bytes, void *stream);
 
 /* Standalone fused ALiBi bias + masked fill + float32 softmax ([P4] Custom CUDA Kernels
  * and Hardware Acceleration; Efficient PyTorch Implementation for ALiBi).

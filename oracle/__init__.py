@@ -26,4 +26,5 @@ from .bloom_oracle import (  # noqa: F401
     masked_softmax,
     new_cache,
     round_bf16,
+    stop_rule,
 )

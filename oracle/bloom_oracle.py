@@ -347,6 +347,27 @@ class GenerateResult:
     cache: list
 
 
+def stop_rule(tokens: np.ndarray, eos_id: int, max_new, pad_id: int):
+    """Per-row end of generation ("Hugging Face BLOOM Inference Optimization", Webserver
+    Architecture and Request Handling: requests in one batch end at their own limits).
+    Row b ends at its first step t whose token is eos_id (kept) or at t = max_new[b] - 1;
+    later tokens become pad_id.  tokens [B, n]; eos_id < 0 for none; max_new None or [B].
+    Returns (tokens with the rule applied, tokens per row)."""
+    tokens = np.array(tokens, copy=True)
+    B, n = tokens.shape
+    lengths = np.full(B, n, dtype=np.int64)
+    for b in range(B):
+        limit = n if max_new is None else max(1, min(n, int(max_new[b])))
+        end = limit
+        for t in range(limit):
+            if eos_id >= 0 and tokens[b, t] == eos_id:
+                end = t + 1
+                break
+        tokens[b, end:] = pad_id
+        lengths[b] = end
+    return tokens, lengths
+
+
 def greedy_argmax(logits: np.ndarray) -> np.ndarray:
     """Lowest token id among the maxima, decided on float32-rounded logits."""
     return np.argmax(logits.astype(np.float32), axis=-1).astype(np.int32)

@@ -39,7 +39,9 @@ def test_status_strings():
 
 
 def test_struct_layout_matches_header():
-    # 10 int32 + 1 float; 16 pointers; 5 pointers + 1 pointer; 2 pointers + 4 int32
+    # 10 int32 + 1 float; 16 pointers; 5 pointers + 1 pointer; 2 pointers + 4 int32;
+    # 2 int32 + 2 pointers
+    assert ctypes.sizeof(tb.bloom_gen_control) == 24
     assert ctypes.sizeof(tb.bloom_config) == 44
     assert ctypes.sizeof(tb.bloom_layer_weights) == 16 * 8
     assert ctypes.sizeof(tb.bloom_weights) == 6 * 8
@@ -148,10 +150,11 @@ def test_decode_validation_paths():
     assert _decode(f) == tb.BLOOM_EINVAL
 
 
-def _generate(f, batch=2, prompt=8, n_new=4, ws_bytes=1 << 40, ids=0x1000):
+def _generate(f, batch=2, prompt=8, n_new=4, ws_bytes=1 << 40, ids=0x1000, ctl=None):
     return tb.lib.bloom_generate(ctypes.byref(f.cfg), ctypes.byref(f.w), ctypes.byref(f.kv),
-                                 batch, prompt, 0x1000, 0x1000, n_new, ids, None, 0x1000,
-                                 ws_bytes, None)
+                                 batch, prompt, 0x1000, 0x1000, n_new, ids, None,
+                                 None if ctl is None else ctypes.byref(ctl), 0x1000, ws_bytes,
+                                 None)
 
 
 def test_generate_validation_paths():
@@ -163,6 +166,9 @@ def test_generate_validation_paths():
     assert _generate(f, ids=None) == tb.BLOOM_EINVAL
     assert _generate(f, ws_bytes=1024) == tb.BLOOM_EWORKSPACE
     assert _generate(f, batch=0) == tb.BLOOM_OK
+    assert _generate(f, ctl=tb.bloom_gen_control(250880, 0, None, None)) == tb.BLOOM_EINVAL
+    assert _generate(f, ctl=tb.bloom_gen_control(5, 0, None, None), ws_bytes=16) == \
+        tb.BLOOM_EWORKSPACE
     assert f.kv.len == 0 and f.kv.prompt_len == 0
 
 

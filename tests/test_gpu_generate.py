@@ -146,3 +146,48 @@ def test_dynamic_batch_extraction_compacts_kv_cache():
     print(f"extraction 4 -> 2 rows: hidden rel {v.hidden_rel:.2e}, exact ids {v.exact_frac:.3f}")
     assert v.hidden_rel <= 1e-2 and v.tokens_ok
     assert kv.len == P + n1 + n2 - 1
+
+
+def test_generation_control_eos_and_row_limits():
+    """bloom_generate with an end token and per-row limits: each row's tokens are those
+    of plain greedy generation up to its end (its own end token kept, or its limit),
+    pad after; the token counts are reported; the hidden states (pad-fed after a row's
+    end) match the oracle teacher-forced on the same tokens."""
+    m = bi.BLOOM_560M.truncated(3)
+    T, dw, cfg = upload(m, seed=81)
+    B, P, n_new, pad = 3, 10, 14, 3
+    prompt, valid = bi.prompts(m, B, P, (10, 6, 10), seed=82)
+    base = _run(cfg, dw, prompt, valid, n_new, graph=True)[0]            # [B, n_new]
+    # greedy decoding of this random-weight model repeats one token per row, so the end
+    # token is row 2's (row 2 ends on its first token), row 1 ends on its limit of 6
+    # tokens and row 0 runs to n_new (the rule's mid-sequence cases are pinned on the
+    # CPU, test_stop_rule_hand_worked)
+    eos = int(base[2, 0])
+    assert eos not in base[:2]
+    max_new = np.array([n_new, 6, n_new], dtype=np.int32)
+    expected, lengths = oracle.stop_rule(base, eos, max_new, pad)
+
+    kv = tb.KVCache(cfg, B, P + n_new, fill=float("nan"))
+    ws = tb.workspace(cfg, B, P)
+    tok = torch.from_numpy(prompt.astype(np.int32)).cuda()
+    vl = torch.from_numpy(np.asarray(valid, dtype=np.int32)).cuda()
+    ids = torch.empty((n_new, B), dtype=torch.int32, device="cuda")
+    hid = torch.empty((n_new, B, m.hidden), dtype=torch.float32, device="cuda")
+    out_len = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+    tb.bloom_generate(cfg, dw, kv, B, P, tok, vl, n_new, ids, hid, ws, eos_id=eos, pad_id=pad,
+                      max_new=torch.from_numpy(max_new).cuda(), out_len=out_len)
+    got = ids.cpu().numpy().T
+    np.testing.assert_array_equal(got, expected)
+    np.testing.assert_array_equal(out_len.cpu().numpy(), lengths)
+    assert kv.len == P + n_new - 1
+
+    om = oracle.OracleModel.from_storage(m, T)
+    om.embed = np.asarray(om.embed, dtype=np.float64)
+    res = oracle.greedy_generate(om, prompt, valid, n_new, forced=got)
+    h = hid.cpu().numpy()
+    rel = float(np.linalg.norm(h - res.hidden) / np.linalg.norm(res.hidden))
+    print(f"generation control: ends {lengths.tolist()}, hidden rel {rel:.2e}")
+    assert rel <= 1e-2
+    for b in range(B):
+        for t in range(int(lengths[b])):
+            assert res.chosen[t, b] >= res.top1[t, b] - 3e-2 * res.rms[t, b]

@@ -463,3 +463,19 @@ def test_decoder_layer_rounding_points(tiny_model):
     np.testing.assert_array_equal(c["v"], oracle.round_bf16(c["v"]))
     rel = np.linalg.norm(yr - y) / np.linalg.norm(y)
     assert 0 < rel < 1e-2
+
+
+def test_stop_rule_hand_worked():
+    toks = np.array([[5, 9, 7, 9, 1],
+                     [3, 3, 3, 3, 3],
+                     [9, 2, 2, 2, 2],
+                     [4, 4, 9, 4, 4]])
+    out, n = oracle.stop_rule(toks, eos_id=9, max_new=[5, 2, 5, 1], pad_id=0)
+    np.testing.assert_array_equal(out, [[5, 9, 0, 0, 0],     # eos at step 1, kept
+                                        [3, 3, 0, 0, 0],     # limit of 2 tokens
+                                        [9, 0, 0, 0, 0],     # eos first
+                                        [4, 0, 0, 0, 0]])    # limit 1 before its eos
+    np.testing.assert_array_equal(n, [2, 2, 1, 1])
+    same, n2 = oracle.stop_rule(toks, eos_id=-1, max_new=None, pad_id=0)
+    np.testing.assert_array_equal(same, toks)
+    np.testing.assert_array_equal(n2, [5, 5, 5, 5])

@@ -54,6 +54,11 @@ class bloom_kv_cache(ctypes.Structure):
                 ("len", _i32), ("prompt_len", _i32)]
 
 
+class bloom_gen_control(ctypes.Structure):
+    _fields_ = [("eos_id", _i32), ("pad_id", _i32), ("d_max_new", _c_void_p),
+                ("d_out_len", _c_void_p)]
+
+
 class BloomError(RuntimeError):
     def __init__(self, code: int, where: str):
         self.code = code
@@ -87,7 +92,8 @@ def _load():
     lib.bloom_decode_step.argtypes = [P(bloom_config), P(bloom_weights), P(bloom_kv_cache), _i32,
                                       vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.bloom_generate.argtypes = [P(bloom_config), P(bloom_weights), P(bloom_kv_cache), _i32,
-                                   _i32, vp, vp, _i32, vp, vp, vp, ctypes.c_size_t, vp]
+                                   _i32, vp, vp, _i32, vp, vp, P(bloom_gen_control), vp,
+                                   ctypes.c_size_t, vp]
     lib.alibi_masked_softmax.argtypes = [vp, _i32, vp, _i32, _i32, _i32, _i32, _i32, _i32, vp,
                                          _i32, vp]
     lib.kv_cache_append.argtypes = [P(bloom_config), P(bloom_kv_cache), _i32, _i32, _i32, vp, vp,
@@ -167,12 +173,19 @@ def bloom_decode_step(cfg, weights, kv, batch: int, tokens, valid_len, next_toke
 
 
 def bloom_generate(cfg, weights, kv, batch: int, prompt_len: int, tokens, valid_len, n_new: int,
-                   ids, hidden_out, ws, stream=None):
+                   ids, hidden_out, ws, stream=None, eos_id: Optional[int] = None, pad_id: int = 0,
+                   max_new=None, out_len=None):
+    """bloom_generate; eos_id / max_new (device int32 [batch]) / out_len (device int32
+    [batch]) fill a bloom_gen_control when any of them is given."""
     w = weights.struct if hasattr(weights, "struct") else weights
     k = kv.struct if hasattr(kv, "struct") else kv
+    ctl = None
+    if eos_id is not None or max_new is not None or out_len is not None:
+        ctl = ctypes.byref(bloom_gen_control(-1 if eos_id is None else eos_id, pad_id,
+                                             _ptr(max_new), _ptr(out_len)))
     _check(lib.bloom_generate(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(k), batch,
                               prompt_len, _ptr(tokens), _ptr(valid_len), n_new, _ptr(ids),
-                              _ptr(hidden_out), _ptr(ws), _nbytes(ws), _stream(stream)),
+                              _ptr(hidden_out), ctl, _ptr(ws), _nbytes(ws), _stream(stream)),
            "bloom_generate")
 
 

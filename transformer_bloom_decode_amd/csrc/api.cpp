@@ -40,7 +40,7 @@ int hip_fail(hipError_t e) {
 }
 
 struct WsPlan {
-  size_t gen, cur, nxt, hfix;   // generation loop state (same offsets for every pass)
+  size_t gen, cur, nxt, hfix, done;   // generation loop state (same offsets for every pass)
   size_t x, xa, q, o, u, af, amv, ami, part, total;
   int lm_blocks;
 };
@@ -66,6 +66,7 @@ WsPlan plan_ws(const bloom_config *c, int batch, int tokens_per_row) {
   p.cur = take((size_t)batch * sizeof(int));
   p.nxt = take((size_t)batch * sizeof(int));
   p.hfix = take((size_t)batch * c->hidden * sizeof(float));
+  p.done = take((size_t)batch * sizeof(int));
   p.x = take(M * c->hidden * 4);
   p.xa = take(M * c->hidden * act);
   p.q = take(M * hd * 4);
@@ -417,7 +418,7 @@ int bloom_decode_step(const bloom_config *cfg, const bloom_weights *w, bloom_kv_
 int bloom_generate(const bloom_config *cfg, const bloom_weights *w, bloom_kv_cache *kv,
                    int32_t batch, int32_t prompt_len, const int32_t *d_tokens,
                    const int32_t *d_valid_len, int32_t n_new, int32_t *d_ids, float *d_hidden,
-                   void *d_ws, size_t ws_bytes, void *stream) {
+                   const bloom_gen_control *ctl, void *d_ws, size_t ws_bytes, void *stream) {
   int s = check_config(cfg);
   if (s != BLOOM_OK) return s;
   if ((s = check_weights(cfg, w)) != BLOOM_OK) return s;
@@ -426,33 +427,53 @@ int bloom_generate(const bloom_config *cfg, const bloom_weights *w, bloom_kv_cac
   if (batch > kv->max_batch || (long)prompt_len + n_new - 1 > kv->max_len) return BLOOM_ECAPACITY;
   if (batch == 0) return BLOOM_OK;
   if (!d_tokens || !d_valid_len || !d_ids || !d_ws) return BLOOM_EINVAL;
+  if (ctl && ctl->eos_id >= cfg->vocab) return BLOOM_EINVAL;
   if (ws_bytes < plan_ws(cfg, batch, prompt_len).total) return BLOOM_EWORKSPACE;
   clear_stale_hip_error();
   hipStream_t st = (hipStream_t)stream;
   char *ws = (char *)d_ws;
-  const size_t hsz = (size_t)batch * cfg->hidden;
-  // the prompt pass, then the first step eagerly (it also runs any one-time set-up)
-  s = run_forward(cfg, w, kv, batch, prompt_len, 0, prompt_len, d_tokens, d_valid_len, d_ids,
-                  d_hidden, ws, st);
-  if (s != BLOOM_OK) return s;
-  kv->prompt_len = prompt_len;
-  kv->len = prompt_len;
-  if (n_new == 1) return BLOOM_OK;
-  s = run_forward(cfg, w, kv, batch, 1, kv->len, kv->prompt_len, d_ids, d_valid_len,
-                  d_ids + batch, d_hidden ? d_hidden + hsz : nullptr, ws, st);
-  if (s != BLOOM_OK) return s;
-  kv->len += 1;
-  if (n_new == 2) return BLOOM_OK;
-
-  // One decode step captured on a side stream: position and input tokens come from
-  // device memory, so the same graph is replayed for every remaining step.
+  // generation state, current / next ids and the hidden rows of a step: the same
+  // workspace offsets for every pass
   const WsPlan wp = plan_ws(cfg, batch, 1);
   int *state = (int *)(ws + wp.gen);
   int *cur = (int *)(ws + wp.cur);
   int *nxt = (int *)(ws + wp.nxt);
   float *hfix = d_hidden ? (float *)(ws + wp.hfix) : nullptr;
-  hipError_t err = launch_gen_init(state, kv->len, 2, d_ids + batch, cur, batch, st);
+  GenControl gc{};
+  gc.done = (int *)(ws + wp.done);
+  gc.eos_id = ctl ? ctl->eos_id : -1;
+  gc.pad_id = ctl ? ctl->pad_id : 0;
+  gc.max_new = ctl ? ctl->d_max_new : nullptr;
+  gc.out_len = ctl ? ctl->d_out_len : nullptr;
+
+  // the prompt pass and the first decode step run eagerly (they also run any one-time
+  // set-up); every step's ids go through the same recording kernel
+  hipError_t err = launch_gen_init(state, prompt_len - 1, 0, gc.done, batch, st);
   if (err != hipSuccess) return hip_fail(err);
+  s = run_forward(cfg, w, kv, batch, prompt_len, 0, prompt_len, d_tokens, d_valid_len, nxt,
+                  hfix, ws, st);
+  if (s != BLOOM_OK) return s;
+  if ((err = launch_gen_record(nxt, cur, d_ids, hfix, d_hidden, state, batch, cfg->hidden, gc,
+                               st)) != hipSuccess)
+    return hip_fail(err);
+  kv->prompt_len = prompt_len;
+  kv->len = prompt_len;
+  if (n_new >= 2) {
+    s = run_forward(cfg, w, kv, batch, 1, kv->len, kv->prompt_len, cur, d_valid_len, nxt, hfix,
+                    ws, st);
+    if (s != BLOOM_OK) return s;
+    if ((err = launch_gen_record(nxt, cur, d_ids, hfix, d_hidden, state, batch, cfg->hidden, gc,
+                                 st)) != hipSuccess)
+      return hip_fail(err);
+    kv->len += 1;
+  }
+  if (n_new <= 2) {
+    const hipError_t serr = hipStreamSynchronize(st);
+    return serr == hipSuccess ? BLOOM_OK : hip_fail(serr);
+  }
+
+  // One decode step captured on a side stream: position and input tokens come from
+  // device memory, so the same graph is replayed for every remaining step.
   hipStream_t side = capture_stream();
   if (!side) return hip_fail(hipErrorInvalidResourceHandle);
   if ((err = hipStreamBeginCapture(side, hipStreamCaptureModeThreadLocal)) != hipSuccess)
@@ -462,7 +483,7 @@ int bloom_generate(const bloom_config *cfg, const bloom_weights *w, bloom_kv_cac
                   state);
   g_timer.capturing = false;
   if (s == BLOOM_OK) {
-    err = launch_gen_record(nxt, cur, d_ids, hfix, d_hidden, state, batch, cfg->hidden, side);
+    err = launch_gen_record(nxt, cur, d_ids, hfix, d_hidden, state, batch, cfg->hidden, gc, side);
     if (err != hipSuccess) s = hip_fail(err);
   }
   hipGraph_t graph = nullptr;

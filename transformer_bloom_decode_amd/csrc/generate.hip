@@ -2,32 +2,45 @@
 // Inference with DeepSpeed and Accelerate", Benchmark Environment: greedy decoding of
 // new tokens with the KV cache).  The decode step that bloom_generate captures in a HIP
 // graph reads its KV position and input tokens from device memory, so one graph serves
-// every step; these kernels record each step's output and advance the position.
+// every step; these kernels record each step's output, apply the per-row stop rule and
+// advance the position.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace bl {
 
-__global__ void k_gen_init(int *__restrict__ state, int pos, int step,
-                           const int *__restrict__ first, int *__restrict__ cur, int batch) {
+__global__ void k_gen_init(int *__restrict__ state, int pos, int step, int *__restrict__ done,
+                           int batch) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < batch; i += gridDim.x * blockDim.x)
-    cur[i] = first[i];
+    done[i] = 0;
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     state[0] = pos;
     state[1] = step;
   }
 }
 
-// One block: every thread reads the step index before thread 0 advances it.
+// One block: every thread reads the step index before thread 0 advances it.  Row i's
+// token of step t is next[i] until the row has finished, pad_id after; a row finishes
+// at the step where it emits eos_id (that token is kept) or reaches max_new[i] tokens
+// ("Hugging Face BLOOM Inference Optimization", Webserver Architecture and Request
+// Handling: per-request limits in one batch).  out_len[i] counts the row's tokens.
 __global__ __launch_bounds__(1024) void k_gen_record(const int *__restrict__ next,
                                                      int *__restrict__ cur, int *__restrict__ ids,
                                                      const float *__restrict__ hfix,
                                                      float *__restrict__ hout, int *state,
-                                                     int batch, int hidden) {
+                                                     int batch, int hidden, GenControl gc) {
   const int t = state[1];
   for (int i = threadIdx.x; i < batch; i += blockDim.x) {
-    ids[(size_t)t * batch + i] = next[i];
-    cur[i] = next[i];
+    int tok = next[i];
+    if (gc.done[i]) {
+      tok = gc.pad_id;
+    } else {
+      if (gc.out_len) gc.out_len[i] = t + 1;
+      if ((gc.eos_id >= 0 && tok == gc.eos_id) || (gc.max_new && t + 1 >= gc.max_new[i]))
+        gc.done[i] = 1;
+    }
+    ids[(size_t)t * batch + i] = tok;
+    cur[i] = tok;
   }
   if (hout) {
     const size_t n = (size_t)batch * hidden;
@@ -41,16 +54,16 @@ __global__ __launch_bounds__(1024) void k_gen_record(const int *__restrict__ nex
   }
 }
 
-hipError_t launch_gen_init(int *state, int pos, int step, const int *first, int *cur, int batch,
-                           hipStream_t st) {
-  hipLaunchKernelGGL(k_gen_init, dim3(1), dim3(256), 0, st, state, pos, step, first, cur, batch);
+hipError_t launch_gen_init(int *state, int pos, int step, int *done, int batch, hipStream_t st) {
+  hipLaunchKernelGGL(k_gen_init, dim3(1), dim3(256), 0, st, state, pos, step, done, batch);
   return hipGetLastError();
 }
 
 hipError_t launch_gen_record(const int *next, int *cur, int *ids, const float *hfix, float *hout,
-                             int *state, int batch, int hidden, hipStream_t st) {
+                             int *state, int batch, int hidden, const GenControl &gc,
+                             hipStream_t st) {
   hipLaunchKernelGGL(k_gen_record, dim3(1), dim3(1024), 0, st, next, cur, ids, hfix, hout, state,
-                     batch, hidden);
+                     batch, hidden, gc);
   return hipGetLastError();
 }
 

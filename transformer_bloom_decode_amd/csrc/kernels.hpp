@@ -98,14 +98,24 @@ hipError_t launch_attention(bool f32, const float *q, const void *kc, const void
                             int n_total, int head_off, int rows_per_seq, int pos_base,
                             const int *pos_dev, int prompt_len, hipStream_t st);
 
-// Bookkeeping of a replayed generation step (state[0] = KV position, state[1] = index of
-// the step being recorded): ids[step][b] = next[b], cur[b] = next[b], hout[step] = hfix
-// (hout nullable); then state[0] += 1, state[1] += 1.  gen_init seeds the state and the
-// current tokens.
-hipError_t launch_gen_init(int *state, int pos, int step, const int *first, int *cur, int batch,
-                           hipStream_t st);
+// Per-row stop rule of the generation loop: done[i] set once row i has finished (its
+// eos_id token emitted, or max_new[i] tokens); finished rows emit pad_id; out_len[i]
+// (nullable) counts a row's tokens.  eos_id < 0: none; max_new nullable: no limit.
+struct GenControl {
+  int *done;
+  int eos_id;
+  int pad_id;
+  const int *max_new;
+  int *out_len;
+};
+
+// Bookkeeping of a generation step (state[0] = KV position, state[1] = index of the
+// step being recorded): ids[step][b] and cur[b] = next[b] (pad_id once row b has
+// finished), hout[step] = hfix (if hout), then state advances by one step.
+hipError_t launch_gen_init(int *state, int pos, int step, int *done, int batch, hipStream_t st);
 hipError_t launch_gen_record(const int *next, int *cur, int *ids, const float *hfix, float *hout,
-                             int *state, int batch, int hidden, hipStream_t st);
+                             int *state, int batch, int hidden, const GenControl &gc,
+                             hipStream_t st);
 // KV-cache compaction: rows[i] -> row i (strictly increasing sources), slots [0, len),
 // all layers and heads, in place.  Sources are passed by value in chunks.
 constexpr int kKvCompactChunk = 256;
