@@ -26,5 +26,6 @@ from .bloom_oracle import (  # noqa: F401
     masked_softmax,
     new_cache,
     round_bf16,
+    sample_tokens,
     stop_rule,
 )

@@ -405,3 +405,82 @@ def greedy_generate(model: OracleModel, prompt: np.ndarray, valid_len, n_new: in
         if t + 1 < n_new:
             h = forward(model, nxt[:, None], P + t, pad, cache)[:, 0]
     return GenerateResult(toks, hid, top1, top2, rms, chosen, cache)
+
+
+# ---------------------------------------------------------------------------
+# per-row sampling (temperature, nucleus / top-p)
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class SampleResult:
+    tokens: np.ndarray        # [B] chosen token ids
+    keep_margin: np.ndarray   # [B] distance of top_p from the nucleus' cumulative-mass bounds
+    draw_margin: np.ndarray   # [B] distance of u from the chosen token's CDF interval bounds
+    nucleus_size: np.ndarray  # [B] tokens in the nucleus
+
+
+def sample_tokens(logits: np.ndarray, temperature, top_p, uniform) -> SampleResult:
+    """One sampled token per row ("Hugging Face BLOOM Inference Optimization", Webserver
+    Architecture and Request Handling: the custom generation loop applies its own
+    sampling parameters, e.g. top-p, to each member of a batch).  The pages define
+    neither step, so the textbook definitions are used (float64):
+
+    * temperature T <= 0: greedy, the lowest id among the largest logits (decided on
+      float32-rounded logits, as ``greedy_argmax``);
+    * otherwise q = softmax(logits / T);
+    * nucleus (Holtzman et al., "The Curious Case of Neural Text Degeneration", ICLR
+      2020, Section 3.1): sort q in decreasing order and take the shortest prefix whose
+      mass reaches top_p; every token whose q equals the last one taken is kept too
+      (ties are not broken by id).  top_p >= 1 keeps every token; top_p <= 0 keeps the
+      tokens of the largest q only;
+    * the draw: the kept tokens in increasing id order, with cumulative mass F (over the
+      kept mass M), give the first id whose F exceeds u * M; u in [0, 1) is an input.
+
+    The margins say how far the decisions are from their rounding-sensitive edges, in
+    units of the (normalised) mass: keep_margin = distance of top_p from the cumulative
+    mass just before and just after the last kept group of equal q; draw_margin =
+    distance of u * M / M from the ends of the chosen token's interval.
+    """
+    logits = np.asarray(logits, dtype=F64)
+    B, V = logits.shape
+    T = np.asarray(temperature, dtype=F64).reshape(B)
+    P = np.asarray(top_p, dtype=F64).reshape(B)
+    U = np.asarray(uniform, dtype=F64).reshape(B)
+    toks = np.zeros(B, dtype=np.int32)
+    keep_m = np.full(B, np.inf)
+    draw_m = np.full(B, np.inf)
+    size = np.zeros(B, dtype=np.int64)
+    for b in range(B):
+        if not T[b] > 0:
+            toks[b] = int(np.argmax(logits[b].astype(np.float32)))
+            size[b] = 1
+            continue
+        z = logits[b] / T[b]
+        q = np.exp(z - z.max())
+        q = q / q.sum()
+        if P[b] >= 1:
+            keep = q > 0
+        else:
+            order = np.argsort(-q, kind="stable")
+            qs = q[order]
+            cum = np.cumsum(qs)
+            # shortest prefix whose mass reaches top_p (at least one token)
+            k = int(np.searchsorted(cum, P[b], side="left")) if P[b] > 0 else 0
+            k = min(k, V - 1)
+            last = qs[k]
+            keep = q >= last
+            # mass before the group of values equal to `last`, and with it
+            before = float(q[q > last].sum())
+            upto = float(q[keep].sum())
+            keep_m[b] = min(P[b] - before, upto - P[b]) if P[b] > 0 else upto
+        idx = np.nonzero(keep)[0]
+        mass = q[idx]
+        M = mass.sum()
+        F = np.cumsum(mass) / M
+        j = int(np.searchsorted(F, U[b], side="right"))
+        j = min(j, len(idx) - 1)
+        toks[b] = int(idx[j])
+        lo = F[j - 1] if j > 0 else 0.0
+        draw_m[b] = min(U[b] - lo, F[j] - U[b])
+        size[b] = len(idx)
+    return SampleResult(toks, keep_m, draw_m, size)
