@@ -39,8 +39,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=3, help="timed generations")
     ap.add_argument("--warmup", type=int, default=1, help="untimed generations")
     ap.add_argument("--workload", default="bloom-176b-tp8-rank0",
-                    help="a decode workload, or 'softmax' for the standalone fused ALiBi + "
-                         "masked softmax (its own JSON line)")
+                    help="a decode workload, 'softmax' for the standalone fused ALiBi + "
+                         "masked softmax, or 'sample' for per-row top-p sampling (each its "
+                         "own JSON line)")
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--new-tokens", type=int, default=None)
     ap.add_argument("--layers", type=int, default=None, help="truncate the stack (development)")
@@ -254,6 +255,55 @@ def softmax_bench(args):
     print(json.dumps(out), flush=True)
 
 
+def sample_bench(args):
+    """bloom_sample_tokens on float32 logits [batch, 250880] (per-row temperature and
+    top-p, one uniform number per row; seeded synthetic logits): kernel time per call,
+    and the oracle's time on the same rows.  The kernel reads each row 11 times (max,
+    mass, 8 radix passes, the draw) from cache; the algorithmic traffic is one read of
+    the logits."""
+    import numpy as np
+    import torch
+
+    import bloom_inputs as bi
+    import transformer_bloom_decode_amd as tb
+
+    B, V = args.batch, 250880
+    logits, T, P, u = bi.sampling_inputs(B, V)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    lg, Td, Pd, ud = d(logits), d(T), d(P), d(u)
+    out = torch.empty(B, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        tb.bloom_sample_tokens(lg, B, V, Td, Pd, ud, out, stream)
+    torch.cuda.synchronize()
+    reps = 50
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        tb.bloom_sample_tokens(lg, B, V, Td, Pd, ud, out, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    nbytes = B * V * 4 + B * 16
+    res = {
+        "metric": "per-row temperature + top-p sampling kernel time",
+        "value": round(us, 2), "unit": "us", "higher_is_better": False, "n_gpus": 1,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "bloom_sample_tokens", "batch": B, "vocab": V,
+                   "logit_std": "3-6 by row", "temperature": "0.5-1.3", "top_p": "0.3-1.0"},
+        "algorithmic_bytes": nbytes,
+        "gb_per_s": round(nbytes / (us * 1e-6) / 1e9, 1),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        t0 = time.perf_counter()
+        oracle.sample_tokens(logits, T, P, u)
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(dt * 1e6, 1), "unit": "us", "cores": 1,
+                               "kind": "oracle", "sample": f"the same {B} rows, float64 numpy"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -264,6 +314,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.workload == "sample":
+        sample_bench(args)
         return
     if args.workload == "softmax":
         softmax_bench(args)

@@ -348,3 +348,24 @@ def softmax_inputs(w: SoftmaxWorkload = SOFTMAX, std: Optional[float] = None,
     scores = normal(seed_scores, 0, (w.batch, w.heads, w.q_len, w.kv_len), std, kind="bf16")
     lengths = ids(seed_lengths, 0, (w.batch,), w.min_valid, w.kv_len - w.min_valid + 1)
     return scores, lengths
+
+
+SEED_SAMPLING = 4
+
+
+def sampling_inputs(batch: int, vocab: int, sigmas=(3.0, 4.0, 5.0, 6.0),
+                    temperatures=(0.5, 0.8, 1.0, 1.3), top_ps=(0.3, 0.8, 0.9, 0.95, 1.0),
+                    seed: int = SEED_SAMPLING) -> tuple:
+    """Per-row sampling inputs: float32 logits [batch, vocab], row b ~ N(0, sigma_b^2)
+    with sigma_b cycling through `sigmas` (peaked enough that the nucleus boundary and
+    the draw sit well clear of float32 rounding for most rows), temperatures and top-p
+    values cycling through the given lists (offset so the combinations mix), and one
+    uniform number in [0, 1) per row."""
+    logits = np.empty((batch, vocab), dtype=np.float32)
+    for b in range(batch):
+        normal(seed, 16 + b, (vocab,), sigmas[b % len(sigmas)], kind="f32", out=logits[b])
+    T = np.array([temperatures[(b // len(sigmas)) % len(temperatures)] for b in range(batch)],
+                 dtype=np.float32)
+    P = np.array([top_ps[(b * 3 + 1) % len(top_ps)] for b in range(batch)], dtype=np.float32)
+    u = (ids(seed, 15, (batch,), 0, 1 << 24).astype(np.float64) / float(1 << 24)).astype(np.float32)
+    return logits, T, P, u

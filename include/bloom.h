@@ -146,7 +146,9 @@ int bloom_workspace_bytes(const bloom_config *cfg, int32_t max_batch, int32_t ma
  * sets kv->prompt_len = kv->len = prompt_len, and writes the greedy next token of
  * each row to d_next_tokens [batch] (lowest id among equal float32 logits).
  * d_hidden_out (nullable) [batch][hidden] float32 receives the final-LayerNorm state
- * of each row's last position.  ECAPACITY if batch > kv->max_batch or
+ * of each row's last position.  d_next_tokens may be NULL when d_hidden_out is not:
+ * the LM head and its argmax are then skipped (a caller that samples its tokens with
+ * bloom_lm_logits + bloom_sample_tokens).  ECAPACITY if batch > kv->max_batch or
  * prompt_len > kv->max_len. */
 int bloom_prefill(const bloom_config *cfg, const bloom_weights *w, bloom_kv_cache *kv,
                   int32_t batch, int32_t prompt_len, const int32_t *d_tokens,
@@ -159,6 +161,7 @@ int bloom_prefill(const bloom_config *cfg, const bloom_weights *w, bloom_kv_cach
  * KV slot kv->len of every layer, attends over slots [prompt_len - valid_len[b],
  * kv->len], writes the greedy next token to d_next_tokens and optionally the
  * final-LayerNorm state to d_hidden_out [batch][hidden], then increments kv->len.
+ * As in bloom_prefill, d_next_tokens may be NULL when d_hidden_out is not (no LM head).
  * ECAPACITY if kv->len >= kv->max_len or batch > kv->max_batch; EINVAL if
  * bloom_prefill has not run (kv->prompt_len <= 0). */
 int bloom_decode_step(const bloom_config *cfg, const bloom_weights *w, bloom_kv_cache *kv,
@@ -197,6 +200,38 @@ int bloom_generate(const bloom_config *cfg, const bloom_weights *w, bloom_kv_cac
                    int32_t batch, int32_t prompt_len, const int32_t *d_tokens,
                    const int32_t *d_valid_len, int32_t n_new, int32_t *d_ids, float *d_hidden,
                    const bloom_gen_control *ctl, void *d_ws, size_t ws_bytes, void *stream);
+
+/* Logits of the tied LM head for caller-held final-LayerNorm states ("Hugging Face
+ * BLOOM Inference Optimization", Webserver Architecture and Request Handling: the custom
+ * generation loop needs the distribution, not only its argmax, to sample).
+ * d_hidden [batch][hidden] float32 (as bloom_prefill / bloom_decode_step write to
+ * d_hidden_out) -> d_logits [batch][vocab] float32, d_logits[b][v] = hidden_b . E_v with
+ * hidden rounded to bf16 for BF16 / INT8 models (the same operands and kernel plan as
+ * the greedy LM head, so the argmax of these logits is the token bloom_decode_step
+ * returns).  Buffers are caller-owned device memory; the workspace is
+ * bloom_workspace_bytes(cfg, batch, 1).  Only w->embed is read.  Asynchronous. */
+int bloom_lm_logits(const bloom_config *cfg, const bloom_weights *w, int32_t batch,
+                    const float *d_hidden, float *d_logits, void *d_ws, size_t ws_bytes,
+                    void *stream);
+
+/* Per-row sampling ("Hugging Face BLOOM Inference Optimization", Webserver Architecture
+ * and Request Handling: different sampling parameters, e.g. top-p, for each member of a
+ * batch; nucleus sampling as defined by Holtzman et al., "The Curious Case of Neural
+ * Text Degeneration", Section 3.1).  For row b of d_logits [batch][vocab] float32 (no
+ * NaN), with T = d_temperature[b], p = d_top_p[b], u = d_uniform[b] (device float32
+ * [batch] each; u is clamped to [0, 1)):
+ *   T <= 0: the greedy token (lowest id among the largest logits);
+ *   else q = softmax(logits / T); the nucleus is the shortest run of tokens in
+ *   decreasing q whose mass reaches p, plus every token tied with its last one (p >= 1:
+ *   all tokens; p <= 0: the largest logits only); the token is the first id, in
+ *   increasing id order over the nucleus, whose cumulative mass exceeds u times the
+ *   nucleus mass.
+ * Writes d_tokens [batch] int32.  All arithmetic is float32 in a fixed order (the same
+ * inputs give the same tokens).  The random numbers are the caller's.  EINVAL for
+ * batch < 0, vocab < 1 or a NULL pointer.  Asynchronous on `stream`. */
+int bloom_sample_tokens(const float *d_logits, int32_t batch, int32_t vocab,
+                        const float *d_temperature, const float *d_top_p,
+                        const float *d_uniform, int32_t *d_tokens, void *stream);
 
 /* Standalone fused ALiBi bias + masked fill + float32 softmax ([P4] Custom CUDA Kernels
  * and Hardware Acceleration; Efficient PyTorch Implementation for ALiBi).

@@ -214,3 +214,37 @@ def test_timer_read_without_launches():
     for cls in (-1, 1, 2, 3):
         ms, n, b = tb.bloom_timer_read(cls)
         assert (ms, n, b) == (0.0, 0, 0.0)
+
+
+def test_prefill_and_decode_need_tokens_or_hidden_out():
+    f = _Fake(bi.BLOOM_560M)
+    call = lambda nxt, hid: tb.lib.bloom_prefill(
+        ctypes.byref(f.cfg), ctypes.byref(f.w), ctypes.byref(f.kv), 2, 8, 0x1000, 0x1000, nxt,
+        hid, 0x1000, 1024, None)
+    # neither output: EINVAL; either one passes that check (and then fails the workspace)
+    assert call(None, None) == tb.BLOOM_EINVAL
+    assert call(None, 0x1000) == tb.BLOOM_EWORKSPACE
+    assert call(0x1000, None) == tb.BLOOM_EWORKSPACE
+    f.kv.prompt_len = f.kv.len = 8
+    dec = lambda nxt, hid: tb.lib.bloom_decode_step(
+        ctypes.byref(f.cfg), ctypes.byref(f.w), ctypes.byref(f.kv), 2, 0x1000, 0x1000, nxt, hid,
+        0x1000, 1024, None)
+    assert dec(None, None) == tb.BLOOM_EINVAL
+    assert dec(None, 0x1000) == tb.BLOOM_EWORKSPACE
+
+
+def test_sampling_and_lm_logits_validation_paths():
+    smp = tb.lib.bloom_sample_tokens
+    assert smp(0x10, -1, 8, 0x10, 0x10, 0x10, 0x10, None) == tb.BLOOM_EINVAL
+    assert smp(0x10, 2, 0, 0x10, 0x10, 0x10, 0x10, None) == tb.BLOOM_EINVAL
+    assert smp(0x10, 2, 8, None, 0x10, 0x10, 0x10, None) == tb.BLOOM_EINVAL
+    assert smp(0x10, 2, 8, 0x10, 0x10, 0x10, None, None) == tb.BLOOM_EINVAL
+    assert smp(None, 0, 8, None, None, None, None, None) == tb.BLOOM_OK        # empty batch
+    f = _Fake(bi.BLOOM_560M)
+    lg = lambda w, b, h, out, wsb: tb.lib.bloom_lm_logits(ctypes.byref(f.cfg), w, b, h, out,
+                                                          0x1000, wsb, None)
+    assert lg(None, 2, 0x10, 0x10, 1 << 40) == tb.BLOOM_EINVAL                  # no weights
+    assert lg(ctypes.byref(f.w), -1, 0x10, 0x10, 1 << 40) == tb.BLOOM_EINVAL
+    assert lg(ctypes.byref(f.w), 2, None, 0x10, 1 << 40) == tb.BLOOM_EINVAL
+    assert lg(ctypes.byref(f.w), 2, 0x10, 0x10, 16) == tb.BLOOM_EWORKSPACE
+    assert lg(ctypes.byref(f.w), 0, None, None, 0) == tb.BLOOM_OK

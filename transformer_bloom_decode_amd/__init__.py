@@ -99,12 +99,16 @@ def _load():
     lib.kv_cache_append.argtypes = [P(bloom_config), P(bloom_kv_cache), _i32, _i32, _i32, vp, vp,
                                     _i32, vp]
     lib.kv_cache_compact.argtypes = [P(bloom_config), P(bloom_kv_cache), _i32, P(_i32), _i32, vp]
+    lib.bloom_lm_logits.argtypes = [P(bloom_config), P(bloom_weights), _i32, vp, vp, vp,
+                                    ctypes.c_size_t, vp]
+    lib.bloom_sample_tokens.argtypes = [vp, _i32, _i32, vp, vp, vp, vp, vp]
     lib.bloom_timer_enable.argtypes = [_i32]
     lib.bloom_timer_disable.argtypes = []
     lib.bloom_timer_read.argtypes = [_i32, P(ctypes.c_double), P(_i32), P(ctypes.c_double)]
     lib.bloom_timer_pause.argtypes = [_i32]
     for name in ("bloom_workspace_bytes", "bloom_prefill", "bloom_decode_step", "bloom_generate",
                  "alibi_masked_softmax", "kv_cache_append", "kv_cache_compact",
+                 "bloom_lm_logits", "bloom_sample_tokens",
                  "bloom_timer_enable",
                  "bloom_timer_disable", "bloom_timer_read", "bloom_timer_pause"):
         getattr(lib, name).restype = ctypes.c_int
@@ -208,6 +212,20 @@ def kv_cache_compact(cfg, kv, batch: int, keep, stream=None):
     arr = (_i32 * max(1, len(keep)))(*[int(k) for k in keep])
     _check(lib.kv_cache_compact(ctypes.byref(cfg), ctypes.byref(s), batch, arr, len(keep),
                                 _stream(stream)), "kv_cache_compact")
+
+
+def bloom_lm_logits(cfg, weights, batch: int, hidden, logits, ws, stream=None):
+    w = weights.struct if hasattr(weights, "struct") else weights
+    _check(lib.bloom_lm_logits(ctypes.byref(cfg), ctypes.byref(w), batch, _ptr(hidden),
+                               _ptr(logits), _ptr(ws), _nbytes(ws), _stream(stream)),
+           "bloom_lm_logits")
+
+
+def bloom_sample_tokens(logits, batch: int, vocab: int, temperature, top_p, uniform, tokens,
+                        stream=None):
+    _check(lib.bloom_sample_tokens(_ptr(logits), batch, vocab, _ptr(temperature), _ptr(top_p),
+                                   _ptr(uniform), _ptr(tokens), _stream(stream)),
+           "bloom_sample_tokens")
 
 
 def bloom_timer_enable(max_launches: int):

@@ -318,14 +318,15 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
     }
   }
 
-  // final LayerNorm of each row's last position, then the tied LM head + argmax
+  // final LayerNorm of each row's last position, then the tied LM head + argmax (the
+  // LM head is skipped when the caller asked for the hidden states only)
   const int nblk = wp.lm_blocks;
   const int wdt_lm = f32 ? WT_F32 : WT_BF16;  // the embedding is never int8
   const double lm_bytes = (double)c->vocab * h * pb;
   err = launch_layernorm(f32, x, tpr, tpr - 1, w->lnf_g, w->lnf_b, af, d_hidden, batch, h,
                          c->ln_eps, st);
   if (err != hipSuccess) return hip_fail(err);
-  for (int r0 = 0; r0 < batch; r0 += 128) {
+  for (int r0 = 0; d_next && r0 < batch; r0 += 128) {
     const int rows = std::min(128, batch - r0);
     EpiParams a{};
     a.mode = EPI_ARGMAX;
@@ -382,7 +383,7 @@ int bloom_prefill(const bloom_config *cfg, const bloom_weights *w, bloom_kv_cach
   if (batch < 0 || prompt_len < 1) return BLOOM_EINVAL;
   if (batch > kv->max_batch || prompt_len > kv->max_len) return BLOOM_ECAPACITY;
   if (batch == 0) return BLOOM_OK;
-  if (!d_tokens || !d_valid_len || !d_next_tokens || !d_ws) return BLOOM_EINVAL;
+  if (!d_tokens || !d_valid_len || !d_ws || (!d_next_tokens && !d_hidden_out)) return BLOOM_EINVAL;
   if (ws_bytes < plan_ws(cfg, batch, prompt_len).total) return BLOOM_EWORKSPACE;
   clear_stale_hip_error();
   s = run_forward(cfg, w, kv, batch, prompt_len, 0, prompt_len, d_tokens, d_valid_len,
@@ -406,7 +407,7 @@ int bloom_decode_step(const bloom_config *cfg, const bloom_weights *w, bloom_kv_
   if (kv->prompt_len <= 0 || kv->len < kv->prompt_len) return BLOOM_EINVAL;
   if (batch > kv->max_batch || kv->len >= kv->max_len) return BLOOM_ECAPACITY;
   if (batch == 0) return BLOOM_OK;
-  if (!d_tokens || !d_valid_len || !d_next_tokens || !d_ws) return BLOOM_EINVAL;
+  if (!d_tokens || !d_valid_len || !d_ws || (!d_next_tokens && !d_hidden_out)) return BLOOM_EINVAL;
   if (ws_bytes < plan_ws(cfg, batch, 1).total) return BLOOM_EWORKSPACE;
   clear_stale_hip_error();
   s = run_forward(cfg, w, kv, batch, 1, kv->len, kv->prompt_len, d_tokens, d_valid_len,
@@ -562,6 +563,58 @@ int kv_cache_compact(const bloom_config *cfg, bloom_kv_cache *kv, int32_t batch,
                                            kv->max_batch, kv->max_len, cfg->head_dim,
                                            act_bytes(cfg), kv->len, keep, n_keep,
                                            (hipStream_t)stream);
+  return err == hipSuccess ? BLOOM_OK : hip_fail(err);
+}
+
+int bloom_lm_logits(const bloom_config *cfg, const bloom_weights *w, int32_t batch,
+                    const float *d_hidden, float *d_logits, void *d_ws, size_t ws_bytes,
+                    void *stream) {
+  int s = check_config(cfg);
+  if (s != BLOOM_OK) return s;
+  if (!w || !w->embed || batch < 0) return BLOOM_EINVAL;
+  if (batch == 0) return BLOOM_OK;
+  if (!d_hidden || !d_logits || !d_ws) return BLOOM_EINVAL;
+  const WsPlan wp = plan_ws(cfg, batch, 1);
+  if (ws_bytes < wp.total) return BLOOM_EWORKSPACE;
+  clear_stale_hip_error();
+  hipStream_t st = (hipStream_t)stream;
+  const bool f32 = cfg->weight_dtype == BLOOM_F32;
+  const int h = cfg->hidden;
+  const void *X = d_hidden;
+  if (!f32) {
+    // the same bf16 rounding of the final-LayerNorm state as the greedy LM head's input
+    void *af = (char *)d_ws + wp.af;
+    const hipError_t e = launch_f32_to_bf16(d_hidden, af, (size_t)batch * h, st);
+    if (e != hipSuccess) return hip_fail(e);
+    X = af;
+  }
+  const int wdt_lm = f32 ? WT_F32 : WT_BF16;
+  const size_t act = act_bytes(cfg);
+  float *part = (float *)((char *)d_ws + wp.part);
+  for (int r0 = 0; r0 < batch; r0 += 128) {
+    const int rows = std::min(128, batch - r0);
+    EpiParams e{};
+    e.mode = EPI_STORE;
+    e.out = d_logits + (size_t)r0 * cfg->vocab;
+    e.ld = cfg->vocab;
+    // the greedy LM head's plan (never split), so the logits are the ones it ranks
+    const LinearPlan p = plan_linear(wdt_lm, rows, cfg->vocab, h, true);
+    const hipError_t err =
+        launch_linear(wdt_lm, p, (const char *)X + (size_t)r0 * h * act, w->embed, part, e, st);
+    if (err != hipSuccess) return hip_fail(err);
+  }
+  return BLOOM_OK;
+}
+
+int bloom_sample_tokens(const float *d_logits, int32_t batch, int32_t vocab,
+                        const float *d_temperature, const float *d_top_p,
+                        const float *d_uniform, int32_t *d_tokens, void *stream) {
+  if (batch < 0 || vocab < 1) return BLOOM_EINVAL;
+  if (batch == 0) return BLOOM_OK;
+  if (!d_logits || !d_temperature || !d_top_p || !d_uniform || !d_tokens) return BLOOM_EINVAL;
+  clear_stale_hip_error();
+  const hipError_t err = launch_sample_rows(d_logits, batch, vocab, d_temperature, d_top_p,
+                                            d_uniform, d_tokens, (hipStream_t)stream);
   return err == hipSuccess ? BLOOM_OK : hip_fail(err);
 }
 

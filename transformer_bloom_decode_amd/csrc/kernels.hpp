@@ -122,6 +122,13 @@ constexpr int kKvCompactChunk = 256;
 hipError_t launch_kv_compact(void *kc, void *vc, int n_layer, int H, int max_batch, int max_len,
                              int d, size_t act, int len, const int *rows, int n_keep,
                              hipStream_t st);
+// Per-row temperature + nucleus (top-p) sampling of float32 logits [batch][V] with one
+// uniform number per row (sample.hip); temperature <= 0 is greedy.
+hipError_t launch_sample_rows(const float *logits, int batch, int V, const float *temperature,
+                              const float *top_p, const float *uniform, int *out,
+                              hipStream_t st);
+// y[i] = bf16(x[i]), round to nearest even.
+hipError_t launch_f32_to_bf16(const float *x, void *y, size_t n, hipStream_t st);
 hipError_t launch_kv_append(bool f32, const void *k, const void *v, void *ck, void *cv,
                             int batch, int H, int n_new, int d, int max_len, int pos,
                             hipStream_t st);
