@@ -250,13 +250,16 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
   auto fuse_ln = [&](const LinearPlan &p) {
     return !f32 && p.splits > 1 && splitk_resid_ln_supported(h, p.splits);
   };
+  // One activation row and a short hidden size: LN1 and LN2 run as the prologue of the
+  // QKV and MLP-up GEMVs instead of as launches of their own.
+  const bool ln_in_gemv = !f32 && gemv_ln_supported(wdt, M, h);
   bool ln1_done = false;   // xa already holds LN1(x) of this layer
   for (int l = 0; l < c->n_layer; ++l) {
     const bloom_layer_weights &L = w->layers[l];
     void *kc = (char *)kv->k + l * layer_stride;
     void *vc = (char *)kv->v + l * layer_stride;
 
-    if (!ln1_done) {
+    if (!ln1_done && !ln_in_gemv) {
       err = launch_layernorm(f32, x, 1, 0, L.ln1_g, L.ln1_b, xa, nullptr, M, h, c->ln_eps, st);
       if (err != hipSuccess) return hip_fail(err);
     }
@@ -270,7 +273,12 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
     e.H = H; e.d = d; e.max_len = kv->max_len;
     e.pos_base = pos_base; e.pos_dev = d_pos; e.rows_per_seq = tpr;
     e.q_scale = 1.0f / sqrtf((float)d);
-    err = timed_linear(wdt, p_qkv, xa, L.w_qkv, part, e, st, wbytes(3 * hd, h));
+    if (ln_in_gemv)
+      err = timed(kernel_class(p_qkv), wbytes(3 * hd, h), st, [&] {
+        return launch_gemv_ln(wdt, 3 * hd, h, x, L.ln1_g, L.ln1_b, c->ln_eps, L.w_qkv, e, st);
+      });
+    else
+      err = timed_linear(wdt, p_qkv, xa, L.w_qkv, part, e, st, wbytes(3 * hd, h));
     if (err != hipSuccess) return hip_fail(err);
 
     err = launch_attention(f32, q, kc, vc, d_valid, o, M, H, d, kv->max_len, c->n_head_total,
@@ -289,7 +297,7 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
     if (fuse_dense)
       err = launch_splitk_resid_ln(part, p_dense.splits, M, L.s_dense, L.b_dense, x, L.ln2_g,
                                    L.ln2_b, xa, h, c->ln_eps, st);
-    else
+    else if (!ln_in_gemv)
       err = launch_layernorm(f32, x, 1, 0, L.ln2_g, L.ln2_b, xa, nullptr, M, h, c->ln_eps, st);
     if (err != hipSuccess) return hip_fail(err);
 
@@ -298,7 +306,12 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
     g.bias = L.b_up;
     g.scale = (const uint16_t *)L.s_up;
     g.out = u; g.ld = F;
-    err = timed_linear(wdt, p_up, xa, L.w_up, part, g, st, wbytes(F, h));
+    if (ln_in_gemv && !fuse_dense)
+      err = timed(kernel_class(p_up), wbytes(F, h), st, [&] {
+        return launch_gemv_ln(wdt, F, h, x, L.ln2_g, L.ln2_b, c->ln_eps, L.w_up, g, st);
+      });
+    else
+      err = timed_linear(wdt, p_up, xa, L.w_up, part, g, st, wbytes(F, h));
     if (err != hipSuccess) return hip_fail(err);
 
     EpiParams dn{};
@@ -306,7 +319,7 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
     dn.bias = L.b_down;
     dn.scale = (const uint16_t *)L.s_down;
     dn.out = x; dn.ld = h;
-    const bool fuse_down = l + 1 < c->n_layer && fuse_ln(p_down);
+    const bool fuse_down = l + 1 < c->n_layer && fuse_ln(p_down) && !ln_in_gemv;
     err = timed_linear(wdt, p_down, u, L.w_down, part, dn, st, wbytes(h, F), !fuse_down);
     if (err != hipSuccess) return hip_fail(err);
     if (fuse_down) {

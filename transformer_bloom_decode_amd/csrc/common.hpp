@@ -114,6 +114,30 @@ __device__ __forceinline__ float gelu_tanh(float y) {
   return 0.5f * y * (1.0f + tanhf(k0 * (y + k1 * y * y * y)));
 }
 
+// Four parameters (gamma or beta) as loaded, unpacked only when used, so that their
+// loads can be issued together with the row's and retire while the statistics run.
+template <typename TP> struct Param4;
+template <> struct Param4<float> {
+  float4 v;
+  __device__ __forceinline__ void load(const float *p) { v = *(const float4 *)p; }
+  __device__ __forceinline__ float4 get() const { return v; }
+};
+template <> struct Param4<bf16_t> {
+  uint2 v;
+  __device__ __forceinline__ void load(const bf16_t *p) { v = *(const uint2 *)p; }
+  __device__ __forceinline__ float4 get() const {
+    return make_float4(lo_bf(v.x), hi_bf(v.x), lo_bf(v.y), hi_bf(v.y));
+  }
+};
+
+template <typename TP>
+__device__ __forceinline__ float4 ln_apply(float4 x, float mean, float rstd, const Param4<TP> &g,
+                                           const Param4<TP> &b) {
+  const float4 gg = g.get(), bb = b.get();
+  return make_float4((x.x - mean) * rstd * gg.x + bb.x, (x.y - mean) * rstd * gg.y + bb.y,
+                     (x.z - mean) * rstd * gg.z + bb.z, (x.w - mean) * rstd * gg.w + bb.w);
+}
+
 // ---------------------------------------------------------------------------
 // linear-layer epilogues
 // ---------------------------------------------------------------------------

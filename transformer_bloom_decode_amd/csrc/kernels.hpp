@@ -64,6 +64,12 @@ struct LinearPlan {
 LinearPlan plan_valu(int wdtype, int M, int N, int K);
 hipError_t launch_valu(int wdtype, const LinearPlan &p, const void *X, const void *W,
                        const EpiParams &ep, hipStream_t st);
+// One-row GEMV whose prologue is the LayerNorm of the float32 row x (gamma g, beta b,
+// bf16): out = epilogue(LN(x) . W^T); bf16 or int8 weights, K a multiple of 16 up to
+// 4096 (gemv_ln_supported).
+bool gemv_ln_supported(int wdtype, int M, int K);
+hipError_t launch_gemv_ln(int wdtype, int N, int K, const float *x, const void *g, const void *b,
+                          float eps, const void *W, const EpiParams &ep, hipStream_t st);
 LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax);
 // (max, index) partials per activation row an argmax-mode launch of the plan writes.
 int argmax_partials_per_row(const LinearPlan &p);
