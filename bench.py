@@ -257,10 +257,10 @@ def softmax_bench(args):
 
 def sample_bench(args):
     """bloom_sample_tokens on float32 logits [batch, 250880] (per-row temperature and
-    top-p, one uniform number per row; seeded synthetic logits): kernel time per call,
-    and the oracle's time on the same rows.  The kernel reads each row 11 times (max,
-    mass, 8 radix passes, the draw) from cache; the algorithmic traffic is one read of
-    the logits."""
+    top-p, one uniform number per row; seeded synthetic logits): time per call (its
+    seven launches), and the oracle's time on the same rows.  The kernels read each row
+    up to six times (max, mass, three radix levels, segment masses) from cache; the
+    algorithmic traffic is one read of the logits."""
     import numpy as np
     import torch
 
@@ -272,15 +272,16 @@ def sample_bench(args):
     d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     lg, Td, Pd, ud = d(logits), d(T), d(P), d(u)
     out = torch.empty(B, dtype=torch.int32, device="cuda")
+    ws = torch.empty(tb.bloom_sample_workspace_bytes(B, V), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
     for _ in range(3):
-        tb.bloom_sample_tokens(lg, B, V, Td, Pd, ud, out, stream)
+        tb.bloom_sample_tokens(lg, B, V, Td, Pd, ud, out, ws, stream)
     torch.cuda.synchronize()
     reps = 50
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(reps):
-        tb.bloom_sample_tokens(lg, B, V, Td, Pd, ud, out, stream)
+        tb.bloom_sample_tokens(lg, B, V, Td, Pd, ud, out, ws, stream)
     e1.record(stream)
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / reps

@@ -226,12 +226,19 @@ int bloom_lm_logits(const bloom_config *cfg, const bloom_weights *w, int32_t bat
  *   all tokens; p <= 0: the largest logits only); the token is the first id, in
  *   increasing id order over the nucleus, whose cumulative mass exceeds u times the
  *   nucleus mass.
- * Writes d_tokens [batch] int32.  All arithmetic is float32 in a fixed order (the same
- * inputs give the same tokens).  The random numbers are the caller's.  EINVAL for
- * batch < 0, vocab < 1 or a NULL pointer.  Asynchronous on `stream`. */
+ * Writes d_tokens [batch] int32.  Probabilities are float32, masses exact sums of
+ * 2^-40 fixed-point units (the same inputs give the same tokens).  The random numbers
+ * are the caller's.  d_ws: device workspace of bloom_sample_workspace_bytes(batch,
+ * vocab) bytes (partial results between the kernels; its contents need no
+ * initialisation).  EINVAL for batch < 0, vocab outside [1, 2^23] or a NULL pointer;
+ * EWORKSPACE if ws_bytes is too small.  Asynchronous on `stream`. */
 int bloom_sample_tokens(const float *d_logits, int32_t batch, int32_t vocab,
                         const float *d_temperature, const float *d_top_p,
-                        const float *d_uniform, int32_t *d_tokens, void *stream);
+                        const float *d_uniform, int32_t *d_tokens, void *d_ws,
+                        size_t ws_bytes, void *stream);
+
+/* Workspace bytes bloom_sample_tokens needs for `batch` rows of `vocab` logits. */
+int bloom_sample_workspace_bytes(int32_t batch, int32_t vocab, size_t *bytes);
 
 /* Standalone fused ALiBi bias + masked fill + float32 softmax ([P4] Custom CUDA Kernels
  * and Hardware Acceleration; Efficient PyTorch Implementation for ALiBi).

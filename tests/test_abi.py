@@ -234,12 +234,18 @@ def test_prefill_and_decode_need_tokens_or_hidden_out():
 
 
 def test_sampling_and_lm_logits_validation_paths():
-    smp = tb.lib.bloom_sample_tokens
-    assert smp(0x10, -1, 8, 0x10, 0x10, 0x10, 0x10, None) == tb.BLOOM_EINVAL
-    assert smp(0x10, 2, 0, 0x10, 0x10, 0x10, 0x10, None) == tb.BLOOM_EINVAL
-    assert smp(0x10, 2, 8, None, 0x10, 0x10, 0x10, None) == tb.BLOOM_EINVAL
-    assert smp(0x10, 2, 8, 0x10, 0x10, 0x10, None, None) == tb.BLOOM_EINVAL
-    assert smp(None, 0, 8, None, None, None, None, None) == tb.BLOOM_OK        # empty batch
+    smp = lambda *a: tb.lib.bloom_sample_tokens(*a[:7], 0x10 if len(a) < 8 else a[7],
+                                                 1 << 30 if len(a) < 9 else a[8], None)
+    assert smp(0x10, -1, 8, 0x10, 0x10, 0x10, 0x10) == tb.BLOOM_EINVAL
+    assert smp(0x10, 2, 0, 0x10, 0x10, 0x10, 0x10) == tb.BLOOM_EINVAL
+    assert smp(0x10, 2, (1 << 23) + 1, 0x10, 0x10, 0x10, 0x10) == tb.BLOOM_EINVAL
+    assert smp(0x10, 2, 8, None, 0x10, 0x10, 0x10) == tb.BLOOM_EINVAL
+    assert smp(0x10, 2, 8, 0x10, 0x10, 0x10, None) == tb.BLOOM_EINVAL
+    assert smp(0x10, 2, 8, 0x10, 0x10, 0x10, 0x10, None) == tb.BLOOM_EINVAL   # no workspace
+    need = tb.bloom_sample_workspace_bytes(2, 250880)
+    assert need > 0 and tb.bloom_sample_workspace_bytes(128, 250880) > need
+    assert smp(0x10, 2, 250880, 0x10, 0x10, 0x10, 0x10, 0x10, need - 1) == tb.BLOOM_EWORKSPACE
+    assert smp(None, 0, 8, None, None, None, None) == tb.BLOOM_OK              # empty batch
     f = _Fake(bi.BLOOM_560M)
     lg = lambda w, b, h, out, wsb: tb.lib.bloom_lm_logits(ctypes.byref(f.cfg), w, b, h, out,
                                                           0x1000, wsb, None)

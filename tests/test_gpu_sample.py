@@ -160,3 +160,18 @@ def test_lm_logits_reproduce_the_greedy_token(wdt):
     tb.bloom_sample_tokens(logits, B, shape.vocab, z, z + 1, z, out)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(out.cpu().numpy(), nxt2.cpu().numpy())
+
+
+def test_workspace_contents_need_no_initialisation():
+    logits, T, P, u = bi.sampling_inputs(6, 250880, seed=13)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    n = tb.bloom_sample_workspace_bytes(6, 250880)
+    outs = []
+    for fill in (0, 255, 17):
+        ws = torch.full((n,), fill, dtype=torch.uint8, device="cuda")
+        out = torch.empty(6, dtype=torch.int32, device="cuda")
+        tb.bloom_sample_tokens(d(logits), 6, 250880, d(T), d(P), d(u), out, ws)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+    np.testing.assert_array_equal(outs[0], outs[1])
+    np.testing.assert_array_equal(outs[0], outs[2])

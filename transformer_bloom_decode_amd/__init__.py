@@ -101,14 +101,16 @@ def _load():
     lib.kv_cache_compact.argtypes = [P(bloom_config), P(bloom_kv_cache), _i32, P(_i32), _i32, vp]
     lib.bloom_lm_logits.argtypes = [P(bloom_config), P(bloom_weights), _i32, vp, vp, vp,
                                     ctypes.c_size_t, vp]
-    lib.bloom_sample_tokens.argtypes = [vp, _i32, _i32, vp, vp, vp, vp, vp]
+    lib.bloom_sample_tokens.argtypes = [vp, _i32, _i32, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                        vp]
+    lib.bloom_sample_workspace_bytes.argtypes = [_i32, _i32, P(ctypes.c_size_t)]
     lib.bloom_timer_enable.argtypes = [_i32]
     lib.bloom_timer_disable.argtypes = []
     lib.bloom_timer_read.argtypes = [_i32, P(ctypes.c_double), P(_i32), P(ctypes.c_double)]
     lib.bloom_timer_pause.argtypes = [_i32]
     for name in ("bloom_workspace_bytes", "bloom_prefill", "bloom_decode_step", "bloom_generate",
                  "alibi_masked_softmax", "kv_cache_append", "kv_cache_compact",
-                 "bloom_lm_logits", "bloom_sample_tokens",
+                 "bloom_lm_logits", "bloom_sample_tokens", "bloom_sample_workspace_bytes",
                  "bloom_timer_enable",
                  "bloom_timer_disable", "bloom_timer_read", "bloom_timer_pause"):
         getattr(lib, name).restype = ctypes.c_int
@@ -221,11 +223,24 @@ def bloom_lm_logits(cfg, weights, batch: int, hidden, logits, ws, stream=None):
            "bloom_lm_logits")
 
 
+def bloom_sample_workspace_bytes(batch: int, vocab: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib.bloom_sample_workspace_bytes(batch, vocab, ctypes.byref(out)),
+           "bloom_sample_workspace_bytes")
+    return out.value
+
+
 def bloom_sample_tokens(logits, batch: int, vocab: int, temperature, top_p, uniform, tokens,
-                        stream=None):
+                        ws=None, stream=None):
+    """bloom_sample_tokens; without `ws` a workspace of the required size is allocated
+    on the logits' device for this call."""
+    if ws is None and batch > 0:
+        import torch
+        ws = torch.empty(bloom_sample_workspace_bytes(batch, vocab), dtype=torch.uint8,
+                         device=logits.device)
     _check(lib.bloom_sample_tokens(_ptr(logits), batch, vocab, _ptr(temperature), _ptr(top_p),
-                                   _ptr(uniform), _ptr(tokens), _stream(stream)),
-           "bloom_sample_tokens")
+                                   _ptr(uniform), _ptr(tokens), _ptr(ws), _nbytes(ws),
+                                   _stream(stream)), "bloom_sample_tokens")
 
 
 def bloom_timer_enable(max_launches: int):

@@ -619,15 +619,24 @@ int bloom_lm_logits(const bloom_config *cfg, const bloom_weights *w, int32_t bat
   return BLOOM_OK;
 }
 
+int bloom_sample_workspace_bytes(int32_t batch, int32_t vocab, size_t *bytes) {
+  if (!bytes || batch < 0 || vocab < 1 || vocab > (1 << 23)) return BLOOM_EINVAL;
+  *bytes = sample_workspace_bytes(batch, vocab);
+  return BLOOM_OK;
+}
+
 int bloom_sample_tokens(const float *d_logits, int32_t batch, int32_t vocab,
                         const float *d_temperature, const float *d_top_p,
-                        const float *d_uniform, int32_t *d_tokens, void *stream) {
-  if (batch < 0 || vocab < 1) return BLOOM_EINVAL;
+                        const float *d_uniform, int32_t *d_tokens, void *d_ws, size_t ws_bytes,
+                        void *stream) {
+  if (batch < 0 || vocab < 1 || vocab > (1 << 23)) return BLOOM_EINVAL;
   if (batch == 0) return BLOOM_OK;
-  if (!d_logits || !d_temperature || !d_top_p || !d_uniform || !d_tokens) return BLOOM_EINVAL;
+  if (!d_logits || !d_temperature || !d_top_p || !d_uniform || !d_tokens || !d_ws)
+    return BLOOM_EINVAL;
+  if (ws_bytes < sample_workspace_bytes(batch, vocab)) return BLOOM_EWORKSPACE;
   clear_stale_hip_error();
   const hipError_t err = launch_sample_rows(d_logits, batch, vocab, d_temperature, d_top_p,
-                                            d_uniform, d_tokens, (hipStream_t)stream);
+                                            d_uniform, d_tokens, d_ws, (hipStream_t)stream);
   return err == hipSuccess ? BLOOM_OK : hip_fail(err);
 }
 

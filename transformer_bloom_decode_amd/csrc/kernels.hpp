@@ -129,9 +129,11 @@ hipError_t launch_kv_compact(void *kc, void *vc, int n_layer, int H, int max_bat
                              int d, size_t act, int len, const int *rows, int n_keep,
                              hipStream_t st);
 // Per-row temperature + nucleus (top-p) sampling of float32 logits [batch][V] with one
-// uniform number per row (sample.hip); temperature <= 0 is greedy.
+// uniform number per row (sample.hip); temperature <= 0 is greedy.  `ws` holds
+// sample_workspace_bytes(batch, V) bytes of partial results.
+size_t sample_workspace_bytes(int batch, int vocab);
 hipError_t launch_sample_rows(const float *logits, int batch, int V, const float *temperature,
-                              const float *top_p, const float *uniform, int *out,
+                              const float *top_p, const float *uniform, int *out, void *ws,
                               hipStream_t st);
 // y[i] = bf16(x[i]), round to nearest even.
 hipError_t launch_f32_to_bf16(const float *x, void *y, size_t n, hipStream_t st);
