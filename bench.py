@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--loop", choices=("eager", "graph"), default="eager",
                     help="decode loop: one bloom_decode_step call per token, or bloom_generate "
                          "(replays of a captured decode step)")
+    ap.add_argument("--sample", action="store_true",
+                    help="with --loop graph: per-row sampling (temperature 0.8, top-p 0.9, "
+                         "seeded uniform numbers) instead of greedy tokens")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--no-kernel-timer", action="store_true",
@@ -350,12 +353,26 @@ def main():
     log(f"setup {time.perf_counter() - t0:.1f}s: {m.name} L={m.n_layer} B={B} P={P} new={n_new}")
 
     graph = args.loop == "graph"
+    if args.sample and not graph:
+        log("--sample needs --loop graph")
+        sys.exit(2)
+    smp = {}
+    if args.sample:
+        import numpy as np
+        u = (bi.ids(bi.SEED_SAMPLING, 99, (n_new, B), 0, 1 << 24).astype(np.float64)
+             / (1 << 24)).astype(np.float32)
+        smp = dict(temperature=torch.full((B,), 0.8, device="cuda"),
+                   top_p=torch.full((B,), 0.9, device="cuda"),
+                   uniform=torch.from_numpy(u).cuda(),
+                   logits=torch.empty((B, m.vocab), dtype=torch.float32, device="cuda"),
+                   sample_ws=torch.empty(tb.bloom_sample_workspace_bytes(B, m.vocab),
+                                         dtype=torch.uint8, device="cuda"))
 
     def generation(ev_mid=None, timed=False):
         kv.struct.len = 0
         kv.struct.prompt_len = 0
         if graph and not timed:
-            tb.bloom_generate(cfg, dw, kv, B, P, tok, vl, n_new, ids, None, ws, stream)
+            tb.bloom_generate(cfg, dw, kv, B, P, tok, vl, n_new, ids, None, ws, stream, **smp)
             return
         if timed:
             tb.bloom_timer_pause(True)
@@ -450,8 +467,9 @@ def main():
         "config": {"workload": m.name, "batch": B, "prompt_len": P, "new_tokens": n_new,
                    "layers": m.n_layer, "hidden": m.hidden, "heads_local": m.n_head_local,
                    "heads_total": m.n_head_total, "ffn_local": m.ffn, "vocab": m.vocab,
-                   "weights": m.weight_dtype, "kv_cache": True, "greedy": True,
-                   "parallelism": "none (1 GPU)", "loop": args.loop},
+                   "weights": m.weight_dtype, "kv_cache": True, "greedy": not args.sample,
+                   "parallelism": "none (1 GPU)", "loop": args.loop,
+                   "tokens": "sampled (temperature 0.8, top-p 0.9)" if args.sample else "greedy"},
         "tokens_per_s": round(B * n_new / (ms_per_step * 1e-3), 2),
         "prefill_ms": round(float(np.median(prefill_ms)), 3),
         "prefill_tflops": round(prefill_flops(m, B, P) / (float(np.median(prefill_ms)) * 1e-3)

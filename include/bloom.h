@@ -177,12 +177,25 @@ int bloom_decode_step(const bloom_config *cfg, const bloom_weights *w, bloom_kv_
  * hidden states of those steps are those of pad tokens).  eos_id < 0: no end token;
  * d_max_new (device [batch] int32) nullable: no per-row limit; d_out_len (device
  * [batch] int32, nullable) receives each row's token count (n_new if it never
- * finished).  Finished rows can be taken out between calls with kv_cache_compact. */
+ * finished).  Finished rows can be taken out between calls with kv_cache_compact.
+ * Sampling (the same page: sampling parameters per member of the batch): with
+ * d_temperature, d_top_p (device float32 [batch]) and d_uniform (device float32
+ * [n_new][batch], the caller's random numbers in [0, 1)) set, every step's token is
+ * drawn as bloom_sample_tokens does, from the tied LM head's logits (written to the
+ * caller's d_logits [batch][vocab] float32 scratch) with d_uniform[step][b]; rows with
+ * temperature <= 0 stay greedy.  d_sample_ws is a device workspace of
+ * bloom_sample_workspace_bytes(batch, vocab) bytes.  All five NULL: greedy. */
 typedef struct {
   int32_t eos_id;
   int32_t pad_id;
   const int32_t *d_max_new;
   int32_t *d_out_len;
+  const float *d_temperature;
+  const float *d_top_p;
+  const float *d_uniform;
+  float *d_logits;
+  void *d_sample_ws;
+  size_t sample_ws_bytes;
 } bloom_gen_control;
 
 /* Greedy generation loop ([P1] Benchmark Environment: greedy generation of new tokens
@@ -195,7 +208,9 @@ typedef struct {
  * nullable: plain greedy) the per-row stop rule above.  kv->len ends at prompt_len +
  * n_new - 1.  Returns after the generation has finished (the graph is released).
  * ECAPACITY if prompt_len + n_new - 1 > kv->max_len or batch > kv->max_batch; EINVAL if
- * ctl->eos_id >= vocab; the workspace is bloom_workspace_bytes(cfg, batch, prompt_len). */
+ * ctl->eos_id >= vocab or the sampling fields are set in part; EWORKSPACE if the
+ * workspace is smaller than bloom_workspace_bytes(cfg, batch, prompt_len) or the
+ * sampling workspace than bloom_sample_workspace_bytes(batch, vocab). */
 int bloom_generate(const bloom_config *cfg, const bloom_weights *w, bloom_kv_cache *kv,
                    int32_t batch, int32_t prompt_len, const int32_t *d_tokens,
                    const int32_t *d_valid_len, int32_t n_new, int32_t *d_ids, float *d_hidden,

@@ -40,8 +40,8 @@ def test_status_strings():
 
 def test_struct_layout_matches_header():
     # 10 int32 + 1 float; 16 pointers; 5 pointers + 1 pointer; 2 pointers + 4 int32;
-    # 2 int32 + 2 pointers
-    assert ctypes.sizeof(tb.bloom_gen_control) == 24
+    # 2 int32 + 7 pointers + 1 size_t
+    assert ctypes.sizeof(tb.bloom_gen_control) == 8 + 7 * 8 + 8
     assert ctypes.sizeof(tb.bloom_config) == 44
     assert ctypes.sizeof(tb.bloom_layer_weights) == 16 * 8
     assert ctypes.sizeof(tb.bloom_weights) == 6 * 8
@@ -169,6 +169,11 @@ def test_generate_validation_paths():
     assert _generate(f, ctl=tb.bloom_gen_control(250880, 0, None, None)) == tb.BLOOM_EINVAL
     assert _generate(f, ctl=tb.bloom_gen_control(5, 0, None, None), ws_bytes=16) == \
         tb.BLOOM_EWORKSPACE
+    # sampling fields: all or none; the sampling workspace must be large enough
+    part = tb.bloom_gen_control(-1, 0, None, None, 0x10, 0x10, None, 0x10, 0x10, 1 << 30)
+    assert _generate(f, ctl=part) == tb.BLOOM_EINVAL
+    full = tb.bloom_gen_control(-1, 0, None, None, 0x10, 0x10, 0x10, 0x10, 0x10, 64)
+    assert _generate(f, ctl=full) == tb.BLOOM_EWORKSPACE
     assert f.kv.len == 0 and f.kv.prompt_len == 0
 
 

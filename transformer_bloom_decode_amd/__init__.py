@@ -56,7 +56,9 @@ class bloom_kv_cache(ctypes.Structure):
 
 class bloom_gen_control(ctypes.Structure):
     _fields_ = [("eos_id", _i32), ("pad_id", _i32), ("d_max_new", _c_void_p),
-                ("d_out_len", _c_void_p)]
+                ("d_out_len", _c_void_p), ("d_temperature", _c_void_p), ("d_top_p", _c_void_p),
+                ("d_uniform", _c_void_p), ("d_logits", _c_void_p), ("d_sample_ws", _c_void_p),
+                ("sample_ws_bytes", ctypes.c_size_t)]
 
 
 class BloomError(RuntimeError):
@@ -180,15 +182,30 @@ def bloom_decode_step(cfg, weights, kv, batch: int, tokens, valid_len, next_toke
 
 def bloom_generate(cfg, weights, kv, batch: int, prompt_len: int, tokens, valid_len, n_new: int,
                    ids, hidden_out, ws, stream=None, eos_id: Optional[int] = None, pad_id: int = 0,
-                   max_new=None, out_len=None):
+                   max_new=None, out_len=None, temperature=None, top_p=None, uniform=None,
+                   logits=None, sample_ws=None):
     """bloom_generate; eos_id / max_new (device int32 [batch]) / out_len (device int32
-    [batch]) fill a bloom_gen_control when any of them is given."""
+    [batch]) and the sampling inputs (temperature, top_p: device float32 [batch];
+    uniform: device float32 [n_new, batch]; logits: device float32 [batch, vocab]
+    scratch; sample_ws: device bytes) fill a bloom_gen_control when any is given.
+    With temperature given and logits / sample_ws not, those are allocated here."""
     w = weights.struct if hasattr(weights, "struct") else weights
     k = kv.struct if hasattr(kv, "struct") else kv
     ctl = None
-    if eos_id is not None or max_new is not None or out_len is not None:
-        ctl = ctypes.byref(bloom_gen_control(-1 if eos_id is None else eos_id, pad_id,
-                                             _ptr(max_new), _ptr(out_len)))
+    if temperature is not None:
+        import torch
+        dev = temperature.device
+        if logits is None:
+            logits = torch.empty((batch, cfg.vocab), dtype=torch.float32, device=dev)
+        if sample_ws is None:
+            sample_ws = torch.empty(bloom_sample_workspace_bytes(batch, cfg.vocab),
+                                    dtype=torch.uint8, device=dev)
+    if (eos_id is not None or max_new is not None or out_len is not None
+            or temperature is not None):
+        ctl = ctypes.byref(bloom_gen_control(
+            -1 if eos_id is None else eos_id, pad_id, _ptr(max_new), _ptr(out_len),
+            _ptr(temperature), _ptr(top_p), _ptr(uniform), _ptr(logits), _ptr(sample_ws),
+            _nbytes(sample_ws)))
     _check(lib.bloom_generate(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(k), batch,
                               prompt_len, _ptr(tokens), _ptr(valid_len), n_new, _ptr(ids),
                               _ptr(hidden_out), ctl, _ptr(ws), _nbytes(ws), _stream(stream)),

@@ -211,7 +211,7 @@ hipStream_t capture_stream() {
 int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *kv, int batch,
                 int tpr, int pos_base, int prompt_len, const int32_t *d_tokens,
                 const int32_t *d_valid, int32_t *d_next, float *d_hidden, char *ws,
-                hipStream_t st, const int *d_pos = nullptr) {
+                hipStream_t st, const int *d_pos = nullptr, float *d_logits = nullptr) {
   const WsPlan wp = plan_ws(c, batch, tpr);
   const bool f32 = c->weight_dtype == BLOOM_F32;
   const int wdt = wtype(c);
@@ -339,6 +339,22 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
   err = launch_layernorm(f32, x, tpr, tpr - 1, w->lnf_g, w->lnf_b, af, d_hidden, batch, h,
                          c->ln_eps, st);
   if (err != hipSuccess) return hip_fail(err);
+  if (d_logits) {
+    // the LM head's float32 logits [batch][vocab] instead of its argmax (sampling), with
+    // the greedy head's plan, so a greedy row of the sampler ranks the same values
+    for (int r0 = 0; r0 < batch; r0 += 128) {
+      const int rows = std::min(128, batch - r0);
+      EpiParams e{};
+      e.mode = EPI_STORE;
+      e.out = d_logits + (size_t)r0 * c->vocab;
+      e.ld = c->vocab;
+      const LinearPlan p_lm = plan_linear(wdt_lm, rows, c->vocab, h, true);
+      err = timed_linear(wdt_lm, p_lm, (const char *)af + (size_t)r0 * h * act, w->embed, part,
+                         e, st, lm_bytes);
+      if (err != hipSuccess) return hip_fail(err);
+    }
+    return BLOOM_OK;
+  }
   for (int r0 = 0; d_next && r0 < batch; r0 += 128) {
     const int rows = std::min(128, batch - r0);
     EpiParams a{};
@@ -443,6 +459,14 @@ int bloom_generate(const bloom_config *cfg, const bloom_weights *w, bloom_kv_cac
   if (!d_tokens || !d_valid_len || !d_ids || !d_ws) return BLOOM_EINVAL;
   if (ctl && ctl->eos_id >= cfg->vocab) return BLOOM_EINVAL;
   if (ws_bytes < plan_ws(cfg, batch, prompt_len).total) return BLOOM_EWORKSPACE;
+  const bool sampled = ctl && (ctl->d_temperature || ctl->d_top_p || ctl->d_uniform ||
+                               ctl->d_logits || ctl->d_sample_ws);
+  if (sampled) {
+    if (!ctl->d_temperature || !ctl->d_top_p || !ctl->d_uniform || !ctl->d_logits ||
+        !ctl->d_sample_ws || cfg->vocab > (1 << 23))
+      return BLOOM_EINVAL;
+    if (ctl->sample_ws_bytes < sample_workspace_bytes(batch, cfg->vocab)) return BLOOM_EWORKSPACE;
+  }
   clear_stale_hip_error();
   hipStream_t st = (hipStream_t)stream;
   char *ws = (char *)d_ws;
@@ -460,12 +484,24 @@ int bloom_generate(const bloom_config *cfg, const bloom_weights *w, bloom_kv_cac
   gc.max_new = ctl ? ctl->d_max_new : nullptr;
   gc.out_len = ctl ? ctl->d_out_len : nullptr;
 
+  // One pass and its token: the greedy LM head's argmax, or (sampling) its logits and
+  // a draw with the uniform number of the step being recorded (state[1]).
+  float *logits = sampled ? ctl->d_logits : nullptr;
+  auto pass = [&](int tpr, int pos_base, const int32_t *toks, hipStream_t sst,
+                  const int *d_pos) -> int {
+    int r = run_forward(cfg, w, kv, batch, tpr, pos_base, prompt_len, toks, d_valid_len, nxt,
+                        hfix, ws, sst, d_pos, logits);
+    if (r != BLOOM_OK || !sampled) return r;
+    const hipError_t e = launch_sample_rows(logits, batch, cfg->vocab, ctl->d_temperature,
+                                            ctl->d_top_p, ctl->d_uniform, nxt, ctl->d_sample_ws,
+                                            sst, state + 1);
+    return e == hipSuccess ? BLOOM_OK : hip_fail(e);
+  };
   // the prompt pass and the first decode step run eagerly (they also run any one-time
   // set-up); every step's ids go through the same recording kernel
   hipError_t err = launch_gen_init(state, prompt_len - 1, 0, gc.done, batch, st);
   if (err != hipSuccess) return hip_fail(err);
-  s = run_forward(cfg, w, kv, batch, prompt_len, 0, prompt_len, d_tokens, d_valid_len, nxt,
-                  hfix, ws, st);
+  s = pass(prompt_len, 0, d_tokens, st, nullptr);
   if (s != BLOOM_OK) return s;
   if ((err = launch_gen_record(nxt, cur, d_ids, hfix, d_hidden, state, batch, cfg->hidden, gc,
                                st)) != hipSuccess)
@@ -473,8 +509,7 @@ int bloom_generate(const bloom_config *cfg, const bloom_weights *w, bloom_kv_cac
   kv->prompt_len = prompt_len;
   kv->len = prompt_len;
   if (n_new >= 2) {
-    s = run_forward(cfg, w, kv, batch, 1, kv->len, kv->prompt_len, cur, d_valid_len, nxt, hfix,
-                    ws, st);
+    s = pass(1, kv->len, cur, st, nullptr);
     if (s != BLOOM_OK) return s;
     if ((err = launch_gen_record(nxt, cur, d_ids, hfix, d_hidden, state, batch, cfg->hidden, gc,
                                  st)) != hipSuccess)
@@ -493,8 +528,7 @@ int bloom_generate(const bloom_config *cfg, const bloom_weights *w, bloom_kv_cac
   if ((err = hipStreamBeginCapture(side, hipStreamCaptureModeThreadLocal)) != hipSuccess)
     return hip_fail(err);
   g_timer.capturing = true;
-  s = run_forward(cfg, w, kv, batch, 1, 0, kv->prompt_len, cur, d_valid_len, nxt, hfix, ws, side,
-                  state);
+  s = pass(1, 0, cur, side, state);
   g_timer.capturing = false;
   if (s == BLOOM_OK) {
     err = launch_gen_record(nxt, cur, d_ids, hfix, d_hidden, state, batch, cfg->hidden, gc, side);

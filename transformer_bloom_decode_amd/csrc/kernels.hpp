@@ -132,9 +132,11 @@ hipError_t launch_kv_compact(void *kc, void *vc, int n_layer, int H, int max_bat
 // uniform number per row (sample.hip); temperature <= 0 is greedy.  `ws` holds
 // sample_workspace_bytes(batch, V) bytes of partial results.
 size_t sample_workspace_bytes(int batch, int vocab);
+// With step_dev set, row b draws with uniform[*step_dev * batch + b] (a generation loop's
+// step index in device memory), else with uniform[b].
 hipError_t launch_sample_rows(const float *logits, int batch, int V, const float *temperature,
                               const float *top_p, const float *uniform, int *out, void *ws,
-                              hipStream_t st);
+                              hipStream_t st, const int *step_dev = nullptr);
 // y[i] = bf16(x[i]), round to nearest even.
 hipError_t launch_f32_to_bf16(const float *x, void *y, size_t n, hipStream_t st);
 hipError_t launch_kv_append(bool f32, const void *k, const void *v, void *ck, void *cv,

@@ -80,6 +80,7 @@ struct SmpArgs {
   const float *logits;
   int V, NB, SL, nseg;
   const float *temperature, *top_p, *uniform;
+  const int *step_dev;
   int *out;
   float *pmax;
   int *pidx;
@@ -408,7 +409,8 @@ __global__ __launch_bounds__(kSmpThreads) void k_smp_draw(SmpArgs a) {
     if (w < wid) base += wsum[w];
     M += wsum[w];
   }
-  const float uu = fminf(fmaxf(a.uniform[b], 0.f), 0x1.fffffep-1f);
+  const int step = a.step_dev ? *a.step_dev : 0;
+  const float uu = fminf(fmaxf(a.uniform[(size_t)step * gridDim.x + b], 0.f), 0x1.fffffep-1f);
   const u64 r = (u64)((double)uu * (double)M);   // < M
   u64 lo = base + incl - mine;
   for (int g = g0; g < g1; ++g) {
@@ -458,11 +460,11 @@ size_t sample_workspace_bytes(int batch, int vocab) {
 
 hipError_t launch_sample_rows(const float *logits, int batch, int V, const float *temperature,
                               const float *top_p, const float *uniform, int *out, void *ws,
-                              hipStream_t st) {
+                              hipStream_t st, const int *step_dev) {
   if (batch <= 0) return hipSuccess;
   const SmpLayout L = sample_layout(batch, V);
   char *w = (char *)ws;
-  SmpArgs a{logits, V, L.NB, L.SL, L.nseg, temperature, top_p, uniform, out,
+  SmpArgs a{logits, V, L.NB, L.SL, L.nseg, temperature, top_p, uniform, step_dev, out,
             (float *)(w + L.pmax), (int *)(w + L.pidx), (u64 *)(w + L.pS),
             (u64 *)(w + L.hist), (u64 *)(w + L.state), (u64 *)(w + L.seg)};
   const dim3 grid(L.NB, batch), block(kSmpThreads);
