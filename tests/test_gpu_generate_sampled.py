@@ -120,3 +120,29 @@ def test_sampled_generation_matches_the_oracle_teacher_forced():
         if t + 1 < n_new:
             h = oracle.forward(om, ids[t][:, None].astype(np.int32), 8 + t, pad, cache)[:, 0]
     assert exact >= 0.75 * B * n_new, exact
+
+
+def test_sampled_generation_with_end_token_and_row_limits():
+    """The stop rule applies to sampled tokens as to greedy ones: each row's ids equal
+    the unconstrained sampled run's up to its end (its end token, or its token limit),
+    then the pad id; token counts are reported."""
+    shape = bi.BLOOM_560M.truncated(2)
+    _, dw, cfg = upload(shape)
+    B, n_new = 3, 8
+    prompt, valid = bi.prompts(shape, B, 16, (16, 9, 12))
+    T, P, u = _inputs(B, n_new, T=(50.0, 40.0, 0.0), P=(1.0, 0.95, 1.0))
+    free, _ = _sampled_graph(cfg, dw, prompt, valid, n_new, T, P, u)
+    eos = int(free[3, 0])                      # row 0 ends at step 3 (or earlier)
+    max_new = np.array([n_new, 5, n_new], dtype=np.int32)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    kv = tb.KVCache(cfg, B, 16 + n_new)
+    ws = tb.workspace(cfg, B, 16)
+    ids = torch.empty((n_new, B), dtype=torch.int32, device="cuda")
+    out_len = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+    tb.bloom_generate(cfg, dw, kv, B, 16, d(prompt), d(valid), n_new, ids, None, ws,
+                      eos_id=eos, pad_id=3, max_new=d(max_new), out_len=out_len,
+                      temperature=d(T), top_p=d(P), uniform=d(u))
+    torch.cuda.synchronize()
+    want, lengths = oracle.stop_rule(free.T, eos, max_new, 3)
+    np.testing.assert_array_equal(ids.cpu().numpy().T, want)
+    np.testing.assert_array_equal(out_len.cpu().numpy(), lengths)
