@@ -58,7 +58,11 @@ struct SmpLayout {
 SmpLayout sample_layout(int B, int V) {
   SmpLayout L{};
   const int nseg = (V + 255) / 256;
-  int nb = std::max(1, std::min(64, 512 / std::max(B, 1)));
+  // up to 64 slices per row while the grid is small, at least 16 (while B <= 128) so
+  // that large batches still fill the chip; measured at batch 128: 4 slices 209 us, 16
+  // slices 190 us per call
+  const int Bc = std::max(B, 1);
+  int nb = std::max(1, std::max(std::min(64, 512 / Bc), std::min(16, 2048 / Bc)));
   nb = std::min(nb, nseg);
   const int segs_per_slice = (nseg + nb - 1) / nb;
   L.SL = 256 * segs_per_slice;
