@@ -123,3 +123,80 @@ def test_temperature_is_a_logit_scale():
     a = oracle.sample_tokens(lg, np.full(6, 2.0), ps, us).tokens
     b = oracle.sample_tokens(lg / 2.0, np.full(6, 1.0), ps, us).tokens
     np.testing.assert_array_equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes: each plausible slip in the sampler must fail one of the pins above
+# ---------------------------------------------------------------------------
+
+def _mutant(kind):
+    from oracle import bloom_oracle as bo
+    orig = bo.sample_tokens
+
+    def sample(logits, temperature, top_p, uniform):
+        logits = np.asarray(logits, dtype=np.float64)
+        T = np.asarray(temperature, dtype=np.float64).reshape(-1)
+        if kind == "temperature_multiplies":
+            return orig(logits * T[:, None] * T[:, None], temperature, top_p, uniform)
+        if kind == "draw_in_probability_order":
+            # same nucleus, but the draw walks it from the most probable token down
+            r = orig(logits, temperature, top_p, uniform)
+            out = r.tokens.copy()
+            for b in range(len(out)):
+                if not T[b] > 0:
+                    continue
+                z = logits[b] / T[b]
+                q = np.exp(z - z.max())
+                q /= q.sum()
+                order = np.argsort(-q, kind="stable")[: int(r.nucleus_size[b])]
+                F = np.cumsum(q[order]) / q[order].sum()
+                j = min(int(np.searchsorted(F, float(np.asarray(uniform).reshape(-1)[b]),
+                                            side="right")), len(order) - 1)
+                out[b] = order[j]
+            return bo.SampleResult(out, r.keep_margin, r.draw_margin, r.nucleus_size)
+        if kind == "boundary_token_dropped":
+            # the nucleus stops before the token that makes its mass reach top_p
+            P = np.asarray(top_p, dtype=np.float64).reshape(-1)
+            U = np.asarray(uniform, dtype=np.float64).reshape(-1)
+            r = orig(logits, temperature, top_p, uniform)
+            out = r.tokens.copy()
+            size = r.nucleus_size.copy()
+            for b in range(len(out)):
+                if not T[b] > 0 or P[b] >= 1:
+                    continue
+                z = logits[b] / T[b]
+                q = np.exp(z - z.max())
+                q /= q.sum()
+                last = np.sort(q)[::-1][int(r.nucleus_size[b]) - 1]
+                keep = q > last
+                if not keep.any():
+                    keep = q >= q.max()
+                idx = np.nonzero(keep)[0]
+                F = np.cumsum(q[idx]) / q[idx].sum()
+                out[b] = idx[min(int(np.searchsorted(F, U[b], side="right")), len(idx) - 1)]
+                size[b] = len(idx)
+            return bo.SampleResult(out, r.keep_margin, r.draw_margin, size)
+        raise ValueError(kind)
+    return sample
+
+
+PINS = [test_hand_worked_four_tokens, test_ties_at_the_boundary_are_all_kept,
+        test_nucleus_is_the_smallest_set_reaching_top_p_brute_force,
+        test_temperature_is_a_logit_scale]
+
+
+def _frequency_pin():
+    test_draw_frequencies_on_a_uniform_grid(0.7, 0.8)
+
+
+@pytest.mark.parametrize("kind", ["temperature_multiplies", "draw_in_probability_order",
+                                  "boundary_token_dropped"])
+def test_planted_sampler_mistakes_fail_a_pin(kind, monkeypatch):
+    monkeypatch.setattr(oracle, "sample_tokens", _mutant(kind))
+    caught = 0
+    for pin in PINS + [_frequency_pin]:
+        try:
+            pin()
+        except AssertionError:
+            caught += 1
+    assert caught >= 1, f"no pin caught the planted mistake {kind}"
