@@ -5,7 +5,8 @@
  * pre-LayerNorm decoder layer (input LayerNorm, fused QKV projection, ALiBi
  * attention over the cached keys with masked fill and an fp32 softmax, output
  * projection with bias and residual, post-attention LayerNorm, tanh-GeLU MLP),
- * the final LayerNorm and the tied LM head with a greedy argmax.
+ * the final LayerNorm and the tied LM head with a greedy argmax, or per-row
+ * temperature / top-p sampling from its logits.
  *
  * Sources (web pages, cited by title and section):
  *   [P1] "Incredibly Fast BLOOM Inference with DeepSpeed and Accelerate",
@@ -18,7 +19,9 @@
  *   [P4] "Hugging Face BLOOM Inference Optimization": Kernel Fusion with
  *        torch.jit.script (fused tanh GeLU), Efficient PyTorch Implementation (ALiBi
  *        computed once; KV "past" laid out to avoid reshapes), Custom CUDA Kernels and
- *        Hardware Acceleration (masked_fill then a float32 softmax).
+ *        Hardware Acceleration (masked_fill then a float32 softmax), Webserver
+ *        Architecture and Request Handling (a custom generation loop with per-request
+ *        parameters, e.g. sampling and top-p, and the extraction of finished requests).
  *
  * Conventions
  *   - Every pointer named d_* (and every pointer inside the structs below) is device
@@ -198,8 +201,9 @@ typedef struct {
   size_t sample_ws_bytes;
 } bloom_gen_control;
 
-/* Greedy generation loop ([P1] Benchmark Environment: greedy generation of new tokens
- * with the KV cache; [P3] III.D: launch overhead at small batch is removed with graphs).
+/* Generation loop ([P1] Benchmark Environment: greedy generation of new tokens with the
+ * KV cache; [P3] III.D: launch overhead at small batch is removed with graphs; [P4]
+ * Webserver Architecture: per-row stop rules and sampling through ctl, above).
  * Runs the prompt pass (as bloom_prefill), then n_new - 1 decode steps: the first
  * eagerly, the rest as replays of one HIP graph captured from a decode step whose KV
  * position and input tokens live in device memory.  d_ids [n_new][batch] int32
