@@ -145,6 +145,8 @@ int bloom_workspace_bytes(const bloom_config *cfg, int32_t max_batch, int32_t ma
 /* Prompt pass ([P1] Benchmark Environment: generation starts from a short prompt).
  * d_tokens [batch][prompt_len] int32, LEFT-padded: row b has d_valid_len[b] real
  * tokens (1 <= valid_len <= prompt_len) at its right end; pad ids are ignored.
+ * Token ids are not checked on the host (they are device data): an id outside
+ * [0, vocab) is clamped to the nearest valid id by the embedding gather.
  * Runs every prompt position through the stack, writes KV slots [0, prompt_len),
  * sets kv->prompt_len = kv->len = prompt_len, and writes the greedy next token of
  * each row to d_next_tokens [batch] (lowest id among equal float32 logits).
@@ -159,7 +161,8 @@ int bloom_prefill(const bloom_config *cfg, const bloom_weights *w, bloom_kv_cach
                   void *d_ws, size_t ws_bytes, void *stream);
 
 /* One generation step ([P1] Benchmark Environment; [P3] III.D fused groups).
- * d_tokens [batch] int32 are the tokens at position kv->len; d_valid_len [batch] are
+ * d_tokens [batch] int32 are the tokens at position kv->len (ids outside [0, vocab)
+ * clamped, as in bloom_prefill); d_valid_len [batch] are
  * the same valid prompt lengths given to bloom_prefill (left-pad masking).  Writes
  * KV slot kv->len of every layer, attends over slots [prompt_len - valid_len[b],
  * kv->len], writes the greedy next token to d_next_tokens and optionally the
@@ -183,7 +186,8 @@ int bloom_decode_step(const bloom_config *cfg, const bloom_weights *w, bloom_kv_
  * finished).  Finished rows can be taken out between calls with kv_cache_compact.
  * Sampling (the same page: sampling parameters per member of the batch): with
  * d_temperature, d_top_p (device float32 [batch]) and d_uniform (device float32
- * [n_new][batch], the caller's random numbers in [0, 1)) set, every step's token is
+ * [n_new][batch], the caller's random numbers in [0, 1); all n_new * batch values are
+ * read, so a shorter buffer is read out of bounds) set, every step's token is
  * drawn as bloom_sample_tokens does, from the tied LM head's logits (written to the
  * caller's d_logits [batch][vocab] float32 scratch) with d_uniform[step][b]; rows with
  * temperature <= 0 stay greedy.  d_sample_ws is a device workspace of
@@ -239,7 +243,8 @@ int bloom_lm_logits(const bloom_config *cfg, const bloom_weights *w, int32_t bat
  * Text Degeneration", Section 3.1).  For row b of d_logits [batch][vocab] float32 (no
  * NaN), with T = d_temperature[b], p = d_top_p[b], u = d_uniform[b] (device float32
  * [batch] each; u is clamped to [0, 1)):
- *   T <= 0: the greedy token (lowest id among the largest logits);
+ *   T <= 0, or T so small that 1/T overflows float32 (below ~2.9e-39): the greedy
+ *   token (lowest id among the largest logits);
  *   else q = softmax(logits / T); the nucleus is the shortest run of tokens in
  *   decreasing q whose mass reaches p, plus every token tied with its last one (p >= 1:
  *   all tokens; p <= 0: the largest logits only); the token is the first id, in

@@ -426,7 +426,10 @@ def sample_tokens(logits: np.ndarray, temperature, top_p, uniform) -> SampleResu
     neither step, so the textbook definitions are used (float64):
 
     * temperature T <= 0: greedy, the lowest id among the largest logits (decided on
-      float32-rounded logits, as ``greedy_argmax``);
+      float32-rounded logits, as ``greedy_argmax``); so is a positive T whose
+      reciprocal overflows float32 (T below about 2.9e-39): softmax(logits / T) tends
+      to the largest logits as T -> 0, and the temperature is an input of float32
+      precision, so the limit is taken once 1/T has no float32 value;
     * otherwise q = softmax(logits / T);
     * nucleus (Holtzman et al., "The Curious Case of Neural Text Degeneration", ICLR
       2020, Section 3.1): sort q in decreasing order and take the shortest prefix whose
@@ -451,7 +454,9 @@ def sample_tokens(logits: np.ndarray, temperature, top_p, uniform) -> SampleResu
     draw_m = np.full(B, np.inf)
     size = np.zeros(B, dtype=np.int64)
     for b in range(B):
-        if not T[b] > 0:
+        with np.errstate(over="ignore", divide="ignore"):
+            inv_t32 = np.float32(1.0) / np.float32(T[b]) if T[b] > 0 else np.float32(0)
+        if not T[b] > 0 or not np.isfinite(inv_t32):
             toks[b] = int(np.argmax(logits[b].astype(np.float32)))
             size[b] = 1
             continue

@@ -66,9 +66,12 @@ def test_sampling_ragged_vocabularies_and_edges():
         # edge values of top_p and u on some rows
         P[0], P[1], P[2] = 1.0, 0.0, 1e-7
         u[3], u[4] = 0.0, np.float32(1.0 - 2 ** -24)
+        # a positive temperature whose reciprocal overflows float32 is greedy
+        T[5] = np.float32(1e-39)
         got, ref, _ = _check_rows(logits, T, P, u, 0.0)
         am = np.argmax(logits, axis=1)
         assert got[1] == am[1] and got[2] == am[2]     # only the largest logit kept
+        assert got[5] == am[5] and ref.tokens[5] == am[5]
         assert np.all((got >= 0) & (got < V))
 
 

@@ -40,6 +40,17 @@ def test_greedy_rows_take_the_lowest_id_of_the_maximum():
         assert tok == 1
 
 
+def test_vanishing_temperature_tends_to_the_argmax():
+    # softmax(logits / T) -> the one-hot of the largest logit as T -> 0: a small T that
+    # still has a float32 reciprocal (the sampling branch) and one whose reciprocal
+    # overflows float32 (taken as greedy) both give the argmax, for any u and top_p
+    lg = [0.5, 2.0, 1.999, -3.0]
+    for T in (1e-6, 1e-30, 1e-39):
+        for u, p in ((0.0, 0.9), (0.999, 1.0), (0.5, 0.3)):
+            tok, _ = _one(lg, T, p, u)
+            assert tok == 1, (T, u, p, tok)
+
+
 def test_ties_at_the_boundary_are_all_kept():
     # four equal tokens, top_p 0.3: the first token taken (0.25 < 0.3) is not enough,
     # the boundary value 0.25 is shared by all four, so all are kept

@@ -149,6 +149,22 @@ def _stream(stream) -> Optional[int]:
 # C functions, same names
 # ---------------------------------------------------------------------------
 
+def _require(t, numel: int, dtype, name: str, device=None):
+    """Raise ValueError unless ``t`` is a contiguous device tensor of ``numel``
+    elements of ``dtype`` (on ``device`` when given): the kernels index such buffers
+    directly, so a short or mistyped one would be read out of bounds."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name}: a device tensor is required")
+    if t.dtype != dtype or not t.is_contiguous() or t.device.type != "cuda":
+        raise ValueError(f"{name}: need a contiguous {dtype} tensor on the GPU, got "
+                         f"{t.dtype} on {t.device} (contiguous={t.is_contiguous()})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    if t.numel() != numel:
+        raise ValueError(f"{name}: {t.numel()} elements, expected {numel}")
+
+
 def bloom_status_string(code: int) -> str:
     return lib.bloom_status_string(code).decode()
 
@@ -192,14 +208,24 @@ def bloom_generate(cfg, weights, kv, batch: int, prompt_len: int, tokens, valid_
     w = weights.struct if hasattr(weights, "struct") else weights
     k = kv.struct if hasattr(kv, "struct") else kv
     ctl = None
-    if temperature is not None:
+    if temperature is not None or top_p is not None or uniform is not None:
         import torch
+        if temperature is None or top_p is None or uniform is None:
+            raise ValueError("temperature, top_p and uniform go together")
         dev = temperature.device
+        _require(temperature, batch, torch.float32, "temperature")
+        _require(top_p, batch, torch.float32, "top_p", dev)
+        _require(uniform, n_new * batch, torch.float32, "uniform", dev)
         if logits is None:
             logits = torch.empty((batch, cfg.vocab), dtype=torch.float32, device=dev)
+        _require(logits, batch * cfg.vocab, torch.float32, "logits", dev)
         if sample_ws is None:
             sample_ws = torch.empty(bloom_sample_workspace_bytes(batch, cfg.vocab),
                                     dtype=torch.uint8, device=dev)
+    for t, name in ((max_new, "max_new"), (out_len, "out_len")):
+        if t is not None:
+            import torch
+            _require(t, batch, torch.int32, name)
     if (eos_id is not None or max_new is not None or out_len is not None
             or temperature is not None):
         ctl = ctypes.byref(bloom_gen_control(
@@ -251,6 +277,13 @@ def bloom_sample_tokens(logits, batch: int, vocab: int, temperature, top_p, unif
                         ws=None, stream=None):
     """bloom_sample_tokens; without `ws` a workspace of the required size is allocated
     on the logits' device for this call."""
+    if batch > 0:
+        import torch
+        _require(logits, batch * vocab, torch.float32, "logits")
+        for t, name in ((temperature, "temperature"), (top_p, "top_p"),
+                        (uniform, "uniform")):
+            _require(t, batch, torch.float32, name, logits.device)
+        _require(tokens, batch, torch.int32, "tokens", logits.device)
     if ws is None and batch > 0:
         import torch
         ws = torch.empty(bloom_sample_workspace_bytes(batch, vocab), dtype=torch.uint8,

@@ -165,9 +165,11 @@ __device__ __forceinline__ RowParams row_params(const SmpArgs &a, int b, bool wi
   RowParams r;
   r.T = a.temperature[b];
   r.P = a.top_p[b];
-  r.greedy = !(r.T > 0.f);
-  r.radix = r.P > 0.f && r.P < 1.f;
   r.invT = 1.0f / r.T;
+  // a positive temperature whose reciprocal overflows float32 (T below ~2.9e-39) samples
+  // from the limit of softmax(logits / T), the largest logits: it is taken as greedy
+  r.greedy = !(r.T > 0.f) || !(r.invT <= 3.402823466e38f);
+  r.radix = r.P > 0.f && r.P < 1.f;
   r.m = with_max ? row_max(a, b) : -INFINITY;
   return r;
 }
