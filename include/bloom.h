@@ -264,6 +264,23 @@ int bloom_sample_tokens(const float *d_logits, int32_t batch, int32_t vocab,
 /* Workspace bytes bloom_sample_tokens needs for `batch` rows of `vocab` logits. */
 int bloom_sample_workspace_bytes(int32_t batch, int32_t vocab, size_t *bytes);
 
+/* bloom_sample_tokens without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same inputs, outputs and results as bloom_sample_tokens; the
+ * partial results live in a scratch array the library holds in each GPU's memory
+ * (16 MiB per GPU, kept until the process ends; nothing is allocated by the call).
+ * Calls on one GPU share that array: calls that overlap in time on one GPU race, so a
+ * caller serialises them (one stream, or its own ordering).  EWORKSPACE if the rows
+ * need more scratch than the array holds (bloom_sample_scratch_limit tells; up to
+ * batch 1396 at vocab 250880); EINVAL as bloom_sample_tokens. */
+int bloom_sample_tokens_static(const float *d_logits, int32_t batch, int32_t vocab,
+                               const float *d_temperature, const float *d_top_p,
+                               const float *d_uniform, int32_t *d_tokens, void *stream);
+
+/* Whether bloom_sample_tokens_static accepts `batch` rows of `vocab` logits (*fits = 1)
+ * and the scratch array's size in bytes (*max_bytes).  Host-only. */
+int bloom_sample_scratch_limit(int32_t batch, int32_t vocab, int32_t *fits, size_t *max_bytes);
+
 /* Standalone fused ALiBi bias + masked fill + float32 softmax ([P4] Custom CUDA Kernels
  * and Hardware Acceleration; Efficient PyTorch Implementation for ALiBi).
  * d_scores [B][H][Q][K] (in_dtype BLOOM_BF16 or BLOOM_F32) are attention scores

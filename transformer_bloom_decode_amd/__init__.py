@@ -106,6 +106,8 @@ def _load():
     lib.bloom_sample_tokens.argtypes = [vp, _i32, _i32, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                         vp]
     lib.bloom_sample_workspace_bytes.argtypes = [_i32, _i32, P(ctypes.c_size_t)]
+    lib.bloom_sample_tokens_static.argtypes = [vp, _i32, _i32, vp, vp, vp, vp, vp]
+    lib.bloom_sample_scratch_limit.argtypes = [_i32, _i32, P(_i32), P(ctypes.c_size_t)]
     lib.bloom_timer_enable.argtypes = [_i32]
     lib.bloom_timer_disable.argtypes = []
     lib.bloom_timer_read.argtypes = [_i32, P(ctypes.c_double), P(_i32), P(ctypes.c_double)]
@@ -113,6 +115,7 @@ def _load():
     for name in ("bloom_workspace_bytes", "bloom_prefill", "bloom_decode_step", "bloom_generate",
                  "alibi_masked_softmax", "kv_cache_append", "kv_cache_compact",
                  "bloom_lm_logits", "bloom_sample_tokens", "bloom_sample_workspace_bytes",
+                 "bloom_sample_tokens_static", "bloom_sample_scratch_limit",
                  "bloom_timer_enable",
                  "bloom_timer_disable", "bloom_timer_read", "bloom_timer_pause"):
         getattr(lib, name).restype = ctypes.c_int
@@ -291,6 +294,29 @@ def bloom_sample_tokens(logits, batch: int, vocab: int, temperature, top_p, unif
     _check(lib.bloom_sample_tokens(_ptr(logits), batch, vocab, _ptr(temperature), _ptr(top_p),
                                    _ptr(uniform), _ptr(tokens), _ptr(ws), _nbytes(ws),
                                    _stream(stream)), "bloom_sample_tokens")
+
+
+def bloom_sample_tokens_static(logits, batch: int, vocab: int, temperature, top_p, uniform,
+                               tokens, stream=None):
+    """bloom_sample_tokens_static: the library's per-GPU scratch array, no workspace."""
+    if batch > 0:
+        import torch
+        _require(logits, batch * vocab, torch.float32, "logits")
+        for t, name in ((temperature, "temperature"), (top_p, "top_p"),
+                        (uniform, "uniform")):
+            _require(t, batch, torch.float32, name, logits.device)
+        _require(tokens, batch, torch.int32, "tokens", logits.device)
+    _check(lib.bloom_sample_tokens_static(_ptr(logits), batch, vocab, _ptr(temperature),
+                                          _ptr(top_p), _ptr(uniform), _ptr(tokens),
+                                          _stream(stream)), "bloom_sample_tokens_static")
+
+
+def bloom_sample_scratch_limit(batch: int, vocab: int):
+    """(fits, scratch bytes) of bloom_sample_tokens_static for these rows."""
+    fits, nbytes = _i32(0), ctypes.c_size_t(0)
+    _check(lib.bloom_sample_scratch_limit(batch, vocab, ctypes.byref(fits), ctypes.byref(nbytes)),
+           "bloom_sample_scratch_limit")
+    return bool(fits.value), nbytes.value
 
 
 def bloom_timer_enable(max_launches: int):

@@ -674,6 +674,27 @@ int bloom_sample_tokens(const float *d_logits, int32_t batch, int32_t vocab,
   return err == hipSuccess ? BLOOM_OK : hip_fail(err);
 }
 
+int bloom_sample_tokens_static(const float *d_logits, int32_t batch, int32_t vocab,
+                               const float *d_temperature, const float *d_top_p,
+                               const float *d_uniform, int32_t *d_tokens, void *stream) {
+  if (batch < 0 || vocab < 1 || vocab > (1 << 23)) return BLOOM_EINVAL;
+  if (batch == 0) return BLOOM_OK;
+  if (!d_logits || !d_temperature || !d_top_p || !d_uniform || !d_tokens) return BLOOM_EINVAL;
+  if (sample_workspace_bytes(batch, vocab) > (size_t)kSampleScratchBytes) return BLOOM_EWORKSPACE;
+  clear_stale_hip_error();
+  const hipError_t err = launch_sample_rows_static(d_logits, batch, vocab, d_temperature,
+                                                   d_top_p, d_uniform, d_tokens,
+                                                   (hipStream_t)stream);
+  return err == hipSuccess ? BLOOM_OK : hip_fail(err);
+}
+
+int bloom_sample_scratch_limit(int32_t batch, int32_t vocab, int32_t *fits, size_t *max_bytes) {
+  if (!fits || !max_bytes || batch < 0 || vocab < 1 || vocab > (1 << 23)) return BLOOM_EINVAL;
+  *max_bytes = (size_t)kSampleScratchBytes;
+  *fits = sample_workspace_bytes(batch, vocab) <= (size_t)kSampleScratchBytes;
+  return BLOOM_OK;
+}
+
 int bloom_timer_enable(int32_t max_launches) {
   if (max_launches <= 0) return BLOOM_EINVAL;
   destroy_timer_events();

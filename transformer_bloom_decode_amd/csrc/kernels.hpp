@@ -137,6 +137,15 @@ size_t sample_workspace_bytes(int batch, int vocab);
 hipError_t launch_sample_rows(const float *logits, int batch, int V, const float *temperature,
                               const float *top_p, const float *uniform, int *out, void *ws,
                               hipStream_t st, const int *step_dev = nullptr);
+// The same sampling with the library's own device scratch array of kSampleScratchBytes
+// per GPU instead of a caller workspace (no allocation); hipErrorInvalidValue when the
+// rows need more than that.  Calls overlapping on one GPU share the array and race.
+constexpr long kSampleScratchBytes = 16l << 20;
+hipError_t launch_sample_rows_static(const float *logits, int batch, int V,
+                                     const float *temperature, const float *top_p,
+                                     const float *uniform, int *out, hipStream_t st);
+// Device address of this GPU's sample scratch array (looked up once per device).
+hipError_t sample_scratch_ptr(void **out);
 // y[i] = bf16(x[i]), round to nearest even.
 hipError_t launch_f32_to_bf16(const float *x, void *y, size_t n, hipStream_t st);
 hipError_t launch_kv_append(bool f32, const void *k, const void *v, void *ck, void *cv,

@@ -31,6 +31,7 @@
 // Every mass is an exact integer sum, so no result depends on the order of additions:
 // the LDS bucket atomics and the slice split leave the tokens bitwise reproducible.
 #include <algorithm>
+#include <mutex>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -481,6 +482,52 @@ hipError_t launch_sample_rows(const float *logits, int batch, int V, const float
   hipLaunchKernelGGL(k_smp_seg, grid, block, 0, st, a);
   hipLaunchKernelGGL(k_smp_draw, dim3(batch), block, 0, st, a);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// the same sampling with a library-held scratch buffer (no workspace argument)
+// ---------------------------------------------------------------------------
+// For callers that cannot allocate device memory (code under graph capture, tight
+// serving loops).  The partial results live in a file-scope device array; each GPU
+// holds its own copy, whose device address is looked up once per device (with that
+// device current) and kept.  Kernels receive that address, never the array's name
+// (which is a host-side stand-in in host code).  Calls on one GPU share the array:
+// calls that overlap in time on one GPU race.  Nothing in it needs to start at zero
+// (every partial is written before it is read within a call).
+static __device__ __align__(256) unsigned char scratch[kSampleScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t sample_scratch_ptr(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_sample_rows_static(const float *logits, int batch, int V,
+                                     const float *temperature, const float *top_p,
+                                     const float *uniform, int *out, hipStream_t st) {
+  if (batch <= 0) return hipSuccess;
+  if (sample_workspace_bytes(batch, V) > (size_t)kSampleScratchBytes) return hipErrorInvalidValue;
+  void *ws = nullptr;
+  const hipError_t e = sample_scratch_ptr(&ws);
+  if (e != hipSuccess) return e;
+  return launch_sample_rows(logits, batch, V, temperature, top_p, uniform, out, ws, st);
 }
 
 __global__ void k_f32_to_bf16(const float *__restrict__ x, bf16_t *__restrict__ y, size_t n) {
