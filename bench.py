@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--new-tokens", type=int, default=None)
     ap.add_argument("--layers", type=int, default=None, help="truncate the stack (development)")
+    ap.add_argument("--act", choices=("f32", "bf16"), default="f32",
+                    help="activation and KV-cache type of bf16 / int8 models: float32 values "
+                         "(the precise path) or bf16")
     ap.add_argument("--loop", choices=("eager", "graph"), default="eager",
                     help="decode loop: one bloom_decode_step call per token, or bloom_generate "
                          "(replays of a captured decode step)")
@@ -73,20 +76,30 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes_per_copy": n, "copies": 5}), flush=True)
 
 
-def upload_weights(m, seed=0):
-    """Generate each tensor on the host and copy it to HBM right away."""
+def device_weights(m, cfg, seed=0):
+    """Allocate the model's tensors in HBM and fill them on the GPU with the seeded
+    generator (bloom_init_weights; bitwise equal to the host generator of the tests)."""
+    import torch
+
     import bloom_inputs as bi
     import transformer_bloom_decode_amd as tb
 
-    g = {name: tb.to_device(bi.tensor(m, name, seed=seed)) for name in bi.global_field_names(m)}
-    layers = []
+    dt = {"f32": torch.float32, "bf16": torch.int16, "int8": torch.int8}
+
+    def buf(name):
+        if name.startswith("s_"):
+            return torch.empty(bi.tensor_shape(m, name), dtype=torch.int16, device="cuda")
+        kind = m.weight_dtype if name.startswith("w_") else m.param_dtype
+        return torch.empty(bi.tensor_shape(m, name), dtype=dt[kind], device="cuda")
+
     t0 = time.perf_counter()
-    for l in range(m.n_layer):
-        layers.append({f: tb.to_device(bi.tensor(m, f, l, seed=seed))
-                       for f in bi.layer_field_names(m)})
-        if (l + 1) % 10 == 0 or l + 1 == m.n_layer:
-            log(f"  uploaded {l + 1}/{m.n_layer} layers ({time.perf_counter() - t0:.1f}s)")
-    return tb.DeviceWeights(g, layers)
+    g = {name: buf(name) for name in bi.global_field_names(m)}
+    layers = [{f: buf(f) for f in bi.layer_field_names(m)} for _ in range(m.n_layer)]
+    dw = tb.DeviceWeights(g, layers)
+    tb.bloom_init_weights(cfg, dw, seed=seed, sigma=m.init_std)
+    torch.cuda.synchronize()
+    log(f"  generated {m.n_layer} layers on the GPU ({time.perf_counter() - t0:.1f}s)")
+    return dw
 
 
 def kernel_source_digest():
@@ -125,7 +138,7 @@ def step_bytes(m, B, P, n_new):
     """Algorithmic HBM bytes of one decode step averaged over the generation: every
     weight byte once (layers + tied LM head + LayerNorm/bias/scales) plus the KV cache
     read (T keys and values per head) and the new key/value written."""
-    act = 4 if m.weight_dtype == "f32" else 2
+    act = m.kv_bytes
     weights = m.n_layer * m.layer_weight_bytes() + m.head_bytes()
     if m.embed_ln:
         weights += 2 * m.hidden * (4 if m.param_dtype == "f32" else 2)
@@ -157,9 +170,23 @@ def cpu_baseline(m, B, P, n_new, budget_s):
 
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        cores = max([i.get("num_threads", 1) for i in blas] or [1])
+        blas_name = ", ".join(f"{i.get('internal_api')} {i.get('version')}" for i in blas)
     except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+        cores, blas_name = os.cpu_count() or 1, "unknown"
+    cpu_model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:  # pragma: no cover
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        affinity = os.cpu_count() or 1
     Ls = min(2, m.n_layer)
     ms = m.truncated(Ls)
     tensors = bi.model_tensors(ms)
@@ -192,6 +219,9 @@ def cpu_baseline(m, B, P, n_new, budget_s):
         "value": round(total_s * 1e3 / (B * n_new), 3),
         "unit": "ms/token",
         "cores": int(cores),
+        "host_cpus_available": int(affinity),
+        "cpu_model": cpu_model,
+        "blas": blas_name,
         "kind": "oracle",
         "sample": (f"float64 numpy oracle on {Ls} of {m.n_layer} layers at full width, batch {B}: "
                    f"{P}-token prompt pass + {steps} single-token steps, each with the full "
@@ -332,16 +362,19 @@ def main():
     import bloom_inputs as bi
     import transformer_bloom_decode_amd as tb
 
+    import dataclasses
     wl = bi.WORKLOADS[args.workload]
     m = wl.model if args.layers is None else wl.model.truncated(args.layers)
+    if m.weight_dtype != "f32":
+        m = dataclasses.replace(m, activations=args.act)
     B = args.batch
     P = wl.prompt_len
     n_new = args.new_tokens or wl.new_tokens
     torch.cuda.set_device(0)
 
     t0 = time.perf_counter()
-    dw = upload_weights(m)
     cfg = tb.make_config(m)
+    dw = device_weights(m, cfg)
     prompt, valid = bi.prompts(m, B, P)
     tok = torch.from_numpy(prompt).cuda()
     vl = torch.from_numpy(valid).cuda()
@@ -462,12 +495,16 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if m.weight_dtype == "bf16" else ("int8-w/bf16" if m.weight_dtype == "int8" else "f32"),
+        "dtype": (("bf16" if m.weight_dtype == "bf16" else "int8")
+                  + (" weights, f32 activations and KV" if m.act_dtype == "f32"
+                     else " weights, bf16 activations and KV")) if m.weight_dtype != "f32"
+                 else "f32",
         "data": "synthetic (seeded random weights and prompt ids)",
         "config": {"workload": m.name, "batch": B, "prompt_len": P, "new_tokens": n_new,
                    "layers": m.n_layer, "hidden": m.hidden, "heads_local": m.n_head_local,
                    "heads_total": m.n_head_total, "ffn_local": m.ffn, "vocab": m.vocab,
-                   "weights": m.weight_dtype, "kv_cache": True, "greedy": not args.sample,
+                   "weights": m.weight_dtype, "activations": m.act_dtype,
+                   "kv_cache": m.act_dtype, "greedy": not args.sample,
                    "parallelism": "none (1 GPU)", "loop": args.loop,
                    "tokens": "sampled (temperature 0.8, top-p 0.9)" if args.sample else "greedy"},
         "tokens_per_s": round(B * n_new / (ms_per_step * 1e-3), 2),

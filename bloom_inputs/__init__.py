@@ -160,6 +160,8 @@ class ModelShape:
     weight_dtype: str       # 'f32' | 'bf16' | 'int8'
     embed_ln: bool = True
     ln_eps: float = 1e-5
+    activations: str = "auto"   # 'auto' (float32 for f32 weights, else bf16) | 'f32' | 'bf16'
+    init_std: float = 0.02      # standard deviation of the synthetic weights
 
     @property
     def param_dtype(self) -> str:
@@ -168,7 +170,14 @@ class ModelShape:
 
     @property
     def act_dtype(self) -> str:
+        """Type of the stored activations and of the KV cache."""
+        if self.activations != "auto":
+            return self.activations
         return "f32" if self.weight_dtype == "f32" else "bf16"
+
+    @property
+    def kv_bytes(self) -> int:
+        return 4 if self.act_dtype == "f32" else 2
 
     @property
     def qkv_rows(self) -> int:
@@ -291,13 +300,14 @@ def tensor(m: ModelShape, name: str, layer: Optional[int] = None, seed: int = SE
     if name.startswith("s_"):
         if m.weight_dtype != "int8":
             raise KeyError(f"{name}: row scales exist only for int8 weights")
-        return row_scales_f16(seed, tid, shape[0], INT8_S0)
+        s0 = m.init_std / float(np.sqrt((255.0 ** 2 - 1.0) / 12.0))
+        return row_scales_f16(seed, tid, shape[0], s0)
     if name.startswith("w_") or name == "embed":
         kind = m.weight_dtype if name.startswith("w_") else m.param_dtype
     else:
         kind = m.param_dtype
     mean = 1.0 if name.endswith("_g") else 0.0
-    return normal(seed, tid, shape, INIT_STD, mean=mean, kind=kind, out=out)
+    return normal(seed, tid, shape, m.init_std, mean=mean, kind=kind, out=out)
 
 
 def layer_field_names(m: ModelShape) -> tuple:

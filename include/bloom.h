@@ -35,16 +35,28 @@
  *     narrow), BLOOM_EWORKSPACE (workspace too small), BLOOM_EHIP (a HIP call
  *     failed).  On any error nothing is launched and no host-side state changes.
  *   - A batch of 0 rows is a valid no-op.
- *   - Concurrent calls must use distinct KV caches and workspaces.
+ *   - Calls are re-entrant: concurrent calls (from several threads, on one or several
+ *     GPUs) are safe when they use distinct KV caches and workspaces.  The library's
+ *     own process-wide state (per-device kernel attributes, the graph-capture stream,
+ *     the launch timer) is guarded by locks; the launch timer is one process-wide
+ *     record, so concurrent timed calls share it.  bloom_sample_tokens_static shares
+ *     one scratch array per GPU (see there).
  *
  * Data types
- *   - weight_dtype BLOOM_F32: all tensors float32 (a generic, unoptimised path).
- *   - weight_dtype BLOOM_BF16: linear weights, embedding, biases, LayerNorm
- *     parameters, activations and the KV cache are bf16; the residual stream,
- *     LayerNorm statistics, GEMM accumulation, softmax and logits are float32.
+ *   - weight_dtype BLOOM_F32: all tensors float32 (a generic, unoptimised path);
+ *     act_dtype and kv_dtype must be BLOOM_F32.
+ *   - weight_dtype BLOOM_BF16: linear weights, embedding, biases and LayerNorm
+ *     parameters are bf16; the residual stream, LayerNorm statistics, GEMM
+ *     accumulation, softmax and logits are float32.
  *   - weight_dtype BLOOM_INT8_ROWSCALE: as BF16, except the four per-layer linear
  *     weights are int8 [out][in] with one fp16 scale per output row in s_*:
- *     W[r][k] = s[r] * q[r][k] (weight-only; activations stay bf16).
+ *     W[r][k] = s[r] * q[r][k] (weight-only).
+ *   - act_dtype (BF16 / INT8_ROWSCALE weights): the activations the linears read
+ *     (LayerNorm outputs, attention output, GeLU output) are held as bf16
+ *     (BLOOM_BF16), or carry float32 values (BLOOM_F32: float32 operands of the
+ *     vector-ALU GEMV; for the MFMA GEMM two bf16 planes hi + lo, each multiplied with
+ *     the weights, which keeps the product to ~2^-17 of the float32 one).  kv_dtype
+ *     must equal act_dtype: the KV cache holds keys and values in that type.
  *
  * Layouts (all row-major, C order)
  *   embed            [vocab][hidden]             also the LM head (tied embeddings)
@@ -95,6 +107,8 @@ typedef struct bloom_config {
   int32_t weight_dtype; /* enum bloom_dtype */
   int32_t embed_ln;     /* 1: LayerNorm right after the embedding gather */
   float ln_eps;         /* LayerNorm epsilon (biased variance) */
+  int32_t act_dtype;    /* BLOOM_BF16 or BLOOM_F32 (see Data types) */
+  int32_t kv_dtype;     /* KV cache element type: equal to act_dtype */
 } bloom_config;
 
 /* Device pointers of one decoder layer.  s_* are the int8 row scales (fp16) and must be
@@ -118,18 +132,48 @@ typedef struct bloom_weights {
 } bloom_weights;
 
 /* KV cache.  k and v are caller-owned device buffers of
- * n_layer * max_batch * n_head_local * max_len * head_dim elements of the activation
- * type (float32 for F32 models, bf16 otherwise).  len and prompt_len are host-side:
- * bloom_prefill sets prompt_len and len = prompt_len; bloom_decode_step writes slot
- * len and then increments it.  Slot j holds absolute position j of every row (left
+ * n_layer * max_batch * n_head_local * max_len * head_dim elements of kv_dtype
+ * (float32 or bf16).  len and prompt_len are host-side: bloom_prefill sets prompt_len
+ * and len = prompt_len; bloom_decode_step writes slot len and then increments it, and
+ * its capacity check uses len.  Slot j holds absolute position j of every row (left
  * padding slots are written but never attended).  A caller may reset len to 0.
- * max_len is at most 2^20. */
+ * max_len is at most 2^20.
+ * d_len (device int32 [1], 4-byte aligned, nullable) is the same length kept in device
+ * memory ("DeepSpeed Inference ...", Section III.D: the forward is captured once as a
+ * graph and replayed): bloom_prefill sets *d_len = prompt_len on the device,
+ * bloom_generate sets it to the final length, and bloom_decode_step reads the step's
+ * position from *d_len (not from len) and advances it by one on the device, so a
+ * caller may capture one bloom_decode_step call in a graph and replay it.  Replays do
+ * not advance the host-side len; the device guards the cache: a step that finds
+ * *d_len == max_len writes no slot, attends over slots [.., max_len - 1], leaves
+ * *d_len at max_len, and its outputs are undefined. */
 typedef struct bloom_kv_cache {
   void *k, *v;
   int32_t max_batch, max_len;
   int32_t len;
   int32_t prompt_len;
+  int32_t *d_len;
 } bloom_kv_cache;
+
+/* Seeded synthetic weights, written on the GPU into the caller's buffers behind w (the
+ * const pointers of bloom_weights are written through here).  Specification: every
+ * element is a pure function of (seed, tensor id, flat row-major index i):
+ *   key = SM(seed << 32 xor id), r = SM(key + i), with SM the SplitMix64 finaliser
+ *   (Steele, Lea and Flood, "Fast splittable pseudorandom number generators", 2014);
+ *   normal: z = (r & 0xffff) + (r >> 16 & 0xffff) + (r >> 32 & 0xffff) + (r >> 48)
+ *     - 131070 (Irwin-Hall of four 16-bit uniforms, centred), v = mean + fp32(z) * c with
+ *     c = fp32(sigma / sqrt((65536^2 - 1) / 3)), float32 round-to-nearest-even steps (no
+ *     fused multiply-add), stored as float32 (F32 models) or bf16 (nearest even);
+ *   int8 weights: r mod 255 - 127; fp16 row scales: fp16 of
+ *     fp32(sigma / sqrt((255^2 - 1) / 12)) * (0.5 + (r >> 40) * 2^-24) in float32.
+ * Tensor ids: embed 1, emb_ln_g 2, emb_ln_b 3, lnf_g 4, lnf_b 5; layer l: 1024 + 16 l +
+ * the field's index in (ln1_g, ln1_b, w_qkv, b_qkv, w_dense, b_dense, ln2_g, ln2_b,
+ * w_up, b_up, w_down, b_down, s_qkv, s_dense, s_up, s_down).  LayerNorm gammas (*_g)
+ * have mean 1, everything else mean 0; linear weights and the embedding N(0, sigma),
+ * biases and betas N(0, sigma).  Asynchronous on `stream`; EINVAL for a bad config,
+ * missing pointers or sigma < 0. */
+int bloom_init_weights(const bloom_config *cfg, const bloom_weights *w, uint64_t seed,
+                       double sigma, void *stream);
 
 /* Human-readable text for a status code. */
 const char *bloom_status_string(int status);
@@ -167,6 +211,8 @@ int bloom_prefill(const bloom_config *cfg, const bloom_weights *w, bloom_kv_cach
  * KV slot kv->len of every layer, attends over slots [prompt_len - valid_len[b],
  * kv->len], writes the greedy next token to d_next_tokens and optionally the
  * final-LayerNorm state to d_hidden_out [batch][hidden], then increments kv->len.
+ * With kv->d_len set, the position is *d_len instead (read on the device, advanced by
+ * one on the device at the end of the step), so the call can be captured in a graph.
  * As in bloom_prefill, d_next_tokens may be NULL when d_hidden_out is not (no LM head).
  * ECAPACITY if kv->len >= kv->max_len or batch > kv->max_batch; EINVAL if
  * bloom_prefill has not run (kv->prompt_len <= 0). */

@@ -39,13 +39,13 @@ def test_status_strings():
 
 
 def test_struct_layout_matches_header():
-    # 10 int32 + 1 float; 16 pointers; 5 pointers + 1 pointer; 2 pointers + 4 int32;
-    # 2 int32 + 7 pointers + 1 size_t
+    # 12 int32 + 1 float; 16 pointers; 5 pointers + 1 pointer; 2 pointers + 4 int32 +
+    # 1 pointer; 2 int32 + 7 pointers + 1 size_t
     assert ctypes.sizeof(tb.bloom_gen_control) == 8 + 7 * 8 + 8
-    assert ctypes.sizeof(tb.bloom_config) == 44
+    assert ctypes.sizeof(tb.bloom_config) == 52
     assert ctypes.sizeof(tb.bloom_layer_weights) == 16 * 8
     assert ctypes.sizeof(tb.bloom_weights) == 6 * 8
-    assert ctypes.sizeof(tb.bloom_kv_cache) == 2 * 8 + 4 * 4
+    assert ctypes.sizeof(tb.bloom_kv_cache) == 2 * 8 + 4 * 4 + 8
 
 
 def _cfg(**kw):

@@ -32,7 +32,7 @@ class bloom_config(ctypes.Structure):
     _fields_ = [("n_layer", _i32), ("hidden", _i32), ("n_head_total", _i32),
                 ("head_offset", _i32), ("n_head_local", _i32), ("head_dim", _i32),
                 ("ffn", _i32), ("vocab", _i32), ("weight_dtype", _i32), ("embed_ln", _i32),
-                ("ln_eps", ctypes.c_float)]
+                ("ln_eps", ctypes.c_float), ("act_dtype", _i32), ("kv_dtype", _i32)]
 
 
 LAYER_FIELDS = ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "s_qkv", "w_dense", "b_dense", "s_dense",
@@ -51,7 +51,7 @@ class bloom_weights(ctypes.Structure):
 
 class bloom_kv_cache(ctypes.Structure):
     _fields_ = [("k", _c_void_p), ("v", _c_void_p), ("max_batch", _i32), ("max_len", _i32),
-                ("len", _i32), ("prompt_len", _i32)]
+                ("len", _i32), ("prompt_len", _i32), ("d_len", _c_void_p)]
 
 
 class bloom_gen_control(ctypes.Structure):
@@ -106,6 +106,8 @@ def _load():
     lib.bloom_sample_tokens.argtypes = [vp, _i32, _i32, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                         vp]
     lib.bloom_sample_workspace_bytes.argtypes = [_i32, _i32, P(ctypes.c_size_t)]
+    lib.bloom_init_weights.argtypes = [P(bloom_config), P(bloom_weights), ctypes.c_uint64,
+                                       ctypes.c_double, vp]
     lib.bloom_sample_tokens_static.argtypes = [vp, _i32, _i32, vp, vp, vp, vp, vp]
     lib.bloom_sample_scratch_limit.argtypes = [_i32, _i32, P(_i32), P(ctypes.c_size_t)]
     lib.bloom_timer_enable.argtypes = [_i32]
@@ -116,6 +118,7 @@ def _load():
                  "alibi_masked_softmax", "kv_cache_append", "kv_cache_compact",
                  "bloom_lm_logits", "bloom_sample_tokens", "bloom_sample_workspace_bytes",
                  "bloom_sample_tokens_static", "bloom_sample_scratch_limit",
+                 "bloom_init_weights",
                  "bloom_timer_enable",
                  "bloom_timer_disable", "bloom_timer_read", "bloom_timer_pause"):
         getattr(lib, name).restype = ctypes.c_int
@@ -353,11 +356,21 @@ def _nbytes(t) -> int:
 # ---------------------------------------------------------------------------
 
 def make_config(shape) -> bloom_config:
-    """bloom_config from any object with the shape attributes (n_layer, hidden, ...)."""
+    """bloom_config from any object with the shape attributes (n_layer, hidden, ...;
+    act_dtype 'f32' or 'bf16', which also sets the KV-cache type)."""
+    act = DTYPE_CODES[getattr(shape, "act_dtype", "f32" if shape.weight_dtype == "f32"
+                              else "bf16")]
     return bloom_config(shape.n_layer, shape.hidden, shape.n_head_total, shape.head_offset,
                         shape.n_head_local, shape.head_dim, shape.ffn, shape.vocab,
                         DTYPE_CODES[shape.weight_dtype], int(bool(shape.embed_ln)),
-                        float(shape.ln_eps))
+                        float(shape.ln_eps), act, act)
+
+
+def bloom_init_weights(cfg, weights, seed: int = 0, sigma: float = 0.02, stream=None):
+    """Fill the weights' device buffers with the seeded synthetic values (bloom.h)."""
+    w = weights.struct if hasattr(weights, "struct") else weights
+    _check(lib.bloom_init_weights(ctypes.byref(cfg), ctypes.byref(w), seed, sigma,
+                                  _stream(stream)), "bloom_init_weights")
 
 
 def to_device(a, device="cuda"):
@@ -393,12 +406,13 @@ class DeviceWeights:
 
 
 class KVCache:
-    """Caller-owned KV cache buffers ([n_layer][max_batch][H][max_len][d]) and the struct."""
+    """Caller-owned KV cache buffers ([n_layer][max_batch][H][max_len][d]) and the struct.
+    device_len=True also keeps the length in device memory (bloom_kv_cache.d_len)."""
 
     def __init__(self, cfg: bloom_config, max_batch: int, max_len: int, device="cuda",
-                 fill: Optional[float] = None):
+                 fill: Optional[float] = None, device_len: bool = False):
         import torch
-        dt = torch.float32 if cfg.weight_dtype == BLOOM_F32 else torch.bfloat16
+        dt = torch.float32 if cfg.kv_dtype == BLOOM_F32 else torch.bfloat16
         shape = (cfg.n_layer, max_batch, cfg.n_head_local, max_len, cfg.head_dim)
         if fill is None:
             self.k = torch.empty(shape, dtype=dt, device=device)
@@ -406,7 +420,9 @@ class KVCache:
         else:
             self.k = torch.full(shape, fill, dtype=dt, device=device)
             self.v = torch.full(shape, fill, dtype=dt, device=device)
-        self.struct = bloom_kv_cache(_ptr(self.k), _ptr(self.v), max_batch, max_len, 0, 0)
+        self.d_len = torch.zeros(1, dtype=torch.int32, device=device) if device_len else None
+        self.struct = bloom_kv_cache(_ptr(self.k), _ptr(self.v), max_batch, max_len, 0, 0,
+                                     _ptr(self.d_len))
 
     @property
     def len(self) -> int:

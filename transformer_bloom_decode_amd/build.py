@@ -7,7 +7,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbloom_mi355x.so")
-SOURCES = ["api.cpp", "softmax.hip", "norm.hip", "gemm.hip", "gemv.hip", "attention.hip", "generate.hip", "sample.hip"]
+SOURCES = ["api.cpp", "softmax.hip", "norm.hip", "gemm.hip", "gemv.hip", "attention.hip", "generate.hip", "sample.hip", "init.hip"]
 ARCH = os.environ.get("BLOOM_OFFLOAD_ARCH", "gfx950")
 
 # Packed-fp32 VALU ops stay off: plain float code must not be turned into

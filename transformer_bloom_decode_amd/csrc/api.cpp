@@ -13,7 +13,9 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "../../include/bloom.h"
@@ -47,7 +49,12 @@ struct WsPlan {
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-int act_bytes(const bloom_config *c) { return c->weight_dtype == BLOOM_F32 ? 4 : 2; }
+// Activations carrying float32 values take 4 bytes per element (float32, or the two bf16
+// planes the MFMA GEMM reads); bf16 activations 2.
+bool act_f32(const bloom_config *c) { return c->act_dtype == BLOOM_F32; }
+int act_bytes(const bloom_config *c) { return act_f32(c) ? 4 : 2; }
+bool kv_f32(const bloom_config *c) { return c->kv_dtype == BLOOM_F32; }
+int kv_bytes(const bloom_config *c) { return kv_f32(c) ? 4 : 2; }
 int wtype(const bloom_config *c) {
   return c->weight_dtype == BLOOM_F32 ? WT_F32 : (c->weight_dtype == BLOOM_BF16 ? WT_BF16 : WT_INT8);
 }
@@ -85,7 +92,8 @@ WsPlan plan_ws(const bloom_config *c, int batch, int tokens_per_row) {
                             {c->hidden, c->ffn}};
     for (const int mrows : {(int)M, batch})
       for (const auto &nk : dims)
-        part = std::max(part, linear_partial_bytes(plan_linear(wdt, mrows, nk[0], nk[1], false)));
+        part = std::max(part, linear_partial_bytes(
+                                  plan_linear(wdt, mrows, nk[0], nk[1], false, act_f32(c))));
   }
   p.part = take(part);
   p.total = off;
@@ -105,6 +113,11 @@ int check_config(const bloom_config *c) {
   if (c->weight_dtype != BLOOM_F32 && c->weight_dtype != BLOOM_BF16 &&
       c->weight_dtype != BLOOM_INT8_ROWSCALE)
     return BLOOM_EDTYPE;
+  // activations and the KV cache: float32 or bf16 (float32 only for float32 weights);
+  // the cache holds the activation type
+  if (c->act_dtype != BLOOM_F32 && c->act_dtype != BLOOM_BF16) return BLOOM_EDTYPE;
+  if (c->weight_dtype == BLOOM_F32 && c->act_dtype != BLOOM_F32) return BLOOM_EDTYPE;
+  if (c->kv_dtype != c->act_dtype) return BLOOM_EDTYPE;
   if (c->weight_dtype != BLOOM_F32) {
     const int hd = c->n_head_local * c->head_dim;
     if (c->hidden % 64 || c->ffn % 64 || hd % 64) return BLOOM_EINVAL;
@@ -132,6 +145,7 @@ int check_weights(const bloom_config *c, const bloom_weights *w) {
 int check_kv(const bloom_config *c, const bloom_kv_cache *kv) {
   (void)c;
   if (!kv || !kv->k || !kv->v || kv->max_batch <= 0 || kv->max_len <= 0) return BLOOM_EINVAL;
+  if (((uintptr_t)kv->d_len & 3) != 0) return BLOOM_EINVAL;
   if (kv->max_len > kMaxLen) return BLOOM_EINVAL;
   if (kv->len < 0 || kv->len > kv->max_len || kv->prompt_len < 0) return BLOOM_EINVAL;
   return BLOOM_OK;
@@ -140,6 +154,9 @@ int check_kv(const bloom_config *c, const bloom_kv_cache *kv) {
 // ---------------------------------------------------------------------------
 // launch timer
 // ---------------------------------------------------------------------------
+// A process-wide measurement aid: its state is guarded by g_timer_mu, so calls from
+// several threads stay safe, but their launches then share (and interleave in) one
+// record list.
 struct Timer {
   bool on = false;
   bool paused = false;
@@ -149,6 +166,7 @@ struct Timer {
   std::vector<double> bytes;
   int used = 0;
 } g_timer;
+std::mutex g_timer_mu;
 
 void destroy_timer_events() {
   for (hipEvent_t e : g_timer.start) (void)hipEventDestroy(e);
@@ -172,9 +190,13 @@ int kernel_class(const LinearPlan &p) {
 // timer is on: its first kernel is launched with the timer's event pair attached.
 template <typename F>
 hipError_t timed(int cls, double wbytes, hipStream_t st, F &&launch) {
-  (void)st;
+  if (!g_timer.on) return launch();   // the common case: no lock taken
+  // launches captured into a graph (the library's own or a caller's) are never timed
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cap) != hipSuccess) cap = hipStreamCaptureStatusActive;
+  std::lock_guard<std::mutex> lock(g_timer_mu);
   const bool on = g_timer.on && !g_timer.paused && !g_timer.capturing &&
-                  g_timer.used < (int)g_timer.start.size();
+                  cap == hipStreamCaptureStatusNone && g_timer.used < (int)g_timer.start.size();
   if (on) g_launch_events = LaunchEvents{g_timer.start[g_timer.used], g_timer.stop[g_timer.used]};
   hipError_t err = launch();
   g_launch_events = LaunchEvents{};
@@ -198,8 +220,10 @@ hipError_t timed_linear(int wdt, const LinearPlan &p, const void *X, const void 
 // decode step; created on first use, kept for the life of the process.
 hipStream_t capture_stream() {
   static hipStream_t side[64] = {};
+  static std::mutex mu;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
   if (!side[dev] && hipStreamCreateWithFlags(&side[dev], hipStreamNonBlocking) != hipSuccess)
     side[dev] = nullptr;
   return side[dev];
@@ -208,12 +232,15 @@ hipStream_t capture_stream() {
 // ---------------------------------------------------------------------------
 // one forward pass over `tpr` tokens per row
 // ---------------------------------------------------------------------------
+// d_pos (nullable): device position of the first row of each sequence (a decode step
+// replayed from a graph, or the KV length a caller keeps on the device); else pos_base.
 int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *kv, int batch,
                 int tpr, int pos_base, int prompt_len, const int32_t *d_tokens,
                 const int32_t *d_valid, int32_t *d_next, float *d_hidden, char *ws,
                 hipStream_t st, const int *d_pos = nullptr, float *d_logits = nullptr) {
   const WsPlan wp = plan_ws(c, batch, tpr);
   const bool f32 = c->weight_dtype == BLOOM_F32;
+  const bool af32 = act_f32(c);
   const int wdt = wtype(c);
   const int M = batch * tpr;
   const int h = c->hidden, H = c->n_head_local, d = c->head_dim, F = c->ffn;
@@ -221,7 +248,6 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
   const size_t wb = c->weight_dtype == BLOOM_F32 ? 4 : (c->weight_dtype == BLOOM_BF16 ? 2 : 1);
   const size_t pb = f32 ? 4 : 2;
   const size_t sb = c->weight_dtype == BLOOM_INT8_ROWSCALE ? 2 : 0;
-  const size_t act = act_bytes(c);
   auto wbytes = [&](int N, int K) { return (double)((size_t)N * K * wb + (size_t)N * (pb + sb)); };
 
   float *x = (float *)(ws + wp.x);
@@ -238,11 +264,14 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
                                 c->vocab, c->embed_ln, c->ln_eps, st);
   if (err != hipSuccess) return hip_fail(err);
 
-  const size_t layer_stride = (size_t)kv->max_batch * H * kv->max_len * d * act;
-  const LinearPlan p_qkv = plan_linear(wdt, M, 3 * hd, h, false);
-  const LinearPlan p_dense = plan_linear(wdt, M, h, hd, false);
-  const LinearPlan p_up = plan_linear(wdt, M, F, h, false);
-  const LinearPlan p_down = plan_linear(wdt, M, h, F, false);
+  const size_t layer_stride = (size_t)kv->max_batch * H * kv->max_len * d * kv_bytes(c);
+  const LinearPlan p_qkv = plan_linear(wdt, M, 3 * hd, h, false, af32);
+  const LinearPlan p_dense = plan_linear(wdt, M, h, hd, false, af32);
+  const LinearPlan p_up = plan_linear(wdt, M, F, h, false, af32);
+  const LinearPlan p_down = plan_linear(wdt, M, h, F, false, af32);
+  // every activation is written in the form its consumer reads
+  const int fmt_qkv = plan_x_fmt(p_qkv), fmt_dense = plan_x_fmt(p_dense);
+  const int fmt_up = plan_x_fmt(p_up), fmt_down = plan_x_fmt(p_down);
 
   // K-split dense / down projections reduce their partials in the kernel that also adds
   // bias and residual and runs the next LayerNorm (LN2 after dense, the next layer's LN1
@@ -260,7 +289,8 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
     void *vc = (char *)kv->v + l * layer_stride;
 
     if (!ln1_done && !ln_in_gemv) {
-      err = launch_layernorm(f32, x, 1, 0, L.ln1_g, L.ln1_b, xa, nullptr, M, h, c->ln_eps, st);
+      err = launch_layernorm(f32, x, 1, 0, L.ln1_g, L.ln1_b, xa, fmt_qkv, nullptr, M, h,
+                             c->ln_eps, st);
       if (err != hipSuccess) return hip_fail(err);
     }
     ln1_done = false;
@@ -270,19 +300,21 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
     e.bias = L.b_qkv;
     e.scale = (const uint16_t *)L.s_qkv;
     e.q = q; e.kc = kc; e.vc = vc;
+    e.kv_fmt = kv_f32(c) ? AF_F32 : AF_BF16;
     e.H = H; e.d = d; e.max_len = kv->max_len;
     e.pos_base = pos_base; e.pos_dev = d_pos; e.rows_per_seq = tpr;
     e.q_scale = 1.0f / sqrtf((float)d);
     if (ln_in_gemv)
       err = timed(kernel_class(p_qkv), wbytes(3 * hd, h), st, [&] {
-        return launch_gemv_ln(wdt, 3 * hd, h, x, L.ln1_g, L.ln1_b, c->ln_eps, L.w_qkv, e, st);
+        return launch_gemv_ln(wdt, af32, 3 * hd, h, x, L.ln1_g, L.ln1_b, c->ln_eps, L.w_qkv, e,
+                              st);
       });
     else
       err = timed_linear(wdt, p_qkv, xa, L.w_qkv, part, e, st, wbytes(3 * hd, h));
     if (err != hipSuccess) return hip_fail(err);
 
-    err = launch_attention(f32, q, kc, vc, d_valid, o, M, H, d, kv->max_len, c->n_head_total,
-                           c->head_offset, tpr, pos_base, d_pos, prompt_len, st);
+    err = launch_attention(kv_f32(c), q, kc, vc, d_valid, o, fmt_dense, M, H, d, kv->max_len,
+                           c->n_head_total, c->head_offset, tpr, pos_base, d_pos, prompt_len, st);
     if (err != hipSuccess) return hip_fail(err);
 
     EpiParams r{};
@@ -296,9 +328,10 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
 
     if (fuse_dense)
       err = launch_splitk_resid_ln(part, p_dense.splits, M, L.s_dense, L.b_dense, x, L.ln2_g,
-                                   L.ln2_b, xa, h, c->ln_eps, st);
+                                   L.ln2_b, xa, fmt_up, h, c->ln_eps, st);
     else if (!ln_in_gemv)
-      err = launch_layernorm(f32, x, 1, 0, L.ln2_g, L.ln2_b, xa, nullptr, M, h, c->ln_eps, st);
+      err = launch_layernorm(f32, x, 1, 0, L.ln2_g, L.ln2_b, xa, fmt_up, nullptr, M, h,
+                             c->ln_eps, st);
     if (err != hipSuccess) return hip_fail(err);
 
     EpiParams g{};
@@ -306,9 +339,11 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
     g.bias = L.b_up;
     g.scale = (const uint16_t *)L.s_up;
     g.out = u; g.ld = F;
+    g.out_fmt = fmt_down;
+    g.plane = (size_t)M * F;
     if (ln_in_gemv && !fuse_dense)
       err = timed(kernel_class(p_up), wbytes(F, h), st, [&] {
-        return launch_gemv_ln(wdt, F, h, x, L.ln2_g, L.ln2_b, c->ln_eps, L.w_up, g, st);
+        return launch_gemv_ln(wdt, af32, F, h, x, L.ln2_g, L.ln2_b, c->ln_eps, L.w_up, g, st);
       });
     else
       err = timed_linear(wdt, p_up, xa, L.w_up, part, g, st, wbytes(F, h));
@@ -325,7 +360,7 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
     if (fuse_down) {
       const bloom_layer_weights &N1 = w->layers[l + 1];
       err = launch_splitk_resid_ln(part, p_down.splits, M, L.s_down, L.b_down, x, N1.ln1_g,
-                                   N1.ln1_b, xa, h, c->ln_eps, st);
+                                   N1.ln1_b, xa, fmt_qkv, h, c->ln_eps, st);
       if (err != hipSuccess) return hip_fail(err);
       ln1_done = true;
     }
@@ -336,40 +371,44 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
   const int nblk = wp.lm_blocks;
   const int wdt_lm = f32 ? WT_F32 : WT_BF16;  // the embedding is never int8
   const double lm_bytes = (double)c->vocab * h * pb;
-  err = launch_layernorm(f32, x, tpr, tpr - 1, w->lnf_g, w->lnf_b, af, d_hidden, batch, h,
-                         c->ln_eps, st);
-  if (err != hipSuccess) return hip_fail(err);
-  if (d_logits) {
-    // the LM head's float32 logits [batch][vocab] instead of its argmax (sampling), with
-    // the greedy head's plan, so a greedy row of the sampler ranks the same values
-    for (int r0 = 0; r0 < batch; r0 += 128) {
-      const int rows = std::min(128, batch - r0);
-      EpiParams e{};
-      e.mode = EPI_STORE;
-      e.out = d_logits + (size_t)r0 * c->vocab;
-      e.ld = c->vocab;
-      const LinearPlan p_lm = plan_linear(wdt_lm, rows, c->vocab, h, true);
-      err = timed_linear(wdt_lm, p_lm, (const char *)af + (size_t)r0 * h * act, w->embed, part,
-                         e, st, lm_bytes);
+  const bool lm_head = d_logits || d_next;
+  if (!lm_head) {
+    err = launch_layernorm(f32, x, tpr, tpr - 1, w->lnf_g, w->lnf_b, af, f32 ? AF_F32 : AF_BF16,
+                           d_hidden, batch, h, c->ln_eps, st);
+    return err == hipSuccess ? BLOOM_OK : hip_fail(err);
+  }
+  const size_t act = act_bytes(c);
+  for (int r0 = 0; r0 < batch; r0 += 128) {
+    // the LM head runs on chunks of up to 128 rows; the final LayerNorm writes each
+    // chunk in the form its plan reads (two bf16 planes: each chunk its own pair)
+    const int rows = std::min(128, batch - r0);
+    const LinearPlan p_lm = plan_linear(wdt_lm, rows, c->vocab, h, true, af32);
+    void *X = (char *)af + (size_t)r0 * h * act;
+    err = launch_layernorm(f32, x + (size_t)r0 * tpr * h, tpr, tpr - 1, w->lnf_g, w->lnf_b, X,
+                           plan_x_fmt(p_lm), d_hidden ? d_hidden + (size_t)r0 * h : nullptr, rows,
+                           h, c->ln_eps, st);
+    if (err != hipSuccess) return hip_fail(err);
+    EpiParams a{};
+    if (d_logits) {
+      // the LM head's float32 logits [batch][vocab] instead of its argmax (sampling), with
+      // the greedy head's plan, so a greedy row of the sampler ranks the same values
+      a.mode = EPI_STORE;
+      a.out = d_logits + (size_t)r0 * c->vocab;
+      a.ld = c->vocab;
+    } else {
+      a.mode = EPI_ARGMAX;
+      a.am_val = amv + (size_t)r0 * nblk;
+      a.am_idx = ami + (size_t)r0 * nblk;
+      a.am_stride = nblk;
+    }
+    err = timed_linear(wdt_lm, p_lm, X, w->embed, part, a, st, lm_bytes);
+    if (err != hipSuccess) return hip_fail(err);
+    if (!d_logits) {
+      // this chunk's kernel wrote one partial per row per weight tile
+      err = launch_argmax_merge(a.am_val, a.am_idx, nblk, argmax_partials_per_row(p_lm), rows,
+                                d_next + r0, st);
       if (err != hipSuccess) return hip_fail(err);
     }
-    return BLOOM_OK;
-  }
-  for (int r0 = 0; d_next && r0 < batch; r0 += 128) {
-    const int rows = std::min(128, batch - r0);
-    EpiParams a{};
-    a.mode = EPI_ARGMAX;
-    a.am_val = amv + (size_t)r0 * nblk;
-    a.am_idx = ami + (size_t)r0 * nblk;
-    a.am_stride = nblk;
-    const LinearPlan p_lm = plan_linear(wdt_lm, rows, c->vocab, h, true);
-    err = timed_linear(wdt_lm, p_lm, (const char *)af + (size_t)r0 * h * act, w->embed, part, a,
-                       st, lm_bytes);
-    if (err != hipSuccess) return hip_fail(err);
-    // this chunk's kernel wrote one partial per row per weight tile
-    err = launch_argmax_merge(a.am_val, a.am_idx, nblk, argmax_partials_per_row(p_lm), rows,
-                              d_next + r0, st);
-    if (err != hipSuccess) return hip_fail(err);
   }
   return BLOOM_OK;
 }
@@ -417,6 +456,11 @@ int bloom_prefill(const bloom_config *cfg, const bloom_weights *w, bloom_kv_cach
   clear_stale_hip_error();
   s = run_forward(cfg, w, kv, batch, prompt_len, 0, prompt_len, d_tokens, d_valid_len,
                   d_next_tokens, d_hidden_out, (char *)d_ws, (hipStream_t)stream);
+  if (s == BLOOM_OK && kv->d_len) {
+    const hipError_t e = launch_len_update(kv->d_len, prompt_len, 0, kv->max_len,
+                                           (hipStream_t)stream);
+    if (e != hipSuccess) s = hip_fail(e);
+  }
   if (s == BLOOM_OK) {
     kv->prompt_len = prompt_len;
     kv->len = prompt_len;
@@ -439,8 +483,14 @@ int bloom_decode_step(const bloom_config *cfg, const bloom_weights *w, bloom_kv_
   if (!d_tokens || !d_valid_len || !d_ws || (!d_next_tokens && !d_hidden_out)) return BLOOM_EINVAL;
   if (ws_bytes < plan_ws(cfg, batch, 1).total) return BLOOM_EWORKSPACE;
   clear_stale_hip_error();
+  // with a device-resident length the step reads its position from it and advances it
+  // (so a captured step can be replayed); the host count follows the calls
   s = run_forward(cfg, w, kv, batch, 1, kv->len, kv->prompt_len, d_tokens, d_valid_len,
-                  d_next_tokens, d_hidden_out, (char *)d_ws, (hipStream_t)stream);
+                  d_next_tokens, d_hidden_out, (char *)d_ws, (hipStream_t)stream, kv->d_len);
+  if (s == BLOOM_OK && kv->d_len) {
+    const hipError_t e = launch_len_update(kv->d_len, -1, 1, kv->max_len, (hipStream_t)stream);
+    if (e != hipSuccess) s = hip_fail(e);
+  }
   if (s == BLOOM_OK) kv->len += 1;
   return s;
 }
@@ -517,6 +567,9 @@ int bloom_generate(const bloom_config *cfg, const bloom_weights *w, bloom_kv_cac
     kv->len += 1;
   }
   if (n_new <= 2) {
+    if (kv->d_len &&
+        (err = launch_len_update(kv->d_len, kv->len, 0, kv->max_len, st)) != hipSuccess)
+      return hip_fail(err);
     const hipError_t serr = hipStreamSynchronize(st);
     return serr == hipSuccess ? BLOOM_OK : hip_fail(serr);
   }
@@ -546,6 +599,8 @@ int bloom_generate(const bloom_config *cfg, const bloom_weights *w, bloom_kv_cac
   (void)hipGraphDestroy(graph);
   if (err != hipSuccess) return hip_fail(err);
   for (int t = 2; t < n_new && err == hipSuccess; ++t) err = hipGraphLaunch(exec, st);
+  if (err == hipSuccess && kv->d_len)
+    err = launch_len_update(kv->d_len, prompt_len + n_new - 1, 0, kv->max_len, st);
   // the executable graph is released once its launches have finished
   const hipError_t serr = hipStreamSynchronize(st);
   (void)hipGraphExecDestroy(exec);
@@ -583,10 +638,10 @@ int kv_cache_append(const bloom_config *cfg, bloom_kv_cache *kv, int32_t layer, 
   if (batch == 0 || n_new == 0) return BLOOM_OK;
   if (!d_k || !d_v) return BLOOM_EINVAL;
   clear_stale_hip_error();
-  const size_t act = act_bytes(cfg);
+  const size_t kvb = kv_bytes(cfg);
   const size_t layer_stride =
-      (size_t)kv->max_batch * cfg->n_head_local * kv->max_len * cfg->head_dim * act;
-  hipError_t err = launch_kv_append(cfg->weight_dtype == BLOOM_F32, d_k, d_v,
+      (size_t)kv->max_batch * cfg->n_head_local * kv->max_len * cfg->head_dim * kvb;
+  hipError_t err = launch_kv_append(kv_f32(cfg), d_k, d_v,
                                     (char *)kv->k + layer * layer_stride,
                                     (char *)kv->v + layer * layer_stride, batch,
                                     cfg->n_head_local, n_new, cfg->head_dim, kv->max_len, pos,
@@ -608,7 +663,7 @@ int kv_cache_compact(const bloom_config *cfg, bloom_kv_cache *kv, int32_t batch,
   clear_stale_hip_error();
   const hipError_t err = launch_kv_compact(kv->k, kv->v, cfg->n_layer, cfg->n_head_local,
                                            kv->max_batch, kv->max_len, cfg->head_dim,
-                                           act_bytes(cfg), kv->len, keep, n_keep,
+                                           kv_bytes(cfg), kv->len, keep, n_keep,
                                            (hipStream_t)stream);
   return err == hipSuccess ? BLOOM_OK : hip_fail(err);
 }
@@ -627,14 +682,6 @@ int bloom_lm_logits(const bloom_config *cfg, const bloom_weights *w, int32_t bat
   hipStream_t st = (hipStream_t)stream;
   const bool f32 = cfg->weight_dtype == BLOOM_F32;
   const int h = cfg->hidden;
-  const void *X = d_hidden;
-  if (!f32) {
-    // the same bf16 rounding of the final-LayerNorm state as the greedy LM head's input
-    void *af = (char *)d_ws + wp.af;
-    const hipError_t e = launch_f32_to_bf16(d_hidden, af, (size_t)batch * h, st);
-    if (e != hipSuccess) return hip_fail(e);
-    X = af;
-  }
   const int wdt_lm = f32 ? WT_F32 : WT_BF16;
   const size_t act = act_bytes(cfg);
   float *part = (float *)((char *)d_ws + wp.part);
@@ -644,13 +691,81 @@ int bloom_lm_logits(const bloom_config *cfg, const bloom_weights *w, int32_t bat
     e.mode = EPI_STORE;
     e.out = d_logits + (size_t)r0 * cfg->vocab;
     e.ld = cfg->vocab;
-    // the greedy LM head's plan (never split), so the logits are the ones it ranks
-    const LinearPlan p = plan_linear(wdt_lm, rows, cfg->vocab, h, true);
-    const hipError_t err =
-        launch_linear(wdt_lm, p, (const char *)X + (size_t)r0 * h * act, w->embed, part, e, st);
+    // the greedy LM head's plan (never split) and operand form, so the logits are the
+    // ones it ranks
+    const LinearPlan p = plan_linear(wdt_lm, rows, cfg->vocab, h, true, act_f32(cfg));
+    const float *hr = d_hidden + (size_t)r0 * h;
+    const void *X = hr;
+    if (plan_x_fmt(p) != AF_F32) {
+      void *af = (char *)d_ws + wp.af + (size_t)r0 * h * act;
+      const hipError_t ce = launch_f32_to_act(hr, af, plan_x_fmt(p), (size_t)rows * h, st);
+      if (ce != hipSuccess) return hip_fail(ce);
+      X = af;
+    }
+    const hipError_t err = launch_linear(wdt_lm, p, X, w->embed, part, e, st);
     if (err != hipSuccess) return hip_fail(err);
   }
   return BLOOM_OK;
+}
+
+int bloom_init_weights(const bloom_config *cfg, const bloom_weights *w, uint64_t seed,
+                       double sigma, void *stream) {
+  int s = check_config(cfg);
+  if (s != BLOOM_OK) return s;
+  if ((s = check_weights(cfg, w)) != BLOOM_OK) return s;
+  if (!(sigma >= 0.0) || !(sigma < 1e30)) return BLOOM_EINVAL;
+  clear_stale_hip_error();
+  hipStream_t st = (hipStream_t)stream;
+  auto smix = [](uint64_t z) {
+    z += 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+  };
+  // scales of the specification, computed in double and rounded to float32 once
+  const float nscale = (float)(sigma / std::sqrt((65536.0 * 65536.0 - 1.0) / 3.0));
+  const float s0 = (float)(sigma / std::sqrt((255.0 * 255.0 - 1.0) / 12.0));
+  const int pkind = cfg->weight_dtype == BLOOM_F32 ? 0 : 1;   // float32 or bf16 storage
+  const bool i8 = cfg->weight_dtype == BLOOM_INT8_ROWSCALE;
+  auto fill = [&](const void *p, size_t n, uint64_t tid, int op, int kind, float mean,
+                  float scale) -> hipError_t {
+    InitTensor t{};
+    t.out = const_cast<void *>(p);
+    t.n = n;
+    t.key = smix((seed << 32) ^ tid);
+    t.op = op; t.kind = kind; t.mean = mean; t.scale = scale;
+    return launch_init_tensor(t, st);
+  };
+  auto normal = [&](const void *p, size_t n, uint64_t tid, float mean) {
+    return fill(p, n, tid, 0, pkind, mean, nscale);
+  };
+  const size_t h = cfg->hidden, hd = (size_t)cfg->n_head_local * cfg->head_dim, F = cfg->ffn;
+  hipError_t e = normal(w->embed, (size_t)cfg->vocab * h, 1, 0.f);
+  if (e == hipSuccess && cfg->embed_ln) e = normal(w->emb_ln_g, h, 2, 1.f);
+  if (e == hipSuccess && cfg->embed_ln) e = normal(w->emb_ln_b, h, 3, 0.f);
+  if (e == hipSuccess) e = normal(w->lnf_g, h, 4, 1.f);
+  if (e == hipSuccess) e = normal(w->lnf_b, h, 5, 0.f);
+  for (int l = 0; l < cfg->n_layer && e == hipSuccess; ++l) {
+    const bloom_layer_weights &L = w->layers[l];
+    const uint64_t base = 1024 + 16 * (uint64_t)l;   // tensor ids of layer l, in field order
+    auto mat = [&](const void *p, size_t n, int idx) {
+      return i8 ? fill(p, n, base + idx, 1, 0, 0.f, 0.f) : normal(p, n, base + idx, 0.f);
+    };
+    const struct { const void *p; size_t n; int idx; int what; } t[] = {
+        {L.ln1_g, h, 0, 1},  {L.ln1_b, h, 1, 0},      {L.w_qkv, 3 * hd * h, 2, 2},
+        {L.b_qkv, 3 * hd, 3, 0}, {L.w_dense, h * hd, 4, 2}, {L.b_dense, h, 5, 0},
+        {L.ln2_g, h, 6, 1},  {L.ln2_b, h, 7, 0},      {L.w_up, F * h, 8, 2},
+        {L.b_up, F, 9, 0},   {L.w_down, h * F, 10, 2}, {L.b_down, h, 11, 0},
+        {L.s_qkv, 3 * hd, 12, 3}, {L.s_dense, h, 13, 3}, {L.s_up, F, 14, 3}, {L.s_down, h, 15, 3}};
+    for (const auto &x : t) {
+      if (e != hipSuccess) break;
+      if (x.what == 0) e = normal(x.p, x.n, base + x.idx, 0.f);
+      else if (x.what == 1) e = normal(x.p, x.n, base + x.idx, 1.f);
+      else if (x.what == 2) e = mat(x.p, x.n, x.idx);
+      else if (i8) e = fill(x.p, x.n, base + x.idx, 2, 0, 0.f, s0);
+    }
+  }
+  return e == hipSuccess ? BLOOM_OK : hip_fail(e);
 }
 
 int bloom_sample_workspace_bytes(int32_t batch, int32_t vocab, size_t *bytes) {

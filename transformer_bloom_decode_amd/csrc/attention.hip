@@ -70,7 +70,8 @@ __global__ __launch_bounds__(256) void k_attention(const float *__restrict__ q,
                                                    const TA *__restrict__ kc,
                                                    const TA *__restrict__ vc,
                                                    const int *__restrict__ valid_len,
-                                                   TA *__restrict__ o, int H, int d, int max_len,
+                                                   void *__restrict__ o, int o_fmt,
+                                                   size_t o_plane, int H, int d, int max_len,
                                                    int n_total, int head_off, int rows_per_seq,
                                                    int pos_base, const int *__restrict__ pos_dev,
                                                    int prompt_len) {
@@ -80,12 +81,14 @@ __global__ __launch_bounds__(256) void k_attention(const float *__restrict__ q,
   const int m = blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x;
   const int b = m / rows_per_seq;
-  const int qpos = (pos_dev ? *pos_dev : pos_base) + (m - b * rows_per_seq);
+  // a position read from device memory is clamped to the cache (the host checks the
+  // others): slots at or past max_len are never addressed
+  const int qpos = min((pos_dev ? *pos_dev : pos_base) + (m - b * rows_per_seq), max_len - 1);
   // The K/V loads below address slots 0..qpos directly and do not wait for valid_len:
   // the left-pad slots [0, first) are loaded too (the prompt pass wrote them) and
   // masked in the scores.
   const int vl_in = valid_len[b];
-  TA *out = o + ((size_t)m * H + h) * d;
+  const size_t out0 = ((size_t)m * H + h) * d;
   const int S = qpos + 1;
   const float slope = alibi_slope(n_total, head_off + h);
   const size_t head_base = ((size_t)b * H + h) * (size_t)max_len * d;
@@ -165,7 +168,7 @@ __global__ __launch_bounds__(256) void k_attention(const float *__restrict__ q,
   for (int e = tid; e < d; e += 256) {
     float s = 0.f;
     for (int gg = 0; gg < G; ++gg) s += pv[gg * d + e];
-    out[e] = from_f<TA>(s * inv);
+    act_store(o, o_fmt, out0 + e, o_plane, s * inv);
   }
 }
 
@@ -183,8 +186,9 @@ constexpr int kPromptTileBytes = 16384;   // LDS per K (and per V) tile
 template <typename TA>
 __global__ __launch_bounds__(256) void k_attention_prompt(
     const float *__restrict__ q, const TA *__restrict__ kc, const TA *__restrict__ vc,
-    const int *__restrict__ valid_len, TA *__restrict__ o, int H, int d, int max_len,
-    int n_total, int head_off, int rows_per_seq, int pos_base, int prompt_len, int nchunk) {
+    const int *__restrict__ valid_len, void *__restrict__ o, int o_fmt, size_t o_plane, int H,
+    int d, int max_len, int n_total, int head_off, int rows_per_seq, int pos_base,
+    int prompt_len, int nchunk) {
   __shared__ __attribute__((aligned(16))) unsigned char ks_raw[kPromptTileBytes];
   __shared__ __attribute__((aligned(16))) unsigned char vs_raw[kPromptTileBytes];
   const TA *ks = (const TA *)ks_raw;
@@ -264,16 +268,19 @@ __global__ __launch_bounds__(256) void k_attention_prompt(
   }
   if (!active) return;
   const float inv = (qpos < first || lsum == 0.f) ? 0.f : 1.0f / lsum;
-  TA *out = o + (m * H + h) * d + 8 * sub;
+  const size_t out0 = (m * H + h) * d + 8 * sub;
 #pragma unroll
-  for (int t = 0; t < 8; ++t) out[t] = from_f<TA>(acc[t] * inv);
+  for (int t = 0; t < 8; t += 4)
+    act_store4(o, o_fmt, out0 + t, o_plane,
+               make_float4(acc[t] * inv, acc[t + 1] * inv, acc[t + 2] * inv, acc[t + 3] * inv));
 }
 
 hipError_t launch_attention(bool f32, const float *q, const void *kc, const void *vc,
-                            const int *valid_len, void *o, int rows, int H, int d, int max_len,
-                            int n_total, int head_off, int rows_per_seq, int pos_base,
-                            const int *pos_dev, int prompt_len, hipStream_t st) {
+                            const int *valid_len, void *o, int o_fmt, int rows, int H, int d,
+                            int max_len, int n_total, int head_off, int rows_per_seq,
+                            int pos_base, const int *pos_dev, int prompt_len, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
+  const size_t o_plane = (size_t)rows * H * d;
   // The prompt kernel when it still fills the chip (>= 256 blocks); a short prompt of
   // one or a few sequences keeps one block per (row, head), which spreads its few keys
   // over more CUs (measured, 176B share batch 1: 14 blocks took 9.7 us, 224 took 6.0).
@@ -284,22 +291,22 @@ hipError_t launch_attention(bool f32, const float *q, const void *kc, const void
     const dim3 grid((unsigned)(rows / rows_per_seq * nchunk), H), block(256);
     if (f32)
       hipLaunchKernelGGL(k_attention_prompt<float>, grid, block, 0, st, q, (const float *)kc,
-                         (const float *)vc, valid_len, (float *)o, H, d, max_len, n_total,
-                         head_off, rows_per_seq, pos_base, prompt_len, nchunk);
+                         (const float *)vc, valid_len, o, o_fmt, o_plane, H, d, max_len,
+                         n_total, head_off, rows_per_seq, pos_base, prompt_len, nchunk);
     else
       hipLaunchKernelGGL(k_attention_prompt<bf16_t>, grid, block, 0, st, q, (const bf16_t *)kc,
-                         (const bf16_t *)vc, valid_len, (bf16_t *)o, H, d, max_len, n_total,
-                         head_off, rows_per_seq, pos_base, prompt_len, nchunk);
+                         (const bf16_t *)vc, valid_len, o, o_fmt, o_plane, H, d, max_len,
+                         n_total, head_off, rows_per_seq, pos_base, prompt_len, nchunk);
     return hipGetLastError();
   }
   const dim3 grid(rows, H), block(256);
   if (f32)
     hipLaunchKernelGGL(k_attention<float>, grid, block, 0, st, q, (const float *)kc,
-                       (const float *)vc, valid_len, (float *)o, H, d, max_len, n_total,
+                       (const float *)vc, valid_len, o, o_fmt, o_plane, H, d, max_len, n_total,
                        head_off, rows_per_seq, pos_base, pos_dev, prompt_len);
   else
     hipLaunchKernelGGL(k_attention<bf16_t>, grid, block, 0, st, q, (const bf16_t *)kc,
-                       (const bf16_t *)vc, valid_len, (bf16_t *)o, H, d, max_len, n_total,
+                       (const bf16_t *)vc, valid_len, o, o_fmt, o_plane, H, d, max_len, n_total,
                        head_off, rows_per_seq, pos_base, pos_dev, prompt_len);
   return hipGetLastError();
 }

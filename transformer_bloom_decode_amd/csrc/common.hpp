@@ -139,6 +139,45 @@ __device__ __forceinline__ float4 ln_apply(float4 x, float mean, float rstd, con
 }
 
 // ---------------------------------------------------------------------------
+// activation storage formats
+// ---------------------------------------------------------------------------
+// Activations (LayerNorm outputs, attention output, GeLU output) are stored in the
+// form their consumer reads: bf16; float32 (read by the vector-ALU GEMV); or a pair of
+// bf16 planes hi = bf16(v), lo = bf16(v - hi) (read by the MFMA GEMM as two bf16
+// operands; hi + lo carries v to within 2^-17 of its value).  The lo plane starts
+// `plane` elements after the hi plane.
+enum ActFmt : int { AF_BF16 = 0, AF_F32 = 1, AF_BF16X2 = 2 };
+
+__device__ __forceinline__ void act_store(void *p, int fmt, size_t i, size_t plane, float v) {
+  if (fmt == AF_F32) {
+    ((float *)p)[i] = v;
+  } else {
+    const bf16_t hi = f2bf(v);
+    ((bf16_t *)p)[i] = hi;
+    if (fmt == AF_BF16X2) ((bf16_t *)p)[i + plane] = f2bf(v - bf2f(hi));
+  }
+}
+
+// four consecutive elements i .. i+3 (i a multiple of 4)
+__device__ __forceinline__ void act_store4(void *p, int fmt, size_t i, size_t plane, float4 v) {
+  if (fmt == AF_F32) {
+    *(float4 *)((float *)p + i) = v;
+    return;
+  }
+  const bf16_t h0 = f2bf(v.x), h1 = f2bf(v.y), h2 = f2bf(v.z), h3 = f2bf(v.w);
+  uint2 t;
+  t.x = (uint32_t)h0 | ((uint32_t)h1 << 16);
+  t.y = (uint32_t)h2 | ((uint32_t)h3 << 16);
+  *(uint2 *)((bf16_t *)p + i) = t;
+  if (fmt == AF_BF16X2) {
+    uint2 l;
+    l.x = (uint32_t)f2bf(v.x - bf2f(h0)) | ((uint32_t)f2bf(v.y - bf2f(h1)) << 16);
+    l.y = (uint32_t)f2bf(v.z - bf2f(h2)) | ((uint32_t)f2bf(v.w - bf2f(h3)) << 16);
+    *(uint2 *)((bf16_t *)p + i + plane) = l;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // linear-layer epilogues
 // ---------------------------------------------------------------------------
 enum EpiMode : int {
@@ -156,23 +195,26 @@ struct EpiParams {
   // EPI_QKV
   float *q;                // [M][H][d]
   void *kc, *vc;           // cache of this layer: [max_batch][H][max_len][d]
+  int kv_fmt;              // AF_BF16 or AF_F32 cache elements
   int H, d, max_len;
   int pos_base;            // absolute position of row m is pos_base + m % rows_per_seq
-  const int *pos_dev;      // if set, *pos_dev replaces pos_base (replayed decode step)
+  const int *pos_dev;      // if set, *pos_dev replaces pos_base (replayed decode step);
+                           // a slot at or past max_len is then not written
   int rows_per_seq;        // 1 (decode) or the prompt length (prefill)
   float q_scale;           // 1/sqrt(d)
   // EPI_RESID / EPI_GELU / EPI_STORE
   void *out;               // [M][ld]
   int ld;
+  int out_fmt;             // EPI_GELU: ActFmt of out (AF_BF16X2: lo plane `plane` later)
+  size_t plane;
   // EPI_ARGMAX
   float *am_val;           // [M][am_stride]
   int *am_idx;
   int am_stride;
 };
 
-// y = acc * scale[n] + bias[n], then the mode's action.  TP = parameter type, TA =
-// activation type.
-template <typename TP, typename TA>
+// y = acc * scale[n] + bias[n], then the mode's action.  TP = parameter type.
+template <typename TP>
 __device__ __forceinline__ void epilogue(const EpiParams &e, int m, int n, float acc) {
   float y = acc;
   if (e.scale) y *= h2f(e.scale[n]);
@@ -189,8 +231,12 @@ __device__ __forceinline__ void epilogue(const EpiParams &e, int m, int n, float
       } else {
         const int b = m / e.rows_per_seq;
         const int pos = (e.pos_dev ? *e.pos_dev : e.pos_base) + (m - b * e.rows_per_seq);
-        TA *cache = (TA *)(t == 1 ? e.kc : e.vc);
-        cache[(((size_t)b * H + hd) * e.max_len + pos) * d + c] = from_f<TA>(y);
+        if (pos < e.max_len) {
+          const size_t i = (((size_t)b * H + hd) * e.max_len + pos) * d + c;
+          void *cache = t == 1 ? e.kc : e.vc;
+          if (e.kv_fmt == AF_F32) ((float *)cache)[i] = y;
+          else ((bf16_t *)cache)[i] = f2bf(y);
+        }
       }
       break;
     }
@@ -200,7 +246,7 @@ __device__ __forceinline__ void epilogue(const EpiParams &e, int m, int n, float
       break;
     }
     case EPI_GELU:
-      ((TA *)e.out)[(size_t)m * e.ld + n] = from_f<TA>(gelu_tanh(y));
+      act_store(e.out, e.out_fmt, (size_t)m * e.ld + n, e.plane, gelu_tanh(y));
       break;
     case EPI_STORE:
       ((float *)e.out)[(size_t)m * e.ld + n] = y;

@@ -14,6 +14,8 @@
 //    sizes and K splits chosen per shape (plan_linear); int8 weights widened from LDS.
 //  * k_gemm_f32: a plain float32 path for the fp32 model.
 //
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "common.hpp"
@@ -77,7 +79,10 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-template <typename TW, int BM, int BN, int WGM, int WGN, int S, int BK>
+// XS = 1: bf16 activations; XS = 2: activations held as two bf16 planes (hi, lo) whose
+// sum carries a float32 value to 2^-17: both planes are staged and each is multiplied
+// with the same weights (two MFMAs per block), so the product keeps that precision.
+template <typename TW, int BM, int BN, int WGM, int WGN, int S, int BK, int XS>
 struct LgCfg {
   static constexpr int kWaves = WGM * WGN;
   static constexpr int kThreads = kWaves * 64;
@@ -85,14 +90,17 @@ struct LgCfg {
   static constexpr int TM = WTM / 32, TN = WTN / 32;
   static constexpr int XRB = BK * 2;                        // X bytes per row per K tile
   static constexpr int WRB = BK * (int)sizeof(TW);          // W bytes per row per K tile
-  static constexpr int CX = BM * XRB / 1024, CW = BN * WRB / 1024;  // 1 KB pieces per K tile
+  static constexpr int CXP = BM * XRB / 1024;               // 1 KB X pieces per plane
+  static constexpr int CX = XS * CXP, CW = BN * WRB / 1024; // 1 KB pieces per K tile
   static constexpr int CPW = (CX + CW) / kWaves;           // pieces per wave per K tile
-  static constexpr int kStage = BM * XRB + BN * WRB;        // bytes per stage
+  static constexpr int kStage = XS * BM * XRB + BN * WRB;   // bytes per stage
   static constexpr int kLds = S * kStage;
   static_assert((CX + CW) % kWaves == 0 && CPW * (S - 1) < 64, "piece split");
   static_assert(S >= 2 && S <= 6, "stages");
   static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
   static_assert(BK == 64 || (BK == 32 && sizeof(TW) == 2), "K tile");
+  static_assert(XS == 1 || XS == 2, "activation planes");
+  static_assert(kLds <= 160 * 1024, "LDS");
 };
 
 // LDS slot of 16-byte piece q of row r for rows of RB bytes (128 or 64): pieces are
@@ -142,7 +150,7 @@ __device__ __attribute__((noinline)) void lg_out16(const EpiParams &ep, float *p
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     const int m = m0 + 8 * (v >> 2) + (v & 3);
-    if (m < M) epilogue<TP, bf16_t>(ep, m, n, acc[v]);
+    if (m < M) epilogue<TP>(ep, m, n, acc[v]);
   }
 }
 
@@ -174,11 +182,11 @@ __device__ __attribute__((noinline)) void lg_argmax16(const EpiParams &ep, int N
 }
 
 template <typename TW, typename TP, int BM, int BN, int WGM, int WGN, int S, int BK,
-          bool SCHED = false>
+          bool SCHED = false, int XS = 1>
 __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_lg(
     const bf16_t *__restrict__ X, const TW *__restrict__ W, int M, int N, int K,
     int tiles_m, int tiles_n, int splits, float *__restrict__ partial, EpiParams ep) {
-  using C = LgCfg<TW, BM, BN, WGM, WGN, S, BK>;
+  using C = LgCfg<TW, BM, BN, WGM, WGN, S, BK, XS>;
   constexpr bool kI8 = sizeof(TW) == 1;
   extern __shared__ __attribute__((aligned(1024))) unsigned char lg_lds[];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -200,9 +208,11 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_lg(
     const int pc = wid * C::CPW + c;
     if (pc < C::CX) {
       constexpr int LPR = C::XRB / 16;
-      const int rr = pc * (1024 / C::XRB) + lane / LPR;
+      const int pl = pc / C::CXP;                     // activation plane (hi, lo)
+      const int rr = (pc - pl * C::CXP) * (1024 / C::XRB) + lane / LPR;
       const int q = lg_slot<C::XRB>(rr, lane % LPR);
-      src[c] = (const unsigned char *)(X + (size_t)min(m0 + rr, M - 1) * K) + q * 16;
+      src[c] = (const unsigned char *)(X + (size_t)pl * M * K + (size_t)min(m0 + rr, M - 1) * K) +
+               q * 16;
     } else {
       constexpr int LPR = C::WRB / 16;
       const int rr = (pc - C::CX) * (1024 / C::WRB) + lane / LPR;
@@ -246,14 +256,17 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_lg(
     const unsigned char *xb = lg_lds + (kt % S) * C::kStage;
     const unsigned char *wb = xb + C::CX * 1024;
     // operands of 16-wide substep s + 1 are read while the MFMAs of substep s run
-    u32x4 a[2][C::TM], bv[2][C::TN];
+    u32x4 a[2][XS][C::TM], bv[2][C::TN];
     auto rd = [&](int s, int q) {
       const int piece = 2 * s + (lane >> 5);   // 8-element k-piece within the K tile
 #pragma unroll
-      for (int i = 0; i < C::TM; ++i) {
-        const int r = wm * C::WTM + 32 * i + (lane & 31);
-        a[q][i] = *(const u32x4 *)(xb + r * C::XRB + 16 * lg_slot<C::XRB>(r, piece));
-      }
+      for (int pl = 0; pl < XS; ++pl)
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i) {
+          const int r = wm * C::WTM + 32 * i + (lane & 31);
+          a[q][pl][i] = *(const u32x4 *)(xb + pl * C::CXP * 1024 + r * C::XRB +
+                                         16 * lg_slot<C::XRB>(r, piece));
+        }
 #pragma unroll
       for (int j = 0; j < C::TN; ++j) {
         const int r = wn * C::WTN + 32 * j + (lane & 31);
@@ -273,9 +286,12 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_lg(
     for (int s = 0; s < BK / 16; ++s) {
       if (s + 1 < BK / 16) rd(s + 1, (s + 1) & 1);
 #pragma unroll
-      for (int i = 0; i < C::TM; ++i)
+      for (int pl = 0; pl < XS; ++pl)
 #pragma unroll
-        for (int j = 0; j < C::TN; ++j) acc[i][j] = mfma32(a[s & 1][i], bv[s & 1][j], acc[i][j]);
+        for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+          for (int j = 0; j < C::TN; ++j)
+            acc[i][j] = mfma32(a[s & 1][pl][i], bv[s & 1][j], acc[i][j]);
       if constexpr (SCHED) {
         // interleave: one MFMA, then one of the next substep's LDS reads, ...
         if (s + 1 < BK / 16) {
@@ -343,7 +359,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float *__restrict__ X,
     for (int k = 0; k < K; ++k) s = fmaf(x[k], w[k], s);
   }
   if (ep.mode != EPI_ARGMAX) {
-    if (n < N) epilogue<float, float>(ep, m, n, s);
+    if (n < N) epilogue<float>(ep, m, n, s);
     return;
   }
   float bv = n < N ? s : -INFINITY;
@@ -370,7 +386,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float *__restrict__ X,
 // loads overlap; the sum runs over z = 0, 1, ... in that fixed order.
 constexpr int kMaxSplits = 8;
 
-template <typename TP, typename TA>
+template <typename TP>
 __global__ __launch_bounds__(256) void k_splitk_epilogue(const float *__restrict__ partial, int S,
                                                          int M, int N, EpiParams ep) {
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
@@ -383,7 +399,7 @@ __global__ __launch_bounds__(256) void k_splitk_epilogue(const float *__restrict
 #pragma unroll
   for (int z = 0; z < kMaxSplits; ++z)
     if (z < S) s += v[z];
-  epilogue<TP, TA>(ep, (int)(idx / N), (int)(idx % N), s);
+  epilogue<TP>(ep, (int)(idx / N), (int)(idx % N), s);
 }
 
 // Final greedy choice per row: lowest index among the per-tile maxima.  1024 threads,
@@ -442,7 +458,7 @@ enum LgTile : int {
   LG_P8 = 9,       // 128 x 256, 4 waves (1 x 4), 2 stages (int8 weights, prompt pass)
 };
 
-LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax) {
+LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax, bool act_f32) {
   LinearPlan p{};
   p.M = M; p.N = N; p.K = K;
   if (wdtype == WT_F32) {
@@ -451,9 +467,14 @@ LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax) {
     p.splits = 1;
     return p;
   }
-  if (M <= kValuMaxRows) return plan_valu(wdtype, M, N, K);
+  if (M <= kValuMaxRows) {
+    p = plan_valu(wdtype, M, N, K);
+    p.x_f32 = act_f32;
+    return p;
+  }
   // Direct-to-LDS MFMA GEMM for everything else (hidden sizes are multiples of 64).
   p.kind = LIN_LG;
+  p.xs = act_f32 ? 2 : 1;
   const int KT = K / kLg;
   if (!argmax && M >= 256) {
     // Prompt passes: tiles of 256 x 256 (8 waves of 64 x 128, one block per CU: 128 KB
@@ -467,7 +488,10 @@ LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax) {
     // rows and 64 columns, so every weight is widened to bf16 once per block), two
     // blocks per CU.  Measured (full 176B int8, 256 rows): QKV 506.6 -> 372.2 us, up
     // 621.7 -> 471.6, down 618.4 -> 486.8; 2048 rows: down 4675 -> 3442 us.
+    // Two activation planes double the X tile: 128 x 128 tiles (96 KB of LDS) are the
+    // largest bf16 prompt tiles that still fit.
     if (wdtype == WT_INT8) p.lg = LG_P8;
+    else if (p.xs == 2) p.lg = LG_128;
     else p.lg = M >= 1024 ? LG_256 : (M >= 512 ? LG_256x128 : LG_128);
     const int bm = (p.lg == LG_128 || p.lg == LG_P8) ? 128 : 256;
     const int bn = (p.lg == LG_256 || p.lg == LG_P8) ? 256 : 128;
@@ -531,6 +555,12 @@ LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax) {
   return p;
 }
 
+int plan_x_fmt(const LinearPlan &p) {
+  if (p.kind == LIN_F32) return AF_F32;
+  if (p.kind == LIN_VALU) return p.x_f32 ? AF_F32 : AF_BF16;
+  return p.xs == 2 ? AF_BF16X2 : AF_BF16;
+}
+
 int argmax_partials_per_row(const LinearPlan &p) {
   return p.kind == LIN_LG ? p.grid_y : p.grid_x;
 }
@@ -539,48 +569,67 @@ size_t linear_partial_bytes(const LinearPlan &p) {
   return p.splits > 1 ? (size_t)p.splits * p.M * p.N * sizeof(float) : 0;
 }
 
-template <typename TW, int BM, int BN, int WGM, int WGN, int S, int BK = kLg,
-          bool SCHED = false>
+// More than 64 KB of dynamic LDS must be allowed once per kernel and device; the flags
+// are set under a lock so that concurrent callers (distinct caches and workspaces) are
+// safe.
+static std::mutex g_lds_attr_mu;
+
+template <typename TW, int BM, int BN, int WGM, int WGN, int S, int BK = kLg, int XS = 1>
 static hipError_t launch_lg_t(const LinearPlan &p, const void *X, const void *W, float *partial,
                               const EpiParams &ep, hipStream_t st) {
-  using C = LgCfg<TW, BM, BN, WGM, WGN, S, BK>;
-  static bool lds_attr = false;  // more than 64 KB of dynamic LDS must be allowed once
-  if (!lds_attr) {
-    const hipError_t e = hipFuncSetAttribute(
-        (const void *)k_gemm_lg<TW, bf16_t, BM, BN, WGM, WGN, S, BK, SCHED>,
-        hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
-    if (e != hipSuccess) return e;
-    lds_attr = true;
+  using C = LgCfg<TW, BM, BN, WGM, WGN, S, BK, XS>;
+  static std::atomic<uint64_t> attr_set{0};   // bit per device
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = 1ull << (dev & 63);
+  if (!(attr_set.load(std::memory_order_acquire) & bit)) {
+    std::lock_guard<std::mutex> lock(g_lds_attr_mu);
+    if (!(attr_set.load(std::memory_order_relaxed) & bit)) {
+      e = hipFuncSetAttribute(
+          (const void *)k_gemm_lg<TW, bf16_t, BM, BN, WGM, WGN, S, BK, false, XS>,
+          hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
+      if (e != hipSuccess) return e;
+      attr_set.fetch_or(bit, std::memory_order_release);
+    }
   }
-  BL_LAUNCH((k_gemm_lg<TW, bf16_t, BM, BN, WGM, WGN, S, BK, SCHED>),
+  BL_LAUNCH((k_gemm_lg<TW, bf16_t, BM, BN, WGM, WGN, S, BK, false, XS>),
             dim3((unsigned)(p.grid_x * p.grid_y * p.splits)), dim3(C::kThreads), C::kLds, st,
             (const bf16_t *)X, (const TW *)W, p.M, p.N, p.K, p.grid_x, p.grid_y, p.splits,
             partial, ep);
   return hipGetLastError();
 }
 
-template <typename TW>
+template <typename TW, int XS>
 static hipError_t launch_lg(const LinearPlan &p, const void *X, const void *W, float *partial,
                             const EpiParams &ep, hipStream_t st) {
   switch (p.lg) {
-    case LG_256: return launch_lg_t<TW, 256, 256, 4, 2, 2>(p, X, W, partial, ep, st);
-    case LG_128: return launch_lg_t<TW, 128, 128, 2, 2, 2>(p, X, W, partial, ep, st);
-    case LG_D32: return launch_lg_t<TW, 32, 128, 1, 4, 4>(p, X, W, partial, ep, st);
-    case LG_D64: return launch_lg_t<TW, 64, 128, 1, 4, 3>(p, X, W, partial, ep, st);
-    case LG_256x128: return launch_lg_t<TW, 256, 128, 4, 2, 3>(p, X, W, partial, ep, st);
+    case LG_256:
+      if constexpr (XS == 1) return launch_lg_t<TW, 256, 256, 4, 2, 2>(p, X, W, partial, ep, st);
+      return hipErrorInvalidValue;
+    case LG_128: return launch_lg_t<TW, 128, 128, 2, 2, 2, kLg, XS>(p, X, W, partial, ep, st);
+    case LG_D32: return launch_lg_t<TW, 32, 128, 1, 4, 4, kLg, XS>(p, X, W, partial, ep, st);
+    case LG_D64: return launch_lg_t<TW, 64, 128, 1, 4, 3, kLg, XS>(p, X, W, partial, ep, st);
+    case LG_256x128:
+      if constexpr (XS == 1) return launch_lg_t<TW, 256, 128, 4, 2, 3>(p, X, W, partial, ep, st);
+      return hipErrorInvalidValue;
     case LG_D32W:
-      if constexpr (sizeof(TW) == 1) return launch_lg_t<TW, 32, 256, 1, 4, 4>(p, X, W, partial, ep, st);
+      if constexpr (sizeof(TW) == 1)
+        return launch_lg_t<TW, 32, 256, 1, 4, 4, kLg, XS>(p, X, W, partial, ep, st);
       return hipErrorInvalidValue;
     case LG_D64W:
-      if constexpr (sizeof(TW) == 1) return launch_lg_t<TW, 64, 256, 1, 4, 3>(p, X, W, partial, ep, st);
+      if constexpr (sizeof(TW) == 1)
+        return launch_lg_t<TW, 64, 256, 1, 4, 3, kLg, XS>(p, X, W, partial, ep, st);
       return hipErrorInvalidValue;
     case LG_D128N:
-      if constexpr (sizeof(TW) == 1) return launch_lg_t<TW, 128, 128, 1, 4, 3>(p, X, W, partial, ep, st);
+      if constexpr (sizeof(TW) == 1)
+        return launch_lg_t<TW, 128, 128, 1, 4, 3, kLg, XS>(p, X, W, partial, ep, st);
       return hipErrorInvalidValue;
     case LG_P8:
-      if constexpr (sizeof(TW) == 1) return launch_lg_t<TW, 128, 256, 1, 4, 2>(p, X, W, partial, ep, st);
+      if constexpr (sizeof(TW) == 1)
+        return launch_lg_t<TW, 128, 256, 1, 4, 2, kLg, XS>(p, X, W, partial, ep, st);
       return hipErrorInvalidValue;
-    default: return launch_lg_t<TW, 128, 128, 2, 2, 3>(p, X, W, partial, ep, st);
+    default: return launch_lg_t<TW, 128, 128, 2, 2, 3, kLg, XS>(p, X, W, partial, ep, st);
   }
 }
 
@@ -594,14 +643,20 @@ hipError_t launch_linear(int wdtype, const LinearPlan &p, const void *X, const v
     return hipGetLastError();
   }
   if (p.kind == LIN_VALU) return launch_valu(wdtype, p, X, W, ep, st);
-  if (p.kind != LIN_LG || p.splits > kMaxSplits) return hipErrorInvalidValue;
-  const hipError_t e = wdtype == WT_BF16 ? launch_lg<bf16_t>(p, X, W, partial, ep, st)
-                                         : launch_lg<int8_t>(p, X, W, partial, ep, st);
+  if (p.kind != LIN_LG || p.splits > kMaxSplits || (p.xs != 1 && p.xs != 2))
+    return hipErrorInvalidValue;
+  hipError_t e;
+  if (wdtype == WT_BF16)
+    e = p.xs == 2 ? launch_lg<bf16_t, 2>(p, X, W, partial, ep, st)
+                  : launch_lg<bf16_t, 1>(p, X, W, partial, ep, st);
+  else
+    e = p.xs == 2 ? launch_lg<int8_t, 2>(p, X, W, partial, ep, st)
+                  : launch_lg<int8_t, 1>(p, X, W, partial, ep, st);
   if (e != hipSuccess) return e;
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || p.splits <= 1 || !splitk_epilogue) return err;
   const size_t MN = (size_t)p.M * p.N;
-  BL_LAUNCH((k_splitk_epilogue<bf16_t, bf16_t>), dim3((unsigned)((MN + 255) / 256)),
+  BL_LAUNCH((k_splitk_epilogue<bf16_t>), dim3((unsigned)((MN + 255) / 256)),
                      dim3(256), 0, st, partial, p.splits, p.M, p.N, ep);
   return hipGetLastError();
 }

@@ -44,17 +44,36 @@ template <> struct VOps<int8_t> {
   }
 };
 
+// Activation pieces: 8 elements of a bf16 row, or 4 of a float32 row, per 16 bytes.
+template <typename TX> struct XOps;
+template <> struct XOps<bf16_t> {
+  static constexpr int kPer16 = 8;
+  static __device__ __forceinline__ void widen(u32x4 v, float *f) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) { f[2 * t] = lo_bf(v[t]); f[2 * t + 1] = hi_bf(v[t]); }
+  }
+};
+template <> struct XOps<float> {
+  static constexpr int kPer16 = 4;
+  static __device__ __forceinline__ void widen(u32x4 v, float *f) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) f[t] = __uint_as_float(v[t]);
+  }
+};
+
 // DB: double-buffered (the next U pieces per row are issued before the current ones
 // are used) or single-buffered (U pieces per row issued at once, then used; with U >=
 // the row's pieces, a wave issues its whole row in one go, which keeps the most bytes
-// in flight when the grid is too small to fill every wave slot).
-template <typename TW, typename TP, int MR, int R, int U, bool DB>
-__global__ __launch_bounds__(256) void k_gemv_valu(const bf16_t *__restrict__ X,
+// in flight when the grid is too small to fill every wave slot).  TX: activation type
+// (bf16, or float32 when the model keeps float32 activations).
+template <typename TW, typename TP, typename TX, int MR, int R, int U, bool DB>
+__global__ __launch_bounds__(256) void k_gemv_valu(const TX *__restrict__ X,
                                                    const TW *__restrict__ W, int M, int N, int K,
                                                    EpiParams ep) {
   using VO = VOps<TW>;
+  using XO = XOps<TX>;
   constexpr int E = VO::kPerLane;
-  constexpr int XP = E / 8;                               // 16-byte activation pieces per step
+  constexpr int XP = E / XO::kPer16;                      // 16-byte activation pieces per step
   __shared__ float am_v[4][MR];
   __shared__ int am_i[4][MR];
   const int lane = threadIdx.x & 63;
@@ -63,7 +82,7 @@ __global__ __launch_bounds__(256) void k_gemv_valu(const bf16_t *__restrict__ X,
   const TW *wr[R];
 #pragma unroll
   for (int i = 0; i < R; ++i) wr[i] = W + (size_t)min(row0 + i, N - 1) * K;
-  const bf16_t *xr[MR];
+  const TX *xr[MR];
 #pragma unroll
   for (int m = 0; m < MR; ++m) xr[m] = X + (size_t)min(m, M - 1) * K;
 
@@ -89,7 +108,7 @@ __global__ __launch_bounds__(256) void k_gemv_valu(const bf16_t *__restrict__ X,
       for (int m = 0; m < MR; ++m)
 #pragma unroll
         for (int p = 0; p < XP; ++p)
-          x[u][m][p] = ok ? *(const u32x4 *)(xr[m] + k + 8 * p) : zero4();
+          x[u][m][p] = ok ? *(const u32x4 *)(xr[m] + k + XO::kPer16 * p) : zero4();
     }
   };
 
@@ -100,12 +119,7 @@ __global__ __launch_bounds__(256) void k_gemv_valu(const bf16_t *__restrict__ X,
 #pragma unroll
       for (int m = 0; m < MR; ++m)
 #pragma unroll
-        for (int p = 0; p < XP; ++p)
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            xf[m][8 * p + 2 * t] = lo_bf(cx[u][m][p][t]);
-            xf[m][8 * p + 2 * t + 1] = hi_bf(cx[u][m][p][t]);
-          }
+        for (int p = 0; p < XP; ++p) XO::widen(cx[u][m][p], &xf[m][XO::kPer16 * p]);
 #pragma unroll
       for (int i = 0; i < R; ++i) {
         float wf[E];
@@ -180,7 +194,7 @@ __global__ __launch_bounds__(256) void k_gemv_valu(const bf16_t *__restrict__ X,
       for (int m = 0; m < MR; ++m)
         if (lane == i * MR + m) v = acc[i][m];
     const int n = row0 + lane / MR, m = lane % MR;
-    if (n < N && m < M) epilogue<TP, bf16_t>(ep, m, n, v);
+    if (n < N && m < M) epilogue<TP>(ep, m, n, v);
   }
 }
 
@@ -227,7 +241,7 @@ __device__ __forceinline__ float gemv_block_sum(float v, float *sh) {
   return (sh[0] + sh[1]) + (sh[2] + sh[3]);
 }
 
-template <typename TW, int NV>
+template <typename TW, typename TX, int NV>
 __global__ __launch_bounds__(256) void k_gemv_ln(const float *__restrict__ x,
                                                  const bf16_t *__restrict__ g,
                                                  const bf16_t *__restrict__ b, float eps,
@@ -238,7 +252,7 @@ __global__ __launch_bounds__(256) void k_gemv_ln(const float *__restrict__ x,
   constexpr int step = 64 * E;                   // elements per wave load
   constexpr int U = NV * 1024 / step;            // loads per weight row
   constexpr int UA = U < 20 ? U : 20;            // issued before the LayerNorm
-  __shared__ __align__(16) bf16_t a_s[NV * 1024];
+  __shared__ __align__(16) TX a_s[NV * 1024];
   __shared__ float red[2][4];
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
@@ -287,10 +301,14 @@ __global__ __launch_bounds__(256) void k_gemv_ln(const float *__restrict__ x,
     const int col = 4 * (threadIdx.x + i * 256);
     if (col < K) {
       const float4 y = ln_apply<bf16_t>(v[i], mean, rstd, gv[i], bv[i]);
-      uint2 t;
-      t.x = (uint32_t)f2bf(y.x) | ((uint32_t)f2bf(y.y) << 16);
-      t.y = (uint32_t)f2bf(y.z) | ((uint32_t)f2bf(y.w) << 16);
-      *(uint2 *)(a_s + col) = t;
+      if constexpr (sizeof(TX) == 4) {
+        *(float4 *)(a_s + col) = y;
+      } else {
+        uint2 t;
+        t.x = (uint32_t)f2bf(y.x) | ((uint32_t)f2bf(y.y) << 16);
+        t.y = (uint32_t)f2bf(y.z) | ((uint32_t)f2bf(y.w) << 16);
+        *(uint2 *)(a_s + col) = t;
+      }
     }
   }
 #pragma unroll
@@ -305,19 +323,18 @@ __global__ __launch_bounds__(256) void k_gemv_ln(const float *__restrict__ x,
     if (k < K) {
       float wf[E];
       VO::widen(cw[u], wf);
+      constexpr int PX = XOps<TX>::kPer16;
 #pragma unroll
-      for (int p = 0; p < E / 8; ++p) {
-        const u32x4 a = *(const u32x4 *)(a_s + k + 8 * p);
+      for (int p = 0; p < E / PX; ++p) {
+        float af[PX];
+        XOps<TX>::widen(*(const u32x4 *)(a_s + k + PX * p), af);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          acc = fmaf(wf[8 * p + 2 * t], lo_bf(a[t]), acc);
-          acc = fmaf(wf[8 * p + 2 * t + 1], hi_bf(a[t]), acc);
-        }
+        for (int t = 0; t < PX; ++t) acc = fmaf(wf[PX * p + t], af[t], acc);
       }
     }
   }
   acc = wave_sum(acc);
-  if (lane == 0 && row < N) epilogue<bf16_t, bf16_t>(ep, 0, row, acc);
+  if (lane == 0 && row < N) epilogue<bf16_t>(ep, 0, row, acc);
 }
 
 bool gemv_ln_supported(int wdtype, int M, int K) {
@@ -325,7 +342,7 @@ bool gemv_ln_supported(int wdtype, int M, int K) {
          K <= kGemvLnMaxK;
 }
 
-template <typename TW>
+template <typename TW, typename TX>
 static void launch_gemv_ln_t(int N, int K, const float *x, const void *g, const void *b,
                              float eps, const void *W, const EpiParams &ep, hipStream_t st) {
   const dim3 grid((N + 3) / 4), block(256);
@@ -333,18 +350,23 @@ static void launch_gemv_ln_t(int N, int K, const float *x, const void *g, const 
   const TW *w = (const TW *)W;
   const int nv = (K + 1023) / 1024;
   if (nv <= 1)
-    BL_LAUNCH((k_gemv_ln<TW, 1>), grid, block, 0, st, x, gg, bb, eps, w, N, K, ep);
+    BL_LAUNCH((k_gemv_ln<TW, TX, 1>), grid, block, 0, st, x, gg, bb, eps, w, N, K, ep);
   else
-    BL_LAUNCH((k_gemv_ln<TW, 4>), grid, block, 0, st, x, gg, bb, eps, w, N, K, ep);
-
+    BL_LAUNCH((k_gemv_ln<TW, TX, 4>), grid, block, 0, st, x, gg, bb, eps, w, N, K, ep);
 }
 
-hipError_t launch_gemv_ln(int wdtype, int N, int K, const float *x, const void *g, const void *b,
-                          float eps, const void *W, const EpiParams &ep, hipStream_t st) {
+hipError_t launch_gemv_ln(int wdtype, bool x_f32, int N, int K, const float *x, const void *g,
+                          const void *b, float eps, const void *W, const EpiParams &ep,
+                          hipStream_t st) {
   if (N <= 0) return hipSuccess;
   if (!gemv_ln_supported(wdtype, 1, K)) return hipErrorInvalidValue;
-  if (wdtype == WT_BF16) launch_gemv_ln_t<bf16_t>(N, K, x, g, b, eps, W, ep, st);
-  else launch_gemv_ln_t<int8_t>(N, K, x, g, b, eps, W, ep, st);
+  if (wdtype == WT_BF16) {
+    if (x_f32) launch_gemv_ln_t<bf16_t, float>(N, K, x, g, b, eps, W, ep, st);
+    else launch_gemv_ln_t<bf16_t, bf16_t>(N, K, x, g, b, eps, W, ep, st);
+  } else {
+    if (x_f32) launch_gemv_ln_t<int8_t, float>(N, K, x, g, b, eps, W, ep, st);
+    else launch_gemv_ln_t<int8_t, bf16_t>(N, K, x, g, b, eps, W, ep, st);
+  }
   return hipGetLastError();
 }
 
@@ -381,36 +403,41 @@ LinearPlan plan_valu(int wdtype, int M, int N, int K) {
   return p;
 }
 
-template <typename TW, typename TP>
+template <typename TW, typename TP, typename TX>
 static void launch_valu_t(const LinearPlan &p, const void *X, const void *W, const EpiParams &ep,
                           hipStream_t st) {
   const dim3 grid(p.grid_x), block(256);
-  const bf16_t *x = (const bf16_t *)X;
+  const TX *x = (const TX *)X;
   const TW *w = (const TW *)W;
   if constexpr (std::is_same<TW, bf16_t>::value) {
     if (p.vr == 1 && p.mt == 1 && !p.vdb) {
       if (p.vu == 16)
-        BL_LAUNCH((k_gemv_valu<TW, TP, 1, 1, 16, false>), grid, block, 0, st, x, w, p.M, p.N, p.K, ep);
+        BL_LAUNCH((k_gemv_valu<TW, TP, TX, 1, 1, 16, false>), grid, block, 0, st, x, w, p.M, p.N, p.K, ep);
       else
-        BL_LAUNCH((k_gemv_valu<TW, TP, 1, 1, 28, false>), grid, block, 0, st, x, w, p.M, p.N, p.K, ep);
+        BL_LAUNCH((k_gemv_valu<TW, TP, TX, 1, 1, 28, false>), grid, block, 0, st, x, w, p.M, p.N, p.K, ep);
       return;
     }
     if (p.vr == 4 && p.mt == 1 && !p.vdb) {
-      BL_LAUNCH((k_gemv_valu<TW, TP, 1, 4, 4, false>), grid, block, 0, st, x, w, p.M, p.N, p.K, ep);
+      BL_LAUNCH((k_gemv_valu<TW, TP, TX, 1, 4, 4, false>), grid, block, 0, st, x, w, p.M, p.N, p.K, ep);
       return;
     }
   }
   switch (p.mt) {
-    case 1: BL_LAUNCH((k_gemv_valu<TW, TP, 1, 2, 4, true>), grid, block, 0, st, x, w, p.M, p.N, p.K, ep); break;
-    case 2: BL_LAUNCH((k_gemv_valu<TW, TP, 2, 2, 4, true>), grid, block, 0, st, x, w, p.M, p.N, p.K, ep); break;
-    default: BL_LAUNCH((k_gemv_valu<TW, TP, 4, 2, 2, true>), grid, block, 0, st, x, w, p.M, p.N, p.K, ep); break;
+    case 1: BL_LAUNCH((k_gemv_valu<TW, TP, TX, 1, 2, 4, true>), grid, block, 0, st, x, w, p.M, p.N, p.K, ep); break;
+    case 2: BL_LAUNCH((k_gemv_valu<TW, TP, TX, 2, 2, 4, true>), grid, block, 0, st, x, w, p.M, p.N, p.K, ep); break;
+    default: BL_LAUNCH((k_gemv_valu<TW, TP, TX, 4, 2, 2, true>), grid, block, 0, st, x, w, p.M, p.N, p.K, ep); break;
   }
 }
 
 hipError_t launch_valu(int wdtype, const LinearPlan &p, const void *X, const void *W,
                        const EpiParams &ep, hipStream_t st) {
-  if (wdtype == WT_BF16) launch_valu_t<bf16_t, bf16_t>(p, X, W, ep, st);
-  else launch_valu_t<int8_t, bf16_t>(p, X, W, ep, st);
+  if (wdtype == WT_BF16) {
+    if (p.x_f32) launch_valu_t<bf16_t, bf16_t, float>(p, X, W, ep, st);
+    else launch_valu_t<bf16_t, bf16_t, bf16_t>(p, X, W, ep, st);
+  } else {
+    if (p.x_f32) launch_valu_t<int8_t, bf16_t, float>(p, X, W, ep, st);
+    else launch_valu_t<int8_t, bf16_t, bf16_t>(p, X, W, ep, st);
+  }
   return hipGetLastError();
 }
 

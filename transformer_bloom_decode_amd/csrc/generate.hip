@@ -54,6 +54,16 @@ __global__ __launch_bounds__(1024) void k_gen_record(const int *__restrict__ nex
   }
 }
 
+// Device-resident KV length of a cache (bloom_kv_cache.d_len).
+__global__ void k_len_update(int *len, int set, int add, int max_len) {
+  if (threadIdx.x == 0) *len = set >= 0 ? set : min(*len + add, max_len);
+}
+
+hipError_t launch_len_update(int *len, int set, int add, int max_len, hipStream_t st) {
+  hipLaunchKernelGGL(k_len_update, dim3(1), dim3(64), 0, st, len, set, add, max_len);
+  return hipGetLastError();
+}
+
 hipError_t launch_gen_init(int *state, int pos, int step, int *done, int batch, hipStream_t st) {
   hipLaunchKernelGGL(k_gen_init, dim3(1), dim3(256), 0, st, state, pos, step, done, batch);
   return hipGetLastError();

@@ -58,6 +58,8 @@ struct LinearPlan {
   int lg;        // LG: tile configuration (LgTile in gemm.hip)
   int grid_x, grid_y;
   int splits;    // K splits (> 1: partial sums + reduction kernel)
+  bool x_f32;    // VALU: float32 activations (else bf16)
+  int xs;        // LG: activation planes (1: bf16; 2: bf16 hi + lo planes of float32 values)
 };
 
 // Vector-ALU GEMV (gemv.hip): plan for M <= kValuMaxRows rows, and its launch.
@@ -68,9 +70,14 @@ hipError_t launch_valu(int wdtype, const LinearPlan &p, const void *X, const voi
 // bf16): out = epilogue(LN(x) . W^T); bf16 or int8 weights, K a multiple of 16 up to
 // 4096 (gemv_ln_supported).
 bool gemv_ln_supported(int wdtype, int M, int K);
-hipError_t launch_gemv_ln(int wdtype, int N, int K, const float *x, const void *g, const void *b,
-                          float eps, const void *W, const EpiParams &ep, hipStream_t st);
-LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax);
+hipError_t launch_gemv_ln(int wdtype, bool x_f32, int N, int K, const float *x, const void *g,
+                          const void *b, float eps, const void *W, const EpiParams &ep,
+                          hipStream_t st);
+// act_f32: the activations carry float32 values (float32 for the vector-ALU GEMV, two
+// bf16 planes for the MFMA GEMM); else bf16.
+LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax, bool act_f32);
+// Storage format (ActFmt) of the activations a linear of this plan reads.
+int plan_x_fmt(const LinearPlan &p);
 // (max, index) partials per activation row an argmax-mode launch of the plan writes.
 int argmax_partials_per_row(const LinearPlan &p);
 // Bytes of split-K partials the plan needs (0 without split-K).
@@ -92,17 +99,22 @@ hipError_t launch_embed(bool f32, const int *tokens, const void *embed, const vo
 // Split-K partials of a bf16 linear [splits][rows][h] -> x += sum * scale + bias, then
 // out = LN(x) (bf16); only for splitk_resid_ln_supported(h, splits).
 bool splitk_resid_ln_supported(int h, int splits);
+// out is written in format fmt (ActFmt; for AF_BF16X2 the lo plane follows rows * h
+// elements after the hi plane).
 hipError_t launch_splitk_resid_ln(const float *partial, int splits, int rows, const void *scale,
                                   const void *bias, float *x, const void *g, const void *b,
-                                  void *out, int h, float eps, hipStream_t stream);
+                                  void *out, int fmt, int h, float eps, hipStream_t stream);
 hipError_t launch_layernorm(bool f32, const float *x, int in_step, int in_off, const void *g,
-                            const void *b, void *out, float *out_f32, int rows, int h, float eps,
-                            hipStream_t stream);
+                            const void *b, void *out, int fmt, float *out_f32, int rows, int h,
+                            float eps, hipStream_t stream);
 
-hipError_t launch_attention(bool f32, const float *q, const void *kc, const void *vc,
-                            const int *valid_len, void *o, int rows, int H, int d, int max_len,
-                            int n_total, int head_off, int rows_per_seq, int pos_base,
-                            const int *pos_dev, int prompt_len, hipStream_t st);
+// kv_f32: float32 cache (else bf16); o written in format o_fmt (ActFmt, lo plane
+// rows * H * d elements after the hi plane).  With pos_dev set, the query position is
+// read from device memory and clamped so that no slot at or past max_len is read.
+hipError_t launch_attention(bool kv_f32, const float *q, const void *kc, const void *vc,
+                            const int *valid_len, void *o, int o_fmt, int rows, int H, int d,
+                            int max_len, int n_total, int head_off, int rows_per_seq,
+                            int pos_base, const int *pos_dev, int prompt_len, hipStream_t st);
 
 // Per-row stop rule of the generation loop: done[i] set once row i has finished (its
 // eos_id token emitted, or max_new[i] tokens); finished rows emit pad_id; out_len[i]
@@ -146,8 +158,22 @@ hipError_t launch_sample_rows_static(const float *logits, int batch, int V,
                                      const float *uniform, int *out, hipStream_t st);
 // Device address of this GPU's sample scratch array (looked up once per device).
 hipError_t sample_scratch_ptr(void **out);
-// y[i] = bf16(x[i]), round to nearest even.
-hipError_t launch_f32_to_bf16(const float *x, void *y, size_t n, hipStream_t st);
+// y = the n float32 values x in activation format fmt (ActFmt; two planes: the lo plane
+// n elements after the hi plane).
+hipError_t launch_f32_to_act(const float *x, void *y, int fmt, size_t n, hipStream_t st);
+// Device KV length: *len = set when set >= 0, else *len = min(*len + add, max_len).
+hipError_t launch_len_update(int *len, int set, int add, int max_len, hipStream_t st);
+// Every tensor of the model in storage form from the counter-hash generator (bloom.h,
+// bloom_init_weights): one launch per tensor.
+struct InitTensor {
+  void *out;
+  size_t n;
+  uint64_t key;     // SplitMix64(seed << 32 ^ tensor id)
+  int op;           // 0 normal, 1 int8, 2 fp16 row scale
+  int kind;         // normal: 0 float32, 1 bf16
+  float mean, scale;
+};
+hipError_t launch_init_tensor(const InitTensor &t, hipStream_t st);
 hipError_t launch_kv_append(bool f32, const void *k, const void *v, void *ck, void *cv,
                             int batch, int H, int n_new, int d, int max_len, int pos,
                             hipStream_t st);

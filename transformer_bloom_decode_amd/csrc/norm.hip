@@ -92,14 +92,16 @@ __global__ __launch_bounds__(kLnThreads) void k_embed(const int *__restrict__ to
   }
 }
 
-// out[row] = LN(x[row * in_step + in_off]) in the activation type; out_f32 (nullable)
-// receives the same values before rounding.
-template <typename TP, typename TA>
+// out[row] = LN(x[row * in_step + in_off]) in the activation format `fmt` (ActFmt; a
+// second bf16 plane `plane` elements later for AF_BF16X2); out_f32 (nullable) receives
+// the same values before rounding.
+template <typename TP>
 __global__ __launch_bounds__(kLnThreads) void k_layernorm(const float *__restrict__ x,
                                                           int in_step, int in_off,
                                                           const TP *__restrict__ g,
                                                           const TP *__restrict__ b,
-                                                          TA *__restrict__ out,
+                                                          void *__restrict__ out, int fmt,
+                                                          size_t plane,
                                                           float *__restrict__ out_f32, int h,
                                                           float eps) {
   __shared__ float sh[kLnWaves];
@@ -120,14 +122,13 @@ __global__ __launch_bounds__(kLnThreads) void k_layernorm(const float *__restric
   }
   float mean, rstd;
   ln_stats(v, h, eps, sh, mean, rstd);
-  TA *o = out + (size_t)row * h;
   float *of = out_f32 ? out_f32 + (size_t)row * h : nullptr;
 #pragma unroll
   for (int i = 0; i < kLnVec; ++i) {
     const int col = 4 * (threadIdx.x + i * kLnThreads);
     if (col < h) {
       const float4 y = ln_apply<TP>(v[i], mean, rstd, gv[i], bv[i]);
-      Vec4<TA>::store(o + col, y);
+      act_store4(out, fmt, (size_t)row * h + col, plane, y);
       if (of) Vec4<float>::store(of + col, y);
     }
   }
@@ -139,11 +140,11 @@ __global__ __launch_bounds__(kLnThreads) void k_layernorm(const float *__restric
 // -- the same float32 operations, in the same order, as k_splitk_epilogue in residual
 // mode -- then out = LN(x) of the updated row, as k_layernorm.  All S partial pieces of a
 // column group are loaded before the first add.
-template <typename TP, typename TA, int S>
+template <typename TP, int S>
 __global__ __launch_bounds__(kLnThreads) void k_splitk_resid_ln(
     const float *__restrict__ partial, int M, const uint16_t *__restrict__ scale,
     const TP *__restrict__ bias, float *__restrict__ x, const TP *__restrict__ g,
-    const TP *__restrict__ b, TA *__restrict__ out, int h, float eps) {
+    const TP *__restrict__ b, void *__restrict__ out, int fmt, size_t plane, int h, float eps) {
   __shared__ float sh[kLnWaves];
   const int row = blockIdx.x;
   const size_t MN = (size_t)M * h;
@@ -186,20 +187,22 @@ __global__ __launch_bounds__(kLnThreads) void k_splitk_resid_ln(
   }
   float mean, rstd;
   ln_stats(v, h, eps, sh, mean, rstd);
-  TA *o = out + (size_t)row * h;
 #pragma unroll
   for (int i = 0; i < kLnVec; ++i) {
     const int col = 4 * (threadIdx.x + i * kLnThreads);
-    if (col < h) Vec4<TA>::store(o + col, ln_apply<TP>(v[i], mean, rstd, gv[i], bv[i]));
+    if (col < h)
+      act_store4(out, fmt, (size_t)row * h + col, plane,
+                 ln_apply<TP>(v[i], mean, rstd, gv[i], bv[i]));
   }
 }
 
 // Rows longer than the register tile, or not a multiple of 4: re-read the row.
-template <typename TP, typename TA>
+template <typename TP>
 __global__ __launch_bounds__(256) void k_layernorm_any(const float *__restrict__ x, int in_step,
                                                        int in_off, const TP *__restrict__ g,
                                                        const TP *__restrict__ b,
-                                                       TA *__restrict__ out,
+                                                       void *__restrict__ out, int fmt,
+                                                       size_t plane,
                                                        float *__restrict__ out_f32, int h,
                                                        float eps) {
   __shared__ float sh[4];
@@ -215,11 +218,10 @@ __global__ __launch_bounds__(256) void k_layernorm_any(const float *__restrict__
   }
   const float var = block_sum<4>(ss, sh) / (float)h;
   const float rstd = 1.0f / sqrtf(var + eps);
-  TA *o = out + (size_t)row * h;
   float *of = out_f32 ? out_f32 + (size_t)row * h : nullptr;
   for (int i = threadIdx.x; i < h; i += 256) {
     const float y = (xr[i] - mean) * rstd * to_f<TP>(g[i]) + to_f<TP>(b[i]);
-    o[i] = from_f<TA>(y);
+    act_store(out, fmt, (size_t)row * h + i, plane, y);
     if (of) of[i] = y;
   }
 }
@@ -290,17 +292,17 @@ bool splitk_resid_ln_supported(int h, int splits) {
 
 hipError_t launch_splitk_resid_ln(const float *partial, int splits, int rows, const void *scale,
                                   const void *bias, float *x, const void *g, const void *b,
-                                  void *out, int h, float eps, hipStream_t stream) {
+                                  void *out, int fmt, int h, float eps, hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
   if (!splitk_resid_ln_supported(h, splits)) return hipErrorInvalidValue;
   const dim3 grid(rows), block(kLnThreads);
   const uint16_t *sc = (const uint16_t *)scale;
   const bf16_t *bi = (const bf16_t *)bias, *gg = (const bf16_t *)g, *bb = (const bf16_t *)b;
-  bf16_t *o = (bf16_t *)out;
+  const size_t plane = (size_t)rows * h;
 #define BL_SRL(S)                                                                          \
   case S:                                                                                  \
-    hipLaunchKernelGGL((k_splitk_resid_ln<bf16_t, bf16_t, S>), grid, block, 0, stream,    \
-                       partial, rows, sc, bi, x, gg, bb, o, h, eps);                        \
+    hipLaunchKernelGGL((k_splitk_resid_ln<bf16_t, S>), grid, block, 0, stream, partial,   \
+                       rows, sc, bi, x, gg, bb, out, fmt, plane, h, eps);                   \
     break;
   switch (splits) {
     BL_SRL(2) BL_SRL(3) BL_SRL(4) BL_SRL(5) BL_SRL(6) BL_SRL(7) BL_SRL(8)
@@ -311,27 +313,28 @@ hipError_t launch_splitk_resid_ln(const float *partial, int splits, int rows, co
 }
 
 hipError_t launch_layernorm(bool f32, const float *x, int in_step, int in_off, const void *g,
-                            const void *b, void *out, float *out_f32, int rows, int h, float eps,
-                            hipStream_t stream) {
+                            const void *b, void *out, int fmt, float *out_f32, int rows, int h,
+                            float eps, hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
   const bool reg = fits_regs(h);
+  const size_t plane = (size_t)rows * h;
   if (f32) {
     if (reg)
-      hipLaunchKernelGGL((k_layernorm<float, float>), dim3(rows), dim3(kLnThreads), 0, stream, x,
-                         in_step, in_off, (const float *)g, (const float *)b, (float *)out,
+      hipLaunchKernelGGL((k_layernorm<float>), dim3(rows), dim3(kLnThreads), 0, stream, x,
+                         in_step, in_off, (const float *)g, (const float *)b, out, fmt, plane,
                          out_f32, h, eps);
     else
-      hipLaunchKernelGGL((k_layernorm_any<float, float>), dim3(rows), dim3(256), 0, stream, x,
-                         in_step, in_off, (const float *)g, (const float *)b, (float *)out,
+      hipLaunchKernelGGL((k_layernorm_any<float>), dim3(rows), dim3(256), 0, stream, x,
+                         in_step, in_off, (const float *)g, (const float *)b, out, fmt, plane,
                          out_f32, h, eps);
   } else {
     if (reg)
-      hipLaunchKernelGGL((k_layernorm<bf16_t, bf16_t>), dim3(rows), dim3(kLnThreads), 0, stream,
-                         x, in_step, in_off, (const bf16_t *)g, (const bf16_t *)b,
-                         (bf16_t *)out, out_f32, h, eps);
+      hipLaunchKernelGGL((k_layernorm<bf16_t>), dim3(rows), dim3(kLnThreads), 0, stream, x,
+                         in_step, in_off, (const bf16_t *)g, (const bf16_t *)b, out, fmt, plane,
+                         out_f32, h, eps);
     else
-      hipLaunchKernelGGL((k_layernorm_any<bf16_t, bf16_t>), dim3(rows), dim3(256), 0, stream, x,
-                         in_step, in_off, (const bf16_t *)g, (const bf16_t *)b, (bf16_t *)out,
+      hipLaunchKernelGGL((k_layernorm_any<bf16_t>), dim3(rows), dim3(256), 0, stream, x,
+                         in_step, in_off, (const bf16_t *)g, (const bf16_t *)b, out, fmt, plane,
                          out_f32, h, eps);
   }
   return hipGetLastError();

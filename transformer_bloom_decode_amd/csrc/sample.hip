@@ -530,16 +530,19 @@ hipError_t launch_sample_rows_static(const float *logits, int batch, int V,
   return launch_sample_rows(logits, batch, V, temperature, top_p, uniform, out, ws, st);
 }
 
-__global__ void k_f32_to_bf16(const float *__restrict__ x, bf16_t *__restrict__ y, size_t n) {
+// y = x (n float32 values) in activation format fmt: bf16 (round to nearest even),
+// float32, or two bf16 planes hi, lo (lo plane n elements after hi).
+__global__ void k_f32_to_act(const float *__restrict__ x, void *__restrict__ y, int fmt,
+                             size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (size_t)gridDim.x * blockDim.x)
-    y[i] = f2bf(x[i]);
+    act_store(y, fmt, i, n, x[i]);
 }
 
-hipError_t launch_f32_to_bf16(const float *x, void *y, size_t n, hipStream_t st) {
+hipError_t launch_f32_to_act(const float *x, void *y, int fmt, size_t n, hipStream_t st) {
   if (n == 0) return hipSuccess;
   const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 4096);
-  hipLaunchKernelGGL(k_f32_to_bf16, dim3(blocks), dim3(256), 0, st, x, (bf16_t *)y, n);
+  hipLaunchKernelGGL(k_f32_to_act, dim3(blocks), dim3(256), 0, st, x, y, fmt, n);
   return hipGetLastError();
 }
 
