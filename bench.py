@@ -45,9 +45,9 @@ def parse():
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--new-tokens", type=int, default=None)
     ap.add_argument("--layers", type=int, default=None, help="truncate the stack (development)")
-    ap.add_argument("--act", choices=("f32", "bf16"), default="f32",
-                    help="activation and KV-cache type of bf16 / int8 models: float32 values "
-                         "(the precise path) or bf16")
+    ap.add_argument("--act", choices=("f32", "f16", "bf16"), default="f16",
+                    help="activation and KV-cache type of bf16 / int8 models: float32, fp16 "
+                         "or bf16")
     ap.add_argument("--loop", choices=("eager", "graph"), default="eager",
                     help="decode loop: one bloom_decode_step call per token, or bloom_generate "
                          "(replays of a captured decode step)")
@@ -495,10 +495,8 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": (("bf16" if m.weight_dtype == "bf16" else "int8")
-                  + (" weights, f32 activations and KV" if m.act_dtype == "f32"
-                     else " weights, bf16 activations and KV")) if m.weight_dtype != "f32"
-                 else "f32",
+        "dtype": (f"{m.weight_dtype} weights, {m.act_dtype} activations and KV"
+                  if m.weight_dtype != "f32" else "f32"),
         "data": "synthetic (seeded random weights and prompt ids)",
         "config": {"workload": m.name, "batch": B, "prompt_len": P, "new_tokens": n_new,
                    "layers": m.n_layer, "hidden": m.hidden, "heads_local": m.n_head_local,

@@ -160,7 +160,8 @@ class ModelShape:
     weight_dtype: str       # 'f32' | 'bf16' | 'int8'
     embed_ln: bool = True
     ln_eps: float = 1e-5
-    activations: str = "auto"   # 'auto' (float32 for f32 weights, else bf16) | 'f32' | 'bf16'
+    activations: str = "auto"   # 'auto' (float32 for f32 weights, else bf16) | 'f32' | 'f16'
+                                # | 'bf16'
     init_std: float = 0.02      # standard deviation of the synthetic weights
 
     @property

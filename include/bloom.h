@@ -53,9 +53,11 @@
  *     W[r][k] = s[r] * q[r][k] (weight-only).
  *   - act_dtype (BF16 / INT8_ROWSCALE weights): the activations the linears read
  *     (LayerNorm outputs, attention output, GeLU output) are held as bf16
- *     (BLOOM_BF16), or carry float32 values (BLOOM_F32: float32 operands of the
- *     vector-ALU GEMV; for the MFMA GEMM two bf16 planes hi + lo, each multiplied with
- *     the weights, which keeps the product to ~2^-17 of the float32 one).  kv_dtype
+ *     (BLOOM_BF16), fp16 (BLOOM_F16: 8x finer than bf16 at the same size; values
+ *     beyond fp16's range, 65504, become infinite) or float32 (BLOOM_F32).  The
+ *     vector-ALU GEMV (batches of up to 4 rows) reads them in that type; for F16 / F32
+ *     the MFMA GEMM reads two bf16 planes hi + lo of each value, each multiplied with
+ *     the weights, which keeps the product to ~2^-17 of the float32 one.  kv_dtype
  *     must equal act_dtype: the KV cache holds keys and values in that type.
  *
  * Layouts (all row-major, C order)
@@ -107,7 +109,7 @@ typedef struct bloom_config {
   int32_t weight_dtype; /* enum bloom_dtype */
   int32_t embed_ln;     /* 1: LayerNorm right after the embedding gather */
   float ln_eps;         /* LayerNorm epsilon (biased variance) */
-  int32_t act_dtype;    /* BLOOM_BF16 or BLOOM_F32 (see Data types) */
+  int32_t act_dtype;    /* BLOOM_BF16, BLOOM_F16 or BLOOM_F32 (see Data types) */
   int32_t kv_dtype;     /* KV cache element type: equal to act_dtype */
 } bloom_config;
 
@@ -133,7 +135,7 @@ typedef struct bloom_weights {
 
 /* KV cache.  k and v are caller-owned device buffers of
  * n_layer * max_batch * n_head_local * max_len * head_dim elements of kv_dtype
- * (float32 or bf16).  len and prompt_len are host-side: bloom_prefill sets prompt_len
+ * (float32, bf16 or fp16).  len and prompt_len are host-side: bloom_prefill sets prompt_len
  * and len = prompt_len; bloom_decode_step writes slot len and then increments it, and
  * its capacity check uses len.  Slot j holds absolute position j of every row (left
  * padding slots are written but never attended).  A caller may reset len to 0.

@@ -1,6 +1,7 @@
-"""Parity of the float32-activation path (bloom_config.act_dtype = BLOOM_F32: float32
-activations and KV cache; the MFMA GEMM reads them as two bf16 planes) against the
-CPU oracle, and greedy generation whose tokens change from step to step.
+"""Parity of the float32- and fp16-activation paths (bloom_config.act_dtype =
+BLOOM_F32 / BLOOM_F16: activations and KV cache in that type; the MFMA GEMM reads them
+as two bf16 planes) against the CPU oracle, and greedy generation whose tokens change
+from step to step.
 
 Tolerance.  The path keeps every activation to within 2^-17 of its float32 value
 (2^-24 where it is stored as float32), against 2^-9 for bf16 storage.  The float64
@@ -9,7 +10,9 @@ layers of the 176B share and 2.5e-2 after 70; rounded to float32 it is 1.6e-7 an
 5e-7.  Scaled by the 2^8 ratio of the bf16-pair rounding to float32 rounding, that
 is <= 1.3e-4 at any depth, so these tests require 1e-3 (the spec gate is
 1e-2), and ids equal to the oracle's, free-running, where the oracle's top-2 logit
-gap exceeds 1e-3 of the row's RMS.
+gap exceeds 1e-3 of the row's RMS.  fp16 storage rounds to 2^-11: the float64 oracle
+with fp16-rounded activations and KV is 9.6e-4 from the exact one after two layers of
+the 176B share and 3.0e-3 after 70, so fp16 runs are held to the 1e-2 gate.
 
 Varied tokens.  With N(0, 0.02) weights each row repeats one token (the embedding
 dominates the final state); with a larger init scale the attention and MLP branches
@@ -105,34 +108,39 @@ def test_560m_varied_tokens_f32_activations(B):
     _free_running(m, T, prompt, valid, run)
 
 
+TOL = {"f32": TOL_F32ACT, "f16": 1e-2}
+
+
+@pytest.mark.parametrize("act", ["f32", "f16"])
 @pytest.mark.parametrize("batch, valid", [(1, None), (3, (16, 9, 2)), (8, None)])
-def test_tp_share_176b_two_layers_f32_activations(batch, valid):
-    m = dataclasses.replace(bi.BLOOM_176B_TP8_RANK0.truncated(2), activations="f32")
+def test_tp_share_176b_two_layers_precise_activations(batch, valid, act):
+    m = dataclasses.replace(bi.BLOOM_176B_TP8_RANK0.truncated(2), activations=act)
     T, dw, cfg = upload(m)
     prompt, vl = bi.prompts(m, batch, 16, valid)
     run = run_gpu(cfg, dw, prompt, vl, 4)
     v = compare(m, T, prompt, vl, run, 1e-2, widen_embed=True)
-    print(f"176b share L2 act f32 B{batch}: hidden rel {v.hidden_rel:.2e}, "
+    print(f"176b share L2 act {act} B{batch}: hidden rel {v.hidden_rel:.2e}, "
           f"exact ids {v.exact_frac:.3f}")
-    assert v.hidden_rel <= TOL_F32ACT and v.tokens_ok
-    # KV slots hold float32 keys / values: within TOL_F32ACT, unwritten slots NaN
+    assert v.hidden_rel <= TOL[act] and v.tokens_ok
+    # KV slots hold the keys / values in the activation type, unwritten slots NaN
     for layer in range(2):
         k, vv = kv_numpy(run.kv, layer)
         for got, ref in ((k, v.oracle.cache[layer]["k"]), (vv, v.oracle.cache[layer]["v"])):
             L = ref.shape[2]
             assert np.isnan(got[:batch, :, L:]).all()
             err = np.linalg.norm(got[:batch, :, :L] - ref) / np.linalg.norm(ref)
-            assert err <= TOL_F32ACT, (layer, err)
+            assert err <= TOL[act], (layer, err)
 
 
+@pytest.mark.parametrize("act", ["f32", "f16"])
 @pytest.mark.parametrize("batch", [1, 16])
-def test_full_176b_int8_two_layers_f32_activations(batch):
-    m = dataclasses.replace(bi.BLOOM_176B_INT8.truncated(2), activations="f32")
+def test_full_176b_int8_two_layers_precise_activations(batch, act):
+    m = dataclasses.replace(bi.BLOOM_176B_INT8.truncated(2), activations=act)
     T, dw, cfg = upload(m)
     prompt, vl = bi.prompts(m, batch, 16)
     run = run_gpu(cfg, dw, prompt, vl, 3)
     del dw
     torch.cuda.empty_cache()
     v = compare(m, T, prompt, vl, run, 2e-2)
-    print(f"176b int8 L2 act f32 B{batch}: hidden rel {v.hidden_rel:.2e}")
-    assert v.hidden_rel <= TOL_F32ACT and v.tokens_ok
+    print(f"176b int8 L2 act {act} B{batch}: hidden rel {v.hidden_rel:.2e}")
+    assert v.hidden_rel <= TOL[act] and v.tokens_ok

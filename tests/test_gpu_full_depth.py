@@ -6,10 +6,12 @@
    forcing fixes every input token, so the KV-cached steps equal that pass, pinned by
    test_incremental_decode_equals_full_rerun).  The oracle does not hold the 70 layers
    at once (about 86 GB in float64): it regenerates and widens one layer at a time.
-   * float32 activations (the benchmarked configuration): hidden rel-L2 <= 1e-2, the
-     spec gate, and <= 1e-3 (the bf16-pair operands keep every activation to
-     2^-17; the float64 oracle with float32-rounded activations is 5e-7 from the exact
-     one at 70 layers).
+   * float32 activations: hidden rel-L2 <= 1e-2, the spec gate, and <= 1e-3 (the
+     bf16-pair operands keep every activation to 2^-17; the float64 oracle with
+     float32-rounded activations is 5e-7 from the exact one at 70 layers).
+   * fp16 activations and KV cache (the benchmarked configuration): <= 1e-2 (the float64
+     oracle with fp16-rounded activations and KV is 3.0e-3 from the exact one at 70
+     layers).
    * bf16 activations do not meet 1e-2 at this depth: the float64 oracle with its
      activations rounded to bf16 at the same points is itself 2.5e-2 from the exact
      oracle (attention scores spread ~6 with these weights, so a rounding of q or k
@@ -118,20 +120,26 @@ def _ids_ok(om, h, ids, n_new, tol):
 def test_tp_share_176b_full_depth_parity(share_weights):
     n_new = 4
     *_, ids32, hid32 = _generate(share_weights, "f32", n_new)
+    *_, idsh, hidh = _generate(share_weights, "f16", n_new)
     *_, ids16, hid16 = _generate(share_weights, "bf16", n_new)
     torch.cuda.empty_cache()
+    assert np.array_equal(ids32, idsh)
     om, h, hr = _oracle_states(ids32, n_new, rounded=np.array_equal(ids32, ids16))
     rel32 = float(np.linalg.norm(hid32[:, 0] - h) / np.linalg.norm(h))
     ok32, ex32 = _ids_ok(om, h, ids32, n_new, 1e-2)
+    relh = float(np.linalg.norm(hidh[:, 0] - h) / np.linalg.norm(h))
+    okh, exh = _ids_ok(om, h, idsh, n_new, 1e-2)
     if hr is None:   # the bf16 run chose other tokens: its own teacher-forced pass
         om, h, hr = _oracle_states(ids16, n_new, rounded=True)
     rel16 = float(np.linalg.norm(hid16[:, 0] - h) / np.linalg.norm(h))
     rel_ref = float(np.linalg.norm(hr - h) / np.linalg.norm(h))
     ok16, ex16 = _ids_ok(om, h, ids16, n_new, 1e-2)
     _log(f"176b share, 70 layers: float32 activations hidden rel {rel32:.2e} (exact ids "
-         f"{ex32:.2f}); bf16 activations {rel16:.2e} against the bf16-activation oracle's "
-         f"{rel_ref:.2e} (exact ids {ex16:.2f})")
+         f"{ex32:.2f}); fp16 {relh:.2e} (exact ids {exh:.2f}); bf16 activations "
+         f"{rel16:.2e} against the bf16-activation oracle's {rel_ref:.2e} (exact ids "
+         f"{ex16:.2f})")
     assert rel32 <= 1e-2 and rel32 <= 1e-3 and ok32          # the gate, float32 activations
+    assert relh <= 1e-2 and okh                               # the gate, fp16 activations
     assert rel16 <= 1.25 * rel_ref and ok16                   # bf16 activations: regression
 
 

@@ -22,7 +22,8 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "bloom.h")
 BLOOM_OK, BLOOM_EINVAL, BLOOM_EDTYPE, BLOOM_ECAPACITY, BLOOM_EWORKSPACE, BLOOM_EHIP = (
     0, -1, -2, -3, -4, -5)
 BLOOM_F32, BLOOM_BF16, BLOOM_INT8_ROWSCALE, BLOOM_F16 = 0, 1, 2, 3
-DTYPE_CODES = {"f32": BLOOM_F32, "bf16": BLOOM_BF16, "int8": BLOOM_INT8_ROWSCALE}
+DTYPE_CODES = {"f32": BLOOM_F32, "bf16": BLOOM_BF16, "int8": BLOOM_INT8_ROWSCALE,
+               "f16": BLOOM_F16}
 
 _c_void_p = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -357,7 +358,7 @@ def _nbytes(t) -> int:
 
 def make_config(shape) -> bloom_config:
     """bloom_config from any object with the shape attributes (n_layer, hidden, ...;
-    act_dtype 'f32' or 'bf16', which also sets the KV-cache type)."""
+    act_dtype 'f32', 'f16' or 'bf16', which also sets the KV-cache type)."""
     act = DTYPE_CODES[getattr(shape, "act_dtype", "f32" if shape.weight_dtype == "f32"
                               else "bf16")]
     return bloom_config(shape.n_layer, shape.hidden, shape.n_head_total, shape.head_offset,
@@ -412,7 +413,8 @@ class KVCache:
     def __init__(self, cfg: bloom_config, max_batch: int, max_len: int, device="cuda",
                  fill: Optional[float] = None, device_len: bool = False):
         import torch
-        dt = torch.float32 if cfg.kv_dtype == BLOOM_F32 else torch.bfloat16
+        dt = {BLOOM_F32: torch.float32, BLOOM_F16: torch.float16}.get(cfg.kv_dtype,
+                                                                      torch.bfloat16)
         shape = (cfg.n_layer, max_batch, cfg.n_head_local, max_len, cfg.head_dim)
         if fill is None:
             self.k = torch.empty(shape, dtype=dt, device=device)

@@ -49,12 +49,17 @@ struct WsPlan {
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-// Activations carrying float32 values take 4 bytes per element (float32, or the two bf16
-// planes the MFMA GEMM reads); bf16 activations 2.
-bool act_f32(const bloom_config *c) { return c->act_dtype == BLOOM_F32; }
-int act_bytes(const bloom_config *c) { return act_f32(c) ? 4 : 2; }
-bool kv_f32(const bloom_config *c) { return c->kv_dtype == BLOOM_F32; }
-int kv_bytes(const bloom_config *c) { return kv_f32(c) ? 4 : 2; }
+// The activation type as a storage format (ActFmt): AF_BF16, AF_F32 or AF_F16.
+int act_fmt(const bloom_config *c) {
+  return c->act_dtype == BLOOM_F32 ? AF_F32 : (c->act_dtype == BLOOM_F16 ? AF_F16 : AF_BF16);
+}
+// Bytes per activation element in the workspace: bf16 2; float32 / fp16 activations 4
+// (float32, fp16, or the two bf16 planes the MFMA GEMM reads).
+int act_bytes(const bloom_config *c) { return act_fmt(c) == AF_BF16 ? 2 : 4; }
+int kv_fmt(const bloom_config *c) {
+  return c->kv_dtype == BLOOM_F32 ? AF_F32 : (c->kv_dtype == BLOOM_F16 ? AF_F16 : AF_BF16);
+}
+int kv_bytes(const bloom_config *c) { return kv_fmt(c) == AF_F32 ? 4 : 2; }
 int wtype(const bloom_config *c) {
   return c->weight_dtype == BLOOM_F32 ? WT_F32 : (c->weight_dtype == BLOOM_BF16 ? WT_BF16 : WT_INT8);
 }
@@ -93,7 +98,7 @@ WsPlan plan_ws(const bloom_config *c, int batch, int tokens_per_row) {
     for (const int mrows : {(int)M, batch})
       for (const auto &nk : dims)
         part = std::max(part, linear_partial_bytes(
-                                  plan_linear(wdt, mrows, nk[0], nk[1], false, act_f32(c))));
+                                  plan_linear(wdt, mrows, nk[0], nk[1], false, act_fmt(c))));
   }
   p.part = take(part);
   p.total = off;
@@ -113,9 +118,10 @@ int check_config(const bloom_config *c) {
   if (c->weight_dtype != BLOOM_F32 && c->weight_dtype != BLOOM_BF16 &&
       c->weight_dtype != BLOOM_INT8_ROWSCALE)
     return BLOOM_EDTYPE;
-  // activations and the KV cache: float32 or bf16 (float32 only for float32 weights);
-  // the cache holds the activation type
-  if (c->act_dtype != BLOOM_F32 && c->act_dtype != BLOOM_BF16) return BLOOM_EDTYPE;
+  // activations and the KV cache: float32, bf16 or fp16 (float32 only for float32
+  // weights); the cache holds the activation type
+  if (c->act_dtype != BLOOM_F32 && c->act_dtype != BLOOM_BF16 && c->act_dtype != BLOOM_F16)
+    return BLOOM_EDTYPE;
   if (c->weight_dtype == BLOOM_F32 && c->act_dtype != BLOOM_F32) return BLOOM_EDTYPE;
   if (c->kv_dtype != c->act_dtype) return BLOOM_EDTYPE;
   if (c->weight_dtype != BLOOM_F32) {
@@ -240,7 +246,7 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
                 hipStream_t st, const int *d_pos = nullptr, float *d_logits = nullptr) {
   const WsPlan wp = plan_ws(c, batch, tpr);
   const bool f32 = c->weight_dtype == BLOOM_F32;
-  const bool af32 = act_f32(c);
+  const int act = act_fmt(c);
   const int wdt = wtype(c);
   const int M = batch * tpr;
   const int h = c->hidden, H = c->n_head_local, d = c->head_dim, F = c->ffn;
@@ -265,10 +271,10 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
   if (err != hipSuccess) return hip_fail(err);
 
   const size_t layer_stride = (size_t)kv->max_batch * H * kv->max_len * d * kv_bytes(c);
-  const LinearPlan p_qkv = plan_linear(wdt, M, 3 * hd, h, false, af32);
-  const LinearPlan p_dense = plan_linear(wdt, M, h, hd, false, af32);
-  const LinearPlan p_up = plan_linear(wdt, M, F, h, false, af32);
-  const LinearPlan p_down = plan_linear(wdt, M, h, F, false, af32);
+  const LinearPlan p_qkv = plan_linear(wdt, M, 3 * hd, h, false, act);
+  const LinearPlan p_dense = plan_linear(wdt, M, h, hd, false, act);
+  const LinearPlan p_up = plan_linear(wdt, M, F, h, false, act);
+  const LinearPlan p_down = plan_linear(wdt, M, h, F, false, act);
   // every activation is written in the form its consumer reads
   const int fmt_qkv = plan_x_fmt(p_qkv), fmt_dense = plan_x_fmt(p_dense);
   const int fmt_up = plan_x_fmt(p_up), fmt_down = plan_x_fmt(p_down);
@@ -300,20 +306,20 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
     e.bias = L.b_qkv;
     e.scale = (const uint16_t *)L.s_qkv;
     e.q = q; e.kc = kc; e.vc = vc;
-    e.kv_fmt = kv_f32(c) ? AF_F32 : AF_BF16;
+    e.kv_fmt = kv_fmt(c);
     e.H = H; e.d = d; e.max_len = kv->max_len;
     e.pos_base = pos_base; e.pos_dev = d_pos; e.rows_per_seq = tpr;
     e.q_scale = 1.0f / sqrtf((float)d);
     if (ln_in_gemv)
       err = timed(kernel_class(p_qkv), wbytes(3 * hd, h), st, [&] {
-        return launch_gemv_ln(wdt, af32, 3 * hd, h, x, L.ln1_g, L.ln1_b, c->ln_eps, L.w_qkv, e,
+        return launch_gemv_ln(wdt, act, 3 * hd, h, x, L.ln1_g, L.ln1_b, c->ln_eps, L.w_qkv, e,
                               st);
       });
     else
       err = timed_linear(wdt, p_qkv, xa, L.w_qkv, part, e, st, wbytes(3 * hd, h));
     if (err != hipSuccess) return hip_fail(err);
 
-    err = launch_attention(kv_f32(c), q, kc, vc, d_valid, o, fmt_dense, M, H, d, kv->max_len,
+    err = launch_attention(kv_fmt(c), q, kc, vc, d_valid, o, fmt_dense, M, H, d, kv->max_len,
                            c->n_head_total, c->head_offset, tpr, pos_base, d_pos, prompt_len, st);
     if (err != hipSuccess) return hip_fail(err);
 
@@ -343,7 +349,7 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
     g.plane = (size_t)M * F;
     if (ln_in_gemv && !fuse_dense)
       err = timed(kernel_class(p_up), wbytes(F, h), st, [&] {
-        return launch_gemv_ln(wdt, af32, F, h, x, L.ln2_g, L.ln2_b, c->ln_eps, L.w_up, g, st);
+        return launch_gemv_ln(wdt, act, F, h, x, L.ln2_g, L.ln2_b, c->ln_eps, L.w_up, g, st);
       });
     else
       err = timed_linear(wdt, p_up, xa, L.w_up, part, g, st, wbytes(F, h));
@@ -377,13 +383,13 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
                            d_hidden, batch, h, c->ln_eps, st);
     return err == hipSuccess ? BLOOM_OK : hip_fail(err);
   }
-  const size_t act = act_bytes(c);
+  const size_t abytes = act_bytes(c);
   for (int r0 = 0; r0 < batch; r0 += 128) {
     // the LM head runs on chunks of up to 128 rows; the final LayerNorm writes each
     // chunk in the form its plan reads (two bf16 planes: each chunk its own pair)
     const int rows = std::min(128, batch - r0);
-    const LinearPlan p_lm = plan_linear(wdt_lm, rows, c->vocab, h, true, af32);
-    void *X = (char *)af + (size_t)r0 * h * act;
+    const LinearPlan p_lm = plan_linear(wdt_lm, rows, c->vocab, h, true, act);
+    void *X = (char *)af + (size_t)r0 * h * abytes;
     err = launch_layernorm(f32, x + (size_t)r0 * tpr * h, tpr, tpr - 1, w->lnf_g, w->lnf_b, X,
                            plan_x_fmt(p_lm), d_hidden ? d_hidden + (size_t)r0 * h : nullptr, rows,
                            h, c->ln_eps, st);
@@ -641,7 +647,7 @@ int kv_cache_append(const bloom_config *cfg, bloom_kv_cache *kv, int32_t layer, 
   const size_t kvb = kv_bytes(cfg);
   const size_t layer_stride =
       (size_t)kv->max_batch * cfg->n_head_local * kv->max_len * cfg->head_dim * kvb;
-  hipError_t err = launch_kv_append(kv_f32(cfg), d_k, d_v,
+  hipError_t err = launch_kv_append(kv_fmt(cfg) == AF_F32, d_k, d_v,
                                     (char *)kv->k + layer * layer_stride,
                                     (char *)kv->v + layer * layer_stride, batch,
                                     cfg->n_head_local, n_new, cfg->head_dim, kv->max_len, pos,
@@ -693,7 +699,7 @@ int bloom_lm_logits(const bloom_config *cfg, const bloom_weights *w, int32_t bat
     e.ld = cfg->vocab;
     // the greedy LM head's plan (never split) and operand form, so the logits are the
     // ones it ranks
-    const LinearPlan p = plan_linear(wdt_lm, rows, cfg->vocab, h, true, act_f32(cfg));
+    const LinearPlan p = plan_linear(wdt_lm, rows, cfg->vocab, h, true, act_fmt(cfg));
     const float *hr = d_hidden + (size_t)r0 * h;
     const void *X = hr;
     if (plan_x_fmt(p) != AF_F32) {

@@ -49,6 +49,13 @@ template <> struct KVRaw<bf16_t> {
     return (t & 1) ? hi_bf(a[t >> 1]) : lo_bf(a[t >> 1]);
   }
 };
+template <> struct KVRaw<f16_t> {
+  u32x4 a;
+  __device__ __forceinline__ void load(const f16_t *p) { a = *(const u32x4 *)p; }
+  __device__ __forceinline__ float get(int t) const {
+    return (t & 1) ? f16hi(a[t >> 1]) : f16lo(a[t >> 1]);
+  }
+};
 template <> struct KVRaw<float> {
   float4 a, b;
   __device__ __forceinline__ void load(const float *p) {
@@ -275,7 +282,26 @@ __global__ __launch_bounds__(256) void k_attention_prompt(
                make_float4(acc[t] * inv, acc[t + 1] * inv, acc[t + 2] * inv, acc[t + 3] * inv));
 }
 
-hipError_t launch_attention(bool f32, const float *q, const void *kc, const void *vc,
+template <typename TA>
+static void launch_attention_t(const float *q, const void *kc, const void *vc,
+                               const int *valid_len, void *o, int o_fmt, size_t o_plane, int rows,
+                               int H, int d, int max_len, int n_total, int head_off,
+                               int rows_per_seq, int pos_base, const int *pos_dev,
+                               int prompt_len, bool prompt_kernel, int nchunk, hipStream_t st) {
+  if (prompt_kernel) {
+    const dim3 grid((unsigned)(rows / rows_per_seq * nchunk), H), block(256);
+    hipLaunchKernelGGL(k_attention_prompt<TA>, grid, block, 0, st, q, (const TA *)kc,
+                       (const TA *)vc, valid_len, o, o_fmt, o_plane, H, d, max_len, n_total,
+                       head_off, rows_per_seq, pos_base, prompt_len, nchunk);
+  } else {
+    const dim3 grid(rows, H), block(256);
+    hipLaunchKernelGGL(k_attention<TA>, grid, block, 0, st, q, (const TA *)kc, (const TA *)vc,
+                       valid_len, o, o_fmt, o_plane, H, d, max_len, n_total, head_off,
+                       rows_per_seq, pos_base, pos_dev, prompt_len);
+  }
+}
+
+hipError_t launch_attention(int kv_fmt, const float *q, const void *kc, const void *vc,
                             const int *valid_len, void *o, int o_fmt, int rows, int H, int d,
                             int max_len, int n_total, int head_off, int rows_per_seq,
                             int pos_base, const int *pos_dev, int prompt_len, hipStream_t st) {
@@ -287,27 +313,19 @@ hipError_t launch_attention(bool f32, const float *q, const void *kc, const void
   const int QR = 256 / (d >> 3);
   const int nchunk = (rows_per_seq + QR - 1) / QR;
   const long prompt_blocks = (long)(rows / max(rows_per_seq, 1)) * nchunk * H;
-  if (rows_per_seq > 1 && !pos_dev && prompt_blocks >= 256) {
-    const dim3 grid((unsigned)(rows / rows_per_seq * nchunk), H), block(256);
-    if (f32)
-      hipLaunchKernelGGL(k_attention_prompt<float>, grid, block, 0, st, q, (const float *)kc,
-                         (const float *)vc, valid_len, o, o_fmt, o_plane, H, d, max_len,
-                         n_total, head_off, rows_per_seq, pos_base, prompt_len, nchunk);
-    else
-      hipLaunchKernelGGL(k_attention_prompt<bf16_t>, grid, block, 0, st, q, (const bf16_t *)kc,
-                         (const bf16_t *)vc, valid_len, o, o_fmt, o_plane, H, d, max_len,
-                         n_total, head_off, rows_per_seq, pos_base, prompt_len, nchunk);
-    return hipGetLastError();
-  }
-  const dim3 grid(rows, H), block(256);
-  if (f32)
-    hipLaunchKernelGGL(k_attention<float>, grid, block, 0, st, q, (const float *)kc,
-                       (const float *)vc, valid_len, o, o_fmt, o_plane, H, d, max_len, n_total,
-                       head_off, rows_per_seq, pos_base, pos_dev, prompt_len);
+  const bool prompt_kernel = rows_per_seq > 1 && !pos_dev && prompt_blocks >= 256;
+  if (kv_fmt == AF_F32)
+    launch_attention_t<float>(q, kc, vc, valid_len, o, o_fmt, o_plane, rows, H, d, max_len,
+                              n_total, head_off, rows_per_seq, pos_base, pos_dev, prompt_len,
+                              prompt_kernel, nchunk, st);
+  else if (kv_fmt == AF_F16)
+    launch_attention_t<f16_t>(q, kc, vc, valid_len, o, o_fmt, o_plane, rows, H, d, max_len,
+                              n_total, head_off, rows_per_seq, pos_base, pos_dev, prompt_len,
+                              prompt_kernel, nchunk, st);
   else
-    hipLaunchKernelGGL(k_attention<bf16_t>, grid, block, 0, st, q, (const bf16_t *)kc,
-                       (const bf16_t *)vc, valid_len, o, o_fmt, o_plane, H, d, max_len, n_total,
-                       head_off, rows_per_seq, pos_base, pos_dev, prompt_len);
+    launch_attention_t<bf16_t>(q, kc, vc, valid_len, o, o_fmt, o_plane, rows, H, d, max_len,
+                               n_total, head_off, rows_per_seq, pos_base, pos_dev, prompt_len,
+                               prompt_kernel, nchunk, st);
   return hipGetLastError();
 }
 

@@ -15,6 +15,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 typedef uint16_t bf16_t;  // bf16 bit pattern
+typedef _Float16 f16_t;   // IEEE binary16 (activations and KV cache in the fp16 mode)
 
 constexpr int kWave = 64;
 
@@ -33,13 +34,26 @@ __device__ __forceinline__ bf16_t f2bf(float f) {
 
 __device__ __forceinline__ float h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
 
+// fp16 <-> float32 (round to nearest even); lo / hi half of a dword
+__device__ __forceinline__ float f16lo(uint32_t w) {
+  return (float)__builtin_bit_cast(f16_t, (uint16_t)(w & 0xffffu));
+}
+__device__ __forceinline__ float f16hi(uint32_t w) {
+  return (float)__builtin_bit_cast(f16_t, (uint16_t)(w >> 16));
+}
+__device__ __forceinline__ uint16_t f2h_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (f16_t)f);
+}
+
 template <typename T> __device__ __forceinline__ float to_f(T v);
 template <> __device__ __forceinline__ float to_f<float>(float v) { return v; }
 template <> __device__ __forceinline__ float to_f<bf16_t>(bf16_t v) { return bf2f(v); }
+template <> __device__ __forceinline__ float to_f<f16_t>(f16_t v) { return (float)v; }
 
 template <typename T> __device__ __forceinline__ T from_f(float v);
 template <> __device__ __forceinline__ float from_f<float>(float v) { return v; }
 template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float v) { return f2bf(v); }
+template <> __device__ __forceinline__ f16_t from_f<f16_t>(float v) { return (f16_t)v; }
 
 // two bf16 packed in a dword -> floats
 __device__ __forceinline__ float lo_bf(uint32_t w) { return __uint_as_float(w << 16); }
@@ -142,15 +156,17 @@ __device__ __forceinline__ float4 ln_apply(float4 x, float mean, float rstd, con
 // activation storage formats
 // ---------------------------------------------------------------------------
 // Activations (LayerNorm outputs, attention output, GeLU output) are stored in the
-// form their consumer reads: bf16; float32 (read by the vector-ALU GEMV); or a pair of
-// bf16 planes hi = bf16(v), lo = bf16(v - hi) (read by the MFMA GEMM as two bf16
+// form their consumer reads: bf16; float32 or fp16 (read by the vector-ALU GEMV); or a
+// pair of bf16 planes hi = bf16(v), lo = bf16(v - hi) (read by the MFMA GEMM as two bf16
 // operands; hi + lo carries v to within 2^-17 of its value).  The lo plane starts
 // `plane` elements after the hi plane.
-enum ActFmt : int { AF_BF16 = 0, AF_F32 = 1, AF_BF16X2 = 2 };
+enum ActFmt : int { AF_BF16 = 0, AF_F32 = 1, AF_BF16X2 = 2, AF_F16 = 3 };
 
 __device__ __forceinline__ void act_store(void *p, int fmt, size_t i, size_t plane, float v) {
   if (fmt == AF_F32) {
     ((float *)p)[i] = v;
+  } else if (fmt == AF_F16) {
+    ((uint16_t *)p)[i] = f2h_bits(v);
   } else {
     const bf16_t hi = f2bf(v);
     ((bf16_t *)p)[i] = hi;
@@ -162,6 +178,13 @@ __device__ __forceinline__ void act_store(void *p, int fmt, size_t i, size_t pla
 __device__ __forceinline__ void act_store4(void *p, int fmt, size_t i, size_t plane, float4 v) {
   if (fmt == AF_F32) {
     *(float4 *)((float *)p + i) = v;
+    return;
+  }
+  if (fmt == AF_F16) {
+    uint2 t;
+    t.x = (uint32_t)f2h_bits(v.x) | ((uint32_t)f2h_bits(v.y) << 16);
+    t.y = (uint32_t)f2h_bits(v.z) | ((uint32_t)f2h_bits(v.w) << 16);
+    *(uint2 *)((uint16_t *)p + i) = t;
     return;
   }
   const bf16_t h0 = f2bf(v.x), h1 = f2bf(v.y), h2 = f2bf(v.z), h3 = f2bf(v.w);
@@ -195,7 +218,7 @@ struct EpiParams {
   // EPI_QKV
   float *q;                // [M][H][d]
   void *kc, *vc;           // cache of this layer: [max_batch][H][max_len][d]
-  int kv_fmt;              // AF_BF16 or AF_F32 cache elements
+  int kv_fmt;              // AF_BF16, AF_F16 or AF_F32 cache elements
   int H, d, max_len;
   int pos_base;            // absolute position of row m is pos_base + m % rows_per_seq
   const int *pos_dev;      // if set, *pos_dev replaces pos_base (replayed decode step);
@@ -235,6 +258,7 @@ __device__ __forceinline__ void epilogue(const EpiParams &e, int m, int n, float
           const size_t i = (((size_t)b * H + hd) * e.max_len + pos) * d + c;
           void *cache = t == 1 ? e.kc : e.vc;
           if (e.kv_fmt == AF_F32) ((float *)cache)[i] = y;
+          else if (e.kv_fmt == AF_F16) ((uint16_t *)cache)[i] = f2h_bits(y);
           else ((bf16_t *)cache)[i] = f2bf(y);
         }
       }

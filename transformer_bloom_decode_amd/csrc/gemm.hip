@@ -458,7 +458,7 @@ enum LgTile : int {
   LG_P8 = 9,       // 128 x 256, 4 waves (1 x 4), 2 stages (int8 weights, prompt pass)
 };
 
-LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax, bool act_f32) {
+LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax, int act) {
   LinearPlan p{};
   p.M = M; p.N = N; p.K = K;
   if (wdtype == WT_F32) {
@@ -469,12 +469,12 @@ LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax, bool act_f3
   }
   if (M <= kValuMaxRows) {
     p = plan_valu(wdtype, M, N, K);
-    p.x_f32 = act_f32;
+    p.x_fmt = act;
     return p;
   }
   // Direct-to-LDS MFMA GEMM for everything else (hidden sizes are multiples of 64).
   p.kind = LIN_LG;
-  p.xs = act_f32 ? 2 : 1;
+  p.xs = act == AF_BF16 ? 1 : 2;
   const int KT = K / kLg;
   if (!argmax && M >= 256) {
     // Prompt passes: tiles of 256 x 256 (8 waves of 64 x 128, one block per CU: 128 KB
@@ -557,7 +557,7 @@ LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax, bool act_f3
 
 int plan_x_fmt(const LinearPlan &p) {
   if (p.kind == LIN_F32) return AF_F32;
-  if (p.kind == LIN_VALU) return p.x_f32 ? AF_F32 : AF_BF16;
+  if (p.kind == LIN_VALU) return p.x_fmt;
   return p.xs == 2 ? AF_BF16X2 : AF_BF16;
 }
 

@@ -60,6 +60,13 @@ template <> struct XOps<float> {
     for (int t = 0; t < 4; ++t) f[t] = __uint_as_float(v[t]);
   }
 };
+template <> struct XOps<f16_t> {
+  static constexpr int kPer16 = 8;
+  static __device__ __forceinline__ void widen(u32x4 v, float *f) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) { f[2 * t] = f16lo(v[t]); f[2 * t + 1] = f16hi(v[t]); }
+  }
+};
 
 // DB: double-buffered (the next U pieces per row are issued before the current ones
 // are used) or single-buffered (U pieces per row issued at once, then used; with U >=
@@ -303,6 +310,11 @@ __global__ __launch_bounds__(256) void k_gemv_ln(const float *__restrict__ x,
       const float4 y = ln_apply<bf16_t>(v[i], mean, rstd, gv[i], bv[i]);
       if constexpr (sizeof(TX) == 4) {
         *(float4 *)(a_s + col) = y;
+      } else if constexpr (std::is_same<TX, f16_t>::value) {
+        uint2 t;
+        t.x = (uint32_t)f2h_bits(y.x) | ((uint32_t)f2h_bits(y.y) << 16);
+        t.y = (uint32_t)f2h_bits(y.z) | ((uint32_t)f2h_bits(y.w) << 16);
+        *(uint2 *)(a_s + col) = t;
       } else {
         uint2 t;
         t.x = (uint32_t)f2bf(y.x) | ((uint32_t)f2bf(y.y) << 16);
@@ -355,18 +367,22 @@ static void launch_gemv_ln_t(int N, int K, const float *x, const void *g, const 
     BL_LAUNCH((k_gemv_ln<TW, TX, 4>), grid, block, 0, st, x, gg, bb, eps, w, N, K, ep);
 }
 
-hipError_t launch_gemv_ln(int wdtype, bool x_f32, int N, int K, const float *x, const void *g,
+template <typename TW>
+static void launch_gemv_ln_w(int x_fmt, int N, int K, const float *x, const void *g,
+                             const void *b, float eps, const void *W, const EpiParams &ep,
+                             hipStream_t st) {
+  if (x_fmt == AF_F32) launch_gemv_ln_t<TW, float>(N, K, x, g, b, eps, W, ep, st);
+  else if (x_fmt == AF_F16) launch_gemv_ln_t<TW, f16_t>(N, K, x, g, b, eps, W, ep, st);
+  else launch_gemv_ln_t<TW, bf16_t>(N, K, x, g, b, eps, W, ep, st);
+}
+
+hipError_t launch_gemv_ln(int wdtype, int x_fmt, int N, int K, const float *x, const void *g,
                           const void *b, float eps, const void *W, const EpiParams &ep,
                           hipStream_t st) {
   if (N <= 0) return hipSuccess;
   if (!gemv_ln_supported(wdtype, 1, K)) return hipErrorInvalidValue;
-  if (wdtype == WT_BF16) {
-    if (x_f32) launch_gemv_ln_t<bf16_t, float>(N, K, x, g, b, eps, W, ep, st);
-    else launch_gemv_ln_t<bf16_t, bf16_t>(N, K, x, g, b, eps, W, ep, st);
-  } else {
-    if (x_f32) launch_gemv_ln_t<int8_t, float>(N, K, x, g, b, eps, W, ep, st);
-    else launch_gemv_ln_t<int8_t, bf16_t>(N, K, x, g, b, eps, W, ep, st);
-  }
+  if (wdtype == WT_BF16) launch_gemv_ln_w<bf16_t>(x_fmt, N, K, x, g, b, eps, W, ep, st);
+  else launch_gemv_ln_w<int8_t>(x_fmt, N, K, x, g, b, eps, W, ep, st);
   return hipGetLastError();
 }
 
@@ -429,15 +445,18 @@ static void launch_valu_t(const LinearPlan &p, const void *X, const void *W, con
   }
 }
 
+template <typename TW>
+static void launch_valu_w(const LinearPlan &p, const void *X, const void *W, const EpiParams &ep,
+                          hipStream_t st) {
+  if (p.x_fmt == AF_F32) launch_valu_t<TW, bf16_t, float>(p, X, W, ep, st);
+  else if (p.x_fmt == AF_F16) launch_valu_t<TW, bf16_t, f16_t>(p, X, W, ep, st);
+  else launch_valu_t<TW, bf16_t, bf16_t>(p, X, W, ep, st);
+}
+
 hipError_t launch_valu(int wdtype, const LinearPlan &p, const void *X, const void *W,
                        const EpiParams &ep, hipStream_t st) {
-  if (wdtype == WT_BF16) {
-    if (p.x_f32) launch_valu_t<bf16_t, bf16_t, float>(p, X, W, ep, st);
-    else launch_valu_t<bf16_t, bf16_t, bf16_t>(p, X, W, ep, st);
-  } else {
-    if (p.x_f32) launch_valu_t<int8_t, bf16_t, float>(p, X, W, ep, st);
-    else launch_valu_t<int8_t, bf16_t, bf16_t>(p, X, W, ep, st);
-  }
+  if (wdtype == WT_BF16) launch_valu_w<bf16_t>(p, X, W, ep, st);
+  else launch_valu_w<int8_t>(p, X, W, ep, st);
   return hipGetLastError();
 }
 

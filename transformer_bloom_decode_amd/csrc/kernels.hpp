@@ -58,7 +58,7 @@ struct LinearPlan {
   int lg;        // LG: tile configuration (LgTile in gemm.hip)
   int grid_x, grid_y;
   int splits;    // K splits (> 1: partial sums + reduction kernel)
-  bool x_f32;    // VALU: float32 activations (else bf16)
+  int x_fmt;     // VALU: activation storage (ActFmt: AF_BF16, AF_F32 or AF_F16)
   int xs;        // LG: activation planes (1: bf16; 2: bf16 hi + lo planes of float32 values)
 };
 
@@ -70,12 +70,13 @@ hipError_t launch_valu(int wdtype, const LinearPlan &p, const void *X, const voi
 // bf16): out = epilogue(LN(x) . W^T); bf16 or int8 weights, K a multiple of 16 up to
 // 4096 (gemv_ln_supported).
 bool gemv_ln_supported(int wdtype, int M, int K);
-hipError_t launch_gemv_ln(int wdtype, bool x_f32, int N, int K, const float *x, const void *g,
+hipError_t launch_gemv_ln(int wdtype, int x_fmt, int N, int K, const float *x, const void *g,
                           const void *b, float eps, const void *W, const EpiParams &ep,
                           hipStream_t st);
-// act_f32: the activations carry float32 values (float32 for the vector-ALU GEMV, two
-// bf16 planes for the MFMA GEMM); else bf16.
-LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax, bool act_f32);
+// act: the model's activation type (ActFmt AF_BF16, AF_F32 or AF_F16).  The vector-ALU
+// GEMV reads activations in that type; the MFMA GEMM reads bf16, or for float32 / fp16
+// activations the two bf16 planes hi + lo.
+LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax, int act);
 // Storage format (ActFmt) of the activations a linear of this plan reads.
 int plan_x_fmt(const LinearPlan &p);
 // (max, index) partials per activation row an argmax-mode launch of the plan writes.
@@ -108,10 +109,11 @@ hipError_t launch_layernorm(bool f32, const float *x, int in_step, int in_off, c
                             const void *b, void *out, int fmt, float *out_f32, int rows, int h,
                             float eps, hipStream_t stream);
 
-// kv_f32: float32 cache (else bf16); o written in format o_fmt (ActFmt, lo plane
-// rows * H * d elements after the hi plane).  With pos_dev set, the query position is
-// read from device memory and clamped so that no slot at or past max_len is read.
-hipError_t launch_attention(bool kv_f32, const float *q, const void *kc, const void *vc,
+// kv_fmt: cache elements (AF_F32, AF_BF16 or AF_F16); o written in format o_fmt (ActFmt,
+// lo plane rows * H * d elements after the hi plane).  With pos_dev set, the query
+// position is read from device memory and clamped so that no slot at or past max_len is
+// read.
+hipError_t launch_attention(int kv_fmt, const float *q, const void *kc, const void *vc,
                             const int *valid_len, void *o, int o_fmt, int rows, int H, int d,
                             int max_len, int n_total, int head_off, int rows_per_seq,
                             int pos_base, const int *pos_dev, int prompt_len, hipStream_t st);
