@@ -45,9 +45,10 @@ def parse():
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--new-tokens", type=int, default=None)
     ap.add_argument("--layers", type=int, default=None, help="truncate the stack (development)")
-    ap.add_argument("--act", choices=("f32", "f16", "bf16"), default="f16",
+    ap.add_argument("--act", choices=("f32", "f16", "bf16"), default=None,
                     help="activation and KV-cache type of bf16 / int8 models: float32, fp16 "
-                         "or bf16")
+                         "or bf16 (default: fp16 for bf16 weights; bf16 for the int8 model, "
+                         "whose configuration states bf16 activations)")
     ap.add_argument("--loop", choices=("eager", "graph"), default="eager",
                     help="decode loop: one bloom_decode_step call per token, or bloom_generate "
                          "(replays of a captured decode step)")
@@ -366,7 +367,8 @@ def main():
     wl = bi.WORKLOADS[args.workload]
     m = wl.model if args.layers is None else wl.model.truncated(args.layers)
     if m.weight_dtype != "f32":
-        m = dataclasses.replace(m, activations=args.act)
+        act = args.act or ("bf16" if m.weight_dtype == "int8" else "f16")
+        m = dataclasses.replace(m, activations=act)
     B = args.batch
     P = wl.prompt_len
     n_new = args.new_tokens or wl.new_tokens

@@ -51,16 +51,26 @@ class Verdict:
     oracle: object
 
 
-def compare(shape, tensors, prompt, valid, run: GpuRun, tol_logit: float, widen_embed=False):
+def compare(shape, tensors, prompt, valid, run: GpuRun, tol_logit: float, widen_embed=False,
+            rows=None):
+    """Teacher-forced comparison of a GPU run with the oracle.  rows (optional): the
+    batch rows to compare; the sequences of a batch never interact (each attends to its
+    own keys only), so the oracle runs on those rows alone while the GPU ran the whole
+    batch with the kernels of its size."""
     om = oracle.OracleModel.from_storage(shape, tensors)
     if widen_embed:
         om.embed = np.asarray(om.embed, dtype=np.float64)
-    n_new = run.ids.shape[1]
-    res = oracle.greedy_generate(om, prompt, valid, n_new, forced=run.ids)
-    rel = float(np.linalg.norm(run.hidden - res.hidden) / np.linalg.norm(res.hidden))
+    ids, hidden = run.ids, run.hidden
+    if rows is not None:
+        rows = np.asarray(rows)
+        prompt, valid = np.asarray(prompt)[rows], np.asarray(valid)[rows]
+        ids, hidden = ids[rows], hidden[:, rows]
+    n_new = ids.shape[1]
+    res = oracle.greedy_generate(om, prompt, valid, n_new, forced=ids)
+    rel = float(np.linalg.norm(hidden - res.hidden) / np.linalg.norm(res.hidden))
     delta = 3.0 * tol_logit * res.rms
     ok = bool(np.all(res.chosen >= res.top1 - delta))
-    exact = run.ids == res.tokens
+    exact = ids == res.tokens
     return Verdict(rel, ok, float(exact.mean()), int((~exact).sum()), res)
 
 

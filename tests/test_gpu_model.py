@@ -236,3 +236,55 @@ def test_tp_share_176b_prompt_pass_batch32():
     v = compare(m, T, prompt, vl, run, 1e-2, widen_embed=True)
     print(f"176b rank-0 share L2 B32: hidden rel {v.hidden_rel:.2e}, exact ids {v.exact_frac:.3f}")
     assert v.hidden_rel <= 1e-2 and v.tokens_ok
+
+
+@pytest.mark.parametrize("act, batch", [("f16", 8), ("f16", 128), ("bf16", 128)])
+def test_tp_share_176b_two_layers_benchmarked_batches(act, batch):
+    """The 176B rank-0 share at the batches the benchmark runs (8: 32-row decode tiles;
+    128: 128-row decode tiles with split-K and the fused split-K residual LayerNorm, and
+    the 2048-row prompt pass on the large prompt tiles), 2 layers, compared on sampled
+    rows (the oracle runs those rows alone)."""
+    m = dataclasses.replace(bi.BLOOM_176B_TP8_RANK0.truncated(2), activations=act)
+    T, dw, cfg = upload(m)
+    prompt, vl = bi.prompts(m, batch, 16)
+    run = run_gpu(cfg, dw, prompt, vl, 4)
+    del dw
+    torch.cuda.empty_cache()
+    rows = list(range(batch)) if batch <= 8 else [0, 57, batch - 1]
+    v = compare(m, T, prompt, vl, run, 1e-2, widen_embed=True, rows=rows)
+    print(f"176b share L2 act {act} B{batch} (rows {rows}): hidden rel {v.hidden_rel:.2e}, "
+          f"exact ids {v.exact_frac:.3f}")
+    assert v.hidden_rel <= 1e-2 and v.tokens_ok
+
+
+@pytest.mark.parametrize("batch", [64, 128])
+def test_full_176b_int8_two_layers_benchmarked_batches(batch):
+    """The full 176B model with int8 weights and bf16 activations at the benchmarked
+    batches 64 and 128 (int8 decode tiles 64 x 256 / 128 x 128, the 1024- and 2048-row
+    int8 prompt passes), 2 layers, sampled rows against the oracle at 2e-2."""
+    m = bi.BLOOM_176B_INT8.truncated(2)
+    T, dw, cfg = upload(m)
+    prompt, vl = bi.prompts(m, batch, 16)
+    run = run_gpu(cfg, dw, prompt, vl, 3)
+    del dw
+    torch.cuda.empty_cache()
+    rows = [0, 31, batch - 1]
+    v = compare(m, T, prompt, vl, run, 2e-2, rows=rows)
+    print(f"176b int8 L2 B{batch} (rows {rows}): hidden rel {v.hidden_rel:.2e}, "
+          f"exact ids {v.exact_frac:.3f}")
+    assert v.hidden_rel <= 2e-2 and v.tokens_ok
+
+
+def test_bloom560m_full_depth_batch32_100_tokens():
+    """BLOOM-560m, 24 layers, batch 32, 100 greedy tokens (the benchmarked configuration
+    of that model), fp16 activations, sampled rows against the oracle."""
+    w = bi.WORKLOADS["bloom-560m"]
+    m = dataclasses.replace(w.model, activations="f16")
+    T, dw, cfg = upload(m)
+    prompt, valid = bi.prompts(m, 32, w.prompt_len)
+    run = run_gpu(cfg, dw, prompt, valid, 100)
+    rows = [0, 13, 31]
+    v = compare(m, T, prompt, valid, run, 1e-2, widen_embed=True, rows=rows)
+    print(f"560m B32 100 tokens (rows {rows}): hidden rel {v.hidden_rel:.2e}, "
+          f"exact ids {v.exact_frac:.3f} ({v.near_ties} accepted near-ties)")
+    assert v.hidden_rel <= 1e-2 and v.tokens_ok
