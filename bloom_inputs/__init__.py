@@ -161,7 +161,9 @@ class ModelShape:
     embed_ln: bool = True
     ln_eps: float = 1e-5
     activations: str = "auto"   # 'auto' (float32 for f32 weights, else bf16) | 'f32' | 'f16'
-                                # | 'bf16'
+                                # | 'bf16' | 'int8' (per-token int8 inputs of the linears,
+                                # with int8 weights)
+    kv_cache: str = "auto"      # 'auto' (the activation type) | 'f32' | 'f16' | 'bf16' | 'int8'
     init_std: float = 0.02      # standard deviation of the synthetic weights
 
     @property
@@ -177,8 +179,14 @@ class ModelShape:
         return "f32" if self.weight_dtype == "f32" else "bf16"
 
     @property
-    def kv_bytes(self) -> int:
-        return 4 if self.act_dtype == "f32" else 2
+    def kv_dtype(self) -> str:
+        """Element type of the KV cache (int8: one float32 scale per token and head)."""
+        return self.act_dtype if self.kv_cache == "auto" else self.kv_cache
+
+    @property
+    def kv_bytes(self) -> float:
+        """Bytes per cached key / value element (an int8 cache's scales included)."""
+        return {"f32": 4, "f16": 2, "bf16": 2, "int8": 1 + 4.0 / self.head_dim}[self.kv_dtype]
 
     @property
     def qkv_rows(self) -> int:

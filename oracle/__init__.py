@@ -15,6 +15,8 @@ from .bloom_oracle import (  # noqa: F401
     alibi_slopes,
     attention,
     decoder_layer,
+    dequantize_int8,
+    int8_rows,
     forward,
     gelu_tanh,
     greedy_argmax,
@@ -25,6 +27,7 @@ from .bloom_oracle import (  # noqa: F401
     lm_logits,
     masked_softmax,
     new_cache,
+    quantize_int8,
     round_bf16,
     sample_tokens,
     stop_rule,

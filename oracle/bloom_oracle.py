@@ -225,6 +225,8 @@ class OracleModel:
     lnf: tuple
     layers: List[dict]
     dtype: type = F64
+    act_round: Optional[object] = None   # the four linears' inputs (int8 activations)
+    kv_round: Optional[object] = None    # new keys / values (int8 KV cache)
 
     @classmethod
     def from_storage(cls, shape, tensors: dict, dtype=F64, widen_weights: bool = True):
@@ -245,13 +247,19 @@ class OracleModel:
         emb_ln = None
         if shape.embed_ln:
             emb_ln = (par(tensors["emb_ln_g"]), par(tensors["emb_ln_b"]))
+        # int8 activations (W8A8) and an int8 KV cache are part of what those modes
+        # compute; every other storage type is an implementation precision, and the
+        # oracle stays exact for it
+        act_int8 = getattr(shape, "act_dtype", None) == "int8"
+        kv_int8 = getattr(shape, "kv_dtype", None) == "int8"
         return cls(n_layer=len(layers), hidden=shape.hidden, n_head_total=shape.n_head_total,
                    head_offset=shape.head_offset, n_head_local=shape.n_head_local,
                    head_dim=shape.head_dim, ffn=shape.ffn, vocab=shape.vocab,
                    embed_ln=bool(shape.embed_ln), ln_eps=float(shape.ln_eps),
                    embed=_widen(tensors["embed"], pd), emb_ln=emb_ln,
                    lnf=(par(tensors["lnf_g"]), par(tensors["lnf_b"])), layers=layers,
-                   dtype=dtype)
+                   dtype=dtype, act_round=int8_rows if act_int8 else None,
+                   kv_round=int8_rows if kv_int8 else None)
 
     @property
     def slopes(self) -> np.ndarray:
@@ -283,10 +291,41 @@ def forward(model: OracleModel, tokens: np.ndarray, start: int, pad: np.ndarray,
     if model.embed_ln:
         x = layer_norm(x, model.emb_ln[0], model.emb_ln[1], model.ln_eps)
     for li, lw in enumerate(model.layers):
-        x = decoder_layer(model, lw, x, pad, start, cache[li])
+        x = decoder_layer(model, lw, x, pad, start, cache[li], act=model.act_round,
+                          kv=model.kv_round)
         if trace is not None:
             trace.append(x.copy())
     return layer_norm(x, model.lnf[0], model.lnf[1], model.ln_eps)
+
+
+def quantize_int8(a: np.ndarray):
+    """Symmetric int8 quantisation with one scale per slice along the last axis (the
+    pages name DeepSpeed's INT8 inference, "DeepSpeed Inference ...", Section VII.B,
+    without its scheme; this is the plain symmetric per-slice form): with
+    amax = max |a| over the slice, the code of each value is the nearest integer (ties
+    to even) to a * (127 / amax), clamped to [-127, 127], and the scale is amax / 127; a
+    slice of zeros has codes 0 and scale 0.  The decisions are taken in float32, the
+    precision the kernels take them in: a is rounded to float32, 127 / amax and the
+    product are float32 operations.  Returns (codes int8, scale float32 with a trailing
+    axis of 1)."""
+    f = np.asarray(a, dtype=np.float32)
+    amax = np.max(np.abs(f), axis=-1, keepdims=True)
+    with np.errstate(divide="ignore"):
+        inv = np.where(amax > 0, np.float32(127.0) / amax, np.float32(0.0)).astype(np.float32)
+    codes = np.clip(np.rint(f * inv), -127, 127).astype(np.int8)
+    scale = (amax / np.float32(127.0)).astype(np.float32)
+    return codes, scale
+
+
+def dequantize_int8(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """The value an int8 code stands for: code * scale, exact in float64."""
+    return np.asarray(codes, dtype=np.float64) * np.asarray(scale, dtype=np.float64)
+
+
+def int8_rows(a: np.ndarray) -> np.ndarray:
+    """The values an int8 path carries for a: quantize_int8 then dequantize_int8 (per
+    slice along the last axis)."""
+    return dequantize_int8(*quantize_int8(a))
 
 
 def round_bf16(a: np.ndarray) -> np.ndarray:
@@ -299,28 +338,33 @@ def round_bf16(a: np.ndarray) -> np.ndarray:
 
 
 def decoder_layer(model: OracleModel, lw: dict, x: np.ndarray, pad: np.ndarray, start: int,
-                  c: dict, act=None) -> np.ndarray:
+                  c: dict, act=None, kv=None) -> np.ndarray:
     """One pre-LayerNorm decoder layer ("DeepSpeed Inference ...", Section III.D) on the
     residual stream x [B, S, hidden] at positions start .. start+S-1, appending the
     layer's K/V to the cache entry ``c`` ({"k", "v"}: [B, H, start, d]).  Only the shape
     fields, ln_eps and the ALiBi slopes of ``model`` are used.
 
-    ``act`` (optional, e.g. round_bf16) is applied to the activations a path may store
-    in a narrower type: both LayerNorm outputs, the new keys and values, the attention
-    output and the GeLU output; the residual stream and q are left exact.  Without it
-    every value stays in ``model.dtype``."""
+    ``act`` (optional) is applied to the input of each of the four linears (both
+    LayerNorm outputs, the attention output [B, S, H*d], the GeLU output), and ``kv``
+    (optional; default ``act``) to the new keys and values [B, S, H, d], before they
+    enter the cache; the residual stream and q are left exact.  Either is a rounding to
+    a narrower type (e.g. round_bf16, a yardstick of a path's storage precision) or, for
+    the int8 modes, part of the method itself (int8_rows: W8A8 per-token activations;
+    per-(token, head) int8 keys and values).  Without them every value stays in
+    ``model.dtype``."""
     dt = model.dtype
     r = act if act is not None else (lambda t: t)
+    rk = kv if kv is not None else r
     pad = np.asarray(pad, dtype=np.int64)
     B, S = x.shape[:2]
     H, d = model.n_head_local, model.head_dim
     a = r(layer_norm(x, lw["ln1"][0], lw["ln1"][1], model.ln_eps))
     qkv = linear(a, lw["qkv"], lw["b_qkv"], dt).reshape(B, S, H, 3, d)
-    q, k, v = qkv[:, :, :, 0, :], r(qkv[:, :, :, 1, :]), r(qkv[:, :, :, 2, :])
+    q, k, v = qkv[:, :, :, 0, :], rk(qkv[:, :, :, 1, :]), rk(qkv[:, :, :, 2, :])
     c["k"] = np.concatenate([c["k"], k.transpose(0, 2, 1, 3)], axis=2)
     c["v"] = np.concatenate([c["v"], v.transpose(0, 2, 1, 3)], axis=2)
-    o = r(attention(q, c["k"], c["v"], model.slopes, pad, start))
-    x = x + linear(o.reshape(B, S, H * d), lw["dense"], lw["b_dense"], dt)
+    o = r(attention(q, c["k"], c["v"], model.slopes, pad, start).reshape(B, S, H * d))
+    x = x + linear(o, lw["dense"], lw["b_dense"], dt)
     a2 = r(layer_norm(x, lw["ln2"][0], lw["ln2"][1], model.ln_eps))
     u = r(gelu_tanh(linear(a2, lw["up"], lw["b_up"], dt)))
     return x + linear(u, lw["down"], lw["b_down"], dt)

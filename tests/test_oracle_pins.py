@@ -436,8 +436,9 @@ def test_round_bf16_closed_forms_and_torch():
 
 def test_decoder_layer_rounding_points(tiny_model):
     """The optional activation rounding of decoder_layer touches exactly the stored
-    activations (LN1 out, new k, new v, attention out, LN2 out, GeLU out) in that
-    order, never the residual stream; without it the layer is the one forward() runs."""
+    activations (LN1 out, new k, new v, attention out as the dense input rows, LN2 out,
+    GeLU out) in that order, never the residual stream; a separate kv hook takes the new
+    keys and values alone; without them the layer is the one forward() runs."""
     m, om = tiny_model
     ids, valid = bi.prompts(m, 2, 8, (8, 5))
     pad = 8 - valid
@@ -452,8 +453,14 @@ def test_decoder_layer_rounding_points(tiny_model):
 
     y = oracle.decoder_layer(om, om.layers[0], x0, pad, 0, {"k": empty, "v": empty}, act=record)
     B, S, h, H, d = 2, 8, m.hidden, m.n_head_local, m.head_dim
-    assert calls == [(B, S, h), (B, S, H, d), (B, S, H, d), (B, S, H, d), (B, S, h),
+    assert calls == [(B, S, h), (B, S, H, d), (B, S, H, d), (B, S, H * d), (B, S, h),
                      (B, S, m.ffn)]
+    acts, kvs = [], []
+    oracle.decoder_layer(om, om.layers[0], x0, pad, 0, {"k": empty, "v": empty},
+                         act=lambda t: acts.append(t.shape) or t,
+                         kv=lambda t: kvs.append(t.shape) or t)
+    assert acts == [(B, S, h), (B, S, H * d), (B, S, h), (B, S, m.ffn)]
+    assert kvs == [(B, S, H, d), (B, S, H, d)]
     trace = []
     oracle.forward(om, ids, 0, pad, oracle.new_cache(om, 2), trace=trace)
     np.testing.assert_array_equal(y, trace[0])
