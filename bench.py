@@ -27,6 +27,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, vendor peak
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (no sparsity)
+MFMA_INT8_PEAK_TOPS = 5000.0    # MI355X dense int8 matrix peak (W8A8 prompt passes)
 
 
 def log(*a):
@@ -45,10 +46,12 @@ def parse():
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--new-tokens", type=int, default=None)
     ap.add_argument("--layers", type=int, default=None, help="truncate the stack (development)")
-    ap.add_argument("--act", choices=("f32", "f16", "bf16"), default=None,
-                    help="activation and KV-cache type of bf16 / int8 models: float32, fp16 "
-                         "or bf16 (default: fp16 for bf16 weights; bf16 for the int8 model, "
-                         "whose configuration states bf16 activations)")
+    ap.add_argument("--act", choices=("f32", "f16", "bf16", "int8"), default=None,
+                    help="activation type of bf16 / int8 models: float32, fp16, bf16, or int8 "
+                         "(W8A8, int8 weights only) (default: fp16 for bf16 weights; bf16 for "
+                         "the int8 model, whose configuration states bf16 activations)")
+    ap.add_argument("--kv", choices=("auto", "f32", "f16", "bf16", "int8"), default="auto",
+                    help="KV-cache type (auto: the activation type)")
     ap.add_argument("--loop", choices=("eager", "graph"), default="eager",
                     help="decode loop: one bloom_decode_step call per token, or bloom_generate "
                          "(replays of a captured decode step)")
@@ -368,7 +371,7 @@ def main():
     m = wl.model if args.layers is None else wl.model.truncated(args.layers)
     if m.weight_dtype != "f32":
         act = args.act or ("bf16" if m.weight_dtype == "int8" else "f16")
-        m = dataclasses.replace(m, activations=act)
+        m = dataclasses.replace(m, activations=act, kv_cache=args.kv)
     B = args.batch
     P = wl.prompt_len
     n_new = args.new_tokens or wl.new_tokens
@@ -497,14 +500,14 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": (f"{m.weight_dtype} weights, {m.act_dtype} activations and KV"
+        "dtype": (f"{m.weight_dtype} weights, {m.act_dtype} activations, {m.kv_dtype} KV"
                   if m.weight_dtype != "f32" else "f32"),
         "data": "synthetic (seeded random weights and prompt ids)",
         "config": {"workload": m.name, "batch": B, "prompt_len": P, "new_tokens": n_new,
                    "layers": m.n_layer, "hidden": m.hidden, "heads_local": m.n_head_local,
                    "heads_total": m.n_head_total, "ffn_local": m.ffn, "vocab": m.vocab,
                    "weights": m.weight_dtype, "activations": m.act_dtype,
-                   "kv_cache": m.act_dtype, "greedy": not args.sample,
+                   "kv_cache": m.kv_dtype, "greedy": not args.sample,
                    "parallelism": "none (1 GPU)", "loop": args.loop,
                    "tokens": "sampled (temperature 0.8, top-p 0.9)" if args.sample else "greedy"},
         "tokens_per_s": round(B * n_new / (ms_per_step * 1e-3), 2),
@@ -512,7 +515,8 @@ def main():
         "prefill_tflops": round(prefill_flops(m, B, P) / (float(np.median(prefill_ms)) * 1e-3)
                                 / 1e12, 1),
         "prefill_mfma_frac": round(prefill_flops(m, B, P) / (float(np.median(prefill_ms)) * 1e-3)
-                                   / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                                   / 1e12 / (MFMA_INT8_PEAK_TOPS if m.act_dtype == "int8"
+                                             else MFMA_BF16_PEAK_TFLOPS), 4),
         "decode_step_ms": round(dec_step_ms, 4),
         "decode_step_gb": round(sb / 1e9, 3),
         "decode_step_hbm_frac": round(sb / (dec_step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

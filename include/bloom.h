@@ -57,8 +57,23 @@
  *     beyond fp16's range, 65504, become infinite) or float32 (BLOOM_F32).  The
  *     vector-ALU GEMV (batches of up to 4 rows) reads them in that type; for F16 / F32
  *     the MFMA GEMM reads two bf16 planes hi + lo of each value, each multiplied with
- *     the weights, which keeps the product to ~2^-17 of the float32 one.  kv_dtype
- *     must equal act_dtype: the KV cache holds keys and values in that type.
+ *     the weights, which keeps the product to ~2^-17 of the float32 one.
+ *   - act_dtype BLOOM_INT8_ROWSCALE (INT8_ROWSCALE weights only; hidden <= 16384):
+ *     W8A8, a variant of DeepSpeed's INT8 inference ([P3] Section VII.B names it
+ *     without its scheme).  Each of the four linears' input rows (one token's
+ *     LayerNorm output, attention output or GeLU output) is quantised symmetrically
+ *     with one float32 scale per row: scale = amax / 127 (amax = the row's largest
+ *     magnitude), code = nearest integer, ties to even, to v * (127 / amax) in float32,
+ *     clamped to [-127, 127]; a row of zeros has scale 0.  The linear is then
+ *     y = scale_row * s[r] * sum_k code[k] q[r][k] + bias (int32 sums on the int8 MFMA
+ *     for 5+ rows; the GEMV of up to 4 rows reads code * scale as float32, the same
+ *     product).  The residual stream, q, the final LayerNorm output and the LM head
+ *     stay as with F32 activations.
+ *   - kv_dtype equals act_dtype, or is BLOOM_INT8_ROWSCALE (any non-F32 weights): an
+ *     int8 KV cache holds, per (layer, row, head, slot), head_dim int8 codes of the key
+ *     (and of the value) with one float32 scale each in k_scale / v_scale, quantised as
+ *     above over the head_dim values; attention multiplies a key's dot product by its
+ *     scale and a value's probability weight by its scale.
  *
  * Layouts (all row-major, C order)
  *   embed            [vocab][hidden]             also the LM head (tied embeddings)
@@ -109,8 +124,8 @@ typedef struct bloom_config {
   int32_t weight_dtype; /* enum bloom_dtype */
   int32_t embed_ln;     /* 1: LayerNorm right after the embedding gather */
   float ln_eps;         /* LayerNorm epsilon (biased variance) */
-  int32_t act_dtype;    /* BLOOM_BF16, BLOOM_F16 or BLOOM_F32 (see Data types) */
-  int32_t kv_dtype;     /* KV cache element type: equal to act_dtype */
+  int32_t act_dtype;    /* BLOOM_BF16, BLOOM_F16, BLOOM_F32 or BLOOM_INT8_ROWSCALE (W8A8) */
+  int32_t kv_dtype;     /* KV cache element type: act_dtype or BLOOM_INT8_ROWSCALE */
 } bloom_config;
 
 /* Device pointers of one decoder layer.  s_* are the int8 row scales (fp16) and must be
@@ -135,7 +150,10 @@ typedef struct bloom_weights {
 
 /* KV cache.  k and v are caller-owned device buffers of
  * n_layer * max_batch * n_head_local * max_len * head_dim elements of kv_dtype
- * (float32, bf16 or fp16).  len and prompt_len are host-side: bloom_prefill sets prompt_len
+ * (float32, bf16, fp16 or int8).  For an int8 cache, k_scale and v_scale are
+ * caller-owned float32 device buffers [n_layer][max_batch][n_head_local][max_len]
+ * (4-byte aligned; EINVAL if missing), one scale per key / value vector; for other
+ * types they are ignored.  len and prompt_len are host-side: bloom_prefill sets prompt_len
  * and len = prompt_len; bloom_decode_step writes slot len and then increments it, and
  * its capacity check uses len.  Slot j holds absolute position j of every row (left
  * padding slots are written but never attended).  A caller may reset len to 0.
@@ -155,6 +173,7 @@ typedef struct bloom_kv_cache {
   int32_t len;
   int32_t prompt_len;
   int32_t *d_len;
+  void *k_scale, *v_scale;
 } bloom_kv_cache;
 
 /* Seeded synthetic weights, written on the GPU into the caller's buffers behind w (the
@@ -344,17 +363,38 @@ int alibi_masked_softmax(const void *d_scores, int32_t in_dtype, const int32_t *
 
 /* Copy n_new new key/value vectors into the cache ([P4] Efficient PyTorch
  * Implementation: the KV "past" kept in a layout that needs no reshape or transpose).
- * d_k, d_v [batch][n_head_local][n_new][head_dim] (activation type) go to slots
- * [pos, pos + n_new) of layer `layer`, rows 0..batch-1.  Does not change kv->len.
+ * d_k, d_v [batch][n_head_local][n_new][head_dim] (the cache's element type; float32
+ * for an int8 cache, which quantises each vector as the forward pass does and writes
+ * its scale) go to slots [pos, pos + n_new) of layer `layer`, rows 0..batch-1.  Does
+ * not change kv->len.
  * ECAPACITY if pos + n_new > kv->max_len or batch > kv->max_batch. */
 int kv_cache_append(const bloom_config *cfg, bloom_kv_cache *kv, int32_t layer, int32_t batch,
                     int32_t pos, const void *d_k, const void *d_v, int32_t n_new, void *stream);
+
+/* One linear layer of the decoder as a standalone call ("DeepSpeed Inference ...",
+ * Section III.C: the weight-streaming GeMM of the QKV, output, MLP-up and MLP-down
+ * projections; the same kernels and plans as the forward pass at these sizes):
+ *   y[m][n] = sum_k x[m][k] W[n][k]  (* s[n] for int8 weights)  (+ b[n] if d_b),
+ * for m < M, n < N.  d_x float32 [M][K] is first stored as the forward pass stores a
+ * linear's input under cfg->act_dtype (bf16 or fp16 rounding; float32 / two bf16
+ * planes; int8 codes with one scale per row, see Data types); d_w [N][K] of
+ * cfg->weight_dtype; d_s fp16 [N] for INT8_ROWSCALE weights (NULL otherwise); d_b [N]
+ * bias in the parameter type (bf16; float32 for F32 weights), nullable; d_y float32
+ * [M][N].  The other fields of cfg only select types.  EINVAL for M < 0, N < 1, K < 1,
+ * K not a multiple of 64 (BF16 / INT8_ROWSCALE weights) or missing pointers;
+ * EWORKSPACE if ws_bytes < bloom_linear_workspace_bytes (d_ws may be NULL when that is
+ * 0).  M = 0 is a no-op. */
+int bloom_linear_workspace_bytes(const bloom_config *cfg, int32_t M, int32_t N, int32_t K,
+                                 size_t *bytes);
+int bloom_linear(const bloom_config *cfg, int32_t M, int32_t N, int32_t K, const float *d_x,
+                 const void *d_w, const void *d_s, const void *d_b, float *d_y, void *d_ws,
+                 size_t ws_bytes, void *stream);
 
 /* Dynamic batch extraction ("Hugging Face BLOOM Inference Optimization", Webserver
  * Architecture and Request Handling: requests that have finished are taken out of the
  * running batch instead of waiting for the longest one).  Compacts the KV cache in
  * place: for i < n_keep, row i of every layer and head takes the slots [0, kv->len) of
- * row keep[i].  keep is a HOST array of n_keep row indices, strictly increasing, each
+ * row keep[i] (an int8 cache's slot scales with them).  keep is a HOST array of n_keep row indices, strictly increasing, each
  * in [0, batch); rows n_keep .. batch-1 keep stale contents.  The caller compacts its
  * own per-row arrays (tokens, valid lengths) the same way and continues with batch =
  * n_keep.  Asynchronous on `stream` (the indices are passed by value, so keep may be

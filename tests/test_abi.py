@@ -40,12 +40,12 @@ def test_status_strings():
 
 def test_struct_layout_matches_header():
     # 12 int32 + 1 float; 16 pointers; 5 pointers + 1 pointer; 2 pointers + 4 int32 +
-    # 1 pointer; 2 int32 + 7 pointers + 1 size_t
+    # 3 pointers; 2 int32 + 7 pointers + 1 size_t
     assert ctypes.sizeof(tb.bloom_gen_control) == 8 + 7 * 8 + 8
     assert ctypes.sizeof(tb.bloom_config) == 52
     assert ctypes.sizeof(tb.bloom_layer_weights) == 16 * 8
     assert ctypes.sizeof(tb.bloom_weights) == 6 * 8
-    assert ctypes.sizeof(tb.bloom_kv_cache) == 2 * 8 + 4 * 4 + 8
+    assert ctypes.sizeof(tb.bloom_kv_cache) == 2 * 8 + 4 * 4 + 3 * 8
 
 
 def _cfg(**kw):
@@ -74,6 +74,37 @@ def test_workspace_rejects_bad_dtype():
     c = _cfg()
     c.weight_dtype = 7
     assert _err(tb.bloom_workspace_bytes, c, 1, 16) == tb.BLOOM_EDTYPE
+
+
+@pytest.mark.parametrize("weights, act, kv, code", [
+    ("int8", "int8", "int8", tb.BLOOM_OK),       # W8A8 with an int8 cache
+    ("int8", "int8", "f16", tb.BLOOM_EDTYPE),    # the cache holds act_dtype or int8
+    ("int8", "f16", "int8", tb.BLOOM_OK),        # int8 cache under fp16 activations
+    ("bf16", "bf16", "int8", tb.BLOOM_OK),
+    ("bf16", "int8", "int8", tb.BLOOM_EDTYPE),   # int8 activations need int8 weights
+    ("f32", "f32", "int8", tb.BLOOM_EDTYPE),     # the float32 model is float32 throughout
+])
+def test_int8_activation_and_cache_types(weights, act, kv, code):
+    shape = dataclasses.replace(bi.BLOOM_176B_INT8.truncated(2), weight_dtype=weights,
+                                activations=act, kv_cache=kv)
+    c = tb.make_config(shape)
+    if code == tb.BLOOM_OK:
+        assert tb.bloom_workspace_bytes(c, 4, 16) > 0
+    else:
+        assert _err(tb.bloom_workspace_bytes, c, 4, 16) == code
+
+
+def test_int8_cache_requires_scale_buffers():
+    shape = dataclasses.replace(bi.BLOOM_176B_INT8.truncated(2), activations="int8",
+                                kv_cache="int8")
+    f = _Fake(shape)
+    assert _prefill(f) == tb.BLOOM_EINVAL                          # no k_scale / v_scale
+    f.kv.k_scale = 0x1000
+    assert _prefill(f) == tb.BLOOM_EINVAL                          # v_scale still missing
+    f.kv.v_scale = 0x1002                                          # not 4-byte aligned
+    assert _prefill(f) == tb.BLOOM_EINVAL
+    f.kv.v_scale = 0x1000
+    assert _prefill(f, ws_bytes=1024) == tb.BLOOM_EWORKSPACE       # checks passed
 
 
 def test_workspace_grows_with_batch_and_prompt():

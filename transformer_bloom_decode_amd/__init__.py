@@ -52,7 +52,8 @@ class bloom_weights(ctypes.Structure):
 
 class bloom_kv_cache(ctypes.Structure):
     _fields_ = [("k", _c_void_p), ("v", _c_void_p), ("max_batch", _i32), ("max_len", _i32),
-                ("len", _i32), ("prompt_len", _i32), ("d_len", _c_void_p)]
+                ("len", _i32), ("prompt_len", _i32), ("d_len", _c_void_p),
+                ("k_scale", _c_void_p), ("v_scale", _c_void_p)]
 
 
 class bloom_gen_control(ctypes.Structure):
@@ -111,6 +112,10 @@ def _load():
                                        ctypes.c_double, vp]
     lib.bloom_sample_tokens_static.argtypes = [vp, _i32, _i32, vp, vp, vp, vp, vp]
     lib.bloom_sample_scratch_limit.argtypes = [_i32, _i32, P(_i32), P(ctypes.c_size_t)]
+    lib.bloom_linear_workspace_bytes.argtypes = [P(bloom_config), _i32, _i32, _i32,
+                                                 P(ctypes.c_size_t)]
+    lib.bloom_linear.argtypes = [P(bloom_config), _i32, _i32, _i32, vp, vp, vp, vp, vp, vp,
+                                 ctypes.c_size_t, vp]
     lib.bloom_timer_enable.argtypes = [_i32]
     lib.bloom_timer_disable.argtypes = []
     lib.bloom_timer_read.argtypes = [_i32, P(ctypes.c_double), P(_i32), P(ctypes.c_double)]
@@ -119,7 +124,7 @@ def _load():
                  "alibi_masked_softmax", "kv_cache_append", "kv_cache_compact",
                  "bloom_lm_logits", "bloom_sample_tokens", "bloom_sample_workspace_bytes",
                  "bloom_sample_tokens_static", "bloom_sample_scratch_limit",
-                 "bloom_init_weights",
+                 "bloom_init_weights", "bloom_linear", "bloom_linear_workspace_bytes",
                  "bloom_timer_enable",
                  "bloom_timer_disable", "bloom_timer_read", "bloom_timer_pause"):
         getattr(lib, name).restype = ctypes.c_int
@@ -273,6 +278,19 @@ def bloom_lm_logits(cfg, weights, batch: int, hidden, logits, ws, stream=None):
            "bloom_lm_logits")
 
 
+def bloom_linear_workspace_bytes(cfg, M: int, N: int, K: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib.bloom_linear_workspace_bytes(ctypes.byref(cfg), M, N, K, ctypes.byref(out)),
+           "bloom_linear_workspace_bytes")
+    return out.value
+
+
+def bloom_linear(cfg, M: int, N: int, K: int, x, w, s, b, y, ws, stream=None):
+    """y = x W^T (* s) (+ b) with the library's linear kernels (bloom.h, bloom_linear)."""
+    _check(lib.bloom_linear(ctypes.byref(cfg), M, N, K, _ptr(x), _ptr(w), _ptr(s), _ptr(b),
+                            _ptr(y), _ptr(ws), _nbytes(ws), _stream(stream)), "bloom_linear")
+
+
 def bloom_sample_workspace_bytes(batch: int, vocab: int) -> int:
     out = ctypes.c_size_t(0)
     _check(lib.bloom_sample_workspace_bytes(batch, vocab, ctypes.byref(out)),
@@ -358,13 +376,16 @@ def _nbytes(t) -> int:
 
 def make_config(shape) -> bloom_config:
     """bloom_config from any object with the shape attributes (n_layer, hidden, ...;
-    act_dtype 'f32', 'f16' or 'bf16', which also sets the KV-cache type)."""
+    act_dtype 'f32', 'f16', 'bf16' or 'int8'; kv_dtype, default the activation type)."""
     act = DTYPE_CODES[getattr(shape, "act_dtype", "f32" if shape.weight_dtype == "f32"
                               else "bf16")]
+    kv = DTYPE_CODES[getattr(shape, "kv_dtype", None) or
+                     getattr(shape, "act_dtype", "f32" if shape.weight_dtype == "f32"
+                             else "bf16")]
     return bloom_config(shape.n_layer, shape.hidden, shape.n_head_total, shape.head_offset,
                         shape.n_head_local, shape.head_dim, shape.ffn, shape.vocab,
                         DTYPE_CODES[shape.weight_dtype], int(bool(shape.embed_ln)),
-                        float(shape.ln_eps), act, act)
+                        float(shape.ln_eps), act, kv)
 
 
 def bloom_init_weights(cfg, weights, seed: int = 0, sigma: float = 0.02, stream=None):
@@ -408,23 +429,33 @@ class DeviceWeights:
 
 class KVCache:
     """Caller-owned KV cache buffers ([n_layer][max_batch][H][max_len][d]) and the struct.
-    device_len=True also keeps the length in device memory (bloom_kv_cache.d_len)."""
+    device_len=True also keeps the length in device memory (bloom_kv_cache.d_len).  An
+    int8 cache also holds float32 scales k_scale / v_scale [n_layer][max_batch][H][max_len];
+    with `fill` given, the scales take that value and the int8 codes -128."""
 
     def __init__(self, cfg: bloom_config, max_batch: int, max_len: int, device="cuda",
                  fill: Optional[float] = None, device_len: bool = False):
         import torch
-        dt = {BLOOM_F32: torch.float32, BLOOM_F16: torch.float16}.get(cfg.kv_dtype,
-                                                                      torch.bfloat16)
+        dt = {BLOOM_F32: torch.float32, BLOOM_F16: torch.float16,
+              BLOOM_INT8_ROWSCALE: torch.int8}.get(cfg.kv_dtype, torch.bfloat16)
         shape = (cfg.n_layer, max_batch, cfg.n_head_local, max_len, cfg.head_dim)
-        if fill is None:
-            self.k = torch.empty(shape, dtype=dt, device=device)
-            self.v = torch.empty(shape, dtype=dt, device=device)
-        else:
-            self.k = torch.full(shape, fill, dtype=dt, device=device)
-            self.v = torch.full(shape, fill, dtype=dt, device=device)
+
+        def buf(shp, dtype, value):
+            if fill is None:
+                return torch.empty(shp, dtype=dtype, device=device)
+            return torch.full(shp, value, dtype=dtype, device=device)
+
+        # int8 codes lie in [-127, 127]: a filled int8 cache holds -128, never a code
+        code_fill = -128 if dt == torch.int8 else fill
+        self.k = buf(shape, dt, code_fill)
+        self.v = buf(shape, dt, code_fill)
+        self.k_scale = self.v_scale = None
+        if cfg.kv_dtype == BLOOM_INT8_ROWSCALE:
+            self.k_scale = buf(shape[:-1], torch.float32, fill)
+            self.v_scale = buf(shape[:-1], torch.float32, fill)
         self.d_len = torch.zeros(1, dtype=torch.int32, device=device) if device_len else None
         self.struct = bloom_kv_cache(_ptr(self.k), _ptr(self.v), max_batch, max_len, 0, 0,
-                                     _ptr(self.d_len))
+                                     _ptr(self.d_len), _ptr(self.k_scale), _ptr(self.v_scale))
 
     @property
     def len(self) -> int:

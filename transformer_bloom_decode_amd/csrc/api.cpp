@@ -44,22 +44,40 @@ int hip_fail(hipError_t e) {
 struct WsPlan {
   size_t gen, cur, nxt, hfix, done;   // generation loop state (same offsets for every pass)
   size_t x, xa, q, o, u, af, amv, ami, part, total;
+  size_t stg;   // int8 activations: float32 attention / GeLU rows before quantisation
+  size_t kvs;   // int8 KV cache: float32 new keys and values [rows][H][2][d]
   int lm_blocks;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-// The activation type as a storage format (ActFmt): AF_BF16, AF_F32 or AF_F16.
-int act_fmt(const bloom_config *c) {
-  return c->act_dtype == BLOOM_F32 ? AF_F32 : (c->act_dtype == BLOOM_F16 ? AF_F16 : AF_BF16);
+int dtype_fmt(int dt) {
+  switch (dt) {
+    case BLOOM_F32: return AF_F32;
+    case BLOOM_F16: return AF_F16;
+    case BLOOM_INT8_ROWSCALE: return AF_I8;
+    default: return AF_BF16;
+  }
 }
+// The activation type as a storage format (ActFmt): AF_BF16, AF_F32, AF_F16 or AF_I8.
+int act_fmt(const bloom_config *c) { return dtype_fmt(c->act_dtype); }
+bool act_q8(const bloom_config *c) { return act_fmt(c) == AF_I8; }
+// The final LayerNorm's output is never quantised: with int8 activations the LM head
+// reads it as float32 activations.
+int lm_act_fmt(const bloom_config *c) { return act_q8(c) ? AF_F32 : act_fmt(c); }
 // Bytes per activation element in the workspace: bf16 2; float32 / fp16 activations 4
-// (float32, fp16, or the two bf16 planes the MFMA GEMM reads).
+// (float32, fp16, or the two bf16 planes the MFMA GEMM reads); int8 4 (the codes, or
+// the codes' float32 values the GEMV reads) plus one float32 scale per row.
 int act_bytes(const bloom_config *c) { return act_fmt(c) == AF_BF16 ? 2 : 4; }
-int kv_fmt(const bloom_config *c) {
-  return c->kv_dtype == BLOOM_F32 ? AF_F32 : (c->kv_dtype == BLOOM_F16 ? AF_F16 : AF_BF16);
+size_t act_region(const bloom_config *c, size_t rows, size_t n) {
+  return rows * n * act_bytes(c) + (act_q8(c) ? rows * 4 : 0);
 }
-int kv_bytes(const bloom_config *c) { return kv_fmt(c) == AF_F32 ? 4 : 2; }
+int kv_fmt(const bloom_config *c) { return dtype_fmt(c->kv_dtype); }
+bool kv_q8(const bloom_config *c) { return kv_fmt(c) == AF_I8; }
+int kv_bytes(const bloom_config *c) {
+  const int f = kv_fmt(c);
+  return f == AF_F32 ? 4 : (f == AF_I8 ? 1 : 2);
+}
 int wtype(const bloom_config *c) {
   return c->weight_dtype == BLOOM_F32 ? WT_F32 : (c->weight_dtype == BLOOM_BF16 ? WT_BF16 : WT_INT8);
 }
@@ -80,11 +98,13 @@ WsPlan plan_ws(const bloom_config *c, int batch, int tokens_per_row) {
   p.hfix = take((size_t)batch * c->hidden * sizeof(float));
   p.done = take((size_t)batch * sizeof(int));
   p.x = take(M * c->hidden * 4);
-  p.xa = take(M * c->hidden * act);
+  p.xa = take(act_region(c, M, c->hidden));
   p.q = take(M * hd * 4);
-  p.o = take(M * hd * act);
-  p.u = take(M * (size_t)c->ffn * act);
+  p.o = take(act_region(c, M, hd));
+  p.u = take(act_region(c, M, (size_t)c->ffn));
   p.af = take((size_t)batch * c->hidden * act);
+  p.stg = act_q8(c) ? take(M * std::max(hd, (size_t)c->ffn) * 4) : 0;
+  p.kvs = kv_q8(c) ? take(M * hd * 2 * 4) : 0;
   p.lm_blocks = lm_blocks(c);
   p.amv = take((size_t)batch * p.lm_blocks * 4);
   p.ami = take((size_t)batch * p.lm_blocks * 4);
@@ -118,16 +138,23 @@ int check_config(const bloom_config *c) {
   if (c->weight_dtype != BLOOM_F32 && c->weight_dtype != BLOOM_BF16 &&
       c->weight_dtype != BLOOM_INT8_ROWSCALE)
     return BLOOM_EDTYPE;
-  // activations and the KV cache: float32, bf16 or fp16 (float32 only for float32
-  // weights); the cache holds the activation type
-  if (c->act_dtype != BLOOM_F32 && c->act_dtype != BLOOM_BF16 && c->act_dtype != BLOOM_F16)
+  // activations: float32, bf16, fp16, or int8 (with int8 weights: W8A8); float32 only
+  // for float32 weights.  The KV cache holds the activation type, or int8.
+  if (c->act_dtype != BLOOM_F32 && c->act_dtype != BLOOM_BF16 && c->act_dtype != BLOOM_F16 &&
+      c->act_dtype != BLOOM_INT8_ROWSCALE)
     return BLOOM_EDTYPE;
   if (c->weight_dtype == BLOOM_F32 && c->act_dtype != BLOOM_F32) return BLOOM_EDTYPE;
-  if (c->kv_dtype != c->act_dtype) return BLOOM_EDTYPE;
+  if (c->act_dtype == BLOOM_INT8_ROWSCALE && c->weight_dtype != BLOOM_INT8_ROWSCALE)
+    return BLOOM_EDTYPE;
+  if (c->kv_dtype != c->act_dtype &&
+      !(c->kv_dtype == BLOOM_INT8_ROWSCALE && c->weight_dtype != BLOOM_F32))
+    return BLOOM_EDTYPE;
   if (c->weight_dtype != BLOOM_F32) {
     const int hd = c->n_head_local * c->head_dim;
     if (c->hidden % 64 || c->ffn % 64 || hd % 64) return BLOOM_EINVAL;
   }
+  // int8 activations: the LayerNorm kernels quantise whole rows held in registers
+  if (c->act_dtype == BLOOM_INT8_ROWSCALE && c->hidden > 16384) return BLOOM_EINVAL;
   return BLOOM_OK;
 }
 
@@ -149,8 +176,10 @@ int check_weights(const bloom_config *c, const bloom_weights *w) {
 }
 
 int check_kv(const bloom_config *c, const bloom_kv_cache *kv) {
-  (void)c;
   if (!kv || !kv->k || !kv->v || kv->max_batch <= 0 || kv->max_len <= 0) return BLOOM_EINVAL;
+  if (c->kv_dtype == BLOOM_INT8_ROWSCALE &&
+      (!kv->k_scale || !kv->v_scale || ((uintptr_t)kv->k_scale & 3) || ((uintptr_t)kv->v_scale & 3)))
+    return BLOOM_EINVAL;
   if (((uintptr_t)kv->d_len & 3) != 0) return BLOOM_EINVAL;
   if (kv->max_len > kMaxLen) return BLOOM_EINVAL;
   if (kv->len < 0 || kv->len > kv->max_len || kv->prompt_len < 0) return BLOOM_EINVAL;
@@ -265,12 +294,15 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
   float *amv = (float *)(ws + wp.amv);
   int *ami = (int *)(ws + wp.ami);
   float *part = (float *)(ws + wp.part);
+  float *stg = act_q8(c) ? (float *)(ws + wp.stg) : nullptr;
+  float *kvs = kv_q8(c) ? (float *)(ws + wp.kvs) : nullptr;
 
   hipError_t err = launch_embed(f32, d_tokens, w->embed, w->emb_ln_g, w->emb_ln_b, x, M, h,
                                 c->vocab, c->embed_ln, c->ln_eps, st);
   if (err != hipSuccess) return hip_fail(err);
 
   const size_t layer_stride = (size_t)kv->max_batch * H * kv->max_len * d * kv_bytes(c);
+  const size_t scale_stride = (size_t)kv->max_batch * H * kv->max_len;   // int8 cache
   const LinearPlan p_qkv = plan_linear(wdt, M, 3 * hd, h, false, act);
   const LinearPlan p_dense = plan_linear(wdt, M, h, hd, false, act);
   const LinearPlan p_up = plan_linear(wdt, M, F, h, false, act);
@@ -278,6 +310,11 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
   // every activation is written in the form its consumer reads
   const int fmt_qkv = plan_x_fmt(p_qkv), fmt_dense = plan_x_fmt(p_dense);
   const int fmt_up = plan_x_fmt(p_up), fmt_down = plan_x_fmt(p_down);
+  // int8 activation codes (AF_I8) carry one scale per row after the codes, which the
+  // consuming linear's epilogue applies
+  auto xscale = [&](int fmt, const void *buf, size_t n) -> const float * {
+    return fmt == AF_I8 ? (const float *)((const char *)buf + (size_t)M * n) : nullptr;
+  };
 
   // K-split dense / down projections reduce their partials in the kernel that also adds
   // bias and residual and runs the next LayerNorm (LN2 after dense, the next layer's LN1
@@ -287,12 +324,14 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
   };
   // One activation row and a short hidden size: LN1 and LN2 run as the prologue of the
   // QKV and MLP-up GEMVs instead of as launches of their own.
-  const bool ln_in_gemv = !f32 && gemv_ln_supported(wdt, M, h);
+  const bool ln_in_gemv = !f32 && !act_q8(c) && gemv_ln_supported(wdt, M, h);
   bool ln1_done = false;   // xa already holds LN1(x) of this layer
   for (int l = 0; l < c->n_layer; ++l) {
     const bloom_layer_weights &L = w->layers[l];
     void *kc = (char *)kv->k + l * layer_stride;
     void *vc = (char *)kv->v + l * layer_stride;
+    float *ksc = kvs ? (float *)kv->k_scale + l * scale_stride : nullptr;
+    float *vsc = kvs ? (float *)kv->v_scale + l * scale_stride : nullptr;
 
     if (!ln1_done && !ln_in_gemv) {
       err = launch_layernorm(f32, x, 1, 0, L.ln1_g, L.ln1_b, xa, fmt_qkv, nullptr, M, h,
@@ -310,6 +349,8 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
     e.H = H; e.d = d; e.max_len = kv->max_len;
     e.pos_base = pos_base; e.pos_dev = d_pos; e.rows_per_seq = tpr;
     e.q_scale = 1.0f / sqrtf((float)d);
+    e.xscale = xscale(fmt_qkv, xa, h);
+    e.kv_stage = kvs;
     if (ln_in_gemv)
       err = timed(kernel_class(p_qkv), wbytes(3 * hd, h), st, [&] {
         return launch_gemv_ln(wdt, act, 3 * hd, h, x, L.ln1_g, L.ln1_b, c->ln_eps, L.w_qkv, e,
@@ -318,9 +359,24 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
     else
       err = timed_linear(wdt, p_qkv, xa, L.w_qkv, part, e, st, wbytes(3 * hd, h));
     if (err != hipSuccess) return hip_fail(err);
+    if (kvs) {
+      // int8 cache: the staged new keys and values [M][H][2][d] -> codes + slot scales
+      KvQuantArgs qa{};
+      qa.k = kvs; qa.v = kvs + d;
+      qa.sb = (long)tpr * H * 2 * d; qa.st = (long)H * 2 * d; qa.sh = 2 * d;
+      qa.batch = batch; qa.n = tpr; qa.H = H; qa.d = d;
+      qa.kc = (int8_t *)kc; qa.vc = (int8_t *)vc; qa.ks = ksc; qa.vs = vsc;
+      qa.max_len = kv->max_len; qa.pos_base = pos_base; qa.pos_dev = d_pos;
+      err = launch_kv_quant(qa, st);
+      if (err != hipSuccess) return hip_fail(err);
+    }
 
-    err = launch_attention(kv_fmt(c), q, kc, vc, d_valid, o, fmt_dense, M, H, d, kv->max_len,
-                           c->n_head_total, c->head_offset, tpr, pos_base, d_pos, prompt_len, st);
+    // int8 activations: attention writes float32 rows, quantised per row for the dense
+    // projection
+    err = launch_attention(kv_fmt(c), q, kc, vc, ksc, vsc, d_valid, stg ? (void *)stg : o,
+                           stg ? AF_F32 : fmt_dense, M, H, d, kv->max_len, c->n_head_total,
+                           c->head_offset, tpr, pos_base, d_pos, prompt_len, st);
+    if (err == hipSuccess && stg) err = launch_quant_rows(stg, M, hd, o, fmt_dense, st);
     if (err != hipSuccess) return hip_fail(err);
 
     EpiParams r{};
@@ -328,13 +384,14 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
     r.bias = L.b_dense;
     r.scale = (const uint16_t *)L.s_dense;
     r.out = x; r.ld = h;
+    r.xscale = xscale(fmt_dense, o, hd);
     const bool fuse_dense = fuse_ln(p_dense);
     err = timed_linear(wdt, p_dense, o, L.w_dense, part, r, st, wbytes(h, hd), !fuse_dense);
     if (err != hipSuccess) return hip_fail(err);
 
     if (fuse_dense)
-      err = launch_splitk_resid_ln(part, p_dense.splits, M, L.s_dense, L.b_dense, x, L.ln2_g,
-                                   L.ln2_b, xa, fmt_up, h, c->ln_eps, st);
+      err = launch_splitk_resid_ln(part, p_dense.splits, M, r.xscale, L.s_dense, L.b_dense, x,
+                                   L.ln2_g, L.ln2_b, xa, fmt_up, h, c->ln_eps, st);
     else if (!ln_in_gemv)
       err = launch_layernorm(f32, x, 1, 0, L.ln2_g, L.ln2_b, xa, fmt_up, nullptr, M, h,
                              c->ln_eps, st);
@@ -347,12 +404,18 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
     g.out = u; g.ld = F;
     g.out_fmt = fmt_down;
     g.plane = (size_t)M * F;
+    g.xscale = xscale(fmt_up, xa, h);
+    if (stg) {   // int8 activations: GeLU rows in float32, then quantised per row
+      g.out = stg;
+      g.out_fmt = AF_F32;
+    }
     if (ln_in_gemv && !fuse_dense)
       err = timed(kernel_class(p_up), wbytes(F, h), st, [&] {
         return launch_gemv_ln(wdt, act, F, h, x, L.ln2_g, L.ln2_b, c->ln_eps, L.w_up, g, st);
       });
     else
       err = timed_linear(wdt, p_up, xa, L.w_up, part, g, st, wbytes(F, h));
+    if (err == hipSuccess && stg) err = launch_quant_rows(stg, M, F, u, fmt_down, st);
     if (err != hipSuccess) return hip_fail(err);
 
     EpiParams dn{};
@@ -360,13 +423,14 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
     dn.bias = L.b_down;
     dn.scale = (const uint16_t *)L.s_down;
     dn.out = x; dn.ld = h;
+    dn.xscale = xscale(fmt_down, u, F);
     const bool fuse_down = l + 1 < c->n_layer && fuse_ln(p_down) && !ln_in_gemv;
     err = timed_linear(wdt, p_down, u, L.w_down, part, dn, st, wbytes(h, F), !fuse_down);
     if (err != hipSuccess) return hip_fail(err);
     if (fuse_down) {
       const bloom_layer_weights &N1 = w->layers[l + 1];
-      err = launch_splitk_resid_ln(part, p_down.splits, M, L.s_down, L.b_down, x, N1.ln1_g,
-                                   N1.ln1_b, xa, fmt_qkv, h, c->ln_eps, st);
+      err = launch_splitk_resid_ln(part, p_down.splits, M, dn.xscale, L.s_down, L.b_down, x,
+                                   N1.ln1_g, N1.ln1_b, xa, fmt_qkv, h, c->ln_eps, st);
       if (err != hipSuccess) return hip_fail(err);
       ln1_done = true;
     }
@@ -388,7 +452,7 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
     // the LM head runs on chunks of up to 128 rows; the final LayerNorm writes each
     // chunk in the form its plan reads (two bf16 planes: each chunk its own pair)
     const int rows = std::min(128, batch - r0);
-    const LinearPlan p_lm = plan_linear(wdt_lm, rows, c->vocab, h, true, act);
+    const LinearPlan p_lm = plan_linear(wdt_lm, rows, c->vocab, h, true, lm_act_fmt(c));
     void *X = (char *)af + (size_t)r0 * h * abytes;
     err = launch_layernorm(f32, x + (size_t)r0 * tpr * h, tpr, tpr - 1, w->lnf_g, w->lnf_b, X,
                            plan_x_fmt(p_lm), d_hidden ? d_hidden + (size_t)r0 * h : nullptr, rows,
@@ -647,6 +711,22 @@ int kv_cache_append(const bloom_config *cfg, bloom_kv_cache *kv, int32_t layer, 
   const size_t kvb = kv_bytes(cfg);
   const size_t layer_stride =
       (size_t)kv->max_batch * cfg->n_head_local * kv->max_len * cfg->head_dim * kvb;
+  if (kv_q8(cfg)) {
+    // float32 inputs, quantised per (row, head, slot) as the forward pass does
+    const int H = cfg->n_head_local, d = cfg->head_dim;
+    const size_t scale_stride = (size_t)kv->max_batch * H * kv->max_len;
+    KvQuantArgs qa{};
+    qa.k = (const float *)d_k; qa.v = (const float *)d_v;
+    qa.sb = (long)H * n_new * d; qa.st = d; qa.sh = (long)n_new * d;
+    qa.batch = batch; qa.n = n_new; qa.H = H; qa.d = d;
+    qa.kc = (int8_t *)kv->k + layer * layer_stride;
+    qa.vc = (int8_t *)kv->v + layer * layer_stride;
+    qa.ks = (float *)kv->k_scale + layer * scale_stride;
+    qa.vs = (float *)kv->v_scale + layer * scale_stride;
+    qa.max_len = kv->max_len; qa.pos_base = pos;
+    const hipError_t qe = launch_kv_quant(qa, (hipStream_t)stream);
+    return qe == hipSuccess ? BLOOM_OK : hip_fail(qe);
+  }
   hipError_t err = launch_kv_append(kv_fmt(cfg) == AF_F32, d_k, d_v,
                                     (char *)kv->k + layer * layer_stride,
                                     (char *)kv->v + layer * layer_stride, batch,
@@ -667,10 +747,14 @@ int kv_cache_compact(const bloom_config *cfg, bloom_kv_cache *kv, int32_t batch,
   for (int i = 0; i < n_keep; ++i)
     if (keep[i] < 0 || keep[i] >= batch || (i > 0 && keep[i] <= keep[i - 1])) return BLOOM_EINVAL;
   clear_stale_hip_error();
-  const hipError_t err = launch_kv_compact(kv->k, kv->v, cfg->n_layer, cfg->n_head_local,
-                                           kv->max_batch, kv->max_len, cfg->head_dim,
-                                           kv_bytes(cfg), kv->len, keep, n_keep,
-                                           (hipStream_t)stream);
+  hipError_t err = launch_kv_compact(kv->k, kv->v, cfg->n_layer, cfg->n_head_local,
+                                     kv->max_batch, kv->max_len, cfg->head_dim, kv_bytes(cfg),
+                                     kv->len, keep, n_keep, (hipStream_t)stream);
+  // an int8 cache's slot scales move with their rows (one float32 per slot)
+  if (err == hipSuccess && kv_q8(cfg))
+    err = launch_kv_compact(kv->k_scale, kv->v_scale, cfg->n_layer, cfg->n_head_local,
+                            kv->max_batch, kv->max_len, 1, 4, kv->len, keep, n_keep,
+                            (hipStream_t)stream);
   return err == hipSuccess ? BLOOM_OK : hip_fail(err);
 }
 
@@ -699,7 +783,7 @@ int bloom_lm_logits(const bloom_config *cfg, const bloom_weights *w, int32_t bat
     e.ld = cfg->vocab;
     // the greedy LM head's plan (never split) and operand form, so the logits are the
     // ones it ranks
-    const LinearPlan p = plan_linear(wdt_lm, rows, cfg->vocab, h, true, act_fmt(cfg));
+    const LinearPlan p = plan_linear(wdt_lm, rows, cfg->vocab, h, true, lm_act_fmt(cfg));
     const float *hr = d_hidden + (size_t)r0 * h;
     const void *X = hr;
     if (plan_x_fmt(p) != AF_F32) {
@@ -712,6 +796,74 @@ int bloom_lm_logits(const bloom_config *cfg, const bloom_weights *w, int32_t bat
     if (err != hipSuccess) return hip_fail(err);
   }
   return BLOOM_OK;
+}
+
+// Workspace of a standalone linear: the activations in the form the plan reads, then
+// the split-K partials.
+struct LinearWs {
+  LinearPlan plan;
+  int fmt;
+  size_t x_bytes, total;
+};
+
+LinearWs plan_linear_ws(const bloom_config *c, int M, int N, int K) {
+  LinearWs w{};
+  w.plan = plan_linear(wtype(c), M, N, K, false, act_fmt(c));
+  w.fmt = plan_x_fmt(w.plan);
+  w.x_bytes = w.fmt == AF_F32 ? 0 : align256(act_region(c, M, K));
+  w.total = w.x_bytes + align256(linear_partial_bytes(w.plan));
+  return w;
+}
+
+int check_linear(const bloom_config *cfg, int32_t M, int32_t N, int32_t K) {
+  int s = check_config(cfg);
+  if (s != BLOOM_OK) return s;
+  if (M < 0 || N < 1 || K < 1) return BLOOM_EINVAL;
+  if (cfg->weight_dtype != BLOOM_F32 && K % 64) return BLOOM_EINVAL;
+  if (cfg->act_dtype == BLOOM_INT8_ROWSCALE && K > 1 << 24) return BLOOM_EINVAL;
+  return BLOOM_OK;
+}
+
+int bloom_linear_workspace_bytes(const bloom_config *cfg, int32_t M, int32_t N, int32_t K,
+                                 size_t *bytes) {
+  int s = check_linear(cfg, M, N, K);
+  if (s != BLOOM_OK) return s;
+  if (!bytes) return BLOOM_EINVAL;
+  *bytes = M == 0 ? 0 : plan_linear_ws(cfg, M, N, K).total;
+  return BLOOM_OK;
+}
+
+int bloom_linear(const bloom_config *cfg, int32_t M, int32_t N, int32_t K, const float *d_x,
+                 const void *d_w, const void *d_s, const void *d_b, float *d_y, void *d_ws,
+                 size_t ws_bytes, void *stream) {
+  int s = check_linear(cfg, M, N, K);
+  if (s != BLOOM_OK) return s;
+  if (M == 0) return BLOOM_OK;
+  if (!d_x || !d_w || !d_y) return BLOOM_EINVAL;
+  if ((d_s != nullptr) != (cfg->weight_dtype == BLOOM_INT8_ROWSCALE)) return BLOOM_EINVAL;
+  const LinearWs lw = plan_linear_ws(cfg, M, N, K);
+  if (lw.total > 0 && (!d_ws || ws_bytes < lw.total)) return BLOOM_EWORKSPACE;
+  clear_stale_hip_error();
+  hipStream_t st = (hipStream_t)stream;
+  // the activations stored as the forward pass stores them for a linear of this plan
+  const void *X = d_x;
+  char *xs = (char *)d_ws;
+  hipError_t err = hipSuccess;
+  if (lw.fmt == AF_I8 || lw.fmt == AF_Q8F32)
+    err = launch_quant_rows(d_x, M, K, xs, lw.fmt, st);
+  else if (lw.fmt != AF_F32)
+    err = launch_f32_to_act(d_x, xs, lw.fmt, (size_t)M * K, st);
+  if (err != hipSuccess) return hip_fail(err);
+  if (lw.fmt != AF_F32) X = xs;
+  EpiParams e{};
+  e.mode = EPI_STORE;
+  e.out = d_y;
+  e.ld = N;
+  e.bias = d_b;
+  e.scale = (const uint16_t *)d_s;
+  e.xscale = lw.fmt == AF_I8 ? (const float *)(xs + (size_t)M * K) : nullptr;
+  err = launch_linear(wtype(cfg), lw.plan, X, d_w, (float *)((char *)d_ws + lw.x_bytes), e, st);
+  return err == hipSuccess ? BLOOM_OK : hip_fail(err);
 }
 
 int bloom_init_weights(const bloom_config *cfg, const bloom_weights *w, uint64_t seed,

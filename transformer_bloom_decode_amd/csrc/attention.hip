@@ -17,6 +17,9 @@
 //   3. o = (sum_j p_j v_j) / sum_j p_j, per lane group over its keys, then summed over
 //      the groups in LDS in a fixed order.
 // A query with no visible key (a left-pad position of the prompt) gets o = 0.
+// An int8 cache holds codes and one float32 scale per (row, head, slot) for keys and for
+// values: the key's scale multiplies its dot product, the value's scale its probability
+// weight in P.V (the same products as with the dequantised vectors, rounded once more).
 // ("Hugging Face BLOOM Inference Optimization", Custom CUDA Kernels and Hardware
 // Acceleration, for the fused mask + float32 softmax; "DeepSpeed Inference ...",
 // Section III.D, attention fused as one kernel.)
@@ -56,6 +59,13 @@ template <> struct KVRaw<f16_t> {
     return (t & 1) ? f16hi(a[t >> 1]) : f16lo(a[t >> 1]);
   }
 };
+template <> struct KVRaw<int8_t> {
+  uint2 a;   // 8 int8 codes; the key's scale is applied to its dot product / probability
+  __device__ __forceinline__ void load(const int8_t *p) { a = *(const uint2 *)p; }
+  __device__ __forceinline__ float get(int t) const {
+    return (float)(int8_t)((t < 4 ? a.x : a.y) >> (8 * (t & 3)));
+  }
+};
 template <> struct KVRaw<float> {
   float4 a, b;
   __device__ __forceinline__ void load(const float *p) {
@@ -76,6 +86,8 @@ template <typename TA>
 __global__ __launch_bounds__(256) void k_attention(const float *__restrict__ q,
                                                    const TA *__restrict__ kc,
                                                    const TA *__restrict__ vc,
+                                                   const float *__restrict__ ksc,
+                                                   const float *__restrict__ vsc,
                                                    const int *__restrict__ valid_len,
                                                    void *__restrict__ o, int o_fmt,
                                                    size_t o_plane, int H, int d, int max_len,
@@ -83,6 +95,7 @@ __global__ __launch_bounds__(256) void k_attention(const float *__restrict__ q,
                                                    int pos_base, const int *__restrict__ pos_dev,
                                                    int prompt_len) {
   constexpr int KB = KeysPerBatch<TA>::value;
+  constexpr bool kQ = sizeof(TA) == 1;   // int8 cache with per-slot scales
   __shared__ float pv[256 * 8];     // [G][d] per-group P.V partials
   __shared__ float red[4];
   const int m = blockIdx.x, h = blockIdx.y;
@@ -101,6 +114,7 @@ __global__ __launch_bounds__(256) void k_attention(const float *__restrict__ q,
   const size_t head_base = ((size_t)b * H + h) * (size_t)max_len * d;
   const TA *kb = kc + head_base;
   const TA *vb = vc + head_base;
+  const size_t scale_base = ((size_t)b * H + h) * (size_t)max_len;
   const float *qr = q + ((size_t)m * H + h) * d;
 
   // lane group g (L = d/8 lanes) handles slots j = g (mod G); lane `sub` owns dims
@@ -123,12 +137,17 @@ __global__ __launch_bounds__(256) void k_attention(const float *__restrict__ q,
   for (int t = 0; t < 8; ++t) acc[t] = 0.f;
   for (int j0 = 0; j0 < S; j0 += G * KB) {
     KVRaw<TA> kr[KB], vr[KB];
+    float ks[KB], vs[KB];
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
       const int jj = j0 + u * G + g;
       if (jj < S) {
         kr[u].load(kb + (size_t)jj * d + 8 * sub);
         vr[u].load(vb + (size_t)jj * d + 8 * sub);
+        if constexpr (kQ) {
+          ks[u] = ksc[scale_base + jj];
+          vs[u] = vsc[scale_base + jj];
+        }
       }
     }
     // scores s_j = q.k_j + slope * (j - qpos), summed across the group's L lanes;
@@ -144,6 +163,7 @@ __global__ __launch_bounds__(256) void k_attention(const float *__restrict__ q,
         for (int t = 0; t < 8; ++t) dot = fmaf(qv[t], kr[u].get(t), dot);
       }
       for (int off = L >> 1; off > 0; off >>= 1) dot += __shfl_xor(dot, off, 64);
+      if constexpr (kQ) dot = jj < S ? dot * ks[u] : 0.f;
       sc[u] = (jj < S && jj >= first) ? dot + slope * (float)(jj - qpos) : -INFINITY;
       bmax = fmaxf(bmax, sc[u]);
     }
@@ -159,8 +179,10 @@ __global__ __launch_bounds__(256) void k_attention(const float *__restrict__ q,
       if (jj < S && jj >= first) {
         const float p = __expf(sc[u] - mnew);
         if (sub == 0) lsum += p;                  // each key counted once per group
+        float pw = p;
+        if constexpr (kQ) pw = p * vs[u];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) acc[t] = fmaf(p, vr[u].get(t), acc[t]);
+        for (int t = 0; t < 8; ++t) acc[t] = fmaf(pw, vr[u].get(t), acc[t]);
       }
     }
     mrun = mnew;
@@ -193,11 +215,14 @@ constexpr int kPromptTileBytes = 16384;   // LDS per K (and per V) tile
 template <typename TA>
 __global__ __launch_bounds__(256) void k_attention_prompt(
     const float *__restrict__ q, const TA *__restrict__ kc, const TA *__restrict__ vc,
+    const float *__restrict__ ksc, const float *__restrict__ vsc,
     const int *__restrict__ valid_len, void *__restrict__ o, int o_fmt, size_t o_plane, int H,
     int d, int max_len, int n_total, int head_off, int rows_per_seq, int pos_base,
     int prompt_len, int nchunk) {
+  constexpr bool kQ = sizeof(TA) == 1;   // int8 cache with per-slot scales
   __shared__ __attribute__((aligned(16))) unsigned char ks_raw[kPromptTileBytes];
   __shared__ __attribute__((aligned(16))) unsigned char vs_raw[kPromptTileBytes];
+  __shared__ float ks_tile[kQ ? 64 : 1], vs_tile[kQ ? 64 : 1];   // the tile's slot scales
   const TA *ks = (const TA *)ks_raw;
   const TA *vs = (const TA *)vs_raw;
   const int tid = threadIdx.x;
@@ -215,6 +240,7 @@ __global__ __launch_bounds__(256) void k_attention_prompt(
   const size_t head_base = ((size_t)b * H + h) * (size_t)max_len * d;
   const TA *kb = kc + head_base;
   const TA *vb = vc + head_base;
+  const size_t scale_base = ((size_t)b * H + h) * (size_t)max_len;
   const size_t m = (size_t)b * rows_per_seq + (active ? r : 0);
   float qv[8];
   const float *qr = q + (m * H + h) * d + 8 * sub;
@@ -235,6 +261,12 @@ __global__ __launch_bounds__(256) void k_attention_prompt(
       ((u32x4 *)ks_raw)[i] = *(const u32x4 *)(kb + (size_t)j0 * d + (size_t)i * piece_elems);
       ((u32x4 *)vs_raw)[i] = *(const u32x4 *)(vb + (size_t)j0 * d + (size_t)i * piece_elems);
     }
+    if constexpr (kQ) {
+      if (tid < cnt) {
+        ks_tile[tid] = ksc[scale_base + j0 + tid];
+        vs_tile[tid] = vsc[scale_base + j0 + tid];
+      }
+    }
     __syncthreads();
     // every group runs every key of the tile (the shuffles stay convergent); keys
     // above the group's own position are masked
@@ -251,6 +283,7 @@ __global__ __launch_bounds__(256) void k_attention_prompt(
           for (int t = 0; t < 8; ++t) dot = fmaf(qv[t], to_f<TA>(kp[t]), dot);
         }
         for (int off = L >> 1; off > 0; off >>= 1) dot += __shfl_xor(dot, off, 64);
+        if constexpr (kQ) dot = jj < cnt ? dot * ks_tile[jj] : 0.f;
         const int j = j0 + jj;
         sc[u] = (jj < cnt && j <= qpos) ? dot + slope * (float)(j - qpos) : -INFINITY;
         cmax = fmaxf(cmax, sc[u]);
@@ -267,8 +300,10 @@ __global__ __launch_bounds__(256) void k_attention_prompt(
         const float p = __expf(sc[u] - mnew);
         lsum += p;
         const TA *vp = vs + (u0 + u) * d + 8 * sub;
+        float pw = p;
+        if constexpr (kQ) pw = p * vs_tile[u0 + u];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) acc[t] = fmaf(p, to_f<TA>(vp[t]), acc[t]);
+        for (int t = 0; t < 8; ++t) acc[t] = fmaf(pw, to_f<TA>(vp[t]), acc[t]);
       }
       mrun = mnew;
     }
@@ -283,25 +318,28 @@ __global__ __launch_bounds__(256) void k_attention_prompt(
 }
 
 template <typename TA>
-static void launch_attention_t(const float *q, const void *kc, const void *vc,
-                               const int *valid_len, void *o, int o_fmt, size_t o_plane, int rows,
+static void launch_attention_t(const float *q, const void *kc, const void *vc, const float *ksc,
+                               const float *vsc, const int *valid_len, void *o, int o_fmt,
+                               size_t o_plane, int rows,
                                int H, int d, int max_len, int n_total, int head_off,
                                int rows_per_seq, int pos_base, const int *pos_dev,
                                int prompt_len, bool prompt_kernel, int nchunk, hipStream_t st) {
   if (prompt_kernel) {
     const dim3 grid((unsigned)(rows / rows_per_seq * nchunk), H), block(256);
     hipLaunchKernelGGL(k_attention_prompt<TA>, grid, block, 0, st, q, (const TA *)kc,
-                       (const TA *)vc, valid_len, o, o_fmt, o_plane, H, d, max_len, n_total,
+                       (const TA *)vc, ksc, vsc, valid_len, o, o_fmt, o_plane, H, d, max_len,
+                       n_total,
                        head_off, rows_per_seq, pos_base, prompt_len, nchunk);
   } else {
     const dim3 grid(rows, H), block(256);
     hipLaunchKernelGGL(k_attention<TA>, grid, block, 0, st, q, (const TA *)kc, (const TA *)vc,
-                       valid_len, o, o_fmt, o_plane, H, d, max_len, n_total, head_off,
+                       ksc, vsc, valid_len, o, o_fmt, o_plane, H, d, max_len, n_total, head_off,
                        rows_per_seq, pos_base, pos_dev, prompt_len);
   }
 }
 
 hipError_t launch_attention(int kv_fmt, const float *q, const void *kc, const void *vc,
+                            const float *ksc, const float *vsc,
                             const int *valid_len, void *o, int o_fmt, int rows, int H, int d,
                             int max_len, int n_total, int head_off, int rows_per_seq,
                             int pos_base, const int *pos_dev, int prompt_len, hipStream_t st) {
@@ -313,19 +351,20 @@ hipError_t launch_attention(int kv_fmt, const float *q, const void *kc, const vo
   const int QR = 256 / (d >> 3);
   const int nchunk = (rows_per_seq + QR - 1) / QR;
   const long prompt_blocks = (long)(rows / max(rows_per_seq, 1)) * nchunk * H;
-  const bool prompt_kernel = rows_per_seq > 1 && !pos_dev && prompt_blocks >= 256;
-  if (kv_fmt == AF_F32)
-    launch_attention_t<float>(q, kc, vc, valid_len, o, o_fmt, o_plane, rows, H, d, max_len,
-                              n_total, head_off, rows_per_seq, pos_base, pos_dev, prompt_len,
-                              prompt_kernel, nchunk, st);
-  else if (kv_fmt == AF_F16)
-    launch_attention_t<f16_t>(q, kc, vc, valid_len, o, o_fmt, o_plane, rows, H, d, max_len,
-                              n_total, head_off, rows_per_seq, pos_base, pos_dev, prompt_len,
-                              prompt_kernel, nchunk, st);
-  else
-    launch_attention_t<bf16_t>(q, kc, vc, valid_len, o, o_fmt, o_plane, rows, H, d, max_len,
-                               n_total, head_off, rows_per_seq, pos_base, pos_dev, prompt_len,
-                               prompt_kernel, nchunk, st);
+  // (its tiles are copied in 16-byte pieces: a key must be a whole number of them)
+  const int elem = kv_fmt == AF_F32 ? 4 : (kv_fmt == AF_I8 ? 1 : 2);
+  const bool prompt_kernel =
+      rows_per_seq > 1 && !pos_dev && prompt_blocks >= 256 && (d * elem) % 16 == 0;
+  if (kv_fmt == AF_I8 && (!ksc || !vsc)) return hipErrorInvalidValue;
+#define BL_ATTN(TA)                                                                        \
+  launch_attention_t<TA>(q, kc, vc, ksc, vsc, valid_len, o, o_fmt, o_plane, rows, H, d,     \
+                         max_len, n_total, head_off, rows_per_seq, pos_base, pos_dev,       \
+                         prompt_len, prompt_kernel, nchunk, st)
+  if (kv_fmt == AF_I8) BL_ATTN(int8_t);
+  else if (kv_fmt == AF_F32) BL_ATTN(float);
+  else if (kv_fmt == AF_F16) BL_ATTN(f16_t);
+  else BL_ATTN(bf16_t);
+#undef BL_ATTN
   return hipGetLastError();
 }
 
@@ -366,6 +405,52 @@ hipError_t launch_kv_append(bool f32, const void *k, const void *v, void *ck, vo
   return hipGetLastError();
 }
 
+// int8 KV cache: new keys and values (float32) -> codes in their slots plus one float32
+// scale per (row, head, slot) each for keys and values (row_quant over the head's d
+// values).  One wave per (row b, new token t, head h, key or value); token t of row b
+// goes to slot pos + t (pos = *pos_dev when set, else pos_base); slots at or past
+// max_len are not written.  The sources are read through strides, so that both the QKV
+// epilogue's staging buffer [rows][H][2][d] and kv_cache_append's [batch][H][n_new][d]
+// inputs serve.
+__global__ __launch_bounds__(256) void k_kv_quant(KvQuantArgs a) {
+  const long w = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (w >= (long)a.batch * a.n * a.H * 2) return;   // uniform per wave
+  const int kind = (int)(w & 1);
+  long r = w >> 1;
+  const int h = (int)(r % a.H);
+  r /= a.H;
+  const int t = (int)(r % a.n), b = (int)(r / a.n);
+  const float *src = (kind ? a.v : a.k) + b * a.sb + t * a.st + h * a.sh;
+  float v[4];
+  float am = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = lane + 64 * i;
+    v[i] = c < a.d ? src[c] : 0.f;
+    am = fmaxf(am, fabsf(v[i]));
+  }
+  const RowQuant rq = row_quant(wave_max(am));
+  const int pos = (a.pos_dev ? *a.pos_dev : a.pos_base) + t;
+  if (pos >= a.max_len) return;
+  const size_t slot = ((size_t)b * a.H + h) * a.max_len + pos;
+  int8_t *dst = (kind ? a.vc : a.kc) + slot * a.d;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = lane + 64 * i;
+    if (c < a.d) dst[c] = (int8_t)quant_code(v[i], rq.inv);
+  }
+  if (lane == 0) (kind ? a.vs : a.ks)[slot] = rq.scale;
+}
+
+hipError_t launch_kv_quant(const KvQuantArgs &a, hipStream_t st) {
+  const long waves = (long)a.batch * a.n * a.H * 2;
+  if (waves == 0) return hipSuccess;
+  if (a.d > 256 || a.d <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_kv_quant, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 // In-place compaction of the KV cache ("Hugging Face BLOOM Inference Optimization",
 // Webserver Architecture and Request Handling: finished requests are extracted from
 // the running batch): destination row j0 + i takes source row rows[i] (rows strictly
@@ -385,6 +470,7 @@ __global__ __launch_bounds__(256) void k_kv_compact(unsigned char *__restrict__ 
                                                     KvRows rows, int n, int j0) {
   const size_t base = blockIdx.x * layer_stride + blockIdx.y * head_stride;
   const size_t pieces = row_bytes / 16;
+  const size_t tail = (row_bytes - 16 * pieces) / 4;   // trailing dwords
   for (int i = 0; i < n; ++i) {
     const int src = rows.src[i], dst = j0 + i;
     if (src == dst) continue;
@@ -394,6 +480,13 @@ __global__ __launch_bounds__(256) void k_kv_compact(unsigned char *__restrict__ 
       const u32x4 b = *(const u32x4 *)(vc + so + 16 * p);
       *(u32x4 *)(kc + dof + 16 * p) = a;
       *(u32x4 *)(vc + dof + 16 * p) = b;
+    }
+    if (threadIdx.x < tail) {
+      const size_t o = 16 * pieces + 4 * threadIdx.x;
+      const uint32_t a = *(const uint32_t *)(kc + so + o);
+      const uint32_t b = *(const uint32_t *)(vc + so + o);
+      *(uint32_t *)(kc + dof + o) = a;
+      *(uint32_t *)(vc + dof + o) = b;
     }
   }
 }

@@ -13,6 +13,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
 
 typedef uint16_t bf16_t;  // bf16 bit pattern
 typedef _Float16 f16_t;   // IEEE binary16 (activations and KV cache in the fp16 mode)
@@ -49,6 +51,7 @@ template <typename T> __device__ __forceinline__ float to_f(T v);
 template <> __device__ __forceinline__ float to_f<float>(float v) { return v; }
 template <> __device__ __forceinline__ float to_f<bf16_t>(bf16_t v) { return bf2f(v); }
 template <> __device__ __forceinline__ float to_f<f16_t>(f16_t v) { return (float)v; }
+template <> __device__ __forceinline__ float to_f<int8_t>(int8_t v) { return (float)v; }
 
 template <typename T> __device__ __forceinline__ T from_f(float v);
 template <> __device__ __forceinline__ float from_f<float>(float v) { return v; }
@@ -160,7 +163,52 @@ __device__ __forceinline__ float4 ln_apply(float4 x, float mean, float rstd, con
 // pair of bf16 planes hi = bf16(v), lo = bf16(v - hi) (read by the MFMA GEMM as two bf16
 // operands; hi + lo carries v to within 2^-17 of its value).  The lo plane starts
 // `plane` elements after the hi plane.
-enum ActFmt : int { AF_BF16 = 0, AF_F32 = 1, AF_BF16X2 = 2, AF_F16 = 3 };
+// The int8 activations of the W8A8 mode are quantised per row (row_quant): AF_I8 holds
+// the int8 codes [rows][n] followed, `plane` bytes after the first code, by one float32
+// scale per row (read by the int8 MFMA GEMM); AF_Q8F32 holds the values those codes
+// stand for, code * scale, as float32 (read by the vector-ALU GEMV).  Only kernels that
+// own whole rows write them (the LayerNorms, k_quant_rows).
+enum ActFmt : int { AF_BF16 = 0, AF_F32 = 1, AF_BF16X2 = 2, AF_F16 = 3, AF_I8 = 4, AF_Q8F32 = 5 };
+
+__device__ __forceinline__ bool act_is_q8(int fmt) { return fmt == AF_I8 || fmt == AF_Q8F32; }
+
+// Symmetric int8 quantisation of a slice whose largest magnitude is amax: scale =
+// amax / 127, and the code of v is the nearest integer (ties to even) to v * (127 /
+// amax), clamped to [-127, 127]; a slice of zeros has scale 0 and codes 0.  Both
+// divisions are IEEE float32 divisions and the product is one float32 multiply (DeepSpeed's
+// INT8 inference, "DeepSpeed Inference ...", Section VII.B, is named without its scheme;
+// this is the plain symmetric per-slice form).
+struct RowQuant {
+  float inv, scale;
+};
+__device__ __forceinline__ RowQuant row_quant(float amax) {
+  RowQuant q;
+  q.inv = amax > 0.f ? 127.0f / amax : 0.f;
+  q.scale = amax / 127.0f;
+  return q;
+}
+__device__ __forceinline__ int quant_code(float v, float inv) {
+  return (int)fminf(fmaxf(rintf(v * inv), -127.f), 127.f);
+}
+__device__ __forceinline__ float fabs4max(float4 v) {
+  return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+}
+// elements i .. i+3 of a row quantised with q, in format fmt (AF_I8 or AF_Q8F32)
+__device__ __forceinline__ void q8_store4(void *p, int fmt, size_t i, float4 v, RowQuant q) {
+  const int a = quant_code(v.x, q.inv), b = quant_code(v.y, q.inv);
+  const int c = quant_code(v.z, q.inv), d = quant_code(v.w, q.inv);
+  if (fmt == AF_I8)
+    *(uint32_t *)((int8_t *)p + i) =
+        (uint32_t)(a & 255) | ((uint32_t)(b & 255) << 8) | ((uint32_t)(c & 255) << 16) |
+        ((uint32_t)(d & 255) << 24);
+  else
+    *(float4 *)((float *)p + i) =
+        make_float4((float)a * q.scale, (float)b * q.scale, (float)c * q.scale, (float)d * q.scale);
+}
+// scale of row `row` of an AF_I8 buffer whose codes take `plane` bytes
+__device__ __forceinline__ float *q8_scale_ptr(void *p, size_t plane) {
+  return (float *)((char *)p + plane);
+}
 
 __device__ __forceinline__ void act_store(void *p, int fmt, size_t i, size_t plane, float v) {
   if (fmt == AF_F32) {
@@ -215,6 +263,7 @@ struct EpiParams {
   int mode;
   const void *bias;        // [N] parameter type, nullable
   const uint16_t *scale;   // [N] fp16 per-row scales (int8 weights), nullable
+  const float *xscale;     // [M] float32 per-row scales of int8 activations, nullable
   // EPI_QKV
   float *q;                // [M][H][d]
   void *kc, *vc;           // cache of this layer: [max_batch][H][max_len][d]
@@ -225,6 +274,8 @@ struct EpiParams {
                            // a slot at or past max_len is then not written
   int rows_per_seq;        // 1 (decode) or the prompt length (prefill)
   float q_scale;           // 1/sqrt(d)
+  float *kv_stage;         // if set, k and v go to kv_stage[m][H][2][d] (float32) instead
+                           // of the cache, for the int8 cache's quantisation kernel
   // EPI_RESID / EPI_GELU / EPI_STORE
   void *out;               // [M][ld]
   int ld;
@@ -240,6 +291,7 @@ struct EpiParams {
 template <typename TP>
 __device__ __forceinline__ void epilogue(const EpiParams &e, int m, int n, float acc) {
   float y = acc;
+  if (e.xscale) y *= e.xscale[m];
   if (e.scale) y *= h2f(e.scale[n]);
   if (e.bias) y += to_f<TP>(((const TP *)e.bias)[n]);
   switch (e.mode) {
@@ -251,6 +303,8 @@ __device__ __forceinline__ void epilogue(const EpiParams &e, int m, int n, float
       const int c = r - t * d;
       if (t == 0) {
         e.q[((size_t)m * H + hd) * d + c] = y * e.q_scale;
+      } else if (e.kv_stage) {
+        e.kv_stage[(((size_t)m * H + hd) * 2 + (t - 1)) * d + c] = y;
       } else {
         const int b = m / e.rows_per_seq;
         const int pos = (e.pos_dev ? *e.pos_dev : e.pos_base) + (m - b * e.rows_per_seq);

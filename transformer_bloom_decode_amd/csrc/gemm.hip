@@ -11,7 +11,8 @@
 //  * k_gemv_valu (up to 4 activation rows, the batch-1..4 decode step), in gemv.hip.
 //  * k_gemm_lg (5+ rows: decode batches, LM heads, prompt passes): MFMA 32x32x16 with
 //    both operands copied straight from global memory into LDS (global_load_lds), tile
-//    sizes and K splits chosen per shape (plan_linear); int8 weights widened from LDS.
+//    sizes and K splits chosen per shape (plan_linear); int8 weights widened from LDS,
+//    or, with int8 activations (W8A8), both operands int8 on the 32x32x32 int8 MFMA.
 //  * k_gemm_f32: a plain float32 path for the fp32 model.
 //
 #include <atomic>
@@ -79,16 +80,27 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// 32x32 block, k = 32, int8 x int8 -> int32 (exact): lane l holds A row l % 32 and B
+// row l % 32, k 16 (l / 32) .. +16, as 16 bytes; D as in the bf16 form (checked on
+// MI355X against a CPU product).
+__device__ __forceinline__ i32x16 mfma32_i8(u32x4 a, u32x4 b, i32x16 c) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a),
+                                               __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
+}
+
 // XS = 1: bf16 activations; XS = 2: activations held as two bf16 planes (hi, lo) whose
 // sum carries a float32 value to 2^-17: both planes are staged and each is multiplied
 // with the same weights (two MFMAs per block), so the product keeps that precision.
-template <typename TW, int BM, int BN, int WGM, int WGN, int S, int BK, int XS>
+// TX = int8_t: int8 activation codes against int8 weights (W8A8), int32 accumulators;
+// the epilogue applies the row's activation scale and the weight row's scale.
+template <typename TW, int BM, int BN, int WGM, int WGN, int S, int BK, int XS,
+          typename TX = bf16_t>
 struct LgCfg {
   static constexpr int kWaves = WGM * WGN;
   static constexpr int kThreads = kWaves * 64;
   static constexpr int WTM = BM / WGM, WTN = BN / WGN;
   static constexpr int TM = WTM / 32, TN = WTN / 32;
-  static constexpr int XRB = BK * 2;                        // X bytes per row per K tile
+  static constexpr int XRB = BK * (int)sizeof(TX);          // X bytes per row per K tile
   static constexpr int WRB = BK * (int)sizeof(TW);          // W bytes per row per K tile
   static constexpr int CXP = BM * XRB / 1024;               // 1 KB X pieces per plane
   static constexpr int CX = XS * CXP, CW = BN * WRB / 1024; // 1 KB pieces per K tile
@@ -100,6 +112,7 @@ struct LgCfg {
   static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
   static_assert(BK == 64 || (BK == 32 && sizeof(TW) == 2), "K tile");
   static_assert(XS == 1 || XS == 2, "activation planes");
+  static_assert(sizeof(TX) == 2 || (sizeof(TW) == 1 && XS == 1 && BK == 64), "W8A8 tiles");
   static_assert(kLds <= 160 * 1024, "LDS");
 };
 
@@ -131,16 +144,18 @@ __device__ __attribute__((noinline)) void lg_out16(const EpiParams &ep, float *p
     const float sc = ep.scale ? h2f(ep.scale[n]) : 1.f;
     const float bi = ep.bias ? to_f<TP>(((const TP *)ep.bias)[n]) : 0.f;
     float *x = (float *)ep.out + n;
-    float xv[16];
+    float xv[16], xs[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int m = min(m0 + 8 * (v >> 2) + (v & 3), M - 1);
       xv[v] = x[(size_t)m * ep.ld];
+      xs[v] = ep.xscale ? ep.xscale[m] : 1.f;
     }
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int m = m0 + 8 * (v >> 2) + (v & 3);
       float y = acc[v];
+      if (ep.xscale) y *= xs[v];
       if (ep.scale) y *= sc;
       if (ep.bias) y += bi;
       if (m < M) x[(size_t)m * ep.ld] = xv[v] + y;
@@ -182,12 +197,14 @@ __device__ __attribute__((noinline)) void lg_argmax16(const EpiParams &ep, int N
 }
 
 template <typename TW, typename TP, int BM, int BN, int WGM, int WGN, int S, int BK,
-          bool SCHED = false, int XS = 1>
+          bool SCHED = false, int XS = 1, typename TX = bf16_t>
 __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_lg(
-    const bf16_t *__restrict__ X, const TW *__restrict__ W, int M, int N, int K,
+    const TX *__restrict__ X, const TW *__restrict__ W, int M, int N, int K,
     int tiles_m, int tiles_n, int splits, float *__restrict__ partial, EpiParams ep) {
-  using C = LgCfg<TW, BM, BN, WGM, WGN, S, BK, XS>;
+  using C = LgCfg<TW, BM, BN, WGM, WGN, S, BK, XS, TX>;
   constexpr bool kI8 = sizeof(TW) == 1;
+  constexpr bool kX8 = sizeof(TX) == 1;   // W8A8: int8 x int8 on the int32 MFMA
+  using Acc = std::conditional_t<kX8, i32x16, f32x16>;
   extern __shared__ __attribute__((aligned(1024))) unsigned char lg_lds[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -233,11 +250,11 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_lg(
     }
   };
 
-  f32x16 acc[C::TM][C::TN];
+  Acc acc[C::TM][C::TN];
 #pragma unroll
   for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-    for (int j = 0; j < C::TN; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < C::TN; ++j) acc[i][j] = Acc{};
 
 #pragma unroll
   for (int p = 0; p < S - 1; ++p)
@@ -255,52 +272,78 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_lg(
     if (kt + S - 1 < kt1) issue(kt + S - 1);
     const unsigned char *xb = lg_lds + (kt % S) * C::kStage;
     const unsigned char *wb = xb + C::CX * 1024;
-    // operands of 16-wide substep s + 1 are read while the MFMAs of substep s run
-    u32x4 a[2][XS][C::TM], bv[2][C::TN];
-    auto rd = [&](int s, int q) {
-      const int piece = 2 * s + (lane >> 5);   // 8-element k-piece within the K tile
+    if constexpr (kX8) {
+      // two 32-wide substeps; both operands are 16-byte pieces of 64-byte rows, read for
+      // both substeps before the MFMAs
+      u32x4 a[2][C::TM], bv[2][C::TN];
 #pragma unroll
-      for (int pl = 0; pl < XS; ++pl)
+      for (int s = 0; s < 2; ++s) {
+        const int piece = 2 * s + (lane >> 5);
 #pragma unroll
         for (int i = 0; i < C::TM; ++i) {
           const int r = wm * C::WTM + 32 * i + (lane & 31);
-          a[q][pl][i] = *(const u32x4 *)(xb + pl * C::CXP * 1024 + r * C::XRB +
-                                         16 * lg_slot<C::XRB>(r, piece));
+          a[s][i] = *(const u32x4 *)(xb + r * 64 + 16 * lg_slot<64>(r, piece));
         }
 #pragma unroll
-      for (int j = 0; j < C::TN; ++j) {
-        const int r = wn * C::WTN + 32 * j + (lane & 31);
-        if constexpr (kI8) {
-          // 8 int8 of k-piece `piece` (half of a 16-byte slot), widened to bf16 (exact)
-          const uint2 t = *(const uint2 *)(wb + r * C::WRB +
-                                           16 * lg_slot<C::WRB>(r, piece >> 1) +
-                                           8 * (piece & 1));
-          bv[q][j] = i8x8_to_bf16x8(t.x, t.y);
-        } else {
-          bv[q][j] = *(const u32x4 *)(wb + r * C::WRB + 16 * lg_slot<C::WRB>(r, piece));
+        for (int j = 0; j < C::TN; ++j) {
+          const int r = wn * C::WTN + 32 * j + (lane & 31);
+          bv[s][j] = *(const u32x4 *)(wb + r * 64 + 16 * lg_slot<64>(r, piece));
         }
       }
-    };
-    rd(0, 0);
 #pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      if (s + 1 < BK / 16) rd(s + 1, (s + 1) & 1);
-#pragma unroll
-      for (int pl = 0; pl < XS; ++pl)
+      for (int s = 0; s < 2; ++s)
 #pragma unroll
         for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-          for (int j = 0; j < C::TN; ++j)
-            acc[i][j] = mfma32(a[s & 1][pl][i], bv[s & 1][j], acc[i][j]);
-      if constexpr (SCHED) {
-        // interleave: one MFMA, then one of the next substep's LDS reads, ...
-        if (s + 1 < BK / 16) {
+          for (int j = 0; j < C::TN; ++j) acc[i][j] = mfma32_i8(a[s][i], bv[s][j], acc[i][j]);
+    } else {
+      // operands of 16-wide substep s + 1 are read while the MFMAs of substep s run
+      u32x4 a[2][XS][C::TM], bv[2][C::TN];
+      auto rd = [&](int s, int q) {
+        const int piece = 2 * s + (lane >> 5);   // 8-element k-piece within the K tile
 #pragma unroll
-          for (int q = 0; q < C::TM + C::TN; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        for (int pl = 0; pl < XS; ++pl)
+#pragma unroll
+          for (int i = 0; i < C::TM; ++i) {
+            const int r = wm * C::WTM + 32 * i + (lane & 31);
+            a[q][pl][i] = *(const u32x4 *)(xb + pl * C::CXP * 1024 + r * C::XRB +
+                                           16 * lg_slot<C::XRB>(r, piece));
           }
-          __builtin_amdgcn_sched_group_barrier(0x008, C::TM * C::TN - (C::TM + C::TN), 0);
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) {
+          const int r = wn * C::WTN + 32 * j + (lane & 31);
+          if constexpr (kI8) {
+            // 8 int8 of k-piece `piece` (half of a 16-byte slot), widened to bf16 (exact)
+            const uint2 t = *(const uint2 *)(wb + r * C::WRB +
+                                             16 * lg_slot<C::WRB>(r, piece >> 1) +
+                                             8 * (piece & 1));
+            bv[q][j] = i8x8_to_bf16x8(t.x, t.y);
+          } else {
+            bv[q][j] = *(const u32x4 *)(wb + r * C::WRB + 16 * lg_slot<C::WRB>(r, piece));
+          }
+        }
+      };
+      rd(0, 0);
+#pragma unroll
+      for (int s = 0; s < BK / 16; ++s) {
+        if (s + 1 < BK / 16) rd(s + 1, (s + 1) & 1);
+#pragma unroll
+        for (int pl = 0; pl < XS; ++pl)
+#pragma unroll
+          for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::TN; ++j)
+              acc[i][j] = mfma32(a[s & 1][pl][i], bv[s & 1][j], acc[i][j]);
+        if constexpr (SCHED) {
+          // interleave: one MFMA, then one of the next substep's LDS reads, ...
+          if (s + 1 < BK / 16) {
+#pragma unroll
+            for (int q = 0; q < C::TM + C::TN; ++q) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, C::TM * C::TN - (C::TM + C::TN), 0);
+          }
         }
       }
     }
@@ -308,38 +351,51 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_lg(
 
   // D layout of a 32x32 block: lane holds column lane % 32, value v row
   // 8 (v / 4) + 4 (lane / 32) + v % 4
-  if (ep.mode == EPI_ARGMAX) {
-    // one (max, index) partial per row per N tile (the plan never splits K here)
-    constexpr int NS = WGN * C::TN;
-    float *red_v = (float *)lg_lds;
-    int *red_i = (int *)(lg_lds + BM * NS * sizeof(float));
-    __syncthreads();  // every wave is done reading the LDS stages
+  if constexpr (kX8) {
+    // int32 sums (exact) -> float32; the scales come in the epilogue
+    float *part = splits > 1 ? partial : nullptr;
 #pragma unroll
     for (int i = 0; i < C::TM; ++i)
 #pragma unroll
       for (int j = 0; j < C::TN; ++j)
-        lg_argmax16<TP>(ep, N, wm * C::WTM + 32 * i + 4 * (lane >> 5),
-                        n0 + wn * C::WTN + 32 * j + (lane & 31), wn * C::TN + j, NS, red_v,
-                        red_i, acc[i][j]);
-    __syncthreads();
-    for (int lr = tid; lr < BM; lr += C::kThreads) {
-      const int m = m0 + lr;
-      if (m >= M) continue;
-      float bv = red_v[lr * NS];
-      int bi = red_i[lr * NS];
-      for (int c = 1; c < NS; ++c) argmax_take(bv, bi, red_v[lr * NS + c], red_i[lr * NS + c]);
-      ep.am_val[(size_t)m * ep.am_stride + nt] = bv;
-      ep.am_idx[(size_t)m * ep.am_stride + nt] = bi;
-    }
+        lg_out16<TP>(ep, part, z, M, N, m0 + wm * C::WTM + 32 * i + 4 * (lane >> 5),
+                     n0 + wn * C::WTN + 32 * j + (lane & 31),
+                     __builtin_convertvector(acc[i][j], f32x16));
     return;
+  } else {
+    if (ep.mode == EPI_ARGMAX) {
+      // one (max, index) partial per row per N tile (the plan never splits K here)
+      constexpr int NS = WGN * C::TN;
+      float *red_v = (float *)lg_lds;
+      int *red_i = (int *)(lg_lds + BM * NS * sizeof(float));
+      __syncthreads();  // every wave is done reading the LDS stages
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+          lg_argmax16<TP>(ep, N, wm * C::WTM + 32 * i + 4 * (lane >> 5),
+                          n0 + wn * C::WTN + 32 * j + (lane & 31), wn * C::TN + j, NS, red_v,
+                          red_i, acc[i][j]);
+      __syncthreads();
+      for (int lr = tid; lr < BM; lr += C::kThreads) {
+        const int m = m0 + lr;
+        if (m >= M) continue;
+        float bv = red_v[lr * NS];
+        int bi = red_i[lr * NS];
+        for (int c = 1; c < NS; ++c) argmax_take(bv, bi, red_v[lr * NS + c], red_i[lr * NS + c]);
+        ep.am_val[(size_t)m * ep.am_stride + nt] = bv;
+        ep.am_idx[(size_t)m * ep.am_stride + nt] = bi;
+      }
+      return;
+    }
+    float *part = splits > 1 ? partial : nullptr;
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j)
+        lg_out16<TP>(ep, part, z, M, N, m0 + wm * C::WTM + 32 * i + 4 * (lane >> 5),
+                     n0 + wn * C::WTN + 32 * j + (lane & 31), acc[i][j]);
   }
-  float *part = splits > 1 ? partial : nullptr;
-#pragma unroll
-  for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-    for (int j = 0; j < C::TN; ++j)
-      lg_out16<TP>(ep, part, z, M, N, m0 + wm * C::WTM + 32 * i + 4 * (lane >> 5),
-                   n0 + wn * C::WTN + 32 * j + (lane & 31), acc[i][j]);
 }
 
 // ---------------------------------------------------------------------------
@@ -467,14 +523,19 @@ LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax, int act) {
     p.splits = 1;
     return p;
   }
+  const bool q8 = act == AF_I8;   // W8A8 (int8 weights only; the caller checks)
   if (M <= kValuMaxRows) {
+    // int8 activations: the GEMV reads the values of the int8 codes as float32
     p = plan_valu(wdtype, M, N, K);
-    p.x_fmt = act;
+    p.x_fmt = q8 ? AF_F32 : act;
+    p.q8 = q8;
     return p;
   }
   // Direct-to-LDS MFMA GEMM for everything else (hidden sizes are multiples of 64).
   p.kind = LIN_LG;
-  p.xs = act == AF_BF16 ? 1 : 2;
+  p.xs = act == AF_BF16 || q8 ? 1 : 2;
+  p.x8 = q8;
+  p.q8 = q8;
   const int KT = K / kLg;
   if (!argmax && M >= 256) {
     // Prompt passes: tiles of 256 x 256 (8 waves of 64 x 128, one block per CU: 128 KB
@@ -490,6 +551,7 @@ LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax, int act) {
     // 621.7 -> 471.6, down 618.4 -> 486.8; 2048 rows: down 4675 -> 3442 us.
     // Two activation planes double the X tile: 128 x 128 tiles (96 KB of LDS) are the
     // largest bf16 prompt tiles that still fit.
+    // W8A8: the same 128 x 256 tiles, int8 activation rows of 64 bytes per K tile.
     if (wdtype == WT_INT8) p.lg = LG_P8;
     else if (p.xs == 2) p.lg = LG_128;
     else p.lg = M >= 1024 ? LG_256 : (M >= 512 ? LG_256x128 : LG_128);
@@ -529,6 +591,11 @@ LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax, int act) {
     p.lg = M <= 32 ? LG_D32 : (M <= 64 ? LG_D64 : LG_D128);
     bm = M <= 32 ? 32 : (M <= 64 ? 64 : 128);
     bn = 128;
+  } else if (q8) {
+    // W8A8: the X tile is 64-byte rows too, so 32-row tiles would not split evenly into
+    // the four waves' 1 KB copies; up to 64 rows take 64 x 256 tiles
+    if (M <= 64) { p.lg = LG_D64W; bm = 64; bn = 256; }
+    else { p.lg = LG_D128N; bm = 128; bn = 128; }
   } else if (M <= 32) {
     p.lg = LG_D32W; bm = 32; bn = 256;
   } else if (M <= 64) {
@@ -557,7 +624,8 @@ LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax, int act) {
 
 int plan_x_fmt(const LinearPlan &p) {
   if (p.kind == LIN_F32) return AF_F32;
-  if (p.kind == LIN_VALU) return p.x_fmt;
+  if (p.kind == LIN_VALU) return p.q8 ? AF_Q8F32 : p.x_fmt;
+  if (p.x8) return AF_I8;
   return p.xs == 2 ? AF_BF16X2 : AF_BF16;
 }
 
@@ -574,10 +642,11 @@ size_t linear_partial_bytes(const LinearPlan &p) {
 // safe.
 static std::mutex g_lds_attr_mu;
 
-template <typename TW, int BM, int BN, int WGM, int WGN, int S, int BK = kLg, int XS = 1>
+template <typename TW, int BM, int BN, int WGM, int WGN, int S, int BK = kLg, int XS = 1,
+          typename TX = bf16_t>
 static hipError_t launch_lg_t(const LinearPlan &p, const void *X, const void *W, float *partial,
                               const EpiParams &ep, hipStream_t st) {
-  using C = LgCfg<TW, BM, BN, WGM, WGN, S, BK, XS>;
+  using C = LgCfg<TW, BM, BN, WGM, WGN, S, BK, XS, TX>;
   static std::atomic<uint64_t> attr_set{0};   // bit per device
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -587,15 +656,15 @@ static hipError_t launch_lg_t(const LinearPlan &p, const void *X, const void *W,
     std::lock_guard<std::mutex> lock(g_lds_attr_mu);
     if (!(attr_set.load(std::memory_order_relaxed) & bit)) {
       e = hipFuncSetAttribute(
-          (const void *)k_gemm_lg<TW, bf16_t, BM, BN, WGM, WGN, S, BK, false, XS>,
+          (const void *)k_gemm_lg<TW, bf16_t, BM, BN, WGM, WGN, S, BK, false, XS, TX>,
           hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
       if (e != hipSuccess) return e;
       attr_set.fetch_or(bit, std::memory_order_release);
     }
   }
-  BL_LAUNCH((k_gemm_lg<TW, bf16_t, BM, BN, WGM, WGN, S, BK, false, XS>),
+  BL_LAUNCH((k_gemm_lg<TW, bf16_t, BM, BN, WGM, WGN, S, BK, false, XS, TX>),
             dim3((unsigned)(p.grid_x * p.grid_y * p.splits)), dim3(C::kThreads), C::kLds, st,
-            (const bf16_t *)X, (const TW *)W, p.M, p.N, p.K, p.grid_x, p.grid_y, p.splits,
+            (const TX *)X, (const TW *)W, p.M, p.N, p.K, p.grid_x, p.grid_y, p.splits,
             partial, ep);
   return hipGetLastError();
 }
@@ -633,6 +702,17 @@ static hipError_t launch_lg(const LinearPlan &p, const void *X, const void *W, f
   }
 }
 
+// W8A8 tiles (int8 activation codes against int8 weights)
+static hipError_t launch_lg_x8(const LinearPlan &p, const void *X, const void *W, float *partial,
+                               const EpiParams &ep, hipStream_t st) {
+  switch (p.lg) {
+    case LG_D64W: return launch_lg_t<int8_t, 64, 256, 1, 4, 3, kLg, 1, int8_t>(p, X, W, partial, ep, st);
+    case LG_D128N: return launch_lg_t<int8_t, 128, 128, 1, 4, 3, kLg, 1, int8_t>(p, X, W, partial, ep, st);
+    case LG_P8: return launch_lg_t<int8_t, 128, 256, 1, 4, 2, kLg, 1, int8_t>(p, X, W, partial, ep, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_linear(int wdtype, const LinearPlan &p, const void *X, const void *W,
                          float *partial, const EpiParams &ep, hipStream_t st,
                          bool splitk_epilogue) {
@@ -645,8 +725,12 @@ hipError_t launch_linear(int wdtype, const LinearPlan &p, const void *X, const v
   if (p.kind == LIN_VALU) return launch_valu(wdtype, p, X, W, ep, st);
   if (p.kind != LIN_LG || p.splits > kMaxSplits || (p.xs != 1 && p.xs != 2))
     return hipErrorInvalidValue;
+  if (p.x8 && (wdtype != WT_INT8 || !ep.xscale || ep.mode == EPI_ARGMAX))
+    return hipErrorInvalidValue;
   hipError_t e;
-  if (wdtype == WT_BF16)
+  if (p.x8)
+    e = launch_lg_x8(p, X, W, partial, ep, st);
+  else if (wdtype == WT_BF16)
     e = p.xs == 2 ? launch_lg<bf16_t, 2>(p, X, W, partial, ep, st)
                   : launch_lg<bf16_t, 1>(p, X, W, partial, ep, st);
   else

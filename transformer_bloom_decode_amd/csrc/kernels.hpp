@@ -60,6 +60,8 @@ struct LinearPlan {
   int splits;    // K splits (> 1: partial sums + reduction kernel)
   int x_fmt;     // VALU: activation storage (ActFmt: AF_BF16, AF_F32 or AF_F16)
   int xs;        // LG: activation planes (1: bf16; 2: bf16 hi + lo planes of float32 values)
+  bool x8;       // LG: int8 activation codes against int8 weights (W8A8)
+  bool q8;       // the activations are int8-quantised rows (AF_I8 or, for VALU, AF_Q8F32)
 };
 
 // Vector-ALU GEMV (gemv.hip): plan for M <= kValuMaxRows rows, and its launch.
@@ -73,9 +75,11 @@ bool gemv_ln_supported(int wdtype, int M, int K);
 hipError_t launch_gemv_ln(int wdtype, int x_fmt, int N, int K, const float *x, const void *g,
                           const void *b, float eps, const void *W, const EpiParams &ep,
                           hipStream_t st);
-// act: the model's activation type (ActFmt AF_BF16, AF_F32 or AF_F16).  The vector-ALU
-// GEMV reads activations in that type; the MFMA GEMM reads bf16, or for float32 / fp16
-// activations the two bf16 planes hi + lo.
+// act: the model's activation type (ActFmt AF_BF16, AF_F32, AF_F16 or, int8 weights
+// only, AF_I8).  The vector-ALU GEMV reads activations in that type (int8 ones as the
+// float32 values of their codes); the MFMA GEMM reads bf16, for float32 / fp16
+// activations the two bf16 planes hi + lo, for int8 ones the codes (the epilogue
+// multiplies by EpiParams::xscale).
 LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax, int act);
 // Storage format (ActFmt) of the activations a linear of this plan reads.
 int plan_x_fmt(const LinearPlan &p);
@@ -102,9 +106,15 @@ hipError_t launch_embed(bool f32, const int *tokens, const void *embed, const vo
 bool splitk_resid_ln_supported(int h, int splits);
 // out is written in format fmt (ActFmt; for AF_BF16X2 the lo plane follows rows * h
 // elements after the hi plane).
-hipError_t launch_splitk_resid_ln(const float *partial, int splits, int rows, const void *scale,
-                                  const void *bias, float *x, const void *g, const void *b,
-                                  void *out, int fmt, int h, float eps, hipStream_t stream);
+// xscale (nullable): per-row scales of int8 activations, applied to the partials' sum.
+hipError_t launch_splitk_resid_ln(const float *partial, int splits, int rows, const float *xscale,
+                                  const void *scale, const void *bias, float *x, const void *g,
+                                  const void *b, void *out, int fmt, int h, float eps,
+                                  hipStream_t stream);
+// float32 rows [rows][K] -> per-row int8 (fmt AF_I8, scales rows * K bytes after the
+// codes, or AF_Q8F32).
+hipError_t launch_quant_rows(const float *in, int rows, int K, void *out, int fmt,
+                             hipStream_t stream);
 hipError_t launch_layernorm(bool f32, const float *x, int in_step, int in_off, const void *g,
                             const void *b, void *out, int fmt, float *out_f32, int rows, int h,
                             float eps, hipStream_t stream);
@@ -113,8 +123,10 @@ hipError_t launch_layernorm(bool f32, const float *x, int in_step, int in_off, c
 // lo plane rows * H * d elements after the hi plane).  With pos_dev set, the query
 // position is read from device memory and clamped so that no slot at or past max_len is
 // read.
+// kv_fmt AF_I8: int8 codes with float32 scales ksc / vsc [max_batch][H][max_len] of this
+// layer (else the scale pointers are unused).
 hipError_t launch_attention(int kv_fmt, const float *q, const void *kc, const void *vc,
-                            const int *valid_len, void *o, int o_fmt, int rows, int H, int d,
+                            const float *ksc, const float *vsc, const int *valid_len, void *o, int o_fmt, int rows, int H, int d,
                             int max_len, int n_total, int head_off, int rows_per_seq,
                             int pos_base, const int *pos_dev, int prompt_len, hipStream_t st);
 
@@ -136,8 +148,23 @@ hipError_t launch_gen_init(int *state, int pos, int step, int *done, int batch, 
 hipError_t launch_gen_record(const int *next, int *cur, int *ids, const float *hfix, float *hout,
                              int *state, int batch, int hidden, const GenControl &gc,
                              hipStream_t st);
+// int8 KV cache writes (k_kv_quant): source element c of (row b, new token t, head h) is
+// k[b * sb + t * st + h * sh + c] (v likewise); it goes to slot pos + t of the layer's
+// int8 cache kc / vc [max_batch][H][max_len][d] and the slot's scale to ks / vs
+// [max_batch][H][max_len]; pos = *pos_dev if set, else pos_base.
+struct KvQuantArgs {
+  const float *k, *v;
+  long sb, st, sh;
+  int batch, n, H, d;
+  int8_t *kc, *vc;
+  float *ks, *vs;
+  int max_len, pos_base;
+  const int *pos_dev;
+};
+hipError_t launch_kv_quant(const KvQuantArgs &a, hipStream_t st);
 // KV-cache compaction: rows[i] -> row i (strictly increasing sources), slots [0, len),
-// all layers and heads, in place.  Sources are passed by value in chunks.
+// all layers and heads, in place (len * d * act bytes per row and head, a multiple of
+// 4).  Sources are passed by value in chunks.
 constexpr int kKvCompactChunk = 256;
 hipError_t launch_kv_compact(void *kc, void *vc, int n_layer, int H, int max_batch, int max_len,
                              int d, size_t act, int len, const int *rows, int n_keep,

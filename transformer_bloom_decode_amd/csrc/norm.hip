@@ -54,6 +54,33 @@ __device__ __forceinline__ void ln_stats(const float4 (&v)[kLnVec], int h, float
   rstd = 1.0f / sqrtf(var + eps);
 }
 
+// Write the register-held row y[] (columns 4 (threadIdx.x + i kLnThreads) < h) in
+// format fmt.  The int8 formats quantise the whole row with one scale (row_quant of the
+// row's largest magnitude, a block reduction in `sh`); AF_I8 stores that scale `plane`
+// bytes after the first code.
+__device__ __forceinline__ void ln_store_row(const float4 (&y)[kLnVec], void *out, int fmt,
+                                             size_t plane, int row, int h, float *sh) {
+  if (act_is_q8(fmt)) {
+    float am = 0.f;
+#pragma unroll
+    for (int i = 0; i < kLnVec; ++i)
+      if (4 * (threadIdx.x + i * kLnThreads) < h) am = fmaxf(am, fabs4max(y[i]));
+    const RowQuant rq = row_quant(block_max<kLnWaves>(am, sh));
+#pragma unroll
+    for (int i = 0; i < kLnVec; ++i) {
+      const int col = 4 * (threadIdx.x + i * kLnThreads);
+      if (col < h) q8_store4(out, fmt, (size_t)row * h + col, y[i], rq);
+    }
+    if (fmt == AF_I8 && threadIdx.x == 0) q8_scale_ptr(out, plane)[row] = rq.scale;
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < kLnVec; ++i) {
+    const int col = 4 * (threadIdx.x + i * kLnThreads);
+    if (col < h) act_store4(out, fmt, (size_t)row * h + col, plane, y[i]);
+  }
+}
+
 // x[row] = E[token[row]] as float32, then optionally LayerNorm'd.
 template <typename TP>
 __global__ __launch_bounds__(kLnThreads) void k_embed(const int *__restrict__ tokens,
@@ -127,11 +154,11 @@ __global__ __launch_bounds__(kLnThreads) void k_layernorm(const float *__restric
   for (int i = 0; i < kLnVec; ++i) {
     const int col = 4 * (threadIdx.x + i * kLnThreads);
     if (col < h) {
-      const float4 y = ln_apply<TP>(v[i], mean, rstd, gv[i], bv[i]);
-      act_store4(out, fmt, (size_t)row * h + col, plane, y);
-      if (of) Vec4<float>::store(of + col, y);
+      v[i] = ln_apply<TP>(v[i], mean, rstd, gv[i], bv[i]);
+      if (of) Vec4<float>::store(of + col, v[i]);
     }
   }
+  ln_store_row(v, out, fmt, plane, row, h, sh);
 }
 
 // Residual + LayerNorm epilogue of a K-split linear ("DeepSpeed Inference ...", Section
@@ -142,14 +169,16 @@ __global__ __launch_bounds__(kLnThreads) void k_layernorm(const float *__restric
 // column group are loaded before the first add.
 template <typename TP, int S>
 __global__ __launch_bounds__(kLnThreads) void k_splitk_resid_ln(
-    const float *__restrict__ partial, int M, const uint16_t *__restrict__ scale,
-    const TP *__restrict__ bias, float *__restrict__ x, const TP *__restrict__ g,
-    const TP *__restrict__ b, void *__restrict__ out, int fmt, size_t plane, int h, float eps) {
+    const float *__restrict__ partial, int M, const float *__restrict__ xscale,
+    const uint16_t *__restrict__ scale, const TP *__restrict__ bias, float *__restrict__ x,
+    const TP *__restrict__ g, const TP *__restrict__ b, void *__restrict__ out, int fmt,
+    size_t plane, int h, float eps) {
   __shared__ float sh[kLnWaves];
   const int row = blockIdx.x;
   const size_t MN = (size_t)M * h;
   float *xr = x + (size_t)row * h;
   const float *pr = partial + (size_t)row * h;
+  const float xs = xscale ? xscale[row] : 1.f;   // int8 activations: the row's scale
   float4 v[kLnVec];
   Param4<TP> gv[kLnVec], bv[kLnVec];
 #pragma unroll
@@ -167,6 +196,9 @@ __global__ __launch_bounds__(kLnThreads) void k_splitk_resid_ln(
 #pragma unroll
     for (int z = 0; z < S; ++z) {
       y.x += pz[z].x; y.y += pz[z].y; y.z += pz[z].z; y.w += pz[z].w;
+    }
+    if (xscale) {
+      y.x *= xs; y.y *= xs; y.z *= xs; y.w *= xs;
     }
     if (scale) {
       y.x *= h2f(scale[col]); y.y *= h2f(scale[col + 1]);
@@ -188,12 +220,39 @@ __global__ __launch_bounds__(kLnThreads) void k_splitk_resid_ln(
   float mean, rstd;
   ln_stats(v, h, eps, sh, mean, rstd);
 #pragma unroll
-  for (int i = 0; i < kLnVec; ++i) {
-    const int col = 4 * (threadIdx.x + i * kLnThreads);
-    if (col < h)
-      act_store4(out, fmt, (size_t)row * h + col, plane,
-                 ln_apply<TP>(v[i], mean, rstd, gv[i], bv[i]));
-  }
+  for (int i = 0; i < kLnVec; ++i)
+    if (4 * (threadIdx.x + i * kLnThreads) < h) v[i] = ln_apply<TP>(v[i], mean, rstd, gv[i], bv[i]);
+  ln_store_row(v, out, fmt, plane, row, h, sh);
+}
+
+// Per-row int8 quantisation of float32 rows in[rows][K] (K a multiple of 4) into format
+// fmt (AF_I8: codes, then the rows' scales `plane` bytes after the first code; AF_Q8F32:
+// the codes' values as float32): the attention and GeLU outputs of the W8A8 mode, whose
+// rows several blocks produce.  One block per row: the row's largest magnitude, then a
+// second pass (from cache) writes the codes.
+constexpr int kQuantThreads = 1024;
+__global__ __launch_bounds__(kQuantThreads) void k_quant_rows(const float *__restrict__ in, int K,
+                                                              void *__restrict__ out, int fmt,
+                                                              size_t plane) {
+  __shared__ float sh[kQuantThreads / 64];
+  const int row = blockIdx.x;
+  const float *r = in + (size_t)row * K;
+  float am = 0.f;
+  for (int c = 4 * threadIdx.x; c < K; c += 4 * kQuantThreads)
+    am = fmaxf(am, fabs4max(*(const float4 *)(r + c)));
+  const RowQuant rq = row_quant(block_max<kQuantThreads / 64>(am, sh));
+  for (int c = 4 * threadIdx.x; c < K; c += 4 * kQuantThreads)
+    q8_store4(out, fmt, (size_t)row * K + c, *(const float4 *)(r + c), rq);
+  if (fmt == AF_I8 && threadIdx.x == 0) q8_scale_ptr(out, plane)[row] = rq.scale;
+}
+
+hipError_t launch_quant_rows(const float *in, int rows, int K, void *out, int fmt,
+                             hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  if ((fmt != AF_I8 && fmt != AF_Q8F32) || K % 4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_quant_rows, dim3(rows), dim3(kQuantThreads), 0, stream, in, K, out, fmt,
+                     (size_t)rows * K);
+  return hipGetLastError();
 }
 
 // Rows longer than the register tile, or not a multiple of 4: re-read the row.
@@ -290,9 +349,10 @@ bool splitk_resid_ln_supported(int h, int splits) {
   return fits_regs(h) && splits >= 2 && splits <= 8;
 }
 
-hipError_t launch_splitk_resid_ln(const float *partial, int splits, int rows, const void *scale,
-                                  const void *bias, float *x, const void *g, const void *b,
-                                  void *out, int fmt, int h, float eps, hipStream_t stream) {
+hipError_t launch_splitk_resid_ln(const float *partial, int splits, int rows, const float *xscale,
+                                  const void *scale, const void *bias, float *x, const void *g,
+                                  const void *b, void *out, int fmt, int h, float eps,
+                                  hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
   if (!splitk_resid_ln_supported(h, splits)) return hipErrorInvalidValue;
   const dim3 grid(rows), block(kLnThreads);
@@ -302,7 +362,7 @@ hipError_t launch_splitk_resid_ln(const float *partial, int splits, int rows, co
 #define BL_SRL(S)                                                                          \
   case S:                                                                                  \
     hipLaunchKernelGGL((k_splitk_resid_ln<bf16_t, S>), grid, block, 0, stream, partial,   \
-                       rows, sc, bi, x, gg, bb, out, fmt, plane, h, eps);                   \
+                       rows, xscale, sc, bi, x, gg, bb, out, fmt, plane, h, eps);           \
     break;
   switch (splits) {
     BL_SRL(2) BL_SRL(3) BL_SRL(4) BL_SRL(5) BL_SRL(6) BL_SRL(7) BL_SRL(8)
@@ -318,6 +378,7 @@ hipError_t launch_layernorm(bool f32, const float *x, int in_step, int in_off, c
   if (rows <= 0) return hipSuccess;
   const bool reg = fits_regs(h);
   const size_t plane = (size_t)rows * h;
+  if ((fmt == AF_I8 || fmt == AF_Q8F32) && !reg) return hipErrorInvalidValue;
   if (f32) {
     if (reg)
       hipLaunchKernelGGL((k_layernorm<float>), dim3(rows), dim3(kLnThreads), 0, stream, x,
