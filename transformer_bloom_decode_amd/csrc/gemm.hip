@@ -110,9 +110,10 @@ struct LgCfg {
   static_assert((CX + CW) % kWaves == 0 && CPW * (S - 1) < 64, "piece split");
   static_assert(S >= 2 && S <= 6, "stages");
   static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
-  static_assert(BK == 64 || (BK == 32 && sizeof(TW) == 2), "K tile");
+  static_assert(BK == 64 || (BK == 32 && sizeof(TW) == 2) || (BK == 128 && sizeof(TX) == 1),
+                "K tile");
   static_assert(XS == 1 || XS == 2, "activation planes");
-  static_assert(sizeof(TX) == 2 || (sizeof(TW) == 1 && XS == 1 && BK == 64), "W8A8 tiles");
+  static_assert(sizeof(TX) == 2 || (sizeof(TW) == 1 && XS == 1), "W8A8 tiles");
   static_assert(kLds <= 160 * 1024, "LDS");
 };
 
@@ -273,25 +274,26 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_lg(
     const unsigned char *xb = lg_lds + (kt % S) * C::kStage;
     const unsigned char *wb = xb + C::CX * 1024;
     if constexpr (kX8) {
-      // two 32-wide substeps; both operands are 16-byte pieces of 64-byte rows, read for
-      // both substeps before the MFMAs
-      u32x4 a[2][C::TM], bv[2][C::TN];
+      // 32-wide substeps; both operands are 16-byte pieces of the K tile's rows, read for
+      // every substep of the tile before its MFMAs
+      constexpr int NSUB = BK / 32;
+      u32x4 a[NSUB][C::TM], bv[NSUB][C::TN];
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
+      for (int s = 0; s < NSUB; ++s) {
         const int piece = 2 * s + (lane >> 5);
 #pragma unroll
         for (int i = 0; i < C::TM; ++i) {
           const int r = wm * C::WTM + 32 * i + (lane & 31);
-          a[s][i] = *(const u32x4 *)(xb + r * 64 + 16 * lg_slot<64>(r, piece));
+          a[s][i] = *(const u32x4 *)(xb + r * C::XRB + 16 * lg_slot<C::XRB>(r, piece));
         }
 #pragma unroll
         for (int j = 0; j < C::TN; ++j) {
           const int r = wn * C::WTN + 32 * j + (lane & 31);
-          bv[s][j] = *(const u32x4 *)(wb + r * 64 + 16 * lg_slot<64>(r, piece));
+          bv[s][j] = *(const u32x4 *)(wb + r * C::WRB + 16 * lg_slot<C::WRB>(r, piece));
         }
       }
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
+      for (int s = 0; s < NSUB; ++s)
 #pragma unroll
         for (int i = 0; i < C::TM; ++i)
 #pragma unroll
@@ -512,6 +514,10 @@ enum LgTile : int {
   LG_D64W = 7,     // 64 x 256, 4 waves (1 x 4), 3 stages (int8 weights, <= 64 rows, long N)
   LG_D128N = 8,    // 128 x 128, 4 waves (1 x 4), 3 stages (int8 weights, <= 128 rows)
   LG_P8 = 9,       // 128 x 256, 4 waves (1 x 4), 2 stages (int8 weights, prompt pass)
+  LG_X8_128 = 10,  // W8A8: 128 x 256, 8 waves (2 x 4), 3 stages of 128-wide K tiles
+  LG_X8_64 = 11,   // W8A8: 64 x 256, 4 waves (1 x 4), 3 stages of 128-wide K tiles
+  LG_X8_32 = 12,   // W8A8: 32 x 256, 4 waves (1 x 4), 4 stages of 128-wide K tiles
+  LG_D128P = 13,   // two bf16 planes: 128 x 256, 8 waves (2 x 4), 4 stages of 32-wide K tiles
 };
 
 LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax, int act) {
@@ -591,11 +597,24 @@ LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax, int act) {
     p.lg = M <= 32 ? LG_D32 : (M <= 64 ? LG_D64 : LG_D128);
     bm = M <= 32 ? 32 : (M <= 64 ? 64 : 128);
     bn = 128;
+    // two bf16 planes and 65-128 rows: 128 x 256 tiles of 32-wide K tiles (one block per
+    // CU; the 176B share's four linears 254 -> 242 us at 128 rows)
+    if (p.xs == 2 && M > 64) { p.lg = LG_D128P; bn = 256; }
   } else if (q8) {
-    // W8A8: the X tile is 64-byte rows too, so 32-row tiles would not split evenly into
-    // the four waves' 1 KB copies; up to 64 rows take 64 x 256 tiles
-    if (M <= 64) { p.lg = LG_D64W; bm = 64; bn = 256; }
-    else { p.lg = LG_D128N; bm = 128; bn = 128; }
+    // W8A8: 256 weight rows per block and 128-wide K tiles (128-byte rows of both
+    // operands per copy); one block per CU.  Measured on MI355X (full 176B int8 linears,
+    // QKV + dense + up + down, against 64-wide K tiles 128 x 128 / 64 x 256): 128 rows
+    // 879 -> 620 us, 64 rows 626 -> 548, 16 rows 540 -> 475.
+    // (K not a multiple of 128: the 64-wide K tiles, 64 x 256 / 128 x 128)
+    if (K % 128) {
+      if (M <= 64) { p.lg = LG_D64W; bm = 64; bn = 256; }
+      else { p.lg = LG_D128N; bm = 128; bn = 128; }
+    } else {
+      if (M <= 32) { p.lg = LG_X8_32; bm = 32; }
+      else if (M <= 64) { p.lg = LG_X8_64; bm = 64; }
+      else { p.lg = LG_X8_128; bm = 128; }
+      bn = 256;
+    }
   } else if (M <= 32) {
     p.lg = LG_D32W; bm = 32; bn = 256;
   } else if (M <= 64) {
@@ -607,16 +626,21 @@ LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax, int act) {
   p.grid_y = (N + bn - 1) / bn;
   const long tiles = (long)p.grid_x * p.grid_y;
   int sp = 1;
-  if (!i8) {
+  if (!i8 && p.lg != LG_D128P) {
     sp = (int)max(1l, min(8l, 256 / tiles));
   } else {
+    // rounds of resident blocks per split (+10% for the reduction): two blocks per CU
+    // for the 64-wide int8 tiles, one for the large ones
+    const long slots = (p.lg == LG_X8_128 || p.lg == LG_X8_64 || p.lg == LG_X8_32 ||
+                        p.lg == LG_D128P) ? 256 : 512;
     double best_cost = 1e30;
     for (int s2 = 1; s2 <= 8; ++s2) {
-      const double cost = (double)((tiles * s2 + 511) / 512) / s2 + (s2 > 1 ? 0.1 : 0.0);
+      const double cost = (double)((tiles * s2 + slots - 1) / slots) / s2 + (s2 > 1 ? 0.1 : 0.0);
       if (cost < best_cost - 1e-9) { best_cost = cost; sp = s2; }
     }
   }
-  while (sp > 1 && KT / sp < 8) --sp;
+  const int kt_plan = p.lg == LG_D128P ? K / 32 : (q8 && !(K % 128) ? K / 128 : KT);
+  while (sp > 1 && kt_plan / sp < 8) --sp;
   while (sp > 1 && (long)sp * M * N > kLgPartialCapFloats) --sp;
   p.splits = argmax ? 1 : sp;
   return p;
@@ -698,6 +722,10 @@ static hipError_t launch_lg(const LinearPlan &p, const void *X, const void *W, f
       if constexpr (sizeof(TW) == 1)
         return launch_lg_t<TW, 128, 256, 1, 4, 2, kLg, XS>(p, X, W, partial, ep, st);
       return hipErrorInvalidValue;
+    case LG_D128P:
+      if constexpr (sizeof(TW) == 2 && XS == 2)
+        return launch_lg_t<TW, 128, 256, 2, 4, 4, 32, XS>(p, X, W, partial, ep, st);
+      return hipErrorInvalidValue;
     default: return launch_lg_t<TW, 128, 128, 2, 2, 3, kLg, XS>(p, X, W, partial, ep, st);
   }
 }
@@ -706,6 +734,10 @@ static hipError_t launch_lg(const LinearPlan &p, const void *X, const void *W, f
 static hipError_t launch_lg_x8(const LinearPlan &p, const void *X, const void *W, float *partial,
                                const EpiParams &ep, hipStream_t st) {
   switch (p.lg) {
+    case LG_X8_128:
+      return launch_lg_t<int8_t, 128, 256, 2, 4, 3, 128, 1, int8_t>(p, X, W, partial, ep, st);
+    case LG_X8_64: return launch_lg_t<int8_t, 64, 256, 1, 4, 3, 128, 1, int8_t>(p, X, W, partial, ep, st);
+    case LG_X8_32: return launch_lg_t<int8_t, 32, 256, 1, 4, 4, 128, 1, int8_t>(p, X, W, partial, ep, st);
     case LG_D64W: return launch_lg_t<int8_t, 64, 256, 1, 4, 3, kLg, 1, int8_t>(p, X, W, partial, ep, st);
     case LG_D128N: return launch_lg_t<int8_t, 128, 128, 1, 4, 3, kLg, 1, int8_t>(p, X, W, partial, ep, st);
     case LG_P8: return launch_lg_t<int8_t, 128, 256, 1, 4, 2, kLg, 1, int8_t>(p, X, W, partial, ep, st);
@@ -726,6 +758,8 @@ hipError_t launch_linear(int wdtype, const LinearPlan &p, const void *X, const v
   if (p.kind != LIN_LG || p.splits > kMaxSplits || (p.xs != 1 && p.xs != 2))
     return hipErrorInvalidValue;
   if (p.x8 && (wdtype != WT_INT8 || !ep.xscale || ep.mode == EPI_ARGMAX))
+    return hipErrorInvalidValue;
+  if ((p.lg == LG_X8_128 || p.lg == LG_X8_64 || p.lg == LG_X8_32) && p.K % 128)
     return hipErrorInvalidValue;
   hipError_t e;
   if (p.x8)
