@@ -46,6 +46,7 @@ struct WsPlan {
   size_t x, xa, q, o, u, af, amv, ami, part, total;
   size_t stg;   // int8 activations: float32 attention / GeLU rows before quantisation
   size_t kvs;   // int8 KV cache: float32 new keys and values [rows][H][2][d]
+  size_t attn;  // key-split attention partials
   int lm_blocks;
 };
 
@@ -105,6 +106,7 @@ WsPlan plan_ws(const bloom_config *c, int batch, int tokens_per_row) {
   p.af = take((size_t)batch * c->hidden * act);
   p.stg = act_q8(c) ? take(M * std::max(hd, (size_t)c->ffn) * 4) : 0;
   p.kvs = kv_q8(c) ? take(M * hd * 2 * 4) : 0;
+  p.attn = take((size_t)kAttnSplitBlocks * (c->head_dim + 2) * sizeof(float));
   p.lm_blocks = lm_blocks(c);
   p.amv = take((size_t)batch * p.lm_blocks * 4);
   p.ami = take((size_t)batch * p.lm_blocks * 4);
@@ -375,7 +377,8 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
     // projection
     err = launch_attention(kv_fmt(c), q, kc, vc, ksc, vsc, d_valid, stg ? (void *)stg : o,
                            stg ? AF_F32 : fmt_dense, M, H, d, kv->max_len, c->n_head_total,
-                           c->head_offset, tpr, pos_base, d_pos, prompt_len, st);
+                           c->head_offset, tpr, pos_base, d_pos, prompt_len,
+                           (float *)(ws + wp.attn), st);
     if (err == hipSuccess && stg) err = launch_quant_rows(stg, M, hd, o, fmt_dense, st);
     if (err != hipSuccess) return hip_fail(err);
 

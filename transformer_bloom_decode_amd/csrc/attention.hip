@@ -23,6 +23,8 @@
 // ("Hugging Face BLOOM Inference Optimization", Custom CUDA Kernels and Hardware
 // Acceleration, for the fused mask + float32 softmax; "DeepSpeed Inference ...",
 // Section III.D, attention fused as one kernel.)
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -93,7 +95,8 @@ __global__ __launch_bounds__(256) void k_attention(const float *__restrict__ q,
                                                    size_t o_plane, int H, int d, int max_len,
                                                    int n_total, int head_off, int rows_per_seq,
                                                    int pos_base, const int *__restrict__ pos_dev,
-                                                   int prompt_len) {
+                                                   int prompt_len, int chunk,
+                                                   float *__restrict__ part) {
   constexpr int KB = KeysPerBatch<TA>::value;
   constexpr bool kQ = sizeof(TA) == 1;   // int8 cache with per-slot scales
   __shared__ float pv[256 * 8];     // [G][d] per-group P.V partials
@@ -131,17 +134,22 @@ __global__ __launch_bounds__(256) void k_attention(const float *__restrict__ q,
   // Online softmax over batches of G*KB slots (one batch when qpos < G*KB): running
   // maximum mrun (block-uniform), per-thread running sum and P.V accumulators, all
   // rescaled by exp(mrun_old - mrun_new) when the maximum grows.
+  // split over the keys (part set): block z takes slots [z chunk, (z + 1) chunk) and
+  // leaves its unnormalised partial (running max, sum, P.V) for k_attention_merge
+  const int z = blockIdx.z;
+  const int jlo = part ? z * chunk : 0;
+  const int jhi = part ? min(S, jlo + chunk) : S;
   float mrun = -INFINITY, lsum = 0.f;
   float acc[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) acc[t] = 0.f;
-  for (int j0 = 0; j0 < S; j0 += G * KB) {
+  for (int j0 = jlo; j0 < jhi; j0 += G * KB) {
     KVRaw<TA> kr[KB], vr[KB];
     float ks[KB], vs[KB];
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
       const int jj = j0 + u * G + g;
-      if (jj < S) {
+      if (jj < jhi) {
         kr[u].load(kb + (size_t)jj * d + 8 * sub);
         vr[u].load(vb + (size_t)jj * d + 8 * sub);
         if constexpr (kQ) {
@@ -158,13 +166,13 @@ __global__ __launch_bounds__(256) void k_attention(const float *__restrict__ q,
     for (int u = 0; u < KB; ++u) {
       const int jj = j0 + u * G + g;
       float dot = 0.f;
-      if (jj < S) {
+      if (jj < jhi) {
 #pragma unroll
         for (int t = 0; t < 8; ++t) dot = fmaf(qv[t], kr[u].get(t), dot);
       }
       for (int off = L >> 1; off > 0; off >>= 1) dot += __shfl_xor(dot, off, 64);
-      if constexpr (kQ) dot = jj < S ? dot * ks[u] : 0.f;
-      sc[u] = (jj < S && jj >= first) ? dot + slope * (float)(jj - qpos) : -INFINITY;
+      if constexpr (kQ) dot = jj < jhi ? dot * ks[u] : 0.f;
+      sc[u] = (jj < jhi && jj >= first) ? dot + slope * (float)(jj - qpos) : -INFINITY;
       bmax = fmaxf(bmax, sc[u]);
     }
     const float mnew = fmaxf(mrun, block_max<4>(bmax, red));
@@ -176,7 +184,7 @@ __global__ __launch_bounds__(256) void k_attention(const float *__restrict__ q,
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
       const int jj = j0 + u * G + g;
-      if (jj < S && jj >= first) {
+      if (jj < jhi && jj >= first) {
         const float p = __expf(sc[u] - mnew);
         if (sub == 0) lsum += p;                  // each key counted once per group
         float pw = p;
@@ -188,16 +196,54 @@ __global__ __launch_bounds__(256) void k_attention(const float *__restrict__ q,
     mrun = mnew;
   }
   const float total = block_sum<4>(lsum, red);
-  // a query with no visible key (a left-pad position of the prompt) gets o = 0
-  const float inv = qpos < first ? 0.f : 1.0f / total;
 
 #pragma unroll
   for (int t = 0; t < 8; ++t) pv[g * d + 8 * sub + t] = acc[t];
   __syncthreads();
+  if (part) {
+    // partial [m][h][z]: max, sum, then the d P.V sums (all relative to the max)
+    float *pp = part + (((size_t)m * H + h) * gridDim.z + z) * (d + 2);
+    if (tid == 0) { pp[0] = mrun; pp[1] = total; }
+    for (int e = tid; e < d; e += 256) {
+      float s = 0.f;
+      for (int gg = 0; gg < G; ++gg) s += pv[gg * d + e];
+      pp[2 + e] = s;
+    }
+    return;
+  }
+  // a query with no visible key (a left-pad position of the prompt) gets o = 0
+  const float inv = qpos < first ? 0.f : 1.0f / total;
   for (int e = tid; e < d; e += 256) {
     float s = 0.f;
     for (int gg = 0; gg < G; ++gg) s += pv[gg * d + e];
     act_store(o, o_fmt, out0 + e, o_plane, s * inv);
+  }
+}
+
+// Merge of the key-split partials of one (row, head) in split order: with M the largest
+// partial max and w_z = exp(max_z - M) (0 for a split without visible keys), o =
+// sum_z w_z PV_z / sum_z w_z sum_z -- the same softmax over all the keys; no visible
+// key at all gives o = 0.
+__global__ __launch_bounds__(128) void k_attention_merge(const float *__restrict__ part, int nsplit,
+                                                         int H, int d, void *__restrict__ o,
+                                                         int o_fmt, size_t o_plane) {
+  const int mh = blockIdx.x;
+  const float *pp = part + (size_t)mh * nsplit * (d + 2);
+  float mx = -INFINITY;
+  for (int z = 0; z < nsplit; ++z) mx = fmaxf(mx, pp[(size_t)z * (d + 2)]);
+  float den = 0.f;
+  for (int z = 0; z < nsplit; ++z) {
+    const float mz = pp[(size_t)z * (d + 2)];
+    if (mz != -INFINITY) den += __expf(mz - mx) * pp[(size_t)z * (d + 2) + 1];
+  }
+  const float inv = den > 0.f ? 1.0f / den : 0.f;
+  for (int e = threadIdx.x; e < d; e += 128) {
+    float s = 0.f;
+    for (int z = 0; z < nsplit; ++z) {
+      const float mz = pp[(size_t)z * (d + 2)];
+      if (mz != -INFINITY) s += __expf(mz - mx) * pp[(size_t)z * (d + 2) + 2 + e];
+    }
+    act_store(o, o_fmt, (size_t)mh * d + e, o_plane, s * inv);
   }
 }
 
@@ -323,7 +369,8 @@ static void launch_attention_t(const float *q, const void *kc, const void *vc, c
                                size_t o_plane, int rows,
                                int H, int d, int max_len, int n_total, int head_off,
                                int rows_per_seq, int pos_base, const int *pos_dev,
-                               int prompt_len, bool prompt_kernel, int nchunk, hipStream_t st) {
+                               int prompt_len, bool prompt_kernel, int nchunk, int nsplit,
+                               float *part, hipStream_t st) {
   if (prompt_kernel) {
     const dim3 grid((unsigned)(rows / rows_per_seq * nchunk), H), block(256);
     hipLaunchKernelGGL(k_attention_prompt<TA>, grid, block, 0, st, q, (const TA *)kc,
@@ -331,19 +378,40 @@ static void launch_attention_t(const float *q, const void *kc, const void *vc, c
                        n_total,
                        head_off, rows_per_seq, pos_base, prompt_len, nchunk);
   } else {
-    const dim3 grid(rows, H), block(256);
+    const int chunk = (max_len + nsplit - 1) / nsplit;
+    const dim3 grid(rows, H, nsplit), block(256);
     hipLaunchKernelGGL(k_attention<TA>, grid, block, 0, st, q, (const TA *)kc, (const TA *)vc,
                        ksc, vsc, valid_len, o, o_fmt, o_plane, H, d, max_len, n_total, head_off,
-                       rows_per_seq, pos_base, pos_dev, prompt_len);
+                       rows_per_seq, pos_base, pos_dev, prompt_len, chunk,
+                       nsplit > 1 ? part : nullptr);
+    if (nsplit > 1)
+      hipLaunchKernelGGL(k_attention_merge, dim3(rows * H), dim3(128), 0, st, part, nsplit, H, d,
+                         o, o_fmt, o_plane);
   }
+}
+
+// Key splits of the decode attention: enough (row, head, split) blocks to spread a long
+// cache over the chip -- at most kAttnSplitBlocks blocks in all, at least 256 slots of
+// the cache's capacity per split, at most kAttnMaxSplits splits (1: no split).  The
+// capacity, not the current length, sets it, so a captured step replays unchanged.
+int attention_splits(int rows, int H, int max_len, int rows_per_seq) {
+  if (rows_per_seq != 1) return 1;
+  const long heads = (long)rows * H;
+  if (heads >= kAttnSplitBlocks) return 1;
+  const long by_blocks = kAttnSplitBlocks / heads;
+  const long by_len = (max_len + 255) / 256;
+  return (int)std::max(1l, std::min({by_blocks, by_len, (long)kAttnMaxSplits}));
 }
 
 hipError_t launch_attention(int kv_fmt, const float *q, const void *kc, const void *vc,
                             const float *ksc, const float *vsc,
                             const int *valid_len, void *o, int o_fmt, int rows, int H, int d,
                             int max_len, int n_total, int head_off, int rows_per_seq,
-                            int pos_base, const int *pos_dev, int prompt_len, hipStream_t st) {
+                            int pos_base, const int *pos_dev, int prompt_len, float *part,
+                            hipStream_t st) {
   if (rows <= 0) return hipSuccess;
+  const int nsplit = attention_splits(rows, H, max_len, rows_per_seq);
+  if (nsplit > 1 && !part) return hipErrorInvalidValue;
   const size_t o_plane = (size_t)rows * H * d;
   // The prompt kernel when it still fills the chip (>= 256 blocks); a short prompt of
   // one or a few sequences keeps one block per (row, head), which spreads its few keys
@@ -359,7 +427,7 @@ hipError_t launch_attention(int kv_fmt, const float *q, const void *kc, const vo
 #define BL_ATTN(TA)                                                                        \
   launch_attention_t<TA>(q, kc, vc, ksc, vsc, valid_len, o, o_fmt, o_plane, rows, H, d,     \
                          max_len, n_total, head_off, rows_per_seq, pos_base, pos_dev,       \
-                         prompt_len, prompt_kernel, nchunk, st)
+                         prompt_len, prompt_kernel, nchunk, nsplit, part, st)
   if (kv_fmt == AF_I8) BL_ATTN(int8_t);
   else if (kv_fmt == AF_F32) BL_ATTN(float);
   else if (kv_fmt == AF_F16) BL_ATTN(f16_t);

@@ -124,11 +124,17 @@ hipError_t launch_layernorm(bool f32, const float *x, int in_step, int in_off, c
 // position is read from device memory and clamped so that no slot at or past max_len is
 // read.
 // kv_fmt AF_I8: int8 codes with float32 scales ksc / vsc [max_batch][H][max_len] of this
-// layer (else the scale pointers are unused).
+// layer (else the scale pointers are unused).  A decode step over a long cache splits
+// the keys over attention_splits(...) blocks per (row, head); part then holds
+// rows * H * splits * (d + 2) floats (at most kAttnSplitBlocks * (d + 2)).
+constexpr int kAttnSplitBlocks = 1024;
+constexpr int kAttnMaxSplits = 16;
+int attention_splits(int rows, int H, int max_len, int rows_per_seq);
 hipError_t launch_attention(int kv_fmt, const float *q, const void *kc, const void *vc,
                             const float *ksc, const float *vsc, const int *valid_len, void *o, int o_fmt, int rows, int H, int d,
                             int max_len, int n_total, int head_off, int rows_per_seq,
-                            int pos_base, const int *pos_dev, int prompt_len, hipStream_t st);
+                            int pos_base, const int *pos_dev, int prompt_len, float *part,
+                            hipStream_t st);
 
 // Per-row stop rule of the generation loop: done[i] set once row i has finished (its
 // eos_id token emitted, or max_new[i] tokens); finished rows emit pad_id; out_len[i]
