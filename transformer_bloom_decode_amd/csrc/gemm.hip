@@ -38,6 +38,28 @@ __device__ __forceinline__ u32x4 i8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
                i8x2_to_bf16x2(hi, 2)};
 }
 
+// fp16 operands (fp16 activations): two fp16 in one dword from two floats (nearest even)
+__device__ __forceinline__ uint32_t f2x_f16(float a, float b) {
+  return (uint32_t)f2h_bits(a) | ((uint32_t)f2h_bits(b) << 16);
+}
+// eight int8 -> fp16 (exact)
+__device__ __forceinline__ u32x4 i8x8_to_f16x8(uint32_t lo, uint32_t hi) {
+  u32x4 r;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const uint32_t w = t < 2 ? lo : hi;
+    const int b0 = 16 * (t & 1);
+    r[t] = f2x_f16((float)(int)(int8_t)(w >> b0), (float)(int)(int8_t)(w >> (b0 + 8)));
+  }
+  return r;
+}
+// eight bf16 -> fp16: exact for magnitudes from 2^-14 to 65504 (bf16's 8-bit significand
+// fits fp16's 11 bits); smaller ones round to fp16's subnormal grid of 2^-24
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 w) {
+  return u32x4{f2x_f16(lo_bf(w[0]), hi_bf(w[0])), f2x_f16(lo_bf(w[1]), hi_bf(w[1])),
+               f2x_f16(lo_bf(w[2]), hi_bf(w[2])), f2x_f16(lo_bf(w[3]), hi_bf(w[3]))};
+}
+
 
 // ---------------------------------------------------------------------------
 // Prompt-pass GEMM on MFMA 32x32x16 with LDS staged by direct-to-LDS loads
@@ -80,6 +102,12 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// the same block shape on fp16 operands
+__device__ __forceinline__ f32x16 mfma32_f16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
 // 32x32 block, k = 32, int8 x int8 -> int32 (exact): lane l holds A row l % 32 and B
 // row l % 32, k 16 (l / 32) .. +16, as 16 bytes; D as in the bf16 form (checked on
 // MI355X against a CPU product).
@@ -93,6 +121,8 @@ __device__ __forceinline__ i32x16 mfma32_i8(u32x4 a, u32x4 b, i32x16 c) {
 // with the same weights (two MFMAs per block), so the product keeps that precision.
 // TX = int8_t: int8 activation codes against int8 weights (W8A8), int32 accumulators;
 // the epilogue applies the row's activation scale and the weight row's scale.
+// TX = f16_t: fp16 activations on the fp16 MFMA; the weights are turned into fp16 as
+// they are read from LDS (int8 exactly; bf16 exactly down to 2^-14 in magnitude).
 template <typename TW, int BM, int BN, int WGM, int WGN, int S, int BK, int XS,
           typename TX = bf16_t>
 struct LgCfg {
@@ -114,6 +144,7 @@ struct LgCfg {
                 "K tile");
   static_assert(XS == 1 || XS == 2, "activation planes");
   static_assert(sizeof(TX) == 2 || (sizeof(TW) == 1 && XS == 1), "W8A8 tiles");
+  static_assert(!std::is_same<TX, f16_t>::value || XS == 1, "fp16 activations: one plane");
   static_assert(kLds <= 160 * 1024, "LDS");
 };
 
@@ -205,6 +236,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_lg(
   using C = LgCfg<TW, BM, BN, WGM, WGN, S, BK, XS, TX>;
   constexpr bool kI8 = sizeof(TW) == 1;
   constexpr bool kX8 = sizeof(TX) == 1;   // W8A8: int8 x int8 on the int32 MFMA
+  constexpr bool kXH = std::is_same<TX, f16_t>::value;   // fp16 activations, fp16 MFMA
   using Acc = std::conditional_t<kX8, i32x16, f32x16>;
   extern __shared__ __attribute__((aligned(1024))) unsigned char lg_lds[];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -319,9 +351,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_lg(
             const uint2 t = *(const uint2 *)(wb + r * C::WRB +
                                              16 * lg_slot<C::WRB>(r, piece >> 1) +
                                              8 * (piece & 1));
-            bv[q][j] = i8x8_to_bf16x8(t.x, t.y);
+            bv[q][j] = kXH ? i8x8_to_f16x8(t.x, t.y) : i8x8_to_bf16x8(t.x, t.y);
           } else {
-            bv[q][j] = *(const u32x4 *)(wb + r * C::WRB + 16 * lg_slot<C::WRB>(r, piece));
+            const u32x4 t = *(const u32x4 *)(wb + r * C::WRB + 16 * lg_slot<C::WRB>(r, piece));
+            bv[q][j] = kXH ? bf16x8_to_f16x8(t) : t;
           }
         }
       };
@@ -335,7 +368,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm_lg(
           for (int i = 0; i < C::TM; ++i)
 #pragma unroll
             for (int j = 0; j < C::TN; ++j)
-              acc[i][j] = mfma32(a[s & 1][pl][i], bv[s & 1][j], acc[i][j]);
+              acc[i][j] = kXH ? mfma32_f16(a[s & 1][pl][i], bv[s & 1][j], acc[i][j])
+                              : mfma32(a[s & 1][pl][i], bv[s & 1][j], acc[i][j]);
         if constexpr (SCHED) {
           // interleave: one MFMA, then one of the next substep's LDS reads, ...
           if (s + 1 < BK / 16) {
@@ -539,7 +573,9 @@ LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax, int act) {
   }
   // Direct-to-LDS MFMA GEMM for everything else (hidden sizes are multiples of 64).
   p.kind = LIN_LG;
-  p.xs = act == AF_BF16 || q8 ? 1 : 2;
+  // fp16 activations: one fp16 plane on the fp16 MFMA; float32 ones: two bf16 planes
+  p.xs = act == AF_F32 ? 2 : 1;
+  p.xh = act == AF_F16;
   p.x8 = q8;
   p.q8 = q8;
   const int KT = K / kLg;
@@ -626,20 +662,26 @@ LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax, int act) {
   p.grid_y = (N + bn - 1) / bn;
   const long tiles = (long)p.grid_x * p.grid_y;
   int sp = 1;
+  const int kt_plan = p.lg == LG_D128P ? K / 32 : (q8 && !(K % 128) ? K / 128 : KT);
+  const bool x8_tile = p.lg == LG_X8_128 || p.lg == LG_X8_64 || p.lg == LG_X8_32;
   if (!i8 && p.lg != LG_D128P) {
     sp = (int)max(1l, min(8l, 256 / tiles));
+  } else if (x8_tile) {
+    // W8A8 tiles, one block per CU: the fewest splits that put 60% of the CUs to work
+    // (measured on the 176B int8 linears: 168 or 224 blocks stream as fast unsplit as
+    // split, and a split's float32 partials cost traffic -- MLP-up at 128 rows 200 us
+    // unsplit, 282 us in two; 56 blocks want 3-4 splits)
+    while (sp < 8 && tiles * sp < 154) ++sp;
   } else {
-    // rounds of resident blocks per split (+10% for the reduction): two blocks per CU
-    // for the 64-wide int8 tiles, one for the large ones
-    const long slots = (p.lg == LG_X8_128 || p.lg == LG_X8_64 || p.lg == LG_X8_32 ||
-                        p.lg == LG_D128P) ? 256 : 512;
+    // the split minimises rounds of resident blocks per split, +10% for the reduction
+    // pass: two blocks per CU for the 64-wide int8 tiles, one for the two-plane 128 x 256
+    const long slots = p.lg == LG_D128P ? 256 : 512;
     double best_cost = 1e30;
     for (int s2 = 1; s2 <= 8; ++s2) {
       const double cost = (double)((tiles * s2 + slots - 1) / slots) / s2 + (s2 > 1 ? 0.1 : 0.0);
       if (cost < best_cost - 1e-9) { best_cost = cost; sp = s2; }
     }
   }
-  const int kt_plan = p.lg == LG_D128P ? K / 32 : (q8 && !(K % 128) ? K / 128 : KT);
   while (sp > 1 && kt_plan / sp < 8) --sp;
   while (sp > 1 && (long)sp * M * N > kLgPartialCapFloats) --sp;
   p.splits = argmax ? 1 : sp;
@@ -650,6 +692,7 @@ int plan_x_fmt(const LinearPlan &p) {
   if (p.kind == LIN_F32) return AF_F32;
   if (p.kind == LIN_VALU) return p.q8 ? AF_Q8F32 : p.x_fmt;
   if (p.x8) return AF_I8;
+  if (p.xh) return AF_F16;
   return p.xs == 2 ? AF_BF16X2 : AF_BF16;
 }
 
@@ -693,40 +736,40 @@ static hipError_t launch_lg_t(const LinearPlan &p, const void *X, const void *W,
   return hipGetLastError();
 }
 
-template <typename TW, int XS>
+template <typename TW, int XS, typename TX = bf16_t>
 static hipError_t launch_lg(const LinearPlan &p, const void *X, const void *W, float *partial,
                             const EpiParams &ep, hipStream_t st) {
   switch (p.lg) {
     case LG_256:
-      if constexpr (XS == 1) return launch_lg_t<TW, 256, 256, 4, 2, 2>(p, X, W, partial, ep, st);
+      if constexpr (XS == 1) return launch_lg_t<TW, 256, 256, 4, 2, 2, kLg, 1, TX>(p, X, W, partial, ep, st);
       return hipErrorInvalidValue;
-    case LG_128: return launch_lg_t<TW, 128, 128, 2, 2, 2, kLg, XS>(p, X, W, partial, ep, st);
-    case LG_D32: return launch_lg_t<TW, 32, 128, 1, 4, 4, kLg, XS>(p, X, W, partial, ep, st);
-    case LG_D64: return launch_lg_t<TW, 64, 128, 1, 4, 3, kLg, XS>(p, X, W, partial, ep, st);
+    case LG_128: return launch_lg_t<TW, 128, 128, 2, 2, 2, kLg, XS, TX>(p, X, W, partial, ep, st);
+    case LG_D32: return launch_lg_t<TW, 32, 128, 1, 4, 4, kLg, XS, TX>(p, X, W, partial, ep, st);
+    case LG_D64: return launch_lg_t<TW, 64, 128, 1, 4, 3, kLg, XS, TX>(p, X, W, partial, ep, st);
     case LG_256x128:
-      if constexpr (XS == 1) return launch_lg_t<TW, 256, 128, 4, 2, 3>(p, X, W, partial, ep, st);
+      if constexpr (XS == 1) return launch_lg_t<TW, 256, 128, 4, 2, 3, kLg, 1, TX>(p, X, W, partial, ep, st);
       return hipErrorInvalidValue;
     case LG_D32W:
       if constexpr (sizeof(TW) == 1)
-        return launch_lg_t<TW, 32, 256, 1, 4, 4, kLg, XS>(p, X, W, partial, ep, st);
+        return launch_lg_t<TW, 32, 256, 1, 4, 4, kLg, XS, TX>(p, X, W, partial, ep, st);
       return hipErrorInvalidValue;
     case LG_D64W:
       if constexpr (sizeof(TW) == 1)
-        return launch_lg_t<TW, 64, 256, 1, 4, 3, kLg, XS>(p, X, W, partial, ep, st);
+        return launch_lg_t<TW, 64, 256, 1, 4, 3, kLg, XS, TX>(p, X, W, partial, ep, st);
       return hipErrorInvalidValue;
     case LG_D128N:
       if constexpr (sizeof(TW) == 1)
-        return launch_lg_t<TW, 128, 128, 1, 4, 3, kLg, XS>(p, X, W, partial, ep, st);
+        return launch_lg_t<TW, 128, 128, 1, 4, 3, kLg, XS, TX>(p, X, W, partial, ep, st);
       return hipErrorInvalidValue;
     case LG_P8:
       if constexpr (sizeof(TW) == 1)
-        return launch_lg_t<TW, 128, 256, 1, 4, 2, kLg, XS>(p, X, W, partial, ep, st);
+        return launch_lg_t<TW, 128, 256, 1, 4, 2, kLg, XS, TX>(p, X, W, partial, ep, st);
       return hipErrorInvalidValue;
     case LG_D128P:
       if constexpr (sizeof(TW) == 2 && XS == 2)
-        return launch_lg_t<TW, 128, 256, 2, 4, 4, 32, XS>(p, X, W, partial, ep, st);
+        return launch_lg_t<TW, 128, 256, 2, 4, 4, 32, XS, TX>(p, X, W, partial, ep, st);
       return hipErrorInvalidValue;
-    default: return launch_lg_t<TW, 128, 128, 2, 2, 3, kLg, XS>(p, X, W, partial, ep, st);
+    default: return launch_lg_t<TW, 128, 128, 2, 2, 3, kLg, XS, TX>(p, X, W, partial, ep, st);
   }
 }
 
@@ -764,6 +807,9 @@ hipError_t launch_linear(int wdtype, const LinearPlan &p, const void *X, const v
   hipError_t e;
   if (p.x8)
     e = launch_lg_x8(p, X, W, partial, ep, st);
+  else if (p.xh)
+    e = wdtype == WT_BF16 ? launch_lg<bf16_t, 1, f16_t>(p, X, W, partial, ep, st)
+                          : launch_lg<int8_t, 1, f16_t>(p, X, W, partial, ep, st);
   else if (wdtype == WT_BF16)
     e = p.xs == 2 ? launch_lg<bf16_t, 2>(p, X, W, partial, ep, st)
                   : launch_lg<bf16_t, 1>(p, X, W, partial, ep, st);

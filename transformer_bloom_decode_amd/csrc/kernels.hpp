@@ -61,6 +61,7 @@ struct LinearPlan {
   int x_fmt;     // VALU: activation storage (ActFmt: AF_BF16, AF_F32 or AF_F16)
   int xs;        // LG: activation planes (1: bf16; 2: bf16 hi + lo planes of float32 values)
   bool x8;       // LG: int8 activation codes against int8 weights (W8A8)
+  bool xh;       // LG: fp16 activations on the fp16 MFMA
   bool q8;       // the activations are int8-quantised rows (AF_I8 or, for VALU, AF_Q8F32)
 };
 
@@ -77,9 +78,9 @@ hipError_t launch_gemv_ln(int wdtype, int x_fmt, int N, int K, const float *x, c
                           hipStream_t st);
 // act: the model's activation type (ActFmt AF_BF16, AF_F32, AF_F16 or, int8 weights
 // only, AF_I8).  The vector-ALU GEMV reads activations in that type (int8 ones as the
-// float32 values of their codes); the MFMA GEMM reads bf16, for float32 / fp16
-// activations the two bf16 planes hi + lo, for int8 ones the codes (the epilogue
-// multiplies by EpiParams::xscale).
+// float32 values of their codes); the MFMA GEMM reads bf16, fp16 (on the fp16 MFMA),
+// for float32 activations the two bf16 planes hi + lo, for int8 ones the codes (the
+// epilogue multiplies by EpiParams::xscale).
 LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax, int act);
 // Storage format (ActFmt) of the activations a linear of this plan reads.
 int plan_x_fmt(const LinearPlan &p);
