@@ -55,9 +55,12 @@
  *     (LayerNorm outputs, attention output, GeLU output) are held as bf16
  *     (BLOOM_BF16), fp16 (BLOOM_F16: 8x finer than bf16 at the same size; values
  *     beyond fp16's range, 65504, become infinite) or float32 (BLOOM_F32).  The
- *     vector-ALU GEMV (batches of up to 4 rows) reads them in that type; for F16 / F32
- *     the MFMA GEMM reads two bf16 planes hi + lo of each value, each multiplied with
- *     the weights, which keeps the product to ~2^-17 of the float32 one.
+ *     vector-ALU GEMV (batches of up to 4 rows) reads them in that type.  The MFMA GEMM
+ *     (5+ rows) reads bf16 activations as bf16; fp16 ones on the fp16 MFMA, with the
+ *     weights turned into fp16 as they are read (int8 exactly; bf16 exactly from 2^-14
+ *     in magnitude, smaller ones to the nearest multiple of 2^-24); float32 ones as two
+ *     bf16 planes hi + lo of each value, each multiplied with the weights, which keeps
+ *     the product to ~2^-17 of the float32 one.
  *   - act_dtype BLOOM_INT8_ROWSCALE (INT8_ROWSCALE weights only; hidden <= 16384):
  *     W8A8, a variant of DeepSpeed's INT8 inference ([P3] Section VII.B names it
  *     without its scheme).  Each of the four linears' input rows (one token's
