@@ -69,8 +69,7 @@
  *     magnitude), code = nearest integer, ties to even, to v * (127 / amax) in float32,
  *     clamped to [-127, 127]; a row of zeros has scale 0.  The linear is then
  *     y = scale_row * s[r] * sum_k code[k] q[r][k] + bias (int32 sums on the int8 MFMA
- *     for 5+ rows; the GEMV of up to 4 rows reads code * scale as float32, the same
- *     product).  The residual stream, q, the final LayerNorm output and the LM head
+ *     for 5+ rows, float32 sums in the vector-ALU GEMV of up to 4 rows).  The residual stream, q, the final LayerNorm output and the LM head
  *     stay as with F32 activations.
  *   - kv_dtype equals act_dtype, or is BLOOM_INT8_ROWSCALE (any non-F32 weights): an
  *     int8 KV cache holds, per (layer, row, head, slot), head_dim int8 codes of the key

@@ -67,8 +67,9 @@ bool act_q8(const bloom_config *c) { return act_fmt(c) == AF_I8; }
 // reads it as float32 activations.
 int lm_act_fmt(const bloom_config *c) { return act_q8(c) ? AF_F32 : act_fmt(c); }
 // Bytes per activation element in the workspace: bf16 2; float32 / fp16 activations 4
-// (float32, fp16, or the two bf16 planes the MFMA GEMM reads); int8 4 (the codes, or
-// the codes' float32 values the GEMV reads) plus one float32 scale per row.
+// (float32, fp16, or the two bf16 planes the MFMA GEMM reads); int8 4 (one code byte is
+// used; the same regions hold the float32 final-LayerNorm rows the LM head reads) plus
+// one float32 scale per row.
 int act_bytes(const bloom_config *c) { return act_fmt(c) == AF_BF16 ? 2 : 4; }
 size_t act_region(const bloom_config *c, size_t rows, size_t n) {
   return rows * n * act_bytes(c) + (act_q8(c) ? rows * 4 : 0);
@@ -852,7 +853,7 @@ int bloom_linear(const bloom_config *cfg, int32_t M, int32_t N, int32_t K, const
   const void *X = d_x;
   char *xs = (char *)d_ws;
   hipError_t err = hipSuccess;
-  if (lw.fmt == AF_I8 || lw.fmt == AF_Q8F32)
+  if (lw.fmt == AF_I8)
     err = launch_quant_rows(d_x, M, K, xs, lw.fmt, st);
   else if (lw.fmt != AF_F32)
     err = launch_f32_to_act(d_x, xs, lw.fmt, (size_t)M * K, st);

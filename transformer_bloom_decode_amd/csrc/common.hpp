@@ -166,12 +166,9 @@ __device__ __forceinline__ float4 ln_apply(float4 x, float mean, float rstd, con
 // `plane` elements after the hi plane.
 // The int8 activations of the W8A8 mode are quantised per row (row_quant): AF_I8 holds
 // the int8 codes [rows][n] followed, `plane` bytes after the first code, by one float32
-// scale per row (read by the int8 MFMA GEMM); AF_Q8F32 holds the values those codes
-// stand for, code * scale, as float32 (read by the vector-ALU GEMV).  Only kernels that
-// own whole rows write them (the LayerNorms, k_quant_rows).
-enum ActFmt : int { AF_BF16 = 0, AF_F32 = 1, AF_BF16X2 = 2, AF_F16 = 3, AF_I8 = 4, AF_Q8F32 = 5 };
-
-__device__ __forceinline__ bool act_is_q8(int fmt) { return fmt == AF_I8 || fmt == AF_Q8F32; }
+// scale per row, which the consuming linear's epilogue applies (EpiParams::xscale).
+// Only kernels that own whole rows write them (the LayerNorms, k_quant_rows).
+enum ActFmt : int { AF_BF16 = 0, AF_F32 = 1, AF_BF16X2 = 2, AF_F16 = 3, AF_I8 = 4 };
 
 // Symmetric int8 quantisation of a slice whose largest magnitude is amax: scale =
 // amax / 127, and the code of v is the nearest integer (ties to even) to v * (127 /
@@ -194,17 +191,12 @@ __device__ __forceinline__ int quant_code(float v, float inv) {
 __device__ __forceinline__ float fabs4max(float4 v) {
   return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
 }
-// elements i .. i+3 of a row quantised with q, in format fmt (AF_I8 or AF_Q8F32)
-__device__ __forceinline__ void q8_store4(void *p, int fmt, size_t i, float4 v, RowQuant q) {
+// codes of elements i .. i+3 of a row quantised with q (AF_I8)
+__device__ __forceinline__ void q8_store4(void *p, size_t i, float4 v, RowQuant q) {
   const int a = quant_code(v.x, q.inv), b = quant_code(v.y, q.inv);
   const int c = quant_code(v.z, q.inv), d = quant_code(v.w, q.inv);
-  if (fmt == AF_I8)
-    *(uint32_t *)((int8_t *)p + i) =
-        (uint32_t)(a & 255) | ((uint32_t)(b & 255) << 8) | ((uint32_t)(c & 255) << 16) |
-        ((uint32_t)(d & 255) << 24);
-  else
-    *(float4 *)((float *)p + i) =
-        make_float4((float)a * q.scale, (float)b * q.scale, (float)c * q.scale, (float)d * q.scale);
+  *(uint32_t *)((int8_t *)p + i) = (uint32_t)(a & 255) | ((uint32_t)(b & 255) << 8) |
+                                   ((uint32_t)(c & 255) << 16) | ((uint32_t)(d & 255) << 24);
 }
 // scale of row `row` of an AF_I8 buffer whose codes take `plane` bytes
 __device__ __forceinline__ float *q8_scale_ptr(void *p, size_t plane) {

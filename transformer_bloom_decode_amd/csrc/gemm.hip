@@ -565,9 +565,9 @@ LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax, int act) {
   }
   const bool q8 = act == AF_I8;   // W8A8 (int8 weights only; the caller checks)
   if (M <= kValuMaxRows) {
-    // int8 activations: the GEMV reads the values of the int8 codes as float32
+    // int8 activations: the GEMV reads the codes (the epilogue applies the row scales)
     p = plan_valu(wdtype, M, N, K);
-    p.x_fmt = q8 ? AF_F32 : act;
+    p.x_fmt = act;
     p.q8 = q8;
     return p;
   }
@@ -690,7 +690,7 @@ LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax, int act) {
 
 int plan_x_fmt(const LinearPlan &p) {
   if (p.kind == LIN_F32) return AF_F32;
-  if (p.kind == LIN_VALU) return p.q8 ? AF_Q8F32 : p.x_fmt;
+  if (p.kind == LIN_VALU) return p.x_fmt;
   if (p.x8) return AF_I8;
   if (p.xh) return AF_F16;
   return p.xs == 2 ? AF_BF16X2 : AF_BF16;

@@ -60,6 +60,15 @@ template <> struct XOps<float> {
     for (int t = 0; t < 4; ++t) f[t] = __uint_as_float(v[t]);
   }
 };
+template <> struct XOps<int8_t> {   // W8A8 activation codes (the row scale comes later)
+  static constexpr int kPer16 = 16;
+  static __device__ __forceinline__ void widen(u32x4 v, float *f) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) f[4 * t + b] = (float)(int)(int8_t)(v[t] >> (8 * b));
+  }
+};
 template <> struct XOps<f16_t> {
   static constexpr int kPer16 = 8;
   static __device__ __forceinline__ void widen(u32x4 v, float *f) {
@@ -450,11 +459,15 @@ static void launch_valu_w(const LinearPlan &p, const void *X, const void *W, con
                           hipStream_t st) {
   if (p.x_fmt == AF_F32) launch_valu_t<TW, bf16_t, float>(p, X, W, ep, st);
   else if (p.x_fmt == AF_F16) launch_valu_t<TW, bf16_t, f16_t>(p, X, W, ep, st);
+  else if (p.x_fmt == AF_I8) {
+    if constexpr (sizeof(TW) == 1) launch_valu_t<TW, bf16_t, int8_t>(p, X, W, ep, st);
+  }
   else launch_valu_t<TW, bf16_t, bf16_t>(p, X, W, ep, st);
 }
 
 hipError_t launch_valu(int wdtype, const LinearPlan &p, const void *X, const void *W,
                        const EpiParams &ep, hipStream_t st) {
+  if (p.x_fmt == AF_I8 && (wdtype != WT_INT8 || !ep.xscale)) return hipErrorInvalidValue;
   if (wdtype == WT_BF16) launch_valu_w<bf16_t>(p, X, W, ep, st);
   else launch_valu_w<int8_t>(p, X, W, ep, st);
   return hipGetLastError();

@@ -62,7 +62,7 @@ struct LinearPlan {
   int xs;        // LG: activation planes (1: bf16; 2: bf16 hi + lo planes of float32 values)
   bool x8;       // LG: int8 activation codes against int8 weights (W8A8)
   bool xh;       // LG: fp16 activations on the fp16 MFMA
-  bool q8;       // the activations are int8-quantised rows (AF_I8 or, for VALU, AF_Q8F32)
+  bool q8;       // the activations are int8-quantised rows (AF_I8)
 };
 
 // Vector-ALU GEMV (gemv.hip): plan for M <= kValuMaxRows rows, and its launch.
@@ -77,8 +77,8 @@ hipError_t launch_gemv_ln(int wdtype, int x_fmt, int N, int K, const float *x, c
                           const void *b, float eps, const void *W, const EpiParams &ep,
                           hipStream_t st);
 // act: the model's activation type (ActFmt AF_BF16, AF_F32, AF_F16 or, int8 weights
-// only, AF_I8).  The vector-ALU GEMV reads activations in that type (int8 ones as the
-// float32 values of their codes); the MFMA GEMM reads bf16, fp16 (on the fp16 MFMA),
+// only, AF_I8).  The vector-ALU GEMV reads activations in that type (int8 ones as codes,
+// the row scales applied by the epilogue); the MFMA GEMM reads bf16, fp16 (on the fp16 MFMA),
 // for float32 activations the two bf16 planes hi + lo, for int8 ones the codes (the
 // epilogue multiplies by EpiParams::xscale).
 LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax, int act);
@@ -112,8 +112,8 @@ hipError_t launch_splitk_resid_ln(const float *partial, int splits, int rows, co
                                   const void *scale, const void *bias, float *x, const void *g,
                                   const void *b, void *out, int fmt, int h, float eps,
                                   hipStream_t stream);
-// float32 rows [rows][K] -> per-row int8 (fmt AF_I8, scales rows * K bytes after the
-// codes, or AF_Q8F32).
+// float32 rows [rows][K] -> per-row int8 (fmt AF_I8: scales rows * K bytes after the
+// codes).
 hipError_t launch_quant_rows(const float *in, int rows, int K, void *out, int fmt,
                              hipStream_t stream);
 hipError_t launch_layernorm(bool f32, const float *x, int in_step, int in_off, const void *g,

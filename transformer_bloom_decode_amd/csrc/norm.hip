@@ -60,7 +60,7 @@ __device__ __forceinline__ void ln_stats(const float4 (&v)[kLnVec], int h, float
 // bytes after the first code.
 __device__ __forceinline__ void ln_store_row(const float4 (&y)[kLnVec], void *out, int fmt,
                                              size_t plane, int row, int h, float *sh) {
-  if (act_is_q8(fmt)) {
+  if (fmt == AF_I8) {
     float am = 0.f;
 #pragma unroll
     for (int i = 0; i < kLnVec; ++i)
@@ -69,9 +69,9 @@ __device__ __forceinline__ void ln_store_row(const float4 (&y)[kLnVec], void *ou
 #pragma unroll
     for (int i = 0; i < kLnVec; ++i) {
       const int col = 4 * (threadIdx.x + i * kLnThreads);
-      if (col < h) q8_store4(out, fmt, (size_t)row * h + col, y[i], rq);
+      if (col < h) q8_store4(out, (size_t)row * h + col, y[i], rq);
     }
-    if (fmt == AF_I8 && threadIdx.x == 0) q8_scale_ptr(out, plane)[row] = rq.scale;
+    if (threadIdx.x == 0) q8_scale_ptr(out, plane)[row] = rq.scale;
     return;
   }
 #pragma unroll
@@ -225,14 +225,13 @@ __global__ __launch_bounds__(kLnThreads) void k_splitk_resid_ln(
   ln_store_row(v, out, fmt, plane, row, h, sh);
 }
 
-// Per-row int8 quantisation of float32 rows in[rows][K] (K a multiple of 4) into format
-// fmt (AF_I8: codes, then the rows' scales `plane` bytes after the first code; AF_Q8F32:
-// the codes' values as float32): the attention and GeLU outputs of the W8A8 mode, whose
-// rows several blocks produce.  One block per row: the row's largest magnitude, then a
+// Per-row int8 quantisation of float32 rows in[rows][K] (K a multiple of 4) into AF_I8
+// (codes, then the rows' scales `plane` bytes after the first code): the attention and
+// GeLU outputs of the W8A8 mode, whose rows several blocks produce.  One block per row: the row's largest magnitude, then a
 // second pass (from cache) writes the codes.
 constexpr int kQuantThreads = 1024;
 __global__ __launch_bounds__(kQuantThreads) void k_quant_rows(const float *__restrict__ in, int K,
-                                                              void *__restrict__ out, int fmt,
+                                                              void *__restrict__ out,
                                                               size_t plane) {
   __shared__ float sh[kQuantThreads / 64];
   const int row = blockIdx.x;
@@ -242,15 +241,15 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_rows(const float *__res
     am = fmaxf(am, fabs4max(*(const float4 *)(r + c)));
   const RowQuant rq = row_quant(block_max<kQuantThreads / 64>(am, sh));
   for (int c = 4 * threadIdx.x; c < K; c += 4 * kQuantThreads)
-    q8_store4(out, fmt, (size_t)row * K + c, *(const float4 *)(r + c), rq);
-  if (fmt == AF_I8 && threadIdx.x == 0) q8_scale_ptr(out, plane)[row] = rq.scale;
+    q8_store4(out, (size_t)row * K + c, *(const float4 *)(r + c), rq);
+  if (threadIdx.x == 0) q8_scale_ptr(out, plane)[row] = rq.scale;
 }
 
 hipError_t launch_quant_rows(const float *in, int rows, int K, void *out, int fmt,
                              hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
-  if ((fmt != AF_I8 && fmt != AF_Q8F32) || K % 4) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_quant_rows, dim3(rows), dim3(kQuantThreads), 0, stream, in, K, out, fmt,
+  if (fmt != AF_I8 || K % 4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_quant_rows, dim3(rows), dim3(kQuantThreads), 0, stream, in, K, out,
                      (size_t)rows * K);
   return hipGetLastError();
 }
@@ -378,7 +377,7 @@ hipError_t launch_layernorm(bool f32, const float *x, int in_step, int in_off, c
   if (rows <= 0) return hipSuccess;
   const bool reg = fits_regs(h);
   const size_t plane = (size_t)rows * h;
-  if ((fmt == AF_I8 || fmt == AF_Q8F32) && !reg) return hipErrorInvalidValue;
+  if (fmt == AF_I8 && !reg) return hipErrorInvalidValue;
   if (f32) {
     if (reg)
       hipLaunchKernelGGL((k_layernorm<float>), dim3(rows), dim3(kLnThreads), 0, stream, x,
