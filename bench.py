@@ -45,6 +45,9 @@ def parse():
                          "own JSON line)")
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--new-tokens", type=int, default=None)
+    ap.add_argument("--prompt-len", type=int, default=None,
+                    help="prompt tokens per row (default: the workload's; long prompts run "
+                         "the decode attention split over the keys)")
     ap.add_argument("--layers", type=int, default=None, help="truncate the stack (development)")
     ap.add_argument("--act", choices=("f32", "f16", "bf16", "int8"), default=None,
                     help="activation type of bf16 / int8 models: float32, fp16, bf16, or int8 "
@@ -373,7 +376,7 @@ def main():
         act = args.act or ("bf16" if m.weight_dtype == "int8" else "f16")
         m = dataclasses.replace(m, activations=act, kv_cache=args.kv)
     B = args.batch
-    P = wl.prompt_len
+    P = args.prompt_len or wl.prompt_len
     n_new = args.new_tokens or wl.new_tokens
     torch.cuda.set_device(0)
 
