@@ -802,6 +802,10 @@ int bloom_lm_logits(const bloom_config *cfg, const bloom_weights *w, int32_t bat
   return BLOOM_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
 // Workspace of a standalone linear: the activations in the form the plan reads, then
 // the split-K partials.
 struct LinearWs {
@@ -827,6 +831,10 @@ int check_linear(const bloom_config *cfg, int32_t M, int32_t N, int32_t K) {
   if (cfg->act_dtype == BLOOM_INT8_ROWSCALE && K > 1 << 24) return BLOOM_EINVAL;
   return BLOOM_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 int bloom_linear_workspace_bytes(const bloom_config *cfg, int32_t M, int32_t N, int32_t K,
                                  size_t *bytes) {
