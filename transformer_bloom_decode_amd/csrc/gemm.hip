@@ -38,9 +38,12 @@ __device__ __forceinline__ u32x4 i8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
                i8x2_to_bf16x2(hi, 2)};
 }
 
-// fp16 operands (fp16 activations): two fp16 in one dword from two floats (nearest even)
+// fp16 operands (fp16 activations): two floats -> two fp16 in one dword, a in the low
+// half (nearest even, one packed conversion instruction)
 __device__ __forceinline__ uint32_t f2x_f16(float a, float b) {
-  return (uint32_t)f2h_bits(a) | ((uint32_t)f2h_bits(b) << 16);
+  typedef f16_t h2v __attribute__((ext_vector_type(2)));
+  typedef float f2v __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2v){a, b}, h2v));
 }
 // eight int8 -> fp16 (exact)
 __device__ __forceinline__ u32x4 i8x8_to_f16x8(uint32_t lo, uint32_t hi) {
