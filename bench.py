@@ -45,6 +45,9 @@ def parse():
                          "own JSON line)")
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--new-tokens", type=int, default=None)
+    ap.add_argument("--ln-fold", action="store_true",
+                    help="fold the LayerNorms of batch-1 steps into the QKV / MLP-up GEMVs "
+                         "(bloom_ln_fold; measured as fast as the separate LayerNorms)")
     ap.add_argument("--prompt-len", type=int, default=None,
                     help="prompt tokens per row (default: the workload's; long prompts run "
                          "the decode attention split over the keys)")
@@ -383,6 +386,11 @@ def main():
     t0 = time.perf_counter()
     cfg = tb.make_config(m)
     dw = device_weights(m, cfg)
+    ln_fold = m.weight_dtype == "bf16" and args.ln_fold
+    if ln_fold:
+        # LayerNorm fold vectors, computed once per model (used by one-row passes)
+        dw.fold_layernorm(cfg)
+        torch.cuda.synchronize()
     prompt, valid = bi.prompts(m, B, P)
     tok = torch.from_numpy(prompt).cuda()
     vl = torch.from_numpy(valid).cuda()
@@ -510,7 +518,7 @@ def main():
                    "layers": m.n_layer, "hidden": m.hidden, "heads_local": m.n_head_local,
                    "heads_total": m.n_head_total, "ffn_local": m.ffn, "vocab": m.vocab,
                    "weights": m.weight_dtype, "activations": m.act_dtype,
-                   "kv_cache": m.kv_dtype, "greedy": not args.sample,
+                   "kv_cache": m.kv_dtype, "ln_fold": ln_fold, "greedy": not args.sample,
                    "parallelism": "none (1 GPU)", "loop": args.loop,
                    "tokens": "sampled (temperature 0.8, top-p 0.9)" if args.sample else "greedy"},
         "tokens_per_s": round(B * n_new / (ms_per_step * 1e-3), 2),

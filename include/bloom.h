@@ -142,12 +142,18 @@ typedef struct bloom_layer_weights {
 } bloom_layer_weights;
 
 /* emb_ln_* may be NULL when embed_ln == 0.  `layers` is a HOST array of n_layer
- * entries (each holding device pointers); it is read during the call only. */
+ * entries (each holding device pointers); it is read during the call only.
+ * ln_fold (nullable) holds the LayerNorm fold vectors written by bloom_ln_fold for these
+ * weights; when set, one-row forward passes of BF16-weight models with bf16 / fp16
+ * activations whose hidden size is above 4096 fold the input and post-attention
+ * LayerNorms into the QKV and MLP-up GEMVs (see bloom_ln_fold).  The vectors must be
+ * rewritten whenever the weights change. */
 typedef struct bloom_weights {
   const void *embed;
   const void *emb_ln_g, *emb_ln_b;
   const void *lnf_g, *lnf_b;
   const bloom_layer_weights *layers;
+  const float *ln_fold;
 } bloom_weights;
 
 /* KV cache.  k and v are caller-owned device buffers of
@@ -391,6 +397,28 @@ int bloom_linear_workspace_bytes(const bloom_config *cfg, int32_t M, int32_t N, 
 int bloom_linear(const bloom_config *cfg, int32_t M, int32_t N, int32_t K, const float *d_x,
                  const void *d_w, const void *d_s, const void *d_b, float *d_y, void *d_ws,
                  size_t ws_bytes, void *stream);
+
+/* LayerNorm fold ("DeepSpeed Inference ...", Section III.D: the input LayerNorm is
+ * fused with the QKV GeMM and the post-attention LayerNorm with the intermediate GeMM).
+ * A LayerNorm followed by a linear is, per output n,
+ *   y_n = sum_k W[n][k] (g_k (x_k - mean) rstd + b_k) + bias_n
+ *       = rstd (sum_k W[n][k] g_k x_k - mean c_n) + d_n,
+ *   c_n = sum_k W[n][k] g_k,   d_n = sum_k W[n][k] b_k + bias_n,
+ * so the linear can run on g * x while the row's statistics are formed beside it.  With
+ * the vectors c and d, a one-row pass has the residual epilogue of the dense (MLP-down)
+ * projection also store g2 * x (the next layer's g1 * x) in the activation type and an
+ * fp16 copy of x; the MLP-up (next QKV) GEMV reads g * x as its activations, forms mean
+ * and rstd of x from the fp16 copy (two passes in float32) and applies the formula in
+ * its epilogue, and the separate LayerNorm launches go away.  Activations are then
+ * rounded as g * x instead of as the LayerNorm output.
+ * bloom_ln_fold writes, for every layer l, float32 [c_qkv (3 Hd) | d_qkv (3 Hd) | c_up (F)
+ * | d_up (F)] at d_fold + l * (6 Hd + 2 F) (sums in float64, rounded once), from the
+ * BF16 weights behind w; bloom_ln_fold_bytes gives the size.  Asynchronous on `stream`.
+ * EDTYPE for weights other than BF16; EINVAL for missing pointers; EWORKSPACE if bytes
+ * is too small. */
+int bloom_ln_fold_bytes(const bloom_config *cfg, size_t *bytes);
+int bloom_ln_fold(const bloom_config *cfg, const bloom_weights *w, float *d_fold,
+                  size_t bytes, void *stream);
 
 /* Dynamic batch extraction ("Hugging Face BLOOM Inference Optimization", Webserver
  * Architecture and Request Handling: requests that have finished are taken out of the

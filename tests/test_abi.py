@@ -44,7 +44,7 @@ def test_struct_layout_matches_header():
     assert ctypes.sizeof(tb.bloom_gen_control) == 8 + 7 * 8 + 8
     assert ctypes.sizeof(tb.bloom_config) == 52
     assert ctypes.sizeof(tb.bloom_layer_weights) == 16 * 8
-    assert ctypes.sizeof(tb.bloom_weights) == 6 * 8
+    assert ctypes.sizeof(tb.bloom_weights) == 7 * 8
     assert ctypes.sizeof(tb.bloom_kv_cache) == 2 * 8 + 4 * 4 + 3 * 8
 
 
@@ -290,3 +290,24 @@ def test_sampling_and_lm_logits_validation_paths():
     assert lg(ctypes.byref(f.w), 2, None, 0x10, 1 << 40) == tb.BLOOM_EINVAL
     assert lg(ctypes.byref(f.w), 2, 0x10, 0x10, 16) == tb.BLOOM_EWORKSPACE
     assert lg(ctypes.byref(f.w), 0, None, None, 0) == tb.BLOOM_OK
+
+
+def test_ln_fold_sizes_and_validation_paths():
+    """bloom_ln_fold_bytes: per layer 2 (3 Hd + F) float32; bloom_ln_fold rejects non-bf16
+    weights, a short buffer, a null buffer and missing weight pointers before launching."""
+    m = bi.BLOOM_176B_TP8_RANK0.truncated(2)
+    f = _Fake(m)
+    n = ctypes.c_size_t(0)
+    assert tb.lib.bloom_ln_fold_bytes(ctypes.byref(f.cfg), ctypes.byref(n)) == tb.BLOOM_OK
+    hd = m.n_head_local * m.head_dim
+    assert n.value == 2 * 2 * (3 * hd + m.ffn) * 4
+
+    def fold(ff, buf=0x1000, nbytes=1 << 40):
+        return tb.lib.bloom_ln_fold(ctypes.byref(ff.cfg), ctypes.byref(ff.w), buf, nbytes, None)
+
+    assert fold(f, nbytes=n.value - 4) == tb.BLOOM_EWORKSPACE
+    assert fold(f, buf=None) == tb.BLOOM_EINVAL
+    f.layers[1].w_up = None
+    assert fold(f) == tb.BLOOM_EINVAL
+    g = _Fake(bi.BLOOM_176B_INT8.truncated(2))
+    assert fold(g) == tb.BLOOM_EDTYPE

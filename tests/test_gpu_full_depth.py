@@ -9,9 +9,10 @@
    * float32 activations: hidden rel-L2 <= 1e-2, the spec gate, and <= 1e-3 (the
      bf16-pair operands keep every activation to 2^-17; the float64 oracle with
      float32-rounded activations is 5e-7 from the exact one at 70 layers).
-   * fp16 activations and KV cache (the benchmarked configuration): <= 1e-2 (the float64
-     oracle with fp16-rounded activations and KV is 3.0e-3 from the exact one at 70
-     layers).
+   * fp16 activations and KV cache: <= 1e-2 (the float64 oracle with fp16-rounded
+     activations and KV is 3.0e-3 from the exact one at 70 layers), also with the
+     LayerNorms of the decode steps folded into the QKV / MLP-up GEMVs (bloom_ln_fold,
+     the benchmarked configuration).
    * bf16 activations do not meet 1e-2 at this depth: the float64 oracle with its
      activations rounded to bf16 at the same points is itself 2.5e-2 from the exact
      oracle (attention scores spread ~6 with these weights, so a rounding of q or k
@@ -122,24 +123,33 @@ def test_tp_share_176b_full_depth_parity(share_weights):
     *_, ids32, hid32 = _generate(share_weights, "f32", n_new)
     *_, idsh, hidh = _generate(share_weights, "f16", n_new)
     *_, ids16, hid16 = _generate(share_weights, "bf16", n_new)
+    # fp16 with the LayerNorms of the decode steps folded into the QKV / MLP-up GEMVs
+    # (the benchmarked configuration)
+    share_weights.fold_layernorm(tb.make_config(dataclasses.replace(M_SHARE, activations="f16")))
+    *_, idsf, hidf = _generate(share_weights, "f16", n_new)
+    share_weights.unfold_layernorm()
     torch.cuda.empty_cache()
-    assert np.array_equal(ids32, idsh)
+    assert np.array_equal(ids32, idsh) and np.array_equal(ids32, idsf)
     om, h, hr = _oracle_states(ids32, n_new, rounded=np.array_equal(ids32, ids16))
     rel32 = float(np.linalg.norm(hid32[:, 0] - h) / np.linalg.norm(h))
     ok32, ex32 = _ids_ok(om, h, ids32, n_new, 1e-2)
     relh = float(np.linalg.norm(hidh[:, 0] - h) / np.linalg.norm(h))
     okh, exh = _ids_ok(om, h, idsh, n_new, 1e-2)
+    relf = float(np.linalg.norm(hidf[:, 0] - h) / np.linalg.norm(h))
+    okf, exf = _ids_ok(om, h, idsf, n_new, 1e-2)
     if hr is None:   # the bf16 run chose other tokens: its own teacher-forced pass
         om, h, hr = _oracle_states(ids16, n_new, rounded=True)
     rel16 = float(np.linalg.norm(hid16[:, 0] - h) / np.linalg.norm(h))
     rel_ref = float(np.linalg.norm(hr - h) / np.linalg.norm(h))
     ok16, ex16 = _ids_ok(om, h, ids16, n_new, 1e-2)
     _log(f"176b share, 70 layers: float32 activations hidden rel {rel32:.2e} (exact ids "
-         f"{ex32:.2f}); fp16 {relh:.2e} (exact ids {exh:.2f}); bf16 activations "
+         f"{ex32:.2f}); fp16 {relh:.2e} (exact ids {exh:.2f}), with folded LayerNorms "
+         f"{relf:.2e} (exact ids {exf:.2f}); bf16 activations "
          f"{rel16:.2e} against the bf16-activation oracle's {rel_ref:.2e} (exact ids "
          f"{ex16:.2f})")
     assert rel32 <= 1e-2 and rel32 <= 1e-3 and ok32          # the gate, float32 activations
     assert relh <= 1e-2 and okh                               # the gate, fp16 activations
+    assert relf <= 1e-2 and okf                               # the gate, folded LayerNorms
     assert rel16 <= 1.25 * rel_ref and ok16                   # bf16 activations: regression
 
 

@@ -47,7 +47,7 @@ class bloom_layer_weights(ctypes.Structure):
 class bloom_weights(ctypes.Structure):
     _fields_ = [("embed", _c_void_p), ("emb_ln_g", _c_void_p), ("emb_ln_b", _c_void_p),
                 ("lnf_g", _c_void_p), ("lnf_b", _c_void_p),
-                ("layers", ctypes.POINTER(bloom_layer_weights))]
+                ("layers", ctypes.POINTER(bloom_layer_weights)), ("ln_fold", _c_void_p)]
 
 
 class bloom_kv_cache(ctypes.Structure):
@@ -110,6 +110,8 @@ def _load():
     lib.bloom_sample_workspace_bytes.argtypes = [_i32, _i32, P(ctypes.c_size_t)]
     lib.bloom_init_weights.argtypes = [P(bloom_config), P(bloom_weights), ctypes.c_uint64,
                                        ctypes.c_double, vp]
+    lib.bloom_ln_fold_bytes.argtypes = [P(bloom_config), P(ctypes.c_size_t)]
+    lib.bloom_ln_fold.argtypes = [P(bloom_config), P(bloom_weights), vp, ctypes.c_size_t, vp]
     lib.bloom_sample_tokens_static.argtypes = [vp, _i32, _i32, vp, vp, vp, vp, vp]
     lib.bloom_sample_scratch_limit.argtypes = [_i32, _i32, P(_i32), P(ctypes.c_size_t)]
     lib.bloom_linear_workspace_bytes.argtypes = [P(bloom_config), _i32, _i32, _i32,
@@ -125,7 +127,7 @@ def _load():
                  "bloom_lm_logits", "bloom_sample_tokens", "bloom_sample_workspace_bytes",
                  "bloom_sample_tokens_static", "bloom_sample_scratch_limit",
                  "bloom_init_weights", "bloom_linear", "bloom_linear_workspace_bytes",
-                 "bloom_timer_enable",
+                 "bloom_ln_fold_bytes", "bloom_ln_fold", "bloom_timer_enable",
                  "bloom_timer_disable", "bloom_timer_read", "bloom_timer_pause"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
@@ -395,6 +397,22 @@ def bloom_init_weights(cfg, weights, seed: int = 0, sigma: float = 0.02, stream=
                                   _stream(stream)), "bloom_init_weights")
 
 
+def bloom_ln_fold_bytes(cfg) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib.bloom_ln_fold_bytes(ctypes.byref(cfg), ctypes.byref(n)), "bloom_ln_fold_bytes")
+    return n.value
+
+
+def bloom_ln_fold(cfg, weights, fold, stream=None):
+    """Write the LayerNorm fold vectors of the weights into `fold` (float32 device tensor of
+    bloom_ln_fold_bytes(cfg) bytes; bloom.h)."""
+    import torch
+    w = weights.struct if hasattr(weights, "struct") else weights
+    _require(fold, bloom_ln_fold_bytes(cfg) // 4, torch.float32, "fold")
+    _check(lib.bloom_ln_fold(ctypes.byref(cfg), ctypes.byref(w), _ptr(fold), _nbytes(fold),
+                             _stream(stream)), "bloom_ln_fold")
+
+
 def to_device(a, device="cuda"):
     """numpy array (float32, int8, or uint16 bit patterns) -> torch device tensor, same bytes."""
     import numpy as np
@@ -418,6 +436,24 @@ class DeviceWeights:
         self.struct = bloom_weights(_ptr(g["embed"]), _ptr(g.get("emb_ln_g")),
                                     _ptr(g.get("emb_ln_b")), _ptr(g["lnf_g"]), _ptr(g["lnf_b"]),
                                     self._layer_arr)
+
+    def fold_layernorm(self, cfg, stream=None):
+        """Compute the LayerNorm fold vectors (bloom_ln_fold) into a new device buffer and
+        point the struct at it: one-row passes then fold LN1 / LN2 into the QKV / MLP-up
+        GEMVs where the library supports it.  Only for BF16 weights; a no-op otherwise."""
+        import torch
+        if cfg.weight_dtype != BLOOM_BF16:
+            return self
+        self.fold = torch.empty(bloom_ln_fold_bytes(cfg) // 4, dtype=torch.float32,
+                                device="cuda")
+        bloom_ln_fold(cfg, self, self.fold, stream)
+        self.struct.ln_fold = _ptr(self.fold)
+        return self
+
+    def unfold_layernorm(self):
+        """Stop folding (the struct's ln_fold back to NULL)."""
+        self.struct.ln_fold = None
+        return self
 
     @classmethod
     def from_arrays(cls, tensors: dict, device="cuda"):

@@ -47,6 +47,7 @@ struct WsPlan {
   size_t stg;   // int8 activations: float32 attention / GeLU rows before quantisation
   size_t kvs;   // int8 KV cache: float32 new keys and values [rows][H][2][d]
   size_t attn;  // key-split attention partials
+  size_t x16;   // folded LayerNorm: fp16 copy of the residual row
   int lm_blocks;
 };
 
@@ -108,6 +109,7 @@ WsPlan plan_ws(const bloom_config *c, int batch, int tokens_per_row) {
   p.stg = act_q8(c) ? take(M * std::max(hd, (size_t)c->ffn) * 4) : 0;
   p.kvs = kv_q8(c) ? take(M * hd * 2 * 4) : 0;
   p.attn = take((size_t)kAttnSplitBlocks * (c->head_dim + 2) * sizeof(float));
+  p.x16 = take((size_t)batch * c->hidden * 2);
   p.lm_blocks = lm_blocks(c);
   p.amv = take((size_t)batch * p.lm_blocks * 4);
   p.ami = take((size_t)batch * p.lm_blocks * 4);
@@ -328,7 +330,21 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
   // One activation row and a short hidden size: LN1 and LN2 run as the prologue of the
   // QKV and MLP-up GEMVs instead of as launches of their own.
   const bool ln_in_gemv = !f32 && !act_q8(c) && gemv_ln_supported(wdt, M, h);
+  // With the caller's fold vectors (bloom_ln_fold), a one-row pass folds LN1 and LN2
+  // into the QKV and MLP-up GEMVs: the residual epilogues of dense and down also store
+  // gamma * x and an fp16 copy of x, and the consumers finish the LayerNorm in their
+  // epilogue.  Layer 0's LN1 (after the embedding) stays a launch.
+  uint16_t *x16 = (uint16_t *)(ws + wp.x16);
+  const size_t fold_layer = 2 * (size_t)(3 * hd + F);
+  EpiParams probe{};
+  probe.mode = EPI_QKV;
+  probe.ln_x16 = x16;
+  probe.ln_cd = w->ln_fold;
+  const bool ln_fold = w->ln_fold && !ln_in_gemv && M == 1 &&
+                       ln_fold_supported(wdt, p_qkv, probe) &&
+                       ln_fold_supported(wdt, p_up, probe) && fmt_qkv == fmt_up;
   bool ln1_done = false;   // xa already holds LN1(x) of this layer
+  bool ln1_folded = false; // xa holds gamma1 * x (the previous down projection's epilogue)
   for (int l = 0; l < c->n_layer; ++l) {
     const bloom_layer_weights &L = w->layers[l];
     void *kc = (char *)kv->k + l * layer_stride;
@@ -336,7 +352,7 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
     float *ksc = kvs ? (float *)kv->k_scale + l * scale_stride : nullptr;
     float *vsc = kvs ? (float *)kv->v_scale + l * scale_stride : nullptr;
 
-    if (!ln1_done && !ln_in_gemv) {
+    if (!ln1_done && !ln1_folded && !ln_in_gemv) {
       err = launch_layernorm(f32, x, 1, 0, L.ln1_g, L.ln1_b, xa, fmt_qkv, nullptr, M, h,
                              c->ln_eps, st);
       if (err != hipSuccess) return hip_fail(err);
@@ -354,6 +370,13 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
     e.q_scale = 1.0f / sqrtf((float)d);
     e.xscale = xscale(fmt_qkv, xa, h);
     e.kv_stage = kvs;
+    if (ln1_folded) {
+      // d_qkv holds the bias
+      e.bias = nullptr;
+      e.ln_x16 = x16;
+      e.ln_cd = w->ln_fold + l * fold_layer;
+      e.ln_eps = c->ln_eps;
+    }
     if (ln_in_gemv)
       err = timed(kernel_class(p_qkv), wbytes(3 * hd, h), st, [&] {
         return launch_gemv_ln(wdt, act, 3 * hd, h, x, L.ln1_g, L.ln1_b, c->ln_eps, L.w_qkv, e,
@@ -389,6 +412,12 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
     r.scale = (const uint16_t *)L.s_dense;
     r.out = x; r.ld = h;
     r.xscale = xscale(fmt_dense, o, hd);
+    if (ln_fold) {
+      r.fold_g = L.ln2_g;
+      r.fold_u = xa;
+      r.fold_fmt = fmt_up;
+      r.fold_x16 = x16;
+    }
     const bool fuse_dense = fuse_ln(p_dense);
     err = timed_linear(wdt, p_dense, o, L.w_dense, part, r, st, wbytes(h, hd), !fuse_dense);
     if (err != hipSuccess) return hip_fail(err);
@@ -396,7 +425,7 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
     if (fuse_dense)
       err = launch_splitk_resid_ln(part, p_dense.splits, M, r.xscale, L.s_dense, L.b_dense, x,
                                    L.ln2_g, L.ln2_b, xa, fmt_up, h, c->ln_eps, st);
-    else if (!ln_in_gemv)
+    else if (!ln_in_gemv && !ln_fold)
       err = launch_layernorm(f32, x, 1, 0, L.ln2_g, L.ln2_b, xa, fmt_up, nullptr, M, h,
                              c->ln_eps, st);
     if (err != hipSuccess) return hip_fail(err);
@@ -412,6 +441,12 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
     if (stg) {   // int8 activations: GeLU rows in float32, then quantised per row
       g.out = stg;
       g.out_fmt = AF_F32;
+    }
+    if (ln_fold) {
+      g.bias = nullptr;   // d_up holds it
+      g.ln_x16 = x16;
+      g.ln_cd = w->ln_fold + l * fold_layer + 2 * (size_t)(3 * hd);
+      g.ln_eps = c->ln_eps;
     }
     if (ln_in_gemv && !fuse_dense)
       err = timed(kernel_class(p_up), wbytes(F, h), st, [&] {
@@ -429,6 +464,13 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
     dn.out = x; dn.ld = h;
     dn.xscale = xscale(fmt_down, u, F);
     const bool fuse_down = l + 1 < c->n_layer && fuse_ln(p_down) && !ln_in_gemv;
+    ln1_folded = ln_fold && l + 1 < c->n_layer;
+    if (ln1_folded) {
+      dn.fold_g = w->layers[l + 1].ln1_g;
+      dn.fold_u = xa;
+      dn.fold_fmt = fmt_qkv;
+      dn.fold_x16 = x16;
+    }
     err = timed_linear(wdt, p_down, u, L.w_down, part, dn, st, wbytes(h, F), !fuse_down);
     if (err != hipSuccess) return hip_fail(err);
     if (fuse_down) {
@@ -876,6 +918,39 @@ int bloom_linear(const bloom_config *cfg, int32_t M, int32_t N, int32_t K, const
   e.xscale = lw.fmt == AF_I8 ? (const float *)(xs + (size_t)M * K) : nullptr;
   err = launch_linear(wtype(cfg), lw.plan, X, d_w, (float *)((char *)d_ws + lw.x_bytes), e, st);
   return err == hipSuccess ? BLOOM_OK : hip_fail(err);
+}
+
+int bloom_ln_fold_bytes(const bloom_config *cfg, size_t *bytes) {
+  int s = check_config(cfg);
+  if (s != BLOOM_OK) return s;
+  if (!bytes) return BLOOM_EINVAL;
+  const size_t hd = (size_t)cfg->n_head_local * cfg->head_dim;
+  *bytes = (size_t)cfg->n_layer * 2 * (3 * hd + (size_t)cfg->ffn) * sizeof(float);
+  return BLOOM_OK;
+}
+
+int bloom_ln_fold(const bloom_config *cfg, const bloom_weights *w, float *d_fold, size_t bytes,
+                  void *stream) {
+  int s = check_config(cfg);
+  if (s != BLOOM_OK) return s;
+  if ((s = check_weights(cfg, w)) != BLOOM_OK) return s;
+  if (cfg->weight_dtype != BLOOM_BF16) return BLOOM_EDTYPE;
+  if (!d_fold) return BLOOM_EINVAL;
+  size_t need = 0;
+  bloom_ln_fold_bytes(cfg, &need);
+  if (bytes < need) return BLOOM_EWORKSPACE;
+  clear_stale_hip_error();
+  hipStream_t st = (hipStream_t)stream;
+  const int h = cfg->hidden, F = cfg->ffn, n3 = 3 * cfg->n_head_local * cfg->head_dim;
+  for (int l = 0; l < cfg->n_layer; ++l) {
+    const bloom_layer_weights &L = w->layers[l];
+    float *f = d_fold + (size_t)l * 2 * (n3 + F);
+    hipError_t e = launch_ln_fold(L.w_qkv, L.ln1_g, L.ln1_b, L.b_qkv, n3, h, f, f + n3, st);
+    if (e == hipSuccess)
+      e = launch_ln_fold(L.w_up, L.ln2_g, L.ln2_b, L.b_up, F, h, f + 2 * n3, f + 2 * n3 + F, st);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return BLOOM_OK;
 }
 
 int bloom_init_weights(const bloom_config *cfg, const bloom_weights *w, uint64_t seed,

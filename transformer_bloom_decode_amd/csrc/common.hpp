@@ -278,6 +278,17 @@ struct EpiParams {
   float *am_val;           // [M][am_stride]
   int *am_idx;
   int am_stride;
+  // EPI_RESID with the next LayerNorm folded into its consumer: also stores
+  // fold_g[n] * x[n] (ActFmt fold_fmt) to fold_u and fp16(x[n]) to fold_x16
+  const void *fold_g;      // [ld] the next LayerNorm's gamma (parameter type), nullable
+  void *fold_u;            // [M][ld]
+  int fold_fmt;
+  uint16_t *fold_x16;      // [M][ld]
+  // consumer of a folded LayerNorm (one-row GEMV): the activations are gamma * x; the
+  // kernel forms mean and rstd of x from ln_x16 and applies rstd (acc - mean c) + d
+  const uint16_t *ln_x16;  // [K] fp16 residual row, nullable
+  const float *ln_cd;      // [2][N]: c then d
+  float ln_eps;
 };
 
 // y = acc * scale[n] + bias[n], then the mode's action.  TP = parameter type.
@@ -313,7 +324,13 @@ __device__ __forceinline__ void epilogue(const EpiParams &e, int m, int n, float
     }
     case EPI_RESID: {
       float *x = (float *)e.out + (size_t)m * e.ld + n;
-      *x = *x + y;
+      const float xn = *x + y;
+      *x = xn;
+      if (e.fold_g) {
+        const size_t i = (size_t)m * e.ld + n;
+        act_store(e.fold_u, e.fold_fmt, i, 0, to_f<TP>(((const TP *)e.fold_g)[n]) * xn);
+        e.fold_x16[i] = f2h_bits(xn);
+      }
       break;
     }
     case EPI_GELU:

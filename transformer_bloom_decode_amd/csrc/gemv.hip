@@ -241,6 +241,12 @@ __global__ __launch_bounds__(256) void k_gemv_valu(const TX *__restrict__ X,
 // keep the separate LayerNorm.
 constexpr int kGemvLnMaxK = 4096;
 
+// s_waitcnt vmcnt(V) alone (expcnt and lgkmcnt unconstrained)
+template <int V> __device__ __forceinline__ void wait_vmcnt_lnf() {
+  static_assert(V >= 0 && V < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((V & 15) | ((V >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // s_waitcnt lgkmcnt(0) alone (vmcnt and expcnt unconstrained), then s_barrier
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));
@@ -395,6 +401,115 @@ hipError_t launch_gemv_ln(int wdtype, int x_fmt, int N, int K, const float *x, c
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// one-row decode GEMV with the preceding LayerNorm folded into it
+// ---------------------------------------------------------------------------
+// The LayerNorm before QKV / MLP-up ("DeepSpeed Inference ...", Section III.D fuses it
+// with the GeMM that follows) as y_n = rstd (sum_k W[n][k] (g x)_k - mean c_n) + d_n with
+// c_n = sum_k W[n][k] g_k and d_n = sum_k W[n][k] b_k + bias_n precomputed (ep.ln_cd):
+// the activations X are g * x, stored by the residual epilogue of the previous
+// projection together with an fp16 copy of x (ep.ln_x16).  One weight row per wave, 4
+// per block; every block forms mean and rstd itself.  In issue order (a wave's vector
+// memory loads complete in that order):
+//   1. the fp16 row x16 straight into LDS, NPW 1 KB copies per wave (no registers);
+//   2. the wave's whole weight row and the activation row g * x (U 16-byte loads each,
+//      every one unconditional, at the wave's piece start plus the lane's offset);
+//   3. once the copies of step 1 have landed (vmcnt: the 2U loads of step 2 may still
+//      be outstanding) and a barrier that waits for LDS only, mean and rstd of x16 from
+//      LDS (two passes, float32, a fixed order), while the weights are in flight;
+//   4. the dot product (each piece as soon as its loads have landed), then
+//      rstd (acc - mean c_n) + d_n into the linear's epilogue.
+// Rows of a multiple of 512 elements up to kLnFoldMaxK.
+constexpr int kLnFoldMaxK = 14336;   // 28 pieces of 512
+template <typename TW, typename TX, int U>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_gemv_lnf(
+    const TX *__restrict__ X, const TW *__restrict__ W, int N, int K, EpiParams ep) {
+  using VO = VOps<TW>;
+  using XO = XOps<TX>;
+  constexpr int E = VO::kPerLane;
+  constexpr int step = 64 * E;
+  static_assert(E == XO::kPer16, "one 16-byte activation piece per weight piece");
+  constexpr int NPW = (kLnFoldMaxK / 512 + 3) / 4;   // copies per wave (1 KB each)
+  static_assert(NPW + 2 * U < 64, "vmcnt");
+  __shared__ __attribute__((aligned(1024))) uint16_t lnx[kLnFoldMaxK];
+  __shared__ float red[2][4];
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row = blockIdx.x * 4 + wid;
+  const TW *wr = W + (size_t)min(row, N - 1) * K;
+
+  // 1. x16 -> LDS: piece pc (512 elements) by wave pc % 4; pieces past the row repeat
+  // its last one (the same bytes to the same place), so every wave issues exactly NPW
+  // copies
+  const int pieces = K / 512;
+#pragma unroll
+  for (int j = 0; j < NPW; ++j) {
+    const int pc = min(wid + 4 * j, pieces - 1);
+    __builtin_amdgcn_global_load_lds((const void *)(ep.ln_x16 + pc * 512 + lane * 8),
+                                     (__attribute__((address_space(3))) void *)(
+                                         (unsigned char *)lnx + pc * 1024),
+                                     16, 0, 0);
+  }
+  // 2. the weight row and the activation row (K is a multiple of the 512-element wave
+  // piece; pieces past the row repeat its last one)
+  u32x4 cw[U], cx[U];
+  const int kmax = K - step;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int k0 = min(u * step, kmax);
+    cw[u] = __builtin_nontemporal_load((const u32x4 *)(wr + k0 + lane * E));
+    cx[u] = *(const u32x4 *)(X + k0 + lane * E);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // 3. statistics of x while the loads above are in flight
+  wait_vmcnt_lnf<2 * U>();
+  lds_barrier();
+  const int n8 = K / 8;
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < kLnFoldMaxK / 8 / 256; ++j) {
+    const int p = threadIdx.x + 256 * j;
+    if (p < n8) {
+      const u32x4 t = *(const u32x4 *)(lnx + 8 * p);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) s += f16lo(t[q]) + f16hi(t[q]);
+    }
+    // one LDS read at a time: the weight and activation rows hold the registers
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const float mean = gemv_block_sum(s, red[0]) / (float)K;
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < kLnFoldMaxK / 8 / 256; ++j) {
+    const int p = threadIdx.x + 256 * j;
+    if (p < n8) {
+      const u32x4 t = *(const u32x4 *)(lnx + 8 * p);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float a = f16lo(t[q]) - mean, b = f16hi(t[q]) - mean;
+        ss += a * a + b * b;
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const float rstd = 1.0f / sqrtf(gemv_block_sum(ss, red[1]) / (float)K + ep.ln_eps);
+  // 4. the dot product (the repeated pieces past the row are skipped)
+  float acc = 0.f;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (u * step < K) {
+      float wf[E], xf[E];
+      VO::widen(cw[u], wf);
+      XO::widen(cx[u], xf);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc = fmaf(wf[e], xf[e], acc);
+    }
+  }
+  acc = wave_sum(acc);
+  if (lane == 0 && row < N)
+    epilogue<bf16_t>(ep, 0, row, rstd * (acc - mean * ep.ln_cd[row]) + ep.ln_cd[N + row]);
+}
+
 LinearPlan plan_valu(int wdtype, int M, int N, int K) {
   LinearPlan p{};
   p.M = M; p.N = N; p.K = K;
@@ -436,6 +551,15 @@ static void launch_valu_t(const LinearPlan &p, const void *X, const void *W, con
   const TW *w = (const TW *)W;
   if constexpr (std::is_same<TW, bf16_t>::value) {
     if (p.vr == 1 && p.mt == 1 && !p.vdb) {
+      if constexpr (sizeof(TX) == 2) {
+        if (ep.ln_x16) {   // LayerNorm folded in (checked by launch_valu)
+          if (p.vu == 16)
+            BL_LAUNCH((k_gemv_lnf<TW, TX, 16>), grid, block, 0, st, x, w, p.N, p.K, ep);
+          else
+            BL_LAUNCH((k_gemv_lnf<TW, TX, 28>), grid, block, 0, st, x, w, p.N, p.K, ep);
+          return;
+        }
+      }
       if (p.vu == 16)
         BL_LAUNCH((k_gemv_valu<TW, TP, TX, 1, 1, 16, false>), grid, block, 0, st, x, w, p.M, p.N, p.K, ep);
       else
@@ -465,11 +589,57 @@ static void launch_valu_w(const LinearPlan &p, const void *X, const void *W, con
   else launch_valu_t<TW, bf16_t, bf16_t>(p, X, W, ep, st);
 }
 
+// The folded-LayerNorm GEMV exists for one row of bf16 / fp16 activations against bf16
+// weights on the whole-row plans, for rows of a multiple of 512 elements up to
+// kLnFoldMaxK.
+bool ln_fold_supported(int wdtype, const LinearPlan &p, const EpiParams &ep) {
+  return wdtype == WT_BF16 && p.kind == LIN_VALU && p.M == 1 && p.mt == 1 && p.vr == 1 &&
+         !p.vdb && (p.x_fmt == AF_F16 || p.x_fmt == AF_BF16) && p.K <= kLnFoldMaxK &&
+         p.K % 512 == 0 && ep.ln_cd && ep.mode != EPI_ARGMAX;
+}
+
 hipError_t launch_valu(int wdtype, const LinearPlan &p, const void *X, const void *W,
                        const EpiParams &ep, hipStream_t st) {
   if (p.x_fmt == AF_I8 && (wdtype != WT_INT8 || !ep.xscale)) return hipErrorInvalidValue;
+  if (ep.ln_x16 && !ln_fold_supported(wdtype, p, ep)) return hipErrorInvalidValue;
   if (wdtype == WT_BF16) launch_valu_w<bf16_t>(p, X, W, ep, st);
   else launch_valu_w<int8_t>(p, X, W, ep, st);
+  return hipGetLastError();
+}
+
+// c_n = sum_k W[n][k] g_k and d_n = sum_k W[n][k] b_k + bias_n for one linear (one
+// wave per row; float64 sums in a fixed order, rounded once to float32).
+__global__ __launch_bounds__(256) void k_ln_fold(const bf16_t *__restrict__ W,
+                                                 const bf16_t *__restrict__ g,
+                                                 const bf16_t *__restrict__ b,
+                                                 const bf16_t *__restrict__ bias, int N, int K,
+                                                 float *__restrict__ c, float *__restrict__ d) {
+  const int lane = threadIdx.x & 63;
+  const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= N) return;
+  const bf16_t *wr = W + (size_t)n * K;
+  double sc = 0.0, sd = 0.0;
+  for (int k = lane; k < K; k += 64) {
+    const double w = (double)bf2f(wr[k]);
+    sc += w * (double)bf2f(g[k]);
+    sd += w * (double)bf2f(b[k]);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    sc += __shfl_xor(sc, o, 64);
+    sd += __shfl_xor(sd, o, 64);
+  }
+  if (lane == 0) {
+    c[n] = (float)sc;
+    d[n] = (float)(sd + (bias ? (double)bf2f(bias[n]) : 0.0));
+  }
+}
+
+hipError_t launch_ln_fold(const void *W, const void *g, const void *b, const void *bias, int N,
+                          int K, float *c, float *d, hipStream_t st) {
+  if (N <= 0) return hipSuccess;
+  BL_LAUNCH(k_ln_fold, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, st, (const bf16_t *)W,
+            (const bf16_t *)g, (const bf16_t *)b, (const bf16_t *)bias, N, K, c, d);
   return hipGetLastError();
 }
 

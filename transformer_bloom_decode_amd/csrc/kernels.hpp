@@ -69,6 +69,12 @@ struct LinearPlan {
 LinearPlan plan_valu(int wdtype, int M, int N, int K);
 hipError_t launch_valu(int wdtype, const LinearPlan &p, const void *X, const void *W,
                        const EpiParams &ep, hipStream_t st);
+// The one-row GEMV with a folded LayerNorm (ep.ln_x16, ep.ln_cd): supported for this plan?
+bool ln_fold_supported(int wdtype, const LinearPlan &p, const EpiParams &ep);
+// LayerNorm fold vectors of one linear: c[n] = sum_k W[n][k] g[k], d[n] = sum_k W[n][k]
+// b[k] + bias[n] (bf16 W [N][K], g, b [K], bias [N] nullable).
+hipError_t launch_ln_fold(const void *W, const void *g, const void *b, const void *bias, int N,
+                          int K, float *c, float *d, hipStream_t st);
 // One-row GEMV whose prologue is the LayerNorm of the float32 row x (gamma g, beta b,
 // bf16): out = epilogue(LN(x) . W^T); bf16 or int8 weights, K a multiple of 16 up to
 // 4096 (gemv_ln_supported).
