@@ -558,6 +558,7 @@ enum LgTile : int {
   LG_256H = 14,    // fp16 activations: 256 x 256, 8 waves (2 x 4), 2 stages (1024+ rows)
   LG_256x128H = 15,  // fp16 activations: 256 x 128, 8 waves (2 x 4), 3 stages (512-1023 rows)
   LG_128H = 16,    // fp16 activations: 128 x 128, 4 waves (1 x 4), 2 stages (256-511 rows)
+  LG_X8_P = 17,    // W8A8 prompt pass: 256 x 256, 8 waves (2 x 4), 2 stages of 128-wide K tiles
 };
 
 LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax, int act) {
@@ -605,13 +606,18 @@ LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax, int act) {
     // 4 x 2, 1 x 4 instead of 2 x 2).  Measured (176B share, the four linears, fp16
     // activations): 2048 rows 2190 -> 1838 us, 512 rows 637 -> 559 us, 256 rows 367 ->
     // 346 us.
-    if (wdtype == WT_INT8) p.lg = LG_P8;
+    // W8A8 with K a multiple of 128: 256 x 256 tiles of 128-wide K tiles (128-byte rows of
+    // both operands per copy, as the bf16 prompt tiles); measured on the full 176B int8
+    // linears against the 128 x 256 tiles of 64-wide K tiles: 256 rows 1556 -> 971 us,
+    // 1024 rows 5322 -> 3184 us, 2048 rows 10353 -> 5792 us (35% of the int8 peak).
+    if (wdtype == WT_INT8) p.lg = (q8 && K % 128 == 0) ? LG_X8_P : LG_P8;
     else if (p.xs == 2) p.lg = LG_128;
     else if (p.xh) p.lg = M >= 1024 ? LG_256H : (M >= 512 ? LG_256x128H : LG_128H);
     else p.lg = M >= 1024 ? LG_256 : (M >= 512 ? LG_256x128 : LG_128);
     const bool bm128 = p.lg == LG_128 || p.lg == LG_P8 || p.lg == LG_128H;
     const int bm = bm128 ? 128 : 256;
-    const int bn = (p.lg == LG_256 || p.lg == LG_P8 || p.lg == LG_256H) ? 256 : 128;
+    const int bn =
+        (p.lg == LG_256 || p.lg == LG_P8 || p.lg == LG_256H || p.lg == LG_X8_P) ? 256 : 128;
     const int slots = bm128 ? 512 : 256;
     p.grid_x = (M + bm - 1) / bm;
     p.grid_y = (N + bn - 1) / bn;
@@ -804,6 +810,7 @@ static hipError_t launch_lg_x8(const LinearPlan &p, const void *X, const void *W
     case LG_D64W: return launch_lg_t<int8_t, 64, 256, 1, 4, 3, kLg, 1, int8_t>(p, X, W, partial, ep, st);
     case LG_D128N: return launch_lg_t<int8_t, 128, 128, 1, 4, 3, kLg, 1, int8_t>(p, X, W, partial, ep, st);
     case LG_P8: return launch_lg_t<int8_t, 128, 256, 1, 4, 2, kLg, 1, int8_t>(p, X, W, partial, ep, st);
+    case LG_X8_P: return launch_lg_t<int8_t, 256, 256, 2, 4, 2, 128, 1, int8_t>(p, X, W, partial, ep, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -822,7 +829,7 @@ hipError_t launch_linear(int wdtype, const LinearPlan &p, const void *X, const v
     return hipErrorInvalidValue;
   if (p.x8 && (wdtype != WT_INT8 || !ep.xscale || ep.mode == EPI_ARGMAX))
     return hipErrorInvalidValue;
-  if ((p.lg == LG_X8_128 || p.lg == LG_X8_64 || p.lg == LG_X8_32) && p.K % 128)
+  if ((p.lg == LG_X8_128 || p.lg == LG_X8_64 || p.lg == LG_X8_32 || p.lg == LG_X8_P) && p.K % 128)
     return hipErrorInvalidValue;
   hipError_t e;
   if (p.x8)
