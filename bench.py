@@ -45,9 +45,10 @@ def parse():
                          "own JSON line)")
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--new-tokens", type=int, default=None)
-    ap.add_argument("--ln-fold", action="store_true",
-                    help="fold the LayerNorms of batch-1 steps into the QKV / MLP-up GEMVs "
-                         "(bloom_ln_fold; measured as fast as the separate LayerNorms)")
+    ap.add_argument("--no-ln-fold", action="store_true",
+                    help="keep the LayerNorms of batch-1 steps as launches of their own "
+                         "(by default bf16-weight batch-1 runs fold them into the QKV / "
+                         "MLP-up GEMVs with bloom_ln_fold)")
     ap.add_argument("--prompt-len", type=int, default=None,
                     help="prompt tokens per row (default: the workload's; long prompts run "
                          "the decode attention split over the keys)")
@@ -386,7 +387,7 @@ def main():
     t0 = time.perf_counter()
     cfg = tb.make_config(m)
     dw = device_weights(m, cfg)
-    ln_fold = m.weight_dtype == "bf16" and args.ln_fold
+    ln_fold = m.weight_dtype == "bf16" and B == 1 and not args.no_ln_fold
     if ln_fold:
         # LayerNorm fold vectors, computed once per model (used by one-row passes)
         dw.fold_layernorm(cfg)

@@ -144,10 +144,9 @@ typedef struct bloom_layer_weights {
 /* emb_ln_* may be NULL when embed_ln == 0.  `layers` is a HOST array of n_layer
  * entries (each holding device pointers); it is read during the call only.
  * ln_fold (nullable) holds the LayerNorm fold vectors written by bloom_ln_fold for these
- * weights; when set, one-row forward passes of BF16-weight models with bf16 / fp16
- * activations whose hidden size is above 4096 fold the input and post-attention
- * LayerNorms into the QKV and MLP-up GEMVs (see bloom_ln_fold).  The vectors must be
- * rewritten whenever the weights change. */
+ * weights; when set, one-row forward passes of BF16-weight models whose hidden size is
+ * above 4096 fold the input and post-attention LayerNorms into the QKV and MLP-up GEMVs
+ * (see bloom_ln_fold).  The vectors must be rewritten whenever the weights change. */
 typedef struct bloom_weights {
   const void *embed;
   const void *emb_ln_g, *emb_ln_b;
@@ -406,11 +405,14 @@ int bloom_linear(const bloom_config *cfg, int32_t M, int32_t N, int32_t K, const
  *   c_n = sum_k W[n][k] g_k,   d_n = sum_k W[n][k] b_k + bias_n,
  * so the linear can run on g * x while the row's statistics are formed beside it.  With
  * the vectors c and d, a one-row pass has the residual epilogue of the dense (MLP-down)
- * projection also store g2 * x (the next layer's g1 * x) in the activation type and an
- * fp16 copy of x; the MLP-up (next QKV) GEMV reads g * x as its activations, forms mean
- * and rstd of x from the fp16 copy (two passes in float32) and applies the formula in
- * its epilogue, and the separate LayerNorm launches go away.  Activations are then
- * rounded as g * x instead of as the LayerNorm output.
+ * projection also store g2 * x (the next layer's g1 * x) in the activation type, and
+ * that projection's blocks add their float64 sums of x and x^2 to integer accumulators
+ * in the workspace (each sum split into its floor and its fraction in 2^-44 units, so
+ * that the totals do not depend on the order of the additions; the pass's embedding
+ * launch zeroes them).  The MLP-up (next QKV) GEMV reads g * x as its activations, forms
+ * mean and rstd of x from the totals and applies the formula in its epilogue, and the
+ * separate LayerNorm launches go away.  Activations are then rounded as g * x instead
+ * of as the LayerNorm output.
  * bloom_ln_fold writes, for every layer l, float32 [c_qkv (3 Hd) | d_qkv (3 Hd) | c_up (F)
  * | d_up (F)] at d_fold + l * (6 Hd + 2 F) (sums in float64, rounded once), from the
  * BF16 weights behind w; bloom_ln_fold_bytes gives the size.  Asynchronous on `stream`.

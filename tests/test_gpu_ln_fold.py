@@ -1,18 +1,20 @@
 """The LayerNorm fold of one-row passes (bloom_ln_fold; include/bloom.h): with the fold
 vectors c_n = sum_k W[n][k] g_k and d_n = sum_k W[n][k] b_k + bias_n, the QKV and MLP-up
 GEMVs of a batch-1 decode step read g * x (stored by the residual epilogue of the
-previous projection) and finish rstd (acc - mean c_n) + d_n, and the separate LayerNorm
+previous projection, whose blocks also add their sums of x and x^2 to integer
+accumulators) and finish rstd (acc - mean c_n) + d_n, and the separate LayerNorm
 launches go away ("DeepSpeed Inference ...", Section III.D fuses each LayerNorm with the
 GeMM that follows it).
 
 * The fold vectors equal float64 sums of the stored weights (float32 rounding).
-* Batch 1 at the 176B share's width (hidden 14336), 2 layers, fp16 and bf16
+* Batch 1 at the 176B share's width (hidden 14336), 2 layers, fp16, bf16 and float32
   activations: against the oracle within the same bound as the unfolded path (1e-2),
   greedy ids by the teacher-forced rule, and close to the unfolded run (the two round
   different values to the activation type: g * x here, the LayerNorm output there).
-* Graph replays equal the eager loop bit for bit; where the fold does not apply (batch 2,
-  or hidden <= 4096, where the LayerNorm already runs inside the GEMV) a folded weight
-  set gives the unfolded results bit for bit.
+* Graph replays equal the eager loop bit for bit (the accumulated sums do not depend on
+  the order in which blocks add them); where the fold does not apply (batch 2, or hidden
+  <= 4096, where the LayerNorm already runs inside the GEMV) a folded weight set gives
+  the unfolded results bit for bit.
 """
 import dataclasses
 
@@ -57,7 +59,7 @@ def test_fold_vectors_equal_float64_sums():
                   f"{np.max(np.abs(c - c_ref) / tc):.2f}")
 
 
-@pytest.mark.parametrize("act", ["f16", "bf16"])
+@pytest.mark.parametrize("act", ["f16", "bf16", "f32"])
 def test_fold_batch1_two_layers_matches_oracle(act):
     m = dataclasses.replace(M2, activations=act)
     T, dw, cfg = upload(m)

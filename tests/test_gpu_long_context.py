@@ -4,8 +4,8 @@ blocks alone would leave the chip idle, and a merge kernel combines the ranges' 
 softmax sums in range order ("Hugging Face BLOOM Inference Optimization", Custom CUDA
 Kernels and Hardware Acceleration: the fused masked softmax in float32).  Compared with
 the oracle, teacher-forced, at a KV length of 2048: left-padded rows (whole key ranges
-masked), a batch whose rows each split, and the captured decode step of bloom_generate
-(its position from device memory)."""
+masked), a batch whose rows each split, the captured decode step of bloom_generate
+(its position from device memory), and the int8 cache."""
 import dataclasses
 
 import numpy as np
@@ -63,4 +63,22 @@ def test_tp_share_176b_kv2048():
     run = run_gpu(cfg, dw, prompt, vl, n_new, max_len=2048)
     v = compare(m, T, prompt, vl, run, 1e-2, widen_embed=True)
     print(f"176b share L1 kv2048: hidden rel {v.hidden_rel:.2e}, exact ids {v.exact_frac:.3f}")
+    assert v.hidden_rel <= 1e-2 and v.tokens_ok
+
+
+@pytest.mark.parametrize("shape, act, batch, valid", [
+    (bi.BLOOM_560M.truncated(2), "f32", 3, (2000, 1500, 900)),
+    (bi.BLOOM_176B_TP8_RANK0.truncated(1), "f16", 1, None)])
+def test_int8_cache_kv2048(shape, act, batch, valid):
+    """The int8 cache over a long cache: each lane reads 16 codes of a key or value row
+    (head dims 64 and 128), the key ranges split and merge as for the other caches; the
+    oracle rounds the cached keys and values to int8 per (row, head, slot)."""
+    m = dataclasses.replace(shape, activations=act, kv_cache="int8")
+    T, dw, cfg = upload(m)
+    P, n_new = (2000, 48) if valid else (2040, 9)
+    prompt, vl = bi.prompts(m, batch, P, valid)
+    run = run_gpu(cfg, dw, prompt, vl, n_new, max_len=2048)
+    v = compare(m, T, prompt, vl, run, 1e-2, widen_embed=True)
+    print(f"{m.name} L{m.n_layer} {act} int8 KV kv2048 B{batch}: hidden rel "
+          f"{v.hidden_rel:.2e}, exact ids {v.exact_frac:.3f}")
     assert v.hidden_rel <= 1e-2 and v.tokens_ok

@@ -47,7 +47,7 @@ struct WsPlan {
   size_t stg;   // int8 activations: float32 attention / GeLU rows before quantisation
   size_t kvs;   // int8 KV cache: float32 new keys and values [rows][H][2][d]
   size_t attn;  // key-split attention partials
-  size_t x16;   // folded LayerNorm: fp16 copy of the residual row
+  size_t stats; // folded LayerNorms: [n_layer][LN1, LN2][kStatWords] sum accumulators
   int lm_blocks;
 };
 
@@ -109,7 +109,7 @@ WsPlan plan_ws(const bloom_config *c, int batch, int tokens_per_row) {
   p.stg = act_q8(c) ? take(M * std::max(hd, (size_t)c->ffn) * 4) : 0;
   p.kvs = kv_q8(c) ? take(M * hd * 2 * 4) : 0;
   p.attn = take((size_t)kAttnSplitBlocks * (c->head_dim + 2) * sizeof(float));
-  p.x16 = take((size_t)batch * c->hidden * 2);
+  p.stats = take((size_t)c->n_layer * 2 * kStatWords * sizeof(unsigned long long));
   p.lm_blocks = lm_blocks(c);
   p.amv = take((size_t)batch * p.lm_blocks * 4);
   p.ami = take((size_t)batch * p.lm_blocks * 4);
@@ -302,9 +302,6 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
   float *stg = act_q8(c) ? (float *)(ws + wp.stg) : nullptr;
   float *kvs = kv_q8(c) ? (float *)(ws + wp.kvs) : nullptr;
 
-  hipError_t err = launch_embed(f32, d_tokens, w->embed, w->emb_ln_g, w->emb_ln_b, x, M, h,
-                                c->vocab, c->embed_ln, c->ln_eps, st);
-  if (err != hipSuccess) return hip_fail(err);
 
   const size_t layer_stride = (size_t)kv->max_batch * H * kv->max_len * d * kv_bytes(c);
   const size_t scale_stride = (size_t)kv->max_batch * H * kv->max_len;   // int8 cache
@@ -332,17 +329,29 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
   const bool ln_in_gemv = !f32 && !act_q8(c) && gemv_ln_supported(wdt, M, h);
   // With the caller's fold vectors (bloom_ln_fold), a one-row pass folds LN1 and LN2
   // into the QKV and MLP-up GEMVs: the residual epilogues of dense and down also store
-  // gamma * x and an fp16 copy of x, and the consumers finish the LayerNorm in their
+  // gamma * x and add their blocks' sums of x and x^2 to the LayerNorm's accumulators
+  // (zeroed by the embedding kernel), and the consumers finish the LayerNorm in their
   // epilogue.  Layer 0's LN1 (after the embedding) stays a launch.
-  uint16_t *x16 = (uint16_t *)(ws + wp.x16);
+  unsigned long long *stats = (unsigned long long *)(ws + wp.stats);
+  auto ln_stats = [&](int l, int which) { return stats + (2 * (size_t)l + which) * kStatWords; };
   const size_t fold_layer = 2 * (size_t)(3 * hd + F);
-  EpiParams probe{};
-  probe.mode = EPI_QKV;
-  probe.ln_x16 = x16;
-  probe.ln_cd = w->ln_fold;
+  EpiParams cons{}, prod{};
+  cons.mode = EPI_QKV;
+  cons.ln_stats = stats;
+  cons.ln_cd = w->ln_fold;
+  prod.mode = EPI_RESID;
+  prod.fold_g = w->ln_fold;   // (any non-null pointer: only the plan is probed)
+  prod.fold_u = xa;
+  prod.fold_stats = stats;
   const bool ln_fold = w->ln_fold && !ln_in_gemv && M == 1 &&
-                       ln_fold_supported(wdt, p_qkv, probe) &&
-                       ln_fold_supported(wdt, p_up, probe) && fmt_qkv == fmt_up;
+                       ln_fold_supported(wdt, p_qkv, cons) &&
+                       ln_fold_supported(wdt, p_up, cons) &&
+                       ln_fold_supported(wdt, p_dense, prod) &&
+                       ln_fold_supported(wdt, p_down, prod) && fmt_qkv == fmt_up;
+  hipError_t err = launch_embed(f32, d_tokens, w->embed, w->emb_ln_g, w->emb_ln_b, x, M, h,
+                                c->vocab, c->embed_ln, c->ln_eps, ln_fold ? stats : nullptr,
+                                ln_fold ? c->n_layer * 2 * kStatWords : 0, st);
+  if (err != hipSuccess) return hip_fail(err);
   bool ln1_done = false;   // xa already holds LN1(x) of this layer
   bool ln1_folded = false; // xa holds gamma1 * x (the previous down projection's epilogue)
   for (int l = 0; l < c->n_layer; ++l) {
@@ -373,7 +382,7 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
     if (ln1_folded) {
       // d_qkv holds the bias
       e.bias = nullptr;
-      e.ln_x16 = x16;
+      e.ln_stats = ln_stats(l, 0);
       e.ln_cd = w->ln_fold + l * fold_layer;
       e.ln_eps = c->ln_eps;
     }
@@ -416,7 +425,7 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
       r.fold_g = L.ln2_g;
       r.fold_u = xa;
       r.fold_fmt = fmt_up;
-      r.fold_x16 = x16;
+      r.fold_stats = ln_stats(l, 1);
     }
     const bool fuse_dense = fuse_ln(p_dense);
     err = timed_linear(wdt, p_dense, o, L.w_dense, part, r, st, wbytes(h, hd), !fuse_dense);
@@ -444,7 +453,7 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
     }
     if (ln_fold) {
       g.bias = nullptr;   // d_up holds it
-      g.ln_x16 = x16;
+      g.ln_stats = ln_stats(l, 1);
       g.ln_cd = w->ln_fold + l * fold_layer + 2 * (size_t)(3 * hd);
       g.ln_eps = c->ln_eps;
     }
@@ -469,7 +478,7 @@ int run_forward(const bloom_config *c, const bloom_weights *w, bloom_kv_cache *k
       dn.fold_g = w->layers[l + 1].ln1_g;
       dn.fold_u = xa;
       dn.fold_fmt = fmt_qkv;
-      dn.fold_x16 = x16;
+      dn.fold_stats = ln_stats(l + 1, 0);
     }
     err = timed_linear(wdt, p_down, u, L.w_down, part, dn, st, wbytes(h, F), !fuse_down);
     if (err != hipSuccess) return hip_fail(err);

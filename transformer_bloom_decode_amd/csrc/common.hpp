@@ -278,26 +278,91 @@ struct EpiParams {
   float *am_val;           // [M][am_stride]
   int *am_idx;
   int am_stride;
-  // EPI_RESID with the next LayerNorm folded into its consumer: also stores
-  // fold_g[n] * x[n] (ActFmt fold_fmt) to fold_u and fp16(x[n]) to fold_x16
+  // EPI_RESID of one row with the next LayerNorm folded into its consumer: also stores
+  // fold_g[n] * x[n] (ActFmt fold_fmt) to fold_u, and the kernel adds the block's sums
+  // of x[n] and x[n]^2 to the accumulators fold_stats (LnStats below)
   const void *fold_g;      // [ld] the next LayerNorm's gamma (parameter type), nullable
-  void *fold_u;            // [M][ld]
+  void *fold_u;            // [ld]
   int fold_fmt;
-  uint16_t *fold_x16;      // [M][ld]
-  // consumer of a folded LayerNorm (one-row GEMV): the activations are gamma * x; the
-  // kernel forms mean and rstd of x from ln_x16 and applies rstd (acc - mean c) + d
-  const uint16_t *ln_x16;  // [K] fp16 residual row, nullable
+  unsigned long long *fold_stats;
+  // consumer of a folded LayerNorm (one-row GEMV): the activations are gamma * x; mean
+  // and rstd of x come from ln_stats, and the epilogue applies rstd (acc - mean c) + d
+  const unsigned long long *ln_stats;   // nullable
   const float *ln_cd;      // [2][N]: c then d
   float ln_eps;
 };
 
-// y = acc * scale[n] + bias[n], then the mode's action.  TP = parameter type.
+// Sums of a row's x and x^2 for a folded LayerNorm, added by the blocks of the GEMV that
+// writes the row and read by the one that consumes it.  A block's sum v goes in as two
+// integers, floor(v) and the fraction v - floor(v) in 2^-kStatFracBits units, each added
+// to its own 64-bit word with an atomic that returns nothing; integer additions commute,
+// so the totals -- and every result that depends on them -- do not depend on the order
+// in which the blocks arrive.  The atomics of one address are served one after another
+// (measured on MI355X: with 8 slots the 3584-block down projection took three times as
+// long), so kStatSlots slots spread them.  Layout per LayerNorm: [kStatSlots][2 sums]
+// [fraction, integer part], 2 KB.
+constexpr int kStatSlots = 64;
+constexpr int kStatWords = kStatSlots * 4;
+constexpr int kStatFracBits = 44;   // a slot's fractions stay below 2^63 for 2^19 blocks
+
+// adds v (clamped to |v| <= 2^62) to the accumulator pair a[0] (fraction) / a[1]
+__device__ __forceinline__ void stat_add(unsigned long long *a, double v) {
+  v = v < 0x1p62 ? (v > -0x1p62 ? v : -0x1p62) : 0x1p62;   // (NaN -> the upper bound)
+  const double ip = floor(v);
+  const long long frac = (long long)ldexp(v - ip, kStatFracBits);
+  atomicAdd(a, (unsigned long long)frac);
+  atomicAdd(a + 1, (unsigned long long)(long long)ip);
+}
+
+// the two totals (sum of x, sum of x^2) of one LayerNorm's accumulators, a copy of which
+// is in LDS: lane l takes slots l, l + 64, ..., then a wave reduction (all 64 lanes get
+// the totals)
+__device__ __forceinline__ void stat_totals_wave(const unsigned long long *lds, double &s1,
+                                                 double &s2) {
+  static_assert(kStatSlots % 64 == 0, "whole slots per lane");
+  const int lane = threadIdx.x & 63;
+  long long v[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int j = 0; j < kStatSlots / 64; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] += (long long)lds[4 * (lane + 64 * j) + q];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] += __shfl_xor(v[q], o, 64);
+  s1 = (double)v[1] + ldexp((double)v[0], -kStatFracBits);
+  s2 = (double)v[3] + ldexp((double)v[2], -kStatFracBits);
+}
+
+// The operands an epilogue loads for output (m, n): bias[n], scale[n], xscale[m], the
+// residual x[m][n] (EPI_RESID) and fold_g[n] (EPI_RESID with a folded LayerNorm after
+// it).  A kernel that loads them before its dot product keeps those loads off the end
+// of the wave, where they would otherwise be waited for one after another.
+struct EpiPre {
+  float bias, scale, xscale, x, g;
+};
+
 template <typename TP>
-__device__ __forceinline__ void epilogue(const EpiParams &e, int m, int n, float acc) {
+__device__ __forceinline__ EpiPre epi_prefetch(const EpiParams &e, int m, int n) {
+  EpiPre p;
+  p.xscale = e.xscale ? e.xscale[m] : 1.f;
+  p.scale = e.scale ? h2f(e.scale[n]) : 1.f;
+  p.bias = e.bias ? to_f<TP>(((const TP *)e.bias)[n]) : 0.f;
+  const bool resid = e.mode == EPI_RESID;
+  p.x = resid ? ((const float *)e.out)[(size_t)m * e.ld + n] : 0.f;
+  p.g = resid && e.fold_g ? to_f<TP>(((const TP *)e.fold_g)[n]) : 0.f;
+  return p;
+}
+
+// y = acc * scale[n] + bias[n], then the mode's action, with the operands of
+// epi_prefetch.  Returns the updated x[m][n] for EPI_RESID, else y.
+template <typename TP>
+__device__ __forceinline__ float epilogue_pre(const EpiParams &e, int m, int n, float acc,
+                                              const EpiPre &p) {
   float y = acc;
-  if (e.xscale) y *= e.xscale[m];
-  if (e.scale) y *= h2f(e.scale[n]);
-  if (e.bias) y += to_f<TP>(((const TP *)e.bias)[n]);
+  if (e.xscale) y *= p.xscale;
+  if (e.scale) y *= p.scale;
+  if (e.bias) y += p.bias;
   switch (e.mode) {
     case EPI_QKV: {
       const int d = e.d, H = e.H;
@@ -323,15 +388,10 @@ __device__ __forceinline__ void epilogue(const EpiParams &e, int m, int n, float
       break;
     }
     case EPI_RESID: {
-      float *x = (float *)e.out + (size_t)m * e.ld + n;
-      const float xn = *x + y;
-      *x = xn;
-      if (e.fold_g) {
-        const size_t i = (size_t)m * e.ld + n;
-        act_store(e.fold_u, e.fold_fmt, i, 0, to_f<TP>(((const TP *)e.fold_g)[n]) * xn);
-        e.fold_x16[i] = f2h_bits(xn);
-      }
-      break;
+      const float xn = p.x + y;
+      ((float *)e.out)[(size_t)m * e.ld + n] = xn;
+      if (e.fold_g) act_store(e.fold_u, e.fold_fmt, (size_t)m * e.ld + n, 0, p.g * xn);
+      return xn;
     }
     case EPI_GELU:
       act_store(e.out, e.out_fmt, (size_t)m * e.ld + n, e.plane, gelu_tanh(y));
@@ -342,6 +402,13 @@ __device__ __forceinline__ void epilogue(const EpiParams &e, int m, int n, float
     default:
       break;
   }
+  return y;
+}
+
+// the epilogue with its operands loaded where it runs.  TP = parameter type.
+template <typename TP>
+__device__ __forceinline__ float epilogue(const EpiParams &e, int m, int n, float acc) {
+  return epilogue_pre<TP>(e, m, n, acc, epi_prefetch<TP>(e, m, n));
 }
 
 }  // namespace bl

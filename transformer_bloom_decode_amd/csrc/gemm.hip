@@ -819,6 +819,8 @@ hipError_t launch_linear(int wdtype, const LinearPlan &p, const void *X, const v
                          float *partial, const EpiParams &ep, hipStream_t st,
                          bool splitk_epilogue) {
   if (p.M <= 0) return hipSuccess;
+  // a folded LayerNorm's statistics exist on the one-row vector-ALU GEMV only
+  if ((ep.ln_stats || ep.fold_stats) && p.kind != LIN_VALU) return hipErrorInvalidValue;
   if (p.kind == LIN_F32) {
     BL_LAUNCH(k_gemm_f32, dim3(p.grid_x, p.M), dim3(256), 0, st, (const float *)X,
                        (const float *)W, p.M, p.N, p.K, ep);

@@ -77,6 +77,37 @@ template <> struct XOps<f16_t> {
   }
 };
 
+// Folded LayerNorm ("DeepSpeed Inference ...", Section III.D fuses each LayerNorm with
+// the GeMM that follows it), one activation row.  The consumer GEMV reads g * x and
+// finishes y_n = rstd (sum_k W[n][k] (g x)_k - mean c_n) + d_n, with c_n = sum_k W[n][k]
+// g_k and d_n = sum_k W[n][k] b_k + bias_n precomputed (ep.ln_cd) and mean, rstd of x
+// from the sums that the blocks of the residual GEMV before it accumulated: every wave
+// copies the accumulators (2 KB) straight into its own LDS region before it requests
+// the weights, and forms the totals from there after its dot products (no barrier).
+
+// The residual GEMV's share: each block adds the float64 sums of its new x[n] and
+// x[n]^2 (xn: this lane's value, 0 for lanes without an output) to slot
+// blockIdx % kStatSlots.
+__device__ __forceinline__ void fold_stats_add(const EpiParams &ep, float xn) {
+  __shared__ double red[2][4];
+  double s1 = xn, s2 = (double)xn * xn;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    s1 += __shfl_xor(s1, o, 64);
+    s2 += __shfl_xor(s2, o, 64);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    red[0][threadIdx.x >> 6] = s1;
+    red[1][threadIdx.x >> 6] = s2;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long *a = ep.fold_stats + 4 * (blockIdx.x % kStatSlots);
+    stat_add(a, (red[0][0] + red[0][1]) + (red[0][2] + red[0][3]));
+    stat_add(a + 2, (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]));
+  }
+}
+
 // DB: double-buffered (the next U pieces per row are issued before the current ones
 // are used) or single-buffered (U pieces per row issued at once, then used; with U >=
 // the row's pieces, a wave issues its whole row in one go, which keeps the most bytes
@@ -101,6 +132,38 @@ __global__ __launch_bounds__(256) void k_gemv_valu(const TX *__restrict__ X,
   const TX *xr[MR];
 #pragma unroll
   for (int m = 0; m < MR; ++m) xr[m] = X + (size_t)min(m, M - 1) * K;
+
+  // one copy of a folded LayerNorm's accumulators per wave
+  __shared__ __attribute__((aligned(16))) unsigned long long lst[MR == 1 ? 4 * kStatWords : 1];
+  unsigned long long *wst = lst + (MR == 1 ? kStatWords * __builtin_amdgcn_readfirstlane(wid) : 0);
+  // lane l < R*MR finishes output (row0 + l / MR, activation row l % MR).  One row of
+  // bf16 / fp16 activations against bf16 weights (the batch-1 decode step): the lane's
+  // epilogue operands are requested now, with the weights (measured on MI355X: the
+  // residual projections waited for them at the end of every wave); the other variants
+  // keep their registers for the weights and load them in the epilogue.
+  constexpr bool kPre = MR == 1 && sizeof(TW) == 2 && sizeof(TX) == 2;
+  const int on = row0 + lane / MR, om = lane % MR;
+  const bool has_out = lane < R * MR && on < N && om < M && ep.mode != EPI_ARGMAX;
+  EpiPre pre{};
+  if constexpr (kPre) {
+    if (has_out) pre = epi_prefetch<TP>(ep, om, on);
+  }
+  float fold_c = 0.f, fold_d = 0.f;   // c_n and d_n of the lane's output row
+  if constexpr (MR == 1) {
+    if (ep.ln_stats) {
+      if (lane < R && row0 + lane < N) {
+        fold_c = ep.ln_cd[row0 + lane];
+        fold_d = ep.ln_cd[N + row0 + lane];
+      }
+      static_assert(kStatWords * 8 % 1024 == 0, "whole 1 KB copies");
+#pragma unroll
+      for (int j = 0; j < kStatWords * 8 / 1024; ++j)
+        __builtin_amdgcn_global_load_lds(
+            (const void *)((const unsigned char *)ep.ln_stats + j * 1024 + lane * 16),
+            (__attribute__((address_space(3))) void *)((unsigned char *)wst + j * 1024), 16, 0,
+            0);
+    }
+  }
 
   float acc[R][MR];
 #pragma unroll
@@ -176,6 +239,20 @@ __global__ __launch_bounds__(256) void k_gemv_valu(const TX *__restrict__ X,
 #pragma unroll
     for (int m = 0; m < MR; ++m) acc[i][m] = wave_sum(acc[i][m]);
 
+  float ln_mean = 0.f, ln_rstd = 0.f;
+  if constexpr (MR == 1) {
+    if (ep.ln_stats) {
+      // vmcnt(0): the wave's copies have landed in its LDS region
+      __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+      double s1, s2;
+      stat_totals_wave(wst, s1, s2);
+      const double md = s1 / K;
+      const double var = s2 / K - md * md;
+      ln_mean = (float)md;
+      ln_rstd = 1.0f / sqrtf((float)(var > 0.0 ? var : 0.0) + ep.ln_eps);
+    }
+  }
+
   if (ep.mode == EPI_ARGMAX) {
     // best of this wave's R rows per activation row, then of the block's 4 waves
     if (lane == 0) {
@@ -201,7 +278,7 @@ __global__ __launch_bounds__(256) void k_gemv_valu(const TX *__restrict__ X,
     }
     return;
   }
-  // lane l < R*MR finishes output (row0 + l / MR, activation row l % MR)
+  float xn = 0.f;   // the updated residual value of the lane's output (EPI_RESID)
   if (lane < R * MR) {
     float v = 0.f;
 #pragma unroll
@@ -209,8 +286,16 @@ __global__ __launch_bounds__(256) void k_gemv_valu(const TX *__restrict__ X,
 #pragma unroll
       for (int m = 0; m < MR; ++m)
         if (lane == i * MR + m) v = acc[i][m];
-    const int n = row0 + lane / MR, m = lane % MR;
-    if (n < N && m < M) epilogue<TP>(ep, m, n, v);
+    if (has_out) {
+      if constexpr (MR == 1) {
+        if (ep.ln_stats) v = ln_rstd * (v - ln_mean * fold_c) + fold_d;
+      }
+      if constexpr (kPre) xn = epilogue_pre<TP>(ep, om, on, v, pre);
+      else xn = epilogue<TP>(ep, om, on, v);
+    }
+  }
+  if constexpr (MR == 1) {
+    if (ep.fold_stats) fold_stats_add(ep, xn);
   }
 }
 
@@ -240,12 +325,6 @@ __global__ __launch_bounds__(256) void k_gemv_valu(const TX *__restrict__ X,
 // kernel was slower than LayerNorm + GEMV (QKV 40.2 against 28.3 + 4.6 us), so long rows
 // keep the separate LayerNorm.
 constexpr int kGemvLnMaxK = 4096;
-
-// s_waitcnt vmcnt(V) alone (expcnt and lgkmcnt unconstrained)
-template <int V> __device__ __forceinline__ void wait_vmcnt_lnf() {
-  static_assert(V >= 0 && V < 64, "vmcnt");
-  __builtin_amdgcn_s_waitcnt((V & 15) | ((V >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 // s_waitcnt lgkmcnt(0) alone (vmcnt and expcnt unconstrained), then s_barrier
 __device__ __forceinline__ void lds_barrier() {
@@ -401,115 +480,6 @@ hipError_t launch_gemv_ln(int wdtype, int x_fmt, int N, int K, const float *x, c
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------
-// one-row decode GEMV with the preceding LayerNorm folded into it
-// ---------------------------------------------------------------------------
-// The LayerNorm before QKV / MLP-up ("DeepSpeed Inference ...", Section III.D fuses it
-// with the GeMM that follows) as y_n = rstd (sum_k W[n][k] (g x)_k - mean c_n) + d_n with
-// c_n = sum_k W[n][k] g_k and d_n = sum_k W[n][k] b_k + bias_n precomputed (ep.ln_cd):
-// the activations X are g * x, stored by the residual epilogue of the previous
-// projection together with an fp16 copy of x (ep.ln_x16).  One weight row per wave, 4
-// per block; every block forms mean and rstd itself.  In issue order (a wave's vector
-// memory loads complete in that order):
-//   1. the fp16 row x16 straight into LDS, NPW 1 KB copies per wave (no registers);
-//   2. the wave's whole weight row and the activation row g * x (U 16-byte loads each,
-//      every one unconditional, at the wave's piece start plus the lane's offset);
-//   3. once the copies of step 1 have landed (vmcnt: the 2U loads of step 2 may still
-//      be outstanding) and a barrier that waits for LDS only, mean and rstd of x16 from
-//      LDS (two passes, float32, a fixed order), while the weights are in flight;
-//   4. the dot product (each piece as soon as its loads have landed), then
-//      rstd (acc - mean c_n) + d_n into the linear's epilogue.
-// Rows of a multiple of 512 elements up to kLnFoldMaxK.
-constexpr int kLnFoldMaxK = 14336;   // 28 pieces of 512
-template <typename TW, typename TX, int U>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_gemv_lnf(
-    const TX *__restrict__ X, const TW *__restrict__ W, int N, int K, EpiParams ep) {
-  using VO = VOps<TW>;
-  using XO = XOps<TX>;
-  constexpr int E = VO::kPerLane;
-  constexpr int step = 64 * E;
-  static_assert(E == XO::kPer16, "one 16-byte activation piece per weight piece");
-  constexpr int NPW = (kLnFoldMaxK / 512 + 3) / 4;   // copies per wave (1 KB each)
-  static_assert(NPW + 2 * U < 64, "vmcnt");
-  __shared__ __attribute__((aligned(1024))) uint16_t lnx[kLnFoldMaxK];
-  __shared__ float red[2][4];
-  const int lane = threadIdx.x & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int row = blockIdx.x * 4 + wid;
-  const TW *wr = W + (size_t)min(row, N - 1) * K;
-
-  // 1. x16 -> LDS: piece pc (512 elements) by wave pc % 4; pieces past the row repeat
-  // its last one (the same bytes to the same place), so every wave issues exactly NPW
-  // copies
-  const int pieces = K / 512;
-#pragma unroll
-  for (int j = 0; j < NPW; ++j) {
-    const int pc = min(wid + 4 * j, pieces - 1);
-    __builtin_amdgcn_global_load_lds((const void *)(ep.ln_x16 + pc * 512 + lane * 8),
-                                     (__attribute__((address_space(3))) void *)(
-                                         (unsigned char *)lnx + pc * 1024),
-                                     16, 0, 0);
-  }
-  // 2. the weight row and the activation row (K is a multiple of the 512-element wave
-  // piece; pieces past the row repeat its last one)
-  u32x4 cw[U], cx[U];
-  const int kmax = K - step;
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int k0 = min(u * step, kmax);
-    cw[u] = __builtin_nontemporal_load((const u32x4 *)(wr + k0 + lane * E));
-    cx[u] = *(const u32x4 *)(X + k0 + lane * E);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  // 3. statistics of x while the loads above are in flight
-  wait_vmcnt_lnf<2 * U>();
-  lds_barrier();
-  const int n8 = K / 8;
-  float s = 0.f;
-#pragma unroll
-  for (int j = 0; j < kLnFoldMaxK / 8 / 256; ++j) {
-    const int p = threadIdx.x + 256 * j;
-    if (p < n8) {
-      const u32x4 t = *(const u32x4 *)(lnx + 8 * p);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) s += f16lo(t[q]) + f16hi(t[q]);
-    }
-    // one LDS read at a time: the weight and activation rows hold the registers
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  const float mean = gemv_block_sum(s, red[0]) / (float)K;
-  float ss = 0.f;
-#pragma unroll
-  for (int j = 0; j < kLnFoldMaxK / 8 / 256; ++j) {
-    const int p = threadIdx.x + 256 * j;
-    if (p < n8) {
-      const u32x4 t = *(const u32x4 *)(lnx + 8 * p);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float a = f16lo(t[q]) - mean, b = f16hi(t[q]) - mean;
-        ss += a * a + b * b;
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  const float rstd = 1.0f / sqrtf(gemv_block_sum(ss, red[1]) / (float)K + ep.ln_eps);
-  // 4. the dot product (the repeated pieces past the row are skipped)
-  float acc = 0.f;
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    if (u * step < K) {
-      float wf[E], xf[E];
-      VO::widen(cw[u], wf);
-      XO::widen(cx[u], xf);
-#pragma unroll
-      for (int e = 0; e < E; ++e) acc = fmaf(wf[e], xf[e], acc);
-    }
-  }
-  acc = wave_sum(acc);
-  if (lane == 0 && row < N)
-    epilogue<bf16_t>(ep, 0, row, rstd * (acc - mean * ep.ln_cd[row]) + ep.ln_cd[N + row]);
-}
-
 LinearPlan plan_valu(int wdtype, int M, int N, int K) {
   LinearPlan p{};
   p.M = M; p.N = N; p.K = K;
@@ -543,6 +513,7 @@ LinearPlan plan_valu(int wdtype, int M, int N, int K) {
   return p;
 }
 
+
 template <typename TW, typename TP, typename TX>
 static void launch_valu_t(const LinearPlan &p, const void *X, const void *W, const EpiParams &ep,
                           hipStream_t st) {
@@ -551,15 +522,6 @@ static void launch_valu_t(const LinearPlan &p, const void *X, const void *W, con
   const TW *w = (const TW *)W;
   if constexpr (std::is_same<TW, bf16_t>::value) {
     if (p.vr == 1 && p.mt == 1 && !p.vdb) {
-      if constexpr (sizeof(TX) == 2) {
-        if (ep.ln_x16) {   // LayerNorm folded in (checked by launch_valu)
-          if (p.vu == 16)
-            BL_LAUNCH((k_gemv_lnf<TW, TX, 16>), grid, block, 0, st, x, w, p.N, p.K, ep);
-          else
-            BL_LAUNCH((k_gemv_lnf<TW, TX, 28>), grid, block, 0, st, x, w, p.N, p.K, ep);
-          return;
-        }
-      }
       if (p.vu == 16)
         BL_LAUNCH((k_gemv_valu<TW, TP, TX, 1, 1, 16, false>), grid, block, 0, st, x, w, p.M, p.N, p.K, ep);
       else
@@ -589,19 +551,24 @@ static void launch_valu_w(const LinearPlan &p, const void *X, const void *W, con
   else launch_valu_t<TW, bf16_t, bf16_t>(p, X, W, ep, st);
 }
 
-// The folded-LayerNorm GEMV exists for one row of bf16 / fp16 activations against bf16
-// weights on the whole-row plans, for rows of a multiple of 512 elements up to
-// kLnFoldMaxK.
+// A folded LayerNorm runs on one-row vector-ALU GEMVs against bf16 weights: its
+// consumer (ln_stats and ln_cd set; not the LM head) and the residual projection before
+// it (fold_g, fold_u and fold_stats set, EPI_RESID).
 bool ln_fold_supported(int wdtype, const LinearPlan &p, const EpiParams &ep) {
-  return wdtype == WT_BF16 && p.kind == LIN_VALU && p.M == 1 && p.mt == 1 && p.vr == 1 &&
-         !p.vdb && (p.x_fmt == AF_F16 || p.x_fmt == AF_BF16) && p.K <= kLnFoldMaxK &&
-         p.K % 512 == 0 && ep.ln_cd && ep.mode != EPI_ARGMAX;
+  if (wdtype != WT_BF16 || p.kind != LIN_VALU || p.M != 1 || p.mt != 1 || p.splits != 1)
+    return false;
+  if (ep.ln_stats && (!ep.ln_cd || ep.mode == EPI_ARGMAX)) return false;
+  if ((ep.fold_g || ep.fold_stats) && (ep.mode != EPI_RESID || !ep.fold_g || !ep.fold_u ||
+                                       !ep.fold_stats))
+    return false;
+  return true;
 }
 
 hipError_t launch_valu(int wdtype, const LinearPlan &p, const void *X, const void *W,
                        const EpiParams &ep, hipStream_t st) {
   if (p.x_fmt == AF_I8 && (wdtype != WT_INT8 || !ep.xscale)) return hipErrorInvalidValue;
-  if (ep.ln_x16 && !ln_fold_supported(wdtype, p, ep)) return hipErrorInvalidValue;
+  if ((ep.ln_stats || ep.fold_g || ep.fold_stats) && !ln_fold_supported(wdtype, p, ep))
+    return hipErrorInvalidValue;
   if (wdtype == WT_BF16) launch_valu_w<bf16_t>(p, X, W, ep, st);
   else launch_valu_w<int8_t>(p, X, W, ep, st);
   return hipGetLastError();

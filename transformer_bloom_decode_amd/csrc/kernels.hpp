@@ -69,7 +69,8 @@ struct LinearPlan {
 LinearPlan plan_valu(int wdtype, int M, int N, int K);
 hipError_t launch_valu(int wdtype, const LinearPlan &p, const void *X, const void *W,
                        const EpiParams &ep, hipStream_t st);
-// The one-row GEMV with a folded LayerNorm (ep.ln_x16, ep.ln_cd): supported for this plan?
+// The one-row GEMVs of a folded LayerNorm (consumer: ep.ln_stats, ep.ln_cd; residual
+// producer: ep.fold_g, fold_u, fold_stats): supported for this plan?
 bool ln_fold_supported(int wdtype, const LinearPlan &p, const EpiParams &ep);
 // LayerNorm fold vectors of one linear: c[n] = sum_k W[n][k] g[k], d[n] = sum_k W[n][k]
 // b[k] + bias[n] (bf16 W [N][K], g, b [K], bias [N] nullable).
@@ -105,9 +106,11 @@ hipError_t launch_alibi_softmax(const void *scores, bool in_bf16, const int *val
                                 void *probs, bool out_bf16, int B, int H, int Q, int K,
                                 int n_total, int head_off, hipStream_t stream);
 
+// zero (nullable): nzero 64-bit words that block 0 also clears (the folded LayerNorms'
+// accumulators of the pass)
 hipError_t launch_embed(bool f32, const int *tokens, const void *embed, const void *g,
                         const void *b, float *x, int rows, int h, int vocab, int do_ln, float eps,
-                        hipStream_t stream);
+                        unsigned long long *zero, int nzero, hipStream_t stream);
 // Split-K partials of a bf16 linear [splits][rows][h] -> x += sum * scale + bias, then
 // out = LN(x) (bf16); only for splitk_resid_ln_supported(h, splits).
 bool splitk_resid_ln_supported(int h, int splits);

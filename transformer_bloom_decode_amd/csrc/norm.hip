@@ -81,16 +81,34 @@ __device__ __forceinline__ void ln_store_row(const float4 (&y)[kLnVec], void *ou
   }
 }
 
-// x[row] = E[token[row]] as float32, then optionally LayerNorm'd.
+// Block z of the clearing blocks zeroes words [z kZeroBlockWords, (z + 1) kZeroBlockWords)
+// of zero[nzero] with 16-byte stores (nzero even, zero 16-byte aligned).
+constexpr int kZeroBlockWords = 8192;
+__device__ __forceinline__ void zero_words(unsigned long long *zero, int nzero, int z,
+                                           int nthreads) {
+  const int end = min(nzero, (z + 1) * kZeroBlockWords);
+  for (int i = z * kZeroBlockWords + 2 * (int)threadIdx.x; i < end; i += 2 * nthreads)
+    *(uint4 *)(zero + i) = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// x[row] = E[token[row]] as float32, then optionally LayerNorm'd.  With nzero > 0 the
+// grid has ceil(nzero / kZeroBlockWords) more blocks, which only clear zero[].
 template <typename TP>
 __global__ __launch_bounds__(kLnThreads) void k_embed(const int *__restrict__ tokens,
                                                       const TP *__restrict__ embed,
                                                       const TP *__restrict__ g,
                                                       const TP *__restrict__ b,
                                                       float *__restrict__ x, int h, int vocab,
-                                                      int do_ln, float eps) {
+                                                      int do_ln, float eps,
+                                                      int rows,
+                                                      unsigned long long *__restrict__ zero,
+                                                      int nzero) {
   __shared__ float sh[kLnWaves];
   const int row = blockIdx.x;
+  if (row >= rows) {   // the blocks past the rows clear the folded-LayerNorm accumulators
+    zero_words(zero, nzero, row - rows, kLnThreads);
+    return;
+  }
   int tok = tokens[row];
   tok = tok < 0 ? 0 : (tok >= vocab ? vocab - 1 : tok);  // ids outside the vocabulary clamp
   const TP *e = embed + (size_t)tok * h;
@@ -290,9 +308,16 @@ __global__ __launch_bounds__(256) void k_embed_any(const int *__restrict__ token
                                                    const TP *__restrict__ g,
                                                    const TP *__restrict__ b,
                                                    float *__restrict__ x, int h, int vocab,
-                                                   int do_ln, float eps) {
+                                                   int do_ln, float eps,
+                                                   int rows,
+                                                   unsigned long long *__restrict__ zero,
+                                                   int nzero) {
   __shared__ float sh[4];
   const int row = blockIdx.x;
+  if (row >= rows) {   // the blocks past the rows clear the folded-LayerNorm accumulators
+    zero_words(zero, nzero, row - rows, 256);
+    return;
+  }
   int tok = tokens[row];
   tok = tok < 0 ? 0 : (tok >= vocab ? vocab - 1 : tok);
   const TP *e = embed + (size_t)tok * h;
@@ -319,27 +344,30 @@ static bool fits_regs(int h) { return h % 4 == 0 && h <= kLnThreads * 4 * kLnVec
 
 hipError_t launch_embed(bool f32, const int *tokens, const void *embed, const void *g,
                         const void *b, float *x, int rows, int h, int vocab, int do_ln, float eps,
-                        hipStream_t stream) {
+                        unsigned long long *zero, int nzero, hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
+  if (nzero < 0 || nzero % 2 || ((uintptr_t)zero & 15)) return hipErrorInvalidValue;
   const bool reg = fits_regs(h);
+  const unsigned grid =
+      (unsigned)rows + (unsigned)((nzero + kZeroBlockWords - 1) / kZeroBlockWords);
   if (f32) {
     if (reg)
-      hipLaunchKernelGGL(k_embed<float>, dim3(rows), dim3(kLnThreads), 0, stream, tokens,
+      hipLaunchKernelGGL(k_embed<float>, dim3(grid), dim3(kLnThreads), 0, stream, tokens,
                          (const float *)embed, (const float *)g, (const float *)b, x, h, vocab,
-                         do_ln, eps);
+                         do_ln, eps, rows, zero, nzero);
     else
-      hipLaunchKernelGGL(k_embed_any<float>, dim3(rows), dim3(256), 0, stream, tokens,
+      hipLaunchKernelGGL(k_embed_any<float>, dim3(grid), dim3(256), 0, stream, tokens,
                          (const float *)embed, (const float *)g, (const float *)b, x, h, vocab,
-                         do_ln, eps);
+                         do_ln, eps, rows, zero, nzero);
   } else {
     if (reg)
-      hipLaunchKernelGGL(k_embed<bf16_t>, dim3(rows), dim3(kLnThreads), 0, stream, tokens,
+      hipLaunchKernelGGL(k_embed<bf16_t>, dim3(grid), dim3(kLnThreads), 0, stream, tokens,
                          (const bf16_t *)embed, (const bf16_t *)g, (const bf16_t *)b, x, h,
-                         vocab, do_ln, eps);
+                         vocab, do_ln, eps, rows, zero, nzero);
     else
-      hipLaunchKernelGGL(k_embed_any<bf16_t>, dim3(rows), dim3(256), 0, stream, tokens,
+      hipLaunchKernelGGL(k_embed_any<bf16_t>, dim3(grid), dim3(256), 0, stream, tokens,
                          (const bf16_t *)embed, (const bf16_t *)g, (const bf16_t *)b, x, h,
-                         vocab, do_ln, eps);
+                         vocab, do_ln, eps, rows, zero, nzero);
   }
   return hipGetLastError();
 }
