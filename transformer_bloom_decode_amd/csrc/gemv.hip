@@ -82,7 +82,7 @@ template <> struct XOps<f16_t> {
 // finishes y_n = rstd (sum_k W[n][k] (g x)_k - mean c_n) + d_n, with c_n = sum_k W[n][k]
 // g_k and d_n = sum_k W[n][k] b_k + bias_n precomputed (ep.ln_cd) and mean, rstd of x
 // from the sums that the blocks of the residual GEMV before it accumulated: every wave
-// copies the accumulators (2 KB) straight into its own LDS region before it requests
+// copies the accumulators (1 KB) straight into its own LDS region before it requests
 // the weights, and forms the totals from there after its dot products (no barrier).
 
 // The residual GEMV's share: each block adds the float64 sums of its new x[n] and
@@ -102,9 +102,9 @@ __device__ __forceinline__ void fold_stats_add(const EpiParams &ep, float xn) {
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    unsigned long long *a = ep.fold_stats + 4 * (blockIdx.x % kStatSlots);
-    stat_add(a, (red[0][0] + red[0][1]) + (red[0][2] + red[0][3]));
-    stat_add(a + 2, (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]));
+    unsigned long long *a = ep.fold_stats + 2 * (blockIdx.x % kStatSlots);
+    stat_add(a, (red[0][0] + red[0][1]) + (red[0][2] + red[0][3]), kStatFrac1);
+    stat_add(a + 1, (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]), kStatFrac2);
   }
 }
 
