@@ -350,15 +350,16 @@ __device__ __forceinline__ EpiPre epi_prefetch(const EpiParams &e, int m, int n)
   return p;
 }
 
-// y = acc * scale[n] + bias[n], then the mode's action, with the operands of
-// epi_prefetch.  Returns the updated x[m][n] for EPI_RESID, else y.
-template <typename TP>
-__device__ __forceinline__ float epilogue_pre(const EpiParams &e, int m, int n, float acc,
-                                              const EpiPre &p) {
+// y = acc * scale[n] + bias[n], then the mode's action.  TP = parameter type.  PRE: the
+// operands come from epi_prefetch (p); otherwise they are loaded here, where they are
+// used.  Returns the updated x[m][n] for EPI_RESID, else y.
+template <typename TP, bool PRE>
+__device__ __forceinline__ float epilogue_impl(const EpiParams &e, int m, int n, float acc,
+                                               const EpiPre &p) {
   float y = acc;
-  if (e.xscale) y *= p.xscale;
-  if (e.scale) y *= p.scale;
-  if (e.bias) y += p.bias;
+  if (e.xscale) y *= PRE ? p.xscale : e.xscale[m];
+  if (e.scale) y *= PRE ? p.scale : h2f(e.scale[n]);
+  if (e.bias) y += PRE ? p.bias : to_f<TP>(((const TP *)e.bias)[n]);
   switch (e.mode) {
     case EPI_QKV: {
       const int d = e.d, H = e.H;
@@ -384,9 +385,12 @@ __device__ __forceinline__ float epilogue_pre(const EpiParams &e, int m, int n, 
       break;
     }
     case EPI_RESID: {
-      const float xn = p.x + y;
-      ((float *)e.out)[(size_t)m * e.ld + n] = xn;
-      if (e.fold_g) act_store(e.fold_u, e.fold_fmt, (size_t)m * e.ld + n, 0, p.g * xn);
+      float *x = (float *)e.out + (size_t)m * e.ld + n;
+      const float xn = (PRE ? p.x : *x) + y;
+      *x = xn;
+      if (e.fold_g)
+        act_store(e.fold_u, e.fold_fmt, (size_t)m * e.ld + n, 0,
+                  (PRE ? p.g : to_f<TP>(((const TP *)e.fold_g)[n])) * xn);
       return xn;
     }
     case EPI_GELU:
@@ -401,10 +405,16 @@ __device__ __forceinline__ float epilogue_pre(const EpiParams &e, int m, int n, 
   return y;
 }
 
+template <typename TP>
+__device__ __forceinline__ float epilogue_pre(const EpiParams &e, int m, int n, float acc,
+                                              const EpiPre &p) {
+  return epilogue_impl<TP, true>(e, m, n, acc, p);
+}
+
 // the epilogue with its operands loaded where it runs.  TP = parameter type.
 template <typename TP>
 __device__ __forceinline__ float epilogue(const EpiParams &e, int m, int n, float acc) {
-  return epilogue_pre<TP>(e, m, n, acc, epi_prefetch<TP>(e, m, n));
+  return epilogue_impl<TP, false>(e, m, n, acc, EpiPre{});
 }
 
 }  // namespace bl

@@ -133,9 +133,11 @@ __global__ __launch_bounds__(256) void k_gemv_valu(const TX *__restrict__ X,
 #pragma unroll
   for (int m = 0; m < MR; ++m) xr[m] = X + (size_t)min(m, M - 1) * K;
 
-  // one copy of a folded LayerNorm's accumulators per wave
-  __shared__ __attribute__((aligned(16))) unsigned long long lst[MR == 1 ? 4 * kStatWords : 1];
-  unsigned long long *wst = lst + (MR == 1 ? kStatWords * __builtin_amdgcn_readfirstlane(wid) : 0);
+  // A folded LayerNorm (one row against bf16 weights; ln_fold_supported): one copy of
+  // its accumulators per wave
+  constexpr bool kFold = MR == 1 && sizeof(TW) == 2;
+  __shared__ __attribute__((aligned(16))) unsigned long long lst[kFold ? 4 * kStatWords : 1];
+  unsigned long long *wst = lst + (kFold ? kStatWords * __builtin_amdgcn_readfirstlane(wid) : 0);
   // lane l < R*MR finishes output (row0 + l / MR, activation row l % MR).  One row of
   // bf16 / fp16 activations against bf16 weights (the batch-1 decode step): the lane's
   // epilogue operands are requested now, with the weights (measured on MI355X: the
@@ -149,7 +151,7 @@ __global__ __launch_bounds__(256) void k_gemv_valu(const TX *__restrict__ X,
     if (has_out) pre = epi_prefetch<TP>(ep, om, on);
   }
   float fold_c = 0.f, fold_d = 0.f;   // c_n and d_n of the lane's output row
-  if constexpr (MR == 1) {
+  if constexpr (kFold) {
     if (ep.ln_stats) {
       if (lane < R && row0 + lane < N) {
         fold_c = ep.ln_cd[row0 + lane];
@@ -240,7 +242,7 @@ __global__ __launch_bounds__(256) void k_gemv_valu(const TX *__restrict__ X,
     for (int m = 0; m < MR; ++m) acc[i][m] = wave_sum(acc[i][m]);
 
   float ln_mean = 0.f, ln_rstd = 0.f;
-  if constexpr (MR == 1) {
+  if constexpr (kFold) {
     if (ep.ln_stats) {
       // vmcnt(0): the wave's copies have landed in its LDS region
       __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
@@ -287,14 +289,14 @@ __global__ __launch_bounds__(256) void k_gemv_valu(const TX *__restrict__ X,
       for (int m = 0; m < MR; ++m)
         if (lane == i * MR + m) v = acc[i][m];
     if (has_out) {
-      if constexpr (MR == 1) {
+      if constexpr (kFold) {
         if (ep.ln_stats) v = ln_rstd * (v - ln_mean * fold_c) + fold_d;
       }
       if constexpr (kPre) xn = epilogue_pre<TP>(ep, om, on, v, pre);
       else xn = epilogue<TP>(ep, om, on, v);
     }
   }
-  if constexpr (MR == 1) {
+  if constexpr (kFold) {
     if (ep.fold_stats) fold_stats_add(ep, xn);
   }
 }
