@@ -138,6 +138,9 @@ hipError_t launch_layernorm(bool f32, const float *x, int in_step, int in_off, c
 // the keys over attention_splits(...) blocks per (row, head); part then holds
 // rows * H * splits * (d + 2) floats (at most kAttnSplitBlocks * (d + 2)).
 constexpr int kAttnSplitBlocks = 1024;
+// Decode steps with at least this many (row, head) pairs and no key split run one wave
+// per pair (k_attention_wave) instead of one block.
+constexpr int kAttnWavePairs = 1024;
 constexpr int kAttnMaxSplits = 16;
 int attention_splits(int rows, int H, int max_len, int rows_per_seq);
 hipError_t launch_attention(int kv_fmt, const float *q, const void *kc, const void *vc,
