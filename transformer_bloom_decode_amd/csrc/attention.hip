@@ -370,14 +370,34 @@ __global__ __launch_bounds__(256) void k_attention_prompt(
 // resident per CU as with one 256-thread block per pair.  Measured on MI355X with
 // 14336 pairs of 17-115 slots (int8 cache, batch 128): the block kernel spent its time
 // in each block's chain of dependent steps rather than in bandwidth.
-template <typename TA>
+// A lane's piece of a key / value row in k_attention_wave: EPL elements, and the keys
+// per lane group per batch.  int8 codes: 16 per lane (one 16-byte load) for head dims
+// of 16 and more.
+struct KVRaw16I8 {
+  u32x4 a;
+  __device__ __forceinline__ void load(const int8_t *p) { a = *(const u32x4 *)p; }
+  __device__ __forceinline__ float get(int t) const {
+    return (float)(int8_t)(a[t >> 2] >> (8 * (t & 3)));
+  }
+};
+template <typename TA, int EPL> struct WavePiece {
+  using T = KVRaw<TA>;
+  static constexpr int kKB = KeysPerBatch<TA>::value;
+};
+template <> struct WavePiece<int8_t, 16> {
+  using T = KVRaw16I8;
+  static constexpr int kKB = 8;
+};
+
+template <typename TA, int EPL>
 __global__ __launch_bounds__(256) void k_attention_wave(
     const float *__restrict__ q, const TA *__restrict__ kc, const TA *__restrict__ vc,
     const float *__restrict__ ksc, const float *__restrict__ vsc,
     const int *__restrict__ valid_len, void *__restrict__ o, int o_fmt, size_t o_plane, int H,
     int d, int max_len, int n_total, int head_off, int pairs, int pos_base,
     const int *__restrict__ pos_dev, int prompt_len) {
-  constexpr int KB = KeysPerBatch<TA>::value;
+  constexpr int KB = WavePiece<TA, EPL>::kKB;
+  using Raw = typename WavePiece<TA, EPL>::T;
   constexpr bool kQ = sizeof(TA) == 1;   // int8 cache with per-slot scales
   const int lane = threadIdx.x & 63;
   const int pair = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
@@ -393,30 +413,30 @@ __global__ __launch_bounds__(256) void k_attention_wave(
   const size_t scale_base = ((size_t)m * H + h) * (size_t)max_len;
   const float *qr = q + ((size_t)m * H + h) * d;
 
-  // lane group g (L = d/8 lanes) takes slots j = g (mod G) of each batch; lane `sub`
-  // owns dims [8 sub, 8 sub + 8)
-  const int L = d >> 3;
+  // lane group g (L = d / EPL lanes) takes slots j = g (mod G) of each batch; lane `sub`
+  // owns dims [EPL sub, EPL sub + EPL)
+  const int L = d / EPL;
   const int G = 64 / L;
   const int g = lane / L, sub = lane - g * L;
-  float qv[8];
+  float qv[EPL];
 #pragma unroll
-  for (int t = 0; t < 8; ++t) qv[t] = qr[8 * sub + t];
+  for (int t = 0; t < EPL; ++t) qv[t] = qr[EPL * sub + t];
   const int vl = vl_in < 1 ? 1 : (vl_in > prompt_len ? prompt_len : vl_in);
   const int first = prompt_len - vl;
 
   float mrun = -INFINITY, lsum = 0.f;
-  float acc[8];
+  float acc[EPL];
 #pragma unroll
-  for (int t = 0; t < 8; ++t) acc[t] = 0.f;
+  for (int t = 0; t < EPL; ++t) acc[t] = 0.f;
   for (int j0 = 0; j0 < S; j0 += G * KB) {
     // slots past the end load slot S - 1 (written, masked below): no branch around loads
-    KVRaw<TA> kr[KB], vr[KB];
+    Raw kr[KB], vr[KB];
     float ks[KB], vs[KB];
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
       const int jj = min(j0 + u * G + g, S - 1);
-      kr[u].load(kb + (size_t)jj * d + 8 * sub);
-      vr[u].load(vb + (size_t)jj * d + 8 * sub);
+      kr[u].load(kb + (size_t)jj * d + EPL * sub);
+      vr[u].load(vb + (size_t)jj * d + EPL * sub);
       if constexpr (kQ) {
         ks[u] = ksc[scale_base + jj];
         vs[u] = vsc[scale_base + jj];
@@ -429,7 +449,7 @@ __global__ __launch_bounds__(256) void k_attention_wave(
       const int jj = j0 + u * G + g;
       float dot = 0.f;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) dot = fmaf(qv[t], kr[u].get(t), dot);
+      for (int t = 0; t < EPL; ++t) dot = fmaf(qv[t], kr[u].get(t), dot);
       for (int off = L >> 1; off > 0; off >>= 1) dot += __shfl_xor(dot, off, 64);
       if constexpr (kQ) dot *= ks[u];
       sc[u] = (jj < S && jj >= first) ? dot + slope * (float)(jj - qpos) : -INFINITY;
@@ -442,7 +462,7 @@ __global__ __launch_bounds__(256) void k_attention_wave(
     const float alpha = mrun == -INFINITY ? 0.f : __expf(mrun - mnew);
     lsum *= alpha;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) acc[t] *= alpha;
+    for (int t = 0; t < EPL; ++t) acc[t] *= alpha;
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
       const int jj = j0 + u * G + g;
@@ -452,7 +472,7 @@ __global__ __launch_bounds__(256) void k_attention_wave(
         float pw = p;
         if constexpr (kQ) pw = p * vs[u];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) acc[t] = fmaf(pw, vr[u].get(t), acc[t]);
+        for (int t = 0; t < EPL; ++t) acc[t] = fmaf(pw, vr[u].get(t), acc[t]);
       }
     }
     mrun = mnew;
@@ -461,16 +481,16 @@ __global__ __launch_bounds__(256) void k_attention_wave(
 #pragma unroll
   for (int off = L; off < 64; off <<= 1)
 #pragma unroll
-    for (int t = 0; t < 8; ++t) acc[t] += __shfl_xor(acc[t], off, 64);
+    for (int t = 0; t < EPL; ++t) acc[t] += __shfl_xor(acc[t], off, 64);
   const float total = wave_sum(lsum);
   if (g == 0) {
     // a query with no visible key gets o = 0
     const float inv = qpos < first ? 0.f : 1.0f / total;
-    const size_t out0 = ((size_t)m * H + h) * d + 8 * sub;
-    act_store4(o, o_fmt, out0, o_plane,
-               make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv));
-    act_store4(o, o_fmt, out0 + 4, o_plane,
-               make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv));
+    const size_t out0 = ((size_t)m * H + h) * d + EPL * sub;
+#pragma unroll
+    for (int t = 0; t < EPL; t += 4)
+      act_store4(o, o_fmt, out0 + t, o_plane,
+                 make_float4(acc[t] * inv, acc[t + 1] * inv, acc[t + 2] * inv, acc[t + 3] * inv));
   }
 }
 
@@ -490,10 +510,19 @@ static void launch_attention_t(const float *q, const void *kc, const void *vc, c
                        head_off, rows_per_seq, pos_base, prompt_len, nchunk);
   } else if (nsplit == 1 && rows_per_seq == 1 && (long)rows * H >= kAttnWavePairs) {
     const int pairs = rows * H;
-    hipLaunchKernelGGL(k_attention_wave<TA>, dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0,
-                       st, q, (const TA *)kc, (const TA *)vc, ksc, vsc, valid_len, o, o_fmt,
-                       o_plane, H, d, max_len, n_total, head_off, pairs, pos_base, pos_dev,
-                       prompt_len);
+    const dim3 grid((unsigned)((pairs + 3) / 4)), block(256);
+    bool wide = false;
+    if constexpr (sizeof(TA) == 1) {
+      wide = d >= 16;
+      if (wide)
+        hipLaunchKernelGGL((k_attention_wave<TA, 16>), grid, block, 0, st, q, (const TA *)kc,
+                           (const TA *)vc, ksc, vsc, valid_len, o, o_fmt, o_plane, H, d,
+                           max_len, n_total, head_off, pairs, pos_base, pos_dev, prompt_len);
+    }
+    if (!wide)
+      hipLaunchKernelGGL((k_attention_wave<TA, 8>), grid, block, 0, st, q, (const TA *)kc,
+                         (const TA *)vc, ksc, vsc, valid_len, o, o_fmt, o_plane, H, d, max_len,
+                         n_total, head_off, pairs, pos_base, pos_dev, prompt_len);
   } else {
     const int chunk = (max_len + nsplit - 1) / nsplit;
     const dim3 grid(rows, H, nsplit), block(256);
