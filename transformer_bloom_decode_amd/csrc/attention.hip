@@ -104,27 +104,48 @@ __global__ __launch_bounds__(256) void k_attention(const float *__restrict__ q,
   const int m = blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x;
   const int b = m / rows_per_seq;
-  // a position read from device memory is clamped to the cache (the host checks the
-  // others): slots at or past max_len are never addressed
-  const int qpos = min((pos_dev ? *pos_dev : pos_base) + (m - b * rows_per_seq), max_len - 1);
-  // The K/V loads below address slots 0..qpos directly and do not wait for valid_len:
-  // the left-pad slots [0, first) are loaded too (the prompt pass wrote them) and
-  // masked in the scores.
-  const int vl_in = valid_len[b];
-  const size_t out0 = ((size_t)m * H + h) * d;
-  const int S = qpos + 1;
-  const float slope = alibi_slope(n_total, head_off + h);
   const size_t head_base = ((size_t)b * H + h) * (size_t)max_len * d;
   const TA *kb = kc + head_base;
   const TA *vb = vc + head_base;
   const size_t scale_base = ((size_t)b * H + h) * (size_t)max_len;
-  const float *qr = q + ((size_t)m * H + h) * d;
 
   // lane group g (L = d/8 lanes) handles slots j = g (mod G); lane `sub` owns dims
   // [8 sub, 8 sub + 8) of each of them
   const int L = d >> 3;
   const int G = 256 / L;
   const int g = tid / L, sub = tid - g * L;
+
+  // The K/V loads address slots directly and wait neither for the position nor for
+  // valid_len: the first batch goes out before the position is read (slots up to the
+  // cache end, in bounds), later ones up to the block's last slot; slots past the last
+  // visible one, and the left-pad slots [0, first) (the prompt pass wrote them), are
+  // masked in the scores.
+  KVRaw<TA> kr[KB], vr[KB];
+  float ks[KB], vs[KB];
+  auto load_batch = [&](int j0, int jcap) {
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      const int jj = min(j0 + u * G + g, jcap);
+      kr[u].load(kb + (size_t)jj * d + 8 * sub);
+      vr[u].load(vb + (size_t)jj * d + 8 * sub);
+      if constexpr (kQ) {
+        ks[u] = ksc[scale_base + jj];
+        vs[u] = vsc[scale_base + jj];
+      }
+    }
+  };
+  const int z = blockIdx.z;
+  const int jlo = part ? z * chunk : 0;
+  load_batch(jlo, max_len - 1);
+
+  // a position read from device memory is clamped to the cache (the host checks the
+  // others): slots at or past max_len are never addressed
+  const int qpos = min((pos_dev ? *pos_dev : pos_base) + (m - b * rows_per_seq), max_len - 1);
+  const int vl_in = valid_len[b];
+  const size_t out0 = ((size_t)m * H + h) * d;
+  const int S = qpos + 1;
+  const float slope = alibi_slope(n_total, head_off + h);
+  const float *qr = q + ((size_t)m * H + h) * d;
   float qv[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) qv[t] = qr[8 * sub + t];
@@ -136,28 +157,13 @@ __global__ __launch_bounds__(256) void k_attention(const float *__restrict__ q,
   // rescaled by exp(mrun_old - mrun_new) when the maximum grows.
   // split over the keys (part set): block z takes slots [z chunk, (z + 1) chunk) and
   // leaves its unnormalised partial (running max, sum, P.V) for k_attention_merge
-  const int z = blockIdx.z;
-  const int jlo = part ? z * chunk : 0;
   const int jhi = part ? min(S, jlo + chunk) : S;
   float mrun = -INFINITY, lsum = 0.f;
   float acc[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) acc[t] = 0.f;
   for (int j0 = jlo; j0 < jhi; j0 += G * KB) {
-    KVRaw<TA> kr[KB], vr[KB];
-    float ks[KB], vs[KB];
-#pragma unroll
-    for (int u = 0; u < KB; ++u) {
-      const int jj = j0 + u * G + g;
-      if (jj < jhi) {
-        kr[u].load(kb + (size_t)jj * d + 8 * sub);
-        vr[u].load(vb + (size_t)jj * d + 8 * sub);
-        if constexpr (kQ) {
-          ks[u] = ksc[scale_base + jj];
-          vs[u] = vsc[scale_base + jj];
-        }
-      }
-    }
+    if (j0 != jlo) load_batch(j0, jhi - 1);
     // scores s_j = q.k_j + slope * (j - qpos), summed across the group's L lanes;
     // slots before `first` are masked
     float sc[KB];
@@ -166,12 +172,10 @@ __global__ __launch_bounds__(256) void k_attention(const float *__restrict__ q,
     for (int u = 0; u < KB; ++u) {
       const int jj = j0 + u * G + g;
       float dot = 0.f;
-      if (jj < jhi) {
 #pragma unroll
-        for (int t = 0; t < 8; ++t) dot = fmaf(qv[t], kr[u].get(t), dot);
-      }
+      for (int t = 0; t < 8; ++t) dot = fmaf(qv[t], kr[u].get(t), dot);
       for (int off = L >> 1; off > 0; off >>= 1) dot += __shfl_xor(dot, off, 64);
-      if constexpr (kQ) dot = jj < jhi ? dot * ks[u] : 0.f;
+      if constexpr (kQ) dot *= ks[u];
       sc[u] = (jj < jhi && jj >= first) ? dot + slope * (float)(jj - qpos) : -INFINITY;
       bmax = fmaxf(bmax, sc[u]);
     }
