@@ -574,6 +574,11 @@ LinearPlan plan_linear(int wdtype, int M, int N, int K, bool argmax, int act) {
   if (M <= kValuMaxRows) {
     // int8 activations: the GEMV reads the codes (the epilogue applies the row scales)
     p = plan_valu(wdtype, M, N, K);
+    if (argmax && p.ks != 1) {   // the argmax epilogue takes whole rows per wave
+      p.ks = 1;
+      p.vu = 28;
+      p.grid_x = (N + 4 * p.vr - 1) / (4 * p.vr);
+    }
     p.x_fmt = act;
     p.q8 = q8;
     return p;

@@ -113,7 +113,11 @@ __device__ __forceinline__ void fold_stats_add(const EpiParams &ep, float xn) {
 // the row's pieces, a wave issues its whole row in one go, which keeps the most bytes
 // in flight when the grid is too small to fill every wave slot).  TX: activation type
 // (bf16, or float32 when the model keeps float32 activations).
-template <typename TW, typename TP, typename TX, int MR, int R, int U, bool DB>
+// KS: waves per weight row.  KS = 2 splits each row's K range in halves between the two
+// waves of a pair (rows per block 4 R / 2): the half-length waves finish in half the
+// time, so the drain of the last round of waves is shorter; the second half's dot
+// product reaches the first through LDS and is added after the first's, in that order.
+template <typename TW, typename TP, typename TX, int MR, int R, int U, bool DB, int KS = 1>
 __global__ __launch_bounds__(256) void k_gemv_valu(const TX *__restrict__ X,
                                                    const TW *__restrict__ W, int M, int N, int K,
                                                    EpiParams ep) {
@@ -123,9 +127,12 @@ __global__ __launch_bounds__(256) void k_gemv_valu(const TX *__restrict__ X,
   constexpr int XP = E / XO::kPer16;                      // 16-byte activation pieces per step
   __shared__ float am_v[4][MR];
   __shared__ int am_i[4][MR];
+  static_assert(KS == 1 || (KS == 2 && !DB), "the K split runs on single-buffered rows");
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
-  const int row0 = (blockIdx.x * 4 + wid) * R;
+  const int wrow = KS == 1 ? wid : (wid >> 1);   // the wave's row group in the block
+  const int half = KS == 1 ? 0 : (wid & 1);      // its part of the K range
+  const int row0 = (blockIdx.x * (4 / KS) + wrow) * R;
   const TW *wr[R];
 #pragma unroll
   for (int i = 0; i < R; ++i) wr[i] = W + (size_t)min(row0 + i, N - 1) * K;
@@ -145,7 +152,8 @@ __global__ __launch_bounds__(256) void k_gemv_valu(const TX *__restrict__ X,
   // keep their registers for the weights and load them in the epilogue.
   constexpr bool kPre = MR == 1 && sizeof(TW) == 2 && sizeof(TX) == 2;
   const int on = row0 + lane / MR, om = lane % MR;
-  const bool has_out = lane < R * MR && on < N && om < M && ep.mode != EPI_ARGMAX;
+  const bool has_out =
+      half == 0 && lane < R * MR && on < N && om < M && ep.mode != EPI_ARGMAX;
   EpiPre pre{};
   if constexpr (kPre) {
     if (has_out) pre = epi_prefetch<TP>(ep, om, on);
@@ -153,7 +161,7 @@ __global__ __launch_bounds__(256) void k_gemv_valu(const TX *__restrict__ X,
   float fold_c = 0.f, fold_d = 0.f;   // c_n and d_n of the lane's output row
   if constexpr (kFold) {
     if (ep.ln_stats) {
-      if (lane < R && row0 + lane < N) {
+      if (half == 0 && lane < R && row0 + lane < N) {
         fold_c = ep.ln_cd[row0 + lane];
         fold_d = ep.ln_cd[N + row0 + lane];
       }
@@ -174,7 +182,9 @@ __global__ __launch_bounds__(256) void k_gemv_valu(const TX *__restrict__ X,
     for (int m = 0; m < MR; ++m) acc[i][m] = 0.f;
 
   const int step = 64 * E;                                // elements per wave step
-  const int nsteps = (K + step - 1) / step;
+  const int nsteps_all = (K + step - 1) / step;
+  const int sbeg = half * ((nsteps_all + KS - 1) / KS);   // the wave's steps [sbeg, nsteps)
+  const int nsteps = KS == 1 ? nsteps_all : min(nsteps_all, sbeg + (nsteps_all + KS - 1) / KS);
   u32x4 cw[U][R], cx[U][MR][XP];
 
   auto load = [&](int s0, u32x4(&w)[U][R], u32x4(&x)[U][MR][XP]) {
@@ -230,7 +240,7 @@ __global__ __launch_bounds__(256) void k_gemv_valu(const TX *__restrict__ X,
       }
     }
   } else {
-    for (int s0 = 0; s0 < nsteps; s0 += U) {
+    for (int s0 = sbeg; s0 < nsteps; s0 += U) {
       load(s0, cw, cx);
       compute();
     }
@@ -240,6 +250,22 @@ __global__ __launch_bounds__(256) void k_gemv_valu(const TX *__restrict__ X,
   for (int i = 0; i < R; ++i)
 #pragma unroll
     for (int m = 0; m < MR; ++m) acc[i][m] = wave_sum(acc[i][m]);
+  if constexpr (KS == 2) {
+    __shared__ float kpart[2][R * MR];   // second halves' dot products, per row group
+    if (half == 1 && lane == 0) {
+#pragma unroll
+      for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int m = 0; m < MR; ++m) kpart[wrow][i * MR + m] = acc[i][m];
+    }
+    __syncthreads();
+    if (half == 0) {
+#pragma unroll
+      for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int m = 0; m < MR; ++m) acc[i][m] += kpart[wrow][i * MR + m];
+    }
+  }
 
   float ln_mean = 0.f, ln_rstd = 0.f;
   if constexpr (kFold) {
@@ -496,11 +522,15 @@ LinearPlan plan_valu(int wdtype, int M, int N, int K) {
   p.vr = 2;
   p.vu = p.mt == 4 ? 2 : 4;
   p.vdb = true;
+  p.ks = 1;
   const int pieces = (K + 511) / 512;  // 1 KB wave loads of bf16
   if (p.mt == 1 && wdtype == WT_BF16 && N < 65536 && pieces > 4 && pieces <= 28) {
     p.vr = 1;
     p.vu = pieces <= 16 ? 16 : 28;
     p.vdb = false;
+    // rows of 17-28 pieces (QKV and MLP-up of the 176B share, K = 14336): each row in
+    // two halves of at most 14 pieces, on the two waves of a pair
+    if (pieces > 16) { p.vu = 14; p.ks = 2; }
   }
   // Batch-1 bf16 linears with short rows (up to 2048) and many of them (the attention
   // output projection of the 176B share, 14336 x 1792): 4 whole rows per wave, so the
@@ -510,7 +540,8 @@ LinearPlan plan_valu(int wdtype, int M, int N, int K) {
     p.vu = 4;
     p.vdb = false;
   }
-  p.grid_x = (N + 4 * p.vr - 1) / (4 * p.vr);
+  const int rows_per_block = 4 * p.vr / p.ks;
+  p.grid_x = (N + rows_per_block - 1) / rows_per_block;
   p.splits = 1;
   return p;
 }
@@ -524,7 +555,9 @@ static void launch_valu_t(const LinearPlan &p, const void *X, const void *W, con
   const TW *w = (const TW *)W;
   if constexpr (std::is_same<TW, bf16_t>::value) {
     if (p.vr == 1 && p.mt == 1 && !p.vdb) {
-      if (p.vu == 16)
+      if (p.ks == 2)
+        BL_LAUNCH((k_gemv_valu<TW, TP, TX, 1, 1, 14, false, 2>), grid, block, 0, st, x, w, p.M, p.N, p.K, ep);
+      else if (p.vu == 16)
         BL_LAUNCH((k_gemv_valu<TW, TP, TX, 1, 1, 16, false>), grid, block, 0, st, x, w, p.M, p.N, p.K, ep);
       else
         BL_LAUNCH((k_gemv_valu<TW, TP, TX, 1, 1, 28, false>), grid, block, 0, st, x, w, p.M, p.N, p.K, ep);

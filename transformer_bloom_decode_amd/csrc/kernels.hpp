@@ -55,6 +55,7 @@ struct LinearPlan {
   int mt;        // VALU: activation rows (1, 2, 4)
   int vr, vu;    // VALU: weight rows per wave, 16-byte pieces per row issued per batch
   bool vdb;      // VALU: double-buffered batches
+  int ks;        // VALU: waves per weight row (1, or 2: the row's K range split in halves)
   int lg;        // LG: tile configuration (LgTile in gemm.hip)
   int grid_x, grid_y;
   int splits;    // K splits (> 1: partial sums + reduction kernel)
