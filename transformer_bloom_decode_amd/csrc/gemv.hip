@@ -1,7 +1,8 @@
 // Decode GEMV on the vector ALU for up to 4 activation rows (the batch-1..4 decode
 // step and LM head): each wave streams one or two weight rows in 1 KB non-temporal
-// loads (whole rows at once when the grid leaves wave slots empty); the block's output
-// rows are finished by the fused epilogue (or an argmax for the LM head).  The pages'
+// loads (whole rows, or half rows on a pair of waves, at once when the grid leaves wave
+// slots empty); the block's output rows are finished by the fused epilogue (or an
+// argmax for the LM head).  The pages'
 // analysis ("DeepSpeed Inference ...", Section III.A) is that small-batch inference is
 // bound by reading the weights once; this kernel is built around streaming W at full
 // bandwidth.  Its planning (rows per wave, pieces in flight) and launch live here too.
@@ -17,13 +18,13 @@ __device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
 // ---------------------------------------------------------------------------
 // decode GEMV on the vector ALU (M <= 4 activation rows)
 // ---------------------------------------------------------------------------
-// Each wave owns R consecutive weight rows over the full K.  Per step every lane
-// loads one 16-byte piece of each of its rows, so a wave load instruction covers
-// 1 KB of one row contiguously; the loads are non-temporal (streamed weights are
-// not kept in the caches that hold activations and the KV cache).  Weights are
-// widened to float32 in registers and multiplied by the matching activation values
-// with fmaf; each lane keeps R*M running sums, reduced across the wave at the end.
-// U steps are loaded ahead of the one being multiplied.
+// Each wave owns R consecutive weight rows over the full K (or, with KS > 1, over its
+// part of K, below).  Per step every lane loads one 16-byte piece of each of its rows,
+// so a wave load instruction covers 1 KB of one row contiguously; the loads are
+// non-temporal (streamed weights are not kept in the caches that hold activations and
+// the KV cache).  Weights are widened to float32 in registers and multiplied by the
+// matching activation values with fmaf; each lane keeps R*M running sums, reduced
+// across the wave at the end.  U steps are loaded ahead of the one being multiplied.
 template <typename TW> struct VOps;
 
 template <> struct VOps<bf16_t> {
